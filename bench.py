@@ -1,0 +1,232 @@
+"""Throughput of the ISD step on one MI355X.
+
+A step is one pass of the whole hot path over the batch: isd_attention ->
+isd_accept -> kv_commit (+ isd_lora_delta for the R-ISD workload), enqueued on
+one stream.  Inputs are synthetic (workloads/), generated on the host and
+resident in HBM before the timed region.  To keep the Infinity Cache (256 MB)
+from serving repeated steps, the timed loop rotates over several independent
+copies of every input whose total exceeds the cache several times over.  The
+commit writes lengths to a second buffer, so every timed step sees the same
+context lengths (the committed rows land in slots the next attention does not
+read).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c32_ctx4k]
+
+Prints one JSON line (see the keys below).  --gpus above 1 is refused: the
+step shards by request with no exchange, but this benchmark runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
+MALL_BYTES = 256 * 2 ** 20
+
+
+def algorithmic_bytes(wl):
+    """Bytes each call must move at least once (inputs read once, outputs written once)."""
+    cfg = wl.cfg
+    s = cfg.elem_bytes
+    B, Q, Hq, Hkv, D, N, V = (cfg.batch, cfg.q_rows, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                              cfg.stride_n, cfg.vocab)
+    ctx = wl.ctx_lens.astype("int64")
+    pages_read = int(((ctx + 15) // 16).sum())
+    attn = (int(ctx.sum()) * Hkv * D * 2 * s          # K and V context
+            + B * Q * Hq * D * s * 2                     # q in, out
+            + B * Q * Hkv * D * s * 2                    # k_new, v_new
+            + pages_read * 4 + B * 4)                    # page-table entries, lengths
+    accept = (2 * B * (N - 1) * V * s                    # p and q logits, one read
+              + B * N * 4 * 2 + B * 4 * 4 + 2 * B * (N - 1) * 4)
+    return {"attention": attn, "accept": accept}
+
+
+def commit_bytes(wl, n_commit):
+    cfg = wl.cfg
+    rows = int(n_commit.sum())
+    return rows * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes * 2 * 2 + cfg.batch * 12
+
+
+def lora_bytes(cfg):
+    d, r = cfg.lora_dim, cfg.lora_rank
+    m = cfg.batch * cfg.stride_n
+    return (m * d + d * r + r * d + 2 * m * d) * 2 + m * 4
+
+
+def cpu_baseline(wl, budget_s: float = 10.0, max_steps: int = 8):
+    """Time the float64 oracle on the host: whole steps (attention for every request, accept,
+    commit) of the same workload, repeated until about ``budget_s`` seconds have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.accept import isd_accept as o_accept
+    from oracle.attention import stride_attention
+    from oracle.commit import kv_commit as o_commit
+
+    cfg = wl.cfg
+    t_start = time.perf_counter()
+    steps_done = 0
+    accepted = 0
+    while steps_done < max_steps:
+        stride_attention(wl.q, wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, wl.page_table,
+                         wl.ctx_lens, cfg.page_size)
+        res = o_accept(wl.p_logits, wl.q_logits, wl.proposals, wl.req_ids, wl.positions,
+                       wl.philox_seed, wl.step)
+        n_commit = np.array([o.n_commit for o in res])
+        o_commit(wl.k_pool, wl.v_pool, wl.page_table, wl.ctx_lens, wl.k_new, wl.v_new, n_commit,
+                 cfg.page_size)
+        accepted += sum(o.accept_len for o in res)
+        steps_done += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    elapsed = time.perf_counter() - t_start
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": round(steps_done / elapsed, 4),
+        "unit": "verify-steps/s",
+        "accepted_tokens_per_s": round(accepted / elapsed, 2),
+        "cores": int(threads),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"{steps_done} whole steps of the {cfg.name} workload (float64 attention for "
+                   f"every request, accept with residual, commit)"),
+        "seconds": round(elapsed, 2),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--config", default="c32_ctx4k")
+    ap.add_argument("--sets", type=int, default=0, help="input copies rotated in the timed loop (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the ISD step shards by request with no exchange, "
+              "and this build measures the single-GPU step (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from introspective_strided_decoding_amd.step import DeviceStep
+    from workloads import get_config, make_workload
+
+    cfg = get_config(args.config)
+    t_gen = time.perf_counter()
+    wl = make_workload(cfg)
+    t_gen = time.perf_counter() - t_gen
+    nbytes = algorithmic_bytes(wl)
+    step_bytes = nbytes["attention"] + nbytes["accept"]
+    per_set = step_bytes + (lora_bytes(cfg) if cfg.lora else 0)
+    sets = args.sets or max(2, min(8, int(np.ceil(4 * MALL_BYTES / per_set))))
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    base = DeviceStep.from_arrays(wl, device=dev, max_ctx=int(wl.ctx_lens.max()))
+    steps = [base]
+    for _ in range(sets - 1):
+        st = DeviceStep.from_arrays(wl, device=dev, max_ctx=int(wl.ctx_lens.max()))
+        steps.append(st)
+    use_lora = cfg.lora
+    if use_lora:
+        try:
+            base.lora_delta()
+            torch.cuda.synchronize()
+        except Exception as e:  # LoRA entry point missing in this build
+            print(f"bench: LoRA delta not run ({e})", file=sys.stderr)
+            use_lora = False
+
+    stream = torch.cuda.current_stream()
+
+    def one_step(st, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st.attention()
+        if ev is not None:
+            ev[1].record(stream)
+        st.accept()
+        st.commit()
+        if use_lora:
+            st.lora_delta()
+
+    for i in range(args.warmup):
+        one_step(steps[i % sets])
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(steps[i % sets], events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    ms_per_step = elapsed * 1e3 / args.steps
+    steps_per_s = args.steps / elapsed
+
+    # accepted / committed tokens of the timed steps (identical draws per set)
+    acc = [int(st.accept_len.sum().item()) for st in steps]
+    ncommit = steps[0].n_commit.cpu().numpy()
+    accepted_per_step = float(np.mean(acc))
+    committed_per_step = float(np.mean([int(st.n_out.sum().item()) for st in steps]))
+    total_bytes = step_bytes + commit_bytes(wl, ncommit) + (lora_bytes(cfg) if use_lora else 0)
+
+    out = {
+        "metric": "ISD verify-steps/s + accepted tokens/s at concurrency 32, N=4; % HBM peak",
+        "value": round(steps_per_s, 2),
+        "unit": "verify-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "ctx": cfg.ctx or list(cfg.ctx_range),
+                   "stride_n": cfg.stride_n, "q_rows": cfg.q_rows, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "vocab": cfg.vocab,
+                   "page_size": cfg.page_size, "lora": bool(use_lora), "input_sets": sets,
+                   "description": cfg.description},
+        "accepted_tokens_per_s": round(accepted_per_step * steps_per_s, 1),
+        "committed_tokens_per_s": round(committed_per_step * steps_per_s, 1),
+        "request_steps_per_s": round(cfg.batch * steps_per_s, 1),
+        "accepted_per_step": accepted_per_step,
+        "step_hbm": {"bytes": int(total_bytes), "achieved_GBs": round(total_bytes / ms_per_step / 1e6, 1),
+                     "frac": round(total_bytes / ms_per_step / 1e6 / HBM_PEAK_GBS, 4)},
+        "roofline": {
+            "kernel": "isd_attention (split-KV MFMA kernel + combine)",
+            "bound": "hbm",
+            "achieved": round(nbytes["attention"] / attn_ms / 1e6, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes["attention"] / attn_ms / 1e6 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": int(nbytes["attention"]),
+            "avg_launch_ms": round(attn_ms, 5),
+        },
+        "input_gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

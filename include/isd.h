@@ -1,0 +1,265 @@
+/*
+ * isd.h -- C ABI of libisd.so: one Introspective Strided Decoding (ISD) step
+ * on an AMD Instinct MI355X (gfx950).
+ *
+ * The step (I-DLM project page, ISD card; "I-DLM：扩散模型如何用'自省一致性'
+ * 追上自回归模型质量", section "Introspective Strided Decoding（ISD）";
+ * "自省扩散语言模型的 token 生成机制与工程实践", section "Token 生成的核心参数与
+ * 验收机制"): every request carries a stride of Q = 2N-1 query rows.  Rows
+ * 0..N-2 are CLEAN rows holding the previous pass's proposals x_1..x_{N-1};
+ * rows N-1..2N-2 are MASK rows that propose the next N tokens.  One forward
+ * both verifies and proposes:
+ *
+ *   isd_attention  strictly causal multi-query attention of the stride over
+ *                  the request's paged KV cache and the stride itself;
+ *   isd_accept     the p/q test: accept x_k with probability min(1, p/q),
+ *                  resample from normalize(max(0, p - q)) at the first
+ *                  rejection;
+ *   kv_commit      append the CLEAN rows of accepted tokens to the KV pages;
+ *   isd_lora_delta the gated low-rank delta of Residual ISD (R-ISD), added at
+ *                  MASK rows only.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers owned by the caller, dense,
+ *   row-major in the index order written next to them.  The library never
+ *   allocates, frees or synchronises on these calls; the work is enqueued on
+ *   `stream` and the call returns at once.  Calls on one stream run in order;
+ *   the intended order per step is attention -> accept -> commit.
+ * - Arguments are validated on the host before anything is enqueued.  A bad
+ *   argument returns an isd_status != ISD_OK and enqueues nothing.  Values
+ *   that live in device memory (context lengths, page-table entries, token
+ *   ids, commit counts) cannot be checked on the host: the kernels bound-check
+ *   them, skip the offending access, and OR a bit into the device flag word
+ *   (ISD_FLAG_*) at byte offset 0 of the workspace.  Results for a request
+ *   that raised a flag are unspecified, but no access leaves the buffers.
+ * - The workspace is caller-owned device memory of at least
+ *   isd_workspace_bytes() bytes, prepared once by isd_workspace_init().  It
+ *   holds scratch partials and the flag word and may be reused by every call
+ *   on the same stream; concurrent calls must use distinct workspaces.
+ * - A launch failure returns ISD_ERR_HIP; isd_last_error() gives the text.
+ *   Nothing crosses the ABI as a C++ exception.
+ */
+#ifndef ISD_H
+#define ISD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum isd_status {
+  ISD_OK = 0,
+  ISD_ERR_NULL = 1,         /* a required pointer is NULL */
+  ISD_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes */
+  ISD_ERR_DTYPE = 3,        /* unknown dtype */
+  ISD_ERR_WORKSPACE = 4,    /* workspace smaller than isd_workspace_bytes() */
+  ISD_ERR_UNSUPPORTED = 5,  /* valid request this build does not implement */
+  ISD_ERR_HIP = 6,          /* a HIP launch or runtime call failed */
+  ISD_ERR_ALIGNMENT = 7     /* a tensor pointer is not 16-byte aligned */
+} isd_status;
+
+typedef enum isd_dtype {
+  ISD_F32 = 0,   /* IEEE binary32 */
+  ISD_BF16 = 1   /* bfloat16 */
+} isd_dtype;
+
+/* Device flag bits (workspace byte offset 0, uint32). */
+#define ISD_FLAG_CTX_RANGE 0x1u    /* ctx_lens[r] < 0 or > max_pages * page_size */
+#define ISD_FLAG_PAGE_RANGE 0x2u   /* a needed page_table entry is outside [0, num_pages) */
+#define ISD_FLAG_TOKEN_RANGE 0x4u  /* a proposal id is outside [0, vocab) */
+#define ISD_FLAG_COMMIT_RANGE 0x8u /* n_commit[r] outside [0, N-1], or no page for a commit slot */
+#define ISD_FLAG_ROW_RANGE 0x10u   /* a LoRA mask row is outside [0, rows) */
+
+/*
+ * Sizes of one step.
+ *   Q = 2 * stride_n - 1 query rows per request; G = n_q_heads / n_kv_heads.
+ *   Supported: stride_n >= 2, head_dim in {64, 128}, page_size == 16,
+ *   G * Q <= 64 (query rows per KV head), n_q_heads % n_kv_heads == 0.
+ *   max_ctx is a hint (an upper bound of the context lengths, used to split
+ *   the KV walk across workgroups); 0 means max_pages * page_size.  A context
+ *   longer than max_ctx is still processed correctly, only less evenly.
+ */
+typedef struct isd_shape {
+  int32_t batch;        /* B: requests in the step */
+  int32_t stride_n;     /* N: proposals per stride */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* Hkv */
+  int32_t head_dim;     /* D */
+  int32_t page_size;    /* tokens per KV page (16) */
+  int32_t max_pages;    /* columns of page_table */
+  int32_t num_pages;    /* pages in the pool */
+  int32_t vocab;        /* V */
+  int32_t max_ctx;      /* hint, see above */
+  isd_dtype kv_dtype;   /* q, k_new, v_new, pages, out */
+  isd_dtype logit_dtype;/* p_logits, q_logits */
+} isd_shape;
+
+/*
+ * KV page pool layout (both pools hold num_pages pages; e = element size):
+ *
+ *   k_pages[page][kv_head][d / 8][slot][d % 8]
+ *   v_pages[page][kv_head][d][sigma(slot)]
+ *
+ * sigma swaps bits 2 and 3 of the slot index (sigma(s) = (s & 3) |
+ * ((s & 4) << 1) | ((s & 8) >> 1)); it is its own inverse.  Token position t
+ * of request r lives in page page_table[r * max_pages + t / page_size],
+ * slot t % page_size.  Both layouts let one 64-lane wavefront read a page's
+ * keys or values as fully used 16-byte vectors that feed the matrix cores
+ * directly.
+ */
+
+/* Workspace bytes needed by isd_attention, isd_accept and kv_commit for `shape`. */
+size_t isd_workspace_bytes(const isd_shape* shape);
+
+/* Zero the workspace header (flag word and internal counters) on `stream`. */
+isd_status isd_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Read the device flag word of `workspace` into *flags.  This call copies
+ * to the host and synchronises `stream`; it is meant for checks, not for the
+ * per-step path.
+ */
+isd_status isd_read_flags(const void* workspace, uint32_t* flags, hipStream_t stream);
+
+/*
+ * isd_attention -- strictly causal stride attention over the paged KV cache.
+ *
+ * Definition ("I-DLM：扩散模型如何用'自省一致性'追上自回归模型质量", section
+ * "三项关键训练创新", item 1: one causal mask over MASK and clean tokens;
+ * I-DLM project page, ISD card): stride row i of request r sits at absolute
+ * position L_r + i (L_r = ctx_lens[r]) and query head h reads KV head h / G.
+ * Row i attends to the cached positions 0..L_r-1 (from the pages) and to the
+ * stride's own rows 0..i (k_new / v_new), never to later rows:
+ *
+ *   out[r][i][h] = sum_t softmax_t(scale * q[r][i][h] . k_t) v_t
+ *
+ *   q      [B][Q][Hq][D]    kv_dtype
+ *   k_new  [B][Q][Hkv][D]   kv_dtype (keys of this pass's stride rows)
+ *   v_new  [B][Q][Hkv][D]   kv_dtype
+ *   k_pages, v_pages        pool layout above, kv_dtype
+ *   page_table [B][max_pages] int32; entries past a request's pages are ignored
+ *   ctx_lens   [B] int32    cached positions per request, 0 allowed
+ *   scale      softmax scale; 0 selects 1/sqrt(D)
+ *   out    [B][Q][Hq][D]    kv_dtype, written
+ *
+ * Accumulation is fp32 (bf16 inputs run on the matrix cores).  Flags:
+ * CTX_RANGE, PAGE_RANGE.
+ */
+isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_new,
+                         const void* v_new, const void* k_pages, const void* v_pages,
+                         const int32_t* page_table, const int32_t* ctx_lens, float scale,
+                         void* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * isd_accept -- the p/q acceptance test with residual resampling.
+ *
+ * Definition ("I-DLM：扩散模型如何用'自省一致性'追上自回归模型质量", section
+ * "Introspective Strided Decoding（ISD）"; "自省扩散语言模型的 token 生成机制与
+ * 工程实践", sections "从质量差距到自省机制" and "Token 生成的核心参数与验收机制";
+ * I-DLM project page, caption on geometric acceptance):
+ *   - x_1 = proposals[r][0] was decided before this step and is always kept.
+ *   - For k = 2..N, row j = k-2 of p_logits is the anchor distribution p
+ *     (from CLEAN row j, logit-shifted) and row j of q_logits the proposal
+ *     distribution q that produced x_k.  Logits are used as given
+ *     (temperature already applied).
+ *   - rho_k = exp(log p(x_k) - log q(x_k)); accept iff u_k < rho_k; stop at
+ *     the first rejection.  accept_len = A = 1 + leading accepts, in [1, N].
+ *   - If A < N, the token at position A+1 is y* = the first y (in vocabulary
+ *     order) whose running sum of max(0, p - q) exceeds u'_k * sum(max(0, p - q)),
+ *     computed in float64; if that sum is 0, p itself is sampled the same way.
+ *   - u_k and u'_k are words 0 and 1 of the Philox4x64-10 block (Salmon et
+ *     al., SC'11) with key (seed_lo, seed_hi) and counter
+ *     (req_ids[r], positions[r] + k - 1, step, 0), each mapped to
+ *     (w >> 11) * 2^-53.  positions[r] is the absolute position of x_1.
+ *
+ *   p_logits, q_logits [B][N-1][V]  logit_dtype
+ *   proposals  [B][N] int32          x_1..x_N
+ *   req_ids    [B] int32 (>= 0)      stable request ids (Philox counter word 0)
+ *   positions  [B] int32 (>= 0)
+ *   accept_len [B] int32             written: A
+ *   out_tokens [B][N] int32          written: x_1..x_A, then y* if A < N, then -1
+ *   n_out      [B] int32             written: A + (A < N)
+ *   n_commit   [B] int32             written: min(A, N-1), the CLEAN rows to commit
+ *   logp_sel, logq_sel [B][N-1] fp32 written: log p(x_k), log q(x_k) for every row
+ *
+ * The log-normalisers behind logp_sel / logq_sel and rho are fp32; the
+ * residual is fp64.  Flags: TOKEN_RANGE (an out-of-range proposal is
+ * rejected).
+ */
+isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* q_logits,
+                      const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
+                      uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
+                      int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
+                      float* logq_sel, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * kv_commit -- append the accepted CLEAN rows of every stride to the KV pages.
+ *
+ * Definition (paged KV cache reused from the AR serving stack:
+ * "I-DLM：扩散模型如何用'自省一致性'追上自回归模型质量", section "推理：复用 AR
+ * 推理栈"): a CLEAN row's key/value is valid iff its token was accepted, so
+ * rows 0..n_commit[r]-1 of k_new[r] / v_new[r] are written to positions
+ * ctx_lens_in[r] + i, and ctx_lens_out[r] = ctx_lens_in[r] + n_commit[r].
+ *
+ *   k_new, v_new  [B][Q][Hkv][D] kv_dtype
+ *   k_pages, v_pages  pool layout above, written in the committed slots only
+ *   page_table    [B][max_pages] int32; the caller maps pages for every slot
+ *                 it may commit (positions up to ctx_len + N - 2)
+ *   ctx_lens_in   [B] int32
+ *   n_commit      [B] int32 in [0, N-1] (isd_accept's output)
+ *   ctx_lens_out  [B] int32, written; may alias ctx_lens_in
+ *
+ * Flags: CTX_RANGE, COMMIT_RANGE, PAGE_RANGE (the row is skipped and the
+ * length still advances by the valid prefix only).
+ */
+isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_new,
+                     void* k_pages, void* v_pages, const int32_t* page_table,
+                     const int32_t* ctx_lens_in, const int32_t* n_commit,
+                     int32_t* ctx_lens_out, void* workspace, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * isd_lora_delta -- the gated rank-r delta of Residual ISD (R-ISD).
+ *
+ * Definition ("自省扩散语言模型的 token 生成机制与工程实践", section "Token 生成
+ * 的核心参数与验收机制"; I-DLM project page, R-ISD card): an adapter is active
+ * at MASK rows only; CLEAN (verifying) rows keep the base weights:
+ *
+ *   Y[m][:] += scale * (X[m][:] @ A) @ Bm   for m in mask_rows[0..n_mask-1]
+ *
+ *   X  [rows][d_in]   bf16
+ *   A  [d_in][rank]   bf16
+ *   Bm [rank][d_out]  bf16
+ *   Y  [rows][d_out]  bf16, updated in place at the gated rows only
+ *   mask_rows [n_mask] int32, distinct, in [0, rows)
+ *
+ * bf16 operands on the matrix cores with fp32 accumulation; the rank-r
+ * intermediate stays fp32 until it is split into two bf16 terms for the
+ * second product.  Supported: rank == 128, d_in % 256 == 0, d_out % 256 == 0.
+ * Workspace: isd_lora_workspace_bytes().  Flags: ROW_RANGE.
+ */
+size_t isd_lora_workspace_bytes(int32_t n_mask, int32_t d_in, int32_t rank);
+isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank,
+                          const void* X, const void* A, const void* Bm,
+                          const int32_t* mask_rows, int32_t n_mask, float scale, void* Y,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Text for a status code (static storage). */
+const char* isd_status_string(isd_status status);
+
+/* Text of the last ISD_ERR_HIP on the calling thread ("" if none). */
+const char* isd_last_error(void);
+
+/* ABI version: bumped on any change of a signature or a layout above. */
+int32_t isd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISD_H */

@@ -1,0 +1,218 @@
+"""ctypes binding of libisd.so (argument marshalling only).
+
+Every function here converts torch tensors to device pointers, checks dtype,
+device and contiguity, and calls the C entry point of the same name; all
+computation runs in the library's HIP kernels.  A non-OK status raises
+IsdError.  Importing this module fails loudly if libisd.so is missing: there
+is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libisd.so")
+
+ISD_F32, ISD_BF16 = 0, 1
+FLAG_CTX_RANGE, FLAG_PAGE_RANGE, FLAG_TOKEN_RANGE, FLAG_COMMIT_RANGE, FLAG_ROW_RANGE = 1, 2, 4, 8, 16
+STATUS = {0: "ISD_OK", 1: "ISD_ERR_NULL", 2: "ISD_ERR_SHAPE", 3: "ISD_ERR_DTYPE",
+          4: "ISD_ERR_WORKSPACE", 5: "ISD_ERR_UNSUPPORTED", 6: "ISD_ERR_HIP", 7: "ISD_ERR_ALIGNMENT"}
+
+# Every symbol include/isd.h declares.
+EXPORTS = ("isd_workspace_bytes", "isd_workspace_init", "isd_read_flags", "isd_attention",
+           "isd_accept", "kv_commit", "isd_lora_workspace_bytes", "isd_lora_delta",
+           "isd_status_string", "isd_last_error", "isd_abi_version")
+
+
+class IsdError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str = ""):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}"
+                         + (f": {detail}" if detail else ""))
+
+
+class CShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "stride_n", "n_q_heads", "n_kv_heads",
+                                              "head_dim", "page_size", "max_pages", "num_pages",
+                                              "vocab", "max_ctx", "kv_dtype", "logit_dtype")]
+
+
+@dataclass(frozen=True)
+class Shape:
+    batch: int
+    stride_n: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    max_pages: int
+    num_pages: int
+    vocab: int
+    kv_dtype: int = ISD_BF16
+    logit_dtype: int = ISD_BF16
+    page_size: int = 16
+    max_ctx: int = 0
+
+    @property
+    def q_rows(self) -> int:
+        return 2 * self.stride_n - 1
+
+    def c(self) -> CShape:
+        return CShape(self.batch, self.stride_n, self.n_q_heads, self.n_kv_heads, self.head_dim,
+                      self.page_size, self.max_pages, self.num_pages, self.vocab, self.max_ctx,
+                      self.kv_dtype, self.logit_dtype)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m introspective_strided_decoding_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, U32, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t
+    SP = ctypes.POINTER(CShape)
+    sig = {
+        "isd_workspace_bytes": (SZ, [SP]),
+        "isd_workspace_init": (I32, [P, SZ, P]),
+        "isd_read_flags": (I32, [P, ctypes.POINTER(U32), P]),
+        "isd_attention": (I32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
+        "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, SZ, P]),
+        "kv_commit": (I32, [SP, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
+        "isd_lora_delta": (I32, [I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
+        "isd_status_string": (ctypes.c_char_p, [I32]),
+        "isd_last_error": (ctypes.c_char_p, []),
+        "isd_abi_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t: torch.Tensor, name: str, dtype=None, numel: Optional[int] = None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _tdtype(code: int):
+    return torch.bfloat16 if code == ISD_BF16 else torch.float32
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        detail = LIB.isd_last_error().decode() if status == 6 else LIB.isd_status_string(status).decode()
+        raise IsdError(fn, status, detail)
+
+
+def isd_workspace_bytes(shape: Shape) -> int:
+    n = LIB.isd_workspace_bytes(ctypes.byref(shape.c()))
+    if n == 0:
+        raise IsdError("isd_workspace_bytes", 2, "shape rejected")
+    return int(n)
+
+
+def new_workspace(shape: Shape, device="cuda", stream=None) -> torch.Tensor:
+    """Allocate (torch) and initialise a workspace for ``shape``."""
+    ws = torch.empty(isd_workspace_bytes(shape), dtype=torch.uint8, device=device)
+    isd_workspace_init(ws, stream)
+    return ws
+
+
+def isd_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    _check("isd_workspace_init", LIB.isd_workspace_init(_ptr(workspace, "workspace", torch.uint8),
+                                                        workspace.numel(), _stream(stream)))
+
+
+def isd_read_flags(workspace: torch.Tensor, stream=None) -> int:
+    out = ctypes.c_uint32(0)
+    _check("isd_read_flags", LIB.isd_read_flags(_ptr(workspace, "workspace", torch.uint8),
+                                                ctypes.byref(out), _stream(stream)))
+    return int(out.value)
+
+
+def isd_attention(shape: Shape, q, k_new, v_new, k_pages, v_pages, page_table, ctx_lens, out,
+                  workspace, scale: float = 0.0, stream=None) -> None:
+    B, Q, Hq, Hkv, D = shape.batch, shape.q_rows, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    dt = _tdtype(shape.kv_dtype)
+    pool = shape.num_pages * Hkv * shape.page_size * D
+    _check("isd_attention", LIB.isd_attention(
+        ctypes.byref(shape.c()), _ptr(q, "q", dt, B * Q * Hq * D), _ptr(k_new, "k_new", dt, B * Q * Hkv * D),
+        _ptr(v_new, "v_new", dt, B * Q * Hkv * D), _ptr(k_pages, "k_pages", dt, pool),
+        _ptr(v_pages, "v_pages", dt, pool),
+        _ptr(page_table, "page_table", torch.int32, B * shape.max_pages),
+        _ptr(ctx_lens, "ctx_lens", torch.int32, B), float(scale), _ptr(out, "out", dt, B * Q * Hq * D),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def isd_accept(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
+               accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, workspace,
+               stream=None) -> None:
+    B, N, V = shape.batch, shape.stride_n, shape.vocab
+    dt = _tdtype(shape.logit_dtype)
+    i32 = torch.int32
+    _check("isd_accept", LIB.isd_accept(
+        ctypes.byref(shape.c()), _ptr(p_logits, "p_logits", dt, B * (N - 1) * V),
+        _ptr(q_logits, "q_logits", dt, B * (N - 1) * V), _ptr(proposals, "proposals", i32, B * N),
+        _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
+        int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF,
+        _ptr(accept_len, "accept_len", i32, B), _ptr(out_tokens, "out_tokens", i32, B * N),
+        _ptr(n_out, "n_out", i32, B), _ptr(n_commit, "n_commit", i32, B),
+        _ptr(logp_sel, "logp_sel", torch.float32, B * (N - 1)),
+        _ptr(logq_sel, "logq_sel", torch.float32, B * (N - 1)),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def kv_commit(shape: Shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
+              ctx_lens_out, workspace, stream=None) -> None:
+    B, Q, Hkv, D = shape.batch, shape.q_rows, shape.n_kv_heads, shape.head_dim
+    dt = _tdtype(shape.kv_dtype)
+    pool = shape.num_pages * Hkv * shape.page_size * D
+    _check("kv_commit", LIB.kv_commit(
+        ctypes.byref(shape.c()), _ptr(k_new, "k_new", dt, B * Q * Hkv * D),
+        _ptr(v_new, "v_new", dt, B * Q * Hkv * D), _ptr(k_pages, "k_pages", dt, pool),
+        _ptr(v_pages, "v_pages", dt, pool),
+        _ptr(page_table, "page_table", torch.int32, B * shape.max_pages),
+        _ptr(ctx_lens_in, "ctx_lens_in", torch.int32, B), _ptr(n_commit, "n_commit", torch.int32, B),
+        _ptr(ctx_lens_out, "ctx_lens_out", torch.int32, B),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def isd_lora_workspace_bytes(n_mask: int, d_in: int, rank: int) -> int:
+    return int(LIB.isd_lora_workspace_bytes(n_mask, d_in, rank))
+
+
+def isd_lora_delta(X, A, Bm, mask_rows, Y, workspace, scale: float = 1.0, stream=None) -> None:
+    rows, d_in = X.shape
+    rank, d_out = Bm.shape
+    bf = torch.bfloat16
+    _check("isd_lora_delta", LIB.isd_lora_delta(
+        rows, d_in, d_out, rank, _ptr(X, "X", bf), _ptr(A, "A", bf, d_in * rank),
+        _ptr(Bm, "Bm", bf), _ptr(mask_rows, "mask_rows", torch.int32), mask_rows.numel(),
+        float(scale), _ptr(Y, "Y", bf, rows * d_out), _ptr(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(stream)))

@@ -1,0 +1,237 @@
+// C ABI of libisd.so: argument validation, planning, workspace layout and
+// dispatch to the HIP kernels.  Everything here runs on the host and returns
+// before any launch when an argument is invalid.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "isd.h"
+#include "isd_internal.hpp"
+
+namespace isd {
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+isd_status hip_fail(hipError_t e, const char* where) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+  return ISD_ERR_HIP;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ceil_div(long long a, long long b) { return int((a + b - 1) / b); }
+
+isd_status check_dtype(isd_dtype d) {
+  return (d == ISD_F32 || d == ISD_BF16) ? ISD_OK : ISD_ERR_DTYPE;
+}
+
+// Checks shared by every step entry point.
+isd_status check_shape(const isd_shape* s) {
+  if (!s) return ISD_ERR_NULL;
+  if (check_dtype(s->kv_dtype) != ISD_OK || check_dtype(s->logit_dtype) != ISD_OK) return ISD_ERR_DTYPE;
+  if (s->batch < 1 || s->stride_n < 2 || s->n_q_heads < 1 || s->n_kv_heads < 1 ||
+      s->max_pages < 1 || s->num_pages < 1 || s->vocab < 1 || s->max_ctx < 0)
+    return ISD_ERR_SHAPE;
+  if (s->n_q_heads % s->n_kv_heads) return ISD_ERR_SHAPE;
+  if (s->page_size != kPage) return ISD_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return ISD_ERR_UNSUPPORTED;
+  if (s->stride_n > 32) return ISD_ERR_UNSUPPORTED;
+  const long long rows = (long long)(s->n_q_heads / s->n_kv_heads) * (2 * s->stride_n - 1);
+  if (rows > 64) return ISD_ERR_UNSUPPORTED;
+  if ((long long)s->max_pages * kPage > (1LL << 30)) return ISD_ERR_SHAPE;
+  return ISD_OK;
+}
+
+isd_status check_ws(const isd_shape* s, const void* ws, size_t bytes) {
+  if (!ws) return ISD_ERR_NULL;
+  if (!aligned16(ws)) return ISD_ERR_ALIGNMENT;
+  if (bytes < ws_layout(*s).total) return ISD_ERR_WORKSPACE;
+  return ISD_OK;
+}
+
+}  // namespace
+
+AttnPlan plan_attention(const isd_shape& s) {
+  AttnPlan p{};
+  p.q_rows = 2 * s.stride_n - 1;
+  p.group = s.n_q_heads / s.n_kv_heads;
+  p.rows = p.group * p.q_rows;
+  p.rows_pad = ceil_div(p.rows, 32) * 32;
+  p.row_blocks = p.rows_pad / 32;
+  const long long cap = (long long)s.max_pages * kPage;
+  const long long hint = (s.max_ctx > 0) ? std::min<long long>(s.max_ctx, cap) : cap;
+  p.tiles_max = std::max(1, ceil_div(hint, kTileTokens));
+  // Aim for about 1024 workgroups (4096 waves: 16 per CU on 256 CUs) without
+  // giving a workgroup fewer than 8 tiles (two per wave) of work.
+  const long long pairs = (long long)s.batch * s.n_kv_heads;
+  int splits = std::max(1, ceil_div(1024, pairs));
+  p.tiles_per_split = std::max(8, ceil_div(p.tiles_max, splits));
+  p.n_splits = std::max(1, ceil_div(p.tiles_max, p.tiles_per_split));
+  return p;
+}
+
+AcceptPlan plan_accept(const isd_shape& s) {
+  AcceptPlan p{};
+  p.rows = 2 * s.batch * (s.stride_n - 1);
+  const int V = s.vocab;
+  // about 2048 workgroups in the normaliser pass, at least 2048 elements each
+  int shards = std::max(1, ceil_div(2048, p.rows));
+  shards = std::min(shards, std::max(1, V / 2048));
+  p.shard_len = ceil_div(ceil_div(V, shards), 8) * 8;
+  p.shards = ceil_div(V, p.shard_len);
+  // the fp64 residual works on 2048-element shards
+  p.r_shard_len = std::min(2048, ceil_div(V, 8) * 8);
+  p.r_shards = ceil_div(V, p.r_shard_len);
+  return p;
+}
+
+WsLayout ws_layout(const isd_shape& s) {
+  WsLayout L;
+  const AttnPlan a = plan_attention(s);
+  const AcceptPlan c = plan_accept(s);
+  size_t off = kHeaderBytes;
+  const size_t partial_rows = (size_t)s.batch * s.n_kv_heads * a.n_splits * a.rows_pad;
+  L.attn_ml = off;
+  off = align_up(off + partial_rows * 8, 256);
+  L.attn_o = off;
+  off = align_up(off + partial_rows * s.head_dim * 4, 256);
+  L.lse = off;
+  off = align_up(off + (size_t)c.rows * c.shards * 8, 256);
+  L.req = off;
+  off = align_up(off + (size_t)s.batch * sizeof(ReqState), 256);
+  L.lse64 = off;
+  off = align_up(off + (size_t)s.batch * c.r_shards * 32, 256);
+  L.mass = off;
+  off = align_up(off + (size_t)s.batch * c.r_shards * 16, 256);
+  L.total = off;
+  return L;
+}
+
+}  // namespace isd
+
+using namespace isd;
+
+extern "C" {
+
+int32_t isd_abi_version(void) { return 1; }
+
+const char* isd_status_string(isd_status status) {
+  switch (status) {
+    case ISD_OK: return "ok";
+    case ISD_ERR_NULL: return "a required pointer is NULL";
+    case ISD_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case ISD_ERR_DTYPE: return "unknown dtype";
+    case ISD_ERR_WORKSPACE: return "workspace smaller than isd_workspace_bytes()";
+    case ISD_ERR_UNSUPPORTED: return "valid request not implemented by this build";
+    case ISD_ERR_HIP: return "HIP launch or runtime error (see isd_last_error)";
+    case ISD_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+const char* isd_last_error(void) { return g_last_error; }
+
+size_t isd_workspace_bytes(const isd_shape* shape) {
+  if (check_shape(shape) != ISD_OK) return 0;
+  return ws_layout(*shape).total;
+}
+
+isd_status isd_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!workspace) return ISD_ERR_NULL;
+  if (!aligned16(workspace)) return ISD_ERR_ALIGNMENT;
+  if (ws_bytes < kHeaderBytes) return ISD_ERR_WORKSPACE;
+  hipError_t e = launch_workspace_init(workspace, kHeaderBytes, stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_workspace_init");
+}
+
+isd_status isd_read_flags(const void* workspace, uint32_t* flags, hipStream_t stream) {
+  if (!workspace || !flags) return ISD_ERR_NULL;
+  hipError_t e = hipMemcpyAsync(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_read_flags");
+}
+
+isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_new, const void* v_new,
+                         const void* k_pages, const void* v_pages, const int32_t* page_table,
+                         const int32_t* ctx_lens, float scale, void* out, void* workspace,
+                         size_t ws_bytes, hipStream_t stream) {
+  isd_status st = check_shape(shape);
+  if (st != ISD_OK) return st;
+  if (!q || !k_new || !v_new || !k_pages || !v_pages || !page_table || !ctx_lens || !out)
+    return ISD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(k_new) ||
+      !aligned16(v_new) || !aligned16(out))
+    return ISD_ERR_ALIGNMENT;
+  if (!(scale >= 0.f) || scale > 1e30f) return ISD_ERR_SHAPE;
+  st = check_ws(shape, workspace, ws_bytes);
+  if (st != ISD_OK) return st;
+  if (scale == 0.f) scale = 1.0f / std::sqrt(float(shape->head_dim));
+  const AttnPlan p = plan_attention(*shape);
+  const WsLayout L = ws_layout(*shape);
+  hipError_t e = launch_attention(*shape, p, q, k_new, v_new, k_pages, v_pages, page_table, ctx_lens,
+                                  scale, out, static_cast<char*>(workspace), L, stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_attention");
+}
+
+isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* q_logits,
+                      const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
+                      uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
+                      int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
+                      float* logq_sel, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  isd_status st = check_shape(shape);
+  if (st != ISD_OK) return st;
+  if (!p_logits || !q_logits || !proposals || !req_ids || !positions || !accept_len || !out_tokens ||
+      !n_out || !n_commit || !logp_sel || !logq_sel)
+    return ISD_ERR_NULL;
+  if (!aligned16(p_logits) || !aligned16(q_logits)) return ISD_ERR_ALIGNMENT;
+  if (shape->batch > 65535) return ISD_ERR_UNSUPPORTED;
+  st = check_ws(shape, workspace, ws_bytes);
+  if (st != ISD_OK) return st;
+  const AcceptPlan p = plan_accept(*shape);
+  if (p.rows > 65535) return ISD_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(*shape);
+  hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
+                               seed_hi, step, accept_len, out_tokens, n_out, n_commit, logp_sel,
+                               logq_sel, static_cast<char*>(workspace), L, stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept");
+}
+
+isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_new, void* k_pages,
+                     void* v_pages, const int32_t* page_table, const int32_t* ctx_lens_in,
+                     const int32_t* n_commit, int32_t* ctx_lens_out, void* workspace,
+                     size_t ws_bytes, hipStream_t stream) {
+  isd_status st = check_shape(shape);
+  if (st != ISD_OK) return st;
+  if (!k_new || !v_new || !k_pages || !v_pages || !page_table || !ctx_lens_in || !n_commit ||
+      !ctx_lens_out)
+    return ISD_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(k_pages)) return ISD_ERR_ALIGNMENT;
+  st = check_ws(shape, workspace, ws_bytes);
+  if (st != ISD_OK) return st;
+  uint32_t* flags = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + ws_layout(*shape).flags);
+  hipError_t e = launch_commit(*shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in,
+                               n_commit, ctx_lens_out, flags, stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "kv_commit");
+}
+
+size_t isd_lora_workspace_bytes(int32_t n_mask, int32_t d_in, int32_t rank) {
+  if (n_mask < 0 || d_in < 1 || rank < 1) return 0;
+  (void)d_in;
+  return kHeaderBytes;
+}
+
+isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
+                          const void* A, const void* Bm, const int32_t* mask_rows, int32_t n_mask,
+                          float scale, void* Y, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  (void)rows; (void)d_in; (void)d_out; (void)rank; (void)X; (void)A; (void)Bm; (void)mask_rows;
+  (void)n_mask; (void)scale; (void)Y; (void)workspace; (void)ws_bytes; (void)stream;
+  return ISD_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

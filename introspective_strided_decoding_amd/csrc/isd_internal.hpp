@@ -1,0 +1,87 @@
+// Host-side planning, workspace layout and kernel launchers of libisd.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "isd.h"
+
+namespace isd {
+
+constexpr int kPage = 16;          // tokens per KV page
+constexpr int kTileTokens = 32;    // tokens per attention tile (two pages)
+constexpr int kAttnWaves = 4;      // waves per attention workgroup
+constexpr size_t kHeaderBytes = 256;
+
+// How the KV walk of isd_attention is split across workgroups.
+struct AttnPlan {
+  int q_rows;           // Q = 2N-1
+  int group;            // G = Hq / Hkv
+  int rows;             // G * Q query rows per KV head
+  int rows_pad;         // rows rounded up to 32
+  int row_blocks;       // rows_pad / 32
+  int tiles_max;        // tiles of the longest context the plan is sized for
+  int tiles_per_split;  // tiles per workgroup (last split takes the remainder)
+  int n_splits;         // workgroups per (request, KV head)
+};
+
+// How isd_accept shards the vocabulary.
+struct AcceptPlan {
+  int rows;             // 2 * B * (N-1) logit rows (p rows first, then q rows)
+  int shards;           // shards per row for the fp32 normaliser
+  int shard_len;        // elements per shard (multiple of 8)
+  int r_shards;         // shards per row for the fp64 residual
+  int r_shard_len;
+};
+
+struct WsLayout {
+  size_t flags = 0;          // uint32 device flags
+  size_t attn_ml = 0;        // float2 (m, l) per partial row
+  size_t attn_o = 0;         // float [D] per partial row
+  size_t lse = 0;            // float2 (max, sum) per (row, shard)
+  size_t req = 0;            // per-request accept state (ReqState)
+  size_t lse64 = 0;          // double2 per (request, residual shard) for p and q
+  size_t mass = 0;           // double2 (residual mass, p mass) per (request, residual shard)
+  size_t total = 0;
+};
+
+// Per-request state handed from the accept decision to the residual kernels.
+struct ReqState {
+  int32_t accept_len;
+  int32_t reject_row;   // j of the rejected row, -1 if all accepted
+  int32_t pad0, pad1;
+  double u_resample;    // u' of the rejected position
+  double pad2;
+};
+
+AttnPlan plan_attention(const isd_shape& s);
+AcceptPlan plan_accept(const isd_shape& s);
+WsLayout ws_layout(const isd_shape& s);
+
+// Launchers (return the first HIP error, hipSuccess otherwise).
+hipError_t launch_attention(const isd_shape& s, const AttnPlan& p, const void* q,
+                            const void* k_new, const void* v_new, const void* k_pages,
+                            const void* v_pages, const int32_t* table, const int32_t* ctx_lens,
+                            float scale, void* out, char* ws, const WsLayout& L,
+                            hipStream_t stream);
+
+hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_logits,
+                         const void* q_logits, const int32_t* proposals, const int32_t* req_ids,
+                         const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
+                         uint32_t step, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
+                         int32_t* n_commit, float* logp_sel, float* logq_sel, char* ws,
+                         const WsLayout& L, hipStream_t stream);
+
+hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
+                         void* v_pages, const int32_t* table, const int32_t* ctx_in,
+                         const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags,
+                         hipStream_t stream);
+
+hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);
+
+hipError_t launch_lora(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
+                       const void* A, const void* Bm, const int32_t* mask_rows, int32_t n_mask,
+                       float scale, void* Y, char* ws, hipStream_t stream);
+
+}  // namespace isd

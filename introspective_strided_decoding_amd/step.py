@@ -1,0 +1,130 @@
+"""Device buffers for one ISD step and the three calls in stream order.
+
+``DeviceStep.from_arrays`` takes host arrays by name (numpy or torch: q,
+k_new, v_new, plain page pools, page_table, ctx_lens, p/q logits, proposals,
+req_ids, positions, step, philox_seed, and optionally the LoRA operands),
+moves them to the device in the library layouts, allocates the outputs and
+the workspace, and ``run()`` enqueues isd_attention -> isd_accept ->
+kv_commit (+ isd_lora_delta when LoRA operands are present).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from .layout import pack_k_pages, pack_v_pages
+
+
+def _t(x, dtype, device):
+    if isinstance(x, np.ndarray):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+    return x.to(device=device, dtype=dtype).contiguous()
+
+
+@dataclass
+class DeviceStep:
+    shape: _lib.Shape
+    q: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    page_table: torch.Tensor
+    ctx_lens: torch.Tensor
+    p_logits: torch.Tensor
+    q_logits: torch.Tensor
+    proposals: torch.Tensor
+    req_ids: torch.Tensor
+    positions: torch.Tensor
+    step: int
+    seed: tuple
+    workspace: torch.Tensor
+    out: torch.Tensor
+    accept_len: torch.Tensor
+    out_tokens: torch.Tensor
+    n_out: torch.Tensor
+    n_commit: torch.Tensor
+    logp_sel: torch.Tensor
+    logq_sel: torch.Tensor
+    ctx_lens_out: torch.Tensor
+    lora: Optional[dict] = None
+    extra: dict = field(default_factory=dict)
+
+    @classmethod
+    def from_arrays(cls, a, device="cuda", max_ctx: int = 0, commit_in_place: bool = False):
+        dt_name = a.cfg.dtype if hasattr(a, "cfg") else a.dtype
+        kv = torch.bfloat16 if dt_name == "bf16" else torch.float32
+        code = _lib.ISD_BF16 if dt_name == "bf16" else _lib.ISD_F32
+        B, Q, Hq, D = a.q.shape
+        Hkv = a.k_new.shape[2]
+        N = (Q + 1) // 2
+        P = a.k_pool.shape[0]
+        V = a.p_logits.shape[-1]
+        shape = _lib.Shape(batch=B, stride_n=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                           max_pages=a.page_table.shape[1], num_pages=P, vocab=V, kv_dtype=code,
+                           logit_dtype=code, max_ctx=max_ctx)
+        i32 = torch.int32
+        k_plain = _t(a.k_pool, kv, device)
+        v_plain = _t(a.v_pool, kv, device)
+        ctx = _t(a.ctx_lens, i32, device)
+        st = cls(
+            shape=shape, q=_t(a.q, kv, device), k_new=_t(a.k_new, kv, device), v_new=_t(a.v_new, kv, device),
+            k_pages=pack_k_pages(k_plain), v_pages=pack_v_pages(v_plain),
+            page_table=_t(a.page_table, i32, device), ctx_lens=ctx,
+            p_logits=_t(a.p_logits, kv, device), q_logits=_t(a.q_logits, kv, device),
+            proposals=_t(a.proposals, i32, device), req_ids=_t(a.req_ids, i32, device),
+            positions=_t(a.positions, i32, device), step=int(a.step), seed=tuple(a.philox_seed),
+            workspace=_lib.new_workspace(shape, device),
+            out=torch.empty(B, Q, Hq, D, dtype=kv, device=device),
+            accept_len=torch.empty(B, dtype=i32, device=device),
+            out_tokens=torch.empty(B, N, dtype=i32, device=device),
+            n_out=torch.empty(B, dtype=i32, device=device),
+            n_commit=torch.empty(B, dtype=i32, device=device),
+            logp_sel=torch.empty(B, N - 1, dtype=torch.float32, device=device),
+            logq_sel=torch.empty(B, N - 1, dtype=torch.float32, device=device),
+            ctx_lens_out=ctx if commit_in_place else torch.empty(B, dtype=i32, device=device),
+        )
+        del k_plain, v_plain
+        if getattr(a, "lora_x", None) is not None:
+            bf = torch.bfloat16
+            st.lora = dict(X=_t(a.lora_x, bf, device), A=_t(a.lora_a, bf, device),
+                           B=_t(a.lora_b, bf, device), Y=_t(a.lora_y, bf, device),
+                           mask_rows=_t(a.mask_rows, i32, device))
+            n_mask = st.lora["mask_rows"].numel()
+            st.lora["ws"] = torch.zeros(
+                max(256, _lib.isd_lora_workspace_bytes(n_mask, st.lora["X"].shape[1], st.lora["A"].shape[1])),
+                dtype=torch.uint8, device=device)
+        return st
+
+    def attention(self, stream=None):
+        _lib.isd_attention(self.shape, self.q, self.k_new, self.v_new, self.k_pages, self.v_pages,
+                           self.page_table, self.ctx_lens, self.out, self.workspace, stream=stream)
+
+    def accept(self, stream=None, step: Optional[int] = None, seed=None):
+        _lib.isd_accept(self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
+                        self.positions, self.seed if seed is None else seed,
+                        self.step if step is None else step, self.accept_len, self.out_tokens,
+                        self.n_out, self.n_commit, self.logp_sel, self.logq_sel, self.workspace,
+                        stream=stream)
+
+    def commit(self, stream=None):
+        _lib.kv_commit(self.shape, self.k_new, self.v_new, self.k_pages, self.v_pages,
+                       self.page_table, self.ctx_lens, self.n_commit, self.ctx_lens_out,
+                       self.workspace, stream=stream)
+
+    def lora_delta(self, stream=None):
+        L = self.lora
+        _lib.isd_lora_delta(L["X"], L["A"], L["B"], L["mask_rows"], L["Y"], L["ws"], stream=stream)
+
+    def run(self, stream=None):
+        """One ISD step: attention -> accept -> commit (-> LoRA delta)."""
+        self.attention(stream)
+        self.accept(stream)
+        self.commit(stream)
+        if self.lora is not None:
+            self.lora_delta(stream)

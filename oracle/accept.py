@@ -101,18 +101,26 @@ class StrideResult:
     accept_margins: np.ndarray = field(default_factory=lambda: np.zeros(0))
 
 
-def verify_stride(p_rows, q_rows, proposals: Sequence[int], uniforms) -> StrideResult:
+def row_normalizers(rows) -> np.ndarray:
+    """Step 2 for every row of a [R, V] array."""
+    return np.array([log_normalizer(r) for r in np.asarray(rows, dtype=np.float64)])
+
+
+def verify_stride(p_rows, q_rows, proposals: Sequence[int], uniforms, lse_p=None,
+                  lse_q=None) -> StrideResult:
     """Steps 2-5 for one request.
 
     p_rows, q_rows: [N-1, V] logits; proposals: x_1..x_N; uniforms: list of
-    (u_accept, u_resample) for k = 2..N (entry k-2).
+    (u_accept, u_resample) for k = 2..N (entry k-2).  lse_p / lse_q may carry
+    this module's own ``row_normalizers`` of the rows when they were computed
+    before (a large vocabulary decided under many draws).
     """
     p_rows = np.asarray(p_rows, dtype=np.float64)
     q_rows = np.asarray(q_rows, dtype=np.float64)
     n = len(proposals)
     rows = n - 1
-    lse_p = np.array([log_normalizer(p_rows[j]) for j in range(rows)])
-    lse_q = np.array([log_normalizer(q_rows[j]) for j in range(rows)])
+    lse_p = row_normalizers(p_rows) if lse_p is None else np.asarray(lse_p, dtype=np.float64)
+    lse_q = row_normalizers(q_rows) if lse_q is None else np.asarray(lse_q, dtype=np.float64)
     x = [int(t) for t in proposals]
     logp = np.array([p_rows[j, x[j + 1]] - lse_p[j] for j in range(rows)])
     logq = np.array([q_rows[j, x[j + 1]] - lse_q[j] for j in range(rows)])
@@ -152,12 +160,17 @@ def stride_uniforms(seed, req_id: int, position: int, step: int, n: int):
 
 
 def isd_accept(p_logits, q_logits, proposals, req_ids, positions, seed, step,
-               requests: Optional[Sequence[int]] = None) -> List[StrideResult]:
-    """Run ``verify_stride`` for every request of a batch with Philox draws."""
+               requests: Optional[Sequence[int]] = None, lse_p=None, lse_q=None) -> List[StrideResult]:
+    """Run ``verify_stride`` for every request of a batch with Philox draws.
+
+    lse_p / lse_q: optional [B, N-1] row normalisers from ``row_normalizers``.
+    """
     B, n = proposals.shape
     reqs = range(B) if requests is None else requests
     out = []
     for r in reqs:
         u = stride_uniforms(seed, int(req_ids[r]), int(positions[r]), int(step), n)
-        out.append(verify_stride(p_logits[r], q_logits[r], proposals[r], u))
+        out.append(verify_stride(p_logits[r], q_logits[r], proposals[r], u,
+                                 None if lse_p is None else lse_p[r],
+                                 None if lse_q is None else lse_q[r]))
     return out

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: libisd.so loads, exports every symbol include/isd.h
+declares, and host-side validation returns the documented status codes before
+any launch (all calls below fail validation, so nothing reaches the device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "isd.h")
+
+lib_mod = pytest.importorskip("introspective_strided_decoding_amd._lib",
+                              reason="libisd.so not built")
+LIB = lib_mod.LIB
+Shape = lib_mod.Shape
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(isd_\w+|kv_commit)\s*\(", text))
+
+
+def test_header_and_library_agree():
+    names = _declared()
+    assert names == set(lib_mod.EXPORTS)
+    for n in names:
+        assert hasattr(LIB, n)
+
+
+def test_abi_version_and_status_strings():
+    assert LIB.isd_abi_version() == 1
+    for code in range(8):
+        assert LIB.isd_status_string(code)
+    assert LIB.isd_status_string(99) == b"unknown status"
+
+
+def _shape(**kw):
+    base = dict(batch=32, stride_n=4, n_q_heads=32, n_kv_heads=8, head_dim=128, max_pages=257,
+                num_pages=8224, vocab=151936)
+    base.update(kw)
+    return Shape(**base)
+
+
+def _ws(shape):
+    return LIB.isd_workspace_bytes(ctypes.byref(shape.c()))
+
+
+def test_workspace_bytes_rejects_bad_shapes():
+    assert _ws(_shape()) > 0
+    for bad in (dict(n_q_heads=30), dict(head_dim=96), dict(stride_n=1), dict(batch=0),
+                dict(page_size=8), dict(stride_n=33, n_q_heads=8, n_kv_heads=8), dict(stride_n=9),
+                dict(kv_dtype=7), dict(vocab=0), dict(max_ctx=-1)):
+        assert _ws(_shape(**bad)) == 0, bad
+
+
+def test_workspace_grows_with_splits():
+    assert _ws(_shape(max_ctx=8192)) >= _ws(_shape(max_ctx=512))
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _attention(shape, q=FAKE, ws=FAKE, ws_bytes=None, scale=0.0):
+    if ws_bytes is None:
+        ws_bytes = _ws(shape) if _ws(shape) else 1 << 30
+    return LIB.isd_attention(ctypes.byref(shape.c()), q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             scale, FAKE, ws, ws_bytes, None)
+
+
+def test_attention_validation():
+    s = _shape()
+    assert _attention(s, q=None) == 1
+    assert _attention(s, q=MISALIGNED) == 7
+    assert _attention(s, ws_bytes=16) == 4
+    assert _attention(s, ws=None) == 1
+    assert _attention(s, scale=-1.0) == 2
+    assert _attention(_shape(head_dim=80)) == 5
+    assert _attention(_shape(n_q_heads=33)) == 2
+    assert _attention(_shape(kv_dtype=3)) == 3
+    assert LIB.isd_attention(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE, 1, None) == 1
+
+
+def test_accept_and_commit_validation():
+    s = _shape()
+    n = _ws(s)
+    args = [FAKE] * 5 + [1, 2, 3] + [FAKE] * 6 + [FAKE, n, None]
+    bad = list(args)
+    bad[2] = None
+    assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 1
+    bad = list(args)
+    bad[0] = MISALIGNED
+    assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 7
+    bad = list(args)
+    bad[-2] = 8
+    assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 4
+    cargs = [FAKE] * 8 + [FAKE, n, None]
+    bad = list(cargs)
+    bad[6] = None
+    assert LIB.kv_commit(ctypes.byref(s.c()), *bad) == 1
+    bad = list(cargs)
+    bad[-2] = 0
+    assert LIB.kv_commit(ctypes.byref(s.c()), *bad) == 4
+
+
+def test_workspace_init_and_flags_validation():
+    assert LIB.isd_workspace_init(None, 1024, None) == 1
+    assert LIB.isd_workspace_init(MISALIGNED, 1024, None) == 7
+    assert LIB.isd_workspace_init(FAKE, 16, None) == 4
+    assert LIB.isd_read_flags(None, None, None) == 1
+
+
+def test_layout_round_trip_cpu():
+    from introspective_strided_decoding_amd.layout import (SIGMA, pack_k_pages, pack_v_pages,
+                                                           unpack_k_pages, unpack_v_pages)
+    assert sorted(SIGMA) == list(range(16)) and all(SIGMA[SIGMA[s]] == s for s in range(16))
+    k = torch.randn(5, 16, 3, 64)
+    v = torch.randn(5, 16, 3, 64)
+    kp, vp = pack_k_pages(k), pack_v_pages(v)
+    assert kp.shape == (5, 3, 8, 16, 8) and vp.shape == (5, 3, 64, 16)
+    assert torch.equal(unpack_k_pages(kp), k) and torch.equal(unpack_v_pages(vp), v)
+    # element addresses as the header states them
+    page, h, slot, d = 3, 2, 11, 45
+    assert kp[page, h, d // 8, slot, d % 8] == k[page, slot, h, d]
+    sig = (slot & 3) | ((slot & 4) << 1) | ((slot & 8) >> 1)
+    assert vp[page, h, d, sig] == v[page, slot, h, d]

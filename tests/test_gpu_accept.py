@@ -1,0 +1,97 @@
+"""isd_accept on the GPU vs the float64 oracle.
+
+Accept lengths, committed tokens, n_out and n_commit must be identical to the
+oracle's under the same Philox draws, except for requests with a near-tie
+decision, which are counted and must stay under 0.01 % of decisions.  The
+selected log-probabilities must match within the dtype tolerance.  Many
+draws per input set come from varying the Philox step counter (and key),
+so one large logit set is decided under thousands of independent uniforms.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from parity import (NEAR_TIE_BUDGET, AcceptTally, check_accept_step, device_step, fetch_accept,
+                    needs_gpu)
+from workloads import get_config, make_workload
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _run(wl, steps, seeds=None, requests=None):
+    st = device_step(wl)
+    tally = AcceptTally()
+    for k in range(steps):
+        step = wl.step + k
+        seed = wl.philox_seed if seeds is None else seeds[k % len(seeds)]
+        st.accept(step=step, seed=seed)
+        torch.cuda.synchronize()
+        check_accept_step(wl, fetch_accept(st), seed, step, tally, requests)
+    from introspective_strided_decoding_amd import isd_read_flags
+    assert isd_read_flags(st.workspace) == 0
+    assert tally.near_tie_rate() < NEAR_TIE_BUDGET, vars(tally)
+    return tally
+
+
+def test_accept_tiny_fp32_many_draws():
+    wl = make_workload(get_config("tiny_fp32"))
+    seeds = [wl.philox_seed, (1, 2), (0xFFFFFFFFFFFFFFFF, 0x8000000000000000)]
+    t = _run(wl, 3000, seeds)
+    assert t.resamples > 100
+    # one fixed proposal: P(accept) = min(1, rho(x_2)), so E[A] = 1 + min(1, rho)
+    from oracle.accept import verify_stride
+    rho = verify_stride(wl.p_logits[0], wl.q_logits[0], wl.proposals[0], [(0.0, 0.0)]).rho[0]
+    p = min(1.0, rho)
+    se = (p * (1 - p) / t.requests) ** 0.5
+    assert abs(t.accept_total / t.requests - (1 + p)) < 4 * se + 1e-9
+
+
+@pytest.mark.parametrize("over", [
+    dict(batch=4, ctx=16, vocab=1000, stride_n=4),          # V not a multiple of 8
+    dict(batch=3, ctx=16, vocab=8, stride_n=8),             # tiny vocabulary, N=8
+    dict(batch=2, ctx=16, vocab=4099, stride_n=5),          # odd V, several shards
+    dict(batch=3, ctx=16, vocab=151936, stride_n=2),        # full vocab, single decision
+])
+def test_accept_small_shapes_bf16(over):
+    wl = make_workload(get_config("b8_ctx2k", **over))
+    _run(wl, 40)
+
+
+def test_accept_fp32_large_vocab():
+    wl = make_workload(get_config("tiny_fp32", batch=4, vocab=50257, stride_n=4))
+    _run(wl, 30)
+
+
+def test_accept_identical_rows_always_accept():
+    wl = make_workload(get_config("b8_ctx2k", batch=4, ctx=16, vocab=2048))
+    wl.q_logits = wl.p_logits.copy()
+    st = device_step(wl)
+    st.accept()
+    torch.cuda.synchronize()
+    g = fetch_accept(st)
+    assert (g["accept_len"] == wl.cfg.stride_n).all()
+    assert (g["n_commit"] == wl.cfg.stride_n - 1).all()
+    assert np.array_equal(g["out_tokens"], wl.proposals)
+
+
+def test_accept_out_of_range_token_flags_and_rejects():
+    from introspective_strided_decoding_amd import isd_read_flags
+    wl = make_workload(get_config("b8_ctx2k", batch=2, ctx=16, vocab=512))
+    wl.proposals[1, 2] = 512
+    st = device_step(wl)
+    st.accept()
+    torch.cuda.synchronize()
+    assert isd_read_flags(st.workspace) & 4
+    g = fetch_accept(st)
+    assert g["accept_len"][1] <= 2
+
+
+@pytest.mark.parametrize("name,steps", [("b8_ctx2k", 100), ("c32_ctx4k", 150), ("c128_lora", 20),
+                                        ("c64_ragged", 20)])
+def test_accept_full_size(name, steps):
+    wl = make_workload(get_config(name))
+    t = _run(wl, steps)
+    print(f"{name}: {t.decisions} decisions, {t.near_ties} near-ties, {t.resamples} resamples, "
+          f"max log-prob err {t.logp_err:.2e}")
+    assert t.resamples > 0

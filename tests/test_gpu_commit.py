@@ -1,0 +1,84 @@
+"""kv_commit on the GPU vs the oracle, and the commit -> attention chain.
+
+The committed pools are unpacked from the library layout and compared bit for
+bit with the oracle's plain pools; lengths must match exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.commit import kv_commit as oracle_commit
+from parity import check_attention, device_step, needs_gpu
+from workloads import get_config, make_workload
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _unpacked(st):
+    from introspective_strided_decoding_amd.layout import unpack_k_pages, unpack_v_pages
+    return (unpack_k_pages(st.k_pages).float().cpu().numpy(),
+            unpack_v_pages(st.v_pages).float().cpu().numpy())
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny_fp32", dict(batch=3, ctx=13, stride_n=4)),
+    ("b8_ctx2k", dict(batch=4, ctx=14, vocab=64)),          # crosses a page boundary
+    ("b8_ctx2k", dict(batch=4, ctx=0, vocab=64)),
+    ("c64_ragged", dict(batch=6, ctx_range=(1, 100), vocab=64)),
+    ("b8_ctx2k", dict(batch=2, ctx=40, vocab=64, head_dim=64)),
+])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_commit_matches_oracle(name, over, in_place):
+    cfg = get_config(name, **over)
+    wl = make_workload(cfg, seed=21, with_logits=False)
+    rng = np.random.Generator(np.random.PCG64(5))
+    n_commit = rng.integers(0, cfg.stride_n, size=cfg.batch).astype(np.int32)
+    n_commit[0] = cfg.stride_n - 1
+    st = device_step(wl, commit_in_place=in_place)
+    st.n_commit.copy_(torch.from_numpy(n_commit))
+    st.commit()
+    torch.cuda.synchronize()
+    k_ref, v_ref, lens_ref = oracle_commit(wl.k_pool, wl.v_pool, wl.page_table, wl.ctx_lens,
+                                           wl.k_new, wl.v_new, n_commit, cfg.page_size)
+    k_got, v_got = _unpacked(st)
+    assert np.array_equal(k_got, k_ref)
+    assert np.array_equal(v_got, v_ref)
+    assert np.array_equal(st.ctx_lens_out.cpu().numpy(), lens_ref)
+    from introspective_strided_decoding_amd import isd_read_flags
+    assert isd_read_flags(st.workspace) == 0
+
+
+def test_commit_then_attention_sees_grown_context():
+    cfg = get_config("b8_ctx2k", batch=3, ctx=30, vocab=64)
+    wl = make_workload(cfg, seed=22, with_logits=False)
+    n_commit = np.array([3, 1, 2], dtype=np.int32)
+    st = device_step(wl, commit_in_place=True)
+    st.n_commit.copy_(torch.from_numpy(n_commit))
+    st.commit()
+    nxt = make_workload(cfg, seed=23, with_logits=False)
+    st.q.copy_(torch.from_numpy(nxt.q).to(st.q.dtype))
+    st.k_new.copy_(torch.from_numpy(nxt.k_new).to(st.k_new.dtype))
+    st.v_new.copy_(torch.from_numpy(nxt.v_new).to(st.v_new.dtype))
+    st.attention()
+    torch.cuda.synchronize()
+    k2, v2, lens2 = oracle_commit(wl.k_pool, wl.v_pool, wl.page_table, wl.ctx_lens, wl.k_new,
+                                  wl.v_new, n_commit, cfg.page_size)
+    nxt.k_pool, nxt.v_pool, nxt.ctx_lens, nxt.page_table = k2, v2, lens2, wl.page_table
+    check_attention(nxt, st.out)
+
+
+def test_commit_range_flags():
+    from introspective_strided_decoding_amd import isd_read_flags
+    cfg = get_config("b8_ctx2k", batch=3, ctx=40, vocab=64)
+    wl = make_workload(cfg, seed=24, with_logits=False)
+    wl.page_table[2, 2] = -1                       # page of positions 32..47 unmapped
+    wl.ctx_lens[2] = 30
+    st = device_step(wl)
+    st.n_commit.copy_(torch.tensor([7, 1, 3], dtype=torch.int32))
+    st.commit()
+    torch.cuda.synchronize()
+    flags = isd_read_flags(st.workspace)
+    assert flags & 8 and flags & 2
+    lens = st.ctx_lens_out.cpu().numpy()
+    assert lens[0] == 40 + 3 and lens[1] == 41 and lens[2] == 32

@@ -107,10 +107,13 @@ def _fit_tau(p: torch.Tensor, z: torch.Tensor, dtype: str, groups: torch.Tensor,
     hi = torch.full((g,), 2.0, dtype=torch.float64)
     counts = torch.bincount(groups, minlength=g).to(torch.float64)
 
+    p_prob = torch.softmax(p.to(torch.float64), dim=-1)
+
     def mean_acc(tau_g):
         tau_rows = tau_g[groups].to(torch.float32).unsqueeze(1)
         lq = _round(p + tau_rows * z, dtype)
-        acc = _acceptance_by_row(p, lq)
+        q_prob = torch.softmax(lq.to(torch.float64), dim=-1)
+        acc = torch.minimum(p_prob, q_prob).sum(dim=-1)
         return torch.zeros(g, dtype=torch.float64).index_add_(0, groups, acc) / counts
 
     # grow hi until the acceptance there is below target
