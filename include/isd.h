@@ -116,8 +116,14 @@ typedef struct isd_shape {
 /* Workspace bytes needed by isd_attention, isd_accept and kv_commit for `shape`. */
 size_t isd_workspace_bytes(const isd_shape* shape);
 
-/* Zero the workspace header (flag word and internal counters) on `stream`. */
-isd_status isd_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream);
+/*
+ * Prepare a workspace for `shape` on `stream`: zero the header (flag word and
+ * internal counters) and fill the 512 KB table of float64 exp() of every
+ * bf16 bit pattern that the residual sampler reads.  Call once per workspace
+ * before its first use; the calls below keep the header consistent after.
+ */
+isd_status isd_workspace_init(const isd_shape* shape, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
 
 /*
  * Read the device flag word of `workspace` into *flags.  This call copies

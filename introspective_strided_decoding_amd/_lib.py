@@ -68,16 +68,16 @@ class Shape:
                       self.kv_dtype, self.logit_dtype)
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m introspective_strided_decoding_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I32, U32, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t
     SP = ctypes.POINTER(CShape)
     sig = {
         "isd_workspace_bytes": (SZ, [SP]),
-        "isd_workspace_init": (I32, [P, SZ, P]),
+        "isd_workspace_init": (I32, [SP, P, SZ, P]),
         "isd_read_flags": (I32, [P, ctypes.POINTER(U32), P]),
         "isd_attention": (I32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, SZ, P]),
@@ -140,13 +140,14 @@ def isd_workspace_bytes(shape: Shape) -> int:
 def new_workspace(shape: Shape, device="cuda", stream=None) -> torch.Tensor:
     """Allocate (torch) and initialise a workspace for ``shape``."""
     ws = torch.empty(isd_workspace_bytes(shape), dtype=torch.uint8, device=device)
-    isd_workspace_init(ws, stream)
+    isd_workspace_init(shape, ws, stream)
     return ws
 
 
-def isd_workspace_init(workspace: torch.Tensor, stream=None) -> None:
-    _check("isd_workspace_init", LIB.isd_workspace_init(_ptr(workspace, "workspace", torch.uint8),
-                                                        workspace.numel(), _stream(stream)))
+def isd_workspace_init(shape: Shape, workspace: torch.Tensor, stream=None) -> None:
+    _check("isd_workspace_init", LIB.isd_workspace_init(
+        ctypes.byref(shape.c()), _ptr(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)))
 
 
 def isd_read_flags(workspace: torch.Tensor, stream=None) -> int:

@@ -48,63 +48,174 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2)
   else s += s2 * __expf(m2 - m);
 }
 
+__device__ __forceinline__ float row_lse(const float2* part, int shards, float& row_max) {
+  float M = -INFINITY, S = 0.f;
+  for (int i = 0; i < shards; ++i) ms_merge(M, S, part[i].x, part[i].y);
+  row_max = M;
+  return M + __logf(S);
+}
+
+// Everything the accept decision reads and writes.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void lse_partial(const T* __restrict__ p_logits,
-                                                        const T* __restrict__ q_logits, int rows_half,
-                                                        int V, int shard_len, int shards,
+struct DecideArgs {
+  const T* p_logits;
+  const T* q_logits;
+  const int32_t* proposals;
+  const int32_t* req_ids;
+  const int32_t* positions;
+  uint64_t seed_lo, seed_hi;
+  uint32_t step;
+  int B, N, V, shards;
+  const float2* part;
+  int32_t *accept_len, *out_tokens, *n_out, *n_commit;
+  float *logp_sel, *logq_sel;
+  ReqState* state;
+  uint32_t* flags;
+  uint32_t* rej_count;
+  int32_t* rej_list;
+  int bf16_logits;
+};
+
+// The accept decision of request r, taken by one wave (lane j < N-1 tests
+// x_{j+2}; a ballot finds the first rejection).
+template <typename T>
+__device__ __forceinline__ void decide_request(const DecideArgs<T>& a, int r) {
+  const T* __restrict__ p_logits = a.p_logits;
+  const T* __restrict__ q_logits = a.q_logits;
+  const int32_t* __restrict__ proposals = a.proposals;
+  const float2* __restrict__ part = a.part;
+  const int N = a.N, V = a.V, B = a.B, shards = a.shards;
+  uint32_t* flags = a.flags;
+  const int lane = threadIdx.x & 63;
+  const int R = N - 1;
+  const int bf16_logits = a.bf16_logits;
+  bool reject = false;
+  bool table_ok = false;
+  double u_res = 0.0;
+  if (lane < R) {
+    const int j = lane;
+    const int rp = r * R + j;                  // p row index
+    const int rq = B * R + r * R + j;          // q row index (after all p rows)
+    float max_p, max_q;
+    const float lse_p = row_lse(part + size_t(rp) * shards, shards, max_p);
+    const float lse_q = row_lse(part + size_t(rq) * shards, shards, max_q);
+    // exp(x) of every logit of both rows is finite and their sums cannot overflow
+    table_ok = bf16_logits && fabsf(max_p) < 600.f && fabsf(max_q) < 600.f;
+    const int x = proposals[size_t(r) * N + j + 1];
+    float lp, lq;
+    if (x < 0 || x >= V) {
+      raise_flag(flags, ISD_FLAG_TOKEN_RANGE);
+      lp = -INFINITY;
+      lq = 0.f;
+    } else {
+      lp = to_f32<T>(p_logits[size_t(rp) * V + x]) - lse_p;
+      lq = to_f32<T>(q_logits[size_t(r * R + j) * V + x]) - lse_q;
+    }
+    a.logp_sel[size_t(r) * R + j] = lp;
+    a.logq_sel[size_t(r) * R + j] = lq;
+    const float rho = __expf(lp - lq);
+    const uint64_t rid = uint64_t(uint32_t(a.req_ids[r]));
+    const uint64_t pos = uint64_t(uint32_t(a.positions[r])) + uint64_t(j + 1);
+    const Philox4x64Out w = philox4x64_10(rid, pos, uint64_t(a.step), 0, a.seed_lo, a.seed_hi);
+    const double u = unit_double(w.w[0]);
+    u_res = unit_double(w.w[1]);
+    reject = !(u < double(rho));
+  }
+  const uint64_t mask = __ballot(reject);
+  const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
+  const int A = (first < 0) ? N : first + 1;
+  const double u_first = __shfl(u_res, first < 0 ? 0 : first);
+  const int tab_first = __shfl(int(table_ok), first < 0 ? 0 : first);
+  if (lane < N) {
+    const int x = proposals[size_t(r) * N + lane];
+    a.out_tokens[size_t(r) * N + lane] = (lane < A) ? x : -1;
+  }
+  if (lane == 0) {
+    a.accept_len[r] = A;
+    a.n_out[r] = A + (A < N ? 1 : 0);
+    a.n_commit[r] = min(A, N - 1);
+    ReqState st;
+    st.accept_len = A;
+    st.reject_row = first;
+    st.table_ok = tab_first;
+    st.pad1 = 0;
+    st.u_resample = u_first;
+    st.pad2 = 0.0;
+    a.state[r] = st;
+    if (first >= 0) a.rej_list[atomicAdd(a.rej_count, 1u)] = r;
+  }
+}
+
+// A shard holds at most kThreads * kLseVec vectors, so every thread issues all
+// of its 16-byte loads before it waits on any of them.
+constexpr int kLseVec = 8;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int rows_half, int shard_len,
                                                         float2* __restrict__ part) {
   constexpr int VN = Vec<T>::N;
+  const T* __restrict__ p_logits = args.p_logits;
+  const T* __restrict__ q_logits = args.q_logits;
+  const int V = args.V, shards = args.shards;
   const int sh = blockIdx.x;
   const int row = blockIdx.y;
-  const T* base = (row < rows_half) ? p_logits + size_t(row) * V : q_logits + size_t(row - rows_half) * V;
+  const size_t row_off = size_t(row < rows_half ? row : row - rows_half) * V;
+  const T* base = (row < rows_half ? p_logits : q_logits) + row_off;
   const int e0 = sh * shard_len;
   const int e1 = min(V, e0 + shard_len);
   float m = -INFINITY, s = 0.f;
   if (e0 < e1) {
-    // head up to 16-byte alignment of the absolute element index, vector body, scalar tail
-    const size_t abs0 = size_t(row < rows_half ? row : row - rows_half) * V + e0;
-    const int head = int((VN - (abs0 % VN)) % VN);
+    // scalar head up to 16-byte alignment of the absolute element index, vector body, scalar tail
+    const int head = int((VN - ((row_off + e0) % VN)) % VN);
     const int hb = min(e1, e0 + head);
     const int nvec = (e1 - hb) / VN;
     const int tb = hb + nvec * VN;
-    for (int e = e0 + threadIdx.x; e < hb; e += kThreads) ms_merge(m, s, to_f32<T>(base[e]), 1.f);
-    for (int e = tb + threadIdx.x; e < e1; e += kThreads) ms_merge(m, s, to_f32<T>(base[e]), 1.f);
     const u32x4* vb = reinterpret_cast<const u32x4*>(base + hb);
-    int v = threadIdx.x;
-    // two vectors per step: one rescale per 2*VN elements
-    for (; v + kThreads < nvec; v += 2 * kThreads) {
-      const u32x4 a = vb[v], b = vb[v + kThreads];
-      float x[2 * VN];
-      unpack(a, x, T());
-      unpack(b, x + VN, T());
-      float mx = x[0];
+    u32x4 raw[kLseVec];
 #pragma unroll
-      for (int i = 1; i < 2 * VN; ++i) mx = fmaxf(mx, x[i]);
-      if (mx > m) { s *= exp2f((m - mx) * kLog2e); m = mx; }
-      const float mb = m * kLog2e;
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 2 * VN; ++i) acc += exp2f(fmaf(x[i], kLog2e, -mb));
-      s += acc;
+    for (int k = 0; k < kLseVec; ++k) {
+      const int v = threadIdx.x + k * kThreads;
+      raw[k] = (v < nvec) ? vb[v] : u32x4{0, 0, 0, 0};
     }
-    if (v < nvec) {
-      const u32x4 a = vb[v];
-      float x[VN];
-      unpack(a, x, T());
-      float mx = x[0];
+    float tail = -INFINITY;
+    bool has_tail = false;
+    for (int e = e0 + threadIdx.x; e < hb; e += kThreads) { tail = fmaxf(tail, to_f32<T>(base[e])); has_tail = true; }
+    for (int e = tb + threadIdx.x; e < e1; e += kThreads) { tail = fmaxf(tail, to_f32<T>(base[e])); has_tail = true; }
+    // pass 1: max over this thread's values (registers only)
+    float mx = tail;
 #pragma unroll
-      for (int i = 1; i < VN; ++i) mx = fmaxf(mx, x[i]);
-      if (mx > m) { s *= exp2f((m - mx) * kLog2e); m = mx; }
-      const float mb = m * kLog2e;
+    for (int k = 0; k < kLseVec; ++k) {
+      if (threadIdx.x + k * kThreads < nvec) {
+        float x[VN];
+        unpack(raw[k], x, T());
+#pragma unroll
+        for (int i = 0; i < VN; ++i) mx = fmaxf(mx, x[i]);
+      }
+    }
+    // pass 2: sum of exp(x - mx) in base 2
+    if (mx != -INFINITY) {
+      const float mb = mx * kLog2e;
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < VN; ++i) acc += exp2f(fmaf(x[i], kLog2e, -mb));
-      s += acc;
+      for (int k = 0; k < kLseVec; ++k) {
+        if (threadIdx.x + k * kThreads < nvec) {
+          float x[VN];
+          unpack(raw[k], x, T());
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc += exp2f(fmaf(x[i], kLog2e, -mb));
+        }
+      }
+      if (has_tail) {
+        for (int e = e0 + threadIdx.x; e < hb; e += kThreads) acc += exp2f(fmaf(to_f32<T>(base[e]), kLog2e, -mb));
+        for (int e = tb + threadIdx.x; e < e1; e += kThreads) acc += exp2f(fmaf(to_f32<T>(base[e]), kLog2e, -mb));
+      }
+      m = mx;
+      s = acc;
     }
   }
   // wave reduce of (m, s)
   const float wm = wave_max(m);
-  float ws = (m == -INFINITY) ? 0.f : s * __expf(m - wm);
+  float ws = (m == -INFINITY) ? 0.f : s * exp2f((m - wm) * kLog2e);
   ws = wave_sum(ws);
   __shared__ float sm[kThreads / 64][2];
   const int wave = threadIdx.x >> 6;
@@ -117,270 +228,338 @@ __global__ __launch_bounds__(kThreads) void lse_partial(const T* __restrict__ p_
   }
 }
 
-__device__ __forceinline__ float row_lse(const float2* part, int shards) {
-  float M = -INFINITY, S = 0.f;
-  for (int i = 0; i < shards; ++i) ms_merge(M, S, part[i].x, part[i].y);
-  return M + __logf(S);
-}
-
+// One wave per request: the accept decision.
 template <typename T>
-__global__ __launch_bounds__(64) void accept_decide(
-    const T* __restrict__ p_logits, const T* __restrict__ q_logits, const int32_t* __restrict__ proposals,
-    const int32_t* __restrict__ req_ids, const int32_t* __restrict__ positions, uint64_t seed_lo,
-    uint64_t seed_hi, uint32_t step, int N, int V, int shards, const float2* __restrict__ part,
-    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tokens, int32_t* __restrict__ n_out,
-    int32_t* __restrict__ n_commit, float* __restrict__ logp_sel, float* __restrict__ logq_sel,
-    ReqState* __restrict__ state, uint32_t* __restrict__ flags) {
-  const int r = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int R = N - 1;
-  const int B = gridDim.x;
-  bool reject = false;
-  double u_res = 0.0;
-  if (lane < R) {
-    const int j = lane;
-    const int rp = r * R + j;                  // p row index
-    const int rq = B * R + r * R + j;          // q row index (after all p rows)
-    const float lse_p = row_lse(part + size_t(rp) * shards, shards);
-    const float lse_q = row_lse(part + size_t(rq) * shards, shards);
-    const int x = proposals[size_t(r) * N + j + 1];
-    float lp, lq;
-    if (x < 0 || x >= V) {
-      raise_flag(flags, ISD_FLAG_TOKEN_RANGE);
-      lp = -INFINITY;
-      lq = 0.f;
-    } else {
-      lp = to_f32<T>(p_logits[size_t(rp) * V + x]) - lse_p;
-      lq = to_f32<T>(q_logits[size_t(r * R + j) * V + x]) - lse_q;
-    }
-    logp_sel[size_t(r) * R + j] = lp;
-    logq_sel[size_t(r) * R + j] = lq;
-    const float rho = __expf(lp - lq);
-    const uint64_t rid = uint64_t(uint32_t(req_ids[r]));
-    const uint64_t pos = uint64_t(uint32_t(positions[r])) + uint64_t(j + 1);
-    const Philox4x64Out w = philox4x64_10(rid, pos, uint64_t(step), 0, seed_lo, seed_hi);
-    const double u = unit_double(w.w[0]);
-    u_res = unit_double(w.w[1]);
-    reject = !(u < double(rho));
-  }
-  const uint64_t mask = __ballot(reject);
-  const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
-  const int A = (first < 0) ? N : first + 1;
-  const double u_first = __shfl(u_res, first < 0 ? 0 : first);
-  if (lane < N) {
-    const int x = proposals[size_t(r) * N + lane];
-    out_tokens[size_t(r) * N + lane] = (lane < A) ? x : -1;
-  }
-  if (lane == 0) {
-    accept_len[r] = A;
-    n_out[r] = A + (A < N ? 1 : 0);
-    n_commit[r] = min(A, N - 1);
-    ReqState st;
-    st.accept_len = A;
-    st.reject_row = first;
-    st.pad0 = st.pad1 = 0;
-    st.u_resample = u_first;
-    st.pad2 = 0.0;
-    state[r] = st;
-  }
+__global__ __launch_bounds__(64) void accept_decide(DecideArgs<T> args) {
+  decide_request<T>(args, blockIdx.x);
 }
 
 // ---- fp64 residual ----
+// Only requests that rejected a proposal take part; the decision kernel
+// lists them compactly, and residual workgroup (shard, k) serves the k-th
+// listed request.  A residual shard is 2048 vocabulary entries: 256 threads x
+// 8 consecutive entries.
+//
+// exp in float64: for bf16 logits whose row maxima lie in (-600, 600), exp(x)
+// is read from a table holding exp() of every bf16 bit pattern, so
+// p(y) = T[x_y] / sum_y T[x_y] (no float64 exp per entry, and no overflow or
+// total underflow of the sums).  Otherwise exp(x - m) is evaluated directly.
+// Shard partials are (m, s) pairs with lse = m + log(s) (m = 0 on the table
+// path) and are combined by whole waves.
+constexpr int kRPer = 8;
+constexpr int kRShard = kThreads * kRPer;
+
 __device__ __forceinline__ void ms_merge_d(double& m, double& s, double m2, double s2) {
   if (m2 == -INFINITY) return;
   if (m == -INFINITY) { m = m2; s = s2; return; }
   if (m2 > m) { s = s * exp(m - m2) + s2; m = m2; }
+  else if (m2 == m) s += s2;
   else s += s2 * exp(m2 - m);
 }
 
-template <int NT>
-__device__ __forceinline__ void block_ms_reduce_d(double& m, double& s, double* sm) {
+__device__ __forceinline__ double block_sum_d(double x, double* sm) {
+  x = wave_sum_d(x);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sm[wave] = x;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kThreads / 64; ++w) t += sm[w];
+  return t;
+}
+
+// (max, sum) over the workgroup; every thread receives the result.
+__device__ __forceinline__ void block_ms_d(double& m, double& s, double* sm) {
   const double wm = wave_max_d(m);
-  double ws = (m == -INFINITY) ? 0.0 : s * exp(m - wm);
+  double ws = (m == -INFINITY) ? 0.0 : (m == wm ? s : s * exp(m - wm));
   ws = wave_sum_d(ws);
   const int wave = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) { sm[2 * wave] = wm; sm[2 * wave + 1] = ws; }
   __syncthreads();
   double M = -INFINITY, S = 0.0;
-  for (int w = 0; w < NT / 64; ++w) ms_merge_d(M, S, sm[2 * w], sm[2 * w + 1]);
+  for (int w = 0; w < kThreads / 64; ++w) ms_merge_d(M, S, sm[2 * w], sm[2 * w + 1]);
   m = M;
   s = S;
+}
+
+// Row log-normalisers of the rejected p and q rows from the shard partials;
+// called by every lane of a wave, all lanes receive the result.
+__device__ __forceinline__ void wave_lse64(const double2* __restrict__ lse64, int k, int r_shards,
+                                           double& lse_p, double& lse_q) {
+  const int lane = threadIdx.x & 63;
+  double mp = -INFINITY, sp = 0.0, mq = -INFINITY, sq = 0.0;
+  for (int i = lane; i < r_shards; i += 64) {
+    const double2 a = lse64[(size_t(k) * r_shards + i) * 2 + 0];
+    const double2 b = lse64[(size_t(k) * r_shards + i) * 2 + 1];
+    ms_merge_d(mp, sp, a.x, a.y);
+    ms_merge_d(mq, sq, b.x, b.y);
+  }
+  const double Mp = wave_max_d(mp), Mq = wave_max_d(mq);
+  const double Sp = wave_sum_d(mp == -INFINITY ? 0.0 : (mp == Mp ? sp : sp * exp(mp - Mp)));
+  const double Sq = wave_sum_d(mq == -INFINITY ? 0.0 : (mq == Mq ? sq : sq * exp(mq - Mq)));
+  lse_p = Mp + log(Sp);
+  lse_q = Mq + log(Sq);
+}
+
+// 8 consecutive logits starting at e0 (entries >= e1 read as -inf)
+template <typename T>
+__device__ __forceinline__ void load_run(const T* __restrict__ row, int e0, int e1, float* x) {
+#pragma unroll
+  for (int k = 0; k < kRPer; ++k) {
+    const int e = e0 + k;
+    x[k] = (e < e1) ? to_f32<T>(row[e]) : -INFINITY;
+  }
+}
+
+// exp(x) from the table (bf16 logits): the bf16 bit pattern is the top half of x
+__device__ __forceinline__ double exp_tab(const double* __restrict__ tab, float x) {
+  return (x == -INFINITY) ? 0.0 : tab[__float_as_uint(x) >> 16];
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void resid_lse64(const T* __restrict__ p_logits,
                                                          const T* __restrict__ q_logits, int N, int V,
-                                                         int r_shard_len, int r_shards,
-                                                         const ReqState* __restrict__ state,
+                                                         int r_shards, const ReqState* __restrict__ state,
+                                                         const uint32_t* __restrict__ rej_count,
+                                                         const int32_t* __restrict__ rej_list,
+                                                         const double* __restrict__ tab,
                                                          double2* __restrict__ lse64) {
   const int sh = blockIdx.x;
-  const int r = blockIdx.y;
-  const int j = state[r].reject_row;
-  if (j < 0) return;
-  const size_t row = size_t(r) * (N - 1) + j;
-  const T* pr = p_logits + row * V;
-  const T* qr = q_logits + row * V;
-  const int e0 = sh * r_shard_len, e1 = min(V, e0 + r_shard_len);
-  double mp = -INFINITY, sp = 0.0, mq = -INFINITY, sq = 0.0;
-  for (int e = e0 + threadIdx.x; e < e1; e += kThreads) {
-    ms_merge_d(mp, sp, double(to_f32<T>(pr[e])), 1.0);
-    ms_merge_d(mq, sq, double(to_f32<T>(qr[e])), 1.0);
+  const int k = blockIdx.y;
+  if (k >= int(*rej_count)) return;
+  const int r = rej_list[k];
+  const ReqState st = state[r];
+  const size_t row = size_t(r) * (N - 1) + st.reject_row;
+  const int e1 = min(V, (sh + 1) * kRShard);
+  const int e0 = sh * kRShard + threadIdx.x * kRPer;
+  float xp[kRPer], xq[kRPer];
+  load_run<T>(p_logits + row * V, e0, e1, xp);
+  load_run<T>(q_logits + row * V, e0, e1, xq);
+  double mp, sp = 0.0, mq, sq = 0.0;
+  if (st.table_ok) {
+    mp = mq = 0.0;
+#pragma unroll
+    for (int i = 0; i < kRPer; ++i) { sp += exp_tab(tab, xp[i]); sq += exp_tab(tab, xq[i]); }
+    __shared__ double sm1[kThreads / 64];
+    sp = block_sum_d(sp, sm1);
+    sq = block_sum_d(sq, sm1);
+  } else {
+    float fp = xp[0], fq = xq[0];
+#pragma unroll
+    for (int i = 1; i < kRPer; ++i) { fp = fmaxf(fp, xp[i]); fq = fmaxf(fq, xq[i]); }
+    mp = fp;
+    mq = fq;
+    if (fp != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < kRPer; ++i) { sp += exp(double(xp[i]) - mp); sq += exp(double(xq[i]) - mq); }
+    }
+    __shared__ double sm2[2 * kThreads / 64];
+    block_ms_d(mp, sp, sm2);
+    block_ms_d(mq, sq, sm2);
   }
-  __shared__ double sm[2 * kThreads / 64];
-  block_ms_reduce_d<kThreads>(mp, sp, sm);
-  block_ms_reduce_d<kThreads>(mq, sq, sm);
   if (threadIdx.x == 0) {
-    lse64[(size_t(r) * r_shards + sh) * 2 + 0] = make_double2(mp, sp);
-    lse64[(size_t(r) * r_shards + sh) * 2 + 1] = make_double2(mq, sq);
+    lse64[(size_t(k) * r_shards + sh) * 2 + 0] = make_double2(mp, sp);
+    lse64[(size_t(k) * r_shards + sh) * 2 + 1] = make_double2(mq, sq);
   }
 }
 
-__device__ __forceinline__ void combine_lse64(const double2* __restrict__ lse64, int r, int r_shards,
-                                              double& lse_p, double& lse_q) {
-  double mp = -INFINITY, sp = 0.0, mq = -INFINITY, sq = 0.0;
-  for (int i = 0; i < r_shards; ++i) {
-    const double2 a = lse64[(size_t(r) * r_shards + i) * 2 + 0];
-    const double2 b = lse64[(size_t(r) * r_shards + i) * 2 + 1];
-    ms_merge_d(mp, sp, a.x, a.y);
-    ms_merge_d(mq, sq, b.x, b.y);
+// r(y) = max(0, p(y) - q(y)) and p(y) for 8 consecutive entries
+__device__ __forceinline__ void resid_values(const float* xp, const float* xq, bool table_ok,
+                                             const double* __restrict__ tab, double lse_p,
+                                             double lse_q, double* rv, double* pv) {
+  if (table_ok) {
+    const double ip = exp(-lse_p), iq = exp(-lse_q);
+#pragma unroll
+    for (int i = 0; i < kRPer; ++i) {
+      const double p = exp_tab(tab, xp[i]) * ip;
+      rv[i] = fmax(0.0, p - exp_tab(tab, xq[i]) * iq);
+      pv[i] = p;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRPer; ++i) {
+      const double p = exp(double(xp[i]) - lse_p);
+      rv[i] = fmax(0.0, p - exp(double(xq[i]) - lse_q));
+      pv[i] = p;
+    }
   }
-  lse_p = mp + log(sp);
-  lse_q = mq + log(sq);
+}
+
+// wave-wide exclusive prefix of one double per lane
+__device__ __forceinline__ double wave_exclusive_d(double x, double& total) {
+  const int lane = threadIdx.x & 63;
+  double incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  total = __shfl(incl, 63);
+  return incl - x;
+}
+
+// Inverse-CDF draw for the k-th listed request, by a whole workgroup: a
+// wave-wide prefix over the shard masses picks the shard holding u' * S, a
+// scan inside that shard in vocabulary order picks y*.
+template <typename T>
+__device__ __forceinline__ void select_request(const T* __restrict__ p_logits,
+                                               const T* __restrict__ q_logits, int N, int V,
+                                               int r_shards, const ReqState* __restrict__ state,
+                                               const int32_t* __restrict__ rej_list,
+                                               const double* __restrict__ tab,
+                                               const double2* __restrict__ lse64,
+                                               const double2* __restrict__ mass,
+                                               int32_t* __restrict__ out_tokens, int k) {
+  const int r = rej_list[k];
+  const ReqState st = state[r];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ double before_sm, target_sm;
+  __shared__ int shard_sm, fb_sm, found_sm, last_sm;
+  __shared__ double wsum[kThreads / 64];
+  double lse_p, lse_q;
+  wave_lse64(lse64, k, r_shards, lse_p, lse_q);
+  if (wave == 0) {
+    // shard masses in vocabulary order: lane l owns shards [l*per, (l+1)*per)
+    const int per = (r_shards + 63) / 64;
+    const int s0 = min(r_shards, lane * per), s1 = min(r_shards, s0 + per);
+    double rsum = 0.0, psum = 0.0;
+    for (int i = s0; i < s1; ++i) {
+      const double2 m = mass[size_t(k) * r_shards + i];
+      rsum += m.x;
+      psum += m.y;
+    }
+    double rtot, ptot;
+    const double rbefore = wave_exclusive_d(rsum, rtot);
+    const double pbefore = wave_exclusive_d(psum, ptot);
+    const bool fb = !(rtot > 0.0);                 // p and q equal up to rounding: sample p
+    const double S = fb ? ptot : rtot;
+    const double target = st.u_resample * S;
+    double cum = fb ? pbefore : rbefore;
+    int pick = -1, last_nz = -1;
+    double pick_before = 0.0, last_before = 0.0;
+    for (int i = s0; i < s1; ++i) {
+      const double2 m = mass[size_t(k) * r_shards + i];
+      const double mi = fb ? m.y : m.x;
+      if (mi > 0.0) { last_nz = i; last_before = cum; }
+      if (pick < 0 && cum + mi > target) { pick = i; pick_before = cum; }
+      cum += mi;
+    }
+    // first lane (lowest shards) that holds the crossing
+    const uint64_t hits = __ballot(pick >= 0);
+    const uint64_t nz = __ballot(last_nz >= 0);
+    if (hits) {
+      const int src = __ffsll((unsigned long long)hits) - 1;
+      const int sh = __shfl(pick, src);
+      const double bf = __shfl(pick_before, src);
+      if (lane == 0) { shard_sm = sh; before_sm = bf; }
+    } else {
+      // rounding left the target at or past the total: take the last shard with mass
+      const int src = nz ? 63 - __clzll((long long)nz) : 0;
+      const int sh = __shfl(last_nz, src);
+      const double bf = __shfl(last_before, src);
+      if (lane == 0) { shard_sm = sh < 0 ? 0 : sh; before_sm = bf; }
+    }
+    if (lane == 0) { target_sm = target; fb_sm = fb; found_sm = INT_MAX; last_sm = -1; }
+  }
+  __syncthreads();
+  const int sh = shard_sm;
+  const double target = target_sm;
+  const size_t row = size_t(r) * (N - 1) + st.reject_row;
+  const int e1 = min(V, (sh + 1) * kRShard);
+  const int e0 = sh * kRShard + threadIdx.x * kRPer;
+  float xp[kRPer], xq[kRPer];
+  load_run<T>(p_logits + row * V, e0, e1, xp);
+  load_run<T>(q_logits + row * V, e0, e1, xq);
+  double rv[kRPer], pv[kRPer], c[kRPer];
+  resid_values(xp, xq, st.table_ok, tab, lse_p, lse_q, rv, pv);
+  double run = 0.0;
+  int last_here = -1;
+#pragma unroll
+  for (int i = 0; i < kRPer; ++i) {
+    const double v = fb_sm ? pv[i] : rv[i];
+    if (v > 0.0 && e0 + i < e1) last_here = e0 + i;
+    run += v;
+    c[i] = run;
+  }
+  // exclusive scan of thread totals (threads in vocabulary order)
+  double wtot;
+  const double wbefore = wave_exclusive_d(run, wtot);
+  if (lane == 0) wsum[wave] = wtot;
+  __syncthreads();
+  double before = before_sm + wbefore;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int hit = INT_MAX;
+#pragma unroll
+  for (int i = kRPer - 1; i >= 0; --i)
+    if (e0 + i < e1 && before + c[i] > target) hit = e0 + i;
+  if (hit != INT_MAX) atomicMin(&found_sm, hit);
+  if (last_here >= 0) atomicMax(&last_sm, last_here);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int y = found_sm;
+    if (y == INT_MAX) y = (last_sm >= 0) ? last_sm : e1 - 1;
+    out_tokens[size_t(r) * N + st.accept_len] = y;
+  }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void resid_mass64(const T* __restrict__ p_logits,
                                                           const T* __restrict__ q_logits, int N, int V,
-                                                          int r_shard_len, int r_shards,
-                                                          const ReqState* __restrict__ state,
+                                                          int r_shards, const ReqState* __restrict__ state,
+                                                          const uint32_t* __restrict__ rej_count,
+                                                          const int32_t* __restrict__ rej_list,
+                                                          const double* __restrict__ tab,
                                                           const double2* __restrict__ lse64,
                                                           double2* __restrict__ mass) {
   const int sh = blockIdx.x;
-  const int r = blockIdx.y;
-  const int j = state[r].reject_row;
-  if (j < 0) return;
-  __shared__ double lse_sm[2];
-  if (threadIdx.x == 0) combine_lse64(lse64, r, r_shards, lse_sm[0], lse_sm[1]);
-  __syncthreads();
-  const double lse_p = lse_sm[0], lse_q = lse_sm[1];
-  const size_t row = size_t(r) * (N - 1) + j;
-  const T* pr = p_logits + row * V;
-  const T* qr = q_logits + row * V;
-  const int e0 = sh * r_shard_len, e1 = min(V, e0 + r_shard_len);
+  const int k = blockIdx.y;
+  if (k >= int(*rej_count)) return;
+  const int r = rej_list[k];
+  const ReqState st = state[r];
+  const size_t row = size_t(r) * (N - 1) + st.reject_row;
+  const int e1 = min(V, (sh + 1) * kRShard);
+  const int e0 = sh * kRShard + threadIdx.x * kRPer;
+  float xp[kRPer], xq[kRPer];
+  load_run<T>(p_logits + row * V, e0, e1, xp);
+  load_run<T>(q_logits + row * V, e0, e1, xq);
+  double lse_p, lse_q;
+  wave_lse64(lse64, k, r_shards, lse_p, lse_q);
+  double rv[kRPer], pv[kRPer];
+  resid_values(xp, xq, st.table_ok, tab, lse_p, lse_q, rv, pv);
   double rs = 0.0, ps = 0.0;
-  for (int e = e0 + threadIdx.x; e < e1; e += kThreads) {
-    const double p = exp(double(to_f32<T>(pr[e])) - lse_p);
-    const double q = exp(double(to_f32<T>(qr[e])) - lse_q);
-    rs += fmax(0.0, p - q);
-    ps += p;
-  }
-  rs = wave_sum_d(rs);
-  ps = wave_sum_d(ps);
-  __shared__ double sm[2][kThreads / 64];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { sm[0][wave] = rs; sm[1][wave] = ps; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double a = 0.0, b = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) { a += sm[0][w]; b += sm[1][w]; }
-    mass[size_t(r) * r_shards + sh] = make_double2(a, b);
-  }
-}
-
-// inclusive scan of one double per thread across the workgroup
-__device__ __forceinline__ double block_scan_d(double x, double* sm_w, double& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) sm_w[wave] = x;
-  __syncthreads();
-  double before = 0.0;
-  total = 0.0;
-  for (int w = 0; w < kThreads / 64; ++w) {
-    if (w < wave) before += sm_w[w];
-    total += sm_w[w];
-  }
-  return before + x;
+  for (int i = 0; i < kRPer; ++i) { rs += rv[i]; ps += pv[i]; }
+  __shared__ double sm[kThreads / 64];
+  rs = block_sum_d(rs, sm);
+  ps = block_sum_d(ps, sm);
+  if (threadIdx.x == 0) mass[size_t(k) * r_shards + sh] = make_double2(rs, ps);
 }
 
+// One workgroup per listed request: the token draw.  The last workgroup of
+// the grid to finish empties the list for the next call.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p_logits,
                                                           const T* __restrict__ q_logits, int N, int V,
-                                                          int r_shard_len, int r_shards,
-                                                          const ReqState* __restrict__ state,
+                                                          int r_shards, const ReqState* __restrict__ state,
+                                                          uint32_t* __restrict__ rej_count,
+                                                          const int32_t* __restrict__ rej_list,
+                                                          const double* __restrict__ tab,
                                                           const double2* __restrict__ lse64,
                                                           const double2* __restrict__ mass,
+                                                          uint32_t* __restrict__ done_count,
                                                           int32_t* __restrict__ out_tokens) {
-  const int r = blockIdx.x;
-  const ReqState st = state[r];
-  const int j = st.reject_row;
-  if (j < 0) return;
-  __shared__ double lse_sm[2];
-  __shared__ double target_sm, before_sm;
-  __shared__ int shard_sm, fallback_sm;
-  if (threadIdx.x == 0) {
-    combine_lse64(lse64, r, r_shards, lse_sm[0], lse_sm[1]);
-    double S = 0.0;
-    for (int i = 0; i < r_shards; ++i) S += mass[size_t(r) * r_shards + i].x;
-    int fb = 0;
-    if (!(S > 0.0)) {
-      fb = 1;
-      S = 0.0;
-      for (int i = 0; i < r_shards; ++i) S += mass[size_t(r) * r_shards + i].y;
-    }
-    const double target = st.u_resample * S;
-    double cum = 0.0;
-    int pick = -1, last_nz = 0;
-    double before_last = 0.0;
-    for (int i = 0; i < r_shards; ++i) {
-      const double mi = fb ? mass[size_t(r) * r_shards + i].y : mass[size_t(r) * r_shards + i].x;
-      if (mi > 0.0) { last_nz = i; before_last = cum; }
-      if (pick < 0 && cum + mi > target) { pick = i; before_sm = cum; }
-      cum += mi;
-    }
-    if (pick < 0) { pick = last_nz; before_sm = before_last; }
-    shard_sm = pick;
-    target_sm = target;
-    fallback_sm = fb;
-  }
+  const int k = blockIdx.x;
+  const int count = int(*rej_count);
+  if (k >= count) return;
+  select_request<T>(p_logits, q_logits, N, V, r_shards, state, rej_list, tab, lse64, mass, out_tokens, k);
   __syncthreads();
-  const double lse_p = lse_sm[0], lse_q = lse_sm[1];
-  const double target = target_sm;
-  const int fb = fallback_sm;
-  const size_t row = size_t(r) * (N - 1) + j;
-  const T* pr = p_logits + row * V;
-  const T* qr = q_logits + row * V;
-  const int e0 = shard_sm * r_shard_len, e1 = min(V, e0 + r_shard_len);
-  __shared__ double sm_w[kThreads / 64];
-  __shared__ int found_sm, last_pos_sm;
-  if (threadIdx.x == 0) { found_sm = INT_MAX; last_pos_sm = -1; }
-  __syncthreads();
-  double before = before_sm;
-  for (int c0 = e0; c0 < e1; c0 += kThreads) {
-    const int e = c0 + threadIdx.x;
-    double rv = 0.0;
-    if (e < e1) {
-      const double p = exp(double(to_f32<T>(pr[e])) - lse_p);
-      if (fb) rv = p;
-      else rv = fmax(0.0, p - exp(double(to_f32<T>(qr[e])) - lse_q));
-    }
-    double total;
-    const double incl = block_scan_d(rv, sm_w, total);
-    if (e < e1 && rv > 0.0) atomicMax(&last_pos_sm, e);
-    if (e < e1 && before + incl > target) atomicMin(&found_sm, e);
-    __syncthreads();
-    if (found_sm != INT_MAX) break;
-    before += total;
-  }
   if (threadIdx.x == 0) {
-    int y = found_sm;
-    if (y == INT_MAX) y = (last_pos_sm >= 0) ? last_pos_sm : e1 - 1;
-    out_tokens[size_t(r) * N + st.accept_len] = y;
+    const uint32_t done = __hip_atomic_fetch_add(done_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == uint32_t(count - 1)) {
+      st_coherent(done_count, 0u);
+      st_coherent(rej_count, 0u);
+    }
   }
 }
 
@@ -398,17 +577,44 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   ReqState* st = reinterpret_cast<ReqState*>(ws + L.req);
   double2* l64 = reinterpret_cast<double2*>(ws + L.lse64);
   double2* mass = reinterpret_cast<double2*>(ws + L.mass);
-  hipLaunchKernelGGL((lse_partial<T>), dim3(p.shards, p.rows), dim3(kThreads), 0, stream, P, Qp,
-                     B * (N - 1), V, p.shard_len, p.shards, part);
-  hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(64), 0, stream, P, Qp, proposals, req_ids,
-                     positions, seed_lo, seed_hi, step, N, V, p.shards, part, accept_len, out_tokens,
-                     n_out, n_commit, logp_sel, logq_sel, st, flags);
+  uint32_t* rej_count = reinterpret_cast<uint32_t*>(ws + kRejCountOffset);
+  uint32_t* done_count = reinterpret_cast<uint32_t*>(ws + kResidDoneOffset);
+  int32_t* rej_list = reinterpret_cast<int32_t*>(ws + L.rej_list);
+  const double* tab = reinterpret_cast<const double*>(ws + L.exp_table);
+  DecideArgs<T> a;
+  a.p_logits = P;
+  a.q_logits = Qp;
+  a.proposals = proposals;
+  a.req_ids = req_ids;
+  a.positions = positions;
+  a.seed_lo = seed_lo;
+  a.seed_hi = seed_hi;
+  a.step = step;
+  a.B = B;
+  a.N = N;
+  a.V = V;
+  a.shards = p.shards;
+  a.part = part;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.n_out = n_out;
+  a.n_commit = n_commit;
+  a.logp_sel = logp_sel;
+  a.logq_sel = logq_sel;
+  a.state = st;
+  a.flags = flags;
+  a.rej_count = rej_count;
+  a.rej_list = rej_list;
+  a.bf16_logits = (s.logit_dtype == ISD_BF16) ? 1 : 0;
+  hipLaunchKernelGGL((lse_partial<T>), dim3(p.shards, p.rows), dim3(kThreads), 0, stream, a, B * (N - 1),
+                     p.shard_len, part);
+  hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(64), 0, stream, a);
   hipLaunchKernelGGL((resid_lse64<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shard_len, p.r_shards, st, l64);
+                     p.r_shards, st, rej_count, rej_list, tab, l64);
   hipLaunchKernelGGL((resid_mass64<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shard_len, p.r_shards, st, l64, mass);
-  hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shard_len, p.r_shards, st, l64, mass, out_tokens);
+                     p.r_shards, st, rej_count, rej_list, tab, l64, mass);
+  hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, st,
+                     rej_count, rej_list, tab, l64, mass, done_count, out_tokens);
   return hipGetLastError();
 }
 

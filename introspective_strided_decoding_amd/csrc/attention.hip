@@ -6,9 +6,10 @@
 // group (G heads x Q stride rows, padded to 32 or 64 columns), an online
 // softmax state (running max m, running sum l, un-normalised output O); the
 // four waves merge through LDS and the workgroup writes one partial (m, l, O)
-// per column.  The combine kernel merges the partials of all splits with the
-// strictly causal block of the stride itself (row i sees stride rows 0..i)
-// and normalises.
+// per column.  The last workgroup of (r, hk) to finish (an atomic arrival
+// count, no waiting) merges the partials of all splits with the strictly
+// causal block of the stride itself (row i sees stride rows 0..i),
+// normalises, and writes the output.
 //
 // bf16 path (matrix cores): per tile, S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (rows = 32 tokens, columns = 32 query columns,
@@ -22,12 +23,19 @@
 // max between the two half-waves.
 //
 // fp32 path: one wave per (request, kv head, split, query column), dot
-// products by wave reduction; the same partial format and combine kernel.
+// products by wave reduction, then a separate combine kernel with the same
+// merge code.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "isd_internal.hpp"
 
 namespace isd {
 namespace {
+
+constexpr int kMaxSplits = 64;
+constexpr int kMaxRows = 64;
+constexpr int kMaxQ = 64;
 
 // slot -> storage index inside a V page row: swap bits 2 and 3
 __device__ __forceinline__ int v_sigma(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
@@ -47,51 +55,50 @@ __device__ __forceinline__ void split_range(int n_tiles, int s, int n_splits, in
   t1 = (s == n_splits - 1) ? n_tiles : min(n_tiles, t0 + tps);
 }
 
-template <int D>
-struct TileFrag {
-  u32x4 k[D / 16];          // S^T operand A per k-step: 8 dims of one token
-  u32x4 v[2][D / 32];       // O^T operand A per (page, dim block): 8 tokens of one dim
-};
+// Splits that take part for a context of n_tiles tiles: a prefix 0..n-1,
+// at least one (an empty context still needs the stride block).
+__device__ __forceinline__ int active_splits(int n_tiles, int n_splits, int tps) {
+  return max(1, min(n_splits, (n_tiles + tps - 1) / tps));
+}
 
+// Operand loads of one 32-token tile (pages pid0, pid1; both valid ids).
+// One base pointer per lane and page; the unrolled k-steps / dim blocks are
+// immediate offsets from it.
 template <int D>
-__device__ __forceinline__ void load_tile(TileFrag<D>& f, const uint16_t* __restrict__ kp,
-                                          const uint16_t* __restrict__ vp, int pid0, int pid1,
-                                          int hk, int Hkv, int lane) {
+__device__ __forceinline__ void load_k(u32x4 (&k)[D / 16], const uint16_t* __restrict__ kp, int pid0,
+                                       int pid1, int hk, int Hkv, int lane) {
   const int h = lane >> 5;
   const int i = lane & 31;
-  const int pid_k = (i < 16) ? pid0 : pid1;
-  const int slot = i & 15;
+  const int pid = (i < 16) ? pid0 : pid1;
+  const u32x4* base = reinterpret_cast<const u32x4*>(
+      kp + (size_t(pid) * Hkv + hk) * (D * kPage) + (h * kPage + (i & 15)) * 8);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    if (pid_k >= 0) {
-      const size_t off = ((size_t(pid_k) * Hkv + hk) * (D / 8) + (2 * s + h)) * (kPage * 8) + slot * 8;
-      f.k[s] = *reinterpret_cast<const u32x4*>(kp + off);
-    } else {
-      f.k[s] = u32x4{0, 0, 0, 0};
-    }
-  }
+  for (int s = 0; s < D / 16; ++s) k[s] = base[s * 2 * kPage];
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(u32x4 (&v)[2][D / 32], const uint16_t* __restrict__ vp, int pid0,
+                                       int pid1, int hk, int Hkv, int lane) {
+  const int h = lane >> 5;
+  const int i = lane & 31;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const int pid = m ? pid1 : pid0;
+    const u32x4* base = reinterpret_cast<const u32x4*>(
+        vp + (size_t(m ? pid1 : pid0) * Hkv + hk) * (D * kPage) + i * kPage + h * 8);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      if (pid >= 0) {
-        const int d = db * 32 + i;
-        const size_t off = ((size_t(pid) * Hkv + hk) * D + d) * kPage + h * 8;
-        f.v[m][db] = *reinterpret_cast<const u32x4*>(vp + off);
-      } else {
-        f.v[m][db] = u32x4{0, 0, 0, 0};
-      }
-    }
+    for (int db = 0; db < D / 32; ++db) v[m][db] = base[db * 32 * 2];
   }
 }
 
+// Page id of logical page lp; an id outside the pool raises the flag and
+// reads page 0 instead (the request's result is then unspecified, but no
+// access leaves the pool).
 __device__ __forceinline__ int page_id(const int32_t* __restrict__ trow, int lp, int num_pages,
                                        uint32_t* flags) {
   const int pid = trow[lp];
   if (pid < 0 || pid >= num_pages) {
     raise_flag(flags, ISD_FLAG_PAGE_RANGE);
-    return -1;
+    return 0;
   }
   return pid;
 }
@@ -115,19 +122,101 @@ __device__ __forceinline__ u32x4 mask_v(u32x4 v, int tok_page0, int L, int h) {
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// Final merge for one (request r, kv head hk), run by a whole 256-thread
+// workgroup: the `active` split partials of (r, hk) and the stride's own
+// causal block, normalised, written to out.
+//   A. every (column c, stride key j <= i(c)) score, one thread per pair;
+//   B. per column: global max over split maxima and stride scores, the
+//      normaliser, and one coefficient per split / stride key (in LDS);
+//   C. every (column, 4 dims) output from the coefficients.
+template <typename T, int D>
+__device__ __forceinline__ void combine_rk(const T* __restrict__ q, const T* __restrict__ k_new,
+                                           const T* __restrict__ v_new, T* __restrict__ out,
+                                           const float2* __restrict__ ws_ml, const float* __restrict__ ws_o,
+                                           int r, int hk, int Qn, int Hq, int Hkv, int G, int rows,
+                                           int rows_pad, int n_splits, int active, float scale_log2,
+                                           float (*sc)[kMaxQ], float (*cs)[kMaxSplits]) {
+  const int tid = threadIdx.x;
+  const int rk = r * Hkv + hk;
+  const size_t base0 = size_t(rk) * n_splits * rows_pad;
+  const int pairs = rows * Qn;
+  for (int pidx = tid; pidx < pairs; pidx += blockDim.x) {
+    const int c = pidx / Qn, j = pidx % Qn;
+    const int g = c / Qn, i = c % Qn;
+    if (j > i) continue;
+    const T* qrow = q + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D;
+    const T* krow = k_new + ((size_t(r) * Qn + j) * Hkv + hk) * D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) acc = fmaf(to_f32<T>(qrow[d]), to_f32<T>(krow[d]), acc);
+    sc[c][j] = acc * scale_log2;
+  }
+  __syncthreads();
+  if (tid < rows) {
+    const int c = tid, i = c % Qn;
+    float M = -INFINITY;
+    for (int s = 0; s < active; ++s) M = fmaxf(M, ld_coherent(&ws_ml[base0 + size_t(s) * rows_pad + c].x));
+    for (int j = 0; j <= i; ++j) M = fmaxf(M, sc[c][j]);
+    float Lsum = 0.f;
+    for (int s = 0; s < active; ++s) {
+      const float2 ml = make_float2(ld_coherent(&ws_ml[base0 + size_t(s) * rows_pad + c].x),
+                                    ld_coherent(&ws_ml[base0 + size_t(s) * rows_pad + c].y));
+      const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+      cs[c][s] = w;
+      Lsum += ml.y * w;
+    }
+    for (int j = 0; j <= i; ++j) {
+      const float w = exp2f(sc[c][j] - M);
+      sc[c][j] = w;
+      Lsum += w;
+    }
+    const float inv = 1.f / Lsum;
+    for (int s = 0; s < active; ++s) cs[c][s] *= inv;
+    for (int j = 0; j <= i; ++j) sc[c][j] *= inv;
+  }
+  __syncthreads();
+  constexpr int D4 = D / 4;
+  for (int u = tid; u < rows * D4; u += blockDim.x) {
+    const int c = u / D4, d0 = (u % D4) * 4;
+    const int g = c / Qn, i = c % Qn;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < active; ++s) {
+      const float* src = ws_o + (base0 + size_t(s) * rows_pad + c) * D + d0;
+      const float w = cs[c][s];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(ld_coherent(src + e), w, acc[e]);
+    }
+    for (int j = 0; j <= i; ++j) {
+      const T* vrow = v_new + ((size_t(r) * Qn + j) * Hkv + hk) * D + d0;
+      const float w = sc[c][j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(to_f32<T>(vrow[e]), w, acc[e]);
+    }
+    T* orow = out + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D + d0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[e] = from_f32<T>(acc[e]);
+  }
+}
+
 template <int D, int RB>
-__global__ __launch_bounds__(256) void attn_split_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
-    const int32_t* __restrict__ table, const int32_t* __restrict__ ctx_lens, int Qn, int Hq, int Hkv,
-    int G, int rows, int max_pages, int num_pages, int tps, int n_splits, float scale_log2,
-    float2* __restrict__ ws_ml, float* __restrict__ ws_o, uint32_t* __restrict__ flags) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, 2))) void attn_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out, int Qn, int Hq, int Hkv, int G,
+    int rows, int max_pages, int num_pages, int tps, int n_splits, float scale_log2,
+    float2* __restrict__ ws_ml, float* __restrict__ ws_o, uint32_t* __restrict__ arrivals,
+    uint32_t* __restrict__ flags) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int COLS = RB * 32;
   constexpr int OSTR = D + 4;  // padded LDS row stride
   __shared__ float sm_m[kAttnWaves][COLS];
   __shared__ float sm_l[kAttnWaves][COLS];
-  __shared__ __attribute__((aligned(16))) float sm_o[2][COLS * OSTR];
+  __shared__ __attribute__((aligned(16))) float sm_o0[COLS * OSTR];
+  __shared__ __attribute__((aligned(16))) float sm_o1[COLS * OSTR];
+  __shared__ __attribute__((aligned(16))) u32x4 sm_q[(D / 8) * COLS];
+  __shared__ float sm_ml[COLS][2];
+  __shared__ int s_last;
 
   const int split = blockIdx.x % n_splits;
   const int rk = blockIdx.x / n_splits;
@@ -135,31 +224,48 @@ __global__ __launch_bounds__(256) void attn_split_bf16(
   const int r = rk / Hkv;
   const int L = clamp_ctx(ctx_lens[r], max_pages, flags);
   const int n_tiles = (L + kTileTokens - 1) / kTileTokens;
+  const int active = active_splits(n_tiles, n_splits, tps);
+  if (split >= active) return;
   int t0, t1;
   split_range(n_tiles, split, n_splits, tps, t0, t1);
-  if (t0 >= t1) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;
   const int col_l = lane & 31;
   const int32_t* trow = table + size_t(r) * max_pages;
+  // split 0's wave 0 also takes the stride's own causal block as one extra tile
+  const bool stride_tile = (split == 0) && (wave == 0);
 
-  // Q^T operand B per (row block, k-step): 8 dims of one query column.
-  u32x4 qf[RB][KS];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int c = rb * 32 + col_l;
+  auto pages = [&](int tt, int& p0, int& p1) {
+    p0 = page_id(trow, 2 * tt, num_pages, flags);
+    // second page past the context: reuse the first (its tokens are masked)
+    p1 = (tt * kTileTokens + kPage < L) ? page_id(trow, 2 * tt + 1, num_pages, flags) : p0;
+  };
+  // context tiles of this wave: t0 + wave + 4*i for i < n
+  const int first = t0 + wave;
+  const int n = (first < t1) ? (t1 - first + kAttnWaves - 1) / kAttnWaves : 0;
+  u32x4 ak[KS], av[2][DB], bk[KS], bv[2][DB];
+  if (n > 0) {   // first tile's loads go out before the Q staging below
+    int p0, p1;
+    pages(first, p0, p1);
+    load_k<D>(ak, kp, p0, p1, hk, Hkv, lane);
+    load_v<D>(av, vp, p0, p1, hk, Hkv, lane);
+  }
+
+  // Q^T operand B staged in LDS as [dim chunk][column] 16-byte cells: lane
+  // (h, column) of k-step ks reads cell (2*ks + h, column); consecutive lanes
+  // read consecutive cells.
+  for (int idx = threadIdx.x; idx < (D / 8) * COLS; idx += blockDim.x) {
+    const int ch = idx / COLS, c = idx % COLS;
+    u32x4 v = u32x4{0, 0, 0, 0};
     if (c < rows) {
       const int g = c / Qn, i = c % Qn;
-      const uint16_t* qrow = q + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[rb][s] = *reinterpret_cast<const u32x4*>(qrow + (2 * s + h) * 8);
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[rb][s] = u32x4{0, 0, 0, 0};
+      v = *reinterpret_cast<const u32x4*>(q + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D + ch * 8);
     }
+    sm_q[idx] = v;
   }
+  __syncthreads();
 
   f32x16 o[RB][DB];
   float m_run[RB], l_run[RB];
@@ -171,69 +277,141 @@ __global__ __launch_bounds__(256) void attn_split_bf16(
     for (int db = 0; db < DB; ++db) o[rb][db] = f32x16{};
   }
 
-  int t = t0 + wave;
-  TileFrag<D> cur, nxt;
-  if (t < t1) {
-    const int p0 = page_id(trow, 2 * t, num_pages, flags);
-    const int p1 = (t * kTileTokens + kPage < L) ? page_id(trow, 2 * t + 1, num_pages, flags) : -1;
-    load_tile<D>(cur, kp, vp, p0, p1, hk, Hkv, lane);
-  }
-  for (; t < t1; t += kAttnWaves) {
-    const int tn = t + kAttnWaves;
-    if (tn < t1) {
-      const int p0 = page_id(trow, 2 * tn, num_pages, flags);
-      const int p1 = (tn * kTileTokens + kPage < L) ? page_id(trow, 2 * tn + 1, num_pages, flags) : -1;
-      load_tile<D>(nxt, kp, vp, p0, p1, hk, Hkv, lane);
-    }
-    const int tok0 = t * kTileTokens;
-    const bool partial = tok0 + kTileTokens > L;
-    if (partial) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) cur.v[m][db] = mask_v(cur.v[m][db], tok0 + 16 * m, L, h);
-    }
+  // S^T = K Q^T for one 32-token tile
+  auto scores = [&](const u32x4 (&ck)[KS], f32x16 (&s)[RB]) {
+    int qcell = h * COLS + col_l;
+    asm volatile("" : "+v"(qcell));   // keep the Q operand reads inside the loop
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      f32x16 s = f32x16{};
+      s[rb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.k[ks]), as_bf16x8(qf[rb][ks]), s, 0, 0, 0);
+        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ck[ks]),
+                                                        as_bf16x8(sm_q[qcell + 2 * ks * COLS + rb * 32]),
+                                                        s[rb], 0, 0, 0);
+    }
+  };
+  // online softmax update and O^T += V^T P^T; valid(rb, v) says whether
+  // accumulator entry v (token (v/4)*8 + h*4 + v%4 of the tile) counts
+  auto consume = [&](f32x16 (&s)[RB], const u32x4 (&cv)[2][DB], auto valid) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int tok = tok0 + (v >> 2) * 8 + h * 4 + (v & 3);
-        float x = s[v] * scale_log2;
-        if (partial && tok >= L) x = -INFINITY;
-        s[v] = x;
+        float x = s[rb][v] * scale_log2;
+        if (!valid(rb, v)) x = -INFINITY;
+        s[rb][v] = x;
         mx = fmaxf(mx, x);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run[rb], mx);
-      const float alpha = exp2f(m_run[rb] - m_new);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[rb] - m_new);
       m_run[rb] = m_new;
       float psum = 0.f;
-      float pv[16];
+      bf16x8 pb[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        pv[v] = exp2f(s[v] - m_new);
-        psum += pv[v];
+        const float p = (s[rb][v] == -INFINITY) ? 0.f : exp2f(s[rb][v] - m_new);
+        psum += p;
+        pb[v >> 3][v & 7] = (__bf16)p;
       }
       l_run[rb] = l_run[rb] * alpha + psum;
-      bf16x8 pb[2];
+      // rescale only when some column's running max moved
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cv[m][db]), pb[m], o[rb][db], 0, 0, 0);
+    }
+  };
+
+  // ---- the stride block: keys/values of this pass's rows, masked j <= i ----
+  if (stride_tile) {
+    u32x4 sk[KS], sv[2][DB];
+    const int ti = lane & 31;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sk[s] = (ti < Qn) ? *reinterpret_cast<const u32x4*>(
+                              k_new + ((size_t(r) * Qn + ti) * Hkv + hk) * D + (2 * s + h) * 8)
+                        : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 32 + (lane & 31);
+        uint32_t w[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          uint32_t pair = 0;
+#pragma unroll
+          for (int hi = 0; hi < 2; ++hi) {
+            const int e = 2 * e2 + hi;
+            const int t = 16 * m + (e >> 2) * 8 + h * 4 + (e & 3);
+            const uint32_t bits =
+                (t < Qn) ? uint32_t(v_new[((size_t(r) * Qn + t) * Hkv + hk) * D + d]) : 0u;
+            pair |= bits << (16 * hi);
+          }
+          w[e2] = pair;
+        }
+        sv[m][db] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    f32x16 s[RB];
+    scores(sk, s);
+    consume(s, sv, [&](int rb, int v) {
+      const int t = (v >> 2) * 8 + h * 4 + (v & 3);
+      const int i = (rb * 32 + col_l) % Qn;    // stride row of this column
+      return t <= i;                           // t < Qn follows from i < Qn
+    });
+  }
+
+  // ---- context tiles: software pipeline over this wave's tiles ----
+  // The next tile's keys are requested before this tile's S^T product and
+  // its values right after it.  Two register sets alternate; the last tile is
+  // peeled so that every load inside the loop is unconditional.
+  auto tile = [&](auto prefetch, u32x4 (&ck)[KS], u32x4 (&cv)[2][DB], u32x4 (&nv)[2][DB], int tt,
+                  int np0, int np1) {
+    const int tok0 = tt * kTileTokens;
+    const bool partial = tok0 + kTileTokens > L;
+    f32x16 s[RB];
+    scores(ck, s);
+    if constexpr (decltype(prefetch)::value) load_v<D>(nv, vp, np0, np1, hk, Hkv, lane);
+    if (partial) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[m][e] = (__bf16)pv[8 * m + e];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        o[rb][db] *= alpha;
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-          o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.v[m][db]), pb[m], o[rb][db], 0, 0, 0);
-      }
+        for (int db = 0; db < DB; ++db) cv[m][db] = mask_v(cv[m][db], tok0 + 16 * m, L, h);
     }
-    cur = nxt;
+    consume(s, cv, [&](int, int v) { return !partial || tok0 + (v >> 2) * 8 + h * 4 + (v & 3) < L; });
+  };
+  using Pre = std::integral_constant<bool, true>;
+  using NoPre = std::integral_constant<bool, false>;
+
+  if (n > 0) {
+    int p0 = 0, p1 = 0;
+    int i = 0;
+    for (; i + 2 < n; i += 2) {
+      const int ta = first + i * kAttnWaves, tb = ta + kAttnWaves, tc = tb + kAttnWaves;
+      pages(tb, p0, p1);
+      load_k<D>(bk, kp, p0, p1, hk, Hkv, lane);
+      tile(Pre{}, ak, av, bv, ta, p0, p1);
+      pages(tc, p0, p1);
+      load_k<D>(ak, kp, p0, p1, hk, Hkv, lane);
+      tile(Pre{}, bk, bv, av, tb, p0, p1);
+    }
+    const int ta = first + i * kAttnWaves;
+    if (i + 1 < n) {
+      pages(ta + kAttnWaves, p0, p1);
+      load_k<D>(bk, kp, p0, p1, hk, Hkv, lane);
+      tile(Pre{}, ak, av, bv, ta, p0, p1);
+      tile(NoPre{}, bk, bv, av, ta + kAttnWaves, 0, 0);
+    } else {
+      tile(NoPre{}, ak, av, bv, ta, 0, 0);
+    }
   }
 
   // ---- merge the four waves of the workgroup ----
@@ -255,7 +433,7 @@ __global__ __launch_bounds__(256) void attn_split_bf16(
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm_m[w][c]);
     wscale[rb] = (m_run[rb] == -INFINITY) ? 0.f : exp2f(m_run[rb] - M);
   }
-  auto put = [&](int buf, bool add) {
+  auto put = [&](float* buf, bool add) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int c = rb * 32 + col_l;
@@ -267,17 +445,12 @@ __global__ __launch_bounds__(256) void attn_split_bf16(
           f32x4 val = {o[rb][db][4 * v4 + 0], o[rb][db][4 * v4 + 1], o[rb][db][4 * v4 + 2],
                        o[rb][db][4 * v4 + 3]};
           val *= wscale[rb];
-          f32x4* dst = reinterpret_cast<f32x4*>(&sm_o[buf][c * OSTR + d0]);
+          f32x4* dst = reinterpret_cast<f32x4*>(&buf[c * OSTR + d0]);
           if (add) *dst += val; else *dst = val;
         }
     }
   };
-  if (wave < 2) put(wave, false);
-  __syncthreads();
-  if (wave >= 2) put(wave - 2, true);
-  __syncthreads();
-
-  const size_t base = (size_t(rk) * n_splits + split) * (RB * 32);
+  if (wave < 2) put(wave ? sm_o1 : sm_o0, false);
   if (threadIdx.x < rows) {
     const int c = threadIdx.x;
     float M = -INFINITY;
@@ -289,14 +462,75 @@ __global__ __launch_bounds__(256) void attn_split_bf16(
       const float mw = sm_m[w][c];
       if (mw != -INFINITY) Lsum += sm_l[w][c] * exp2f(mw - M);
     }
-    ws_ml[base + c] = make_float2(M, Lsum);
+    sm_ml[c][0] = M;
+    sm_ml[c][1] = Lsum;
   }
+  __syncthreads();
+  if (wave >= 2) put(wave == 3 ? sm_o1 : sm_o0, true);
+  __syncthreads();
+
   constexpr int V4 = D / 4;
+  auto write_out = [&](int c, int d0, f32x4 v) {
+    const int g = c / Qn, i = c % Qn;
+    uint16_t* dst = out + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D + d0;
+    const uint32_t lo = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
+    const uint32_t hi = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  };
+  if (active == 1) {
+    // the only split: normalise straight from LDS
+    for (int idx = threadIdx.x; idx < rows * V4; idx += blockDim.x) {
+      const int c = idx / V4, d0 = (idx % V4) * 4;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&sm_o0[c * OSTR + d0]);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(&sm_o1[c * OSTR + d0]);
+      write_out(c, d0, (a + b) * (1.f / sm_ml[c][1]));
+    }
+    return;
+  }
+
+  // several splits: publish this split's partial, the last to arrive merges
+  const size_t base = (size_t(rk) * n_splits + split) * COLS;
+  if (threadIdx.x < rows) {
+    st_coherent(&ws_ml[base + threadIdx.x].x, sm_ml[threadIdx.x][0]);
+    st_coherent(&ws_ml[base + threadIdx.x].y, sm_ml[threadIdx.x][1]);
+  }
   for (int idx = threadIdx.x; idx < rows * V4; idx += blockDim.x) {
     const int c = idx / V4, d0 = (idx % V4) * 4;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(&sm_o[0][c * OSTR + d0]);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(&sm_o[1][c * OSTR + d0]);
-    *reinterpret_cast<f32x4*>(ws_o + (base + c) * D + d0) = a + b;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(&sm_o0[c * OSTR + d0]);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(&sm_o1[c * OSTR + d0]);
+    float* dst = ws_o + (base + c) * D + d0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_coherent(dst + e, a[e] + b[e]);
+  }
+  if (!arrive_last(&arrivals[rk], uint32_t(active), &s_last)) return;
+  // per column: global max and the split weights (normaliser folded in)
+  __shared__ float sm_w[COLS][kMaxSplits];
+  const size_t base0 = size_t(rk) * n_splits * COLS;
+  if (threadIdx.x < rows) {
+    const int c = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < active; ++s) M = fmaxf(M, ld_coherent(&ws_ml[base0 + size_t(s) * COLS + c].x));
+    float Lsum = 0.f;
+    for (int s = 0; s < active; ++s) {
+      const float ms = ld_coherent(&ws_ml[base0 + size_t(s) * COLS + c].x);
+      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      sm_w[c][s] = w;
+      Lsum += w * ld_coherent(&ws_ml[base0 + size_t(s) * COLS + c].y);
+    }
+    const float inv = 1.f / Lsum;
+    for (int s = 0; s < active; ++s) sm_w[c][s] *= inv;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rows * V4; idx += blockDim.x) {
+    const int c = idx / V4, d0 = (idx % V4) * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < active; ++s) {
+      const float* src = ws_o + (base0 + size_t(s) * COLS + c) * D + d0;
+      const float w = sm_w[c][s];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(ld_coherent(src + e), w, acc[e]);
+    }
+    write_out(c, d0, acc);
   }
 }
 
@@ -317,9 +551,9 @@ __global__ __launch_bounds__(64) void attn_split_f32(
   if (c >= rows) return;
   const int L = clamp_ctx(ctx_lens[r], max_pages, flags);
   const int n_tiles = (L + kTileTokens - 1) / kTileTokens;
+  if (split >= active_splits(n_tiles, n_splits, tps)) return;
   int t0, t1;
   split_range(n_tiles, split, n_splits, tps, t0, t1);
-  if (t0 >= t1) return;
   const int lane = threadIdx.x;
   const int g = c / Qn, i = c % Qn;
   const float* qrow = q + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D;
@@ -331,7 +565,6 @@ __global__ __launch_bounds__(64) void attn_split_f32(
   const int tok_end = min(L, t1 * kTileTokens);
   for (int tok = t0 * kTileTokens; tok < tok_end; ++tok) {
     const int pid = page_id(trow, tok / kPage, num_pages, flags);
-    if (pid < 0) continue;
     const int slot = tok % kPage;
     float part = 0.f;
     float vv[E];
@@ -357,80 +590,22 @@ __global__ __launch_bounds__(64) void attn_split_f32(
   for (int e = 0; e < E; ++e) ws_o[(base + c) * D + lane * E + e] = acc[e];
 }
 
-// Merge split partials with the stride's own causal block; normalise; write out.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     const int32_t* __restrict__ ctx_lens, T* __restrict__ out, const float2* __restrict__ ws_ml,
     const float* __restrict__ ws_o, int Qn, int Hq, int Hkv, int G, int rows, int rows_pad,
     int max_pages, int tps, int n_splits, float scale_log2) {
-  constexpr int E = D / 64;
+  __shared__ float sc[kMaxRows][kMaxQ];
+  __shared__ float cs[kMaxRows][kMaxSplits];
   const int rk = blockIdx.x;
   const int hk = rk % Hkv;
   const int r = rk / Hkv;
   int L = ctx_lens[r];
   L = (L < 0) ? 0 : min(L, max_pages * kPage);   // flag already raised by the split kernel
   const int n_tiles = (L + kTileTokens - 1) / kTileTokens;
-  int active = 0;
-  for (int s = 0; s < n_splits; ++s) {
-    int t0, t1;
-    split_range(n_tiles, s, n_splits, tps, t0, t1);
-    if (t0 < t1) active = s + 1;
-  }
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  for (int c = wave; c < rows; c += nwaves) {
-    const int g = c / Qn, i = c % Qn;
-    const int hq = hk * G + g;
-    const T* qrow = q + ((size_t(r) * Qn + i) * Hq + hq) * D;
-    float qv[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) qv[e] = to_f32<T>(qrow[lane * E + e]);
-    // split partials first
-    const size_t base0 = size_t(rk) * n_splits * rows_pad;
-    float M = -INFINITY;
-    for (int s = 0; s < active; ++s) {
-      int t0, t1;
-      split_range(n_tiles, s, n_splits, tps, t0, t1);
-      if (t0 < t1) M = fmaxf(M, ws_ml[base0 + size_t(s) * rows_pad + c].x);
-    }
-    float Lsum = 0.f;
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int s = 0; s < active; ++s) {
-      int t0, t1;
-      split_range(n_tiles, s, n_splits, tps, t0, t1);
-      if (t0 >= t1) continue;
-      const size_t pr = base0 + size_t(s) * rows_pad + c;
-      const float2 ml = ws_ml[pr];
-      const float w = exp2f(ml.x - M);
-      Lsum += ml.y * w;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(ws_o[pr * D + lane * E + e], w, acc[e]);
-    }
-    // then the stride's own rows j <= i, merged online (base-2 scores)
-    for (int j = 0; j <= i; ++j) {
-      const T* krow = k_new + ((size_t(r) * Qn + j) * Hkv + hk) * D;
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) part = fmaf(qv[e], to_f32<T>(krow[lane * E + e]), part);
-      const float sc = wave_sum(part) * scale_log2;
-      const float m_new = fmaxf(M, sc);
-      const float alpha = exp2f(M - m_new);
-      const float p = exp2f(sc - m_new);
-      Lsum = Lsum * alpha + p;
-      const T* vrow = v_new + ((size_t(r) * Qn + j) * Hkv + hk) * D;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(to_f32<T>(vrow[lane * E + e]), p, acc[e] * alpha);
-      M = m_new;
-    }
-    const float inv = 1.f / Lsum;
-    T* orow = out + ((size_t(r) * Qn + i) * Hq + hq) * D;
-#pragma unroll
-    for (int e = 0; e < E; ++e) orow[lane * E + e] = from_f32<T>(acc[e] * inv);
-  }
+  combine_rk<T, D>(q, k_new, v_new, out, ws_ml, ws_o, r, hk, Qn, Hq, Hkv, G, rows, rows_pad, n_splits,
+                   active_splits(n_tiles, n_splits, tps), scale_log2, sc, cs);
 }
 
 template <int D>
@@ -440,28 +615,25 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
                     const WsLayout& Lw, hipStream_t stream) {
   const float scale_log2 = scale * kLog2e;
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws + Lw.flags);
+  uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + Lw.attn_cnt);
   float2* ml = reinterpret_cast<float2*>(ws + Lw.attn_ml);
   float* po = reinterpret_cast<float*>(ws + Lw.attn_o);
   const int nwg = s.batch * s.n_kv_heads * p.n_splits;
   if (s.kv_dtype == ISD_BF16) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const uint16_t* kn = static_cast<const uint16_t*>(k_new);
+    const uint16_t* vn = static_cast<const uint16_t*>(v_new);
     const uint16_t* kp = static_cast<const uint16_t*>(k_pages);
     const uint16_t* vp = static_cast<const uint16_t*>(v_pages);
+    uint16_t* o = static_cast<uint16_t*>(out);
     if (p.row_blocks == 1)
-      hipLaunchKernelGGL((attn_split_bf16<D, 1>), dim3(nwg), dim3(256), 0, stream, qq, kp, vp, table,
-                         ctx_lens, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group, p.rows, s.max_pages,
-                         s.num_pages, p.tiles_per_split, p.n_splits, scale_log2, ml, po, flags);
+      hipLaunchKernelGGL((attn_bf16<D, 1>), dim3(nwg), dim3(256), 0, stream, qq, kn, vn, kp, vp, table,
+                         ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group, p.rows, s.max_pages,
+                         s.num_pages, p.tiles_per_split, p.n_splits, scale_log2, ml, po, arrivals, flags);
     else
-      hipLaunchKernelGGL((attn_split_bf16<D, 2>), dim3(nwg), dim3(256), 0, stream, qq, kp, vp, table,
-                         ctx_lens, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group, p.rows, s.max_pages,
-                         s.num_pages, p.tiles_per_split, p.n_splits, scale_log2, ml, po, flags);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_combine<uint16_t, D>), dim3(s.batch * s.n_kv_heads), dim3(256), 0, stream,
-                       qq, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                       ctx_lens, static_cast<uint16_t*>(out), ml, po, p.q_rows, s.n_q_heads,
-                       s.n_kv_heads, p.group, p.rows, p.rows_pad, s.max_pages, p.tiles_per_split,
-                       p.n_splits, scale_log2);
+      hipLaunchKernelGGL((attn_bf16<D, 2>), dim3(nwg), dim3(256), 0, stream, qq, kn, vn, kp, vp, table,
+                         ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group, p.rows, s.max_pages,
+                         s.num_pages, p.tiles_per_split, p.n_splits, scale_log2, ml, po, arrivals, flags);
   } else {
     const float* qq = static_cast<const float*>(q);
     hipLaunchKernelGGL((attn_split_f32<D>), dim3(nwg, p.rows), dim3(64), 0, stream, qq,

@@ -19,55 +19,72 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(
     const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ kp, T* __restrict__ vp,
     const int32_t* __restrict__ table, const int32_t* ctx_in, const int32_t* __restrict__ n_commit,
     int32_t* ctx_out, int N, int Hkv, int D, int max_pages, int num_pages, uint32_t* __restrict__ flags) {
+  __shared__ int pid_sm[64];
+  __shared__ int L_sm, n_sm, nv_sm;
   const int r = blockIdx.x;
   const int Qn = 2 * N - 1;
   const int cap = max_pages * kPage;
-  int L = ctx_in[r];
-  int n = n_commit[r];
-  bool bad_ctx = false;
-  if (L < 0 || L > cap) { bad_ctx = true; L = L < 0 ? 0 : cap; }
-  if (n < 0 || n > N - 1) {
-    if (threadIdx.x == 0) raise_flag(flags, ISD_FLAG_COMMIT_RANGE);
-    n = n < 0 ? 0 : N - 1;
+  if (threadIdx.x == 0) {
+    int L = ctx_in[r];
+    int n = n_commit[r];
+    if (n < 0 || n > N - 1) {
+      raise_flag(flags, ISD_FLAG_COMMIT_RANGE);
+      n = n < 0 ? 0 : N - 1;
+    }
+    if (L < 0 || L > cap) {
+      raise_flag(flags, ISD_FLAG_CTX_RANGE);
+      L = L < 0 ? 0 : cap;
+      n = 0;
+    }
+    L_sm = L;
+    n_sm = n;
   }
-  if (bad_ctx) {
-    if (threadIdx.x == 0) raise_flag(flags, ISD_FLAG_CTX_RANGE);
-    n = 0;
+  __syncthreads();
+  const int L = L_sm, n = n_sm;
+  // page of every committed row, resolved in parallel
+  if (threadIdx.x < n) {
+    const int pos = L + threadIdx.x;
+    int pid = -1;
+    if (pos < cap) {
+      pid = table[size_t(r) * max_pages + pos / kPage];
+      if (pid < 0 || pid >= num_pages) pid = -2;
+    }
+    pid_sm[threadIdx.x] = pid;
   }
-  // valid prefix: every committed row needs a mapped page
-  int nv = 0;
-  for (int i = 0; i < n; ++i) {
-    const int pos = L + i;
-    if (pos >= cap) { if (threadIdx.x == 0) raise_flag(flags, ISD_FLAG_COMMIT_RANGE); break; }
-    const int pid = table[size_t(r) * max_pages + pos / kPage];
-    if (pid < 0 || pid >= num_pages) { if (threadIdx.x == 0) raise_flag(flags, ISD_FLAG_PAGE_RANGE); break; }
-    nv = i + 1;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int nv = n;
+    for (int i = 0; i < n; ++i)
+      if (pid_sm[i] < 0) {
+        raise_flag(flags, pid_sm[i] == -1 ? ISD_FLAG_COMMIT_RANGE : ISD_FLAG_PAGE_RANGE);
+        nv = i;
+        break;
+      }
+    nv_sm = nv;
   }
+  __syncthreads();
+  const int nv = nv_sm;
   constexpr int EV = 16 / sizeof(T);            // elements per 16-byte vector
   const int kvec = D / EV;                       // 16-byte vectors per key row
-  // keys: 16-byte chunks of 8 dims (bf16) or 4 dims (fp32)
   const int kwork = nv * Hkv * kvec;
   for (int w = threadIdx.x; w < kwork; w += blockDim.x) {
     const int c = w % kvec;
     const int hk = (w / kvec) % Hkv;
     const int i = w / (kvec * Hkv);
-    const int pos = L + i;
-    const int pid = table[size_t(r) * max_pages + pos / kPage];
-    const int slot = pos % kPage;
+    const int pid = pid_sm[i];
+    const int slot = (L + i) % kPage;
     const int d0 = c * EV;
     const T* src = k_new + ((size_t(r) * Qn + i) * Hkv + hk) * D + d0;
     T* dst = kp + ((size_t(pid) * Hkv + hk) * (D / 8) + d0 / 8) * (kPage * 8) + slot * 8 + (d0 & 7);
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
   }
-  // values: one element per thread step
   const int vwork = nv * Hkv * D;
   for (int w = threadIdx.x; w < vwork; w += blockDim.x) {
     const int d = w % D;
     const int hk = (w / D) % Hkv;
     const int i = w / (D * Hkv);
-    const int pos = L + i;
-    const int pid = table[size_t(r) * max_pages + pos / kPage];
-    const int slot = pos % kPage;
+    const int pid = pid_sm[i];
+    const int slot = (L + i) % kPage;
     vp[((size_t(pid) * Hkv + hk) * D + d) * kPage + v_sigma(slot)] =
         v_new[((size_t(r) * Qn + i) * Hkv + hk) * D + d];
   }
@@ -78,6 +95,12 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(
 __global__ void fill_zero_u32(uint32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
+}
+
+// exp of every bf16 bit pattern, float64 (used by the residual sampler)
+__global__ void build_exp_table(double* t) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < kExpTableSize) t[b] = exp(double(bf16_bits_to_f32(uint16_t(b))));
 }
 
 }  // namespace
@@ -101,10 +124,11 @@ hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_ne
   return hipGetLastError();
 }
 
-hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream) {
-  const int n = int(bytes / 4);
+hipError_t launch_workspace_init(void* ws, size_t header_bytes, double* exp_table, hipStream_t stream) {
+  const int n = int(header_bytes / 4);
   hipLaunchKernelGGL(fill_zero_u32, dim3((n + 255) / 256), dim3(256), 0, stream,
                      static_cast<uint32_t*>(ws), n);
+  hipLaunchKernelGGL(build_exp_table, dim3(kExpTableSize / 256), dim3(256), 0, stream, exp_table);
   return hipGetLastError();
 }
 

@@ -58,6 +58,40 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return x;
 }
 
+// Cross-workgroup hand-off without cache flushes.  Data one workgroup
+// publishes for another in the same kernel is written and read with
+// device-scope relaxed atomic accesses (coherent across the XCDs' L2 caches
+// on their own); the writer waits for its stores to complete before it
+// counts its arrival, and only the last arrival reads the data.
+template <typename T>
+__device__ __forceinline__ void st_coherent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coherent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's stores have completed (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void wait_stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Count this workgroup's arrival; true in the last of `expected` arrivals,
+// which also rewinds the counter for the next launch.  Call with all threads.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* s_flag) {
+  wait_stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = (prev == expected - 1);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 // Device flag word (workspace offset 0).
 __device__ __forceinline__ void raise_flag(uint32_t* flags, uint32_t bit) {
   if (flags) atomicOr(flags, bit);

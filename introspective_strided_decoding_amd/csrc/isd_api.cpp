@@ -11,6 +11,12 @@
 #include "isd.h"
 #include "isd_internal.hpp"
 
+// Workgroups the attention split aims for with one 32-column block (two per
+// CU on 256 CUs); half that with two blocks (one per CU).
+#ifndef ISD_ATTN_TARGET_WGS
+#define ISD_ATTN_TARGET_WGS 256
+#endif
+
 namespace isd {
 namespace {
 
@@ -67,11 +73,15 @@ AttnPlan plan_attention(const isd_shape& s) {
   const long long cap = (long long)s.max_pages * kPage;
   const long long hint = (s.max_ctx > 0) ? std::min<long long>(s.max_ctx, cap) : cap;
   p.tiles_max = std::max(1, ceil_div(hint, kTileTokens));
-  // Aim for about 1024 workgroups (4096 waves: 16 per CU on 256 CUs) without
-  // giving a workgroup fewer than 8 tiles (two per wave) of work.
+  // Aim for one full round of resident workgroups (two per CU on 256 CUs with
+  // one 32-column block, one per CU with two) without giving a workgroup
+  // fewer than 8 tiles (two per wave) of work.
   const long long pairs = (long long)s.batch * s.n_kv_heads;
-  int splits = std::max(1, ceil_div(1024, pairs));
+  const int target = (p.row_blocks == 1) ? ISD_ATTN_TARGET_WGS : ISD_ATTN_TARGET_WGS / 2;
+  int splits = std::max(1, ceil_div(target, pairs));
   p.tiles_per_split = std::max(8, ceil_div(p.tiles_max, splits));
+  // the combine kernel keeps one coefficient per split in LDS: at most 64 splits
+  p.tiles_per_split = std::max(p.tiles_per_split, ceil_div(p.tiles_max, 64));
   p.n_splits = std::max(1, ceil_div(p.tiles_max, p.tiles_per_split));
   return p;
 }
@@ -80,13 +90,16 @@ AcceptPlan plan_accept(const isd_shape& s) {
   AcceptPlan p{};
   p.rows = 2 * s.batch * (s.stride_n - 1);
   const int V = s.vocab;
-  // about 2048 workgroups in the normaliser pass, at least 2048 elements each
+  // About 2048 workgroups in the normaliser pass, at least 2048 entries each,
+  // and at most 256 threads x 8 vectors of 16 bytes per shard.
+  const int vec = (s.logit_dtype == ISD_BF16) ? 8 : 4;
   int shards = std::max(1, ceil_div(2048, p.rows));
   shards = std::min(shards, std::max(1, V / 2048));
+  shards = std::max(shards, ceil_div(V, 256 * 8 * vec));
   p.shard_len = ceil_div(ceil_div(V, shards), 8) * 8;
   p.shards = ceil_div(V, p.shard_len);
-  // the fp64 residual works on 2048-element shards
-  p.r_shard_len = std::min(2048, ceil_div(V, 8) * 8);
+  // the fp64 residual works on 2048-element shards (256 threads x 8 entries)
+  p.r_shard_len = 2048;
   p.r_shards = ceil_div(V, p.r_shard_len);
   return p;
 }
@@ -96,6 +109,13 @@ WsLayout ws_layout(const isd_shape& s) {
   const AttnPlan a = plan_attention(s);
   const AcceptPlan c = plan_accept(s);
   size_t off = kHeaderBytes;
+  L.attn_cnt = off;
+  off = align_up(off + (size_t)s.batch * s.n_kv_heads * 4, 256);
+  L.req_cnt = off;
+  off = align_up(off + (size_t)s.batch * 4, 256);
+  L.sel_cnt = off;
+  off = align_up(off + (size_t)s.batch * 4, 256);
+  L.zero_end = off;
   const size_t partial_rows = (size_t)s.batch * s.n_kv_heads * a.n_splits * a.rows_pad;
   L.attn_ml = off;
   off = align_up(off + partial_rows * 8, 256);
@@ -109,6 +129,10 @@ WsLayout ws_layout(const isd_shape& s) {
   off = align_up(off + (size_t)s.batch * c.r_shards * 32, 256);
   L.mass = off;
   off = align_up(off + (size_t)s.batch * c.r_shards * 16, 256);
+  L.rej_list = off;
+  off = align_up(off + (size_t)s.batch * 4, 256);
+  L.exp_table = off;
+  off = align_up(off + (size_t)kExpTableSize * 8, 256);
   L.total = off;
   return L;
 }
@@ -142,11 +166,16 @@ size_t isd_workspace_bytes(const isd_shape* shape) {
   return ws_layout(*shape).total;
 }
 
-isd_status isd_workspace_init(void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (!workspace) return ISD_ERR_NULL;
-  if (!aligned16(workspace)) return ISD_ERR_ALIGNMENT;
-  if (ws_bytes < kHeaderBytes) return ISD_ERR_WORKSPACE;
-  hipError_t e = launch_workspace_init(workspace, kHeaderBytes, stream);
+isd_status isd_workspace_init(const isd_shape* shape, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  isd_status st = check_shape(shape);
+  if (st != ISD_OK) return st;
+  st = check_ws(shape, workspace, ws_bytes);
+  if (st != ISD_OK) return st;
+  const WsLayout L = ws_layout(*shape);
+  hipError_t e = launch_workspace_init(workspace, L.zero_end,
+                                       reinterpret_cast<double*>(static_cast<char*>(workspace) + L.exp_table),
+                                       stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_workspace_init");
 }
 
@@ -191,6 +220,7 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
     return ISD_ERR_NULL;
   if (!aligned16(p_logits) || !aligned16(q_logits)) return ISD_ERR_ALIGNMENT;
   if (shape->batch > 65535) return ISD_ERR_UNSUPPORTED;
+  if (shape->vocab > 2048 * 1024) return ISD_ERR_UNSUPPORTED;   // residual shards per row <= 1024
   st = check_ws(shape, workspace, ws_bytes);
   if (st != ISD_OK) return st;
   const AcceptPlan p = plan_accept(*shape);

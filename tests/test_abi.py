@@ -108,9 +108,12 @@ def test_accept_and_commit_validation():
 
 
 def test_workspace_init_and_flags_validation():
-    assert LIB.isd_workspace_init(None, 1024, None) == 1
-    assert LIB.isd_workspace_init(MISALIGNED, 1024, None) == 7
-    assert LIB.isd_workspace_init(FAKE, 16, None) == 4
+    s = _shape()
+    n = _ws(s)
+    assert LIB.isd_workspace_init(ctypes.byref(s.c()), None, n, None) == 1
+    assert LIB.isd_workspace_init(ctypes.byref(s.c()), MISALIGNED, n, None) == 7
+    assert LIB.isd_workspace_init(ctypes.byref(s.c()), FAKE, 16, None) == 4
+    assert LIB.isd_workspace_init(None, FAKE, n, None) == 1
     assert LIB.isd_read_flags(None, None, None) == 1
 
 

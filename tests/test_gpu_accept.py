@@ -63,6 +63,17 @@ def test_accept_fp32_large_vocab():
     _run(wl, 30)
 
 
+def test_accept_large_logits_take_the_direct_exp_path():
+    """Row maxima beyond +-600 leave the exp table; the float64 residual evaluates exp directly."""
+    import torch as _t
+    wl = make_workload(get_config("b8_ctx2k", batch=4, ctx=16, vocab=3000))
+    for name, off in (("p_logits", 650.0), ("q_logits", 650.0)):
+        x = _t.from_numpy(getattr(wl, name)) + off
+        setattr(wl, name, x.to(_t.bfloat16).to(_t.float32).numpy())
+    t = _run(wl, 60)
+    assert t.resamples > 0
+
+
 def test_accept_identical_rows_always_accept():
     wl = make_workload(get_config("b8_ctx2k", batch=4, ctx=16, vocab=2048))
     wl.q_logits = wl.p_logits.copy()
