@@ -236,24 +236,29 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
  * 的核心参数与验收机制"; I-DLM project page, R-ISD card): an adapter is active
  * at MASK rows only; CLEAN (verifying) rows keep the base weights:
  *
- *   Y[m][:] += scale * (X[m][:] @ A) @ Bm   for m in mask_rows[0..n_mask-1]
+ *   Y[m][:] += scale * (X[m][:] @ A) @ B   for m in mask_rows[0..n_mask-1]
  *
- *   X  [rows][d_in]   bf16
- *   A  [d_in][rank]   bf16
- *   Bm [rank][d_out]  bf16
- *   Y  [rows][d_out]  bf16, updated in place at the gated rows only
- *   mask_rows [n_mask] int32, distinct, in [0, rows)
+ * The adapter weights are taken in the layouts a linear layer stores them:
+ *   X    [rows][d_in]    bf16   input activations of the adapted projection
+ *   A_t  [rank][d_in]    bf16   down projection (A transposed)
+ *   B_t  [d_out][rank]   bf16   up projection (B transposed)
+ *   Y    [rows][d_out]   bf16   base projection output, updated in place at
+ *                               the gated rows only (other rows untouched)
+ *   mask_rows [n_mask] int32    distinct row indices in [0, rows)
  *
  * bf16 operands on the matrix cores with fp32 accumulation; the rank-r
- * intermediate stays fp32 until it is split into two bf16 terms for the
- * second product.  Supported: rank == 128, d_in % 256 == 0, d_out % 256 == 0.
- * Workspace: isd_lora_workspace_bytes().  Flags: ROW_RANGE.
+ * intermediate is summed in fp32 and enters the second product as two bf16
+ * terms (value and rounding remainder).  Supported: rank == 128,
+ * d_in % 256 == 0, d_out % 128 == 0.  Workspace: at least
+ * isd_lora_workspace_bytes() bytes; its first 4 bytes are a flag word
+ * (ISD_FLAG_ROW_RANGE: a gated row outside [0, rows) is skipped) that the
+ * caller zeroes before the first call.  Rows listed twice race.
  */
 size_t isd_lora_workspace_bytes(int32_t n_mask, int32_t d_in, int32_t rank);
-isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank,
-                          const void* X, const void* A, const void* Bm,
-                          const int32_t* mask_rows, int32_t n_mask, float scale, void* Y,
-                          void* workspace, size_t ws_bytes, hipStream_t stream);
+isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
+                          const void* A_t, const void* B_t, const int32_t* mask_rows,
+                          int32_t n_mask, float scale, void* Y, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
 
 /* Text for a status code (static storage). */
 const char* isd_status_string(isd_status status);

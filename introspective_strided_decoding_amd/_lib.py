@@ -208,12 +208,14 @@ def isd_lora_workspace_bytes(n_mask: int, d_in: int, rank: int) -> int:
     return int(LIB.isd_lora_workspace_bytes(n_mask, d_in, rank))
 
 
-def isd_lora_delta(X, A, Bm, mask_rows, Y, workspace, scale: float = 1.0, stream=None) -> None:
+def isd_lora_delta(X, A_t, B_t, mask_rows, Y, workspace, scale: float = 1.0, stream=None) -> None:
+    """Y[m] += scale * (X[m] @ A_t.T) @ B_t.T for the gated rows m (see include/isd.h)."""
     rows, d_in = X.shape
-    rank, d_out = Bm.shape
+    rank = A_t.shape[0]
+    d_out = B_t.shape[0]
     bf = torch.bfloat16
     _check("isd_lora_delta", LIB.isd_lora_delta(
-        rows, d_in, d_out, rank, _ptr(X, "X", bf), _ptr(A, "A", bf, d_in * rank),
-        _ptr(Bm, "Bm", bf), _ptr(mask_rows, "mask_rows", torch.int32), mask_rows.numel(),
+        rows, d_in, d_out, rank, _ptr(X, "X", bf), _ptr(A_t, "A_t", bf, rank * d_in),
+        _ptr(B_t, "B_t", bf, d_out * rank), _ptr(mask_rows, "mask_rows", torch.int32), mask_rows.numel(),
         float(scale), _ptr(Y, "Y", bf, rows * d_out), _ptr(workspace, "workspace", torch.uint8),
         workspace.numel(), _stream(stream)))

@@ -251,17 +251,24 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
 }
 
 size_t isd_lora_workspace_bytes(int32_t n_mask, int32_t d_in, int32_t rank) {
-  if (n_mask < 0 || d_in < 1 || rank < 1) return 0;
-  (void)d_in;
-  return kHeaderBytes;
+  if (n_mask < 0 || d_in < 256 || d_in % 256 || rank != 128) return 0;
+  return lora_layout(n_mask, d_in, rank).total;
 }
 
 isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
-                          const void* A, const void* Bm, const int32_t* mask_rows, int32_t n_mask,
+                          const void* A_t, const void* B_t, const int32_t* mask_rows, int32_t n_mask,
                           float scale, void* Y, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  (void)rows; (void)d_in; (void)d_out; (void)rank; (void)X; (void)A; (void)Bm; (void)mask_rows;
-  (void)n_mask; (void)scale; (void)Y; (void)workspace; (void)ws_bytes; (void)stream;
-  return ISD_ERR_UNSUPPORTED;
+  if (rows < 1 || n_mask < 0 || n_mask > rows || d_in < 1 || d_out < 1 || rank < 1) return ISD_ERR_SHAPE;
+  if (rank != 128 || d_in % 256 || d_out % 128) return ISD_ERR_UNSUPPORTED;
+  if ((n_mask + 31) / 32 > 65535) return ISD_ERR_UNSUPPORTED;
+  if (!(scale == scale)) return ISD_ERR_SHAPE;
+  if (!X || !A_t || !B_t || !Y || !workspace || (n_mask > 0 && !mask_rows)) return ISD_ERR_NULL;
+  if (!aligned16(X) || !aligned16(A_t) || !aligned16(B_t) || !aligned16(Y) || !aligned16(workspace))
+    return ISD_ERR_ALIGNMENT;
+  if (ws_bytes < lora_layout(n_mask, d_in, rank).total) return ISD_ERR_WORKSPACE;
+  hipError_t e = launch_lora(rows, d_in, d_out, rank, X, A_t, B_t, mask_rows, n_mask, scale, Y,
+                             static_cast<char*>(workspace), stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_lora_delta");
 }
 
 }  // extern "C"

@@ -92,6 +92,14 @@ hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_ne
 
 hipError_t launch_workspace_init(void* ws, size_t header_bytes, double* exp_table, hipStream_t stream);
 
+struct LoraLayout {
+  size_t part = 0;    // float [d_in/256][n_mask padded to 32][rank]
+  size_t t_hi = 0;    // bf16 [n_mask padded][rank]
+  size_t t_lo = 0;
+  size_t total = 0;
+};
+LoraLayout lora_layout(int32_t n_mask, int32_t d_in, int32_t rank);
+
 hipError_t launch_lora(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
                        const void* A, const void* Bm, const int32_t* mask_rows, int32_t n_mask,
                        float scale, void* Y, char* ws, hipStream_t stream);

@@ -92,13 +92,13 @@ class DeviceStep:
         del k_plain, v_plain
         if getattr(a, "lora_x", None) is not None:
             bf = torch.bfloat16
-            st.lora = dict(X=_t(a.lora_x, bf, device), A=_t(a.lora_a, bf, device),
-                           B=_t(a.lora_b, bf, device), Y=_t(a.lora_y, bf, device),
+            # linear-layer layouts: down weight [rank, d_in], up weight [d_out, rank]
+            st.lora = dict(X=_t(a.lora_x, bf, device), A_t=_t(np.ascontiguousarray(a.lora_a.T), bf, device),
+                           B_t=_t(np.ascontiguousarray(a.lora_b.T), bf, device), Y=_t(a.lora_y, bf, device),
                            mask_rows=_t(a.mask_rows, i32, device))
             n_mask = st.lora["mask_rows"].numel()
-            st.lora["ws"] = torch.zeros(
-                max(256, _lib.isd_lora_workspace_bytes(n_mask, st.lora["X"].shape[1], st.lora["A"].shape[1])),
-                dtype=torch.uint8, device=device)
+            nbytes = _lib.isd_lora_workspace_bytes(n_mask, st.lora["X"].shape[1], st.lora["A_t"].shape[0])
+            st.lora["ws"] = torch.zeros(max(256, nbytes), dtype=torch.uint8, device=device)
         return st
 
     def attention(self, stream=None):
@@ -119,7 +119,7 @@ class DeviceStep:
 
     def lora_delta(self, stream=None):
         L = self.lora
-        _lib.isd_lora_delta(L["X"], L["A"], L["B"], L["mask_rows"], L["Y"], L["ws"], stream=stream)
+        _lib.isd_lora_delta(L["X"], L["A_t"], L["B_t"], L["mask_rows"], L["Y"], L["ws"], stream=stream)
 
     def run(self, stream=None):
         """One ISD step: attention -> accept -> commit (-> LoRA delta)."""

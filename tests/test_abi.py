@@ -131,3 +131,25 @@ def test_layout_round_trip_cpu():
     assert kp[page, h, d // 8, slot, d % 8] == k[page, slot, h, d]
     sig = (slot & 3) | ((slot & 4) << 1) | ((slot & 8) >> 1)
     assert vp[page, h, d, sig] == v[page, slot, h, d]
+
+
+def test_lora_validation():
+    assert LIB.isd_lora_workspace_bytes(512, 4096, 128) > 0
+    assert LIB.isd_lora_workspace_bytes(512, 4000, 128) == 0
+    assert LIB.isd_lora_workspace_bytes(512, 4096, 64) == 0
+    n = LIB.isd_lora_workspace_bytes(512, 4096, 128)
+    ok = dict(rows=896, d_in=4096, d_out=4096, rank=128, X=FAKE, A=FAKE, B=FAKE, m=FAKE, n_mask=512,
+              scale=1.0, Y=FAKE, ws=FAKE, wsb=n)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return LIB.isd_lora_delta(a["rows"], a["d_in"], a["d_out"], a["rank"], a["X"], a["A"], a["B"], a["m"],
+                                  a["n_mask"], a["scale"], a["Y"], a["ws"], a["wsb"], None)
+    assert call(rank=64) == 5
+    assert call(d_in=4000) == 5
+    assert call(d_out=4000) == 5
+    assert call(n_mask=900) == 2
+    assert call(X=None) == 1
+    assert call(Y=MISALIGNED) == 7
+    assert call(wsb=100) == 4
+    assert call(scale=float("nan")) == 2
