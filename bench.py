@@ -32,6 +32,26 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 MALL_BYTES = 256 * 2 ** 20
 
 
+def measured_traffic(cfg_name):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None when there is none for this workload or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_bf16_hbm_traffic_{cfg_name}.md")
+    if not os.path.exists(path):
+        return None
+    want, traffic = None, None
+    for line in open(path):
+        if line.startswith("kernel_source_sha256:"):
+            want = line.split(":", 1)[1].strip()
+        elif line.startswith("traffic_bytes_per_launch"):
+            traffic = int(line.rsplit(":", 1)[1].strip())
+    h = hashlib.sha256()
+    for f in ("attention.hip", "device_common.hpp", "isd_internal.hpp"):
+        with open(os.path.join(ROOT, "introspective_strided_decoding_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return traffic if want == h.hexdigest() else None
+
+
 def algorithmic_bytes(wl):
     """Bytes each call must move at least once (inputs read once, outputs written once)."""
     cfg = wl.cfg
@@ -110,6 +130,9 @@ def main(argv=None):
     ap.add_argument("--config", default="c32_ctx4k")
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated in the timed loop (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB device copy before the timed loop (a known-size reference "
+                         "for hardware traffic counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -161,6 +184,13 @@ def main(argv=None):
         if use_lora:
             st.lora_delta()
 
+    if args.calibrate_copy:
+        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         one_step(steps[i % sets])
     torch.cuda.synchronize()
@@ -210,13 +240,13 @@ def main(argv=None):
         "step_hbm": {"bytes": int(total_bytes), "achieved_GBs": round(total_bytes / ms_per_step / 1e6, 1),
                      "frac": round(total_bytes / ms_per_step / 1e6 / HBM_PEAK_GBS, 4)},
         "roofline": {
-            "kernel": "isd_attention (split-KV MFMA kernel + combine)",
+            "kernel": "attn_bf16 (isd_attention: paged stride attention, one launch)",
             "bound": "hbm",
             "achieved": round(nbytes["attention"] / attn_ms / 1e6, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(nbytes["attention"] / attn_ms / 1e6 / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name),
             "bytes_per_launch": int(nbytes["attention"]),
             "avg_launch_ms": round(attn_ms, 5),
         },
