@@ -61,6 +61,15 @@ __device__ __forceinline__ int active_splits(int n_tiles, int n_splits, int tps)
   return max(1, min(n_splits, (n_tiles + tps - 1) / tps));
 }
 
+// KV pages are read exactly once per step: stream them past the caches.
+__device__ __forceinline__ u32x4 kv_load(const u32x4* p) {
+#if ISD_KV_NONTEMPORAL
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
 // Operand loads of one 32-token tile (pages pid0, pid1; both valid ids).
 // One base pointer per lane and page; the unrolled k-steps / dim blocks are
 // immediate offsets from it.
@@ -73,7 +82,7 @@ __device__ __forceinline__ void load_k(u32x4 (&k)[D / 16], const uint16_t* __res
   const u32x4* base = reinterpret_cast<const u32x4*>(
       kp + (size_t(pid) * Hkv + hk) * (D * kPage) + (h * kPage + (i & 15)) * 8);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) k[s] = base[s * 2 * kPage];
+  for (int s = 0; s < D / 16; ++s) k[s] = kv_load(base + s * 2 * kPage);
 }
 
 template <int D>
@@ -86,7 +95,7 @@ __device__ __forceinline__ void load_v(u32x4 (&v)[2][D / 32], const uint16_t* __
     const u32x4* base = reinterpret_cast<const u32x4*>(
         vp + (size_t(m ? pid1 : pid0) * Hkv + hk) * (D * kPage) + i * kPage + h * 8);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) v[m][db] = base[db * 32 * 2];
+    for (int db = 0; db < D / 32; ++db) v[m][db] = kv_load(base + db * 32 * 2);
   }
 }
 
@@ -198,8 +207,8 @@ __device__ __forceinline__ void combine_rk(const T* __restrict__ q, const T* __r
   }
 }
 
-template <int D, int RB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, 2))) void attn_bf16(
+template <int D, int RB, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, 2))) void attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out, int Qn, int Hq, int Hkv, int G,
@@ -210,8 +219,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
   constexpr int DB = D / 32;
   constexpr int COLS = RB * 32;
   constexpr int OSTR = D + 4;  // padded LDS row stride
-  __shared__ float sm_m[kAttnWaves][COLS];
-  __shared__ float sm_l[kAttnWaves][COLS];
+  __shared__ float sm_m[W][COLS];
+  __shared__ float sm_l[W][COLS];
   __shared__ __attribute__((aligned(16))) float sm_o0[COLS * OSTR];
   __shared__ __attribute__((aligned(16))) float sm_o1[COLS * OSTR];
   __shared__ __attribute__((aligned(16))) u32x4 sm_q[(D / 8) * COLS];
@@ -237,18 +246,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
   // split 0's wave 0 also takes the stride's own causal block as one extra tile
   const bool stride_tile = (split == 0) && (wave == 0);
 
-  auto pages = [&](int tt, int& p0, int& p1) {
-    p0 = page_id(trow, 2 * tt, num_pages, flags);
-    // second page past the context: reuse the first (its tokens are masked)
-    p1 = (tt * kTileTokens + kPage < L) ? page_id(trow, 2 * tt + 1, num_pages, flags) : p0;
-  };
-  // context tiles of this wave: t0 + wave + 4*i for i < n
+  // context tiles of this wave: first + W*i for i < n
   const int first = t0 + wave;
-  const int n = (first < t1) ? (t1 - first + kAttnWaves - 1) / kAttnWaves : 0;
+  const int n = (first < t1) ? (t1 - first + W - 1) / W : 0;
+  // Page ids of this wave's tiles live in one register, 32 tiles at a time:
+  // lane 2j+h holds the id of page h of tile j of the current chunk, so the
+  // loop reads them with readlane instead of a dependent memory load.
+  int pid_reg = 0, pid_chunk = -1;
+  auto load_chunk = [&](int chunk) {
+    const int j = chunk * 32 + (lane >> 1);
+    int pid = 0;
+    if (j < n) {
+      const int tt = first + W * j;
+      // second page past the context: reuse the first (its tokens are masked)
+      const int lp = ((lane & 1) && tt * kTileTokens + kPage < L) ? 2 * tt + 1 : 2 * tt;
+      pid = page_id(trow, lp, num_pages, flags);
+    }
+    pid_reg = pid;
+    pid_chunk = chunk;
+  };
+  auto pages_i = [&](int i, int& p0, int& p1) {   // i: index of the tile among this wave's tiles
+    if ((i >> 5) != pid_chunk) load_chunk(i >> 5);
+    p0 = __builtin_amdgcn_readlane(pid_reg, 2 * (i & 31));
+    p1 = __builtin_amdgcn_readlane(pid_reg, 2 * (i & 31) + 1);
+  };
   u32x4 ak[KS], av[2][DB], bk[KS], bv[2][DB];
   if (n > 0) {   // first tile's loads go out before the Q staging below
     int p0, p1;
-    pages(first, p0, p1);
+    pages_i(0, p0, p1);
     load_k<D>(ak, kp, p0, p1, hk, Hkv, lane);
     load_v<D>(av, vp, p0, p1, hk, Hkv, lane);
   }
@@ -395,20 +420,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
     int p0 = 0, p1 = 0;
     int i = 0;
     for (; i + 2 < n; i += 2) {
-      const int ta = first + i * kAttnWaves, tb = ta + kAttnWaves, tc = tb + kAttnWaves;
-      pages(tb, p0, p1);
+      const int ta = first + i * W, tb = ta + W;
+      pages_i(i + 1, p0, p1);
       load_k<D>(bk, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, ak, av, bv, ta, p0, p1);
-      pages(tc, p0, p1);
+      pages_i(i + 2, p0, p1);
       load_k<D>(ak, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, bk, bv, av, tb, p0, p1);
     }
-    const int ta = first + i * kAttnWaves;
+    const int ta = first + i * W;
     if (i + 1 < n) {
-      pages(ta + kAttnWaves, p0, p1);
+      pages_i(i + 1, p0, p1);
       load_k<D>(bk, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, ak, av, bv, ta, p0, p1);
-      tile(NoPre{}, bk, bv, av, ta + kAttnWaves, 0, 0);
+      tile(NoPre{}, bk, bv, av, ta + W, 0, 0);
     } else {
       tile(NoPre{}, ak, av, bv, ta, 0, 0);
     }
@@ -430,7 +455,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
     const int c = rb * 32 + col_l;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm_m[w][c]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][c]);
     wscale[rb] = (m_run[rb] == -INFINITY) ? 0.f : exp2f(m_run[rb] - M);
   }
   auto put = [&](float* buf, bool add) {
@@ -455,10 +480,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
     const int c = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm_m[w][c]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][c]);
     float Lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float mw = sm_m[w][c];
       if (mw != -INFINITY) Lsum += sm_l[w][c] * exp2f(mw - M);
     }
@@ -466,8 +491,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
     sm_ml[c][1] = Lsum;
   }
   __syncthreads();
-  if (wave >= 2) put(wave == 3 ? sm_o1 : sm_o0, true);
-  __syncthreads();
+#pragma unroll
+  for (int k = 1; k < W / 2; ++k) {
+    if (wave == 2 * k || wave == 2 * k + 1) put((wave & 1) ? sm_o1 : sm_o0, true);
+    __syncthreads();
+  }
 
   constexpr int V4 = D / 4;
   auto write_out = [&](int c, int d0, f32x4 v) {
@@ -503,19 +531,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
     for (int e = 0; e < 4; ++e) st_coherent(dst + e, a[e] + b[e]);
   }
   if (!arrive_last(&arrivals[rk], uint32_t(active), &s_last)) return;
+  // The partials were written through to memory before their writers
+  // arrived; drop any stale cached copies here, then read them plainly.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // per column: global max and the split weights (normaliser folded in)
   __shared__ float sm_w[COLS][kMaxSplits];
   const size_t base0 = size_t(rk) * n_splits * COLS;
   if (threadIdx.x < rows) {
     const int c = threadIdx.x;
     float M = -INFINITY;
-    for (int s = 0; s < active; ++s) M = fmaxf(M, ld_coherent(&ws_ml[base0 + size_t(s) * COLS + c].x));
+    for (int s = 0; s < active; ++s) M = fmaxf(M, ws_ml[base0 + size_t(s) * COLS + c].x);
     float Lsum = 0.f;
     for (int s = 0; s < active; ++s) {
-      const float ms = ld_coherent(&ws_ml[base0 + size_t(s) * COLS + c].x);
-      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      const float2 ml = ws_ml[base0 + size_t(s) * COLS + c];
+      const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
       sm_w[c][s] = w;
-      Lsum += w * ld_coherent(&ws_ml[base0 + size_t(s) * COLS + c].y);
+      Lsum += w * ml.y;
     }
     const float inv = 1.f / Lsum;
     for (int s = 0; s < active; ++s) sm_w[c][s] *= inv;
@@ -524,12 +555,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
   for (int idx = threadIdx.x; idx < rows * V4; idx += blockDim.x) {
     const int c = idx / V4, d0 = (idx % V4) * 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < active; ++s) {
-      const float* src = ws_o + (base0 + size_t(s) * COLS + c) * D + d0;
-      const float w = sm_w[c][s];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(ld_coherent(src + e), w, acc[e]);
-    }
+    for (int s = 0; s < active; ++s)
+      acc += *reinterpret_cast<const f32x4*>(ws_o + (base0 + size_t(s) * COLS + c) * D + d0) * sm_w[c][s];
     write_out(c, d0, acc);
   }
 }
@@ -627,11 +654,11 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
     const uint16_t* vp = static_cast<const uint16_t*>(v_pages);
     uint16_t* o = static_cast<uint16_t*>(out);
     if (p.row_blocks == 1)
-      hipLaunchKernelGGL((attn_bf16<D, 1>), dim3(nwg), dim3(256), 0, stream, qq, kn, vn, kp, vp, table,
+      hipLaunchKernelGGL((attn_bf16<D, 1, kAttnWaves1>), dim3(nwg), dim3(64 * kAttnWaves1), 0, stream, qq, kn, vn, kp, vp, table,
                          ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group, p.rows, s.max_pages,
                          s.num_pages, p.tiles_per_split, p.n_splits, scale_log2, ml, po, arrivals, flags);
     else
-      hipLaunchKernelGGL((attn_bf16<D, 2>), dim3(nwg), dim3(256), 0, stream, qq, kn, vn, kp, vp, table,
+      hipLaunchKernelGGL((attn_bf16<D, 2, kAttnWaves2>), dim3(nwg), dim3(64 * kAttnWaves2), 0, stream, qq, kn, vn, kp, vp, table,
                          ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group, p.rows, s.max_pages,
                          s.num_pages, p.tiles_per_split, p.n_splits, scale_log2, ml, po, arrivals, flags);
   } else {

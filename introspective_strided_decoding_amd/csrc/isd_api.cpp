@@ -11,8 +11,8 @@
 #include "isd.h"
 #include "isd_internal.hpp"
 
-// Workgroups the attention split aims for with one 32-column block (two per
-// CU on 256 CUs); half that with two blocks (one per CU).
+// Workgroups the attention aims for: one per CU on 256 CUs (each is 8 waves
+// with one 32-column block, or 4 waves with two).
 #ifndef ISD_ATTN_TARGET_WGS
 #define ISD_ATTN_TARGET_WGS 256
 #endif
@@ -73,14 +73,13 @@ AttnPlan plan_attention(const isd_shape& s) {
   const long long cap = (long long)s.max_pages * kPage;
   const long long hint = (s.max_ctx > 0) ? std::min<long long>(s.max_ctx, cap) : cap;
   p.tiles_max = std::max(1, ceil_div(hint, kTileTokens));
-  // Aim for one full round of resident workgroups (two per CU on 256 CUs with
-  // one 32-column block, one per CU with two) without giving a workgroup
-  // fewer than 8 tiles (two per wave) of work.
+  // Splits per (request, KV head): enough workgroups for one per CU, but no
+  // more (each extra split costs a partial and a merge).
   const long long pairs = (long long)s.batch * s.n_kv_heads;
-  const int target = (p.row_blocks == 1) ? ISD_ATTN_TARGET_WGS : ISD_ATTN_TARGET_WGS / 2;
+  const int target = ISD_ATTN_TARGET_WGS;
   int splits = std::max(1, ceil_div(target, pairs));
   p.tiles_per_split = std::max(8, ceil_div(p.tiles_max, splits));
-  // the combine kernel keeps one coefficient per split in LDS: at most 64 splits
+  // the final merge keeps one weight per split in LDS: at most 64 splits
   p.tiles_per_split = std::max(p.tiles_per_split, ceil_div(p.tiles_max, 64));
   p.n_splits = std::max(1, ceil_div(p.tiles_max, p.tiles_per_split));
   return p;

@@ -11,7 +11,16 @@ namespace isd {
 
 constexpr int kPage = 16;          // tokens per KV page
 constexpr int kTileTokens = 32;    // tokens per attention tile (two pages)
-constexpr int kAttnWaves = 4;      // waves per attention workgroup
+// Waves per attention workgroup: eight with one 32-column block (two waves
+// per SIMD), four with two blocks (their registers allow one wave per SIMD).
+#ifndef ISD_ATTN_WAVES1
+#define ISD_ATTN_WAVES1 8
+#endif
+constexpr int kAttnWaves1 = ISD_ATTN_WAVES1;
+constexpr int kAttnWaves2 = 4;
+#ifndef ISD_KV_NONTEMPORAL
+#define ISD_KV_NONTEMPORAL 1
+#endif
 constexpr size_t kHeaderBytes = 256;
 
 // How the KV walk of isd_attention is split across workgroups.
