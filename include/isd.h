@@ -78,7 +78,8 @@ typedef enum isd_dtype {
 /*
  * Sizes of one step.
  *   Q = 2 * stride_n - 1 query rows per request; G = n_q_heads / n_kv_heads.
- *   Supported: stride_n >= 2, head_dim in {64, 128}, page_size == 16,
+ *   Supported: 1 <= batch <= 65535, stride_n in [2, 32], head_dim in {64, 128},
+ *   page_size == 16,
  *   G * Q <= 64 (query rows per KV head), n_q_heads % n_kv_heads == 0.
  *   max_ctx is a hint (an upper bound of the context lengths, used to split
  *   the KV walk across workgroups); 0 means max_pages * page_size.  A context

@@ -1,11 +1,13 @@
 // p/q acceptance with residual resampling (isd_accept).
 //
 // Kernels, in stream order:
-//   lse_partial    one read of every p and q row: per (row, vocab shard) the
-//                  max and the sum of exp(l - max), fp32, 16-byte vector loads,
-//                  wave reductions by lane exchange, then across the 4 waves.
-//   accept_decide  one wave per request: combine the shard partials into the
-//                  row log-normalisers, gather log p / log q at the proposals,
+//   lse_partial    one read of every p and q row: per (row, vocabulary shard)
+//                  the max and the sum of exp(l - max), fp32, 16-byte
+//                  streaming loads, wave reductions by lane exchange, then
+//                  across the 4 waves.
+//   accept_decide  one workgroup per request: its waves combine the shard
+//                  partials of the request's rows into log-normalisers while
+//                  the first wave already holds the logits at the proposals;
 //                  rho = exp(log p - log q), Philox uniforms, accept iff
 //                  u < rho, first rejection by a wave ballot.
 //   resid_lse64    rejecting requests only: fp64 (max, sum exp) of the
@@ -16,7 +18,10 @@
 //                  shard holding u' * S, a workgroup scan inside that shard in
 //                  vocabulary order picks y*.
 // The residual runs in fp64 so the inverse CDF agrees with a float64
-// reference up to rounding of the running sums.
+// reference up to rounding of the running sums.  The decision lists the
+// rejecting requests compactly (an atomic counter the normaliser kernel
+// rewinds), so the residual workgroups that have work are the first ones
+// dispatched; the rest return after reading the count.
 #include <climits>
 
 #include "device_common.hpp"
@@ -48,13 +53,6 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2)
   else s += s2 * __expf(m2 - m);
 }
 
-__device__ __forceinline__ float row_lse(const float2* part, int shards, float& row_max) {
-  float M = -INFINITY, S = 0.f;
-  for (int i = 0; i < shards; ++i) ms_merge(M, S, part[i].x, part[i].y);
-  row_max = M;
-  return M + __logf(S);
-}
-
 // Everything the accept decision reads and writes.
 template <typename T>
 struct DecideArgs {
@@ -65,102 +63,32 @@ struct DecideArgs {
   const int32_t* positions;
   uint64_t seed_lo, seed_hi;
   uint32_t step;
-  int B, N, V, shards;
-  const float2* part;
+  int N, V, shards;
   int32_t *accept_len, *out_tokens, *n_out, *n_commit;
   float *logp_sel, *logq_sel;
-  ReqState* state;
+  ReqState* jobs;          // compact list of rejecting requests
+  uint32_t* rej_count;     // its length
   uint32_t* flags;
-  uint32_t* rej_count;
-  int32_t* rej_list;
   int bf16_logits;
 };
-
-// The accept decision of request r, taken by one wave (lane j < N-1 tests
-// x_{j+2}; a ballot finds the first rejection).
-template <typename T>
-__device__ __forceinline__ void decide_request(const DecideArgs<T>& a, int r) {
-  const T* __restrict__ p_logits = a.p_logits;
-  const T* __restrict__ q_logits = a.q_logits;
-  const int32_t* __restrict__ proposals = a.proposals;
-  const float2* __restrict__ part = a.part;
-  const int N = a.N, V = a.V, B = a.B, shards = a.shards;
-  uint32_t* flags = a.flags;
-  const int lane = threadIdx.x & 63;
-  const int R = N - 1;
-  const int bf16_logits = a.bf16_logits;
-  bool reject = false;
-  bool table_ok = false;
-  double u_res = 0.0;
-  if (lane < R) {
-    const int j = lane;
-    const int rp = r * R + j;                  // p row index
-    const int rq = B * R + r * R + j;          // q row index (after all p rows)
-    float max_p, max_q;
-    const float lse_p = row_lse(part + size_t(rp) * shards, shards, max_p);
-    const float lse_q = row_lse(part + size_t(rq) * shards, shards, max_q);
-    // exp(x) of every logit of both rows is finite and their sums cannot overflow
-    table_ok = bf16_logits && fabsf(max_p) < 600.f && fabsf(max_q) < 600.f;
-    const int x = proposals[size_t(r) * N + j + 1];
-    float lp, lq;
-    if (x < 0 || x >= V) {
-      raise_flag(flags, ISD_FLAG_TOKEN_RANGE);
-      lp = -INFINITY;
-      lq = 0.f;
-    } else {
-      lp = to_f32<T>(p_logits[size_t(rp) * V + x]) - lse_p;
-      lq = to_f32<T>(q_logits[size_t(r * R + j) * V + x]) - lse_q;
-    }
-    a.logp_sel[size_t(r) * R + j] = lp;
-    a.logq_sel[size_t(r) * R + j] = lq;
-    const float rho = __expf(lp - lq);
-    const uint64_t rid = uint64_t(uint32_t(a.req_ids[r]));
-    const uint64_t pos = uint64_t(uint32_t(a.positions[r])) + uint64_t(j + 1);
-    const Philox4x64Out w = philox4x64_10(rid, pos, uint64_t(a.step), 0, a.seed_lo, a.seed_hi);
-    const double u = unit_double(w.w[0]);
-    u_res = unit_double(w.w[1]);
-    reject = !(u < double(rho));
-  }
-  const uint64_t mask = __ballot(reject);
-  const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
-  const int A = (first < 0) ? N : first + 1;
-  const double u_first = __shfl(u_res, first < 0 ? 0 : first);
-  const int tab_first = __shfl(int(table_ok), first < 0 ? 0 : first);
-  if (lane < N) {
-    const int x = proposals[size_t(r) * N + lane];
-    a.out_tokens[size_t(r) * N + lane] = (lane < A) ? x : -1;
-  }
-  if (lane == 0) {
-    a.accept_len[r] = A;
-    a.n_out[r] = A + (A < N ? 1 : 0);
-    a.n_commit[r] = min(A, N - 1);
-    ReqState st;
-    st.accept_len = A;
-    st.reject_row = first;
-    st.table_ok = tab_first;
-    st.pad1 = 0;
-    st.u_resample = u_first;
-    st.pad2 = 0.0;
-    a.state[r] = st;
-    if (first >= 0) a.rej_list[atomicAdd(a.rej_count, 1u)] = r;
-  }
-}
 
 // A shard holds at most kThreads * kLseVec vectors, so every thread issues all
 // of its 16-byte loads before it waits on any of them.
 constexpr int kLseVec = 8;
 
+// Grid (2(N-1) * shards, B): workgroup (jj * shards + sh, r) reduces shard sh
+// of row jj of request r, where rows jj < N-1 are p rows and the rest q rows;
+// its partial lands at part[(r * 2(N-1) + jj) * shards + sh].
 template <typename T>
-__global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int rows_half, int shard_len,
+__global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int shard_len,
                                                         float2* __restrict__ part) {
   constexpr int VN = Vec<T>::N;
-  const T* __restrict__ p_logits = args.p_logits;
-  const T* __restrict__ q_logits = args.q_logits;
-  const int V = args.V, shards = args.shards;
-  const int sh = blockIdx.x;
-  const int row = blockIdx.y;
-  const size_t row_off = size_t(row < rows_half ? row : row - rows_half) * V;
-  const T* base = (row < rows_half ? p_logits : q_logits) + row_off;
+  const int V = args.V, shards = args.shards, R = args.N - 1;
+  const int r = blockIdx.y;
+  const int jj = blockIdx.x / shards, sh = blockIdx.x % shards;
+  const bool is_q = jj >= R;
+  const size_t row_off = (size_t(r) * R + (is_q ? jj - R : jj)) * V;
+  const T* base = (is_q ? args.q_logits : args.p_logits) + row_off;
   const int e0 = sh * shard_len;
   const int e1 = min(V, e0 + shard_len);
   float m = -INFINITY, s = 0.f;
@@ -175,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
 #pragma unroll
     for (int k = 0; k < kLseVec; ++k) {
       const int v = threadIdx.x + k * kThreads;
-      raw[k] = (v < nvec) ? vb[v] : u32x4{0, 0, 0, 0};
+      raw[k] = (v < nvec) ? __builtin_nontemporal_load(vb + v) : u32x4{0, 0, 0, 0};
     }
     float tail = -INFINITY;
     bool has_tail = false;
@@ -224,21 +152,105 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
   if (threadIdx.x == 0) {
     float M = -INFINITY, S = 0.f;
     for (int w = 0; w < kThreads / 64; ++w) ms_merge(M, S, sm[w][0], sm[w][1]);
-    part[size_t(row) * shards + sh] = make_float2(M, S);
+    part[(size_t(r) * 2 * R + jj) * shards + sh] = make_float2(M, S);
+    // the decision kernel, next in the stream, lists rejecting requests from zero
+    if (blockIdx.x == 0 && blockIdx.y == 0) *args.rej_count = 0u;
   }
 }
 
-// One wave per request: the accept decision.
+// One workgroup per request.  Lane j < N-1 of wave 0 tests x_{j+2} against
+// p row j and q row j; a ballot finds the first rejection.
 template <typename T>
-__global__ __launch_bounds__(64) void accept_decide(DecideArgs<T> args) {
-  decide_request<T>(args, blockIdx.x);
+__global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const float2* __restrict__ part) {
+  const int r = blockIdx.x;
+  const int N = a.N, V = a.V, R = N - 1, shards = a.shards;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float lse_sm[64], max_sm[64];
+  // wave 0: the proposals and the logits at them, requested before the combine
+  int x = 0;
+  float raw_p = 0.f, raw_q = 0.f;
+  bool in_range = false;
+  if (wave == 0 && lane < R) {
+    x = a.proposals[size_t(r) * N + lane + 1];
+    in_range = x >= 0 && x < V;
+    if (in_range) {
+      const size_t row = size_t(r) * R + lane;
+      raw_p = to_f32<T>(a.p_logits[row * V + x]);
+      raw_q = to_f32<T>(a.q_logits[row * V + x]);
+    }
+  }
+  // every wave: rows wave, wave + 4, ... of the request's 2(N-1) rows
+  const float2* req_part = part + size_t(r) * 2 * R * shards;
+  for (int row = wave; row < 2 * R; row += kThreads / 64) {
+    float rm = -INFINITY, rs = 0.f;
+    for (int i = lane; i < shards; i += 64) {
+      const float2 v = req_part[size_t(row) * shards + i];
+      ms_merge(rm, rs, v.x, v.y);
+    }
+    const float M = wave_max(rm);
+    const float S = wave_sum((rm == -INFINITY) ? 0.f : rs * __expf(rm - M));
+    if (lane == 0) { lse_sm[row] = M + __logf(S); max_sm[row] = M; }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  bool reject = false;
+  bool table_ok = false;
+  double u_res = 0.0;
+  if (lane < R) {
+    const int j = lane;
+    const size_t row = size_t(r) * R + j;
+    // exp(x) of every logit of both rows is finite and their sums cannot overflow
+    table_ok = a.bf16_logits && fabsf(max_sm[j]) < 600.f && fabsf(max_sm[R + j]) < 600.f;
+    float lp, lq;
+    if (!in_range) {
+      raise_flag(a.flags, ISD_FLAG_TOKEN_RANGE);
+      lp = -INFINITY;
+      lq = 0.f;
+    } else {
+      lp = raw_p - lse_sm[j];
+      lq = raw_q - lse_sm[R + j];
+    }
+    a.logp_sel[row] = lp;
+    a.logq_sel[row] = lq;
+    const float rho = __expf(lp - lq);
+    const uint64_t rid = uint64_t(uint32_t(a.req_ids[r]));
+    const uint64_t pos = uint64_t(uint32_t(a.positions[r])) + uint64_t(j + 1);
+    const Philox4x64Out w = philox4x64_10(rid, pos, uint64_t(a.step), 0, a.seed_lo, a.seed_hi);
+    const double u = unit_double(w.w[0]);
+    u_res = unit_double(w.w[1]);
+    reject = !(u < double(rho));
+  }
+  const uint64_t mask = __ballot(reject);
+  const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
+  const int A = (first < 0) ? N : first + 1;
+  const double u_first = __shfl(u_res, first < 0 ? 0 : first);
+  const int tab_first = __shfl(int(table_ok), first < 0 ? 0 : first);
+  if (lane < N) {
+    const int xl = a.proposals[size_t(r) * N + lane];
+    a.out_tokens[size_t(r) * N + lane] = (lane < A) ? xl : -1;
+  }
+  if (lane == 0) {
+    a.accept_len[r] = A;
+    a.n_out[r] = A + (A < N ? 1 : 0);
+    a.n_commit[r] = min(A, N - 1);
+    if (first >= 0) {
+      ReqState st;
+      st.req = r;
+      st.accept_len = A;
+      st.reject_row = first;
+      st.table_ok = tab_first;
+      st.u_resample = u_first;
+      st.pad = 0.0;
+      a.jobs[atomicAdd(a.rej_count, 1u)] = st;
+    }
+  }
 }
 
 // ---- fp64 residual ----
-// Only requests that rejected a proposal take part; the decision kernel
-// lists them compactly, and residual workgroup (shard, k) serves the k-th
-// listed request.  A residual shard is 2048 vocabulary entries: 256 threads x
-// 8 consecutive entries.
+// Residual workgroup (shard, k) serves the k-th listed rejecting request; it
+// requests its list entry together with the count (the selection kernel also
+// its normaliser partials).  A residual shard is 2048 vocabulary entries:
+// 256 threads x 8 consecutive entries.
 //
 // exp in float64: for bf16 logits whose row maxima lie in (-600, 600), exp(x)
 // is read from a table holding exp() of every bf16 bit pattern, so
@@ -283,8 +295,9 @@ __device__ __forceinline__ void block_ms_d(double& m, double& s, double* sm) {
   s = S;
 }
 
-// Row log-normalisers of the rejected p and q rows from the shard partials;
-// called by every lane of a wave, all lanes receive the result.
+// Row log-normalisers of the k-th listed request's rejected p and q rows from
+// the shard partials; called by every lane of a wave, all lanes receive the
+// result.
 __device__ __forceinline__ void wave_lse64(const double2* __restrict__ lse64, int k, int r_shards,
                                            double& lse_p, double& lse_q) {
   const int lane = threadIdx.x & 63;
@@ -320,17 +333,15 @@ __device__ __forceinline__ double exp_tab(const double* __restrict__ tab, float 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void resid_lse64(const T* __restrict__ p_logits,
                                                          const T* __restrict__ q_logits, int N, int V,
-                                                         int r_shards, const ReqState* __restrict__ state,
+                                                         int r_shards, const ReqState* __restrict__ jobs,
                                                          const uint32_t* __restrict__ rej_count,
-                                                         const int32_t* __restrict__ rej_list,
                                                          const double* __restrict__ tab,
                                                          double2* __restrict__ lse64) {
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
+  const ReqState st = jobs[k];
   if (k >= int(*rej_count)) return;
-  const int r = rej_list[k];
-  const ReqState st = state[r];
-  const size_t row = size_t(r) * (N - 1) + st.reject_row;
+  const size_t row = size_t(st.req) * (N - 1) + st.reject_row;
   const int e1 = min(V, (sh + 1) * kRShard);
   const int e0 = sh * kRShard + threadIdx.x * kRPer;
   float xp[kRPer], xq[kRPer];
@@ -399,26 +410,59 @@ __device__ __forceinline__ double wave_exclusive_d(double x, double& total) {
   return incl - x;
 }
 
-// Inverse-CDF draw for the k-th listed request, by a whole workgroup: a
-// wave-wide prefix over the shard masses picks the shard holding u' * S, a
-// scan inside that shard in vocabulary order picks y*.
 template <typename T>
-__device__ __forceinline__ void select_request(const T* __restrict__ p_logits,
-                                               const T* __restrict__ q_logits, int N, int V,
-                                               int r_shards, const ReqState* __restrict__ state,
-                                               const int32_t* __restrict__ rej_list,
-                                               const double* __restrict__ tab,
-                                               const double2* __restrict__ lse64,
-                                               const double2* __restrict__ mass,
-                                               int32_t* __restrict__ out_tokens, int k) {
-  const int r = rej_list[k];
-  const ReqState st = state[r];
+__global__ __launch_bounds__(kThreads) void resid_mass64(const T* __restrict__ p_logits,
+                                                          const T* __restrict__ q_logits, int N, int V,
+                                                          int r_shards, const ReqState* __restrict__ jobs,
+                                                          const uint32_t* __restrict__ rej_count,
+                                                          const double* __restrict__ tab,
+                                                          const double2* __restrict__ lse64,
+                                                          double2* __restrict__ mass) {
+  const int sh = blockIdx.x;
+  const int k = blockIdx.y;
+  const ReqState st = jobs[k];
+  if (k >= int(*rej_count)) return;
+  const size_t row = size_t(st.req) * (N - 1) + st.reject_row;
+  const int e1 = min(V, (sh + 1) * kRShard);
+  const int e0 = sh * kRShard + threadIdx.x * kRPer;
+  float xp[kRPer], xq[kRPer];
+  load_run<T>(p_logits + row * V, e0, e1, xp);
+  load_run<T>(q_logits + row * V, e0, e1, xq);
+  double lse_p, lse_q;
+  wave_lse64(lse64, k, r_shards, lse_p, lse_q);
+  double rv[kRPer], pv[kRPer];
+  resid_values(xp, xq, st.table_ok, tab, lse_p, lse_q, rv, pv);
+  double rs = 0.0, ps = 0.0;
+#pragma unroll
+  for (int i = 0; i < kRPer; ++i) { rs += rv[i]; ps += pv[i]; }
+  __shared__ double sm[kThreads / 64];
+  rs = block_sum_d(rs, sm);
+  ps = block_sum_d(ps, sm);
+  if (threadIdx.x == 0) mass[size_t(k) * r_shards + sh] = make_double2(rs, ps);
+}
+
+// One workgroup per listed request: the inverse-CDF draw.  A wave-wide prefix over
+// the shard masses picks the shard holding u' * S, a scan inside that shard
+// in vocabulary order picks y*.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p_logits,
+                                                          const T* __restrict__ q_logits, int N, int V,
+                                                          int r_shards, const ReqState* __restrict__ jobs,
+                                                          const uint32_t* __restrict__ rej_count,
+                                                          const double* __restrict__ tab,
+                                                          const double2* __restrict__ lse64,
+                                                          const double2* __restrict__ mass,
+                                                          int32_t* __restrict__ out_tokens) {
+  const int k = blockIdx.x;
+  const ReqState st = jobs[k];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ double before_sm, target_sm;
   __shared__ int shard_sm, fb_sm, found_sm, last_sm;
   __shared__ double wsum[kThreads / 64];
   double lse_p, lse_q;
   wave_lse64(lse64, k, r_shards, lse_p, lse_q);
+  if (k >= int(*rej_count)) return;
+  const int r = st.req;
   if (wave == 0) {
     // shard masses in vocabulary order: lane l owns shards [l*per, (l+1)*per)
     const int per = (r_shards + 63) / 64;
@@ -504,66 +548,6 @@ __device__ __forceinline__ void select_request(const T* __restrict__ p_logits,
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void resid_mass64(const T* __restrict__ p_logits,
-                                                          const T* __restrict__ q_logits, int N, int V,
-                                                          int r_shards, const ReqState* __restrict__ state,
-                                                          const uint32_t* __restrict__ rej_count,
-                                                          const int32_t* __restrict__ rej_list,
-                                                          const double* __restrict__ tab,
-                                                          const double2* __restrict__ lse64,
-                                                          double2* __restrict__ mass) {
-  const int sh = blockIdx.x;
-  const int k = blockIdx.y;
-  if (k >= int(*rej_count)) return;
-  const int r = rej_list[k];
-  const ReqState st = state[r];
-  const size_t row = size_t(r) * (N - 1) + st.reject_row;
-  const int e1 = min(V, (sh + 1) * kRShard);
-  const int e0 = sh * kRShard + threadIdx.x * kRPer;
-  float xp[kRPer], xq[kRPer];
-  load_run<T>(p_logits + row * V, e0, e1, xp);
-  load_run<T>(q_logits + row * V, e0, e1, xq);
-  double lse_p, lse_q;
-  wave_lse64(lse64, k, r_shards, lse_p, lse_q);
-  double rv[kRPer], pv[kRPer];
-  resid_values(xp, xq, st.table_ok, tab, lse_p, lse_q, rv, pv);
-  double rs = 0.0, ps = 0.0;
-#pragma unroll
-  for (int i = 0; i < kRPer; ++i) { rs += rv[i]; ps += pv[i]; }
-  __shared__ double sm[kThreads / 64];
-  rs = block_sum_d(rs, sm);
-  ps = block_sum_d(ps, sm);
-  if (threadIdx.x == 0) mass[size_t(k) * r_shards + sh] = make_double2(rs, ps);
-}
-
-// One workgroup per listed request: the token draw.  The last workgroup of
-// the grid to finish empties the list for the next call.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p_logits,
-                                                          const T* __restrict__ q_logits, int N, int V,
-                                                          int r_shards, const ReqState* __restrict__ state,
-                                                          uint32_t* __restrict__ rej_count,
-                                                          const int32_t* __restrict__ rej_list,
-                                                          const double* __restrict__ tab,
-                                                          const double2* __restrict__ lse64,
-                                                          const double2* __restrict__ mass,
-                                                          uint32_t* __restrict__ done_count,
-                                                          int32_t* __restrict__ out_tokens) {
-  const int k = blockIdx.x;
-  const int count = int(*rej_count);
-  if (k >= count) return;
-  select_request<T>(p_logits, q_logits, N, V, r_shards, state, rej_list, tab, lse64, mass, out_tokens, k);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(done_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == uint32_t(count - 1)) {
-      st_coherent(done_count, 0u);
-      st_coherent(rej_count, 0u);
-    }
-  }
-}
-
-template <typename T>
 hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, const void* ql,
                     const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
                     uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
@@ -572,14 +556,11 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   const T* P = static_cast<const T*>(pl);
   const T* Qp = static_cast<const T*>(ql);
   const int N = s.stride_n, V = s.vocab, B = s.batch;
-  uint32_t* flags = reinterpret_cast<uint32_t*>(ws + L.flags);
   float2* part = reinterpret_cast<float2*>(ws + L.lse);
-  ReqState* st = reinterpret_cast<ReqState*>(ws + L.req);
+  ReqState* jobs = reinterpret_cast<ReqState*>(ws + L.jobs);
+  uint32_t* rej_count = reinterpret_cast<uint32_t*>(ws + kRejCountOffset);
   double2* l64 = reinterpret_cast<double2*>(ws + L.lse64);
   double2* mass = reinterpret_cast<double2*>(ws + L.mass);
-  uint32_t* rej_count = reinterpret_cast<uint32_t*>(ws + kRejCountOffset);
-  uint32_t* done_count = reinterpret_cast<uint32_t*>(ws + kResidDoneOffset);
-  int32_t* rej_list = reinterpret_cast<int32_t*>(ws + L.rej_list);
   const double* tab = reinterpret_cast<const double*>(ws + L.exp_table);
   DecideArgs<T> a;
   a.p_logits = P;
@@ -590,31 +571,28 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.seed_lo = seed_lo;
   a.seed_hi = seed_hi;
   a.step = step;
-  a.B = B;
   a.N = N;
   a.V = V;
   a.shards = p.shards;
-  a.part = part;
   a.accept_len = accept_len;
   a.out_tokens = out_tokens;
   a.n_out = n_out;
   a.n_commit = n_commit;
   a.logp_sel = logp_sel;
   a.logq_sel = logq_sel;
-  a.state = st;
-  a.flags = flags;
+  a.jobs = jobs;
   a.rej_count = rej_count;
-  a.rej_list = rej_list;
+  a.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
   a.bf16_logits = (s.logit_dtype == ISD_BF16) ? 1 : 0;
-  hipLaunchKernelGGL((lse_partial<T>), dim3(p.shards, p.rows), dim3(kThreads), 0, stream, a, B * (N - 1),
+  hipLaunchKernelGGL((lse_partial<T>), dim3(2 * (N - 1) * p.shards, B), dim3(kThreads), 0, stream, a,
                      p.shard_len, part);
-  hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
   hipLaunchKernelGGL((resid_lse64<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shards, st, rej_count, rej_list, tab, l64);
+                     p.r_shards, jobs, rej_count, tab, l64);
   hipLaunchKernelGGL((resid_mass64<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shards, st, rej_count, rej_list, tab, l64, mass);
-  hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, st,
-                     rej_count, rej_list, tab, l64, mass, done_count, out_tokens);
+                     p.r_shards, jobs, rej_count, tab, l64, mass);
+  hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,
+                     rej_count, tab, l64, mass, out_tokens);
   return hipGetLastError();
 }
 

@@ -1,11 +1,12 @@
 // Appending accepted CLEAN rows to the KV pages (kv_commit) and the
 // workspace header fill.
 //
-// One workgroup per request: it reads the request's length once, copies
-// n_commit rows of k_new / v_new into their page slots (16-byte stores into
-// the key layout, element stores into the transposed value layout), and only
-// after a barrier writes the new length, so ctx_lens_out may alias
-// ctx_lens_in.
+// One workgroup per (request, CLEAN row i).  It requests the row's key and
+// value vectors before the request's length and page id arrive, stores them
+// if i < n_commit and the pages of rows 0..i are mapped (16-byte stores into
+// the key layout, element stores into the transposed value layout), and
+// counts its arrival; the request's last arrival writes the new length, so
+// ctx_lens_out may alias ctx_lens_in.
 #include "device_common.hpp"
 #include "isd_internal.hpp"
 
@@ -14,82 +15,95 @@ namespace {
 
 __device__ __forceinline__ int v_sigma(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
+constexpr int kCommitThreads = 256;
+constexpr int kCommitPre = 2;   // 16-byte vectors per thread requested up front
+
+// Page id of committed row t of request r (position L + t); -1 when the
+// position is past the table, -2 when the table entry is not a pool page.
+__device__ __forceinline__ int commit_page(const int32_t* __restrict__ table, int r, int L, int t,
+                                           int max_pages, int num_pages) {
+  const int pos = L + t;
+  if (pos >= max_pages * kPage) return -1;
+  const int pid = table[size_t(r) * max_pages + pos / kPage];
+  return (pid < 0 || pid >= num_pages) ? -2 : pid;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void kv_commit_kernel(
+__device__ __forceinline__ void commit_store(int w, int rvec, int D, int Hkv, int pid, int slot,
+                                             const u32x4& v, T* __restrict__ kp, T* __restrict__ vp) {
+  constexpr int EV = 16 / sizeof(T);
+  if (w < rvec) {
+    const int e0 = w * EV, hk = e0 / D, d0 = e0 % D;
+    T* dst = kp + ((size_t(pid) * Hkv + hk) * (D / 8) + d0 / 8) * (kPage * 8) + slot * 8 + (d0 & 7);
+    *reinterpret_cast<u32x4*>(dst) = v;
+  } else {
+    const int e0 = (w - rvec) * EV, hk = e0 / D, d0 = e0 % D;
+    T* dst = vp + ((size_t(pid) * Hkv + hk) * D + d0) * kPage + v_sigma(slot);
+    T x[EV];
+    __builtin_memcpy(x, &v, 16);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) dst[e * kPage] = x[e];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
     const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ kp, T* __restrict__ vp,
     const int32_t* __restrict__ table, const int32_t* ctx_in, const int32_t* __restrict__ n_commit,
-    int32_t* ctx_out, int N, int Hkv, int D, int max_pages, int num_pages, uint32_t* __restrict__ flags) {
-  __shared__ int pid_sm[64];
-  __shared__ int L_sm, n_sm, nv_sm;
-  const int r = blockIdx.x;
-  const int Qn = 2 * N - 1;
+    int32_t* ctx_out, int N, int Hkv, int D, int max_pages, int num_pages, uint32_t* __restrict__ flags,
+    uint32_t* __restrict__ arrivals) {
+  constexpr int EV = 16 / sizeof(T);
+  __shared__ int s_last;
+  const int i = blockIdx.x, r = blockIdx.y;
+  const int R = N - 1, Qn = 2 * N - 1;
+  const int rvec = Hkv * D / EV;                 // 16-byte vectors per key (or value) row
+  const size_t row_off = (size_t(r) * Qn + i) * Hkv * D;
+  const u32x4* ksrc = reinterpret_cast<const u32x4*>(k_new + row_off);
+  const u32x4* vsrc = reinterpret_cast<const u32x4*>(v_new + row_off);
+  u32x4 pre[kCommitPre];
+#pragma unroll
+  for (int m = 0; m < kCommitPre; ++m) {
+    const int w = threadIdx.x + m * kCommitThreads;
+    if (w < 2 * rvec) pre[m] = (w < rvec) ? ksrc[w] : vsrc[w - rvec];
+  }
   const int cap = max_pages * kPage;
-  if (threadIdx.x == 0) {
-    int L = ctx_in[r];
-    int n = n_commit[r];
-    if (n < 0 || n > N - 1) {
-      raise_flag(flags, ISD_FLAG_COMMIT_RANGE);
-      n = n < 0 ? 0 : N - 1;
-    }
-    if (L < 0 || L > cap) {
-      raise_flag(flags, ISD_FLAG_CTX_RANGE);
-      L = L < 0 ? 0 : cap;
-      n = 0;
-    }
-    L_sm = L;
-    n_sm = n;
+  int L = ctx_in[r], n = n_commit[r];
+  const bool bad_n = n < 0 || n > R, bad_L = L < 0 || L > cap;
+  if (bad_n) n = n < 0 ? 0 : R;
+  if (bad_L) { L = L < 0 ? 0 : cap; n = 0; }
+  // rows 0..i must all be mapped for row i to be stored
+  bool store = i < n;
+  if (store) {
+    const int lane = threadIdx.x & 63;
+    const int pid_t = (lane <= i) ? commit_page(table, r, L, lane, max_pages, num_pages) : 0;
+    const uint64_t bad = __ballot(pid_t < 0);
+    store = (bad == 0);
   }
-  __syncthreads();
-  const int L = L_sm, n = n_sm;
-  // page of every committed row, resolved in parallel
-  if (threadIdx.x < n) {
-    const int pos = L + threadIdx.x;
-    int pid = -1;
-    if (pos < cap) {
-      pid = table[size_t(r) * max_pages + pos / kPage];
-      if (pid < 0 || pid >= num_pages) pid = -2;
-    }
-    pid_sm[threadIdx.x] = pid;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int nv = n;
-    for (int i = 0; i < n; ++i)
-      if (pid_sm[i] < 0) {
-        raise_flag(flags, pid_sm[i] == -1 ? ISD_FLAG_COMMIT_RANGE : ISD_FLAG_PAGE_RANGE);
-        nv = i;
-        break;
-      }
-    nv_sm = nv;
-  }
-  __syncthreads();
-  const int nv = nv_sm;
-  constexpr int EV = 16 / sizeof(T);            // elements per 16-byte vector
-  const int kvec = D / EV;                       // 16-byte vectors per key row
-  const int kwork = nv * Hkv * kvec;
-  for (int w = threadIdx.x; w < kwork; w += blockDim.x) {
-    const int c = w % kvec;
-    const int hk = (w / kvec) % Hkv;
-    const int i = w / (kvec * Hkv);
-    const int pid = pid_sm[i];
+  if (store) {
+    const int pid = commit_page(table, r, L, i, max_pages, num_pages);
     const int slot = (L + i) % kPage;
-    const int d0 = c * EV;
-    const T* src = k_new + ((size_t(r) * Qn + i) * Hkv + hk) * D + d0;
-    T* dst = kp + ((size_t(pid) * Hkv + hk) * (D / 8) + d0 / 8) * (kPage * 8) + slot * 8 + (d0 & 7);
-    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+    for (int m = 0; m < kCommitPre; ++m) {
+      const int w = threadIdx.x + m * kCommitThreads;
+      if (w < 2 * rvec) commit_store<T>(w, rvec, D, Hkv, pid, slot, pre[m], kp, vp);
+    }
+    for (int w = threadIdx.x + kCommitPre * kCommitThreads; w < 2 * rvec; w += kCommitThreads)
+      commit_store<T>(w, rvec, D, Hkv, pid, slot, (w < rvec) ? ksrc[w] : vsrc[w - rvec], kp, vp);
   }
-  const int vwork = nv * Hkv * D;
-  for (int w = threadIdx.x; w < vwork; w += blockDim.x) {
-    const int d = w % D;
-    const int hk = (w / D) % Hkv;
-    const int i = w / (D * Hkv);
-    const int pid = pid_sm[i];
-    const int slot = (L + i) % kPage;
-    vp[((size_t(pid) * Hkv + hk) * D + d) * kPage + v_sigma(slot)] =
-        v_new[((size_t(r) * Qn + i) * Hkv + hk) * D + d];
+  if (!arrive_last(&arrivals[r], uint32_t(R), &s_last)) return;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int pid_t = (lane < n) ? commit_page(table, r, L, lane, max_pages, num_pages) : 0;
+    const uint64_t bad = __ballot(pid_t < 0);
+    const int nv = bad ? (__ffsll((unsigned long long)bad) - 1) : n;
+    const int first_bad = __shfl(pid_t, bad ? nv : 0);
+    if (lane == 0) {
+      if (bad_n) raise_flag(flags, ISD_FLAG_COMMIT_RANGE);
+      if (bad_L) raise_flag(flags, ISD_FLAG_CTX_RANGE);
+      if (bad) raise_flag(flags, first_bad == -1 ? ISD_FLAG_COMMIT_RANGE : ISD_FLAG_PAGE_RANGE);
+      ctx_out[r] = L + nv;
+    }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) ctx_out[r] = L + nv;
 }
 
 __global__ void fill_zero_u32(uint32_t* p, int n) {
@@ -108,19 +122,20 @@ __global__ void build_exp_table(double* t) {
 hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
                          void* v_pages, const int32_t* table, const int32_t* ctx_in,
                          const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags,
-                         hipStream_t stream) {
+                         uint32_t* arrivals, hipStream_t stream) {
+  const dim3 grid(s.stride_n - 1, s.batch);
   if (s.kv_dtype == ISD_BF16)
-    hipLaunchKernelGGL((kv_commit_kernel<uint16_t>), dim3(s.batch), dim3(256), 0, stream,
+    hipLaunchKernelGGL((kv_commit_kernel<uint16_t>), grid, dim3(kCommitThreads), 0, stream,
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                        static_cast<uint16_t*>(k_pages), static_cast<uint16_t*>(v_pages), table, ctx_in,
                        n_commit, ctx_out, s.stride_n, s.n_kv_heads, s.head_dim, s.max_pages,
-                       s.num_pages, flags);
+                       s.num_pages, flags, arrivals);
   else
-    hipLaunchKernelGGL((kv_commit_kernel<float>), dim3(s.batch), dim3(256), 0, stream,
+    hipLaunchKernelGGL((kv_commit_kernel<float>), grid, dim3(kCommitThreads), 0, stream,
                        static_cast<const float*>(k_new), static_cast<const float*>(v_new),
                        static_cast<float*>(k_pages), static_cast<float*>(v_pages), table, ctx_in,
                        n_commit, ctx_out, s.stride_n, s.n_kv_heads, s.head_dim, s.max_pages,
-                       s.num_pages, flags);
+                       s.num_pages, flags, arrivals);
   return hipGetLastError();
 }
 

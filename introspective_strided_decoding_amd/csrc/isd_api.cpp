@@ -47,7 +47,7 @@ isd_status check_shape(const isd_shape* s) {
   if (s->n_q_heads % s->n_kv_heads) return ISD_ERR_SHAPE;
   if (s->page_size != kPage) return ISD_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return ISD_ERR_UNSUPPORTED;
-  if (s->stride_n > 32) return ISD_ERR_UNSUPPORTED;
+  if (s->stride_n > 32 || s->batch > 65535) return ISD_ERR_UNSUPPORTED;
   const long long rows = (long long)(s->n_q_heads / s->n_kv_heads) * (2 * s->stride_n - 1);
   if (rows > 64) return ISD_ERR_UNSUPPORTED;
   if ((long long)s->max_pages * kPage > (1LL << 30)) return ISD_ERR_SHAPE;
@@ -110,9 +110,7 @@ WsLayout ws_layout(const isd_shape& s) {
   size_t off = kHeaderBytes;
   L.attn_cnt = off;
   off = align_up(off + (size_t)s.batch * s.n_kv_heads * 4, 256);
-  L.req_cnt = off;
-  off = align_up(off + (size_t)s.batch * 4, 256);
-  L.sel_cnt = off;
+  L.cmt_cnt = off;
   off = align_up(off + (size_t)s.batch * 4, 256);
   L.zero_end = off;
   const size_t partial_rows = (size_t)s.batch * s.n_kv_heads * a.n_splits * a.rows_pad;
@@ -122,14 +120,12 @@ WsLayout ws_layout(const isd_shape& s) {
   off = align_up(off + partial_rows * s.head_dim * 4, 256);
   L.lse = off;
   off = align_up(off + (size_t)c.rows * c.shards * 8, 256);
-  L.req = off;
+  L.jobs = off;
   off = align_up(off + (size_t)s.batch * sizeof(ReqState), 256);
   L.lse64 = off;
   off = align_up(off + (size_t)s.batch * c.r_shards * 32, 256);
   L.mass = off;
   off = align_up(off + (size_t)s.batch * c.r_shards * 16, 256);
-  L.rej_list = off;
-  off = align_up(off + (size_t)s.batch * 4, 256);
   L.exp_table = off;
   off = align_up(off + (size_t)kExpTableSize * 8, 256);
   L.total = off;
@@ -240,12 +236,14 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
   if (!k_new || !v_new || !k_pages || !v_pages || !page_table || !ctx_lens_in || !n_commit ||
       !ctx_lens_out)
     return ISD_ERR_NULL;
-  if (!aligned16(k_new) || !aligned16(k_pages)) return ISD_ERR_ALIGNMENT;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages)) return ISD_ERR_ALIGNMENT;
   st = check_ws(shape, workspace, ws_bytes);
   if (st != ISD_OK) return st;
-  uint32_t* flags = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + ws_layout(*shape).flags);
+  const WsLayout L = ws_layout(*shape);
+  char* ws = static_cast<char*>(workspace);
   hipError_t e = launch_commit(*shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in,
-                               n_commit, ctx_lens_out, flags, stream);
+                               n_commit, ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
+                               reinterpret_cast<uint32_t*>(ws + L.cmt_cnt), stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "kv_commit");
 }
 

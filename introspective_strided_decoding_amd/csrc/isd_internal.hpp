@@ -47,33 +47,32 @@ struct AcceptPlan {
 struct WsLayout {
   size_t flags = 0;          // uint32 device flags
   size_t attn_cnt = 0;       // uint32 per (request, kv head): split arrivals
-  size_t req_cnt = 0;        // uint32 per request: normaliser workgroups arrived
-  size_t sel_cnt = 0;        // uint32 per request: residual-mass workgroups arrived
+  size_t cmt_cnt = 0;        // uint32 per request: commit workgroups arrived
   size_t zero_end = 0;       // [0, zero_end) is zeroed by isd_workspace_init
   size_t attn_ml = 0;        // float2 (m, l) per partial row
   size_t attn_o = 0;         // float [D] per partial row
   size_t lse = 0;            // float2 (max, sum) per (row, shard)
-  size_t req = 0;            // per-request accept state (ReqState)
-  size_t lse64 = 0;          // double2 per (request, residual shard) for p and q
-  size_t mass = 0;           // double2 (residual mass, p mass) per (request, residual shard)
-  size_t rej_list = 0;       // int32 per request: requests that rejected a proposal, compacted
+  size_t jobs = 0;           // ReqState per rejecting request, compacted
+  size_t lse64 = 0;          // double2 per (listed request, residual shard) for p and q
+  size_t mass = 0;           // double2 (residual mass, p mass) per (listed request, residual shard)
   size_t exp_table = 0;      // double[65536]: exp of every bf16 bit pattern
   size_t total = 0;
 };
 
-// Header words (uint32 at these byte offsets of the workspace).
-constexpr size_t kRejCountOffset = 4;     // number of entries in rej_list
-constexpr size_t kResidDoneOffset = 8;    // residual-mass workgroups finished in this call
 constexpr int kExpTableSize = 65536;
 
-// Per-request state handed from the accept decision to the residual kernels.
+// Header word (uint32 at this byte offset of the workspace).
+constexpr size_t kRejCountOffset = 4;     // entries in the list of rejecting requests
+
+// One entry of the list of rejecting requests, handed from the accept
+// decision to the residual kernels.
 struct ReqState {
-  int32_t accept_len;
-  int32_t reject_row;   // j of the rejected row, -1 if all accepted
+  int32_t req;          // request index r
+  int32_t accept_len;   // A
+  int32_t reject_row;   // j of the rejected row
   int32_t table_ok;     // bf16 rows whose max logit lies in (-600, 600): exp from the table
-  int32_t pad1;
   double u_resample;    // u' of the rejected position
-  double pad2;
+  double pad;
 };
 
 AttnPlan plan_attention(const isd_shape& s);
@@ -97,7 +96,7 @@ hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_
 hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
                          void* v_pages, const int32_t* table, const int32_t* ctx_in,
                          const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags,
-                         hipStream_t stream);
+                         uint32_t* arrivals, hipStream_t stream);
 
 hipError_t launch_workspace_init(void* ws, size_t header_bytes, double* exp_table, hipStream_t stream);
 
