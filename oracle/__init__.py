@@ -24,9 +24,10 @@ Modules:
   commit     writing the accepted CLEAN rows into KV pages
   lora       the gated low-rank delta of R-ISD
   tpf        expected acceptance, tokens per forward, the compute-bound identity
+  propose    drawing the next N tokens at the MASK rows (sampling or argmax)
 
 Every function is pinned by a test in ``tests/test_oracle_*.py`` against a
 closed form, a printed value, a library routine or a brute-force count.
 """
 
-from . import accept, attention, commit, lora, philox, tpf  # noqa: F401
+from . import accept, attention, commit, lora, philox, propose, tpf  # noqa: F401

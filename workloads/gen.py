@@ -21,6 +21,9 @@ Recipe (one reading of the workload text, applied to every config):
   the row that proposed it.
 * LoRA operands (R-ISD configs): ``X, Y ~ N(0, 1)``, ``A, B ~ N(0, lora_std^2)``,
   all rounded to bf16; the gated rows are the N MASK rows of every stride.
+* MASK-row logits (``with_mask_logits``), from which the next N proposals are
+  drawn: ``N(0, logit_std^2)`` rounded to the dtype, drawn after everything
+  above so the other fields do not depend on the flag.
 
 Bulk normals come from ``torch.randn`` with a seeded CPU generator (fast and
 deterministic for a given torch build); small integer draws come from numpy's
@@ -78,6 +81,7 @@ class Workload:
     lora_b: Optional[np.ndarray] = None   # [r, d]
     lora_y: Optional[np.ndarray] = None   # [B*Q, d]
     mask_rows: Optional[np.ndarray] = None  # [B*N] int32
+    mask_logits: Optional[np.ndarray] = None  # [B, N, V] logits of the MASK rows
 
     @property
     def num_pages(self) -> int:
@@ -136,7 +140,8 @@ def _fit_tau(p: torch.Tensor, z: torch.Tensor, dtype: str, groups: torch.Tensor,
 
 
 def make_workload(cfg: WorkloadConfig, seed: Optional[int] = None, *, junk: str = "random",
-                  tau_mode: Optional[str] = None, with_logits: bool = True) -> Workload:
+                  tau_mode: Optional[str] = None, with_logits: bool = True,
+                  with_mask_logits: bool = False) -> Workload:
     """Build one seeded ISD step input for ``cfg``.
 
     tau_mode: "batch" (one tau for the whole batch), "request" or "row".  Default: "request"
@@ -258,4 +263,6 @@ def make_workload(cfg: WorkloadConfig, seed: Optional[int] = None, *, junk: str 
         wl.lora_y = _round(normals(rows, d), "bf16").numpy()
         _, mrows = stride_rows(cfg)
         wl.mask_rows = (np.arange(B)[:, None] * Q + np.asarray(mrows)[None, :]).reshape(-1).astype(np.int32)
+    if with_mask_logits:
+        wl.mask_logits = _round(normals(B, N, V, std=cfg.logit_std), cfg.dtype).numpy()
     return wl
