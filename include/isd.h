@@ -114,7 +114,7 @@ typedef struct isd_shape {
  * directly.
  */
 
-/* Workspace bytes needed by isd_attention, isd_accept and kv_commit for `shape`. */
+/* Workspace bytes needed by isd_attention, isd_accept, kv_commit and isd_propose for `shape`. */
 size_t isd_workspace_bytes(const isd_shape* shape);
 
 /*
@@ -229,6 +229,44 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
                      const int32_t* ctx_lens_in, const int32_t* n_commit,
                      int32_t* ctx_lens_out, void* workspace, size_t ws_bytes,
                      hipStream_t stream);
+
+/*
+ * isd_propose -- draw the next N proposals at the MASK rows.
+ *
+ * Definition ("I-DLM：扩散模型如何用'自省一致性'追上自回归模型质量", section
+ * "Introspective Strided Decoding（ISD）": every forward pass draws N new
+ * tokens at the MASK positions from the proposal distribution q;
+ * "自省扩散语言模型的 token 生成机制与工程实践", section "从质量差距到自省机制",
+ * and section "服务部署与 SGLang 集成" for the argmax proposal policy):
+ *
+ *   ISD_PROPOSE_SAMPLE  proposals[r][k] = the first y (vocabulary order)
+ *                       whose running sum of q = softmax(mask_logits[r][k])
+ *                       exceeds u * (total), sums in float64; u is word 0 of
+ *                       the Philox4x64-10 block with key (seed_lo, seed_hi)
+ *                       and counter (req_ids[r], positions[r] + N + k, step,
+ *                       1), mapped to (w >> 11) * 2^-53.  positions[r] is the
+ *                       absolute position of x_1, so MASK row k proposes the
+ *                       token at positions[r] + N + k.
+ *   ISD_PROPOSE_ARGMAX  proposals[r][k] = the smallest index of the largest
+ *                       logit (req_ids, positions, seed and step unused and
+ *                       may be NULL / 0).
+ *
+ *   mask_logits [B][N][V] logit_dtype, 16-byte aligned; every row holds at
+ *               least one finite logit
+ *   proposals   [B][N] int32, written
+ *
+ * Uses the same workspace as the calls above (isd_workspace_bytes()).
+ * Supported: batch * stride_n <= 65535.
+ */
+typedef enum isd_propose_mode {
+  ISD_PROPOSE_SAMPLE = 0,
+  ISD_PROPOSE_ARGMAX = 1
+} isd_propose_mode;
+
+isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const int32_t* req_ids,
+                       const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
+                       uint32_t step, int32_t mode, int32_t* proposals, void* workspace,
+                       size_t ws_bytes, hipStream_t stream);
 
 /*
  * isd_lora_delta -- the gated rank-r delta of Residual ISD (R-ISD).

@@ -26,8 +26,9 @@ STATUS = {0: "ISD_OK", 1: "ISD_ERR_NULL", 2: "ISD_ERR_SHAPE", 3: "ISD_ERR_DTYPE"
 
 # Every symbol include/isd.h declares.
 EXPORTS = ("isd_workspace_bytes", "isd_workspace_init", "isd_read_flags", "isd_attention",
-           "isd_accept", "kv_commit", "isd_lora_workspace_bytes", "isd_lora_delta",
+           "isd_accept", "kv_commit", "isd_propose", "isd_lora_workspace_bytes", "isd_lora_delta",
            "isd_status_string", "isd_last_error", "isd_abi_version")
+PROPOSE_SAMPLE, PROPOSE_ARGMAX = 0, 1
 
 
 class IsdError(RuntimeError):
@@ -82,6 +83,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "isd_attention": (I32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, SZ, P]),
         "kv_commit": (I32, [SP, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, I32, P, P, SZ, P]),
         "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
         "isd_lora_delta": (I32, [I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
         "isd_status_string": (ctypes.c_char_p, [I32]),
@@ -201,6 +203,20 @@ def kv_commit(shape: Shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens
         _ptr(page_table, "page_table", torch.int32, B * shape.max_pages),
         _ptr(ctx_lens_in, "ctx_lens_in", torch.int32, B), _ptr(n_commit, "n_commit", torch.int32, B),
         _ptr(ctx_lens_out, "ctx_lens_out", torch.int32, B),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, mode: int,
+                proposals, workspace, stream=None) -> None:
+    B, N, V = shape.batch, shape.stride_n, shape.vocab
+    i32 = torch.int32
+    sample = mode == PROPOSE_SAMPLE
+    _check("isd_propose", LIB.isd_propose(
+        ctypes.byref(shape.c()), _ptr(mask_logits, "mask_logits", _tdtype(shape.logit_dtype), B * N * V),
+        _ptr(req_ids, "req_ids", i32, B) if sample or req_ids is not None else None,
+        _ptr(positions, "positions", i32, B) if sample or positions is not None else None,
+        int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(mode),
+        _ptr(proposals, "proposals", i32, B * N),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
 
 

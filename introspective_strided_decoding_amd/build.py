@@ -1,6 +1,8 @@
 """Build libisd.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
 
-    python -m introspective_strided_decoding_amd.build
+    python introspective_strided_decoding_amd/build.py
+
+(run as a script: importing the package loads the library this builds).
 
 Every source is compiled to an object under _build/ and linked into
 introspective_strided_decoding_amd/libisd.so.  Packed-fp32 VALU instructions
@@ -23,7 +25,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libisd.so")
 ARCH = "gfx950"
 
-SOURCES = ["isd_api.cpp", "attention.hip", "accept.hip", "commit.hip", "lora.hip"]
+SOURCES = ["isd_api.cpp", "attention.hip", "accept.hip", "commit.hip", "propose.hip", "lora.hip"]
 
 
 def hipcc() -> str:
@@ -56,7 +58,10 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    srcs = list(SOURCES)
+    missing = [s for s in srcs if not os.path.exists(os.path.join(CSRC, s))]
+    if missing:
+        raise RuntimeError(f"missing sources: {missing}")
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"

@@ -126,6 +126,8 @@ WsLayout ws_layout(const isd_shape& s) {
   off = align_up(off + (size_t)s.batch * c.r_shards * 32, 256);
   L.mass = off;
   off = align_up(off + (size_t)s.batch * c.r_shards * 16, 256);
+  L.prop = off;
+  off = align_up(off + (size_t)s.batch * s.stride_n * prop_shards(s.vocab) * sizeof(PropPart), 256);
   L.exp_table = off;
   off = align_up(off + (size_t)kExpTableSize * 8, 256);
   L.total = off;
@@ -138,7 +140,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 1; }
+int32_t isd_abi_version(void) { return 2; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {
@@ -219,7 +221,6 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
   st = check_ws(shape, workspace, ws_bytes);
   if (st != ISD_OK) return st;
   const AcceptPlan p = plan_accept(*shape);
-  if (p.rows > 65535) return ISD_ERR_UNSUPPORTED;
   const WsLayout L = ws_layout(*shape);
   hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
                                seed_hi, step, accept_len, out_tokens, n_out, n_commit, logp_sel,
@@ -245,6 +246,24 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
                                n_commit, ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
                                reinterpret_cast<uint32_t*>(ws + L.cmt_cnt), stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "kv_commit");
+}
+
+isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const int32_t* req_ids,
+                       const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
+                       int32_t mode, int32_t* proposals, void* workspace, size_t ws_bytes,
+                       hipStream_t stream) {
+  isd_status st = check_shape(shape);
+  if (st != ISD_OK) return st;
+  if (mode != ISD_PROPOSE_SAMPLE && mode != ISD_PROPOSE_ARGMAX) return ISD_ERR_UNSUPPORTED;
+  if (!mask_logits || !proposals || (mode == ISD_PROPOSE_SAMPLE && (!req_ids || !positions)))
+    return ISD_ERR_NULL;
+  if (!aligned16(mask_logits)) return ISD_ERR_ALIGNMENT;
+  if ((long long)shape->batch * shape->stride_n > 65535) return ISD_ERR_UNSUPPORTED;
+  st = check_ws(shape, workspace, ws_bytes);
+  if (st != ISD_OK) return st;
+  hipError_t e = launch_propose(*shape, mask_logits, req_ids, positions, seed_lo, seed_hi, step, mode,
+                                proposals, static_cast<char*>(workspace), ws_layout(*shape), stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_propose");
 }
 
 size_t isd_lora_workspace_bytes(int32_t n_mask, int32_t d_in, int32_t rank) {

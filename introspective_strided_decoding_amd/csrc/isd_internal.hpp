@@ -55,6 +55,7 @@ struct WsLayout {
   size_t jobs = 0;           // ReqState per rejecting request, compacted
   size_t lse64 = 0;          // double2 per (listed request, residual shard) for p and q
   size_t mass = 0;           // double2 (residual mass, p mass) per (listed request, residual shard)
+  size_t prop = 0;           // PropPart per (MASK row, proposal shard)
   size_t exp_table = 0;      // double[65536]: exp of every bf16 bit pattern
   size_t total = 0;
 };
@@ -74,6 +75,14 @@ struct ReqState {
   double u_resample;    // u' of the rejected position
   double pad;
 };
+
+// Per (MASK row, vocabulary shard) summary written by the proposal kernels.
+struct PropPart {
+  double sum;           // sum of exp(l - max) over the shard (sampling policy)
+  float max;            // shard max logit
+  int32_t idx;          // first index holding it
+};
+int prop_shards(int vocab);   // 4096-entry shards of a MASK row
 
 AttnPlan plan_attention(const isd_shape& s);
 AcceptPlan plan_accept(const isd_shape& s);
@@ -97,6 +106,10 @@ hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_ne
                          void* v_pages, const int32_t* table, const int32_t* ctx_in,
                          const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags,
                          uint32_t* arrivals, hipStream_t stream);
+
+hipError_t launch_propose(const isd_shape& s, const void* mask_logits, const int32_t* req_ids,
+                          const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
+                          int mode, int32_t* proposals, char* ws, const WsLayout& L, hipStream_t stream);
 
 hipError_t launch_workspace_init(void* ws, size_t header_bytes, double* exp_table, hipStream_t stream);
 

@@ -2,10 +2,11 @@
 
 ``DeviceStep.from_arrays`` takes host arrays by name (numpy or torch: q,
 k_new, v_new, plain page pools, page_table, ctx_lens, p/q logits, proposals,
-req_ids, positions, step, philox_seed, and optionally the LoRA operands),
-moves them to the device in the library layouts, allocates the outputs and
-the workspace, and ``run()`` enqueues isd_attention -> isd_accept ->
-kv_commit (+ isd_lora_delta when LoRA operands are present).
+req_ids, positions, step, philox_seed, and optionally the LoRA operands and
+the MASK-row logits), moves them to the device in the library layouts,
+allocates the outputs and the workspace, and ``run()`` enqueues
+isd_attention -> isd_accept -> kv_commit (+ isd_lora_delta when LoRA
+operands are present, + isd_propose when MASK-row logits are present).
 """
 
 from __future__ import annotations
@@ -53,6 +54,8 @@ class DeviceStep:
     logq_sel: torch.Tensor
     ctx_lens_out: torch.Tensor
     lora: Optional[dict] = None
+    mask_logits: Optional[torch.Tensor] = None
+    next_proposals: Optional[torch.Tensor] = None
     extra: dict = field(default_factory=dict)
 
     @classmethod
@@ -90,6 +93,9 @@ class DeviceStep:
             ctx_lens_out=ctx if commit_in_place else torch.empty(B, dtype=i32, device=device),
         )
         del k_plain, v_plain
+        if getattr(a, "mask_logits", None) is not None:
+            st.mask_logits = _t(a.mask_logits, kv, device)
+            st.next_proposals = torch.empty(B, N, dtype=i32, device=device)
         if getattr(a, "lora_x", None) is not None:
             bf = torch.bfloat16
             # linear-layer layouts: down weight [rank, d_in], up weight [d_out, rank]
@@ -117,14 +123,21 @@ class DeviceStep:
                        self.page_table, self.ctx_lens, self.n_commit, self.ctx_lens_out,
                        self.workspace, stream=stream)
 
+    def propose(self, stream=None, mode: int = _lib.PROPOSE_SAMPLE, step: Optional[int] = None, seed=None):
+        _lib.isd_propose(self.shape, self.mask_logits, self.req_ids, self.positions,
+                         self.seed if seed is None else seed, self.step if step is None else step,
+                         mode, self.next_proposals, self.workspace, stream=stream)
+
     def lora_delta(self, stream=None):
         L = self.lora
         _lib.isd_lora_delta(L["X"], L["A_t"], L["B_t"], L["mask_rows"], L["Y"], L["ws"], stream=stream)
 
     def run(self, stream=None):
-        """One ISD step: attention -> accept -> commit (-> LoRA delta)."""
+        """One ISD step: attention -> accept -> commit (-> LoRA delta) (-> proposals)."""
         self.attention(stream)
         self.accept(stream)
         self.commit(stream)
         if self.lora is not None:
             self.lora_delta(stream)
+        if self.mask_logits is not None:
+            self.propose(stream)

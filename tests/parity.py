@@ -5,7 +5,8 @@ Tolerances (written here once, used by every GPU test):
 * accept lengths and token ids: exact, except requests with a near-tie
   decision (|u - rho| < 1e-5 for an accept test, or u' * S within 1e-12 * S
   of an edge of the chosen residual interval); near-ties must stay under
-  0.01 % of the decisions taken.
+  0.01 % of the decisions taken.  Proposals drawn at the MASK rows follow the
+  residual's rule (u * total within 1e-12 * total of an edge).
 """
 
 from __future__ import annotations
@@ -20,6 +21,7 @@ from oracle.attention import stride_attention
 ATOL = {"bf16": 2e-2, "f32": 1e-5}
 ACCEPT_NEAR_TIE = 1e-5
 RESAMPLE_NEAR_TIE = 1e-12
+PROPOSE_NEAR_TIE = 1e-12        # u * total within 1e-12 * total of an edge of the drawn token
 NEAR_TIE_BUDGET = 1e-4
 
 

@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 1
+    assert LIB.isd_abi_version() == 2
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"
@@ -105,6 +105,27 @@ def test_accept_and_commit_validation():
     bad = list(cargs)
     bad[-2] = 0
     assert LIB.kv_commit(ctypes.byref(s.c()), *bad) == 4
+
+
+def test_propose_validation():
+    s = _shape()
+    n = _ws(s)
+
+    def call(logits=FAKE, req=FAKE, pos=FAKE, mode=0, out=FAKE, ws=FAKE, ws_bytes=n, shape=s):
+        return LIB.isd_propose(ctypes.byref(shape.c()), logits, req, pos, 1, 2, 3, mode, out, ws,
+                               ws_bytes, None)
+
+    assert call(ws_bytes=8) == 4                      # every check passes up to the workspace size
+    assert call(mode=2) == 5
+    assert call(mode=-1) == 5
+    assert call(logits=None) == 1
+    assert call(out=None) == 1
+    assert call(req=None) == 1                        # the sampling policy needs the Philox counter
+    assert call(req=None, pos=None, mode=1, ws_bytes=8) == 4   # argmax does not
+    assert call(logits=MISALIGNED) == 7
+    assert call(ws=None) == 1
+    assert call(shape=_shape(batch=20000, stride_n=4), ws_bytes=8) == 5   # B * N rows > 65535
+    assert call(shape=_shape(logit_dtype=5)) == 3
 
 
 def test_workspace_init_and_flags_validation():
