@@ -2,13 +2,16 @@
 
 A step is one pass of the whole hot path over the batch: isd_attention ->
 isd_accept -> kv_commit (+ isd_lora_delta for the R-ISD workload), enqueued on
-one stream.  Inputs are synthetic (workloads/), generated on the host and
-resident in HBM before the timed region.  To keep the Infinity Cache (256 MB)
-from serving repeated steps, the timed loop rotates over several independent
-copies of every input whose total exceeds the cache several times over.  The
-commit writes lengths to a second buffer, so every timed step sees the same
-context lengths (the committed rows land in slots the next attention does not
-read).
+one stream.  The MASK-row proposals for the next step (isd_propose, sampling
+and argmax policies) are timed in a loop of their own after the steps and
+reported under "propose"; they do not enter "value".
+
+Inputs are synthetic (workloads/), generated on the host and resident in HBM
+before the timed region.  To keep the Infinity Cache (256 MB) from serving
+repeated steps, the timed loop rotates over several independent copies of
+every input whose total exceeds the cache several times over.  The commit
+writes lengths to a second buffer, so every timed step sees the same context
+lengths (the committed rows land in slots the next attention does not read).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c32_ctx4k]
 
@@ -81,6 +84,11 @@ def lora_bytes(cfg):
     return (m * d + d * r + r * d + 2 * m * d) * 2 + m * 4
 
 
+def propose_bytes(cfg):
+    """MASK-row logits read once, proposals written once."""
+    return cfg.batch * cfg.stride_n * (cfg.vocab * cfg.elem_bytes + 4)
+
+
 def cpu_baseline(wl, budget_s: float = 10.0, max_steps: int = 8):
     """Time the float64 oracle on the host: whole steps (attention for every request, accept,
     commit) of the same workload, repeated until about ``budget_s`` seconds have passed."""
@@ -148,11 +156,11 @@ def main(argv=None):
 
     cfg = get_config(args.config)
     t_gen = time.perf_counter()
-    wl = make_workload(cfg)
+    wl = make_workload(cfg, with_mask_logits=True)
     t_gen = time.perf_counter() - t_gen
     nbytes = algorithmic_bytes(wl)
     step_bytes = nbytes["attention"] + nbytes["accept"]
-    per_set = step_bytes + (lora_bytes(cfg) if cfg.lora else 0)
+    per_set = step_bytes + (lora_bytes(cfg) if cfg.lora else 0) + propose_bytes(cfg)
     sets = args.sets or max(2, min(8, int(np.ceil(4 * MALL_BYTES / per_set))))
 
     torch.cuda.set_device(0)
@@ -208,6 +216,27 @@ def main(argv=None):
     ms_per_step = elapsed * 1e3 / args.steps
     steps_per_s = args.steps / elapsed
 
+    # MASK-row proposals, timed on their own (both policies)
+    from introspective_strided_decoding_amd._lib import PROPOSE_ARGMAX, PROPOSE_SAMPLE
+    prop = {}
+    pbytes = propose_bytes(cfg)
+    for name, mode in (("sample", PROPOSE_SAMPLE), ("argmax", PROPOSE_ARGMAX)):
+        for i in range(min(args.warmup, 10)):
+            steps[i % sets].propose(mode=mode)
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(max(20, args.steps // 3))]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(pev):
+            a.record(stream)
+            steps[i % sets].propose(mode=mode)
+            b.record(stream)
+        torch.cuda.synchronize()
+        pms = float(np.mean([a.elapsed_time(b) for a, b in pev]))
+        prop[name] = {"avg_call_ms": round(pms, 5), "achieved_GBs": round(pbytes / pms / 1e6, 1),
+                      "frac": round(pbytes / pms / 1e6 / HBM_PEAK_GBS, 4)}
+    prop["bytes_per_call"] = int(pbytes)
+    prop["steps_per_s_with_sampled_proposals"] = round(1e3 / (ms_per_step + prop["sample"]["avg_call_ms"]), 2)
+
     # accepted / committed tokens of the timed steps (identical draws per set)
     acc = [int(st.accept_len.sum().item()) for st in steps]
     ncommit = steps[0].n_commit.cpu().numpy()
@@ -250,6 +279,7 @@ def main(argv=None):
             "bytes_per_launch": int(nbytes["attention"]),
             "avg_launch_ms": round(attn_ms, 5),
         },
+        "propose": prop,
         "input_gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:

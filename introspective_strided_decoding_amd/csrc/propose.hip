@@ -12,11 +12,13 @@
 //                 over them picks the shard holding u * total, and a
 //                 workgroup scan inside that shard in vocabulary order picks
 //                 the first token whose running mass exceeds u * total.
-// Sums and the scan run in float64, so the draw agrees with a float64
-// inverse CDF up to rounding of the running sums.
+// Sums and the scan run in float64 (exp by the table-driven exp_nonpos, its
+// 64-entry table in LDS), so the draw agrees with a float64 inverse CDF up to
+// rounding of the running sums.
 #include <climits>
 
 #include "device_common.hpp"
+#include "exp64.hpp"
 #include "isd_internal.hpp"
 
 namespace isd {
@@ -25,6 +27,12 @@ namespace {
 constexpr int kPThreads = 256;
 constexpr int kPPer = 16;                     // entries per thread
 constexpr int kPShard = kPThreads * kPPer;    // entries per shard
+
+// 2^(j/64), j = 0..63, for exp_nonpos; call with all threads of the workgroup.
+__device__ __forceinline__ void fill_exp_table(double* tab64) {
+  if (threadIdx.x < 64) tab64[threadIdx.x] = exp2(double(threadIdx.x) * (1.0 / 64.0));
+  __syncthreads();
+}
 
 template <typename T>
 __device__ __forceinline__ void load_entries(const T* __restrict__ row, int e0, int e1, bool vec,
@@ -49,6 +57,8 @@ __device__ __forceinline__ void load_entries(const T* __restrict__ row, int e0, 
 template <typename T>
 __global__ __launch_bounds__(kPThreads) void prop_partial(const T* __restrict__ logits, int V, int shards,
                                                           int sample, PropPart* __restrict__ part) {
+  __shared__ double tab64[64];
+  if (sample) fill_exp_table(tab64);
   const int sh = blockIdx.x;
   const size_t row = blockIdx.y;
   const T* base = logits + row * V;
@@ -86,9 +96,15 @@ __global__ __launch_bounds__(kPThreads) void prop_partial(const T* __restrict__ 
   double s = 0.0;
   if (sample && M != -INFINITY) {
     const double md = M;
+    double e[kPPer];
 #pragma unroll
-    for (int i = 0; i < kPPer; ++i) s += exp(double(x[i]) - md);
-    s = wave_sum_d(s);
+    for (int i = 0; i < kPPer; ++i) e[i] = exp_nonpos(double(x[i]) - md, tab64);
+    // pairwise sum of the thread's 16 terms
+#pragma unroll
+    for (int w = kPPer / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) e[i] += e[i + w];
+    s = wave_sum_d(e[0]);
     if (lane == 0) ssum[wave] = s;
     __syncthreads();
     s = 0.0;
@@ -128,18 +144,26 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
   const int r = row / N, k = row % N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const PropPart* rp = part + size_t(row) * shards;
+  __shared__ double tab64[64];
   __shared__ double before_sm, target_sm, scale_sm;
   __shared__ float mshard_sm;
   __shared__ int shard_sm, found_sm, last_sm;
   __shared__ double wsum[kPThreads / 64];
+  // lane l of wave 0 owns shards [l*per, (l+1)*per) in vocabulary order; the
+  // first of them is requested before the table is built
+  const int per = (shards + 63) / 64;
+  const int s0 = min(shards, lane * per), s1 = min(shards, s0 + per);
+  PropPart first_part;
+  first_part.sum = 0.0;
+  first_part.max = -INFINITY;
+  first_part.idx = INT_MAX;
+  if (wave == 0 && s0 < s1) first_part = rp[s0];
+  if (sample) fill_exp_table(tab64);
   if (wave == 0) {
-    // lane l owns shards [l*per, (l+1)*per) in vocabulary order
-    const int per = (shards + 63) / 64;
-    const int s0 = min(shards, lane * per), s1 = min(shards, s0 + per);
     float mx = -INFINITY;
     int ix = INT_MAX;
     for (int i = s0; i < s1; ++i) {
-      const PropPart p = rp[i];
+      const PropPart p = (i == s0) ? first_part : rp[i];
       if (p.max > mx || (p.max == mx && p.idx < ix)) { mx = p.max; ix = p.idx; }
     }
     float M = mx;
@@ -161,8 +185,8 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
       const double Md = M;
       double wsh = 0.0;
       for (int i = s0; i < s1; ++i) {
-        const PropPart p = rp[i];
-        if (p.max != -INFINITY) wsh += p.sum * exp(double(p.max) - Md);
+        const PropPart p = (i == s0) ? first_part : rp[i];
+        if (p.max != -INFINITY) wsh += p.sum * exp_nonpos(double(p.max) - Md, tab64);
       }
       double tot;
       const double before_lane = wave_exclusive_d(wsh, tot);
@@ -171,8 +195,8 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
       int pick = -1, last_nz = -1;
       double pick_before = 0.0, last_before = 0.0;
       for (int i = s0; i < s1; ++i) {
-        const PropPart p = rp[i];
-        const double wi = (p.max == -INFINITY) ? 0.0 : p.sum * exp(double(p.max) - Md);
+        const PropPart p = (i == s0) ? first_part : rp[i];
+        const double wi = (p.max == -INFINITY) ? 0.0 : p.sum * exp_nonpos(double(p.max) - Md, tab64);
         if (wi > 0.0) { last_nz = i; last_before = cum; }
         if (pick < 0 && cum + wi > target) { pick = i; pick_before = cum; }
         cum += wi;
@@ -198,7 +222,7 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
         before_sm = bf;
         target_sm = target;
         mshard_sm = ms;
-        scale_sm = (ms == -INFINITY) ? 0.0 : exp(double(ms) - Md);
+        scale_sm = (ms == -INFINITY) ? 0.0 : exp_nonpos(double(ms) - Md, tab64);
         found_sm = INT_MAX;
         last_sm = -1;
       }
@@ -221,7 +245,7 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
   int last_here = -1;
 #pragma unroll
   for (int i = 0; i < kPPer; ++i) {
-    const double v = (x[i] == -INFINITY) ? 0.0 : exp(double(x[i]) - ms) * scale;
+    const double v = (x[i] == -INFINITY) ? 0.0 : exp_nonpos(double(x[i]) - ms, tab64) * scale;
     if (v > 0.0) last_here = e0 + i;
     run += v;
     c[i] = run;
