@@ -138,6 +138,7 @@ def main(argv=None):
     ap.add_argument("--config", default="c32_ctx4k")
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated in the timed loop (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device copy before the timed loop (a known-size reference "
                          "for hardware traffic counters)")
@@ -216,6 +217,34 @@ def main(argv=None):
     ms_per_step = elapsed * 1e3 / args.steps
     steps_per_s = args.steps / elapsed
 
+    # the same steps replayed from HIP graphs (one recorded step per input set)
+    graph = None
+    if not args.no_graph:
+        graphs = [st.capture() if not use_lora else None for st in steps]
+        if all(g is not None for g in graphs):
+            # the recorded step also draws the next proposals; time it against eager steps that do too
+            for i in range(args.warmup):
+                graphs[i % sets].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                graphs[i % sets].replay()
+            torch.cuda.synchronize()
+            g_elapsed = time.perf_counter() - t0
+            for i in range(args.warmup):
+                steps[i % sets].run()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                steps[i % sets].run()
+            torch.cuda.synchronize()
+            e_elapsed = time.perf_counter() - t0
+            graph = {"what": "attention, accept, commit and sampled proposals per step",
+                     "graph_steps_per_s": round(args.steps / g_elapsed, 2),
+                     "eager_steps_per_s": round(args.steps / e_elapsed, 2),
+                     "graph_ms_per_step": round(g_elapsed * 1e3 / args.steps, 5)}
+            del graphs
+
     # MASK-row proposals, timed on their own (both policies)
     from introspective_strided_decoding_amd._lib import PROPOSE_ARGMAX, PROPOSE_SAMPLE
     prop = {}
@@ -280,6 +309,7 @@ def main(argv=None):
             "avg_launch_ms": round(attn_ms, 5),
         },
         "propose": prop,
+        "graph": graph,
         "input_gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:

@@ -1,15 +1,18 @@
 // Stride attention over the paged KV cache (isd_attention).
 //
-// Work split: workgroup (r, kv head hk, split s) walks tiles of 32 context
-// tokens (two 16-token pages) of request r.  Its four waves take the tiles of
-// the split round-robin.  Each wave keeps, for every query column of the GQA
-// group (G heads x Q stride rows, padded to 32 or 64 columns), an online
-// softmax state (running max m, running sum l, un-normalised output O); the
-// four waves merge through LDS and the workgroup writes one partial (m, l, O)
-// per column.  The last workgroup of (r, hk) to finish (an atomic arrival
-// count, no waiting) merges the partials of all splits with the strictly
-// causal block of the stride itself (row i sees stride rows 0..i),
-// normalises, and writes the output.
+// Work split: a work unit is (request r, KV head hk, split s): a run of
+// 32-token tiles (two 16-token pages) of r's context.  One workgroup of eight
+// waves serves one unit for one block of 32 query columns (the GQA group's G
+// heads x Q stride rows; groups of more than 32 columns get one workgroup per
+// block, placed on the same XCD so the second read of the pages hits L2).
+// The waves take the unit's tiles round-robin, and wave 0 of split 0 also
+// takes the stride's own strictly causal block (row i sees stride rows 0..i)
+// as one extra, masked tile.  Each wave keeps per column an online softmax
+// state (running max m, running sum l, un-normalised output O); the waves
+// merge through LDS.  A unit that is the only split of its (r, hk) normalises
+// and writes the output directly; otherwise each split publishes a partial
+// (m, l, O) with write-through stores and the last split to arrive (an
+// atomic count, nobody waits) merges them.
 //
 // bf16 path (matrix cores): per tile, S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (rows = 32 tokens, columns = 32 query columns,
@@ -23,8 +26,8 @@
 // max between the two half-waves.
 //
 // fp32 path: one wave per (request, kv head, split, query column), dot
-// products by wave reduction, then a separate combine kernel with the same
-// merge code.
+// products by wave reduction, then a separate combine kernel that merges the
+// splits with the stride block.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -61,19 +64,19 @@ __device__ __forceinline__ int active_splits(int n_tiles, int n_splits, int tps)
   return max(1, min(n_splits, (n_tiles + tps - 1) / tps));
 }
 
-// KV pages are read exactly once per step: stream them past the caches.
+// KV page loads.  Pages read exactly once per step are streamed past the
+// caches (NT); pages that a second workgroup of the same XCD reads moments
+// later (row-block workgroups) are loaded normally so that read hits L2.
+template <bool NT>
 __device__ __forceinline__ u32x4 kv_load(const u32x4* p) {
-#if ISD_KV_NONTEMPORAL
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
 }
 
 // Operand loads of one 32-token tile (pages pid0, pid1; both valid ids).
 // One base pointer per lane and page; the unrolled k-steps / dim blocks are
 // immediate offsets from it.
-template <int D>
+template <int D, bool NT>
 __device__ __forceinline__ void load_k(u32x4 (&k)[D / 16], const uint16_t* __restrict__ kp, int pid0,
                                        int pid1, int hk, int Hkv, int lane) {
   const int h = lane >> 5;
@@ -82,10 +85,10 @@ __device__ __forceinline__ void load_k(u32x4 (&k)[D / 16], const uint16_t* __res
   const u32x4* base = reinterpret_cast<const u32x4*>(
       kp + (size_t(pid) * Hkv + hk) * (D * kPage) + (h * kPage + (i & 15)) * 8);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) k[s] = kv_load(base + s * 2 * kPage);
+  for (int s = 0; s < D / 16; ++s) k[s] = kv_load<NT>(base + s * 2 * kPage);
 }
 
-template <int D>
+template <int D, bool NT>
 __device__ __forceinline__ void load_v(u32x4 (&v)[2][D / 32], const uint16_t* __restrict__ vp, int pid0,
                                        int pid1, int hk, int Hkv, int lane) {
   const int h = lane >> 5;
@@ -95,7 +98,7 @@ __device__ __forceinline__ void load_v(u32x4 (&v)[2][D / 32], const uint16_t* __
     const u32x4* base = reinterpret_cast<const u32x4*>(
         vp + (size_t(m ? pid1 : pid0) * Hkv + hk) * (D * kPage) + i * kPage + h * 8);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) v[m][db] = kv_load(base + db * 32 * 2);
+    for (int db = 0; db < D / 32; ++db) v[m][db] = kv_load<NT>(base + db * 32 * 2);
   }
 }
 
@@ -207,16 +210,17 @@ __device__ __forceinline__ void combine_rk(const T* __restrict__ q, const T* __r
   }
 }
 
-template <int D, int RB, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, 2))) void attn_bf16(
+template <int D, int W, bool NT>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out, int Qn, int Hq, int Hkv, int G,
-    int rows, int max_pages, int num_pages, int tps, int n_splits, float scale_log2,
+    int rows, int max_pages, int num_pages, int tps, int n_splits, int nb, int units, float scale_log2,
     float2* __restrict__ ws_ml, float* __restrict__ ws_o, uint32_t* __restrict__ arrivals,
     uint32_t* __restrict__ flags) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int RB = 1;          // row blocks of 32 columns per wave
   constexpr int COLS = RB * 32;
   constexpr int OSTR = D + 4;  // padded LDS row stride
   __shared__ float sm_m[W][COLS];
@@ -227,10 +231,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   __shared__ float sm_ml[COLS][2];
   __shared__ int s_last;
 
-  const int split = blockIdx.x % n_splits;
-  const int rk = blockIdx.x / n_splits;
+  // Work unit u = (request, KV head, split); with nb > 1 each unit is served by
+  // nb workgroups, one per block of COLS query rows.  Workgroup ids are laid
+  // out as [group of 8 units][row block][unit in group], so the row blocks of
+  // a unit land on the same XCD (ids equal mod 8) at nearly the same time and
+  // the second read of the unit's pages is served by that XCD's L2.
+  const int grp = blockIdx.x / (8 * nb), rem = blockIdx.x % (8 * nb);
+  const int b = rem / 8;
+  const int u = grp * 8 + rem % 8;
+  if (u >= units) return;
+  const int split = u % n_splits;
+  const int rk = u / n_splits;
   const int hk = rk % Hkv;
   const int r = rk / Hkv;
+  const int row0 = b * COLS;                    // first query row of this workgroup
+  const int rows_b = min(COLS, rows - row0);    // query rows of this workgroup
   const int L = clamp_ctx(ctx_lens[r], max_pages, flags);
   const int n_tiles = (L + kTileTokens - 1) / kTileTokens;
   const int active = active_splits(n_tiles, n_splits, tps);
@@ -274,8 +289,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   if (n > 0) {   // first tile's loads go out before the Q staging below
     int p0, p1;
     pages_i(0, p0, p1);
-    load_k<D>(ak, kp, p0, p1, hk, Hkv, lane);
-    load_v<D>(av, vp, p0, p1, hk, Hkv, lane);
+    load_k<D, NT>(ak, kp, p0, p1, hk, Hkv, lane);
+    load_v<D, NT>(av, vp, p0, p1, hk, Hkv, lane);
   }
 
   // Q^T operand B staged in LDS as [dim chunk][column] 16-byte cells: lane
@@ -284,8 +299,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   for (int idx = threadIdx.x; idx < (D / 8) * COLS; idx += blockDim.x) {
     const int ch = idx / COLS, c = idx % COLS;
     u32x4 v = u32x4{0, 0, 0, 0};
-    if (c < rows) {
-      const int g = c / Qn, i = c % Qn;
+    if (c < rows_b) {
+      const int g = (row0 + c) / Qn, i = (row0 + c) % Qn;
       v = *reinterpret_cast<const u32x4*>(q + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D + ch * 8);
     }
     sm_q[idx] = v;
@@ -389,7 +404,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
     scores(sk, s);
     consume(s, sv, [&](int rb, int v) {
       const int t = (v >> 2) * 8 + h * 4 + (v & 3);
-      const int i = (rb * 32 + col_l) % Qn;    // stride row of this column
+      const int i = (row0 + rb * 32 + col_l) % Qn;    // stride row of this column
       return t <= i;                           // t < Qn follows from i < Qn
     });
   }
@@ -404,7 +419,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
     const bool partial = tok0 + kTileTokens > L;
     f32x16 s[RB];
     scores(ck, s);
-    if constexpr (decltype(prefetch)::value) load_v<D>(nv, vp, np0, np1, hk, Hkv, lane);
+    if constexpr (decltype(prefetch)::value) load_v<D, NT>(nv, vp, np0, np1, hk, Hkv, lane);
     if (partial) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -422,16 +437,16 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
     for (; i + 2 < n; i += 2) {
       const int ta = first + i * W, tb = ta + W;
       pages_i(i + 1, p0, p1);
-      load_k<D>(bk, kp, p0, p1, hk, Hkv, lane);
+      load_k<D, NT>(bk, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, ak, av, bv, ta, p0, p1);
       pages_i(i + 2, p0, p1);
-      load_k<D>(ak, kp, p0, p1, hk, Hkv, lane);
+      load_k<D, NT>(ak, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, bk, bv, av, tb, p0, p1);
     }
     const int ta = first + i * W;
     if (i + 1 < n) {
       pages_i(i + 1, p0, p1);
-      load_k<D>(bk, kp, p0, p1, hk, Hkv, lane);
+      load_k<D, NT>(bk, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, ak, av, bv, ta, p0, p1);
       tile(NoPre{}, bk, bv, av, ta + W, 0, 0);
     } else {
@@ -476,7 +491,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
     }
   };
   if (wave < 2) put(wave ? sm_o1 : sm_o0, false);
-  if (threadIdx.x < rows) {
+  if (threadIdx.x < rows_b) {
     const int c = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
@@ -499,7 +514,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
 
   constexpr int V4 = D / 4;
   auto write_out = [&](int c, int d0, f32x4 v) {
-    const int g = c / Qn, i = c % Qn;
+    const int g = (row0 + c) / Qn, i = (row0 + c) % Qn;
     uint16_t* dst = out + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D + d0;
     const uint32_t lo = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
     const uint32_t hi = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
@@ -507,58 +522,100 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RB == 1 
   };
   if (active == 1) {
     // the only split: normalise straight from LDS
-    for (int idx = threadIdx.x; idx < rows * V4; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < rows_b * V4; idx += blockDim.x) {
       const int c = idx / V4, d0 = (idx % V4) * 4;
       const f32x4 a = *reinterpret_cast<const f32x4*>(&sm_o0[c * OSTR + d0]);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(&sm_o1[c * OSTR + d0]);
-      write_out(c, d0, (a + b) * (1.f / sm_ml[c][1]));
+      const f32x4 b2 = *reinterpret_cast<const f32x4*>(&sm_o1[c * OSTR + d0]);
+      write_out(c, d0, (a + b2) * (1.f / sm_ml[c][1]));
     }
     return;
   }
 
   // several splits: publish this split's partial, the last to arrive merges
-  const size_t base = (size_t(rk) * n_splits + split) * COLS;
-  if (threadIdx.x < rows) {
-    st_coherent(&ws_ml[base + threadIdx.x].x, sm_ml[threadIdx.x][0]);
-    st_coherent(&ws_ml[base + threadIdx.x].y, sm_ml[threadIdx.x][1]);
+  const int RSTR = nb * COLS;                   // partial rows per (request, KV head, split)
+  const size_t base = (size_t(rk) * n_splits + split) * RSTR + row0;
+  // Write-through stores, consecutive lanes on consecutive addresses, so each
+  // store instruction covers whole cache lines.
+  if (threadIdx.x < rows_b) {
+    const uint64_t ml = uint64_t(__float_as_uint(sm_ml[threadIdx.x][0])) |
+                        (uint64_t(__float_as_uint(sm_ml[threadIdx.x][1])) << 32);
+    st_coherent(reinterpret_cast<uint64_t*>(ws_ml + base + threadIdx.x), ml);
   }
-  for (int idx = threadIdx.x; idx < rows * V4; idx += blockDim.x) {
-    const int c = idx / V4, d0 = (idx % V4) * 4;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(&sm_o0[c * OSTR + d0]);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(&sm_o1[c * OSTR + d0]);
-    float* dst = ws_o + (base + c) * D + d0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st_coherent(dst + e, a[e] + b[e]);
+  for (int f = threadIdx.x; f < rows_b * D; f += blockDim.x) {
+    const int c = f / D, d = f % D;
+    st_coherent(ws_o + (base + c) * D + d, sm_o0[c * OSTR + d] + sm_o1[c * OSTR + d]);
   }
-  if (!arrive_last(&arrivals[rk], uint32_t(active), &s_last)) return;
+  if (!arrive_last(&arrivals[size_t(rk) * nb + b], uint32_t(active), &s_last)) return;
   // The partials were written through to memory before their writers
-  // arrived; drop any stale cached copies here, then read them plainly.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // per column: global max and the split weights (normaliser folded in)
+  // arrived; device-coherent loads read them from there.  (An acquire fence
+  // plus plain loads invalidates the XCD's L2 and costs far more.)
+#define MERGE_LD(p) ld_coherent(p)
+  // per row: global max and the split weights (normaliser folded in); the
+  // loads of each batch of splits are all issued before any is used
   __shared__ float sm_w[COLS][kMaxSplits];
-  const size_t base0 = size_t(rk) * n_splits * COLS;
-  if (threadIdx.x < rows) {
+  __shared__ float sm_sm[COLS][kMaxSplits];
+  const size_t base0 = size_t(rk) * n_splits * RSTR + row0;
+  if (threadIdx.x < rows_b) {
     const int c = threadIdx.x;
     float M = -INFINITY;
-    for (int s = 0; s < active; ++s) M = fmaxf(M, ws_ml[base0 + size_t(s) * COLS + c].x);
+    for (int s0 = 0; s0 < active; s0 += 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = (s0 + k < active)
+                   ? MERGE_LD(reinterpret_cast<const uint64_t*>(ws_ml + base0 + size_t(s0 + k) * RSTR + c))
+                   : 0ull;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < active) {
+          const float m = __uint_as_float(uint32_t(v[k]));
+          sm_sm[c][s0 + k] = m;
+          sm_w[c][s0 + k] = __uint_as_float(uint32_t(v[k] >> 32));
+          M = fmaxf(M, m);
+        }
+    }
     float Lsum = 0.f;
     for (int s = 0; s < active; ++s) {
-      const float2 ml = ws_ml[base0 + size_t(s) * COLS + c];
-      const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+      const float m = sm_sm[c][s];
+      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      Lsum += w * sm_w[c][s];
       sm_w[c][s] = w;
-      Lsum += w * ml.y;
     }
     const float inv = 1.f / Lsum;
     for (int s = 0; s < active; ++s) sm_w[c][s] *= inv;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < rows * V4; idx += blockDim.x) {
-    const int c = idx / V4, d0 = (idx % V4) * 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < active; ++s)
-      acc += *reinterpret_cast<const f32x4*>(ws_o + (base0 + size_t(s) * COLS + c) * D + d0) * sm_w[c][s];
-    write_out(c, d0, acc);
+  // every thread owns up to J 4-float pieces of the output; per split, the
+  // loads of all of them go out before the sums
+  constexpr int J = (COLS * V4 + 64 * W - 1) / (64 * W);
+  const int n4 = rows_b * V4;
+  f32x4 acc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < active; ++s) {
+    f32x4 v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int f4 = threadIdx.x + j * 64 * W;
+      v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (f4 < n4) {
+        const int c = f4 / V4, d0 = (f4 % V4) * 4;
+        const float* src = ws_o + (base0 + size_t(s) * RSTR + c) * D + d0;
+        v[j] = f32x4{MERGE_LD(src), MERGE_LD(src + 1), MERGE_LD(src + 2), MERGE_LD(src + 3)};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int f4 = threadIdx.x + j * 64 * W;
+      if (f4 < n4) acc[j] += v[j] * sm_w[f4 / V4][s];
+    }
   }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int f4 = threadIdx.x + j * 64 * W;
+    if (f4 < n4) write_out(f4 / V4, (f4 % V4) * 4, acc[j]);
+  }
+#undef MERGE_LD
 }
 
 // fp32 path: one wave per (request, kv head, split) x query column.
@@ -646,6 +703,7 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
   float2* ml = reinterpret_cast<float2*>(ws + Lw.attn_ml);
   float* po = reinterpret_cast<float*>(ws + Lw.attn_o);
   const int nwg = s.batch * s.n_kv_heads * p.n_splits;
+  const int grid8 = (nwg + 7) / 8 * 8;          // work units rounded up to a multiple of 8
   if (s.kv_dtype == ISD_BF16) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kn = static_cast<const uint16_t*>(k_new);
@@ -653,14 +711,17 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
     const uint16_t* kp = static_cast<const uint16_t*>(k_pages);
     const uint16_t* vp = static_cast<const uint16_t*>(v_pages);
     uint16_t* o = static_cast<uint16_t*>(out);
+    // one workgroup per 32 query rows of a (request, KV head, split)
     if (p.row_blocks == 1)
-      hipLaunchKernelGGL((attn_bf16<D, 1, kAttnWaves1>), dim3(nwg), dim3(64 * kAttnWaves1), 0, stream, qq, kn, vn, kp, vp, table,
-                         ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group, p.rows, s.max_pages,
-                         s.num_pages, p.tiles_per_split, p.n_splits, scale_log2, ml, po, arrivals, flags);
+      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, true>), dim3(grid8), dim3(64 * kAttnWaves), 0, stream,
+                         qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group,
+                         p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, 1, nwg, scale_log2, ml,
+                         po, arrivals, flags);
     else
-      hipLaunchKernelGGL((attn_bf16<D, 2, kAttnWaves2>), dim3(nwg), dim3(64 * kAttnWaves2), 0, stream, qq, kn, vn, kp, vp, table,
-                         ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group, p.rows, s.max_pages,
-                         s.num_pages, p.tiles_per_split, p.n_splits, scale_log2, ml, po, arrivals, flags);
+      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, false>), dim3(grid8 * p.row_blocks), dim3(64 * kAttnWaves), 0,
+                         stream, qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads,
+                         p.group, p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, p.row_blocks,
+                         nwg, scale_log2, ml, po, arrivals, flags);
   } else {
     const float* qq = static_cast<const float*>(q);
     hipLaunchKernelGGL((attn_split_f32<D>), dim3(nwg, p.rows), dim3(64), 0, stream, qq,

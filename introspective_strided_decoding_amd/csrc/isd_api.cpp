@@ -109,7 +109,7 @@ WsLayout ws_layout(const isd_shape& s) {
   const AcceptPlan c = plan_accept(s);
   size_t off = kHeaderBytes;
   L.attn_cnt = off;
-  off = align_up(off + (size_t)s.batch * s.n_kv_heads * 4, 256);
+  off = align_up(off + (size_t)s.batch * s.n_kv_heads * a.row_blocks * 4, 256);
   L.cmt_cnt = off;
   off = align_up(off + (size_t)s.batch * 4, 256);
   L.zero_end = off;

@@ -11,16 +11,9 @@ namespace isd {
 
 constexpr int kPage = 16;          // tokens per KV page
 constexpr int kTileTokens = 32;    // tokens per attention tile (two pages)
-// Waves per attention workgroup: eight with one 32-column block (two waves
-// per SIMD), four with two blocks (their registers allow one wave per SIMD).
-#ifndef ISD_ATTN_WAVES1
-#define ISD_ATTN_WAVES1 8
-#endif
-constexpr int kAttnWaves1 = ISD_ATTN_WAVES1;
-constexpr int kAttnWaves2 = 4;
-#ifndef ISD_KV_NONTEMPORAL
-#define ISD_KV_NONTEMPORAL 1
-#endif
+// Waves per attention workgroup (two per SIMD; each wave takes 32-token tiles
+// round-robin for one block of 32 query rows).
+constexpr int kAttnWaves = 8;
 constexpr size_t kHeaderBytes = 256;
 
 // How the KV walk of isd_attention is split across workgroups.
@@ -46,7 +39,7 @@ struct AcceptPlan {
 
 struct WsLayout {
   size_t flags = 0;          // uint32 device flags
-  size_t attn_cnt = 0;       // uint32 per (request, kv head): split arrivals
+  size_t attn_cnt = 0;       // uint32 per (request, kv head, row block): split arrivals
   size_t cmt_cnt = 0;        // uint32 per request: commit workgroups arrived
   size_t zero_end = 0;       // [0, zero_end) is zeroed by isd_workspace_init
   size_t attn_ml = 0;        // float2 (m, l) per partial row

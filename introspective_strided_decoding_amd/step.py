@@ -132,6 +132,25 @@ class DeviceStep:
         L = self.lora
         _lib.isd_lora_delta(L["X"], L["A_t"], L["B_t"], L["mask_rows"], L["Y"], L["ws"], stream=stream)
 
+    def capture(self):
+        """Record one ``run()`` into a HIP graph (``torch.cuda.CUDAGraph``) and return it.
+
+        Every call of the step enqueues kernels only (no allocation, no memset, no
+        host synchronisation), and the workspace counters the kernels use are
+        rewound by the kernels themselves, so the graph can be replayed any number
+        of times; each replay recomputes the step from the buffers' current contents.
+        """
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()                      # first launches outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run()
+        return graph
+
     def run(self, stream=None):
         """One ISD step: attention -> accept -> commit (-> LoRA delta) (-> proposals)."""
         self.attention(stream)
