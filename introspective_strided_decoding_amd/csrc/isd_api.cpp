@@ -78,7 +78,11 @@ AttnPlan plan_attention(const isd_shape& s) {
   const long long pairs = (long long)s.batch * s.n_kv_heads;
   const int target = ISD_ATTN_TARGET_WGS;
   int splits = std::max(1, ceil_div(target, pairs));
-  p.tiles_per_split = std::max(8, ceil_div(p.tiles_max, splits));
+  // bf16 workgroups stage Q and fill a load pipeline first, so a split gets at
+  // least 8 tiles; the fp32 path (one wave per query column, tokens one at a
+  // time) splits down to single tiles.
+  const int min_tps = (s.kv_dtype == ISD_BF16) ? 8 : 1;
+  p.tiles_per_split = std::max(min_tps, ceil_div(p.tiles_max, splits));
   // the final merge keeps one weight per split in LDS: at most 64 splits
   p.tiles_per_split = std::max(p.tiles_per_split, ceil_div(p.tiles_max, 64));
   p.n_splits = std::max(1, ceil_div(p.tiles_max, p.tiles_per_split));
