@@ -37,6 +37,7 @@ namespace isd {
 namespace {
 
 constexpr int kMaxSplits = 64;
+constexpr int kRankMax = 256;     // batches up to this size are served longest request first
 constexpr int kMaxRows = 64;
 constexpr int kMaxQ = 64;
 
@@ -241,9 +242,31 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int u = grp * 8 + rem % 8;
   if (u >= units) return;
   const int split = u % n_splits;
-  const int rk = u / n_splits;
-  const int hk = rk % Hkv;
-  const int r = rk / Hkv;
+  const int hk = (u / n_splits) % Hkv;
+  // Requests are served longest first (ties in index order): long contexts
+  // start early and short ones fill in at the end.  For up to kRankMax
+  // requests every workgroup ranks the lengths itself; beyond that, index order.
+  const int rank = u / (n_splits * Hkv);
+  const int B = units / (n_splits * Hkv);
+  int r = rank;
+  if (B <= kRankMax) {
+    __shared__ int sm_len[kRankMax];
+    __shared__ int sm_req;
+    for (int t = threadIdx.x; t < B; t += blockDim.x) sm_len[t] = ctx_lens[t];
+    __syncthreads();
+    for (int t = threadIdx.x; t < B; t += blockDim.x) {
+      const int lt = sm_len[t];
+      int before = 0;
+      for (int j = 0; j < B; ++j) {
+        const int lj = sm_len[j];
+        before += (lj > lt || (lj == lt && j < t)) ? 1 : 0;
+      }
+      if (before == rank) sm_req = t;
+    }
+    __syncthreads();
+    r = sm_req;
+  }
+  const int rk = r * Hkv + hk;
   const int row0 = b * COLS;                    // first query row of this workgroup
   const int rows_b = min(COLS, rows - row0);    // query rows of this workgroup
   const int L = clamp_ctx(ctx_lens[r], max_pages, flags);
