@@ -25,9 +25,10 @@ Modules:
   lora       the gated low-rank delta of R-ISD
   tpf        expected acceptance, tokens per forward, the compute-bound identity
   propose    drawing the next N tokens at the MASK rows (sampling or argmax)
+  loop       the multi-step decoding loop: per-request VERIFY / REPROPOSE bookkeeping
 
 Every function is pinned by a test in ``tests/test_oracle_*.py`` against a
 closed form, a printed value, a library routine or a brute-force count.
 """
 
-from . import accept, attention, commit, lora, philox, propose, tpf  # noqa: F401
+from . import accept, attention, commit, lora, loop, philox, propose, tpf  # noqa: F401

@@ -1,0 +1,104 @@
+"""The multi-step ISD decoding loop on a stationary batch, in plain Python.
+
+TEST INFRASTRUCTURE ONLY (see the package header).
+
+What the pages fix: every forward verifies the previous proposals and proposes
+N new ones ([hypho] "Introspective Strided Decoding（ISD）"); each request
+advances on its own, with no batch synchronisation ([project], caption on SDAR
+synchronisation); the TPF column of [hotdry] "Token 生成的核心参数与验收机制"
+is reproduced by a cycle that keeps A + [A < N] tokens and spends 1 + [A < N]
+forwards (``oracle.tpf``): after a rejection one more forward proposes again
+from the corrected prefix.
+
+The loop, per request (the reading taken where the pages are silent):
+
+* state: mode (VERIFY or REPROPOSE), the stride's proposals x_1..x_N, ``pos``
+  (the ``positions`` value the next forward is called with), committed tokens
+  and forwards so far;
+* one forward of the batch = the accept test on the current proposals, then
+  N proposals from the MASK rows (both with Philox draws at this forward's
+  step), then ``advance``:
+
+  - VERIFY, A = N: tokens += N; the MASK proposals become the next stride;
+    pos += N (x_1 of the next stride is the token after x_N).
+  - VERIFY, A < N: tokens += A + 1 (x_1..x_A and the resampled token); the
+    MASK proposals followed a rejected prefix and are dropped; mode becomes
+    REPROPOSE and pos += A + 1 - N, so that the re-proposing forward's MASK
+    row k proposes the token at (old pos) + A + 1 + k under the proposal
+    positions of ``oracle.propose``.
+  - REPROPOSE: its accept result is ignored and nothing is committed; its MASK
+    proposals become the next stride; mode becomes VERIFY and pos += N.
+  - forwards += 1 in every case.
+
+* KV rows committed by a forward: min(A, N-1) CLEAN rows in VERIFY mode, none
+  in REPROPOSE mode (``advance`` returns the gated counts).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import accept, propose
+
+VERIFY = 0
+REPROPOSE = 1
+
+
+@dataclass
+class LoopState:
+    mode: np.ndarray          # [B] VERIFY / REPROPOSE
+    proposals: np.ndarray     # [B, N] the stride's x_1..x_N
+    pos: np.ndarray           # [B] positions argument of the next forward
+    tokens: np.ndarray        # [B] committed tokens so far
+    forwards: np.ndarray      # [B] forwards so far
+
+    @classmethod
+    def start(cls, proposals, positions):
+        proposals = np.array(proposals, dtype=np.int64)
+        B = proposals.shape[0]
+        return cls(mode=np.full(B, VERIFY, dtype=np.int64), proposals=proposals,
+                   pos=np.array(positions, dtype=np.int64), tokens=np.zeros(B, dtype=np.int64),
+                   forwards=np.zeros(B, dtype=np.int64))
+
+    def copy(self):
+        return LoopState(self.mode.copy(), self.proposals.copy(), self.pos.copy(), self.tokens.copy(),
+                         self.forwards.copy())
+
+
+def advance(state: LoopState, accept_len, n_out, next_proposals, n_commit):
+    """Apply one forward's results to every request; returns the gated commit counts."""
+    n = state.proposals.shape[1]
+    gated = np.array(n_commit, dtype=np.int64).copy()
+    for r in range(state.mode.shape[0]):
+        state.forwards[r] += 1
+        if state.mode[r] == VERIFY:
+            a = int(accept_len[r])
+            state.tokens[r] += int(n_out[r])
+            if a == n:
+                state.proposals[r] = next_proposals[r]
+                state.pos[r] += n
+            else:
+                state.mode[r] = REPROPOSE
+                state.pos[r] += int(n_out[r]) - n
+        else:
+            gated[r] = 0
+            state.proposals[r] = next_proposals[r]
+            state.mode[r] = VERIFY
+            state.pos[r] += n
+    return gated
+
+
+def forward(state: LoopState, p_logits, q_logits, mask_logits, req_ids, seed, step: int,
+            lse_p=None, lse_q=None):
+    """One forward of the batch on the oracle: accept, proposals, advance.
+
+    Returns (accept results, proposal margins [B, N], gated n_commit [B]).
+    """
+    res = accept.isd_accept(p_logits, q_logits, state.proposals, req_ids, state.pos, seed, step,
+                            lse_p=lse_p, lse_q=lse_q)
+    nxt, margins = propose.isd_propose(mask_logits, req_ids, state.pos, seed, step)
+    gated = advance(state, [o.accept_len for o in res], [o.n_out for o in res], nxt,
+                    [o.n_commit for o in res])
+    return res, margins, gated

@@ -1,0 +1,122 @@
+"""Pins for oracle.loop (the multi-step decoding loop).
+
+* The printed TPF column ([hotdry] "Token 生成的核心参数与验收机制", stored in
+  tests/golden/isd_acceptance_table.json): ``advance`` driven by accept
+  lengths drawn with per-position acceptance 0.9 gives tokens / forwards
+  within 4 standard errors of each printed TPF (plus its rounding), for
+  N = 2, 3, 4, 5, 8.
+* Bookkeeping invariants on real oracle forwards: every request spends one
+  forward per call; committed tokens are the n_out of its VERIFY forwards;
+  every REPROPOSE forward follows a rejecting VERIFY forward and commits no
+  KV rows; the positions move by the committed tokens, less N when the last
+  forward was a rejecting VERIFY.
+* The compute-bound identity on measured counts: TPF / OH = TPF^2 / Q.
+* End to end on small logits with per-row acceptance 0.9: the oracle's own
+  accept test and proposals inside the loop give the closed-form TPF.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import loop, propose, tpf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "isd_acceptance_table.json")
+
+
+def _table():
+    return {row["N"]: row for row in json.load(open(GOLDEN))["rows"]}
+
+
+def _geometric_accepts(rng, n, alpha, size):
+    """A = 1 + number of leading successes among N-1 Bernoulli(alpha) tests."""
+    tests = rng.random((size, n - 1)) < alpha
+    lead = np.where(tests.all(axis=1), n - 1, np.argmin(tests, axis=1))
+    return 1 + lead
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 8])
+def test_advance_reproduces_printed_tpf(n):
+    rng = np.random.Generator(np.random.PCG64(100 + n))
+    B, T = 512, 400
+    st = loop.LoopState.start(np.zeros((B, n), dtype=np.int64), np.full(B, 1000))
+    nxt = np.zeros((B, n), dtype=np.int64)
+    for _ in range(T):
+        a = _geometric_accepts(rng, n, 0.9, B)
+        loop.advance(st, a, a + (a < n), nxt, np.minimum(a, n - 1))
+    per_req = st.tokens / st.forwards
+    tpf_hat = st.tokens.sum() / st.forwards.sum()
+    se = per_req.std(ddof=1) / np.sqrt(B)
+    printed = _table()[n]["TPF"]
+    assert abs(tpf_hat - printed) < 4 * se + 0.005 + 1.0 / T, (n, tpf_hat, printed, se)
+    assert abs(tpf_hat - tpf.tpf_closed_form(n, 0.9)) < 4 * se + 1.0 / T
+
+
+def test_bookkeeping_invariants():
+    n, B = 4, 200
+    rng = np.random.Generator(np.random.PCG64(7))
+    st = loop.LoopState.start(rng.integers(0, 50, size=(B, n)), np.full(B, 500))
+    pos0 = st.pos.copy()
+    n_out_verify = np.zeros(B, dtype=np.int64)
+    last_rejecting_verify = np.zeros(B, dtype=bool)
+    for t in range(60):
+        mode_before = st.mode.copy()
+        a = _geometric_accepts(rng, n, 0.8, B)
+        n_out = a + (a < n)
+        nxt = rng.integers(0, 50, size=(B, n))
+        gated = loop.advance(st, a, n_out, nxt, np.minimum(a, n - 1))
+        was_verify = mode_before == loop.VERIFY
+        n_out_verify += np.where(was_verify, n_out, 0)
+        assert (gated[~was_verify] == 0).all()
+        assert (gated[was_verify] == np.minimum(a, n - 1)[was_verify]).all()
+        # a REPROPOSE forward only ever follows a rejecting VERIFY forward
+        assert (st.mode[was_verify & (a < n)] == loop.REPROPOSE).all()
+        assert (st.mode[~was_verify] == loop.VERIFY).all()
+        # the next stride is the MASK proposals unless the forward rejected
+        keep = was_verify & (a < n)
+        assert (st.proposals[~keep] == nxt[~keep]).all()
+        last_rejecting_verify = was_verify & (a < n)
+    assert (st.forwards == 60).all()
+    assert (st.tokens == n_out_verify).all()
+    assert (st.pos - pos0 == st.tokens - n * last_rejecting_verify).all()
+
+
+def test_identity_on_measured_counts():
+    n = 4
+    q = tpf.queries_per_forward(n)
+    rng = np.random.Generator(np.random.PCG64(3))
+    st = loop.LoopState.start(np.zeros((64, n), dtype=np.int64), np.full(64, 100))
+    for _ in range(100):
+        a = _geometric_accepts(rng, n, 0.9, 64)
+        loop.advance(st, a, a + (a < n), np.zeros((64, n), dtype=np.int64), np.minimum(a, n - 1))
+    tokens, forwards = int(st.tokens.sum()), int(st.forwards.sum())
+    t = tokens / forwards
+    oh = forwards * q / tokens
+    assert abs(t / oh - t * t / q) < 1e-12
+
+
+def test_end_to_end_oracle_loop_matches_closed_form():
+    """Oracle accept test and proposals inside the loop, logits with per-row acceptance 0.9."""
+    from workloads import get_config, make_workload
+    n, B, T = 4, 48, 40
+    cfg = get_config("tiny_fp32", batch=B, stride_n=n, vocab=256, ctx=16, n_q_heads=1, n_kv_heads=1)
+    pool = []
+    for k in range(4):
+        wl = make_workload(cfg, seed=500 + k, tau_mode="row")
+        extra = np.random.Generator(np.random.PCG64(900 + k)).normal(0.0, 3.0, size=(B, 1, 256))
+        mask = np.concatenate([extra, wl.q_logits.astype(np.float64)], axis=1)
+        pool.append((wl.p_logits, wl.q_logits, mask))
+    req_ids = np.arange(B) + 7
+    seed = (11, 22)
+    st = loop.LoopState.start(np.zeros((B, n), dtype=np.int64), np.full(B, 64))
+    # the first stride comes from the forward before the loop (pool entry 3's MASK rows)
+    st.proposals, _ = propose.isd_propose(pool[3][2], req_ids, st.pos - n, seed, 10**6)
+    for t in range(T):
+        p, q, _ = pool[(t - 1) % 4]
+        loop.forward(st, p, q, pool[t % 4][2], req_ids, seed, t)
+    per_req = st.tokens / st.forwards
+    tpf_hat = st.tokens.sum() / st.forwards.sum()
+    se = per_req.std(ddof=1) / np.sqrt(B)
+    assert abs(tpf_hat - tpf.tpf_closed_form(n, 0.9)) < 4 * se + 1.0 / T, (tpf_hat, se)
