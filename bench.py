@@ -4,7 +4,9 @@ A step is one pass of the whole hot path over the batch: isd_attention ->
 isd_accept -> kv_commit (+ isd_lora_delta for the R-ISD workload), enqueued on
 one stream.  The MASK-row proposals for the next step (isd_propose, sampling
 and argmax policies) are timed in a loop of their own after the steps and
-reported under "propose"; they do not enter "value".
+reported under "propose"; they do not enter "value".  Neither do "graph" (the
+step replayed from HIP graphs) and "loop" (whole forwards of the multi-step
+decoding loop, with its measured tokens per forward).
 
 Inputs are synthetic (workloads/), generated on the host and resident in HBM
 before the timed region.  To keep the Infinity Cache (256 MB) from serving
@@ -139,6 +141,7 @@ def main(argv=None):
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated in the timed loop (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--no-loop", action="store_true", help="skip the decoding-loop measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device copy before the timed loop (a known-size reference "
                          "for hardware traffic counters)")
@@ -157,7 +160,8 @@ def main(argv=None):
 
     cfg = get_config(args.config)
     t_gen = time.perf_counter()
-    wl = make_workload(cfg, with_mask_logits=True)
+    loop_forwards = 0 if args.no_loop else max(20, min(200, args.steps))
+    wl = make_workload(cfg, with_mask_logits=True, extra_tokens=(loop_forwards + 8) * (cfg.stride_n - 1))
     t_gen = time.perf_counter() - t_gen
     nbytes = algorithmic_bytes(wl)
     step_bytes = nbytes["attention"] + nbytes["accept"]
@@ -245,6 +249,36 @@ def main(argv=None):
                      "graph_ms_per_step": round(g_elapsed * 1e3 / args.steps, 5)}
             del graphs
 
+    # the decoding loop: whole forwards (attention, accept, proposals, bookkeeping, commit in place)
+    loop = None
+    if loop_forwards and not use_lora:
+        # every forward verifies proposals drawn from the q rows it is tested against, so the
+        # per-position acceptance is the workload's target
+        lp = DeviceStep.from_arrays(wl, device=dev, max_ctx=int(wl.ctx_lens.max()) + (loop_forwards + 8) * cfg.stride_n,
+                                    commit_in_place=True)
+        row0 = lp.mask_logits[:, :1].clone()
+        lp.mask_logits.copy_(torch.cat([row0, lp.q_logits], dim=1))
+        lp.loop_start()
+        for t in range(4):
+            lp.loop_forward(step=t)
+        torch.cuda.synchronize()
+        tok0 = int(lp.extra["tokens"].sum().item())
+        fw0 = int(lp.extra["forwards"].sum().item())
+        t0 = time.perf_counter()
+        for t in range(4, 4 + loop_forwards):
+            lp.loop_forward(step=t)
+        torch.cuda.synchronize()
+        l_elapsed = time.perf_counter() - t0
+        tokens = int(lp.extra["tokens"].sum().item()) - tok0
+        fws = int(lp.extra["forwards"].sum().item()) - fw0
+        loop = {"what": "decoding loop: attention, accept, sampled proposals, bookkeeping, commit in place",
+                "forwards": loop_forwards,
+                "forwards_per_s": round(loop_forwards / l_elapsed, 2),
+                "tokens_per_s": round(tokens / l_elapsed, 1),
+                "tpf": round(tokens / fws, 4),
+                "ms_per_forward": round(l_elapsed * 1e3 / loop_forwards, 5)}
+        del lp
+
     # MASK-row proposals, timed on their own (both policies)
     from introspective_strided_decoding_amd._lib import PROPOSE_ARGMAX, PROPOSE_SAMPLE
     prop = {}
@@ -310,6 +344,7 @@ def main(argv=None):
         },
         "propose": prop,
         "graph": graph,
+        "loop": loop,
         "input_gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:

@@ -269,6 +269,51 @@ isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const in
                        size_t ws_bytes, hipStream_t stream);
 
 /*
+ * isd_loop_advance -- per-request bookkeeping of the multi-step decoding loop.
+ *
+ * Definition (every forward verifies the previous proposals and proposes N
+ * new ones: "I-DLM：扩散模型如何用'自省一致性'追上自回归模型质量", section
+ * "Introspective Strided Decoding（ISD）"; each request advances on its own:
+ * I-DLM project page, caption on SDAR synchronisation; a rejection costs one
+ * more forward that proposes again from the corrected prefix, the reading
+ * that reproduces the TPF column of "自省扩散语言模型的 token 生成机制与工程
+ * 实践", section "Token 生成的核心参数与验收机制").  A forward of the batch is
+ * isd_attention -> isd_accept -> isd_propose -> isd_loop_advance -> kv_commit
+ * on one stream, with isd_accept and isd_propose called with `proposals` and
+ * `positions` below.  Per request r:
+ *
+ *   forwards[r] += 1, and
+ *   mode VERIFY, accept_len A = N: tokens += N, proposals <- next_proposals,
+ *                                   positions += N;
+ *   mode VERIFY, A < N:            tokens += n_out (= A + 1), proposals kept,
+ *                                   mode <- REPROPOSE, positions += n_out - N
+ *                                   (so the re-proposing forward's MASK row k
+ *                                   proposes the token right after the
+ *                                   committed prefix, plus k);
+ *   mode REPROPOSE:                its accept result is ignored, n_commit <- 0
+ *                                   (no KV rows committed), proposals <-
+ *                                   next_proposals, mode <- VERIFY,
+ *                                   positions += N.
+ *
+ *   accept_len, n_out [B] int32   this forward's isd_accept outputs
+ *   next_proposals [B][N] int32   this forward's isd_propose output
+ *   n_commit  [B] int32           isd_accept's output, gated in place
+ *   mode      [B] int32           ISD_LOOP_VERIFY / ISD_LOOP_REPROPOSE, in/out
+ *   proposals [B][N] int32        the stride's x_1..x_N, in/out
+ *   positions [B] int32           positions argument of the next forward, in/out;
+ *                                 start at >= N - 1 so it stays non-negative
+ *   tokens, forwards [B] int64    running counts, in/out (start at 0)
+ *
+ * TPF of a request = tokens / forwards.  No workspace; no flags.
+ */
+#define ISD_LOOP_VERIFY 0
+#define ISD_LOOP_REPROPOSE 1
+isd_status isd_loop_advance(const isd_shape* shape, const int32_t* accept_len, const int32_t* n_out,
+                            const int32_t* next_proposals, int32_t* n_commit, int32_t* mode,
+                            int32_t* proposals, int32_t* positions, int64_t* tokens,
+                            int64_t* forwards, hipStream_t stream);
+
+/*
  * isd_lora_delta -- the gated rank-r delta of Residual ISD (R-ISD).
  *
  * Definition ("自省扩散语言模型的 token 生成机制与工程实践", section "Token 生成

@@ -26,9 +26,11 @@ STATUS = {0: "ISD_OK", 1: "ISD_ERR_NULL", 2: "ISD_ERR_SHAPE", 3: "ISD_ERR_DTYPE"
 
 # Every symbol include/isd.h declares.
 EXPORTS = ("isd_workspace_bytes", "isd_workspace_init", "isd_read_flags", "isd_attention",
-           "isd_accept", "kv_commit", "isd_propose", "isd_lora_workspace_bytes", "isd_lora_delta",
+           "isd_accept", "kv_commit", "isd_propose", "isd_loop_advance", "isd_lora_workspace_bytes",
+           "isd_lora_delta",
            "isd_status_string", "isd_last_error", "isd_abi_version")
 PROPOSE_SAMPLE, PROPOSE_ARGMAX = 0, 1
+LOOP_VERIFY, LOOP_REPROPOSE = 0, 1
 
 
 class IsdError(RuntimeError):
@@ -84,6 +86,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, SZ, P]),
         "kv_commit": (I32, [SP, P, P, P, P, P, P, P, P, P, SZ, P]),
         "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, I32, P, P, SZ, P]),
+        "isd_loop_advance": (I32, [SP, P, P, P, P, P, P, P, P, P, P]),
         "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
         "isd_lora_delta": (I32, [I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
         "isd_status_string": (ctypes.c_char_p, [I32]),
@@ -218,6 +221,18 @@ def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, 
         int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(mode),
         _ptr(proposals, "proposals", i32, B * N),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def isd_loop_advance(shape: Shape, accept_len, n_out, next_proposals, n_commit, mode, proposals,
+                     positions, tokens, forwards, stream=None) -> None:
+    B, N = shape.batch, shape.stride_n
+    i32, i64 = torch.int32, torch.int64
+    _check("isd_loop_advance", LIB.isd_loop_advance(
+        ctypes.byref(shape.c()), _ptr(accept_len, "accept_len", i32, B), _ptr(n_out, "n_out", i32, B),
+        _ptr(next_proposals, "next_proposals", i32, B * N), _ptr(n_commit, "n_commit", i32, B),
+        _ptr(mode, "mode", i32, B), _ptr(proposals, "proposals", i32, B * N),
+        _ptr(positions, "positions", i32, B), _ptr(tokens, "tokens", i64, B),
+        _ptr(forwards, "forwards", i64, B), _stream(stream)))
 
 
 def isd_lora_workspace_bytes(n_mask: int, d_in: int, rank: int) -> int:

@@ -144,7 +144,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 2; }
+int32_t isd_abi_version(void) { return 3; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {
@@ -268,6 +268,20 @@ isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const in
   hipError_t e = launch_propose(*shape, mask_logits, req_ids, positions, seed_lo, seed_hi, step, mode,
                                 proposals, static_cast<char*>(workspace), ws_layout(*shape), stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_propose");
+}
+
+isd_status isd_loop_advance(const isd_shape* shape, const int32_t* accept_len, const int32_t* n_out,
+                            const int32_t* next_proposals, int32_t* n_commit, int32_t* mode,
+                            int32_t* proposals, int32_t* positions, int64_t* tokens, int64_t* forwards,
+                            hipStream_t stream) {
+  isd_status st = check_shape(shape);
+  if (st != ISD_OK) return st;
+  if (!accept_len || !n_out || !next_proposals || !n_commit || !mode || !proposals || !positions ||
+      !tokens || !forwards)
+    return ISD_ERR_NULL;
+  hipError_t e = launch_loop_advance(shape->batch, shape->stride_n, accept_len, n_out, next_proposals,
+                                     n_commit, mode, proposals, positions, tokens, forwards, stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_loop_advance");
 }
 
 size_t isd_lora_workspace_bytes(int32_t n_mask, int32_t d_in, int32_t rank) {

@@ -104,6 +104,11 @@ hipError_t launch_propose(const isd_shape& s, const void* mask_logits, const int
                           const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
                           int mode, int32_t* proposals, char* ws, const WsLayout& L, hipStream_t stream);
 
+hipError_t launch_loop_advance(int B, int N, const int32_t* accept_len, const int32_t* n_out,
+                               const int32_t* next_proposals, int32_t* n_commit, int32_t* mode,
+                               int32_t* proposals, int32_t* positions, int64_t* tokens, int64_t* forwards,
+                               hipStream_t stream);
+
 hipError_t launch_workspace_init(void* ws, size_t header_bytes, double* exp_table, hipStream_t stream);
 
 struct LoraLayout {

@@ -128,6 +128,30 @@ class DeviceStep:
                          self.seed if seed is None else seed, self.step if step is None else step,
                          mode, self.next_proposals, self.workspace, stream=stream)
 
+    def loop_start(self):
+        """Device state of the multi-step loop: every request starts verifying its proposals."""
+        B = self.shape.batch
+        dev = self.proposals.device
+        self.extra["mode"] = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.extra["tokens"] = torch.zeros(B, dtype=torch.int64, device=dev)
+        self.extra["forwards"] = torch.zeros(B, dtype=torch.int64, device=dev)
+
+    def loop_advance(self, stream=None):
+        e = self.extra
+        _lib.isd_loop_advance(self.shape, self.accept_len, self.n_out, self.next_proposals, self.n_commit,
+                              e["mode"], self.proposals, self.positions, e["tokens"], e["forwards"],
+                              stream=stream)
+
+    def loop_forward(self, step: int, attention: bool = True, stream=None):
+        """One forward of the decoding loop: attention, accept, proposals, bookkeeping, commit."""
+        if attention:
+            self.attention(stream)
+        self.accept(stream, step=step)
+        self.propose(stream, step=step)
+        self.loop_advance(stream)
+        if attention:
+            self.commit(stream)
+
     def lora_delta(self, stream=None):
         L = self.lora
         _lib.isd_lora_delta(L["X"], L["A_t"], L["B_t"], L["mask_rows"], L["Y"], L["ws"], stream=stream)

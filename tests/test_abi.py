@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 2
+    assert LIB.isd_abi_version() == 3
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"
@@ -126,6 +126,17 @@ def test_propose_validation():
     assert call(ws=None) == 1
     assert call(shape=_shape(batch=20000, stride_n=4), ws_bytes=8) == 5   # B * N rows > 65535
     assert call(shape=_shape(logit_dtype=5)) == 3
+
+
+def test_loop_advance_validation():
+    s = _shape()
+    args = [FAKE] * 9
+    assert LIB.isd_loop_advance(None, *args, None) == 1
+    for i in range(9):
+        bad = list(args)
+        bad[i] = None
+        assert LIB.isd_loop_advance(ctypes.byref(s.c()), *bad, None) == 1, i
+    assert LIB.isd_loop_advance(ctypes.byref(_shape(stride_n=1).c()), *args, None) == 2
 
 
 def test_workspace_init_and_flags_validation():

@@ -1,0 +1,152 @@
+"""The multi-step decoding loop on the GPU.
+
+* Transition parity: a full loop (attention, accept, proposals, bookkeeping,
+  commit) runs for a number of forwards; before each forward the GPU's loop
+  state is read back and the oracle applies the same forward to it (accept
+  test, proposals, bookkeeping, commit).  Accept lengths, committed tokens,
+  proposals, the new state and the gated commit counts must be identical,
+  except for requests with a near-tie decision; the KV pools and lengths are
+  compared bit for bit at the end, and a last attention call is checked on
+  the grown contexts.
+* TPF: the loop's measured tokens per forward (accept + proposals +
+  bookkeeping, logits with per-row acceptance 0.9) reproduce the closed form
+  and the printed TPF column for N = 2, 3, 4, 5, 8.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from parity import ACCEPT_NEAR_TIE, PROPOSE_NEAR_TIE, RESAMPLE_NEAR_TIE, check_attention, device_step, needs_gpu
+from workloads import get_config, make_workload
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "isd_acceptance_table.json")
+
+
+def _round(x, dtype):
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32))
+    return (t.to(torch.bfloat16).float() if dtype == "bf16" else t).numpy()
+
+
+def _pool(cfg, entries, seed0, tau_mode):
+    """Logit sets for successive forwards: (p rows, q rows, MASK rows = [free row | q rows])."""
+    out = []
+    for k in range(entries):
+        wl = make_workload(cfg, seed=seed0 + k, tau_mode=tau_mode)
+        row0 = np.random.Generator(np.random.PCG64(seed0 + 77 + k)).normal(
+            0.0, cfg.logit_std, size=(cfg.batch, 1, cfg.vocab))
+        mask = np.concatenate([_round(row0, cfg.dtype), wl.q_logits], axis=1)
+        out.append((wl.p_logits, wl.q_logits, mask))
+    return out
+
+
+def _dev(x, like):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=like.device, dtype=like.dtype)
+
+
+def test_loop_transitions_match_oracle():
+    from oracle import accept as oaccept
+    from oracle import loop as oloop
+    from oracle import propose as oprop
+    from oracle.commit import kv_commit as ocommit
+    from oracle.attention import stride_attention
+
+    T, K = 12, 3
+    cfg = get_config("b8_ctx2k", batch=12, ctx=40, vocab=1000, stride_n=4)
+    n = cfg.stride_n
+    wl = make_workload(cfg, seed=61, with_mask_logits=True, extra_tokens=T * (n - 1))
+    pool = _pool(cfg, K, 300, "batch")
+    st = device_step(wl, commit_in_place=True)
+    st.loop_start()
+    seeds = wl.philox_seed
+    k_pool, v_pool, ctx = wl.k_pool.copy(), wl.v_pool.copy(), wl.ctx_lens.copy()
+    near = 0
+    for t in range(T):
+        p, q = (wl.p_logits, wl.q_logits) if t == 0 else pool[(t - 1) % K][:2]
+        mask = pool[t % K][2]
+        st.p_logits.copy_(_dev(p, st.p_logits))
+        st.q_logits.copy_(_dev(q, st.q_logits))
+        st.mask_logits.copy_(_dev(mask, st.mask_logits))
+        pre = oloop.LoopState(st.extra["mode"].cpu().numpy().astype(np.int64),
+                              st.proposals.cpu().numpy().astype(np.int64),
+                              st.positions.cpu().numpy().astype(np.int64),
+                              st.extra["tokens"].cpu().numpy(), st.extra["forwards"].cpu().numpy())
+        st.loop_forward(step=t)
+        torch.cuda.synchronize()
+        # the oracle applies the same forward to the same state
+        res = oaccept.isd_accept(p, q, pre.proposals, wl.req_ids, pre.pos, seeds, t)
+        nxt, margins = oprop.isd_propose(mask, wl.req_ids, pre.pos, seeds, t)
+        post = pre.copy()
+        gated = oloop.advance(post, [o.accept_len for o in res], [o.n_out for o in res], nxt,
+                              [o.n_commit for o in res])
+        tie = np.zeros(cfg.batch, dtype=bool)
+        for r, o in enumerate(res):
+            verifying = pre.mode[r] == oloop.VERIFY
+            tie[r] = verifying and (bool((o.accept_margins < ACCEPT_NEAR_TIE).any())
+                                    or o.resample_margin < RESAMPLE_NEAR_TIE)
+            tie[r] |= bool((margins[r] < PROPOSE_NEAR_TIE).any())
+        near += int(tie.sum())
+        ok = ~tie
+        got = {k: v.cpu().numpy() for k, v in (("accept_len", st.accept_len), ("n_out", st.n_out),
+                                                ("next", st.next_proposals), ("n_commit", st.n_commit),
+                                                ("mode", st.extra["mode"]), ("proposals", st.proposals),
+                                                ("positions", st.positions), ("tokens", st.extra["tokens"]),
+                                                ("forwards", st.extra["forwards"]))}
+        verifying = pre.mode == oloop.VERIFY
+        assert (got["accept_len"][ok & verifying] == np.array([o.accept_len for o in res])[ok & verifying]).all(), t
+        assert (got["n_out"][ok & verifying] == np.array([o.n_out for o in res])[ok & verifying]).all(), t
+        assert (got["next"][ok] == nxt[ok]).all(), t
+        assert (got["n_commit"][ok] == gated[ok]).all(), t
+        assert (got["mode"][ok] == post.mode[ok]).all(), t
+        assert (got["proposals"][ok] == post.proposals[ok]).all(), t
+        assert (got["positions"][ok] == post.pos[ok]).all(), t
+        assert (got["tokens"][ok] == post.tokens[ok]).all(), t
+        assert (got["forwards"] == t + 1).all()
+        # the oracle's commit with the GPU's gated counts (equal to its own outside near-ties)
+        k_pool, v_pool, ctx = ocommit(k_pool, v_pool, wl.page_table, ctx, wl.k_new, wl.v_new,
+                                      got["n_commit"], cfg.page_size)
+        assert (st.ctx_lens.cpu().numpy() == ctx).all(), t
+    assert near == 0 or near / (T * cfg.batch) < 1e-4
+    from introspective_strided_decoding_amd.layout import unpack_k_pages, unpack_v_pages
+    assert np.array_equal(unpack_k_pages(st.k_pages).float().cpu().numpy(), k_pool)
+    assert np.array_equal(unpack_v_pages(st.v_pages).float().cpu().numpy(), v_pool)
+    # attention over the grown contexts
+    st.attention()
+    torch.cuda.synchronize()
+    wl.k_pool, wl.v_pool, wl.ctx_lens = k_pool, v_pool, ctx
+    check_attention(wl, st.out)
+    from introspective_strided_decoding_amd import isd_read_flags
+    assert isd_read_flags(st.workspace) == 0
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 8])
+def test_loop_reproduces_tpf_column(n):
+    from oracle import tpf
+    table = {row["N"]: row["TPF"] for row in json.load(open(GOLDEN))["rows"]}
+    T, K = 60, 3
+    cfg = get_config("tiny_fp32", batch=256, stride_n=n, vocab=512, ctx=16, n_q_heads=1, n_kv_heads=1)
+    wl = make_workload(cfg, seed=700 + n, tau_mode="row", with_mask_logits=True)
+    pool = _pool(cfg, K, 800 + 10 * n, "row")
+    st = device_step(wl)
+    st.loop_start()
+    for t in range(T):
+        p, q = (wl.p_logits, wl.q_logits) if t == 0 else pool[(t - 1) % K][:2]
+        st.p_logits.copy_(_dev(p, st.p_logits))
+        st.q_logits.copy_(_dev(q, st.q_logits))
+        st.mask_logits.copy_(_dev(pool[t % K][2], st.mask_logits))
+        st.loop_forward(step=t, attention=False)
+    torch.cuda.synchronize()
+    tokens = st.extra["tokens"].cpu().numpy().astype(np.float64)
+    forwards = st.extra["forwards"].cpu().numpy().astype(np.float64)
+    assert (forwards == T).all()
+    tpf_hat = tokens.sum() / forwards.sum()
+    se = (tokens / forwards).std(ddof=1) / np.sqrt(cfg.batch)
+    closed = tpf.tpf_closed_form(n, 0.9)
+    # the loop ends mid-cycle for some requests: allow 1/T of bias
+    assert abs(tpf_hat - closed) < 4 * se + 1.0 / T, (n, tpf_hat, closed, se)
+    assert abs(tpf_hat - table[n]) < 4 * se + 1.0 / T + 0.005, (n, tpf_hat, table[n], se)

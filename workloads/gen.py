@@ -141,11 +141,13 @@ def _fit_tau(p: torch.Tensor, z: torch.Tensor, dtype: str, groups: torch.Tensor,
 
 def make_workload(cfg: WorkloadConfig, seed: Optional[int] = None, *, junk: str = "random",
                   tau_mode: Optional[str] = None, with_logits: bool = True,
-                  with_mask_logits: bool = False) -> Workload:
+                  with_mask_logits: bool = False, extra_tokens: int = 0) -> Workload:
     """Build one seeded ISD step input for ``cfg``.
 
     tau_mode: "batch" (one tau for the whole batch), "request" or "row".  Default: "request"
     when the config draws a target per request, else "batch".
+    extra_tokens: page room for that many more tokens per request (a decoding loop commits
+    into it); 0 keeps the recipe's allocation.
     """
     if seed is None:
         seed = cfg.seed_base
@@ -165,7 +167,7 @@ def make_workload(cfg: WorkloadConfig, seed: Optional[int] = None, *, junk: str 
         ctx = rng.integers(lo, hi + 1, size=B).astype(np.int32)
 
     # shuffled page allocation
-    pages_per = (ctx.astype(np.int64) + Q + ps - 1) // ps
+    pages_per = (ctx.astype(np.int64) + Q + int(extra_tokens) + ps - 1) // ps
     n_pages = int(pages_per.sum())
     perm = rng.permutation(n_pages).astype(np.int32)
     max_pages = int(pages_per.max())
