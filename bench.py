@@ -161,7 +161,7 @@ def main(argv=None):
     cfg = get_config(args.config)
     t_gen = time.perf_counter()
     loop_forwards = 0 if args.no_loop else max(20, min(200, args.steps))
-    wl = make_workload(cfg, with_mask_logits=True, extra_tokens=(loop_forwards + 8) * (cfg.stride_n - 1))
+    wl = make_workload(cfg, with_mask_logits=True)
     t_gen = time.perf_counter() - t_gen
     nbytes = algorithmic_bytes(wl)
     step_bytes = nbytes["attention"] + nbytes["accept"]
@@ -254,8 +254,11 @@ def main(argv=None):
     if loop_forwards and not use_lora:
         # every forward verifies proposals drawn from the q rows it is tested against, so the
         # per-position acceptance is the workload's target
-        lp = DeviceStep.from_arrays(wl, device=dev, max_ctx=int(wl.ctx_lens.max()) + (loop_forwards + 8) * cfg.stride_n,
+        # the same workload with page room for the tokens the loop commits
+        lwl = make_workload(cfg, with_mask_logits=True, extra_tokens=(loop_forwards + 8) * (cfg.stride_n - 1))
+        lp = DeviceStep.from_arrays(lwl, device=dev, max_ctx=int(lwl.ctx_lens.max()) + (loop_forwards + 8) * cfg.stride_n,
                                     commit_in_place=True)
+        del lwl
         row0 = lp.mask_logits[:, :1].clone()
         lp.mask_logits.copy_(torch.cat([row0, lp.q_logits], dim=1))
         lp.loop_start()

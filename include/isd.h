@@ -16,6 +16,9 @@
  *                  resample from normalize(max(0, p - q)) at the first
  *                  rejection;
  *   kv_commit      append the CLEAN rows of accepted tokens to the KV pages;
+ *   isd_propose    draw the next N proposals at the MASK rows (sampling or
+ *                  argmax);
+ *   isd_loop_advance  per-request bookkeeping of the multi-step decoding loop;
  *   isd_lora_delta the gated low-rank delta of Residual ISD (R-ISD), added at
  *                  MASK rows only.
  *
@@ -25,7 +28,11 @@
  *   row-major in the index order written next to them.  The library never
  *   allocates, frees or synchronises on these calls; the work is enqueued on
  *   `stream` and the call returns at once.  Calls on one stream run in order;
- *   the intended order per step is attention -> accept -> commit.
+ *   the intended order per step is attention -> accept -> commit (a decoding
+ *   loop: attention -> accept -> propose -> loop_advance -> commit).  Calls
+ *   enqueue kernels only (no memset, no allocation), so they may be recorded
+ *   into a HIP graph.  The only state kept between calls is each device's
+ *   compute-unit count, queried once.
  * - Arguments are validated on the host before anything is enqueued.  A bad
  *   argument returns an isd_status != ISD_OK and enqueues nothing.  Values
  *   that live in device memory (context lengths, page-table entries, token

@@ -216,7 +216,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out, int Qn, int Hq, int Hkv, int G,
-    int rows, int max_pages, int num_pages, int tps, int n_splits, int nb, int units, float scale_log2,
+    int rows, int max_pages, int num_pages, int tps, int n_splits, int nb, int units, int longest_first,
+    float scale_log2,
     float2* __restrict__ ws_ml, float* __restrict__ ws_o, uint32_t* __restrict__ arrivals,
     uint32_t* __restrict__ flags) {
   constexpr int KS = D / 16;
@@ -243,13 +244,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   if (u >= units) return;
   const int split = u % n_splits;
   const int hk = (u / n_splits) % Hkv;
-  // Requests are served longest first (ties in index order): long contexts
-  // start early and short ones fill in at the end.  For up to kRankMax
-  // requests every workgroup ranks the lengths itself; beyond that, index order.
+  // When the grid takes more than one round of the chip, requests are served
+  // longest first (ties in index order): long contexts start early and short
+  // ones fill in at the end.  For up to kRankMax requests every workgroup
+  // ranks the lengths itself; otherwise, and in a single round, index order.
   const int rank = u / (n_splits * Hkv);
   const int B = units / (n_splits * Hkv);
   int r = rank;
-  if (B <= kRankMax) {
+  if (longest_first && B <= kRankMax) {
     __shared__ int sm_len[kRankMax];
     __shared__ int sm_req;
     for (int t = threadIdx.x; t < B; t += blockDim.x) sm_len[t] = ctx_lens[t];
@@ -727,6 +729,7 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
   float* po = reinterpret_cast<float*>(ws + Lw.attn_o);
   const int nwg = s.batch * s.n_kv_heads * p.n_splits;
   const int grid8 = (nwg + 7) / 8 * 8;          // work units rounded up to a multiple of 8
+  const int longest_first = (grid8 * p.row_blocks > device_cus()) ? 1 : 0;
   if (s.kv_dtype == ISD_BF16) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kn = static_cast<const uint16_t*>(k_new);
@@ -738,13 +741,13 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
     if (p.row_blocks == 1)
       hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, true>), dim3(grid8), dim3(64 * kAttnWaves), 0, stream,
                          qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group,
-                         p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, 1, nwg, scale_log2, ml,
-                         po, arrivals, flags);
+                         p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, 1, nwg, longest_first,
+                         scale_log2, ml, po, arrivals, flags);
     else
       hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, false>), dim3(grid8 * p.row_blocks), dim3(64 * kAttnWaves), 0,
                          stream, qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads,
                          p.group, p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, p.row_blocks,
-                         nwg, scale_log2, ml, po, arrivals, flags);
+                         nwg, longest_first, scale_log2, ml, po, arrivals, flags);
   } else {
     const float* qq = static_cast<const float*>(q);
     hipLaunchKernelGGL((attn_split_f32<D>), dim3(nwg, p.rows), dim3(64), 0, stream, qq,

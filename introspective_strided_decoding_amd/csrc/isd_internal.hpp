@@ -77,6 +77,9 @@ struct PropPart {
 };
 int prop_shards(int vocab);   // 4096-entry shards of a MASK row
 
+// Compute units of the current device (queried once per device and cached).
+int device_cus();
+
 AttnPlan plan_attention(const isd_shape& s);
 AcceptPlan plan_accept(const isd_shape& s);
 WsLayout ws_layout(const isd_shape& s);
