@@ -126,9 +126,8 @@ size_t isd_workspace_bytes(const isd_shape* shape);
 
 /*
  * Prepare a workspace for `shape` on `stream`: zero the header (flag word and
- * internal counters) and fill the 512 KB table of float64 exp() of every
- * bf16 bit pattern that the residual sampler reads.  Call once per workspace
- * before its first use; the calls below keep the header consistent after.
+ * internal counters).  Call once per workspace before its first use; the
+ * calls below keep the header consistent after.
  */
 isd_status isd_workspace_init(const isd_shape* shape, void* workspace, size_t ws_bytes,
                               hipStream_t stream);

@@ -10,8 +10,9 @@
 //                  the first wave already holds the logits at the proposals;
 //                  rho = exp(log p - log q), Philox uniforms, accept iff
 //                  u < rho, first rejection by a wave ballot.
-//   resid_lse64    rejecting requests only: fp64 (max, sum exp) of the
-//                  rejected p and q rows, sharded finely over the vocabulary.
+//   resid_lse64    rejecting requests only: fp64 sums of exp(l - row max)
+//                  over the rejected p and q rows, sharded finely over the
+//                  vocabulary (the row maxima come exact from the decision).
 //   resid_mass64   per shard: fp64 sum of r(y) = max(0, p(y) - q(y)) (and of
 //                  p(y) for the zero-mass fallback).
 //   resid_select   per rejecting request: prefix over shard masses picks the
@@ -25,6 +26,7 @@
 #include <climits>
 
 #include "device_common.hpp"
+#include "exp64.hpp"
 #include "isd_internal.hpp"
 
 namespace isd {
@@ -69,7 +71,6 @@ struct DecideArgs {
   ReqState* jobs;          // compact list of rejecting requests
   uint32_t* rej_count;     // its length
   uint32_t* flags;
-  int bf16_logits;
 };
 
 // A shard holds at most kThreads * kLseVec vectors, so every thread issues all
@@ -194,13 +195,10 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   __syncthreads();
   if (wave != 0) return;
   bool reject = false;
-  bool table_ok = false;
   double u_res = 0.0;
   if (lane < R) {
     const int j = lane;
     const size_t row = size_t(r) * R + j;
-    // exp(x) of every logit of both rows is finite and their sums cannot overflow
-    table_ok = a.bf16_logits && fabsf(max_sm[j]) < 600.f && fabsf(max_sm[R + j]) < 600.f;
     float lp, lq;
     if (!in_range) {
       raise_flag(a.flags, ISD_FLAG_TOKEN_RANGE);
@@ -224,7 +222,6 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
   const int A = (first < 0) ? N : first + 1;
   const double u_first = __shfl(u_res, first < 0 ? 0 : first);
-  const int tab_first = __shfl(int(table_ok), first < 0 ? 0 : first);
   if (lane < N) {
     const int xl = a.proposals[size_t(r) * N + lane];
     a.out_tokens[size_t(r) * N + lane] = (lane < A) ? xl : -1;
@@ -238,9 +235,10 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
       st.req = r;
       st.accept_len = A;
       st.reject_row = first;
-      st.table_ok = tab_first;
+      st.pad = 0;
+      st.max_p = max_sm[first];
+      st.max_q = max_sm[R + first];
       st.u_resample = u_first;
-      st.pad = 0.0;
       a.jobs[atomicAdd(a.rej_count, 1u)] = st;
     }
   }
@@ -252,21 +250,22 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
 // its normaliser partials).  A residual shard is 2048 vocabulary entries:
 // 256 threads x 8 consecutive entries.
 //
-// exp in float64: for bf16 logits whose row maxima lie in (-600, 600), exp(x)
-// is read from a table holding exp() of every bf16 bit pattern, so
-// p(y) = T[x_y] / sum_y T[x_y] (no float64 exp per entry, and no overflow or
-// total underflow of the sums).  Otherwise exp(x - m) is evaluated directly.
-// Shard partials are (m, s) pairs with lse = m + log(s) (m = 0 on the table
-// path) and are combined by whole waves.
+// Every residual value is exp(l - m) in float64 with m the row's exact max
+// (carried in the list entry), by the table-driven exp_nonpos (its 64-entry
+// table in LDS), so each kernel recomputes exactly the same values:
+// p(y) = exp(l_p(y) - m_p) / S_p with S_p = sum_y exp(l_p(y) - m_p), and the
+// same for q.  No value overflows and the sums need no rescaling.
 constexpr int kRPer = 8;
 constexpr int kRShard = kThreads * kRPer;
 
-__device__ __forceinline__ void ms_merge_d(double& m, double& s, double m2, double s2) {
-  if (m2 == -INFINITY) return;
-  if (m == -INFINITY) { m = m2; s = s2; return; }
-  if (m2 > m) { s = s * exp(m - m2) + s2; m = m2; }
-  else if (m2 == m) s += s2;
-  else s += s2 * exp(m2 - m);
+// 2^(j/64), j = 0..63, for exp_nonpos; call with all threads of the workgroup.
+__device__ __forceinline__ void fill_exp_table(double* tab64) {
+  if (threadIdx.x < 64) tab64[threadIdx.x] = exp2(double(threadIdx.x) * (1.0 / 64.0));
+  __syncthreads();
+}
+
+__device__ __forceinline__ double exp_shift(float x, float m, const double* tab64) {
+  return (x == -INFINITY) ? 0.0 : exp_nonpos(double(x) - double(m), tab64);
 }
 
 __device__ __forceinline__ double block_sum_d(double x, double* sm) {
@@ -280,39 +279,19 @@ __device__ __forceinline__ double block_sum_d(double x, double* sm) {
   return t;
 }
 
-// (max, sum) over the workgroup; every thread receives the result.
-__device__ __forceinline__ void block_ms_d(double& m, double& s, double* sm) {
-  const double wm = wave_max_d(m);
-  double ws = (m == -INFINITY) ? 0.0 : (m == wm ? s : s * exp(m - wm));
-  ws = wave_sum_d(ws);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) { sm[2 * wave] = wm; sm[2 * wave + 1] = ws; }
-  __syncthreads();
-  double M = -INFINITY, S = 0.0;
-  for (int w = 0; w < kThreads / 64; ++w) ms_merge_d(M, S, sm[2 * w], sm[2 * w + 1]);
-  m = M;
-  s = S;
-}
-
-// Row log-normalisers of the k-th listed request's rejected p and q rows from
-// the shard partials; called by every lane of a wave, all lanes receive the
-// result.
-__device__ __forceinline__ void wave_lse64(const double2* __restrict__ lse64, int k, int r_shards,
-                                           double& lse_p, double& lse_q) {
+// Row sums S_p, S_q of the k-th listed request from the shard partials;
+// called by every lane of a wave, all lanes receive the result.
+__device__ __forceinline__ void wave_row_sums(const double2* __restrict__ sums, int k, int r_shards,
+                                              double& sp, double& sq) {
   const int lane = threadIdx.x & 63;
-  double mp = -INFINITY, sp = 0.0, mq = -INFINITY, sq = 0.0;
+  double a = 0.0, b = 0.0;
   for (int i = lane; i < r_shards; i += 64) {
-    const double2 a = lse64[(size_t(k) * r_shards + i) * 2 + 0];
-    const double2 b = lse64[(size_t(k) * r_shards + i) * 2 + 1];
-    ms_merge_d(mp, sp, a.x, a.y);
-    ms_merge_d(mq, sq, b.x, b.y);
+    const double2 v = sums[size_t(k) * r_shards + i];
+    a += v.x;
+    b += v.y;
   }
-  const double Mp = wave_max_d(mp), Mq = wave_max_d(mq);
-  const double Sp = wave_sum_d(mp == -INFINITY ? 0.0 : (mp == Mp ? sp : sp * exp(mp - Mp)));
-  const double Sq = wave_sum_d(mq == -INFINITY ? 0.0 : (mq == Mq ? sq : sq * exp(mq - Mq)));
-  lse_p = Mp + log(Sp);
-  lse_q = Mq + log(Sq);
+  sp = wave_sum_d(a);
+  sq = wave_sum_d(b);
 }
 
 // 8 consecutive logits starting at e0 (entries >= e1 read as -inf)
@@ -325,18 +304,14 @@ __device__ __forceinline__ void load_run(const T* __restrict__ row, int e0, int 
   }
 }
 
-// exp(x) from the table (bf16 logits): the bf16 bit pattern is the top half of x
-__device__ __forceinline__ double exp_tab(const double* __restrict__ tab, float x) {
-  return (x == -INFINITY) ? 0.0 : tab[__float_as_uint(x) >> 16];
-}
-
 template <typename T>
 __global__ __launch_bounds__(kThreads) void resid_lse64(const T* __restrict__ p_logits,
                                                          const T* __restrict__ q_logits, int N, int V,
                                                          int r_shards, const ReqState* __restrict__ jobs,
                                                          const uint32_t* __restrict__ rej_count,
-                                                         const double* __restrict__ tab,
-                                                         double2* __restrict__ lse64) {
+                                                         double2* __restrict__ sums) {
+  __shared__ double tab64[64];
+  __shared__ double sm[kThreads / 64];
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
   const ReqState st = jobs[k];
@@ -347,53 +322,26 @@ __global__ __launch_bounds__(kThreads) void resid_lse64(const T* __restrict__ p_
   float xp[kRPer], xq[kRPer];
   load_run<T>(p_logits + row * V, e0, e1, xp);
   load_run<T>(q_logits + row * V, e0, e1, xq);
-  double mp, sp = 0.0, mq, sq = 0.0;
-  if (st.table_ok) {
-    mp = mq = 0.0;
+  fill_exp_table(tab64);
+  double sp = 0.0, sq = 0.0;
 #pragma unroll
-    for (int i = 0; i < kRPer; ++i) { sp += exp_tab(tab, xp[i]); sq += exp_tab(tab, xq[i]); }
-    __shared__ double sm1[kThreads / 64];
-    sp = block_sum_d(sp, sm1);
-    sq = block_sum_d(sq, sm1);
-  } else {
-    float fp = xp[0], fq = xq[0];
-#pragma unroll
-    for (int i = 1; i < kRPer; ++i) { fp = fmaxf(fp, xp[i]); fq = fmaxf(fq, xq[i]); }
-    mp = fp;
-    mq = fq;
-    if (fp != -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < kRPer; ++i) { sp += exp(double(xp[i]) - mp); sq += exp(double(xq[i]) - mq); }
-    }
-    __shared__ double sm2[2 * kThreads / 64];
-    block_ms_d(mp, sp, sm2);
-    block_ms_d(mq, sq, sm2);
+  for (int i = 0; i < kRPer; ++i) {
+    sp += exp_shift(xp[i], st.max_p, tab64);
+    sq += exp_shift(xq[i], st.max_q, tab64);
   }
-  if (threadIdx.x == 0) {
-    lse64[(size_t(k) * r_shards + sh) * 2 + 0] = make_double2(mp, sp);
-    lse64[(size_t(k) * r_shards + sh) * 2 + 1] = make_double2(mq, sq);
-  }
+  sp = block_sum_d(sp, sm);
+  sq = block_sum_d(sq, sm);
+  if (threadIdx.x == 0) sums[size_t(k) * r_shards + sh] = make_double2(sp, sq);
 }
 
 // r(y) = max(0, p(y) - q(y)) and p(y) for 8 consecutive entries
-__device__ __forceinline__ void resid_values(const float* xp, const float* xq, bool table_ok,
-                                             const double* __restrict__ tab, double lse_p,
-                                             double lse_q, double* rv, double* pv) {
-  if (table_ok) {
-    const double ip = exp(-lse_p), iq = exp(-lse_q);
+__device__ __forceinline__ void resid_values(const float* xp, const float* xq, const ReqState& st, double ip,
+                                             double iq, const double* tab64, double* rv, double* pv) {
 #pragma unroll
-    for (int i = 0; i < kRPer; ++i) {
-      const double p = exp_tab(tab, xp[i]) * ip;
-      rv[i] = fmax(0.0, p - exp_tab(tab, xq[i]) * iq);
-      pv[i] = p;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kRPer; ++i) {
-      const double p = exp(double(xp[i]) - lse_p);
-      rv[i] = fmax(0.0, p - exp(double(xq[i]) - lse_q));
-      pv[i] = p;
-    }
+  for (int i = 0; i < kRPer; ++i) {
+    const double p = exp_shift(xp[i], st.max_p, tab64) * ip;
+    rv[i] = fmax(0.0, p - exp_shift(xq[i], st.max_q, tab64) * iq);
+    pv[i] = p;
   }
 }
 
@@ -415,9 +363,10 @@ __global__ __launch_bounds__(kThreads) void resid_mass64(const T* __restrict__ p
                                                           const T* __restrict__ q_logits, int N, int V,
                                                           int r_shards, const ReqState* __restrict__ jobs,
                                                           const uint32_t* __restrict__ rej_count,
-                                                          const double* __restrict__ tab,
-                                                          const double2* __restrict__ lse64,
+                                                          const double2* __restrict__ sums,
                                                           double2* __restrict__ mass) {
+  __shared__ double tab64[64];
+  __shared__ double sm[kThreads / 64];
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
   const ReqState st = jobs[k];
@@ -428,14 +377,14 @@ __global__ __launch_bounds__(kThreads) void resid_mass64(const T* __restrict__ p
   float xp[kRPer], xq[kRPer];
   load_run<T>(p_logits + row * V, e0, e1, xp);
   load_run<T>(q_logits + row * V, e0, e1, xq);
-  double lse_p, lse_q;
-  wave_lse64(lse64, k, r_shards, lse_p, lse_q);
+  double sp, sq;
+  wave_row_sums(sums, k, r_shards, sp, sq);
+  fill_exp_table(tab64);
   double rv[kRPer], pv[kRPer];
-  resid_values(xp, xq, st.table_ok, tab, lse_p, lse_q, rv, pv);
+  resid_values(xp, xq, st, 1.0 / sp, 1.0 / sq, tab64, rv, pv);
   double rs = 0.0, ps = 0.0;
 #pragma unroll
   for (int i = 0; i < kRPer; ++i) { rs += rv[i]; ps += pv[i]; }
-  __shared__ double sm[kThreads / 64];
   rs = block_sum_d(rs, sm);
   ps = block_sum_d(ps, sm);
   if (threadIdx.x == 0) mass[size_t(k) * r_shards + sh] = make_double2(rs, ps);
@@ -449,27 +398,31 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
                                                           const T* __restrict__ q_logits, int N, int V,
                                                           int r_shards, const ReqState* __restrict__ jobs,
                                                           const uint32_t* __restrict__ rej_count,
-                                                          const double* __restrict__ tab,
-                                                          const double2* __restrict__ lse64,
+                                                          const double2* __restrict__ sums,
                                                           const double2* __restrict__ mass,
                                                           int32_t* __restrict__ out_tokens) {
+  __shared__ double tab64[64];
   const int k = blockIdx.x;
   const ReqState st = jobs[k];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ double before_sm, target_sm;
   __shared__ int shard_sm, fb_sm, found_sm, last_sm;
   __shared__ double wsum[kThreads / 64];
-  double lse_p, lse_q;
-  wave_lse64(lse64, k, r_shards, lse_p, lse_q);
+  // lane l of wave 0 owns shards [l*per, (l+1)*per) in vocabulary order; the
+  // partials and masses are requested before the count is known
+  const int per = (r_shards + 63) / 64;
+  const int s0 = min(r_shards, lane * per), s1 = min(r_shards, s0 + per);
+  double sp, sq;
+  wave_row_sums(sums, k, r_shards, sp, sq);
+  double2 first_mass = make_double2(0.0, 0.0);
+  if (wave == 0 && s0 < s1) first_mass = mass[size_t(k) * r_shards + s0];
   if (k >= int(*rej_count)) return;
   const int r = st.req;
+  fill_exp_table(tab64);
   if (wave == 0) {
-    // shard masses in vocabulary order: lane l owns shards [l*per, (l+1)*per)
-    const int per = (r_shards + 63) / 64;
-    const int s0 = min(r_shards, lane * per), s1 = min(r_shards, s0 + per);
     double rsum = 0.0, psum = 0.0;
     for (int i = s0; i < s1; ++i) {
-      const double2 m = mass[size_t(k) * r_shards + i];
+      const double2 m = (i == s0) ? first_mass : mass[size_t(k) * r_shards + i];
       rsum += m.x;
       psum += m.y;
     }
@@ -483,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
     int pick = -1, last_nz = -1;
     double pick_before = 0.0, last_before = 0.0;
     for (int i = s0; i < s1; ++i) {
-      const double2 m = mass[size_t(k) * r_shards + i];
+      const double2 m = (i == s0) ? first_mass : mass[size_t(k) * r_shards + i];
       const double mi = fb ? m.y : m.x;
       if (mi > 0.0) { last_nz = i; last_before = cum; }
       if (pick < 0 && cum + mi > target) { pick = i; pick_before = cum; }
@@ -516,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   load_run<T>(p_logits + row * V, e0, e1, xp);
   load_run<T>(q_logits + row * V, e0, e1, xq);
   double rv[kRPer], pv[kRPer], c[kRPer];
-  resid_values(xp, xq, st.table_ok, tab, lse_p, lse_q, rv, pv);
+  resid_values(xp, xq, st, 1.0 / sp, 1.0 / sq, tab64, rv, pv);
   double run = 0.0;
   int last_here = -1;
 #pragma unroll
@@ -559,9 +512,8 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   float2* part = reinterpret_cast<float2*>(ws + L.lse);
   ReqState* jobs = reinterpret_cast<ReqState*>(ws + L.jobs);
   uint32_t* rej_count = reinterpret_cast<uint32_t*>(ws + kRejCountOffset);
-  double2* l64 = reinterpret_cast<double2*>(ws + L.lse64);
+  double2* sums = reinterpret_cast<double2*>(ws + L.resid_sums);
   double2* mass = reinterpret_cast<double2*>(ws + L.mass);
-  const double* tab = reinterpret_cast<const double*>(ws + L.exp_table);
   DecideArgs<T> a;
   a.p_logits = P;
   a.q_logits = Qp;
@@ -583,16 +535,15 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.jobs = jobs;
   a.rej_count = rej_count;
   a.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
-  a.bf16_logits = (s.logit_dtype == ISD_BF16) ? 1 : 0;
   hipLaunchKernelGGL((lse_partial<T>), dim3(2 * (N - 1) * p.shards, B), dim3(kThreads), 0, stream, a,
                      p.shard_len, part);
   hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
   hipLaunchKernelGGL((resid_lse64<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shards, jobs, rej_count, tab, l64);
+                     p.r_shards, jobs, rej_count, sums);
   hipLaunchKernelGGL((resid_mass64<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shards, jobs, rej_count, tab, l64, mass);
+                     p.r_shards, jobs, rej_count, sums, mass);
   hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,
-                     rej_count, tab, l64, mass, out_tokens);
+                     rej_count, sums, mass, out_tokens);
   return hipGetLastError();
 }
 

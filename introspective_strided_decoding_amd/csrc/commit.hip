@@ -1,5 +1,5 @@
 // Appending accepted CLEAN rows to the KV pages (kv_commit) and the
-// workspace header fill.
+// workspace header fill (isd_workspace_init).
 //
 // One workgroup per (request, CLEAN row i).  It requests the row's key and
 // value vectors before the request's length and page id arrive, stores them
@@ -111,12 +111,6 @@ __global__ void fill_zero_u32(uint32_t* p, int n) {
   if (i < n) p[i] = 0u;
 }
 
-// exp of every bf16 bit pattern, float64 (used by the residual sampler)
-__global__ void build_exp_table(double* t) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < kExpTableSize) t[b] = exp(double(bf16_bits_to_f32(uint16_t(b))));
-}
-
 }  // namespace
 
 hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
@@ -139,11 +133,10 @@ hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_ne
   return hipGetLastError();
 }
 
-hipError_t launch_workspace_init(void* ws, size_t header_bytes, double* exp_table, hipStream_t stream) {
+hipError_t launch_workspace_init(void* ws, size_t header_bytes, hipStream_t stream) {
   const int n = int(header_bytes / 4);
   hipLaunchKernelGGL(fill_zero_u32, dim3((n + 255) / 256), dim3(256), 0, stream,
                      static_cast<uint32_t*>(ws), n);
-  hipLaunchKernelGGL(build_exp_table, dim3(kExpTableSize / 256), dim3(256), 0, stream, exp_table);
   return hipGetLastError();
 }
 

@@ -141,14 +141,12 @@ WsLayout ws_layout(const isd_shape& s) {
   off = align_up(off + (size_t)c.rows * c.shards * 8, 256);
   L.jobs = off;
   off = align_up(off + (size_t)s.batch * sizeof(ReqState), 256);
-  L.lse64 = off;
-  off = align_up(off + (size_t)s.batch * c.r_shards * 32, 256);
+  L.resid_sums = off;
+  off = align_up(off + (size_t)s.batch * c.r_shards * 16, 256);
   L.mass = off;
   off = align_up(off + (size_t)s.batch * c.r_shards * 16, 256);
   L.prop = off;
   off = align_up(off + (size_t)s.batch * s.stride_n * prop_shards(s.vocab) * sizeof(PropPart), 256);
-  L.exp_table = off;
-  off = align_up(off + (size_t)kExpTableSize * 8, 256);
   L.total = off;
   return L;
 }
@@ -189,9 +187,7 @@ isd_status isd_workspace_init(const isd_shape* shape, void* workspace, size_t ws
   st = check_ws(shape, workspace, ws_bytes);
   if (st != ISD_OK) return st;
   const WsLayout L = ws_layout(*shape);
-  hipError_t e = launch_workspace_init(workspace, L.zero_end,
-                                       reinterpret_cast<double*>(static_cast<char*>(workspace) + L.exp_table),
-                                       stream);
+  hipError_t e = launch_workspace_init(workspace, L.zero_end, stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_workspace_init");
 }
 

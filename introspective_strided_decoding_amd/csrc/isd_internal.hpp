@@ -46,14 +46,12 @@ struct WsLayout {
   size_t attn_o = 0;         // float [D] per partial row
   size_t lse = 0;            // float2 (max, sum) per (row, shard)
   size_t jobs = 0;           // ReqState per rejecting request, compacted
-  size_t lse64 = 0;          // double2 per (listed request, residual shard) for p and q
+  size_t resid_sums = 0;     // double2 (S_p, S_q) per (listed request, residual shard)
   size_t mass = 0;           // double2 (residual mass, p mass) per (listed request, residual shard)
   size_t prop = 0;           // PropPart per (MASK row, proposal shard)
-  size_t exp_table = 0;      // double[65536]: exp of every bf16 bit pattern
   size_t total = 0;
 };
 
-constexpr int kExpTableSize = 65536;
 
 // Header word (uint32 at this byte offset of the workspace).
 constexpr size_t kRejCountOffset = 4;     // entries in the list of rejecting requests
@@ -64,9 +62,10 @@ struct ReqState {
   int32_t req;          // request index r
   int32_t accept_len;   // A
   int32_t reject_row;   // j of the rejected row
-  int32_t table_ok;     // bf16 rows whose max logit lies in (-600, 600): exp from the table
+  int32_t pad;
+  float max_p;          // exact max logit of the rejected p row
+  float max_q;          // and of its q row
   double u_resample;    // u' of the rejected position
-  double pad;
 };
 
 // Per (MASK row, vocabulary shard) summary written by the proposal kernels.
@@ -112,7 +111,7 @@ hipError_t launch_loop_advance(int B, int N, const int32_t* accept_len, const in
                                int32_t* proposals, int32_t* positions, int64_t* tokens, int64_t* forwards,
                                hipStream_t stream);
 
-hipError_t launch_workspace_init(void* ws, size_t header_bytes, double* exp_table, hipStream_t stream);
+hipError_t launch_workspace_init(void* ws, size_t header_bytes, hipStream_t stream);
 
 struct LoraLayout {
   size_t part = 0;    // float [d_in/256][n_mask padded to 32][rank]
