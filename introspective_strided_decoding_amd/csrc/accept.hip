@@ -10,14 +10,16 @@
 //                  the first wave already holds the logits at the proposals;
 //                  rho = exp(log p - log q), Philox uniforms, accept iff
 //                  u < rho, first rejection by a wave ballot.
-//   resid_lse64    rejecting requests only: fp64 sums of exp(l - row max)
-//                  over the rejected p and q rows, sharded finely over the
-//                  vocabulary (the row maxima come exact from the decision).
-//   resid_mass64   per shard: fp64 sum of r(y) = max(0, p(y) - q(y)) (and of
-//                  p(y) for the zero-mass fallback).
-//   resid_select   per rejecting request: prefix over shard masses picks the
-//                  shard holding u' * S, a workgroup scan inside that shard in
-//                  vocabulary order picks y*.
+//   resid_pass     rejecting requests only, one pass over the rejected p
+//                  and q rows, sharded finely over the vocabulary: fp64 sums
+//                  of e_p = exp(l_p - max p) and e_q = exp(l_q - max q) (the
+//                  row maxima come exact from the decision), and the
+//                  residual's pieces under the decision's fp32 estimate of
+//                  the normaliser ratio (see below).
+//   resid_select   per rejecting request: exact shard masses from those
+//                  pieces, a prefix over them picks the shard holding
+//                  u' * S, a workgroup scan inside that shard in vocabulary
+//                  order picks y*.
 // The residual runs in fp64 so the inverse CDF agrees with a float64
 // reference up to rounding of the running sums.  The decision lists the
 // rejecting requests compactly (an atomic counter the normaliser kernel
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
       st.req = r;
       st.accept_len = A;
       st.reject_row = first;
-      st.pad = 0;
+      st.log_kappa = (lse_sm[first] - max_sm[first]) - (lse_sm[R + first] - max_sm[R + first]);
       st.max_p = max_sm[first];
       st.max_q = max_sm[R + first];
       st.u_resample = u_first;
@@ -247,16 +249,27 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
 // ---- fp64 residual ----
 // Residual workgroup (shard, k) serves the k-th listed rejecting request; it
 // requests its list entry together with the count (the selection kernel also
-// its normaliser partials).  A residual shard is 2048 vocabulary entries:
-// 256 threads x 8 consecutive entries.
+// its shard records).  A residual shard is 2048 vocabulary entries: 256
+// threads x 8 consecutive entries.
 //
-// Every residual value is exp(l - m) in float64 with m the row's exact max
-// (carried in the list entry), by the table-driven exp_nonpos (its 64-entry
-// table in LDS), so each kernel recomputes exactly the same values:
-// p(y) = exp(l_p(y) - m_p) / S_p with S_p = sum_y exp(l_p(y) - m_p), and the
-// same for q.  No value overflows and the sums need no rescaling.
+// Every value is e = exp(l - m) in float64 with m the row's exact max (carried
+// in the list entry), by the table-driven exp_nonpos (its 64-entry table in
+// LDS), so both kernels recompute exactly the same values.  With
+// S_p = sum e_p, S_q = sum e_q and kappa = S_p / S_q, the residual is
+// r(y) = max(0, e_p - kappa e_q) / S_p.  kappa is only known once every shard
+// is summed, so the pass sorts each entry by the decision's fp32 estimate
+// kappa~ (relative error far below the band kResidBand): entries clearly
+// inside the support add e_p and e_q to (a, b); entries within the band are
+// grouped by their exact logit difference l_p - l_q (equal differences mean
+// equal ratios e_p / e_q, so a group lies wholly on one side of any kappa),
+// and each group keeps its (sum e_p, sum e_q), for up to kResidAmb groups per
+// shard.  The selection kernel then has the exact shard mass
+// (a - kappa b + sum over groups of max(0, sum e_p - kappa sum e_q)) / S_p.
+// If a shard had more groups, or kappa~ is off by more than half the band,
+// the selection kernel recomputes the shard from the logits.
 constexpr int kRPer = 8;
 constexpr int kRShard = kThreads * kRPer;
+constexpr double kResidBand = 1e-4;
 
 // 2^(j/64), j = 0..63, for exp_nonpos; call with all threads of the workgroup.
 __device__ __forceinline__ void fill_exp_table(double* tab64) {
@@ -279,21 +292,6 @@ __device__ __forceinline__ double block_sum_d(double x, double* sm) {
   return t;
 }
 
-// Row sums S_p, S_q of the k-th listed request from the shard partials;
-// called by every lane of a wave, all lanes receive the result.
-__device__ __forceinline__ void wave_row_sums(const double2* __restrict__ sums, int k, int r_shards,
-                                              double& sp, double& sq) {
-  const int lane = threadIdx.x & 63;
-  double a = 0.0, b = 0.0;
-  for (int i = lane; i < r_shards; i += 64) {
-    const double2 v = sums[size_t(k) * r_shards + i];
-    a += v.x;
-    b += v.y;
-  }
-  sp = wave_sum_d(a);
-  sq = wave_sum_d(b);
-}
-
 // 8 consecutive logits starting at e0 (entries >= e1 read as -inf)
 template <typename T>
 __device__ __forceinline__ void load_run(const T* __restrict__ row, int e0, int e1, float* x) {
@@ -305,13 +303,16 @@ __device__ __forceinline__ void load_run(const T* __restrict__ row, int e0, int 
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void resid_lse64(const T* __restrict__ p_logits,
-                                                         const T* __restrict__ q_logits, int N, int V,
-                                                         int r_shards, const ReqState* __restrict__ jobs,
-                                                         const uint32_t* __restrict__ rej_count,
-                                                         double2* __restrict__ sums) {
+__global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_logits,
+                                                        const T* __restrict__ q_logits, int N, int V,
+                                                        int r_shards, const ReqState* __restrict__ jobs,
+                                                        const uint32_t* __restrict__ rej_count,
+                                                        ResidShard* __restrict__ shard_out) {
+  constexpr unsigned long long kEmpty = ~0ull;   // a NaN pattern, never an exact difference
   __shared__ double tab64[64];
   __shared__ double sm[kThreads / 64];
+  __shared__ unsigned long long cls_sm[kResidAmb];
+  __shared__ int overflow_sm;
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
   const ReqState st = jobs[k];
@@ -322,16 +323,87 @@ __global__ __launch_bounds__(kThreads) void resid_lse64(const T* __restrict__ p_
   float xp[kRPer], xq[kRPer];
   load_run<T>(p_logits + row * V, e0, e1, xp);
   load_run<T>(q_logits + row * V, e0, e1, xq);
+  if (threadIdx.x < kResidAmb) cls_sm[threadIdx.x] = kEmpty;
+  if (threadIdx.x == 0) overflow_sm = 0;
   fill_exp_table(tab64);
-  double sp = 0.0, sq = 0.0;
+  const double kap = exp(double(st.log_kappa));
+  double sp = 0.0, sq = 0.0, a = 0.0, b = 0.0;
+  double ep[kRPer], eq[kRPer];
+  unsigned amb = 0;
 #pragma unroll
   for (int i = 0; i < kRPer; ++i) {
-    sp += exp_shift(xp[i], st.max_p, tab64);
-    sq += exp_shift(xq[i], st.max_q, tab64);
+    ep[i] = exp_shift(xp[i], st.max_p, tab64);
+    eq[i] = exp_shift(xq[i], st.max_q, tab64);
+    sp += ep[i];
+    sq += eq[i];
+    const double d = ep[i] - kap * eq[i], band = kResidBand * kap * eq[i];
+    if (d > band) {
+      a += ep[i];
+      b += eq[i];
+    } else if (d >= -band && ep[i] > 0.0) {
+      amb |= 1u << i;
+    }
   }
   sp = block_sum_d(sp, sm);
   sq = block_sum_d(sq, sm);
-  if (threadIdx.x == 0) sums[size_t(k) * r_shards + sh] = make_double2(sp, sq);
+  a = block_sum_d(a, sm);
+  b = block_sum_d(b, sm);
+  // entries near the boundary: group them by their exact logit difference
+  int n_cls = 0;
+  double cls_p[kResidAmb], cls_q[kResidAmb];
+  if (__syncthreads_or(amb != 0)) {
+#pragma unroll
+    for (int i = 0; i < kRPer; ++i) {
+      if (amb & (1u << i)) {
+        const unsigned long long key = __double_as_longlong(double(xp[i]) - double(xq[i]));
+        bool placed = false;
+        for (int c = 0; c < kResidAmb && !placed; ++c) {
+          const unsigned long long old = atomicCAS(&cls_sm[c], kEmpty, key);
+          placed = (old == kEmpty || old == key);
+        }
+        if (!placed) overflow_sm = 1;
+      }
+    }
+    __syncthreads();
+    // the groups in increasing order of their difference, so the record is deterministic
+    if (threadIdx.x == 0) {
+      for (int c = 1; c < kResidAmb && cls_sm[c] != kEmpty; ++c)
+        for (int j = c; j > 0 && __longlong_as_double(cls_sm[j]) < __longlong_as_double(cls_sm[j - 1]); --j) {
+          const unsigned long long t = cls_sm[j];
+          cls_sm[j] = cls_sm[j - 1];
+          cls_sm[j - 1] = t;
+        }
+    }
+    __syncthreads();
+    for (int c = 0; c < kResidAmb; ++c) {
+      const unsigned long long key = cls_sm[c];
+      if (key == kEmpty) break;
+      double gp = 0.0, gq = 0.0;
+#pragma unroll
+      for (int i = 0; i < kRPer; ++i)
+        if ((amb & (1u << i)) && __double_as_longlong(double(xp[i]) - double(xq[i])) == (long long)key) {
+          gp += ep[i];
+          gq += eq[i];
+        }
+      cls_p[c] = block_sum_d(gp, sm);
+      cls_q[c] = block_sum_d(gq, sm);
+      n_cls = c + 1;
+    }
+  }
+  if (threadIdx.x == 0) {
+    ResidShard rs;
+    rs.sp = sp;
+    rs.sq = sq;
+    rs.a = a;
+    rs.b = b;
+    rs.n_amb = overflow_sm ? kResidAmb + 1 : n_cls;
+    rs.pad = 0;
+    for (int j = 0; j < kResidAmb; ++j) {
+      rs.amb[j][0] = (j < n_cls) ? cls_p[j] : 0.0;
+      rs.amb[j][1] = (j < n_cls) ? cls_q[j] : 0.0;
+    }
+    shard_out[size_t(k) * r_shards + sh] = rs;
+  }
 }
 
 // r(y) = max(0, p(y) - q(y)) and p(y) for 8 consecutive entries
@@ -358,73 +430,85 @@ __device__ __forceinline__ double wave_exclusive_d(double x, double& total) {
   return incl - x;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void resid_mass64(const T* __restrict__ p_logits,
-                                                          const T* __restrict__ q_logits, int N, int V,
-                                                          int r_shards, const ReqState* __restrict__ jobs,
-                                                          const uint32_t* __restrict__ rej_count,
-                                                          const double2* __restrict__ sums,
-                                                          double2* __restrict__ mass) {
-  __shared__ double tab64[64];
-  __shared__ double sm[kThreads / 64];
-  const int sh = blockIdx.x;
-  const int k = blockIdx.y;
-  const ReqState st = jobs[k];
-  if (k >= int(*rej_count)) return;
-  const size_t row = size_t(st.req) * (N - 1) + st.reject_row;
-  const int e1 = min(V, (sh + 1) * kRShard);
-  const int e0 = sh * kRShard + threadIdx.x * kRPer;
-  float xp[kRPer], xq[kRPer];
-  load_run<T>(p_logits + row * V, e0, e1, xp);
-  load_run<T>(q_logits + row * V, e0, e1, xq);
-  double sp, sq;
-  wave_row_sums(sums, k, r_shards, sp, sq);
-  fill_exp_table(tab64);
-  double rv[kRPer], pv[kRPer];
-  resid_values(xp, xq, st, 1.0 / sp, 1.0 / sq, tab64, rv, pv);
-  double rs = 0.0, ps = 0.0;
-#pragma unroll
-  for (int i = 0; i < kRPer; ++i) { rs += rv[i]; ps += pv[i]; }
-  rs = block_sum_d(rs, sm);
-  ps = block_sum_d(ps, sm);
-  if (threadIdx.x == 0) mass[size_t(k) * r_shards + sh] = make_double2(rs, ps);
-}
-
-// One workgroup per listed request: the inverse-CDF draw.  A wave-wide prefix over
-// the shard masses picks the shard holding u' * S, a scan inside that shard
-// in vocabulary order picks y*.
+// One workgroup per listed request: exact shard masses, then the inverse-CDF
+// draw.  A wave-wide prefix over the shard masses picks the shard holding
+// u' * S, a scan inside that shard in vocabulary order picks y*.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p_logits,
                                                           const T* __restrict__ q_logits, int N, int V,
                                                           int r_shards, const ReqState* __restrict__ jobs,
                                                           const uint32_t* __restrict__ rej_count,
-                                                          const double2* __restrict__ sums,
-                                                          const double2* __restrict__ mass,
+                                                          const ResidShard* __restrict__ shards_in,
                                                           int32_t* __restrict__ out_tokens) {
   __shared__ double tab64[64];
-  const int k = blockIdx.x;
-  const ReqState st = jobs[k];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ double rmass[kMaxResidShards], pmass[kMaxResidShards];
+  __shared__ int redo[kMaxResidShards];
+  __shared__ int n_redo_sm;
+  __shared__ double red[kThreads / 64];
   __shared__ double before_sm, target_sm;
   __shared__ int shard_sm, fb_sm, found_sm, last_sm;
   __shared__ double wsum[kThreads / 64];
-  // lane l of wave 0 owns shards [l*per, (l+1)*per) in vocabulary order; the
-  // partials and masses are requested before the count is known
-  const int per = (r_shards + 63) / 64;
-  const int s0 = min(r_shards, lane * per), s1 = min(r_shards, s0 + per);
-  double sp, sq;
-  wave_row_sums(sums, k, r_shards, sp, sq);
-  double2 first_mass = make_double2(0.0, 0.0);
-  if (wave == 0 && s0 < s1) first_mass = mass[size_t(k) * r_shards + s0];
+  const int k = blockIdx.x;
+  const ReqState st = jobs[k];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const ResidShard* recs = shards_in + size_t(k) * r_shards;
   if (k >= int(*rej_count)) return;
   const int r = st.req;
+  const size_t row = size_t(r) * (N - 1) + st.reject_row;
+  if (threadIdx.x == 0) n_redo_sm = 0;
   fill_exp_table(tab64);
+  // exact row sums and kappa (every wave, lanes over shards)
+  double sp = 0.0, sq = 0.0;
+  for (int i = lane; i < r_shards; i += 64) {
+    sp += recs[i].sp;
+    sq += recs[i].sq;
+  }
+  sp = wave_sum_d(sp);
+  sq = wave_sum_d(sq);
+  const double kap = sp / sq;
+  const bool estimate_ok = fabs(exp(double(st.log_kappa)) / kap - 1.0) < 0.5 * kResidBand;
+  const double ip = 1.0 / sp, iq = 1.0 / sq;
+  // exact shard masses from the records; shards that cannot be completed are queued
   if (wave == 0) {
+    for (int i = lane; i < r_shards; i += 64) {
+      const ResidShard& rs = recs[i];
+      pmass[i] = rs.sp * ip;
+      if (estimate_ok && rs.n_amb <= kResidAmb) {
+        double m = rs.a - kap * rs.b;
+        for (int j = 0; j < rs.n_amb; ++j) m += fmax(0.0, rs.amb[j][0] - kap * rs.amb[j][1]);
+        rmass[i] = fmax(0.0, m) * ip;
+      } else {
+        redo[atomicAdd(&n_redo_sm, 1)] = i;
+      }
+    }
+  }
+  __syncthreads();
+  // rare: recompute queued shards from the logits
+  const int n_redo = n_redo_sm;
+  for (int t = 0; t < n_redo; ++t) {
+    const int i = redo[t];
+    const int e1 = min(V, (i + 1) * kRShard);
+    const int e0 = i * kRShard + threadIdx.x * kRPer;
+    float xp[kRPer], xq[kRPer];
+    load_run<T>(p_logits + row * V, e0, e1, xp);
+    load_run<T>(q_logits + row * V, e0, e1, xq);
+    double rv[kRPer], pv[kRPer];
+    resid_values(xp, xq, st, ip, iq, tab64, rv, pv);
+    double m = 0.0;
+#pragma unroll
+    for (int j = 0; j < kRPer; ++j) m += rv[j];
+    m = block_sum_d(m, red);
+    if (threadIdx.x == 0) rmass[i] = m;
+    __syncthreads();
+  }
+  if (wave == 0) {
+    // shard masses in vocabulary order: lane l owns shards [l*per, (l+1)*per)
+    const int per = (r_shards + 63) / 64;
+    const int s0 = min(r_shards, lane * per), s1 = min(r_shards, s0 + per);
     double rsum = 0.0, psum = 0.0;
     for (int i = s0; i < s1; ++i) {
-      const double2 m = (i == s0) ? first_mass : mass[size_t(k) * r_shards + i];
-      rsum += m.x;
-      psum += m.y;
+      rsum += rmass[i];
+      psum += pmass[i];
     }
     double rtot, ptot;
     const double rbefore = wave_exclusive_d(rsum, rtot);
@@ -436,8 +520,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
     int pick = -1, last_nz = -1;
     double pick_before = 0.0, last_before = 0.0;
     for (int i = s0; i < s1; ++i) {
-      const double2 m = (i == s0) ? first_mass : mass[size_t(k) * r_shards + i];
-      const double mi = fb ? m.y : m.x;
+      const double mi = fb ? pmass[i] : rmass[i];
       if (mi > 0.0) { last_nz = i; last_before = cum; }
       if (pick < 0 && cum + mi > target) { pick = i; pick_before = cum; }
       cum += mi;
@@ -462,14 +545,13 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   __syncthreads();
   const int sh = shard_sm;
   const double target = target_sm;
-  const size_t row = size_t(r) * (N - 1) + st.reject_row;
   const int e1 = min(V, (sh + 1) * kRShard);
   const int e0 = sh * kRShard + threadIdx.x * kRPer;
   float xp[kRPer], xq[kRPer];
   load_run<T>(p_logits + row * V, e0, e1, xp);
   load_run<T>(q_logits + row * V, e0, e1, xq);
   double rv[kRPer], pv[kRPer], c[kRPer];
-  resid_values(xp, xq, st, 1.0 / sp, 1.0 / sq, tab64, rv, pv);
+  resid_values(xp, xq, st, ip, iq, tab64, rv, pv);
   double run = 0.0;
   int last_here = -1;
 #pragma unroll
@@ -512,8 +594,7 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   float2* part = reinterpret_cast<float2*>(ws + L.lse);
   ReqState* jobs = reinterpret_cast<ReqState*>(ws + L.jobs);
   uint32_t* rej_count = reinterpret_cast<uint32_t*>(ws + kRejCountOffset);
-  double2* sums = reinterpret_cast<double2*>(ws + L.resid_sums);
-  double2* mass = reinterpret_cast<double2*>(ws + L.mass);
+  ResidShard* rshards = reinterpret_cast<ResidShard*>(ws + L.resid);
   DecideArgs<T> a;
   a.p_logits = P;
   a.q_logits = Qp;
@@ -538,12 +619,10 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   hipLaunchKernelGGL((lse_partial<T>), dim3(2 * (N - 1) * p.shards, B), dim3(kThreads), 0, stream, a,
                      p.shard_len, part);
   hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
-  hipLaunchKernelGGL((resid_lse64<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shards, jobs, rej_count, sums);
-  hipLaunchKernelGGL((resid_mass64<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shards, jobs, rej_count, sums, mass);
+  hipLaunchKernelGGL((resid_pass<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
+                     p.r_shards, jobs, rej_count, rshards);
   hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,
-                     rej_count, sums, mass, out_tokens);
+                     rej_count, rshards, out_tokens);
   return hipGetLastError();
 }
 

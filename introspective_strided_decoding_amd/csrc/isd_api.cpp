@@ -141,10 +141,8 @@ WsLayout ws_layout(const isd_shape& s) {
   off = align_up(off + (size_t)c.rows * c.shards * 8, 256);
   L.jobs = off;
   off = align_up(off + (size_t)s.batch * sizeof(ReqState), 256);
-  L.resid_sums = off;
-  off = align_up(off + (size_t)s.batch * c.r_shards * 16, 256);
-  L.mass = off;
-  off = align_up(off + (size_t)s.batch * c.r_shards * 16, 256);
+  L.resid = off;
+  off = align_up(off + (size_t)s.batch * c.r_shards * sizeof(ResidShard), 256);
   L.prop = off;
   off = align_up(off + (size_t)s.batch * s.stride_n * prop_shards(s.vocab) * sizeof(PropPart), 256);
   L.total = off;

@@ -46,8 +46,7 @@ struct WsLayout {
   size_t attn_o = 0;         // float [D] per partial row
   size_t lse = 0;            // float2 (max, sum) per (row, shard)
   size_t jobs = 0;           // ReqState per rejecting request, compacted
-  size_t resid_sums = 0;     // double2 (S_p, S_q) per (listed request, residual shard)
-  size_t mass = 0;           // double2 (residual mass, p mass) per (listed request, residual shard)
+  size_t resid = 0;          // ResidShard per (listed request, residual shard)
   size_t prop = 0;           // PropPart per (MASK row, proposal shard)
   size_t total = 0;
 };
@@ -62,10 +61,25 @@ struct ReqState {
   int32_t req;          // request index r
   int32_t accept_len;   // A
   int32_t reject_row;   // j of the rejected row
-  int32_t pad;
+  float log_kappa;      // fp32 estimate of log(S_p / S_q), S = sum of exp(l - row max)
   float max_p;          // exact max logit of the rejected p row
   float max_q;          // and of its q row
   double u_resample;    // u' of the rejected position
+};
+
+// Residual pass output per (listed request, 2048-entry shard): float64 sums
+// of e_p = exp(l_p - max p) and e_q, the same over the entries clearly in the
+// residual's support under the estimated ratio, and the same again for each
+// group of entries near its boundary that share one exact logit difference.
+constexpr int kResidAmb = 8;
+constexpr int kMaxResidShards = 1024;   // vocabularies up to 2048 * 1024 entries
+struct ResidShard {
+  double sp, sq;
+  double a, b;
+  int32_t n_amb;        // groups near the boundary (kResidAmb + 1: more than fit)
+  int32_t pad;
+  double amb[kResidAmb][2];
+  double pad2;
 };
 
 // Per (MASK row, vocabulary shard) summary written by the proposal kernels.

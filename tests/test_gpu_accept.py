@@ -76,6 +76,38 @@ def test_accept_logits_far_outside_exp_range(off):
     assert t.resamples > 0
 
 
+@pytest.mark.parametrize("kind", ["one_difference", "many_differences"])
+def test_accept_residual_with_many_boundary_entries(kind):
+    """Many entries sit on the boundary of the residual's support.
+
+    The second half of the vocabulary differs (with equal mass in each half), so
+    rejections happen.  one_difference: p and q agree on the first half, so half
+    of every row shares one logit difference and the one-pass summaries keep
+    that group exactly.  many_differences: on the first half q is p plus tiny
+    offsets, so those entries are near the boundary with thousands of distinct
+    differences and the selection recomputes their shards from the logits."""
+    wl = make_workload(get_config("tiny_fp32", batch=4, vocab=8192, stride_n=4, ctx=16))
+    B, R, V = wl.p_logits.shape
+    rng = np.random.Generator(np.random.PCG64(41))
+    p = rng.normal(0.0, 3.0, size=(B, R, V))
+    lse = lambda x: x.max(-1, keepdims=True) + np.log(np.exp(x - x.max(-1, keepdims=True)).sum(-1, keepdims=True))
+    h = V // 2
+    q = p.copy()
+    if kind == "many_differences":
+        q[:, :, :h] += rng.uniform(-3e-5, 3e-5, size=(B, R, h))
+    q[:, :, h:] = rng.normal(0.0, 3.0, size=(B, R, V - h))
+    q[:, :, h:] += lse(p[:, :, h:]) - lse(q[:, :, h:])
+    wl.p_logits = p.astype(np.float32)
+    wl.q_logits = q.astype(np.float32)
+    for r in range(B):
+        for j in range(R):
+            prob = np.exp(wl.q_logits[r, j].astype(np.float64) - lse(wl.q_logits[r, j].astype(np.float64)))
+            wl.proposals[r, j + 1] = min(V - 1, int(np.searchsorted(np.cumsum(prob), rng.random() * prob.sum(), "right")))
+    wl._lse_cache = None
+    t = _run(wl, 40)
+    assert t.resamples > 10
+
+
 def test_accept_identical_rows_always_accept():
     wl = make_workload(get_config("b8_ctx2k", batch=4, ctx=16, vocab=2048))
     wl.q_logits = wl.p_logits.copy()
