@@ -292,13 +292,64 @@ __device__ __forceinline__ double block_sum_d(double x, double* sm) {
   return t;
 }
 
-// 8 consecutive logits starting at e0 (entries >= e1 read as -inf)
-template <typename T>
-__device__ __forceinline__ void load_run(const T* __restrict__ row, int e0, int e1, float* x) {
+// Workgroup sums of K doubles per thread, with one pair of barriers for all K.
+template <int K>
+__device__ __forceinline__ void block_sum_dk(double* x, double (*sm)[K]) {
 #pragma unroll
-  for (int k = 0; k < kRPer; ++k) {
-    const int e = e0 + k;
-    x[k] = (e < e1) ? to_f32<T>(row[e]) : -INFINITY;
+  for (int m = 1; m < 64; m <<= 1)
+#pragma unroll
+    for (int i = 0; i < K; ++i) x[i] += __shfl_xor(x[i], m);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int i = 0; i < K; ++i) sm[wave][i] = x[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    double t = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) t += sm[w][i];
+    x[i] = t;
+  }
+}
+
+// 8 consecutive logits of a p row and of a q row starting at e0 (entries
+// >= e1 read as -inf), all loads in flight together.  Whole 16-byte aligned
+// runs are one or two vector loads per row; otherwise the indices are clamped
+// into the shard so that every load is unconditional.
+template <typename T>
+__device__ __forceinline__ void load_runs(const T* __restrict__ prow, const T* __restrict__ qrow, int e0,
+                                          int e1, float* xp, float* xq) {
+  constexpr int VN = Vec<T>::N;
+  const bool vec = e0 + kRPer <= e1 && ((reinterpret_cast<uintptr_t>(prow + e0) |
+                                         reinterpret_cast<uintptr_t>(qrow + e0)) & 15) == 0;
+  if (vec) {
+    const u32x4* vp = reinterpret_cast<const u32x4*>(prow + e0);
+    const u32x4* vq = reinterpret_cast<const u32x4*>(qrow + e0);
+    u32x4 rp[kRPer / VN], rq[kRPer / VN];
+#pragma unroll
+    for (int k = 0; k < kRPer / VN; ++k) {
+      rp[k] = vp[k];
+      rq[k] = vq[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kRPer / VN; ++k) {
+      unpack(rp[k], xp + k * VN, T());
+      unpack(rq[k], xq + k * VN, T());
+    }
+  } else {
+    T rp[kRPer], rq[kRPer];
+#pragma unroll
+    for (int k = 0; k < kRPer; ++k) {
+      const int e = min(e0 + k, e1 - 1);
+      rp[k] = prow[e];
+      rq[k] = qrow[e];
+    }
+#pragma unroll
+    for (int k = 0; k < kRPer; ++k) {
+      xp[k] = (e0 + k < e1) ? to_f32<T>(rp[k]) : -INFINITY;
+      xq[k] = (e0 + k < e1) ? to_f32<T>(rq[k]) : -INFINITY;
+    }
   }
 }
 
@@ -311,7 +362,9 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   constexpr unsigned long long kEmpty = ~0ull;   // a NaN pattern, never an exact difference
   __shared__ double tab64[64];
   __shared__ double sm[kThreads / 64];
+  __shared__ double sm5[kThreads / 64][5];
   __shared__ unsigned long long cls_sm[kResidAmb];
+  __shared__ double cls_sum[kResidAmb][2];
   __shared__ int overflow_sm;
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
@@ -321,8 +374,7 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   const int e1 = min(V, (sh + 1) * kRShard);
   const int e0 = sh * kRShard + threadIdx.x * kRPer;
   float xp[kRPer], xq[kRPer];
-  load_run<T>(p_logits + row * V, e0, e1, xp);
-  load_run<T>(q_logits + row * V, e0, e1, xq);
+  load_runs<T>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
   if (threadIdx.x < kResidAmb) cls_sm[threadIdx.x] = kEmpty;
   if (threadIdx.x == 0) overflow_sm = 0;
   fill_exp_table(tab64);
@@ -344,14 +396,15 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
       amb |= 1u << i;
     }
   }
-  sp = block_sum_d(sp, sm);
-  sq = block_sum_d(sq, sm);
-  a = block_sum_d(a, sm);
-  b = block_sum_d(b, sm);
+  double tot[5] = {sp, sq, a, b, double(__builtin_popcount(amb))};
+  block_sum_dk<5>(tot, sm5);
+  sp = tot[0];
+  sq = tot[1];
+  a = tot[2];
+  b = tot[3];
   // entries near the boundary: group them by their exact logit difference
   int n_cls = 0;
-  double cls_p[kResidAmb], cls_q[kResidAmb];
-  if (__syncthreads_or(amb != 0)) {
+  if (tot[4] > 0.0) {
 #pragma unroll
     for (int i = 0; i < kRPer; ++i) {
       if (amb & (1u << i)) {
@@ -385,8 +438,12 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
           gp += ep[i];
           gq += eq[i];
         }
-      cls_p[c] = block_sum_d(gp, sm);
-      cls_q[c] = block_sum_d(gq, sm);
+      gp = block_sum_d(gp, sm);
+      gq = block_sum_d(gq, sm);
+      if (threadIdx.x == 0) {
+        cls_sum[c][0] = gp;
+        cls_sum[c][1] = gq;
+      }
       n_cls = c + 1;
     }
   }
@@ -399,8 +456,8 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
     rs.n_amb = overflow_sm ? kResidAmb + 1 : n_cls;
     rs.pad = 0;
     for (int j = 0; j < kResidAmb; ++j) {
-      rs.amb[j][0] = (j < n_cls) ? cls_p[j] : 0.0;
-      rs.amb[j][1] = (j < n_cls) ? cls_q[j] : 0.0;
+      rs.amb[j][0] = (j < n_cls) ? cls_sum[j][0] : 0.0;
+      rs.amb[j][1] = (j < n_cls) ? cls_sum[j][1] : 0.0;
     }
     shard_out[size_t(k) * r_shards + sh] = rs;
   }
@@ -448,40 +505,46 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   __shared__ double before_sm, target_sm;
   __shared__ int shard_sm, fb_sm, found_sm, last_sm;
   __shared__ double wsum[kThreads / 64];
+  __shared__ double sm2[kThreads / 64][2];
   const int k = blockIdx.x;
-  const ReqState st = jobs[k];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const ResidShard* recs = shards_in + size_t(k) * r_shards;
+  // thread t's first shard record is requested together with the list entry
+  const bool mine_ok = threadIdx.x < r_shards;
+  ResidShard mine;
+  if (mine_ok) mine = recs[threadIdx.x];
+  const ReqState st = jobs[k];
   if (k >= int(*rej_count)) return;
   const int r = st.req;
   const size_t row = size_t(r) * (N - 1) + st.reject_row;
   if (threadIdx.x == 0) n_redo_sm = 0;
   fill_exp_table(tab64);
-  // exact row sums and kappa (every wave, lanes over shards)
-  double sp = 0.0, sq = 0.0;
-  for (int i = lane; i < r_shards; i += 64) {
-    sp += recs[i].sp;
-    sq += recs[i].sq;
+  // exact row sums and kappa (threads over shards)
+  double tot[2] = {mine_ok ? mine.sp : 0.0, mine_ok ? mine.sq : 0.0};
+  for (int i = threadIdx.x + kThreads; i < r_shards; i += kThreads) {
+    tot[0] += recs[i].sp;
+    tot[1] += recs[i].sq;
   }
-  sp = wave_sum_d(sp);
-  sq = wave_sum_d(sq);
+  block_sum_dk<2>(tot, sm2);
+  const double sp = tot[0], sq = tot[1];
   const double kap = sp / sq;
   const bool estimate_ok = fabs(exp(double(st.log_kappa)) / kap - 1.0) < 0.5 * kResidBand;
   const double ip = 1.0 / sp, iq = 1.0 / sq;
   // exact shard masses from the records; shards that cannot be completed are queued
-  if (wave == 0) {
-    for (int i = lane; i < r_shards; i += 64) {
-      const ResidShard& rs = recs[i];
-      pmass[i] = rs.sp * ip;
-      if (estimate_ok && rs.n_amb <= kResidAmb) {
-        double m = rs.a - kap * rs.b;
-        for (int j = 0; j < rs.n_amb; ++j) m += fmax(0.0, rs.amb[j][0] - kap * rs.amb[j][1]);
-        rmass[i] = fmax(0.0, m) * ip;
-      } else {
-        redo[atomicAdd(&n_redo_sm, 1)] = i;
-      }
+  auto shard_mass = [&](const ResidShard& rs, int i) {
+    pmass[i] = rs.sp * ip;
+    if (estimate_ok && rs.n_amb <= kResidAmb) {
+      double m = rs.a - kap * rs.b;
+#pragma unroll
+      for (int j = 0; j < kResidAmb; ++j)
+        if (j < rs.n_amb) m += fmax(0.0, rs.amb[j][0] - kap * rs.amb[j][1]);
+      rmass[i] = fmax(0.0, m) * ip;
+    } else {
+      redo[atomicAdd(&n_redo_sm, 1)] = i;
     }
-  }
+  };
+  if (mine_ok) shard_mass(mine, threadIdx.x);
+  for (int i = threadIdx.x + kThreads; i < r_shards; i += kThreads) shard_mass(recs[i], i);
   __syncthreads();
   // rare: recompute queued shards from the logits
   const int n_redo = n_redo_sm;
@@ -490,8 +553,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
     const int e1 = min(V, (i + 1) * kRShard);
     const int e0 = i * kRShard + threadIdx.x * kRPer;
     float xp[kRPer], xq[kRPer];
-    load_run<T>(p_logits + row * V, e0, e1, xp);
-    load_run<T>(q_logits + row * V, e0, e1, xq);
+    load_runs<T>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
     double rv[kRPer], pv[kRPer];
     resid_values(xp, xq, st, ip, iq, tab64, rv, pv);
     double m = 0.0;
@@ -548,8 +610,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   const int e1 = min(V, (sh + 1) * kRShard);
   const int e0 = sh * kRShard + threadIdx.x * kRPer;
   float xp[kRPer], xq[kRPer];
-  load_run<T>(p_logits + row * V, e0, e1, xp);
-  load_run<T>(q_logits + row * V, e0, e1, xq);
+  load_runs<T>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
   double rv[kRPer], pv[kRPer], c[kRPer];
   resid_values(xp, xq, st, ip, iq, tab64, rv, pv);
   double run = 0.0;

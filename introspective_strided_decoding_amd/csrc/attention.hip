@@ -397,18 +397,33 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   // ---- the stride block: keys/values of this pass's rows, masked j <= i ----
   if (stride_tile) {
+    // rows past Qn read row Qn - 1 and are zeroed after the load, so every
+    // load is unconditional and all of them are in flight together
     u32x4 sk[KS], sv[2][DB];
     const int ti = lane & 31;
+    const int tic = min(ti, Qn - 1);
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      sk[s] = (ti < Qn) ? *reinterpret_cast<const u32x4*>(
-                              k_new + ((size_t(r) * Qn + ti) * Hkv + hk) * D + (2 * s + h) * 8)
-                        : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(k_new + ((size_t(r) * Qn + tic) * Hkv + hk) * D +
+                                                      (2 * s + h) * 8);
+      sk[s] = (ti < Qn) ? v : u32x4{0, 0, 0, 0};
+    }
+    // Values: lane (h, c) needs 8 tokens of dim c, so the block's rows are
+    // staged in LDS (the merge buffer, untouched until the waves combine at
+    // the end) with whole-row 16-byte loads and picked from there.
+    uint16_t* sm_vn = reinterpret_cast<uint16_t*>(sm_o0);
+    constexpr int CH = D / 8;   // 16-byte chunks per row
+    for (int c = lane; c < Qn * CH; c += 64)
+      *reinterpret_cast<u32x4*>(sm_vn + (c / CH) * D + (c % CH) * 8) = *reinterpret_cast<const u32x4*>(
+          v_new + ((size_t(r) * Qn + c / CH) * Hkv + hk) * D + (c % CH) * 8);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = db * 32 + (lane & 31);
+        const uint16_t* vcol = sm_vn + db * 32 + (lane & 31);
         uint32_t w[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -417,8 +432,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           for (int hi = 0; hi < 2; ++hi) {
             const int e = 2 * e2 + hi;
             const int t = 16 * m + (e >> 2) * 8 + h * 4 + (e & 3);
-            const uint32_t bits =
-                (t < Qn) ? uint32_t(v_new[((size_t(r) * Qn + t) * Hkv + hk) * D + d]) : 0u;
+            const uint32_t raw = vcol[min(t, Qn - 1) * D];
+            const uint32_t bits = (t < Qn) ? raw : 0u;
             pair |= bits << (16 * hi);
           }
           w[e2] = pair;

@@ -108,10 +108,11 @@ AcceptPlan plan_accept(const isd_shape& s) {
   AcceptPlan p{};
   p.rows = 2 * s.batch * (s.stride_n - 1);
   const int V = s.vocab;
-  // About 2048 workgroups in the normaliser pass, at least 2048 entries each,
-  // and at most 256 threads x 8 vectors of 16 bytes per shard.
+  // At most 2048 workgroups in the normaliser pass (what 256 CUs hold at once
+  // at its 8 waves per SIMD, so no workgroup waits for a slot), at least 2048
+  // entries each, and at most 256 threads x 8 vectors of 16 bytes per shard.
   const int vec = (s.logit_dtype == ISD_BF16) ? 8 : 4;
-  int shards = std::max(1, ceil_div(2048, p.rows));
+  int shards = std::max(1, 2048 / p.rows);
   shards = std::min(shards, std::max(1, V / 2048));
   shards = std::max(shards, ceil_div(V, 256 * 8 * vec));
   p.shard_len = ceil_div(ceil_div(V, shards), 8) * 8;

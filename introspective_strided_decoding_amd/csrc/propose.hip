@@ -48,8 +48,13 @@ __device__ __forceinline__ void load_entries(const T* __restrict__ row, int e0, 
       for (int i = 0; i < EV; ++i) x[v * EV + i] = to_f32<T>(t[i]);
     }
   } else {
+    // indices clamped into the row so that every load is unconditional and
+    // all of them are in flight together
+    T t[kPPer];
 #pragma unroll
-    for (int i = 0; i < kPPer; ++i) x[i] = (e0 + i < e1) ? to_f32<T>(row[e0 + i]) : -INFINITY;
+    for (int i = 0; i < kPPer; ++i) t[i] = row[min(e0 + i, e1 - 1)];
+#pragma unroll
+    for (int i = 0; i < kPPer; ++i) x[i] = (e0 + i < e1) ? to_f32<T>(t[i]) : -INFINITY;
   }
 }
 
@@ -158,6 +163,11 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
   first_part.max = -INFINITY;
   first_part.idx = INT_MAX;
   if (wave == 0 && s0 < s1) first_part = rp[s0];
+  uint32_t rid32 = 0, pos32 = 0;
+  if (wave == 0 && sample) {
+    rid32 = uint32_t(req_ids[r]);
+    pos32 = uint32_t(positions[r]);
+  }
   if (sample) fill_exp_table(tab64);
   if (wave == 0) {
     float mx = -INFINITY;
@@ -178,8 +188,8 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
       if (lane == 0) out[row] = (I == INT_MAX) ? 0 : I;
     } else {
       // uniform of this proposal: counter (request, position + N + k, step, 1), word 0
-      const uint64_t rid = uint64_t(uint32_t(req_ids[r]));
-      const uint64_t pos = uint64_t(uint32_t(positions[r])) + uint64_t(N + k);
+      const uint64_t rid = uint64_t(rid32);
+      const uint64_t pos = uint64_t(pos32) + uint64_t(N + k);
       const double u = unit_double(philox4x64_10(rid, pos, uint64_t(step), 1, seed_lo, seed_hi).w[0]);
       // shard masses in units of exp(row max)
       const double Md = M;
@@ -194,30 +204,36 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
       double cum = before_lane;
       int pick = -1, last_nz = -1;
       double pick_before = 0.0, last_before = 0.0;
+      float pick_max = -INFINITY, last_max = -INFINITY;
       for (int i = s0; i < s1; ++i) {
         const PropPart p = (i == s0) ? first_part : rp[i];
         const double wi = (p.max == -INFINITY) ? 0.0 : p.sum * exp_nonpos(double(p.max) - Md, tab64);
-        if (wi > 0.0) { last_nz = i; last_before = cum; }
-        if (pick < 0 && cum + wi > target) { pick = i; pick_before = cum; }
+        if (wi > 0.0) { last_nz = i; last_before = cum; last_max = p.max; }
+        if (pick < 0 && cum + wi > target) { pick = i; pick_before = cum; pick_max = p.max; }
         cum += wi;
       }
       const uint64_t hits = __ballot(pick >= 0);
       const uint64_t nz = __ballot(last_nz >= 0);
       int sh;
       double bf;
+      float ms;
       if (hits) {
         const int src = __ffsll((unsigned long long)hits) - 1;
         sh = __shfl(pick, src);
         bf = __shfl(pick_before, src);
+        ms = __shfl(pick_max, src);
       } else {
         // rounding left the target at or past the total: the last shard with mass
         const int src = nz ? 63 - __clzll((long long)nz) : 0;
         sh = __shfl(last_nz, src);
         bf = __shfl(last_before, src);
-        if (sh < 0) sh = 0;
+        ms = __shfl(last_max, src);
+        if (sh < 0) {
+          sh = 0;
+          ms = -INFINITY;
+        }
       }
       if (lane == 0) {
-        const float ms = rp[sh].max;
         shard_sm = sh;
         before_sm = bf;
         target_sm = target;
