@@ -4,10 +4,11 @@
 //   lse_partial    one read of every p and q row: per (row, vocabulary shard)
 //                  the max and the sum of exp(l - max), fp32, 16-byte
 //                  streaming loads, wave reductions by lane exchange, then
-//                  across the 4 waves.
+//                  across the 4 waves; the workgroup whose shard holds the
+//                  row's proposal also records the logit there.
 //   accept_decide  one workgroup per request: its waves combine the shard
 //                  partials of the request's rows into log-normalisers while
-//                  the first wave already holds the logits at the proposals;
+//                  the first wave loads the recorded logits at the proposals;
 //                  rho = exp(log p - log q), Philox uniforms, accept iff
 //                  u < rho, first rejection by a wave ballot.
 //   resid_pass     rejecting requests only, one pass over the rejected p
@@ -72,6 +73,7 @@ struct DecideArgs {
   float *logp_sel, *logq_sel;
   ReqState* jobs;          // compact list of rejecting requests
   uint32_t* rej_count;     // its length
+  float* gath;             // per (request, p/q row): the row's logit at its proposal
   uint32_t* flags;
 };
 
@@ -94,6 +96,10 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
   const T* base = (is_q ? args.q_logits : args.p_logits) + row_off;
   const int e0 = sh * shard_len;
   const int e1 = min(V, e0 + shard_len);
+  // the proposal this row tests (x_{j+2} for p row and q row j)
+  const int xg = args.proposals[size_t(r) * args.N + (is_q ? jj - R : jj) + 1];
+  float xv = 0.f;
+  bool has_x = false;
   float m = -INFINITY, s = 0.f;
   if (e0 < e1) {
     // scalar head up to 16-byte alignment of the absolute element index, vector body, scalar tail
@@ -110,8 +116,32 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
     }
     float tail = -INFINITY;
     bool has_tail = false;
-    for (int e = e0 + threadIdx.x; e < hb; e += kThreads) { tail = fmaxf(tail, to_f32<T>(base[e])); has_tail = true; }
-    for (int e = tb + threadIdx.x; e < e1; e += kThreads) { tail = fmaxf(tail, to_f32<T>(base[e])); has_tail = true; }
+    for (int e = e0 + threadIdx.x; e < hb; e += kThreads) {
+      const float v = to_f32<T>(base[e]);
+      tail = fmaxf(tail, v);
+      has_tail = true;
+      if (e == xg) { xv = v; has_x = true; }
+    }
+    for (int e = tb + threadIdx.x; e < e1; e += kThreads) {
+      const float v = to_f32<T>(base[e]);
+      tail = fmaxf(tail, v);
+      has_tail = true;
+      if (e == xg) { xv = v; has_x = true; }
+    }
+    // the logit at the proposal, from the registers of the thread that holds it
+    if (xg >= hb && xg < tb && (xg - hb) / VN % kThreads == int(threadIdx.x)) {
+      const int kx = (xg - hb) / VN / kThreads, ix = (xg - hb) % VN;
+#pragma unroll
+      for (int k = 0; k < kLseVec; ++k)
+        if (k == kx) {
+          float x[VN];
+          unpack(raw[k], x, T());
+#pragma unroll
+          for (int i = 0; i < VN; ++i)
+            if (i == ix) xv = x[i];
+        }
+      has_x = true;
+    }
     // pass 1: max over this thread's values (registers only)
     float mx = tail;
 #pragma unroll
@@ -159,10 +189,12 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
     // the decision kernel, next in the stream, lists rejecting requests from zero
     if (blockIdx.x == 0 && blockIdx.y == 0) *args.rej_count = 0u;
   }
+  if (has_x) args.gath[size_t(r) * 2 * R + jj] = xv;
 }
 
 // One workgroup per request.  Lane j < N-1 of wave 0 tests x_{j+2} against
-// p row j and q row j; a ballot finds the first rejection.
+// p row j and q row j (their logits there were recorded by the normaliser
+// kernel); a ballot finds the first rejection.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const float2* __restrict__ part) {
   const int r = blockIdx.x;
@@ -170,18 +202,17 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float lse_sm[64], max_sm[64];
   // wave 0: the proposals and the logits at them, requested before the combine
-  int x = 0;
+  int x = 0, xl = 0;
   float raw_p = 0.f, raw_q = 0.f;
-  bool in_range = false;
-  if (wave == 0 && lane < R) {
-    x = a.proposals[size_t(r) * N + lane + 1];
-    in_range = x >= 0 && x < V;
-    if (in_range) {
-      const size_t row = size_t(r) * R + lane;
-      raw_p = to_f32<T>(a.p_logits[row * V + x]);
-      raw_q = to_f32<T>(a.q_logits[row * V + x]);
+  if (wave == 0) {
+    if (lane < R) {
+      x = a.proposals[size_t(r) * N + lane + 1];
+      raw_p = a.gath[size_t(r) * 2 * R + lane];
+      raw_q = a.gath[size_t(r) * 2 * R + R + lane];
     }
+    if (lane < N) xl = a.proposals[size_t(r) * N + lane];
   }
+  const bool in_range = x >= 0 && x < V;
   // every wave: rows wave, wave + 4, ... of the request's 2(N-1) rows
   const float2* req_part = part + size_t(r) * 2 * R * shards;
   for (int row = wave; row < 2 * R; row += kThreads / 64) {
@@ -224,10 +255,7 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
   const int A = (first < 0) ? N : first + 1;
   const double u_first = __shfl(u_res, first < 0 ? 0 : first);
-  if (lane < N) {
-    const int xl = a.proposals[size_t(r) * N + lane];
-    a.out_tokens[size_t(r) * N + lane] = (lane < A) ? xl : -1;
-  }
+  if (lane < N) a.out_tokens[size_t(r) * N + lane] = (lane < A) ? xl : -1;
   if (lane == 0) {
     a.accept_len[r] = A;
     a.n_out[r] = A + (A < N ? 1 : 0);
@@ -676,6 +704,7 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.logq_sel = logq_sel;
   a.jobs = jobs;
   a.rej_count = rej_count;
+  a.gath = reinterpret_cast<float*>(ws + L.gath);
   a.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
   hipLaunchKernelGGL((lse_partial<T>), dim3(2 * (N - 1) * p.shards, B), dim3(kThreads), 0, stream, a,
                      p.shard_len, part);

@@ -142,6 +142,8 @@ WsLayout ws_layout(const isd_shape& s) {
   off = align_up(off + (size_t)c.rows * c.shards * 8, 256);
   L.jobs = off;
   off = align_up(off + (size_t)s.batch * sizeof(ReqState), 256);
+  L.gath = off;
+  off = align_up(off + (size_t)c.rows * 4, 256);
   L.resid = off;
   off = align_up(off + (size_t)s.batch * c.r_shards * sizeof(ResidShard), 256);
   L.prop = off;
