@@ -531,7 +531,8 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   __shared__ int n_redo_sm;
   __shared__ double red[kThreads / 64];
   __shared__ double before_sm, target_sm;
-  __shared__ int shard_sm, fb_sm, found_sm, last_sm;
+  __shared__ int shard_sm, fb_sm;
+  __shared__ int hit_sm[kThreads / 64], last_sm[kThreads / 64];
   __shared__ double wsum[kThreads / 64];
   __shared__ double sm2[kThreads / 64][2];
   const int k = blockIdx.x;
@@ -630,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
       const double bf = __shfl(last_before, src);
       if (lane == 0) { shard_sm = sh < 0 ? 0 : sh; before_sm = bf; }
     }
-    if (lane == 0) { target_sm = target; fb_sm = fb; found_sm = INT_MAX; last_sm = -1; }
+    if (lane == 0) { target_sm = target; fb_sm = fb; }
   }
   __syncthreads();
   const int sh = shard_sm;
@@ -661,12 +662,11 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
 #pragma unroll
   for (int i = kRPer - 1; i >= 0; --i)
     if (e0 + i < e1 && before + c[i] > target) hit = e0 + i;
-  if (hit != INT_MAX) atomicMin(&found_sm, hit);
-  if (last_here >= 0) atomicMax(&last_sm, last_here);
-  __syncthreads();
+  int first_hit, last_nz;
+  block_first_last(hit, last_here, hit_sm, last_sm, first_hit, last_nz);
   if (threadIdx.x == 0) {
-    int y = found_sm;
-    if (y == INT_MAX) y = (last_sm >= 0) ? last_sm : e1 - 1;
+    int y = first_hit;
+    if (y == INT_MAX) y = (last_nz >= 0) ? last_nz : e1 - 1;
     out_tokens[size_t(r) * N + st.accept_len] = y;
   }
 }

@@ -1,6 +1,8 @@
 // Device helpers shared by the ISD kernels (gfx950, wave64).
 #pragma once
 
+#include <climits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,6 +92,30 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
   }
   __syncthreads();
   return *s_flag != 0;
+}
+
+// Smallest `hit` (INT_MAX: none) and largest `last` (-1: none) over the
+// workgroup: a ballot per wave, one LDS slot per wave (arrays of at least
+// blockDim.x / 64 entries), a barrier, and every thread reads the slots.
+// (Divergent LDS atomics would be turned into a loop over the active lanes.)
+__device__ __forceinline__ void block_first_last(int hit, int last, int* sm_hit, int* sm_last, int& out_hit,
+                                                 int& out_last) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const uint64_t hb = __ballot(hit != INT_MAX);
+  const uint64_t lb = __ballot(last >= 0);
+  const int wh = __shfl(hit, hb ? __ffsll((unsigned long long)hb) - 1 : 0);
+  const int wl = __shfl(last, lb ? 63 - __clzll((long long)lb) : 0);
+  if (lane == 0) {
+    sm_hit[wave] = hb ? wh : INT_MAX;
+    sm_last[wave] = lb ? wl : -1;
+  }
+  __syncthreads();
+  out_hit = INT_MAX;
+  out_last = -1;
+  for (int w = 0; w < int(blockDim.x) / kWave; ++w) {
+    out_hit = min(out_hit, sm_hit[w]);
+    out_last = max(out_last, sm_last[w]);
+  }
 }
 
 // Device flag word (workspace offset 0).

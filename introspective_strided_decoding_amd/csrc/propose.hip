@@ -152,7 +152,8 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
   __shared__ double tab64[64];
   __shared__ double before_sm, target_sm, scale_sm;
   __shared__ float mshard_sm;
-  __shared__ int shard_sm, found_sm, last_sm;
+  __shared__ int shard_sm;
+  __shared__ int hit_sm[kPThreads / 64], last_sm[kPThreads / 64];
   __shared__ double wsum[kPThreads / 64];
   // lane l of wave 0 owns shards [l*per, (l+1)*per) in vocabulary order; the
   // first of them is requested before the table is built
@@ -239,8 +240,6 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
         target_sm = target;
         mshard_sm = ms;
         scale_sm = (ms == -INFINITY) ? 0.0 : exp_nonpos(double(ms) - Md, tab64);
-        found_sm = INT_MAX;
-        last_sm = -1;
       }
     }
   }
@@ -277,12 +276,11 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
 #pragma unroll
   for (int i = kPPer - 1; i >= 0; --i)
     if (e0 + i < e1 && before + c[i] > target) hit = e0 + i;
-  if (hit != INT_MAX) atomicMin(&found_sm, hit);
-  if (last_here >= 0) atomicMax(&last_sm, last_here);
-  __syncthreads();
+  int first_hit, last_nz;
+  block_first_last(hit, last_here, hit_sm, last_sm, first_hit, last_nz);
   if (threadIdx.x == 0) {
-    int y = found_sm;
-    if (y == INT_MAX) y = (last_sm >= 0) ? last_sm : max(0, e1 - 1);
+    int y = first_hit;
+    if (y == INT_MAX) y = (last_nz >= 0) ? last_nz : max(0, e1 - 1);
     out[row] = y;
   }
 }
