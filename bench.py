@@ -1,8 +1,9 @@
 """Throughput of the ISD step on one MI355X.
 
 A step is one pass of the whole hot path over the batch: isd_attention ->
-isd_accept -> kv_commit (+ isd_lora_delta for the R-ISD workload), enqueued on
-one stream.  The MASK-row proposals for the next step (isd_propose, sampling
+isd_accept_commit (the accept test, residual resampling and the KV commit of
+the accepted rows in one call) (+ isd_lora_delta for the R-ISD workload),
+enqueued on one stream.  The MASK-row proposals for the next step (isd_propose, sampling
 and argmax policies) are timed in a loop of their own after the steps and
 reported under "propose"; they do not enter "value".  Neither do "graph" (the
 step replayed from HIP graphs) and "loop" (whole forwards of the multi-step
@@ -192,8 +193,7 @@ def main(argv=None):
         st.attention()
         if ev is not None:
             ev[1].record(stream)
-        st.accept()
-        st.commit()
+        st.accept_commit()
         if use_lora:
             st.lora_delta()
 

@@ -15,7 +15,8 @@
  *   isd_accept     the p/q test: accept x_k with probability min(1, p/q),
  *                  resample from normalize(max(0, p - q)) at the first
  *                  rejection;
- *   kv_commit      append the CLEAN rows of accepted tokens to the KV pages;
+ *   kv_commit      append the CLEAN rows of accepted tokens to the KV pages
+ *                  (isd_accept_commit: both in one call);
  *   isd_propose    draw the next N proposals at the MASK rows (sampling or
  *                  argmax);
  *   isd_loop_advance  per-request bookkeeping of the multi-step decoding loop;
@@ -235,6 +236,30 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
                      const int32_t* ctx_lens_in, const int32_t* n_commit,
                      int32_t* ctx_lens_out, void* workspace, size_t ws_bytes,
                      hipStream_t stream);
+
+/*
+ * isd_accept_commit -- isd_accept, then kv_commit of the rows it accepted, in
+ * one call with one launch fewer.
+ *
+ * Same definitions, arguments and outputs as isd_accept followed by
+ * kv_commit(shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in,
+ * n_commit, ctx_lens_out, ...) on the same stream, with n_commit the
+ * isd_accept output; results are identical to those two calls.  The commit's
+ * workgroups run inside the residual launch, next to the residual work,
+ * once the accept decision is known.  For the plain step (attention ->
+ * accept -> commit); a decoding loop that gates n_commit with
+ * isd_loop_advance between accept and commit calls the two separately.
+ * Flags: those of both calls.
+ */
+isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const void* q_logits,
+                             const int32_t* proposals, const int32_t* req_ids,
+                             const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
+                             uint32_t step, int32_t* accept_len, int32_t* out_tokens,
+                             int32_t* n_out, int32_t* n_commit, float* logp_sel, float* logq_sel,
+                             const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                             const int32_t* page_table, const int32_t* ctx_lens_in,
+                             int32_t* ctx_lens_out, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
 
 /*
  * isd_propose -- draw the next N proposals at the MASK rows.

@@ -26,7 +26,7 @@ STATUS = {0: "ISD_OK", 1: "ISD_ERR_NULL", 2: "ISD_ERR_SHAPE", 3: "ISD_ERR_DTYPE"
 
 # Every symbol include/isd.h declares.
 EXPORTS = ("isd_workspace_bytes", "isd_workspace_init", "isd_read_flags", "isd_attention",
-           "isd_accept", "kv_commit", "isd_propose", "isd_loop_advance", "isd_lora_workspace_bytes",
+           "isd_accept", "kv_commit", "isd_accept_commit", "isd_propose", "isd_loop_advance", "isd_lora_workspace_bytes",
            "isd_lora_delta",
            "isd_status_string", "isd_last_error", "isd_abi_version")
 PROPOSE_SAMPLE, PROPOSE_ARGMAX = 0, 1
@@ -85,6 +85,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "isd_attention": (I32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, SZ, P]),
         "kv_commit": (I32, [SP, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "isd_accept_commit": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P,
+                                    P, P, P, P, P, P, P, P, SZ, P]),
         "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, I32, P, P, SZ, P]),
         "isd_loop_advance": (I32, [SP, P, P, P, P, P, P, P, P, P, P]),
         "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
@@ -206,6 +208,31 @@ def kv_commit(shape: Shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens
         _ptr(page_table, "page_table", torch.int32, B * shape.max_pages),
         _ptr(ctx_lens_in, "ctx_lens_in", torch.int32, B), _ptr(n_commit, "n_commit", torch.int32, B),
         _ptr(ctx_lens_out, "ctx_lens_out", torch.int32, B),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
+                      accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new, v_new, k_pages,
+                      v_pages, page_table, ctx_lens_in, ctx_lens_out, workspace, stream=None) -> None:
+    """isd_accept followed by kv_commit of the accepted rows, in one call."""
+    B, N, V = shape.batch, shape.stride_n, shape.vocab
+    Q, Hkv, D = shape.q_rows, shape.n_kv_heads, shape.head_dim
+    dt, kt = _tdtype(shape.logit_dtype), _tdtype(shape.kv_dtype)
+    pool = shape.num_pages * Hkv * shape.page_size * D
+    i32 = torch.int32
+    _check("isd_accept_commit", LIB.isd_accept_commit(
+        ctypes.byref(shape.c()), _ptr(p_logits, "p_logits", dt, B * (N - 1) * V),
+        _ptr(q_logits, "q_logits", dt, B * (N - 1) * V), _ptr(proposals, "proposals", i32, B * N),
+        _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
+        int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF,
+        _ptr(accept_len, "accept_len", i32, B), _ptr(out_tokens, "out_tokens", i32, B * N),
+        _ptr(n_out, "n_out", i32, B), _ptr(n_commit, "n_commit", i32, B),
+        _ptr(logp_sel, "logp_sel", torch.float32, B * (N - 1)),
+        _ptr(logq_sel, "logq_sel", torch.float32, B * (N - 1)),
+        _ptr(k_new, "k_new", kt, B * Q * Hkv * D), _ptr(v_new, "v_new", kt, B * Q * Hkv * D),
+        _ptr(k_pages, "k_pages", kt, pool), _ptr(v_pages, "v_pages", kt, pool),
+        _ptr(page_table, "page_table", i32, B * shape.max_pages),
+        _ptr(ctx_lens_in, "ctx_lens_in", i32, B), _ptr(ctx_lens_out, "ctx_lens_out", i32, B),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
 
 

@@ -28,6 +28,7 @@
 // dispatched; the rest return after reading the count.
 #include <climits>
 
+#include "commit_row.hpp"
 #include "device_common.hpp"
 #include "exp64.hpp"
 #include "isd_internal.hpp"
@@ -36,6 +37,7 @@ namespace isd {
 namespace {
 
 constexpr int kThreads = 256;
+static_assert(kThreads == kCommitThreads, "commit workgroups run inside the residual pass launch");
 
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> { static constexpr int N = 8; };
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
                                                         const T* __restrict__ q_logits, int N, int V,
                                                         int r_shards, const ReqState* __restrict__ jobs,
                                                         const uint32_t* __restrict__ rej_count,
-                                                        ResidShard* __restrict__ shard_out) {
+                                                        ResidShard* __restrict__ shard_out, CommitArgs cm) {
   constexpr unsigned long long kEmpty = ~0ull;   // a NaN pattern, never an exact difference
   __shared__ double tab64[64];
   __shared__ double sm[kThreads / 64];
@@ -394,8 +396,18 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   __shared__ unsigned long long cls_sm[kResidAmb];
   __shared__ double cls_sum[kResidAmb][2];
   __shared__ int overflow_sm;
+  __shared__ int commit_last;
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
+  // columns past the residual shards (isd_accept_commit only): commit CLEAN
+  // row sh - r_shards of request k while the residual work runs
+  if (sh >= r_shards) {
+    if (cm.kv_bf16)
+      commit_row<uint16_t>(cm, sh - r_shards, k, &commit_last);
+    else
+      commit_row<float>(cm, sh - r_shards, k, &commit_last);
+    return;
+  }
   const ReqState st = jobs[k];
   if (k >= int(*rej_count)) return;
   const size_t row = size_t(st.req) * (N - 1) + st.reject_row;
@@ -676,7 +688,8 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
                     const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
                     uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
                     int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
-                    float* logq_sel, char* ws, const WsLayout& L, hipStream_t stream) {
+                    float* logq_sel, char* ws, const WsLayout& L, const CommitArgs* commit,
+                    hipStream_t stream) {
   const T* P = static_cast<const T*>(pl);
   const T* Qp = static_cast<const T*>(ql);
   const int N = s.stride_n, V = s.vocab, B = s.batch;
@@ -709,8 +722,12 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   hipLaunchKernelGGL((lse_partial<T>), dim3(2 * (N - 1) * p.shards, B), dim3(kThreads), 0, stream, a,
                      p.shard_len, part);
   hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
-  hipLaunchKernelGGL((resid_pass<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shards, jobs, rej_count, rshards);
+  // with a commit, N - 1 more columns of workgroups: one per (CLEAN row, request)
+  CommitArgs cm{};
+  if (commit) cm = *commit;
+  const int cols = p.r_shards + (commit ? N - 1 : 0);
+  hipLaunchKernelGGL((resid_pass<T>), dim3(cols, B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,
+                     rej_count, rshards, cm);
   hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,
                      rej_count, rshards, out_tokens);
   return hipGetLastError();
@@ -723,13 +740,13 @@ hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_
                          const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
                          int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit,
                          float* logp_sel, float* logq_sel, char* ws, const WsLayout& L,
-                         hipStream_t stream) {
+                         const CommitArgs* commit, hipStream_t stream) {
   if (s.logit_dtype == ISD_BF16)
     return launch_t<uint16_t>(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi,
                               step, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L,
-                              stream);
+                              commit, stream);
   return launch_t<float>(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi, step,
-                         accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L, stream);
+                         accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L, commit, stream);
 }
 
 }  // namespace isd

@@ -1,109 +1,15 @@
 // Appending accepted CLEAN rows to the KV pages (kv_commit) and the
-// workspace header fill (isd_workspace_init).
-//
-// One workgroup per (request, CLEAN row i).  It requests the row's key and
-// value vectors before the request's length and page id arrive, stores them
-// if i < n_commit and the pages of rows 0..i are mapped (16-byte stores into
-// the key layout, element stores into the transposed value layout), and
-// counts its arrival; the request's last arrival writes the new length, so
-// ctx_lens_out may alias ctx_lens_in.
-#include "device_common.hpp"
-#include "isd_internal.hpp"
+// workspace header fill (isd_workspace_init).  The row commit itself lives
+// in commit_row.hpp: one workgroup per (request, CLEAN row).
+#include "commit_row.hpp"
 
 namespace isd {
 namespace {
 
-__device__ __forceinline__ int v_sigma(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
-
-constexpr int kCommitThreads = 256;
-constexpr int kCommitPre = 2;   // 16-byte vectors per thread requested up front
-
-// Page id of committed row t of request r (position L + t); -1 when the
-// position is past the table, -2 when the table entry is not a pool page.
-__device__ __forceinline__ int commit_page(const int32_t* __restrict__ table, int r, int L, int t,
-                                           int max_pages, int num_pages) {
-  const int pos = L + t;
-  if (pos >= max_pages * kPage) return -1;
-  const int pid = table[size_t(r) * max_pages + pos / kPage];
-  return (pid < 0 || pid >= num_pages) ? -2 : pid;
-}
-
 template <typename T>
-__device__ __forceinline__ void commit_store(int w, int rvec, int D, int Hkv, int pid, int slot,
-                                             const u32x4& v, T* __restrict__ kp, T* __restrict__ vp) {
-  constexpr int EV = 16 / sizeof(T);
-  if (w < rvec) {
-    const int e0 = w * EV, hk = e0 / D, d0 = e0 % D;
-    T* dst = kp + ((size_t(pid) * Hkv + hk) * (D / 8) + d0 / 8) * (kPage * 8) + slot * 8 + (d0 & 7);
-    *reinterpret_cast<u32x4*>(dst) = v;
-  } else {
-    const int e0 = (w - rvec) * EV, hk = e0 / D, d0 = e0 % D;
-    T* dst = vp + ((size_t(pid) * Hkv + hk) * D + d0) * kPage + v_sigma(slot);
-    T x[EV];
-    __builtin_memcpy(x, &v, 16);
-#pragma unroll
-    for (int e = 0; e < EV; ++e) dst[e * kPage] = x[e];
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
-    const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ kp, T* __restrict__ vp,
-    const int32_t* __restrict__ table, const int32_t* ctx_in, const int32_t* __restrict__ n_commit,
-    int32_t* ctx_out, int N, int Hkv, int D, int max_pages, int num_pages, uint32_t* __restrict__ flags,
-    uint32_t* __restrict__ arrivals) {
-  constexpr int EV = 16 / sizeof(T);
+__global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitArgs c) {
   __shared__ int s_last;
-  const int i = blockIdx.x, r = blockIdx.y;
-  const int R = N - 1, Qn = 2 * N - 1;
-  const int rvec = Hkv * D / EV;                 // 16-byte vectors per key (or value) row
-  const size_t row_off = (size_t(r) * Qn + i) * Hkv * D;
-  const u32x4* ksrc = reinterpret_cast<const u32x4*>(k_new + row_off);
-  const u32x4* vsrc = reinterpret_cast<const u32x4*>(v_new + row_off);
-  u32x4 pre[kCommitPre];
-#pragma unroll
-  for (int m = 0; m < kCommitPre; ++m) {
-    const int w = threadIdx.x + m * kCommitThreads;
-    if (w < 2 * rvec) pre[m] = (w < rvec) ? ksrc[w] : vsrc[w - rvec];
-  }
-  const int cap = max_pages * kPage;
-  int L = ctx_in[r], n = n_commit[r];
-  const bool bad_n = n < 0 || n > R, bad_L = L < 0 || L > cap;
-  if (bad_n) n = n < 0 ? 0 : R;
-  if (bad_L) { L = L < 0 ? 0 : cap; n = 0; }
-  // rows 0..i must all be mapped for row i to be stored
-  bool store = i < n;
-  if (store) {
-    const int lane = threadIdx.x & 63;
-    const int pid_t = (lane <= i) ? commit_page(table, r, L, lane, max_pages, num_pages) : 0;
-    const uint64_t bad = __ballot(pid_t < 0);
-    store = (bad == 0);
-  }
-  if (store) {
-    const int pid = commit_page(table, r, L, i, max_pages, num_pages);
-    const int slot = (L + i) % kPage;
-#pragma unroll
-    for (int m = 0; m < kCommitPre; ++m) {
-      const int w = threadIdx.x + m * kCommitThreads;
-      if (w < 2 * rvec) commit_store<T>(w, rvec, D, Hkv, pid, slot, pre[m], kp, vp);
-    }
-    for (int w = threadIdx.x + kCommitPre * kCommitThreads; w < 2 * rvec; w += kCommitThreads)
-      commit_store<T>(w, rvec, D, Hkv, pid, slot, (w < rvec) ? ksrc[w] : vsrc[w - rvec], kp, vp);
-  }
-  if (!arrive_last(&arrivals[r], uint32_t(R), &s_last)) return;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int pid_t = (lane < n) ? commit_page(table, r, L, lane, max_pages, num_pages) : 0;
-    const uint64_t bad = __ballot(pid_t < 0);
-    const int nv = bad ? (__ffsll((unsigned long long)bad) - 1) : n;
-    const int first_bad = __shfl(pid_t, bad ? nv : 0);
-    if (lane == 0) {
-      if (bad_n) raise_flag(flags, ISD_FLAG_COMMIT_RANGE);
-      if (bad_L) raise_flag(flags, ISD_FLAG_CTX_RANGE);
-      if (bad) raise_flag(flags, first_bad == -1 ? ISD_FLAG_COMMIT_RANGE : ISD_FLAG_PAGE_RANGE);
-      ctx_out[r] = L + nv;
-    }
-  }
+  commit_row<T>(c, blockIdx.x, blockIdx.y, &s_last);
 }
 
 __global__ void fill_zero_u32(uint32_t* p, int n) {
@@ -113,23 +19,35 @@ __global__ void fill_zero_u32(uint32_t* p, int n) {
 
 }  // namespace
 
-hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
-                         void* v_pages, const int32_t* table, const int32_t* ctx_in,
-                         const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags,
-                         uint32_t* arrivals, hipStream_t stream) {
+CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
+                       void* v_pages, const int32_t* table, const int32_t* ctx_in,
+                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags, uint32_t* arrivals) {
+  CommitArgs c;
+  c.k_new = k_new;
+  c.v_new = v_new;
+  c.k_pages = k_pages;
+  c.v_pages = v_pages;
+  c.table = table;
+  c.ctx_in = ctx_in;
+  c.n_commit = n_commit;
+  c.ctx_out = ctx_out;
+  c.flags = flags;
+  c.arrivals = arrivals;
+  c.N = s.stride_n;
+  c.Hkv = s.n_kv_heads;
+  c.D = s.head_dim;
+  c.max_pages = s.max_pages;
+  c.num_pages = s.num_pages;
+  c.kv_bf16 = (s.kv_dtype == ISD_BF16) ? 1 : 0;
+  return c;
+}
+
+hipError_t launch_commit(const isd_shape& s, const CommitArgs& c, hipStream_t stream) {
   const dim3 grid(s.stride_n - 1, s.batch);
-  if (s.kv_dtype == ISD_BF16)
-    hipLaunchKernelGGL((kv_commit_kernel<uint16_t>), grid, dim3(kCommitThreads), 0, stream,
-                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                       static_cast<uint16_t*>(k_pages), static_cast<uint16_t*>(v_pages), table, ctx_in,
-                       n_commit, ctx_out, s.stride_n, s.n_kv_heads, s.head_dim, s.max_pages,
-                       s.num_pages, flags, arrivals);
+  if (c.kv_bf16)
+    hipLaunchKernelGGL((kv_commit_kernel<uint16_t>), grid, dim3(kCommitThreads), 0, stream, c);
   else
-    hipLaunchKernelGGL((kv_commit_kernel<float>), grid, dim3(kCommitThreads), 0, stream,
-                       static_cast<const float*>(k_new), static_cast<const float*>(v_new),
-                       static_cast<float*>(k_pages), static_cast<float*>(v_pages), table, ctx_in,
-                       n_commit, ctx_out, s.stride_n, s.n_kv_heads, s.head_dim, s.max_pages,
-                       s.num_pages, flags, arrivals);
+    hipLaunchKernelGGL((kv_commit_kernel<float>), grid, dim3(kCommitThreads), 0, stream, c);
   return hipGetLastError();
 }
 

@@ -158,7 +158,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 3; }
+int32_t isd_abi_version(void) { return 4; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {
@@ -240,8 +240,40 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
   const WsLayout L = ws_layout(*shape);
   hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
                                seed_hi, step, accept_len, out_tokens, n_out, n_commit, logp_sel,
-                               logq_sel, static_cast<char*>(workspace), L, stream);
+                               logq_sel, static_cast<char*>(workspace), L, nullptr, stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept");
+}
+
+isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const void* q_logits,
+                             const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
+                             uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
+                             int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
+                             float* logq_sel, const void* k_new, const void* v_new, void* k_pages,
+                             void* v_pages, const int32_t* page_table, const int32_t* ctx_lens_in,
+                             int32_t* ctx_lens_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  isd_status st = check_shape(shape);
+  if (st != ISD_OK) return st;
+  if (!p_logits || !q_logits || !proposals || !req_ids || !positions || !accept_len || !out_tokens ||
+      !n_out || !n_commit || !logp_sel || !logq_sel || !k_new || !v_new || !k_pages || !v_pages ||
+      !page_table || !ctx_lens_in || !ctx_lens_out)
+    return ISD_ERR_NULL;
+  if (!aligned16(p_logits) || !aligned16(q_logits) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned16(k_pages))
+    return ISD_ERR_ALIGNMENT;
+  if (shape->batch > 65535) return ISD_ERR_UNSUPPORTED;
+  if (shape->vocab > 2048 * 1024) return ISD_ERR_UNSUPPORTED;
+  st = check_ws(shape, workspace, ws_bytes);
+  if (st != ISD_OK) return st;
+  const AcceptPlan p = plan_accept(*shape);
+  const WsLayout L = ws_layout(*shape);
+  char* ws = static_cast<char*>(workspace);
+  const CommitArgs c = commit_args(*shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
+                                   ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
+                                   reinterpret_cast<uint32_t*>(ws + L.cmt_cnt));
+  hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
+                               seed_hi, step, accept_len, out_tokens, n_out, n_commit, logp_sel,
+                               logq_sel, ws, L, &c, stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept_commit");
 }
 
 isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_new, void* k_pages,
@@ -258,9 +290,10 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
   if (st != ISD_OK) return st;
   const WsLayout L = ws_layout(*shape);
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = launch_commit(*shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in,
-                               n_commit, ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
-                               reinterpret_cast<uint32_t*>(ws + L.cmt_cnt), stream);
+  const CommitArgs c = commit_args(*shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
+                                   ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
+                                   reinterpret_cast<uint32_t*>(ws + L.cmt_cnt));
+  hipError_t e = launch_commit(*shape, c, stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "kv_commit");
 }
 

@@ -98,6 +98,26 @@ AttnPlan plan_attention(const isd_shape& s);
 AcceptPlan plan_accept(const isd_shape& s);
 WsLayout ws_layout(const isd_shape& s);
 
+// Everything one KV commit reads and writes (kv_commit, and isd_accept_commit
+// whose residual launch also runs the commit's workgroups).
+struct CommitArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_pages;
+  void* v_pages;
+  const int32_t* table;
+  const int32_t* ctx_in;
+  const int32_t* n_commit;
+  int32_t* ctx_out;
+  uint32_t* flags;
+  uint32_t* arrivals;     // per request, rewound by the last arrival
+  int N, Hkv, D, max_pages, num_pages;
+  int kv_bf16;            // 1: bf16 pages, 0: fp32
+};
+CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
+                       void* v_pages, const int32_t* table, const int32_t* ctx_in,
+                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags, uint32_t* arrivals);
+
 // Launchers (return the first HIP error, hipSuccess otherwise).
 hipError_t launch_attention(const isd_shape& s, const AttnPlan& p, const void* q,
                             const void* k_new, const void* v_new, const void* k_pages,
@@ -110,12 +130,9 @@ hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_
                          const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
                          uint32_t step, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
                          int32_t* n_commit, float* logp_sel, float* logq_sel, char* ws,
-                         const WsLayout& L, hipStream_t stream);
+                         const WsLayout& L, const CommitArgs* commit, hipStream_t stream);
 
-hipError_t launch_commit(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
-                         void* v_pages, const int32_t* table, const int32_t* ctx_in,
-                         const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags,
-                         uint32_t* arrivals, hipStream_t stream);
+hipError_t launch_commit(const isd_shape& s, const CommitArgs& c, hipStream_t stream);
 
 hipError_t launch_propose(const isd_shape& s, const void* mask_logits, const int32_t* req_ids,
                           const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,

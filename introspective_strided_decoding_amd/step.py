@@ -123,6 +123,15 @@ class DeviceStep:
                        self.page_table, self.ctx_lens, self.n_commit, self.ctx_lens_out,
                        self.workspace, stream=stream)
 
+    def accept_commit(self, stream=None, step: Optional[int] = None, seed=None):
+        """accept, then commit of the accepted rows, in one library call."""
+        _lib.isd_accept_commit(self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
+                               self.positions, self.seed if seed is None else seed,
+                               self.step if step is None else step, self.accept_len, self.out_tokens,
+                               self.n_out, self.n_commit, self.logp_sel, self.logq_sel, self.k_new,
+                               self.v_new, self.k_pages, self.v_pages, self.page_table, self.ctx_lens,
+                               self.ctx_lens_out, self.workspace, stream=stream)
+
     def propose(self, stream=None, mode: int = _lib.PROPOSE_SAMPLE, step: Optional[int] = None, seed=None):
         _lib.isd_propose(self.shape, self.mask_logits, self.req_ids, self.positions,
                          self.seed if seed is None else seed, self.step if step is None else step,
@@ -176,10 +185,9 @@ class DeviceStep:
         return graph
 
     def run(self, stream=None):
-        """One ISD step: attention -> accept -> commit (-> LoRA delta) (-> proposals)."""
+        """One ISD step: attention -> accept + commit (-> LoRA delta) (-> proposals)."""
         self.attention(stream)
-        self.accept(stream)
-        self.commit(stream)
+        self.accept_commit(stream)
         if self.lora is not None:
             self.lora_delta(stream)
         if self.mask_logits is not None:

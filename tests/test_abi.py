@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 3
+    assert LIB.isd_abi_version() == 4
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"
@@ -105,6 +105,21 @@ def test_accept_and_commit_validation():
     bad = list(cargs)
     bad[-2] = 0
     assert LIB.kv_commit(ctypes.byref(s.c()), *bad) == 4
+    # isd_accept_commit: the accept arguments, then k_new .. ctx_lens_out, workspace, stream
+    fargs = [FAKE] * 5 + [1, 2, 3] + [FAKE] * 6 + [FAKE] * 7 + [FAKE, n, None]
+    assert len(fargs) == 24
+    for i in (2, 14, 18, 20):       # proposals, k_new, page_table, ctx_lens_out
+        bad = list(fargs)
+        bad[i] = None
+        assert LIB.isd_accept_commit(ctypes.byref(s.c()), *bad) == 1, i
+    for i in (0, 14, 15, 16):       # p_logits, k_new, v_new, k_pages
+        bad = list(fargs)
+        bad[i] = MISALIGNED
+        assert LIB.isd_accept_commit(ctypes.byref(s.c()), *bad) == 7, i
+    bad = list(fargs)
+    bad[-2] = 8
+    assert LIB.isd_accept_commit(ctypes.byref(s.c()), *bad) == 4
+    assert LIB.isd_accept_commit(None, *fargs) == 1
 
 
 def test_propose_validation():

@@ -82,3 +82,44 @@ def test_commit_range_flags():
     assert flags & 8 and flags & 2
     lens = st.ctx_lens_out.cpu().numpy()
     assert lens[0] == 40 + 3 and lens[1] == 41 and lens[2] == 32
+
+
+def _bits(t):
+    return t.contiguous().view(torch.uint8).cpu()
+
+
+@pytest.mark.parametrize("name,over,in_place", [
+    ("b8_ctx2k", dict(batch=6, ctx=30, vocab=3000), False),
+    ("b8_ctx2k", dict(batch=5, ctx=14, vocab=4099, stride_n=5), True),
+    ("tiny_fp32", dict(batch=4, ctx=13, vocab=1000), True),
+    ("c64_ragged", dict(batch=7, ctx_range=(1, 100), vocab=2048), True),
+])
+def test_accept_commit_equals_accept_then_commit(name, over, in_place):
+    """isd_accept_commit leaves every output, the pools and the lengths exactly as
+    isd_accept followed by kv_commit does, step after step, and the pools are the
+    oracle's commit of the accepted counts."""
+    cfg = get_config(name, **over)
+    steps = 4
+    wl = make_workload(cfg, seed=31, extra_tokens=steps * (cfg.stride_n - 1))
+    a = device_step(wl, commit_in_place=in_place)
+    b = device_step(wl, commit_in_place=in_place)
+    k_ref, v_ref, lens = wl.k_pool, wl.v_pool, wl.ctx_lens.copy()
+    for step in range(steps):
+        a.accept(step=step)
+        a.commit()
+        b.accept_commit(step=step)
+        torch.cuda.synchronize()
+        for f in ("accept_len", "out_tokens", "n_out", "n_commit", "logp_sel", "logq_sel", "ctx_lens_out"):
+            assert torch.equal(_bits(getattr(a, f)), _bits(getattr(b, f))), (step, f)
+        assert torch.equal(_bits(a.k_pages), _bits(b.k_pages)), step
+        assert torch.equal(_bits(a.v_pages), _bits(b.v_pages)), step
+        k_ref, v_ref, out_lens = oracle_commit(k_ref, v_ref, wl.page_table, lens, wl.k_new, wl.v_new,
+                                               b.n_commit.cpu().numpy(), cfg.page_size)
+        assert np.array_equal(b.ctx_lens_out.cpu().numpy(), out_lens), step
+        if in_place:
+            lens = out_lens
+    k_got, v_got = _unpacked(b)
+    assert np.array_equal(k_got, k_ref)
+    assert np.array_equal(v_got, v_ref)
+    from introspective_strided_decoding_amd import isd_read_flags
+    assert isd_read_flags(a.workspace) == 0 and isd_read_flags(b.workspace) == 0
