@@ -151,12 +151,37 @@ class DeviceStep:
                               e["mode"], self.proposals, self.positions, e["tokens"], e["forwards"],
                               stream=stream)
 
-    def loop_forward(self, step: int, attention: bool = True, stream=None):
-        """One forward of the decoding loop: attention, accept, proposals, bookkeeping, commit."""
+    def _side_stream(self) -> torch.cuda.Stream:
+        s = self.extra.get("side_stream")
+        if s is None:
+            s = torch.cuda.Stream(device=self.proposals.device)     # default priority
+            self.extra["side_stream"] = s
+        return s
+
+    def _accept_and_propose(self, accept_fn, stream, step: Optional[int], overlap: bool):
+        """The accept chain on ``stream`` and the proposals on a second stream, joined after.
+
+        Both read this forward's logits and neither writes what the other reads
+        (their workspace regions are disjoint), so they may run side by side; the
+        proposals still start only after everything enqueued before on ``stream``.
+        """
+        if overlap and (stream is None or isinstance(stream, torch.cuda.Stream)):
+            main = torch.cuda.current_stream() if stream is None else stream
+            side = self._side_stream()
+            side.wait_stream(main)
+            accept_fn(main, step)
+            self.propose(side, step=step)
+            main.wait_stream(side)
+        else:
+            accept_fn(stream, step)
+            self.propose(stream, step=step)
+
+    def loop_forward(self, step: int, attention: bool = True, stream=None, overlap: bool = True):
+        """One forward of the decoding loop: attention, accept and proposals (side by side
+        unless ``overlap`` is False), bookkeeping, commit."""
         if attention:
             self.attention(stream)
-        self.accept(stream, step=step)
-        self.propose(stream, step=step)
+        self._accept_and_propose(lambda s, t: self.accept(s, step=t), stream, step, overlap)
         self.loop_advance(stream)
         if attention:
             self.commit(stream)
@@ -184,11 +209,13 @@ class DeviceStep:
             self.run()
         return graph
 
-    def run(self, stream=None):
-        """One ISD step: attention -> accept + commit (-> LoRA delta) (-> proposals)."""
+    def run(self, stream=None, overlap: bool = True):
+        """One ISD step: attention -> accept + commit (-> LoRA delta); with MASK logits the
+        next proposals run beside the accept chain (``overlap``) or after it."""
         self.attention(stream)
-        self.accept_commit(stream)
+        if self.mask_logits is not None:
+            self._accept_and_propose(lambda s, t: self.accept_commit(s, step=t), stream, None, overlap)
+        else:
+            self.accept_commit(stream)
         if self.lora is not None:
             self.lora_delta(stream)
-        if self.mask_logits is not None:
-            self.propose(stream)

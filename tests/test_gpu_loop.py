@@ -150,3 +150,31 @@ def test_loop_reproduces_tpf_column(n):
     # the loop ends mid-cycle for some requests: allow 1/T of bias
     assert abs(tpf_hat - closed) < 4 * se + 1.0 / T, (n, tpf_hat, closed, se)
     assert abs(tpf_hat - table[n]) < 4 * se + 1.0 / T + 0.005, (n, tpf_hat, table[n], se)
+
+
+def test_loop_with_proposals_beside_accept_matches_sequential():
+    """Proposals on a second stream beside the accept chain give the same forwards,
+    bit for bit, as the calls issued one after another."""
+    T, K = 6, 3
+    cfg = get_config("b8_ctx2k", batch=10, ctx=40, vocab=3000, stride_n=4)
+    wl = make_workload(cfg, seed=62, with_mask_logits=True, extra_tokens=T * (cfg.stride_n - 1))
+    pool = _pool(cfg, K, 310, "batch")
+    a = device_step(wl, commit_in_place=True)
+    b = device_step(wl, commit_in_place=True)
+    for st in (a, b):
+        st.loop_start()
+    names = ("accept_len", "n_out", "next_proposals", "n_commit", "proposals", "positions", "ctx_lens",
+             "out_tokens", "k_pages", "v_pages")
+    for t in range(T):
+        p, q = (wl.p_logits, wl.q_logits) if t == 0 else pool[(t - 1) % K][:2]
+        for st in (a, b):
+            st.p_logits.copy_(_dev(p, st.p_logits))
+            st.q_logits.copy_(_dev(q, st.q_logits))
+            st.mask_logits.copy_(_dev(pool[t % K][2], st.mask_logits))
+        a.loop_forward(step=t, overlap=True)
+        b.loop_forward(step=t, overlap=False)
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(a, n).view(torch.uint8), getattr(b, n).view(torch.uint8)), (t, n)
+        for n in ("mode", "tokens", "forwards"):
+            assert torch.equal(a.extra[n], b.extra[n]), (t, n)
