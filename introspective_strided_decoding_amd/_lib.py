@@ -131,6 +131,65 @@ def _tdtype(code: int):
     return torch.bfloat16 if code == ISD_BF16 else torch.float32
 
 
+class _Captured(Exception):
+    def __init__(self, name, args):
+        super().__init__(name)
+        self.name, self.args = name, args
+
+
+_capturing = False
+
+
+def _call(name: str, *args) -> None:
+    if _capturing:
+        raise _Captured(name, args)
+    _check(name, getattr(LIB, name)(*args))
+
+
+# argument index of seed_lo (seed_hi and step follow) in the calls that draw
+_DRAW_POS = {"isd_accept": 6, "isd_accept_commit": 6, "isd_propose": 4}
+_M64 = 2**64 - 1
+
+
+class Prepared:
+    """A library call checked and marshalled once: launching it again re-reads only
+    the stream and, for the calls that draw, the step counter and the seed."""
+
+    __slots__ = ("name", "lib", "fn", "args", "draw")
+
+    def __init__(self, name: str, args):
+        self.name, self.lib, self.fn = name, LIB, getattr(LIB, name)
+        self.args = list(args)
+        self.draw = _DRAW_POS.get(name)
+
+    def __call__(self, stream=None, step: Optional[int] = None, seed=None) -> None:
+        a = self.args
+        a[-1] = _stream(stream)
+        d = self.draw
+        if d is not None:
+            if seed is not None:
+                a[d], a[d + 1] = int(seed[0]) & _M64, int(seed[1]) & _M64
+            if step is not None:
+                a[d + 2] = int(step) & 0xFFFFFFFF
+        status = self.fn(*a)
+        if status != 0:
+            _check(self.name, status)
+
+
+def prepare(wrapper, *args, **kw) -> Prepared:
+    """Validate and marshal ``wrapper(*args, **kw)`` (one of the call wrappers of this
+    module) without launching it; the result launches it."""
+    global _capturing
+    _capturing = True
+    try:
+        wrapper(*args, **kw)
+    except _Captured as c:
+        return Prepared(c.name, c.args)
+    finally:
+        _capturing = False
+    raise RuntimeError(f"{getattr(wrapper, '__name__', wrapper)} is not a library call wrapper")
+
+
 def _check(fn: str, status: int):
     if status != 0:
         detail = LIB.isd_last_error().decode() if status == 6 else LIB.isd_status_string(status).decode()
@@ -152,15 +211,14 @@ def new_workspace(shape: Shape, device="cuda", stream=None) -> torch.Tensor:
 
 
 def isd_workspace_init(shape: Shape, workspace: torch.Tensor, stream=None) -> None:
-    _check("isd_workspace_init", LIB.isd_workspace_init(
+    _call("isd_workspace_init",
         ctypes.byref(shape.c()), _ptr(workspace, "workspace", torch.uint8), workspace.numel(),
-        _stream(stream)))
+        _stream(stream))
 
 
 def isd_read_flags(workspace: torch.Tensor, stream=None) -> int:
     out = ctypes.c_uint32(0)
-    _check("isd_read_flags", LIB.isd_read_flags(_ptr(workspace, "workspace", torch.uint8),
-                                                ctypes.byref(out), _stream(stream)))
+    _call("isd_read_flags", _ptr(workspace, "workspace", torch.uint8), ctypes.byref(out), _stream(stream))
     return int(out.value)
 
 
@@ -169,13 +227,13 @@ def isd_attention(shape: Shape, q, k_new, v_new, k_pages, v_pages, page_table, c
     B, Q, Hq, Hkv, D = shape.batch, shape.q_rows, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     dt = _tdtype(shape.kv_dtype)
     pool = shape.num_pages * Hkv * shape.page_size * D
-    _check("isd_attention", LIB.isd_attention(
+    _call("isd_attention",
         ctypes.byref(shape.c()), _ptr(q, "q", dt, B * Q * Hq * D), _ptr(k_new, "k_new", dt, B * Q * Hkv * D),
         _ptr(v_new, "v_new", dt, B * Q * Hkv * D), _ptr(k_pages, "k_pages", dt, pool),
         _ptr(v_pages, "v_pages", dt, pool),
         _ptr(page_table, "page_table", torch.int32, B * shape.max_pages),
         _ptr(ctx_lens, "ctx_lens", torch.int32, B), float(scale), _ptr(out, "out", dt, B * Q * Hq * D),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 
 def isd_accept(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
@@ -184,7 +242,7 @@ def isd_accept(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, 
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     dt = _tdtype(shape.logit_dtype)
     i32 = torch.int32
-    _check("isd_accept", LIB.isd_accept(
+    _call("isd_accept",
         ctypes.byref(shape.c()), _ptr(p_logits, "p_logits", dt, B * (N - 1) * V),
         _ptr(q_logits, "q_logits", dt, B * (N - 1) * V), _ptr(proposals, "proposals", i32, B * N),
         _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
@@ -193,7 +251,7 @@ def isd_accept(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, 
         _ptr(n_out, "n_out", i32, B), _ptr(n_commit, "n_commit", i32, B),
         _ptr(logp_sel, "logp_sel", torch.float32, B * (N - 1)),
         _ptr(logq_sel, "logq_sel", torch.float32, B * (N - 1)),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 
 def kv_commit(shape: Shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
@@ -201,14 +259,14 @@ def kv_commit(shape: Shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens
     B, Q, Hkv, D = shape.batch, shape.q_rows, shape.n_kv_heads, shape.head_dim
     dt = _tdtype(shape.kv_dtype)
     pool = shape.num_pages * Hkv * shape.page_size * D
-    _check("kv_commit", LIB.kv_commit(
+    _call("kv_commit",
         ctypes.byref(shape.c()), _ptr(k_new, "k_new", dt, B * Q * Hkv * D),
         _ptr(v_new, "v_new", dt, B * Q * Hkv * D), _ptr(k_pages, "k_pages", dt, pool),
         _ptr(v_pages, "v_pages", dt, pool),
         _ptr(page_table, "page_table", torch.int32, B * shape.max_pages),
         _ptr(ctx_lens_in, "ctx_lens_in", torch.int32, B), _ptr(n_commit, "n_commit", torch.int32, B),
         _ptr(ctx_lens_out, "ctx_lens_out", torch.int32, B),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 
 def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
@@ -220,7 +278,7 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
     dt, kt = _tdtype(shape.logit_dtype), _tdtype(shape.kv_dtype)
     pool = shape.num_pages * Hkv * shape.page_size * D
     i32 = torch.int32
-    _check("isd_accept_commit", LIB.isd_accept_commit(
+    _call("isd_accept_commit",
         ctypes.byref(shape.c()), _ptr(p_logits, "p_logits", dt, B * (N - 1) * V),
         _ptr(q_logits, "q_logits", dt, B * (N - 1) * V), _ptr(proposals, "proposals", i32, B * N),
         _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
@@ -233,7 +291,7 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
         _ptr(k_pages, "k_pages", kt, pool), _ptr(v_pages, "v_pages", kt, pool),
         _ptr(page_table, "page_table", i32, B * shape.max_pages),
         _ptr(ctx_lens_in, "ctx_lens_in", i32, B), _ptr(ctx_lens_out, "ctx_lens_out", i32, B),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 
 def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, mode: int,
@@ -241,25 +299,25 @@ def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, 
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     i32 = torch.int32
     sample = mode == PROPOSE_SAMPLE
-    _check("isd_propose", LIB.isd_propose(
+    _call("isd_propose",
         ctypes.byref(shape.c()), _ptr(mask_logits, "mask_logits", _tdtype(shape.logit_dtype), B * N * V),
         _ptr(req_ids, "req_ids", i32, B) if sample or req_ids is not None else None,
         _ptr(positions, "positions", i32, B) if sample or positions is not None else None,
         int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(mode),
         _ptr(proposals, "proposals", i32, B * N),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 
 def isd_loop_advance(shape: Shape, accept_len, n_out, next_proposals, n_commit, mode, proposals,
                      positions, tokens, forwards, stream=None) -> None:
     B, N = shape.batch, shape.stride_n
     i32, i64 = torch.int32, torch.int64
-    _check("isd_loop_advance", LIB.isd_loop_advance(
+    _call("isd_loop_advance",
         ctypes.byref(shape.c()), _ptr(accept_len, "accept_len", i32, B), _ptr(n_out, "n_out", i32, B),
         _ptr(next_proposals, "next_proposals", i32, B * N), _ptr(n_commit, "n_commit", i32, B),
         _ptr(mode, "mode", i32, B), _ptr(proposals, "proposals", i32, B * N),
         _ptr(positions, "positions", i32, B), _ptr(tokens, "tokens", i64, B),
-        _ptr(forwards, "forwards", i64, B), _stream(stream)))
+        _ptr(forwards, "forwards", i64, B), _stream(stream))
 
 
 def isd_lora_workspace_bytes(n_mask: int, d_in: int, rank: int) -> int:
@@ -272,8 +330,8 @@ def isd_lora_delta(X, A_t, B_t, mask_rows, Y, workspace, scale: float = 1.0, str
     rank = A_t.shape[0]
     d_out = B_t.shape[0]
     bf = torch.bfloat16
-    _check("isd_lora_delta", LIB.isd_lora_delta(
+    _call("isd_lora_delta",
         rows, d_in, d_out, rank, _ptr(X, "X", bf), _ptr(A_t, "A_t", bf, rank * d_in),
         _ptr(B_t, "B_t", bf, d_out * rank), _ptr(mask_rows, "mask_rows", torch.int32), mask_rows.numel(),
         float(scale), _ptr(Y, "Y", bf, rows * d_out), _ptr(workspace, "workspace", torch.uint8),
-        workspace.numel(), _stream(stream)))
+        workspace.numel(), _stream(stream))

@@ -107,55 +107,72 @@ class DeviceStep:
             st.lora["ws"] = torch.zeros(max(256, nbytes), dtype=torch.uint8, device=device)
         return st
 
+    def __setattr__(self, name, value):
+        # a buffer replaced by another drops the calls marshalled with the old one
+        object.__setattr__(self, name, value)
+        self.__dict__.pop("_calls", None)
+
+    def _call(self, key, build):
+        """The library call ``key``, checked and marshalled on first use (``build``)."""
+        calls = self.__dict__.setdefault("_calls", {})
+        c = calls.get(key)
+        if c is None or c.lib is not _lib.LIB:
+            c = calls[key] = build()
+        return c
+
     def attention(self, stream=None):
-        _lib.isd_attention(self.shape, self.q, self.k_new, self.v_new, self.k_pages, self.v_pages,
-                           self.page_table, self.ctx_lens, self.out, self.workspace, stream=stream)
+        self._call("attention", lambda: _lib.prepare(
+            _lib.isd_attention, self.shape, self.q, self.k_new, self.v_new, self.k_pages, self.v_pages,
+            self.page_table, self.ctx_lens, self.out, self.workspace))(stream)
 
     def accept(self, stream=None, step: Optional[int] = None, seed=None):
-        _lib.isd_accept(self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
-                        self.positions, self.seed if seed is None else seed,
-                        self.step if step is None else step, self.accept_len, self.out_tokens,
-                        self.n_out, self.n_commit, self.logp_sel, self.logq_sel, self.workspace,
-                        stream=stream)
+        self._call("accept", lambda: _lib.prepare(
+            _lib.isd_accept, self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
+            self.positions, self.seed, self.step, self.accept_len, self.out_tokens, self.n_out, self.n_commit,
+            self.logp_sel, self.logq_sel, self.workspace))(
+            stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def commit(self, stream=None):
-        _lib.kv_commit(self.shape, self.k_new, self.v_new, self.k_pages, self.v_pages,
-                       self.page_table, self.ctx_lens, self.n_commit, self.ctx_lens_out,
-                       self.workspace, stream=stream)
+        self._call("commit", lambda: _lib.prepare(
+            _lib.kv_commit, self.shape, self.k_new, self.v_new, self.k_pages, self.v_pages, self.page_table,
+            self.ctx_lens, self.n_commit, self.ctx_lens_out, self.workspace))(stream)
 
     def accept_commit(self, stream=None, step: Optional[int] = None, seed=None):
         """accept, then commit of the accepted rows, in one library call."""
-        _lib.isd_accept_commit(self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
-                               self.positions, self.seed if seed is None else seed,
-                               self.step if step is None else step, self.accept_len, self.out_tokens,
-                               self.n_out, self.n_commit, self.logp_sel, self.logq_sel, self.k_new,
-                               self.v_new, self.k_pages, self.v_pages, self.page_table, self.ctx_lens,
-                               self.ctx_lens_out, self.workspace, stream=stream)
+        self._call("accept_commit", lambda: _lib.prepare(
+            _lib.isd_accept_commit, self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
+            self.positions, self.seed, self.step, self.accept_len, self.out_tokens, self.n_out, self.n_commit,
+            self.logp_sel, self.logq_sel, self.k_new, self.v_new, self.k_pages, self.v_pages, self.page_table,
+            self.ctx_lens, self.ctx_lens_out, self.workspace))(
+            stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def propose(self, stream=None, mode: int = _lib.PROPOSE_SAMPLE, step: Optional[int] = None, seed=None):
-        _lib.isd_propose(self.shape, self.mask_logits, self.req_ids, self.positions,
-                         self.seed if seed is None else seed, self.step if step is None else step,
-                         mode, self.next_proposals, self.workspace, stream=stream)
+        self._call(("propose", mode), lambda: _lib.prepare(
+            _lib.isd_propose, self.shape, self.mask_logits, self.req_ids, self.positions, self.seed,
+            self.step, mode, self.next_proposals, self.workspace))(
+            stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def loop_start(self):
         """Device state of the multi-step loop: every request starts verifying its proposals."""
         B = self.shape.batch
         dev = self.proposals.device
+        self.__dict__.get("_calls", {}).pop("loop_advance", None)    # marshalled with the old state
         self.extra["mode"] = torch.zeros(B, dtype=torch.int32, device=dev)
         self.extra["tokens"] = torch.zeros(B, dtype=torch.int64, device=dev)
         self.extra["forwards"] = torch.zeros(B, dtype=torch.int64, device=dev)
 
     def loop_advance(self, stream=None):
         e = self.extra
-        _lib.isd_loop_advance(self.shape, self.accept_len, self.n_out, self.next_proposals, self.n_commit,
-                              e["mode"], self.proposals, self.positions, e["tokens"], e["forwards"],
-                              stream=stream)
+        self._call("loop_advance", lambda: _lib.prepare(
+            _lib.isd_loop_advance, self.shape, self.accept_len, self.n_out, self.next_proposals, self.n_commit,
+            e["mode"], self.proposals, self.positions, e["tokens"], e["forwards"]))(stream)
 
-    def _side_stream(self) -> torch.cuda.Stream:
+    def _side_stream(self):
+        """A second stream (default priority) and the two events of a fork and a join."""
         s = self.extra.get("side_stream")
         if s is None:
-            s = torch.cuda.Stream(device=self.proposals.device)     # default priority
-            self.extra["side_stream"] = s
+            dev = self.proposals.device
+            s = self.extra["side_stream"] = (torch.cuda.Stream(device=dev), torch.cuda.Event(), torch.cuda.Event())
         return s
 
     def _accept_and_propose(self, accept_fn, stream, step: Optional[int], overlap: bool):
@@ -167,11 +184,13 @@ class DeviceStep:
         """
         if overlap and (stream is None or isinstance(stream, torch.cuda.Stream)):
             main = torch.cuda.current_stream() if stream is None else stream
-            side = self._side_stream()
-            side.wait_stream(main)
+            side, fork, join = self._side_stream()
+            fork.record(main)
+            side.wait_event(fork)
             accept_fn(main, step)
             self.propose(side, step=step)
-            main.wait_stream(side)
+            join.record(side)
+            main.wait_event(join)
         else:
             accept_fn(stream, step)
             self.propose(stream, step=step)
