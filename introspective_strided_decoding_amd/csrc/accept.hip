@@ -326,9 +326,7 @@ __device__ __forceinline__ double block_sum_d(double x, double* sm) {
 template <int K>
 __device__ __forceinline__ void block_sum_dk(double* x, double (*sm)[K]) {
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1)
-#pragma unroll
-    for (int i = 0; i < K; ++i) x[i] += __shfl_xor(x[i], m);
+  for (int i = 0; i < K; ++i) x[i] = wave_sum_d(x[i]);
   const int wave = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0)
@@ -512,19 +510,6 @@ __device__ __forceinline__ void resid_values(const float* xp, const float* xq, c
     rv[i] = fmax(0.0, p - exp_shift(xq[i], st.max_q, tab64) * iq);
     pv[i] = p;
   }
-}
-
-// wave-wide exclusive prefix of one double per lane
-__device__ __forceinline__ double wave_exclusive_d(double x, double& total) {
-  const int lane = threadIdx.x & 63;
-  double incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  total = __shfl(incl, 63);
-  return incl - x;
 }
 
 // One workgroup per listed request: exact shard masses, then the inverse-CDF

@@ -38,26 +38,121 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16_bits(v); }
 
-// Wave-wide reductions (all 64 lanes receive the result).
+// Lane exchange by DPP (a VALU operand modifier of the gfx9 encoding: no LDS
+// crossbar trip).  Lanes whose row is masked off, or whose source lane lies
+// outside its row, read 0.
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;   // row_shr:n
+constexpr int kMirror = 0x140;      // row_mirror: lane i of a 16-lane row reads lane 15 - i
+constexpr int kHalfMirror = 0x141;  // row_half_mirror: within 8 lanes, 7 - i
+constexpr int kBcast15 = 0x142;     // row_bcast:15: lane 15 of each row into the next row
+constexpr int kBcast31 = 0x143;     // row_bcast:31: lane 31 into rows 2 and 3
+}  // namespace dpp
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, ROWS, 0xF, true));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(x)));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint64_t lo = dpp_u32<CTRL, ROWS>(uint32_t(u)), hi = dpp_u32<CTRL, ROWS>(uint32_t(u >> 32));
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+__device__ __forceinline__ double readlane_d(double x, int lane) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), lane));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), lane));
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+
+// Wave-wide reduction with an associative, commutative `op` (all 64 lanes
+// receive the result): sums within each 16-lane row by quad and mirror
+// exchanges, rows combined into lane 63 by the two row broadcasts, then
+// read from lane 63 (rows a broadcast skips keep their value).
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op) {
+  if constexpr (sizeof(T) == 8) {
+    x = op(x, dpp_d<dpp::kQuadXor1>(x));
+    x = op(x, dpp_d<dpp::kQuadXor2>(x));
+    x = op(x, dpp_d<dpp::kHalfMirror>(x));
+    x = op(x, dpp_d<dpp::kMirror>(x));
+    const T r1 = dpp_d<dpp::kBcast15, 0xA>(x);
+    x = ((threadIdx.x & 16) ? op(x, r1) : x);
+    const T r2 = dpp_d<dpp::kBcast31, 0xC>(x);
+    x = ((threadIdx.x & 32) ? op(x, r2) : x);
+    return readlane_d(x, kWave - 1);
+  } else {
+    x = op(x, dpp_f<dpp::kQuadXor1>(x));
+    x = op(x, dpp_f<dpp::kQuadXor2>(x));
+    x = op(x, dpp_f<dpp::kHalfMirror>(x));
+    x = op(x, dpp_f<dpp::kMirror>(x));
+    const T r1 = dpp_f<dpp::kBcast15, 0xA>(x);
+    x = ((threadIdx.x & 16) ? op(x, r1) : x);
+    const T r2 = dpp_f<dpp::kBcast31, 0xC>(x);
+    x = ((threadIdx.x & 32) ? op(x, r2) : x);
+    return readlane_f(x, kWave - 1);
+  }
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+  return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
-  return x;
+  return wave_reduce(x, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ double wave_max_d(double x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x = fmax(x, __shfl_xor(x, m));
-  return x;
+  return wave_reduce(x, [](double a, double b) { return fmax(a, b); });
 }
 __device__ __forceinline__ double wave_sum_d(double x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
-  return x;
+  return wave_reduce(x, [](double a, double b) { return a + b; });
+}
+
+// (max, first index) over the wave: the larger value wins, ties go to the
+// smaller index (INT_MAX marks "no entry").  Same exchange pattern.
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+  auto take = [&](float om, int oi) {
+    if (om > m || (om == m && oi < i)) { m = om; i = oi; }
+  };
+  take(dpp_f<dpp::kQuadXor1>(m), int(dpp_u32<dpp::kQuadXor1>(uint32_t(i))));
+  take(dpp_f<dpp::kQuadXor2>(m), int(dpp_u32<dpp::kQuadXor2>(uint32_t(i))));
+  take(dpp_f<dpp::kHalfMirror>(m), int(dpp_u32<dpp::kHalfMirror>(uint32_t(i))));
+  take(dpp_f<dpp::kMirror>(m), int(dpp_u32<dpp::kMirror>(uint32_t(i))));
+  {
+    const float om = dpp_f<dpp::kBcast15, 0xA>(m);
+    const int oi = int(dpp_u32<dpp::kBcast15, 0xA>(uint32_t(i)));
+    if (threadIdx.x & 16) take(om, oi);
+  }
+  {
+    const float om = dpp_f<dpp::kBcast31, 0xC>(m);
+    const int oi = int(dpp_u32<dpp::kBcast31, 0xC>(uint32_t(i)));
+    if (threadIdx.x & 32) take(om, oi);
+  }
+  m = readlane_f(m, kWave - 1);
+  i = __builtin_amdgcn_readlane(i, kWave - 1);
+}
+
+// Wave-wide inclusive prefix sum in lane order: a Hillis-Steele scan inside
+// each 16-lane row by row shifts, then the row totals carried forward by the
+// two row broadcasts.  Returns x's exclusive prefix; `total` = the sum.
+__device__ __forceinline__ double wave_exclusive_d(double x, double& total) {
+  double incl = x;
+  incl += dpp_d<dpp::kShr1>(incl);
+  incl += dpp_d<dpp::kShr2>(incl);
+  incl += dpp_d<dpp::kShr4>(incl);
+  incl += dpp_d<dpp::kShr8>(incl);
+  incl += dpp_d<dpp::kBcast15, 0xA>(incl);
+  incl += dpp_d<dpp::kBcast31, 0xC>(incl);
+  total = readlane_d(incl, kWave - 1);
+  return incl - x;
 }
 
 // Cross-workgroup hand-off without cache flushes.  Data one workgroup

@@ -82,12 +82,7 @@ __global__ __launch_bounds__(kPThreads) void prop_partial(const T* __restrict__ 
   if (mx == -INFINITY) ix = INT_MAX;
   // workgroup max, ties to the smallest index
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const float om = __shfl_xor(mx, m);
-    const int oi = __shfl_xor(ix, m);
-    if (om > mx || (om == mx && oi < ix)) { mx = om; ix = oi; }
-  }
+  wave_argmax(mx, ix);
   __shared__ float smx[kPThreads / 64];
   __shared__ int six[kPThreads / 64];
   __shared__ double ssum[kPThreads / 64];
@@ -123,18 +118,6 @@ __global__ __launch_bounds__(kPThreads) void prop_partial(const T* __restrict__ 
     p.idx = I;
     part[row * shards + sh] = p;
   }
-}
-
-__device__ __forceinline__ double wave_exclusive_d(double x, double& total) {
-  const int lane = threadIdx.x & 63;
-  double incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  total = __shfl(incl, 63);
-  return incl - x;
 }
 
 template <typename T>
@@ -179,12 +162,7 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
     }
     float M = mx;
     int I = ix;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const float om = __shfl_xor(M, m);
-      const int oi = __shfl_xor(I, m);
-      if (om > M || (om == M && oi < I)) { M = om; I = oi; }
-    }
+    wave_argmax(M, I);
     if (!sample) {
       if (lane == 0) out[row] = (I == INT_MAX) ? 0 : I;
     } else {
