@@ -86,7 +86,8 @@ typedef enum isd_dtype {
 /*
  * Sizes of one step.
  *   Q = 2 * stride_n - 1 query rows per request; G = n_q_heads / n_kv_heads.
- *   Supported: 1 <= batch <= 65535, stride_n in [2, 32], head_dim in {64, 128},
+ *   Supported: 1 <= batch <= 65535, stride_n in [2, 16] (Q <= 31: the stride
+ *   block is one 32-token attention tile), head_dim in {64, 128},
  *   page_size == 16,
  *   G * Q <= 64 (query rows per KV head), n_q_heads % n_kv_heads == 0.
  *   max_ctx is a hint (an upper bound of the context lengths, used to split

@@ -271,6 +271,40 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int rk = r * Hkv + hk;
   const int row0 = b * COLS;                    // first query row of this workgroup
   const int rows_b = min(COLS, rows - row0);    // query rows of this workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int col_l = lane & 31;
+  // split 0's wave 0 also takes the stride's own causal block as one extra tile
+  const bool stride_tile = (split == 0) && (wave == 0);
+  constexpr int CH = D / 8;   // 16-byte chunks per row
+
+  // Requested first, ahead of the context pages (which would otherwise queue
+  // in front of them): this thread's Q cells, and for the stride wave the
+  // first 32 key rows of the stride block and its first value-row chunks.
+  // Indices are clamped so every load is unconditional.
+  constexpr int QC = (CH * COLS + 64 * W - 1) / (64 * W);
+  u32x4 qc[QC];
+#pragma unroll
+  for (int j = 0; j < QC; ++j) {
+    const int idx = min(int(threadIdx.x) + j * 64 * W, CH * COLS - 1);
+    const int ch = idx / COLS, c = min(idx % COLS, rows_b - 1);
+    const int g = (row0 + c) / Qn, i = (row0 + c) % Qn;
+    qc[j] = *reinterpret_cast<const u32x4*>(q + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D + ch * 8);
+  }
+  constexpr int kVnEarly = 4;   // value-row chunks per lane requested early (Qn * CH <= 256)
+  u32x4 sk[KS], vn[kVnEarly];
+  if (stride_tile) {
+    const int tic = min(lane & 31, Qn - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sk[s] = *reinterpret_cast<const u32x4*>(k_new + ((size_t(r) * Qn + tic) * Hkv + hk) * D + (2 * s + h) * 8);
+#pragma unroll
+    for (int j = 0; j < kVnEarly; ++j) {
+      const int c = min(lane + 64 * j, Qn * CH - 1);
+      vn[j] = *reinterpret_cast<const u32x4*>(v_new + ((size_t(r) * Qn + c / CH) * Hkv + hk) * D + (c % CH) * 8);
+    }
+  }
   const int L = clamp_ctx(ctx_lens[r], max_pages, flags);
   const int n_tiles = (L + kTileTokens - 1) / kTileTokens;
   const int active = active_splits(n_tiles, n_splits, tps);
@@ -278,13 +312,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   int t0, t1;
   split_range(n_tiles, split, n_splits, tps, t0, t1);
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int h = lane >> 5;
-  const int col_l = lane & 31;
   const int32_t* trow = table + size_t(r) * max_pages;
-  // split 0's wave 0 also takes the stride's own causal block as one extra tile
-  const bool stride_tile = (split == 0) && (wave == 0);
 
   // context tiles of this wave: first + W*i for i < n
   const int first = t0 + wave;
@@ -310,25 +338,38 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     p0 = __builtin_amdgcn_readlane(pid_reg, 2 * (i & 31));
     p1 = __builtin_amdgcn_readlane(pid_reg, 2 * (i & 31) + 1);
   };
+  if (n > 0) load_chunk(0);   // page ids of the first tiles, in flight during the staging
+
+  // The stride block's value rows go to LDS (the merge buffer, untouched
+  // until the waves combine at the end): lane (h, c) of the PV product needs
+  // 8 tokens of dim c, picked from there.
+  uint16_t* sm_vn = reinterpret_cast<uint16_t*>(sm_o0);
+  if (stride_tile) {
+#pragma unroll
+    for (int j = 0; j < kVnEarly; ++j) {
+      const int c = lane + 64 * j;
+      if (c < Qn * CH) *reinterpret_cast<u32x4*>(sm_vn + (c / CH) * D + (c % CH) * 8) = vn[j];
+    }
+    for (int c = lane + 64 * kVnEarly; c < Qn * CH; c += 64)
+      *reinterpret_cast<u32x4*>(sm_vn + (c / CH) * D + (c % CH) * 8) = *reinterpret_cast<const u32x4*>(
+          v_new + ((size_t(r) * Qn + c / CH) * Hkv + hk) * D + (c % CH) * 8);
+  }
+  // Q^T operand B staged in LDS as [dim chunk][column] 16-byte cells: lane
+  // (h, column) of k-step ks reads cell (2*ks + h, column); consecutive lanes
+  // read consecutive cells.  Columns past the workgroup's rows are zero.
+#pragma unroll
+  for (int j = 0; j < QC; ++j) {
+    const int idx = int(threadIdx.x) + j * 64 * W;
+    if (idx < CH * COLS) sm_q[idx] = (idx % COLS < rows_b) ? qc[j] : u32x4{0, 0, 0, 0};
+  }
+  // The first tile's loads go out after the staging: a wait for the staged
+  // values placed after them would also wait for the tile.
   u32x4 ak[KS], av[2][DB], bk[KS], bv[2][DB];
-  if (n > 0) {   // first tile's loads go out before the Q staging below
+  if (n > 0) {
     int p0, p1;
     pages_i(0, p0, p1);
     load_k<D, NT>(ak, kp, p0, p1, hk, Hkv, lane);
     load_v<D, NT>(av, vp, p0, p1, hk, Hkv, lane);
-  }
-
-  // Q^T operand B staged in LDS as [dim chunk][column] 16-byte cells: lane
-  // (h, column) of k-step ks reads cell (2*ks + h, column); consecutive lanes
-  // read consecutive cells.
-  for (int idx = threadIdx.x; idx < (D / 8) * COLS; idx += blockDim.x) {
-    const int ch = idx / COLS, c = idx % COLS;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (c < rows_b) {
-      const int g = (row0 + c) / Qn, i = (row0 + c) % Qn;
-      v = *reinterpret_cast<const u32x4*>(q + ((size_t(r) * Qn + i) * Hq + hk * G + g) * D + ch * 8);
-    }
-    sm_q[idx] = v;
   }
   __syncthreads();
 
@@ -396,29 +437,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   };
 
   // ---- the stride block: keys/values of this pass's rows, masked j <= i ----
+  // One 32-token block (Qn <= 31); key rows past Qn were read as row Qn - 1
+  // and are zeroed here, value rows past Qn read as zero.
   if (stride_tile) {
-    // rows past Qn read row Qn - 1 and are zeroed after the load, so every
-    // load is unconditional and all of them are in flight together
-    u32x4 sk[KS], sv[2][DB];
-    const int ti = lane & 31;
-    const int tic = min(ti, Qn - 1);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(k_new + ((size_t(r) * Qn + tic) * Hkv + hk) * D +
-                                                      (2 * s + h) * 8);
-      sk[s] = (ti < Qn) ? v : u32x4{0, 0, 0, 0};
-    }
-    // Values: lane (h, c) needs 8 tokens of dim c, so the block's rows are
-    // staged in LDS (the merge buffer, untouched until the waves combine at
-    // the end) with whole-row 16-byte loads and picked from there.
-    uint16_t* sm_vn = reinterpret_cast<uint16_t*>(sm_o0);
-    constexpr int CH = D / 8;   // 16-byte chunks per row
-    for (int c = lane; c < Qn * CH; c += 64)
-      *reinterpret_cast<u32x4*>(sm_vn + (c / CH) * D + (c % CH) * 8) = *reinterpret_cast<const u32x4*>(
-          v_new + ((size_t(r) * Qn + c / CH) * Hkv + hk) * D + (c % CH) * 8);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int s = 0; s < KS; ++s)
+      if ((lane & 31) >= Qn) sk[s] = u32x4{0, 0, 0, 0};
+    u32x4 sv[2][DB];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll

@@ -48,7 +48,8 @@ isd_status check_shape(const isd_shape* s) {
   if (s->n_q_heads % s->n_kv_heads) return ISD_ERR_SHAPE;
   if (s->page_size != kPage) return ISD_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return ISD_ERR_UNSUPPORTED;
-  if (s->stride_n > 32 || s->batch > 65535) return ISD_ERR_UNSUPPORTED;
+  // the stride's own block is one 32-token attention tile: Q = 2N - 1 <= 31
+  if (s->stride_n > 16 || s->batch > 65535) return ISD_ERR_UNSUPPORTED;
   const long long rows = (long long)(s->n_q_heads / s->n_kv_heads) * (2 * s->stride_n - 1);
   if (rows > 64) return ISD_ERR_UNSUPPORTED;
   if ((long long)s->max_pages * kPage > (1LL << 30)) return ISD_ERR_SHAPE;

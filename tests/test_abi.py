@@ -53,8 +53,10 @@ def test_workspace_bytes_rejects_bad_shapes():
     assert _ws(_shape()) > 0
     for bad in (dict(n_q_heads=30), dict(head_dim=96), dict(stride_n=1), dict(batch=0),
                 dict(page_size=8), dict(stride_n=33, n_q_heads=8, n_kv_heads=8), dict(stride_n=9),
+                dict(stride_n=17, n_q_heads=8, n_kv_heads=8),
                 dict(kv_dtype=7), dict(vocab=0), dict(max_ctx=-1)):
         assert _ws(_shape(**bad)) == 0, bad
+    assert _ws(_shape(stride_n=16, n_q_heads=8, n_kv_heads=8)) > 0     # Q = 31: one stride tile
 
 
 def test_workspace_grows_with_splits():

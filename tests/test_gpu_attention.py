@@ -2,7 +2,8 @@
 
 Small cases span several 32-token tiles, ragged tails (context not a multiple
 of the tile or the page), empty contexts, GQA groups of 1, 2 and 4, stride
-sizes N = 2..8 (one and two 32-column row blocks), head dims 64 and 128, fp32
+sizes N = 2..8 and 16 (one and two 32-column row blocks; Q = 31 fills the
+stride tile), head dims 64 and 128, fp32
 and bf16, and NaN in every pool slot no request owns.  Full-size cases use
 the five named workloads at their real shapes (launch configuration as in
 the benchmark) and check sampled requests.
@@ -33,6 +34,8 @@ SMALL = [
     ("b8_ctx2k", dict(batch=2, ctx=129, vocab=64, n_q_heads=16, n_kv_heads=8, stride_n=2)),
     ("c64_ragged", dict(batch=5, ctx_range=(1, 700), vocab=64)),          # N=8: 60 rows, two blocks
     ("c64_ragged", dict(batch=3, ctx_range=(30, 90), vocab=64, head_dim=64)),
+    ("b8_ctx2k", dict(batch=2, ctx=70, vocab=64, n_q_heads=16, n_kv_heads=8, stride_n=16)),  # Q = 31, two blocks
+    ("tiny_fp32", dict(ctx=45, stride_n=16, n_q_heads=2, n_kv_heads=2, batch=2)),            # Q = 31, fp32
 ]
 
 
