@@ -196,6 +196,8 @@ def main(argv=None):
         st.accept_commit()
         if use_lora:
             st.lora_delta()
+        if ev is not None:
+            ev[2].record(stream)
 
     if args.calibrate_copy:
         src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
@@ -208,8 +210,7 @@ def main(argv=None):
         one_step(steps[i % sets])
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -217,7 +218,11 @@ def main(argv=None):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    attn_each = np.array([e[0].elapsed_time(e[1]) for e in events])
+    step_each = np.array([e[0].elapsed_time(e[2]) for e in events])
+    attn_ms = float(np.mean(attn_each))
+    pct = lambda x: {"p10": round(float(np.percentile(x, 10)), 5), "p50": round(float(np.percentile(x, 50)), 5),
+                     "p90": round(float(np.percentile(x, 90)), 5)}
     ms_per_step = elapsed * 1e3 / args.steps
     steps_per_s = args.steps / elapsed
 
@@ -332,6 +337,7 @@ def main(argv=None):
         "committed_tokens_per_s": round(committed_per_step * steps_per_s, 1),
         "request_steps_per_s": round(cfg.batch * steps_per_s, 1),
         "accepted_per_step": accepted_per_step,
+        "event_ms": {"step": pct(step_each), "attention": pct(attn_each)},
         "step_hbm": {"bytes": int(total_bytes), "achieved_GBs": round(total_bytes / ms_per_step / 1e6, 1),
                      "frac": round(total_bytes / ms_per_step / 1e6 / HBM_PEAK_GBS, 4)},
         "roofline": {
