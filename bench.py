@@ -196,8 +196,6 @@ def main(argv=None):
         st.accept_commit()
         if use_lora:
             st.lora_delta()
-        if ev is not None:
-            ev[2].record(stream)
 
     if args.calibrate_copy:
         src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
@@ -210,7 +208,7 @@ def main(argv=None):
         one_step(steps[i % sets])
     torch.cuda.synchronize()
 
-    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -219,7 +217,8 @@ def main(argv=None):
     elapsed = time.perf_counter() - t0
 
     attn_each = np.array([e[0].elapsed_time(e[1]) for e in events])
-    step_each = np.array([e[0].elapsed_time(e[2]) for e in events])
+    # a step's duration: from its first event to the next step's (no extra event in the loop)
+    step_each = np.array([a[0].elapsed_time(b[0]) for a, b in zip(events[:-1], events[1:])])
     attn_ms = float(np.mean(attn_each))
     pct = lambda x: {"p10": round(float(np.percentile(x, 10)), 5), "p50": round(float(np.percentile(x, 50)), 5),
                      "p90": round(float(np.percentile(x, 90)), 5)}
@@ -260,8 +259,9 @@ def main(argv=None):
         # every forward verifies proposals drawn from the q rows it is tested against, so the
         # per-position acceptance is the workload's target
         # the same workload with page room for the tokens the loop commits
-        lwl = make_workload(cfg, with_mask_logits=True, extra_tokens=(loop_forwards + 8) * (cfg.stride_n - 1))
-        lp = DeviceStep.from_arrays(lwl, device=dev, max_ctx=int(lwl.ctx_lens.max()) + (loop_forwards + 8) * cfg.stride_n,
+        room = 2 * loop_forwards + 16          # the eager forwards, then the same number replayed
+        lwl = make_workload(cfg, with_mask_logits=True, extra_tokens=room * (cfg.stride_n - 1))
+        lp = DeviceStep.from_arrays(lwl, device=dev, max_ctx=int(lwl.ctx_lens.max()) + room * cfg.stride_n,
                                     commit_in_place=True)
         del lwl
         row0 = lp.mask_logits[:, :1].clone()
@@ -285,6 +285,25 @@ def main(argv=None):
                 "tokens_per_s": round(tokens / l_elapsed, 1),
                 "tpf": round(tokens / fws, 4),
                 "ms_per_forward": round(l_elapsed * 1e3 / loop_forwards, 5)}
+        # the same loop with one forward recorded into a HIP graph and replayed (Philox steps
+        # from the device forward counts)
+        for _ in range(4):
+            lp.loop_forward(device_step=True)
+        torch.cuda.synchronize()
+        lgraph = lp.capture_loop_forward()
+        tok0 = int(lp.extra["tokens"].sum().item())
+        fw0 = int(lp.extra["forwards"].sum().item())
+        t0 = time.perf_counter()
+        for _ in range(loop_forwards):
+            lgraph.replay()
+        torch.cuda.synchronize()
+        g_elapsed = time.perf_counter() - t0
+        tokens = int(lp.extra["tokens"].sum().item()) - tok0
+        fws = int(lp.extra["forwards"].sum().item()) - fw0
+        loop["graph"] = {"forwards_per_s": round(loop_forwards / g_elapsed, 2),
+                         "tokens_per_s": round(tokens / g_elapsed, 1), "tpf": round(tokens / fws, 4),
+                         "ms_per_forward": round(g_elapsed * 1e3 / loop_forwards, 5)}
+        del lgraph
         del lp
 
     # MASK-row proposals, timed on their own (both policies)

@@ -191,6 +191,9 @@ isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_ne
  *     al., SC'11) with key (seed_lo, seed_hi) and counter
  *     (req_ids[r], positions[r] + k - 1, step, 0), each mapped to
  *     (w >> 11) * 2^-53.  positions[r] is the absolute position of x_1.
+ *     step is the `step` argument, or, when step_per_request is not NULL,
+ *     the low 32 bits of step_per_request[r] (a device array, so a recorded
+ *     graph of a decoding loop draws afresh on every replay).
  *
  *   p_logits, q_logits [B][N-1][V]  logit_dtype
  *   proposals  [B][N] int32          x_1..x_N
@@ -208,9 +211,10 @@ isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_ne
  */
 isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* q_logits,
                       const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
-                      uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
-                      int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
-                      float* logq_sel, void* workspace, size_t ws_bytes, hipStream_t stream);
+                      uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
+                      const int64_t* step_per_request, int32_t* accept_len, int32_t* out_tokens,
+                      int32_t* n_out, int32_t* n_commit, float* logp_sel, float* logq_sel,
+                      void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * kv_commit -- append the accepted CLEAN rows of every stride to the KV pages.
@@ -255,8 +259,8 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
 isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const void* q_logits,
                              const int32_t* proposals, const int32_t* req_ids,
                              const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
-                             uint32_t step, int32_t* accept_len, int32_t* out_tokens,
-                             int32_t* n_out, int32_t* n_commit, float* logp_sel, float* logq_sel,
+                             uint32_t step, const int64_t* step_per_request,
+                             int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel, float* logq_sel,
                              const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                              const int32_t* page_table, const int32_t* ctx_lens_in,
                              int32_t* ctx_lens_out, void* workspace, size_t ws_bytes,
@@ -278,10 +282,12 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
  *                       and counter (req_ids[r], positions[r] + N + k, step,
  *                       1), mapped to (w >> 11) * 2^-53.  positions[r] is the
  *                       absolute position of x_1, so MASK row k proposes the
- *                       token at positions[r] + N + k.
+ *                       token at positions[r] + N + k.  step is the `step`
+ *                       argument or, when step_per_request is not NULL, the
+ *                       low 32 bits of step_per_request[r] (device array).
  *   ISD_PROPOSE_ARGMAX  proposals[r][k] = the smallest index of the largest
- *                       logit (req_ids, positions, seed and step unused and
- *                       may be NULL / 0).
+ *                       logit (req_ids, positions, seed, step and
+ *                       step_per_request unused and may be NULL / 0).
  *
  *   mask_logits [B][N][V] logit_dtype, 16-byte aligned; every row holds at
  *               least one finite logit
@@ -297,8 +303,8 @@ typedef enum isd_propose_mode {
 
 isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const int32_t* req_ids,
                        const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
-                       uint32_t step, int32_t mode, int32_t* proposals, void* workspace,
-                       size_t ws_bytes, hipStream_t stream);
+                       uint32_t step, const int64_t* step_per_request, int32_t mode,
+                       int32_t* proposals, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * isd_loop_advance -- per-request bookkeeping of the multi-step decoding loop.
@@ -337,6 +343,10 @@ isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const in
  *   tokens, forwards [B] int64    running counts, in/out (start at 0)
  *
  * TPF of a request = tokens / forwards.  No workspace; no flags.
+ * `forwards` can serve as the step_per_request array of isd_accept and
+ * isd_propose: it advances by one per forward on the device, so one forward
+ * recorded into a HIP graph draws fresh uniforms on every replay (for a
+ * batch whose requests all start together it equals the forward index).
  */
 #define ISD_LOOP_VERIFY 0
 #define ISD_LOOP_REPROPOSE 1

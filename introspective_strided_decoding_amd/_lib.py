@@ -83,11 +83,11 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "isd_workspace_init": (I32, [SP, P, SZ, P]),
         "isd_read_flags": (I32, [P, ctypes.POINTER(U32), P]),
         "isd_attention": (I32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
-        "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, SZ, P]),
+        "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, P, SZ, P]),
         "kv_commit": (I32, [SP, P, P, P, P, P, P, P, P, P, SZ, P]),
-        "isd_accept_commit": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P,
+        "isd_accept_commit": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P,
                                     P, P, P, P, P, P, P, P, SZ, P]),
-        "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, I32, P, P, SZ, P]),
+        "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, P, I32, P, P, SZ, P]),
         "isd_loop_advance": (I32, [SP, P, P, P, P, P, P, P, P, P, P]),
         "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
         "isd_lora_delta": (I32, [I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
@@ -238,7 +238,7 @@ def isd_attention(shape: Shape, q, k_new, v_new, k_pages, v_pages, page_table, c
 
 def isd_accept(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
                accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, workspace,
-               stream=None) -> None:
+               stream=None, step_dev=None) -> None:
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     dt = _tdtype(shape.logit_dtype)
     i32 = torch.int32
@@ -247,6 +247,7 @@ def isd_accept(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, 
         _ptr(q_logits, "q_logits", dt, B * (N - 1) * V), _ptr(proposals, "proposals", i32, B * N),
         _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
         int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF,
+        None if step_dev is None else _ptr(step_dev, "step_dev", torch.int64, B),
         _ptr(accept_len, "accept_len", i32, B), _ptr(out_tokens, "out_tokens", i32, B * N),
         _ptr(n_out, "n_out", i32, B), _ptr(n_commit, "n_commit", i32, B),
         _ptr(logp_sel, "logp_sel", torch.float32, B * (N - 1)),
@@ -271,7 +272,8 @@ def kv_commit(shape: Shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens
 
 def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
                       accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new, v_new, k_pages,
-                      v_pages, page_table, ctx_lens_in, ctx_lens_out, workspace, stream=None) -> None:
+                      v_pages, page_table, ctx_lens_in, ctx_lens_out, workspace, stream=None,
+                      step_dev=None) -> None:
     """isd_accept followed by kv_commit of the accepted rows, in one call."""
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     Q, Hkv, D = shape.q_rows, shape.n_kv_heads, shape.head_dim
@@ -283,6 +285,7 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
         _ptr(q_logits, "q_logits", dt, B * (N - 1) * V), _ptr(proposals, "proposals", i32, B * N),
         _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
         int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF,
+        None if step_dev is None else _ptr(step_dev, "step_dev", torch.int64, B),
         _ptr(accept_len, "accept_len", i32, B), _ptr(out_tokens, "out_tokens", i32, B * N),
         _ptr(n_out, "n_out", i32, B), _ptr(n_commit, "n_commit", i32, B),
         _ptr(logp_sel, "logp_sel", torch.float32, B * (N - 1)),
@@ -295,7 +298,7 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
 
 
 def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, mode: int,
-                proposals, workspace, stream=None) -> None:
+                proposals, workspace, stream=None, step_dev=None) -> None:
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     i32 = torch.int32
     sample = mode == PROPOSE_SAMPLE
@@ -303,7 +306,8 @@ def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, 
         ctypes.byref(shape.c()), _ptr(mask_logits, "mask_logits", _tdtype(shape.logit_dtype), B * N * V),
         _ptr(req_ids, "req_ids", i32, B) if sample or req_ids is not None else None,
         _ptr(positions, "positions", i32, B) if sample or positions is not None else None,
-        int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(mode),
+        int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF,
+        None if step_dev is None else _ptr(step_dev, "step_dev", torch.int64, B), int(mode),
         _ptr(proposals, "proposals", i32, B * N),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 

@@ -70,6 +70,7 @@ struct DecideArgs {
   const int32_t* positions;
   uint64_t seed_lo, seed_hi;
   uint32_t step;
+  const int64_t* step_dev;   // per-request step counters in device memory (NULL: `step` for all)
   int N, V, shards;
   int32_t *accept_len, *out_tokens, *n_out, *n_commit;
   float *logp_sel, *logq_sel;
@@ -206,11 +207,15 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   // wave 0: the proposals and the logits at them, requested before the combine
   int x = 0, xl = 0;
   float raw_p = 0.f, raw_q = 0.f;
+  uint32_t rid32 = 0, pos32 = 0, step32 = a.step;
   if (wave == 0) {
     if (lane < R) {
       x = a.proposals[size_t(r) * N + lane + 1];
       raw_p = a.gath[size_t(r) * 2 * R + lane];
       raw_q = a.gath[size_t(r) * 2 * R + R + lane];
+      rid32 = uint32_t(a.req_ids[r]);
+      pos32 = uint32_t(a.positions[r]);
+      if (a.step_dev) step32 = uint32_t(a.step_dev[r]);
     }
     if (lane < N) xl = a.proposals[size_t(r) * N + lane];
   }
@@ -246,9 +251,8 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
     a.logp_sel[row] = lp;
     a.logq_sel[row] = lq;
     const float rho = __expf(lp - lq);
-    const uint64_t rid = uint64_t(uint32_t(a.req_ids[r]));
-    const uint64_t pos = uint64_t(uint32_t(a.positions[r])) + uint64_t(j + 1);
-    const Philox4x64Out w = philox4x64_10(rid, pos, uint64_t(a.step), 0, a.seed_lo, a.seed_hi);
+    const uint64_t pos = uint64_t(pos32) + uint64_t(j + 1);
+    const Philox4x64Out w = philox4x64_10(uint64_t(rid32), pos, uint64_t(step32), 0, a.seed_lo, a.seed_hi);
     const double u = unit_double(w.w[0]);
     u_res = unit_double(w.w[1]);
     reject = !(u < double(rho));
@@ -671,10 +675,10 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
 template <typename T>
 hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, const void* ql,
                     const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
-                    uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
-                    int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
-                    float* logq_sel, char* ws, const WsLayout& L, const CommitArgs* commit,
-                    hipStream_t stream) {
+                    uint64_t seed_lo, uint64_t seed_hi, uint32_t step, const int64_t* step_dev,
+                    int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit,
+                    float* logp_sel, float* logq_sel, char* ws, const WsLayout& L,
+                    const CommitArgs* commit, hipStream_t stream) {
   const T* P = static_cast<const T*>(pl);
   const T* Qp = static_cast<const T*>(ql);
   const int N = s.stride_n, V = s.vocab, B = s.batch;
@@ -691,6 +695,7 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.seed_lo = seed_lo;
   a.seed_hi = seed_hi;
   a.step = step;
+  a.step_dev = step_dev;
   a.N = N;
   a.V = V;
   a.shards = p.shards;
@@ -723,15 +728,16 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
 hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_logits,
                          const void* q_logits, const int32_t* proposals, const int32_t* req_ids,
                          const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                         int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit,
-                         float* logp_sel, float* logq_sel, char* ws, const WsLayout& L,
+                         const int64_t* step_dev, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
+                         int32_t* n_commit, float* logp_sel, float* logq_sel, char* ws, const WsLayout& L,
                          const CommitArgs* commit, hipStream_t stream) {
   if (s.logit_dtype == ISD_BF16)
     return launch_t<uint16_t>(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi,
-                              step, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L,
-                              commit, stream);
+                              step, step_dev, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel,
+                              ws, L, commit, stream);
   return launch_t<float>(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi, step,
-                         accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L, commit, stream);
+                         step_dev, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L, commit,
+                         stream);
 }
 
 }  // namespace isd

@@ -159,7 +159,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 4; }
+int32_t isd_abi_version(void) { return 5; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {
@@ -224,7 +224,8 @@ isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_ne
 
 isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* q_logits,
                       const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
-                      uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
+                      uint64_t seed_lo, uint64_t seed_hi, uint32_t step, const int64_t* step_per_request,
+                      int32_t* accept_len,
                       int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
                       float* logq_sel, void* workspace, size_t ws_bytes, hipStream_t stream) {
   isd_status st = check_shape(shape);
@@ -240,14 +241,15 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
   const AcceptPlan p = plan_accept(*shape);
   const WsLayout L = ws_layout(*shape);
   hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
-                               seed_hi, step, accept_len, out_tokens, n_out, n_commit, logp_sel,
-                               logq_sel, static_cast<char*>(workspace), L, nullptr, stream);
+                               seed_hi, step, step_per_request, accept_len, out_tokens, n_out, n_commit,
+                               logp_sel, logq_sel, static_cast<char*>(workspace), L, nullptr, stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept");
 }
 
 isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const void* q_logits,
                              const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
-                             uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int32_t* accept_len,
+                             uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
+                             const int64_t* step_per_request, int32_t* accept_len,
                              int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
                              float* logq_sel, const void* k_new, const void* v_new, void* k_pages,
                              void* v_pages, const int32_t* page_table, const int32_t* ctx_lens_in,
@@ -272,8 +274,8 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
                                    ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
                                    reinterpret_cast<uint32_t*>(ws + L.cmt_cnt));
   hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
-                               seed_hi, step, accept_len, out_tokens, n_out, n_commit, logp_sel,
-                               logq_sel, ws, L, &c, stream);
+                               seed_hi, step, step_per_request, accept_len, out_tokens, n_out, n_commit,
+                               logp_sel, logq_sel, ws, L, &c, stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept_commit");
 }
 
@@ -300,8 +302,8 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
 
 isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const int32_t* req_ids,
                        const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                       int32_t mode, int32_t* proposals, void* workspace, size_t ws_bytes,
-                       hipStream_t stream) {
+                       const int64_t* step_per_request, int32_t mode, int32_t* proposals, void* workspace,
+                       size_t ws_bytes, hipStream_t stream) {
   isd_status st = check_shape(shape);
   if (st != ISD_OK) return st;
   if (mode != ISD_PROPOSE_SAMPLE && mode != ISD_PROPOSE_ARGMAX) return ISD_ERR_UNSUPPORTED;
@@ -311,8 +313,9 @@ isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const in
   if ((long long)shape->batch * shape->stride_n > 65535) return ISD_ERR_UNSUPPORTED;
   st = check_ws(shape, workspace, ws_bytes);
   if (st != ISD_OK) return st;
-  hipError_t e = launch_propose(*shape, mask_logits, req_ids, positions, seed_lo, seed_hi, step, mode,
-                                proposals, static_cast<char*>(workspace), ws_layout(*shape), stream);
+  hipError_t e = launch_propose(*shape, mask_logits, req_ids, positions, seed_lo, seed_hi, step,
+                                step_per_request, mode, proposals, static_cast<char*>(workspace),
+                                ws_layout(*shape), stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_propose");
 }
 

@@ -127,6 +127,7 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
                                                          const int32_t* __restrict__ req_ids,
                                                          const int32_t* __restrict__ positions,
                                                          uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
+                                                         const int64_t* __restrict__ step_dev,
                                                          int32_t* __restrict__ out) {
   const int row = blockIdx.x;
   const int r = row / N, k = row % N;
@@ -147,10 +148,11 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
   first_part.max = -INFINITY;
   first_part.idx = INT_MAX;
   if (wave == 0 && s0 < s1) first_part = rp[s0];
-  uint32_t rid32 = 0, pos32 = 0;
+  uint32_t rid32 = 0, pos32 = 0, step32 = step;
   if (wave == 0 && sample) {
     rid32 = uint32_t(req_ids[r]);
     pos32 = uint32_t(positions[r]);
+    if (step_dev) step32 = uint32_t(step_dev[r]);
   }
   if (sample) fill_exp_table(tab64);
   if (wave == 0) {
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
       // uniform of this proposal: counter (request, position + N + k, step, 1), word 0
       const uint64_t rid = uint64_t(rid32);
       const uint64_t pos = uint64_t(pos32) + uint64_t(N + k);
-      const double u = unit_double(philox4x64_10(rid, pos, uint64_t(step), 1, seed_lo, seed_hi).w[0]);
+      const double u = unit_double(philox4x64_10(rid, pos, uint64_t(step32), 1, seed_lo, seed_hi).w[0]);
       // shard masses in units of exp(row max)
       const double Md = M;
       double wsh = 0.0;
@@ -265,8 +267,8 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
 
 template <typename T>
 hipError_t launch_t(const isd_shape& s, const void* logits, const int32_t* req_ids, const int32_t* positions,
-                    uint64_t seed_lo, uint64_t seed_hi, uint32_t step, int mode, int32_t* out,
-                    char* ws, const WsLayout& L, hipStream_t stream) {
+                    uint64_t seed_lo, uint64_t seed_hi, uint32_t step, const int64_t* step_dev, int mode,
+                    int32_t* out, char* ws, const WsLayout& L, hipStream_t stream) {
   const T* lg = static_cast<const T*>(logits);
   const int N = s.stride_n, V = s.vocab, B = s.batch;
   const int shards = prop_shards(V);
@@ -275,7 +277,7 @@ hipError_t launch_t(const isd_shape& s, const void* logits, const int32_t* req_i
   hipLaunchKernelGGL((prop_partial<T>), dim3(shards, B * N), dim3(kPThreads), 0, stream, lg, V, shards,
                      sample, part);
   hipLaunchKernelGGL((prop_select<T>), dim3(B * N), dim3(kPThreads), 0, stream, lg, N, V, shards, sample,
-                     part, req_ids, positions, seed_lo, seed_hi, step, out);
+                     part, req_ids, positions, seed_lo, seed_hi, step, step_dev, out);
   return hipGetLastError();
 }
 
@@ -285,12 +287,13 @@ int prop_shards(int vocab) { return (vocab + kPShard - 1) / kPShard; }
 
 hipError_t launch_propose(const isd_shape& s, const void* mask_logits, const int32_t* req_ids,
                           const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                          int mode, int32_t* proposals, char* ws, const WsLayout& L, hipStream_t stream) {
+                          const int64_t* step_dev, int mode, int32_t* proposals, char* ws, const WsLayout& L,
+                          hipStream_t stream) {
   if (s.logit_dtype == ISD_BF16)
-    return launch_t<uint16_t>(s, mask_logits, req_ids, positions, seed_lo, seed_hi, step, mode, proposals,
-                              ws, L, stream);
-  return launch_t<float>(s, mask_logits, req_ids, positions, seed_lo, seed_hi, step, mode, proposals, ws,
-                         L, stream);
+    return launch_t<uint16_t>(s, mask_logits, req_ids, positions, seed_lo, seed_hi, step, step_dev, mode,
+                              proposals, ws, L, stream);
+  return launch_t<float>(s, mask_logits, req_ids, positions, seed_lo, seed_hi, step, step_dev, mode,
+                         proposals, ws, L, stream);
 }
 
 }  // namespace isd

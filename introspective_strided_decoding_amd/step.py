@@ -125,11 +125,15 @@ class DeviceStep:
             _lib.isd_attention, self.shape, self.q, self.k_new, self.v_new, self.k_pages, self.v_pages,
             self.page_table, self.ctx_lens, self.out, self.workspace))(stream)
 
-    def accept(self, stream=None, step: Optional[int] = None, seed=None):
-        self._call("accept", lambda: _lib.prepare(
+    def _step_dev(self, device_step: bool):
+        return self.extra["forwards"] if device_step else None
+
+    def accept(self, stream=None, step: Optional[int] = None, seed=None, device_step: bool = False):
+        """``device_step``: each request's Philox step is its forward count on the device."""
+        self._call(("accept", device_step), lambda: _lib.prepare(
             _lib.isd_accept, self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
             self.positions, self.seed, self.step, self.accept_len, self.out_tokens, self.n_out, self.n_commit,
-            self.logp_sel, self.logq_sel, self.workspace))(
+            self.logp_sel, self.logq_sel, self.workspace, step_dev=self._step_dev(device_step)))(
             stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def commit(self, stream=None):
@@ -146,17 +150,18 @@ class DeviceStep:
             self.ctx_lens, self.ctx_lens_out, self.workspace))(
             stream, self.step if step is None else step, self.seed if seed is None else seed)
 
-    def propose(self, stream=None, mode: int = _lib.PROPOSE_SAMPLE, step: Optional[int] = None, seed=None):
-        self._call(("propose", mode), lambda: _lib.prepare(
+    def propose(self, stream=None, mode: int = _lib.PROPOSE_SAMPLE, step: Optional[int] = None, seed=None,
+                device_step: bool = False):
+        self._call(("propose", mode, device_step), lambda: _lib.prepare(
             _lib.isd_propose, self.shape, self.mask_logits, self.req_ids, self.positions, self.seed,
-            self.step, mode, self.next_proposals, self.workspace))(
+            self.step, mode, self.next_proposals, self.workspace, step_dev=self._step_dev(device_step)))(
             stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def loop_start(self):
         """Device state of the multi-step loop: every request starts verifying its proposals."""
         B = self.shape.batch
         dev = self.proposals.device
-        self.__dict__.get("_calls", {}).pop("loop_advance", None)    # marshalled with the old state
+        self.__dict__.pop("_calls", None)    # calls marshalled with the old loop state
         self.extra["mode"] = torch.zeros(B, dtype=torch.int32, device=dev)
         self.extra["tokens"] = torch.zeros(B, dtype=torch.int64, device=dev)
         self.extra["forwards"] = torch.zeros(B, dtype=torch.int64, device=dev)
@@ -175,7 +180,8 @@ class DeviceStep:
             s = self.extra["side_stream"] = (torch.cuda.Stream(device=dev), torch.cuda.Event(), torch.cuda.Event())
         return s
 
-    def _accept_and_propose(self, accept_fn, stream, step: Optional[int], overlap: bool):
+    def _accept_and_propose(self, accept_fn, stream, step: Optional[int], overlap: bool,
+                            device_step: bool = False):
         """The accept chain on ``stream`` and the proposals on a second stream, joined after.
 
         Both read this forward's logits and neither writes what the other reads
@@ -188,22 +194,43 @@ class DeviceStep:
             fork.record(main)
             side.wait_event(fork)
             accept_fn(main, step)
-            self.propose(side, step=step)
+            self.propose(side, step=step, device_step=device_step)
             join.record(side)
             main.wait_event(join)
         else:
             accept_fn(stream, step)
-            self.propose(stream, step=step)
+            self.propose(stream, step=step, device_step=device_step)
 
-    def loop_forward(self, step: int, attention: bool = True, stream=None, overlap: bool = True):
+    def loop_forward(self, step: int = 0, attention: bool = True, stream=None, overlap: bool = True,
+                     device_step: bool = False):
         """One forward of the decoding loop: attention, accept and proposals (side by side
-        unless ``overlap`` is False), bookkeeping, commit."""
+        unless ``overlap`` is False), bookkeeping, commit.  With ``device_step`` the Philox
+        step of every request is its forward count on the device (``step`` unused), so the
+        forward can be recorded once and replayed."""
         if attention:
             self.attention(stream)
-        self._accept_and_propose(lambda s, t: self.accept(s, step=t), stream, step, overlap)
+        self._accept_and_propose(lambda s, t: self.accept(s, step=t, device_step=device_step), stream, step,
+                                 overlap, device_step)
         self.loop_advance(stream)
         if attention:
             self.commit(stream)
+
+    def capture_loop_forward(self, overlap: bool = True):
+        """Record one ``loop_forward(device_step=True)`` into a HIP graph and return it.
+
+        Every replay is the next forward: the loop state (proposals, positions, mode,
+        forward counts, KV pages and lengths) lives on the device and the Philox step
+        comes from the forward counts.  The logits are read from the same buffers on
+        every replay, so the caller refreshes them in place between replays.  Recording
+        runs nothing; call ``loop_forward(device_step=True, overlap=...)`` eagerly at
+        least once before, so every call is marshalled and the second stream exists."""
+        if ("accept", True) not in self.__dict__.get("_calls", {}) or (
+                overlap and "side_stream" not in self.extra):
+            raise RuntimeError("run loop_forward(device_step=True) eagerly before recording it")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.loop_forward(overlap=overlap, device_step=True)
+        return graph
 
     def lora_delta(self, stream=None):
         L = self.lora

@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 4
+    assert LIB.isd_abi_version() == 5
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"
@@ -90,7 +90,9 @@ def test_attention_validation():
 def test_accept_and_commit_validation():
     s = _shape()
     n = _ws(s)
-    args = [FAKE] * 5 + [1, 2, 3] + [FAKE] * 6 + [FAKE, n, None]
+    # the accept arguments: 5 tensors, seed_lo, seed_hi, step, step_per_request (may be NULL),
+    # 6 outputs, workspace, its size, stream
+    args = [FAKE] * 5 + [1, 2, 3, None] + [FAKE] * 6 + [FAKE, n, None]
     bad = list(args)
     bad[2] = None
     assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 1
@@ -108,13 +110,13 @@ def test_accept_and_commit_validation():
     bad[-2] = 0
     assert LIB.kv_commit(ctypes.byref(s.c()), *bad) == 4
     # isd_accept_commit: the accept arguments, then k_new .. ctx_lens_out, workspace, stream
-    fargs = [FAKE] * 5 + [1, 2, 3] + [FAKE] * 6 + [FAKE] * 7 + [FAKE, n, None]
-    assert len(fargs) == 24
-    for i in (2, 14, 18, 20):       # proposals, k_new, page_table, ctx_lens_out
+    fargs = [FAKE] * 5 + [1, 2, 3, None] + [FAKE] * 6 + [FAKE] * 7 + [FAKE, n, None]
+    assert len(fargs) == 25
+    for i in (2, 15, 19, 21):       # proposals, k_new, page_table, ctx_lens_out
         bad = list(fargs)
         bad[i] = None
         assert LIB.isd_accept_commit(ctypes.byref(s.c()), *bad) == 1, i
-    for i in (0, 14, 15, 16):       # p_logits, k_new, v_new, k_pages
+    for i in (0, 15, 16, 17):       # p_logits, k_new, v_new, k_pages
         bad = list(fargs)
         bad[i] = MISALIGNED
         assert LIB.isd_accept_commit(ctypes.byref(s.c()), *bad) == 7, i
@@ -129,7 +131,7 @@ def test_propose_validation():
     n = _ws(s)
 
     def call(logits=FAKE, req=FAKE, pos=FAKE, mode=0, out=FAKE, ws=FAKE, ws_bytes=n, shape=s):
-        return LIB.isd_propose(ctypes.byref(shape.c()), logits, req, pos, 1, 2, 3, mode, out, ws,
+        return LIB.isd_propose(ctypes.byref(shape.c()), logits, req, pos, 1, 2, 3, None, mode, out, ws,
                                ws_bytes, None)
 
     assert call(ws_bytes=8) == 4                      # every check passes up to the workspace size

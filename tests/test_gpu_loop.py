@@ -178,3 +178,71 @@ def test_loop_with_proposals_beside_accept_matches_sequential():
             assert torch.equal(getattr(a, n).view(torch.uint8), getattr(b, n).view(torch.uint8)), (t, n)
         for n in ("mode", "tokens", "forwards"):
             assert torch.equal(a.extra[n], b.extra[n]), (t, n)
+
+
+def _feed(st, pool, wl, t, K):
+    p, q = (wl.p_logits, wl.q_logits) if t == 0 else pool[(t - 1) % K][:2]
+    st.p_logits.copy_(_dev(p, st.p_logits))
+    st.q_logits.copy_(_dev(q, st.q_logits))
+    st.mask_logits.copy_(_dev(pool[t % K][2], st.mask_logits))
+
+
+_STATE = ("accept_len", "n_out", "next_proposals", "n_commit", "proposals", "positions", "ctx_lens",
+          "out_tokens", "k_pages", "v_pages")
+
+
+def _same_state(a, b, t):
+    for n in _STATE:
+        assert torch.equal(getattr(a, n).view(torch.uint8), getattr(b, n).view(torch.uint8)), (t, n)
+    for n in ("mode", "tokens", "forwards"):
+        assert torch.equal(a.extra[n], b.extra[n]), (t, n)
+
+
+def test_loop_device_step_matches_step_argument():
+    """Philox steps read from the device forward counts draw what the step argument t
+    draws when every request started together (forwards = t)."""
+    T, K = 5, 3
+    cfg = get_config("b8_ctx2k", batch=9, ctx=40, vocab=3000, stride_n=4)
+    wl = make_workload(cfg, seed=63, with_mask_logits=True, extra_tokens=T * (cfg.stride_n - 1))
+    pool = _pool(cfg, K, 320, "batch")
+    a = device_step(wl, commit_in_place=True)
+    b = device_step(wl, commit_in_place=True)
+    for st in (a, b):
+        st.loop_start()
+    for t in range(T):
+        for st in (a, b):
+            _feed(st, pool, wl, t, K)
+        a.loop_forward(step=t)
+        b.loop_forward(device_step=True)
+        torch.cuda.synchronize()
+        _same_state(a, b, t)
+
+
+@pytest.mark.parametrize("overlap", [True, False])
+def test_loop_forward_graph_replays_match_eager(overlap):
+    """One loop forward recorded into a HIP graph and replayed forward after forward
+    (logits refreshed in place in between) leaves the same state, pools and lengths as
+    the same forwards issued eagerly."""
+    T, K, warm = 6, 3, 1
+    cfg = get_config("b8_ctx2k", batch=8, ctx=40, vocab=3000, stride_n=4)
+    wl = make_workload(cfg, seed=64, with_mask_logits=True, extra_tokens=(T + warm) * (cfg.stride_n - 1))
+    pool = _pool(cfg, K, 330, "batch")
+    a = device_step(wl, commit_in_place=True)
+    b = device_step(wl, commit_in_place=True)
+    for st in (a, b):
+        st.loop_start()
+    for t in range(warm):
+        for st in (a, b):
+            _feed(st, pool, wl, t, K)
+            st.loop_forward(device_step=True, overlap=overlap)
+    torch.cuda.synchronize()
+    graph = b.capture_loop_forward(overlap=overlap)
+    for t in range(warm, warm + T):
+        for st in (a, b):
+            _feed(st, pool, wl, t, K)
+        a.loop_forward(device_step=True, overlap=overlap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _same_state(a, b, t)
+    assert int(b.extra["forwards"][0]) == warm + T
