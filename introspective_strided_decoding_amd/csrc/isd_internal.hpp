@@ -11,9 +11,10 @@ namespace isd {
 
 constexpr int kPage = 16;          // tokens per KV page
 constexpr int kTileTokens = 32;    // tokens per attention tile (two pages)
-// Waves per attention workgroup (two per SIMD; each wave takes 32-token tiles
-// round-robin for one block of 32 query rows).
-constexpr int kAttnWaves = 8;
+// Waves per attention workgroup (one per SIMD, so two workgroups share a CU
+// and one streams while the other stages its operands or writes its output;
+// each wave takes 32-token tiles round-robin for one block of 32 query rows).
+constexpr int kAttnWaves = 4;
 constexpr size_t kHeaderBytes = 256;
 
 // How the KV walk of isd_attention is split across workgroups.
