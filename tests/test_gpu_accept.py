@@ -52,6 +52,7 @@ def test_accept_tiny_fp32_many_draws():
     dict(batch=3, ctx=16, vocab=8, stride_n=8),             # tiny vocabulary, N=8
     dict(batch=2, ctx=16, vocab=4099, stride_n=5),          # odd V, several shards
     dict(batch=3, ctx=16, vocab=151936, stride_n=2),        # full vocab, single decision
+    dict(batch=300, ctx=16, vocab=4099, stride_n=4),        # many requests, one normaliser shard per row
 ])
 def test_accept_small_shapes_bf16(over):
     wl = make_workload(get_config("b8_ctx2k", **over))

@@ -104,3 +104,19 @@ def test_attention_full_size(name, sample):
     check_attention(wl, st.out, requests=sample)
     from introspective_strided_decoding_amd import isd_read_flags
     assert isd_read_flags(st.workspace) == 0
+
+
+@pytest.mark.parametrize("batch", [300, 520])
+def test_attention_many_requests_past_ranking_limit(batch):
+    """More requests than the in-kernel longest-first ranking handles (256) and a grid of
+    several rounds: the workgroups fall back to index order; every sampled request is
+    exact, including the first and last ones."""
+    cfg = get_config("b8_ctx2k", batch=batch, ctx_range=(1, 300), ctx=None, vocab=64)
+    wl = make_workload(cfg, seed=15, with_logits=False)
+    st = device_step(wl)
+    st.attention()
+    torch.cuda.synchronize()
+    order = np.argsort(wl.ctx_lens)
+    check_attention(wl, st.out, requests=[0, batch - 1, int(order[0]), int(order[-1]), batch // 2])
+    from introspective_strided_decoding_amd import isd_read_flags
+    assert isd_read_flags(st.workspace) == 0
