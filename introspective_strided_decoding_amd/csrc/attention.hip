@@ -1,8 +1,9 @@
 // Stride attention over the paged KV cache (isd_attention).
 //
 // Work split: a work unit is (request r, KV head hk, split s): a run of
-// 32-token tiles (two 16-token pages) of r's context.  One workgroup of eight
-// waves serves one unit for one block of 32 query columns (the GQA group's G
+// 32-token tiles (two 16-token pages) of r's context.  One workgroup of W
+// waves (four: one per SIMD, two workgroups per CU) serves one unit for one
+// block of 32 query columns (the GQA group's G
 // heads x Q stride rows; groups of more than 32 columns get one workgroup per
 // block, placed on the same XCD so the second read of the pages hits L2).
 // The waves take the unit's tiles round-robin, and wave 0 of split 0 also
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
   }
 
-  // ---- merge the four waves of the workgroup ----
+  // ---- merge the W waves of the workgroup ----
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32);
