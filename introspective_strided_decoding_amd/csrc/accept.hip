@@ -304,6 +304,7 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
 constexpr int kRPer = 8;
 constexpr int kRShard = kThreads * kRPer;
 constexpr double kResidBand = 1e-4;
+constexpr int kAmbSlots = 64;   // boundary entries a pass workgroup lists (more: the shard is recomputed)
 
 // 2^(j/64), j = 0..63, for exp_nonpos; call with all threads of the workgroup.
 __device__ __forceinline__ void fill_exp_table(double* tab64) {
@@ -391,13 +392,20 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
                                                         int r_shards, const ReqState* __restrict__ jobs,
                                                         const uint32_t* __restrict__ rej_count,
                                                         ResidShard* __restrict__ shard_out, CommitArgs cm) {
-  constexpr unsigned long long kEmpty = ~0ull;   // a NaN pattern, never an exact difference
   __shared__ double tab64[64];
-  __shared__ double sm[kThreads / 64];
-  __shared__ double sm5[kThreads / 64][5];
-  __shared__ unsigned long long cls_sm[kResidAmb];
+  __shared__ double sm4[kThreads / 64][4];
+  // entries near the boundary, listed as they are found (rare): exact logit
+  // difference, vocabulary index, e_p and e_q
+  __shared__ double amb_key[kAmbSlots];
+  __shared__ int amb_idx[kAmbSlots];
+  __shared__ double amb_e[kAmbSlots][2];
+  __shared__ int n_amb_sm;
+  __shared__ double cls_key[kResidAmb];
   __shared__ double cls_sum[kResidAmb][2];
-  __shared__ int overflow_sm;
+  __shared__ int n_cls_sm;
+  __shared__ unsigned long long cls_bits[kResidAmb];
+  __shared__ float shift_sm[2];
+  __shared__ double sm2[kThreads / 64][2];
   __shared__ int commit_last;
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
@@ -417,89 +425,156 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   const int e0 = sh * kRShard + threadIdx.x * kRPer;
   float xp[kRPer], xq[kRPer];
   load_runs<T>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
-  if (threadIdx.x < kResidAmb) cls_sm[threadIdx.x] = kEmpty;
-  if (threadIdx.x == 0) overflow_sm = 0;
+  if (threadIdx.x == 0) {
+    n_amb_sm = 0;
+    shift_sm[0] = st.max_p;
+    shift_sm[1] = st.max_q;
+  }
   fill_exp_table(tab64);
   const double kap = exp(double(st.log_kappa));
-  double sp = 0.0, sq = 0.0, a = 0.0, b = 0.0;
-  double ep[kRPer], eq[kRPer];
+  double tot[4] = {0.0, 0.0, 0.0, 0.0};   // S_p, S_q, and (a, b) over the clear part of the support
   unsigned amb = 0;
 #pragma unroll
   for (int i = 0; i < kRPer; ++i) {
-    ep[i] = exp_shift(xp[i], st.max_p, tab64);
-    eq[i] = exp_shift(xq[i], st.max_q, tab64);
-    sp += ep[i];
-    sq += eq[i];
-    const double d = ep[i] - kap * eq[i], band = kResidBand * kap * eq[i];
+    const double ep = exp_shift(xp[i], st.max_p, tab64);
+    const double eq = exp_shift(xq[i], st.max_q, tab64);
+    tot[0] += ep;
+    tot[1] += eq;
+    const double d = ep - kap * eq, band = kResidBand * kap * eq;
     if (d > band) {
-      a += ep[i];
-      b += eq[i];
-    } else if (d >= -band && ep[i] > 0.0) {
+      tot[2] += ep;
+      tot[3] += eq;
+    } else if (d >= -band && ep > 0.0) {
       amb |= 1u << i;
-    }
-  }
-  double tot[5] = {sp, sq, a, b, double(__builtin_popcount(amb))};
-  block_sum_dk<5>(tot, sm5);
-  sp = tot[0];
-  sq = tot[1];
-  a = tot[2];
-  b = tot[3];
-  // entries near the boundary: group them by their exact logit difference
-  int n_cls = 0;
-  if (tot[4] > 0.0) {
-#pragma unroll
-    for (int i = 0; i < kRPer; ++i) {
-      if (amb & (1u << i)) {
-        const unsigned long long key = __double_as_longlong(double(xp[i]) - double(xq[i]));
-        bool placed = false;
-        for (int c = 0; c < kResidAmb && !placed; ++c) {
-          const unsigned long long old = atomicCAS(&cls_sm[c], kEmpty, key);
-          placed = (old == kEmpty || old == key);
-        }
-        if (!placed) overflow_sm = 1;
+      const int slot = atomicAdd(&n_amb_sm, 1);
+      if (slot < kAmbSlots) {
+        amb_key[slot] = double(xp[i]) - double(xq[i]);
+        amb_idx[slot] = e0 + i;
+        amb_e[slot][0] = ep;
+        amb_e[slot][1] = eq;
       }
     }
-    __syncthreads();
-    // the groups in increasing order of their difference, so the record is deterministic
+  }
+  block_sum_dk<4>(tot, sm4);   // its barriers also publish the boundary list
+  const double sp = tot[0], sq = tot[1], a = tot[2], b = tot[3];
+  // Entries near the boundary, grouped by their exact logit difference (equal
+  // differences: equal ratios e_p / e_q): one thread, in vocabulary order, so
+  // the sums do not depend on the order the entries were listed in.
+  const int na = n_amb_sm;
+  if (na > 0) {
     if (threadIdx.x == 0) {
-      for (int c = 1; c < kResidAmb && cls_sm[c] != kEmpty; ++c)
-        for (int j = c; j > 0 && __longlong_as_double(cls_sm[j]) < __longlong_as_double(cls_sm[j - 1]); --j) {
-          const unsigned long long t = cls_sm[j];
-          cls_sm[j] = cls_sm[j - 1];
-          cls_sm[j - 1] = t;
+      int n_cls = 0;
+      if (na > kAmbSlots) {
+        n_cls = kResidAmb + 1;
+      } else {
+        for (int c = 1; c < na; ++c)      // insertion sort by vocabulary index
+          for (int j = c; j > 0 && amb_idx[j] < amb_idx[j - 1]; --j) {
+            const double tk = amb_key[j];
+            amb_key[j] = amb_key[j - 1];
+            amb_key[j - 1] = tk;
+            const int ti = amb_idx[j];
+            amb_idx[j] = amb_idx[j - 1];
+            amb_idx[j - 1] = ti;
+            const double t0 = amb_e[j][0], t1 = amb_e[j][1];
+            amb_e[j][0] = amb_e[j - 1][0];
+            amb_e[j][1] = amb_e[j - 1][1];
+            amb_e[j - 1][0] = t0;
+            amb_e[j - 1][1] = t1;
+          }
+        for (int j = 0; j < na && n_cls <= kResidAmb; ++j) {
+          int c = 0;
+          while (c < n_cls && cls_key[c] != amb_key[j]) ++c;
+          if (c == n_cls) {
+            if (n_cls == kResidAmb) { n_cls = kResidAmb + 1; break; }
+            cls_key[c] = amb_key[j];
+            cls_sum[c][0] = 0.0;
+            cls_sum[c][1] = 0.0;
+            ++n_cls;
+          }
+          cls_sum[c][0] += amb_e[j][0];
+          cls_sum[c][1] += amb_e[j][1];
         }
+        if (n_cls <= kResidAmb) {
+          // the groups in increasing order of their difference, so the record is deterministic
+          for (int c = 1; c < n_cls; ++c)
+            for (int j = c; j > 0 && cls_key[j] < cls_key[j - 1]; --j) {
+              const double tk = cls_key[j], tp = cls_sum[j][0], tq = cls_sum[j][1];
+              cls_key[j] = cls_key[j - 1];
+              cls_sum[j][0] = cls_sum[j - 1][0];
+              cls_sum[j][1] = cls_sum[j - 1][1];
+              cls_key[j - 1] = tk;
+              cls_sum[j - 1][0] = tp;
+              cls_sum[j - 1][1] = tq;
+            }
+        }
+      }
+      n_cls_sm = n_cls;
     }
     __syncthreads();
-    for (int c = 0; c < kResidAmb; ++c) {
-      const unsigned long long key = cls_sm[c];
-      if (key == kEmpty) break;
-      double gp = 0.0, gq = 0.0;
+    if (na > kAmbSlots) {
+      // More boundary entries than the list holds (many equal logits on both
+      // sides, say): the groups' keys are collected with compare-and-swap,
+      // then one workgroup sum per group with each entry's exps recomputed.
+      constexpr unsigned long long kEmpty = ~0ull;   // a NaN pattern, never a difference
+      if (threadIdx.x < kResidAmb) cls_bits[threadIdx.x] = kEmpty;
+      __syncthreads();
+      bool over = false;
 #pragma unroll
       for (int i = 0; i < kRPer; ++i)
-        if ((amb & (1u << i)) && __double_as_longlong(double(xp[i]) - double(xq[i])) == (long long)key) {
-          gp += ep[i];
-          gq += eq[i];
+        if (amb & (1u << i)) {
+          const unsigned long long key = __double_as_longlong(double(xp[i]) - double(xq[i]));
+          bool placed = false;
+          for (int c = 0; c < kResidAmb && !placed; ++c) {
+            const unsigned long long old = atomicCAS(&cls_bits[c], kEmpty, key);
+            placed = (old == kEmpty || old == key);
+          }
+          over |= !placed;
         }
-      gp = block_sum_d(gp, sm);
-      gq = block_sum_d(gq, sm);
-      if (threadIdx.x == 0) {
-        cls_sum[c][0] = gp;
-        cls_sum[c][1] = gq;
+      const bool any_over = __syncthreads_or(over);
+      if (threadIdx.x == 0 && !any_over) {   // groups in increasing order of their difference
+        for (int c = 1; c < kResidAmb && cls_bits[c] != kEmpty; ++c)
+          for (int j = c; j > 0 && __longlong_as_double(cls_bits[j]) < __longlong_as_double(cls_bits[j - 1]); --j) {
+            const unsigned long long t = cls_bits[j];
+            cls_bits[j] = cls_bits[j - 1];
+            cls_bits[j - 1] = t;
+          }
       }
-      n_cls = c + 1;
+      __syncthreads();
+      int nc = any_over ? kResidAmb + 1 : 0;
+      for (int c = 0; c < kResidAmb && !any_over; ++c) {
+        const unsigned long long key = cls_bits[c];
+        if (key == kEmpty) break;
+        const float mp = shift_sm[0], mq = shift_sm[1];
+        double g[2] = {0.0, 0.0};
+#pragma unroll
+        for (int i = 0; i < kRPer; ++i)
+          if ((amb & (1u << i)) && __double_as_longlong(double(xp[i]) - double(xq[i])) == (long long)key) {
+            g[0] += exp_shift(xp[i], mp, tab64);
+            g[1] += exp_shift(xq[i], mq, tab64);
+          }
+        block_sum_dk<2>(g, sm2);
+        if (threadIdx.x == 0) {
+          cls_sum[c][0] = g[0];
+          cls_sum[c][1] = g[1];
+        }
+        nc = c + 1;
+      }
+      if (threadIdx.x == 0) n_cls_sm = nc;
+      __syncthreads();
     }
   }
+  const int n_cls = (na > 0) ? n_cls_sm : 0;
   if (threadIdx.x == 0) {
     ResidShard rs;
     rs.sp = sp;
     rs.sq = sq;
     rs.a = a;
     rs.b = b;
-    rs.n_amb = overflow_sm ? kResidAmb + 1 : n_cls;
+    rs.n_amb = n_cls;
     rs.pad = 0;
     for (int j = 0; j < kResidAmb; ++j) {
-      rs.amb[j][0] = (j < n_cls) ? cls_sum[j][0] : 0.0;
-      rs.amb[j][1] = (j < n_cls) ? cls_sum[j][1] : 0.0;
+      rs.amb[j][0] = (j < n_cls && n_cls <= kResidAmb) ? cls_sum[j][0] : 0.0;
+      rs.amb[j][1] = (j < n_cls && n_cls <= kResidAmb) ? cls_sum[j][1] : 0.0;
     }
     shard_out[size_t(k) * r_shards + sh] = rs;
   }
