@@ -22,7 +22,7 @@ Modules:
   attention  strictly causal stride attention over a paged KV cache
   accept     log-normalisers, the p/q acceptance test, residual resampling
   commit     writing the accepted CLEAN rows into KV pages
-  lora       the gated low-rank delta of R-ISD
+  lora       the gated low-rank delta of R-ISD, and a whole gated projection
   tpf        expected acceptance, tokens per forward, the compute-bound identity
   propose    drawing the next N tokens at the MASK rows (sampling or argmax)
   loop       the multi-step decoding loop: per-request VERIFY / REPROPOSE bookkeeping

@@ -24,3 +24,20 @@ def gated_lora_delta(x, a, b, y, mask_rows, scale: float = 1.0) -> np.ndarray:
     gate[np.asarray(mask_rows, dtype=np.int64)] = 1.0
     delta = (x @ np.asarray(a, dtype=np.float64)) @ np.asarray(b, dtype=np.float64)
     return out + scale * gate[:, None] * delta
+
+
+def gated_projection(x, w, a, b, mask_rows, scale: float = 1.0) -> np.ndarray:
+    """One projection of an R-ISD layer, in float64: base weights on every row, the
+    adapter added on the MASK rows only ([hotdry] "Token 生成的核心参数与验收机制";
+    [project] R-ISD card):
+
+        out[m, :] = x[m, :] @ w + gate[m] * scale * (x[m, :] @ a) @ b
+
+    x: [rows, d_in], w: [d_in, d_out], a: [d_in, r], b: [r, d_out].  With a and b
+    None the projection is the base one.  A CLEAN row (gate 0) gets exactly x @ w.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    base = x @ np.asarray(w, dtype=np.float64)
+    if a is None:
+        return base
+    return gated_lora_delta(x, a, b, base, mask_rows, scale)

@@ -6,6 +6,10 @@ attention with the grown context; only the named slots change.
 
 lora: brute-force triple loop on a tiny case; A = 0 and an empty gate leave
 Y unchanged; CLEAN rows never change; the delta is linear in the scale.
+
+gated projection: explicit loops on a tiny case; identity weights return the
+input; zero weights reduce to the delta alone; CLEAN rows equal the base
+projection bit for bit; the adapter is a rank-r update.
 """
 
 import numpy as np
@@ -13,7 +17,7 @@ import torch
 
 from oracle.attention import stride_attention
 from oracle.commit import kv_commit
-from oracle.lora import gated_lora_delta
+from oracle.lora import gated_lora_delta, gated_projection
 from workloads import get_config, make_workload
 
 
@@ -105,3 +109,40 @@ def test_lora_special_cases():
     d1 = gated_lora_delta(x, a, b, y, [2, 5], scale=1.0) - y
     d2 = gated_lora_delta(x, a, b, y, [2, 5], scale=2.0) - y
     np.testing.assert_allclose(d2, 2 * d1, rtol=1e-14, atol=1e-14)
+
+
+def test_gated_projection_brute_force():
+    """Every output element by explicit loops: base product on all rows, the adapter's
+    two products added on the gated rows only."""
+    rng = np.random.Generator(np.random.PCG64(18))
+    rows, d_in, rank, d_out = 6, 5, 2, 3
+    x, w = rng.normal(size=(rows, d_in)), rng.normal(size=(d_in, d_out))
+    a, b = rng.normal(size=(d_in, rank)), rng.normal(size=(rank, d_out))
+    mask = [0, 3, 4]
+    got = gated_projection(x, w, a, b, mask, scale=0.75)
+    for m in range(rows):
+        for o in range(d_out):
+            want = sum(x[m, i] * w[i, o] for i in range(d_in))
+            if m in mask:
+                want += 0.75 * sum(sum(x[m, i] * a[i, k] for i in range(d_in)) * b[k, o] for k in range(rank))
+            assert abs(got[m, o] - want) <= 1e-12 * (1 + abs(want)), (m, o)
+
+
+def test_gated_projection_special_cases():
+    rng = np.random.Generator(np.random.PCG64(19))
+    x, w = rng.normal(size=(7, 8)), rng.normal(size=(8, 8))
+    a, b = rng.normal(size=(8, 2)), rng.normal(size=(2, 8))
+    mask = [1, 2, 6]
+    out = gated_projection(x, w, a, b, mask)
+    # identity weights: the base product is the input itself
+    np.testing.assert_array_equal(gated_projection(x, np.eye(8), None, None, []), x)
+    # zero base weights: only the gated delta is left, as the delta alone computes it
+    np.testing.assert_allclose(gated_projection(x, np.zeros((8, 8)), a, b, mask),
+                               gated_lora_delta(x, a, b, np.zeros((7, 8)), mask), rtol=0, atol=1e-13)
+    # CLEAN rows are bit for bit the base projection; no adapter = empty gate
+    base = gated_projection(x, w, None, None, [])
+    clean = [0, 3, 4, 5]
+    assert np.array_equal(out[clean], base[clean])
+    assert np.array_equal(gated_projection(x, w, a, b, []), base)
+    # the adapter is a rank-2 update of the gated rows
+    assert np.linalg.matrix_rank(out[mask] - base[mask]) <= 2
