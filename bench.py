@@ -133,6 +133,76 @@ def cpu_baseline(wl, budget_s: float = 10.0, max_steps: int = 8):
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD published
+
+
+def r_isd_projections(cfg, dev, stream, reps):
+    """The seven projections of one R-ISD layer of the 8B shape (hidden Hq*D, KV Hkv*D, MLP
+    3*hidden) at this workload's stride rows, gated (adapter on the MASK rows) and base-only,
+    each recorded into a HIP graph and replayed; PyTorch's own linear layers (hipBLASLt) time
+    the base projections for comparison."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    from introspective_strided_decoding_amd.r_isd import RIsdProjections, stride_mask_rows
+
+    hidden, kv = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    if hidden % 256 or kv % 128:
+        return None
+    rows = cfg.batch * cfg.q_rows
+    proj = RIsdProjections(rows, stride_mask_rows(cfg.batch, cfg.stride_n), hidden=hidden, kv=kv,
+                           mlp=3 * hidden, seed=11, device=dev)
+    res = {"what": "q, k, v, o, gate, up, down projections of one layer; adapter rank 128 on the MASK rows",
+           "rows": rows, "gated_rows": int(proj.mask.numel()), "hidden": hidden, "kv": kv, "mlp": 3 * hidden}
+    for gated in (True, False):
+        for _ in range(3):
+            proj.run(gated)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            proj.run(gated)
+        for _ in range(3):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        f, by = proj.flops(gated), proj.bytes(gated)
+        res["gated" if gated else "base"] = {
+            "ms": round(ms, 5), "tflops": round(f / ms / 1e9, 1),
+            "mfma_frac": round(f / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "GBs": round(by / ms / 1e6, 1), "hbm_frac": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "flops": int(f), "bytes": int(by)}
+        del g
+    res["alpha"] = round(res["gated"]["ms"] / res["base"]["ms"], 4)
+    t_mfma = proj.flops(False) / (MFMA_BF16_PEAK_TFLOPS * 1e9)
+    t_hbm = proj.bytes(False) / (HBM_PEAK_GBS * 1e6)
+    res["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
+    res["base_frac_of_bound"] = round(max(t_mfma, t_hbm) / res["base"]["ms"], 4)
+    # the same base projections through torch.nn.functional.linear
+    pairs = [(t["X"], t["W_t"]) for t in proj.p.values()]
+    for _ in range(3):
+        for x, w in pairs:
+            F.linear(x, w)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        for x, w in pairs:
+            F.linear(x, w)
+    b.record(stream)
+    torch.cuda.synchronize()
+    res["torch_linear_base_ms"] = round(a.elapsed_time(b) / reps, 5)
+    del proj, pairs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +213,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--no-loop", action="store_true", help="skip the decoding-loop measurement")
+    ap.add_argument("--no-r-isd", action="store_true", help="skip the R-ISD layer projections")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device copy before the timed loop (a known-size reference "
                          "for hardware traffic counters)")
@@ -327,6 +398,8 @@ def main(argv=None):
     prop["bytes_per_call"] = int(pbytes)
     prop["steps_per_s_with_sampled_proposals"] = round(1e3 / (ms_per_step + prop["sample"]["avg_call_ms"]), 2)
 
+    r_isd = None if args.no_r_isd else r_isd_projections(cfg, dev, stream, reps=max(20, args.steps // 3))
+
     # accepted / committed tokens of the timed steps (identical draws per set)
     acc = [int(st.accept_len.sum().item()) for st in steps]
     ncommit = steps[0].n_commit.cpu().numpy()
@@ -373,6 +446,7 @@ def main(argv=None):
         "propose": prop,
         "graph": graph,
         "loop": loop,
+        "r_isd": r_isd,
         "input_gen_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:

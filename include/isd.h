@@ -22,6 +22,8 @@
  *   isd_loop_advance  per-request bookkeeping of the multi-step decoding loop;
  *   isd_lora_delta the gated low-rank delta of Residual ISD (R-ISD), added at
  *                  MASK rows only.
+ *   isd_gated_linear  a whole R-ISD projection: base weights on every row,
+ *                  the adapter fused in on the MASK rows.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -385,6 +387,53 @@ isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t ran
                           const void* A_t, const void* B_t, const int32_t* mask_rows,
                           int32_t n_mask, float scale, void* Y, void* workspace, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * isd_gated_linear -- one whole projection of an R-ISD layer: the base
+ * weights on every row, plus the rank-r adapter on the MASK rows.
+ *
+ * Definition ("自省扩散语言模型的 token 生成机制与工程实践", section "Token 生成
+ * 的核心参数与验收机制"; I-DLM project page, R-ISD card): the verifying
+ * (CLEAN) rows run the base weights alone, which is what keeps their output
+ * equal to the base model's; the MASK rows add the gated adapter:
+ *
+ *   Y[m][:] = X[m][:] @ W + gate[m] * scale * (X[m][:] @ A) @ B
+ *
+ * with gate[m] = 1 for m in mask_rows[0..n_mask-1], else 0.  Layouts are those
+ * a linear layer stores:
+ *   X    [rows][d_in]    bf16   input activations
+ *   W_t  [d_out][d_in]   bf16   base weight (W transposed)
+ *   A_t  [rank][d_in]    bf16   adapter down projection (A transposed)
+ *   B_t  [d_out][rank]   bf16   adapter up projection (B transposed)
+ *   Y    [rows][d_out]   bf16   output, every element written; must not
+ *                               overlap X
+ *   mask_rows [n_mask] int32    row indices in [0, rows)
+ *
+ * rank == 0 runs the base projection alone (A_t, B_t and mask_rows are not
+ * read and may be NULL); rank == 128 runs the gated one.  Arithmetic: bf16
+ * operands on the matrix cores, fp32 sums, one rounding to bf16 at the end;
+ * the adapter's rank-r intermediate is summed in fp32, scaled, and rounded
+ * once to bf16 before the second product.  A row outside the gate comes out
+ * bit for bit equal to the rank == 0 call's row of the same shape (the sums
+ * over W run in an order fixed by (rows, d_in, d_out) alone), provided B_t is
+ * finite.
+ *
+ * Supported: 1 <= rows <= 65536, d_in % 256 == 0, d_out % 128 == 0, rank in
+ * {0, 128}, 0 <= n_mask <= rows, scale not NaN or infinite.  Workspace: at
+ * least isd_gated_linear_workspace_bytes() bytes (0 for an unsupported
+ * shape); its first 4 bytes are a flag word that the caller zeroes before
+ * the first call (ISD_FLAG_ROW_RANGE: a gated row outside [0, rows) is
+ * skipped).  A row listed twice is
+ * adapted once.  Errors: ISD_ERR_SHAPE, ISD_ERR_UNSUPPORTED, ISD_ERR_NULL,
+ * ISD_ERR_ALIGNMENT (every pointer 16-byte aligned), ISD_ERR_WORKSPACE,
+ * ISD_ERR_HIP.
+ */
+size_t isd_gated_linear_workspace_bytes(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank,
+                                        int32_t n_mask);
+isd_status isd_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
+                            const void* W_t, const void* A_t, const void* B_t, const int32_t* mask_rows,
+                            int32_t n_mask, float scale, void* Y, void* workspace, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* Text for a status code (static storage). */
 const char* isd_status_string(isd_status status);

@@ -27,7 +27,7 @@ STATUS = {0: "ISD_OK", 1: "ISD_ERR_NULL", 2: "ISD_ERR_SHAPE", 3: "ISD_ERR_DTYPE"
 # Every symbol include/isd.h declares.
 EXPORTS = ("isd_workspace_bytes", "isd_workspace_init", "isd_read_flags", "isd_attention",
            "isd_accept", "kv_commit", "isd_accept_commit", "isd_propose", "isd_loop_advance", "isd_lora_workspace_bytes",
-           "isd_lora_delta",
+           "isd_lora_delta", "isd_gated_linear_workspace_bytes", "isd_gated_linear",
            "isd_status_string", "isd_last_error", "isd_abi_version")
 PROPOSE_SAMPLE, PROPOSE_ARGMAX = 0, 1
 LOOP_VERIFY, LOOP_REPROPOSE = 0, 1
@@ -91,6 +91,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "isd_loop_advance": (I32, [SP, P, P, P, P, P, P, P, P, P, P]),
         "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
         "isd_lora_delta": (I32, [I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
+        "isd_gated_linear_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
+        "isd_gated_linear": (I32, [I32, I32, I32, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
         "isd_status_string": (ctypes.c_char_p, [I32]),
         "isd_last_error": (ctypes.c_char_p, []),
         "isd_abi_version": (I32, []),
@@ -339,3 +341,28 @@ def isd_lora_delta(X, A_t, B_t, mask_rows, Y, workspace, scale: float = 1.0, str
         _ptr(B_t, "B_t", bf, d_out * rank), _ptr(mask_rows, "mask_rows", torch.int32), mask_rows.numel(),
         float(scale), _ptr(Y, "Y", bf, rows * d_out), _ptr(workspace, "workspace", torch.uint8),
         workspace.numel(), _stream(stream))
+
+
+def isd_gated_linear_workspace_bytes(rows: int, d_in: int, d_out: int, rank: int, n_mask: int) -> int:
+    return int(LIB.isd_gated_linear_workspace_bytes(rows, d_in, d_out, rank, n_mask))
+
+
+def isd_gated_linear(X, W_t, Y, workspace, A_t=None, B_t=None, mask_rows=None, scale: float = 1.0,
+                     stream=None) -> None:
+    """Y = X @ W_t.T, plus scale * (X[m] @ A_t.T) @ B_t.T on the gated rows m when an
+    adapter is given (see include/isd.h)."""
+    rows, d_in = X.shape
+    d_out = W_t.shape[0]
+    bf = torch.bfloat16
+    if A_t is None:
+        rank, a, b, m, n_mask = 0, None, None, None, 0
+    else:
+        rank = A_t.shape[0]
+        a = _ptr(A_t, "A_t", bf, rank * d_in)
+        b = _ptr(B_t, "B_t", bf, d_out * rank)
+        n_mask = mask_rows.numel()
+        m = _ptr(mask_rows, "mask_rows", torch.int32)
+    _call("isd_gated_linear",
+          rows, d_in, d_out, rank, _ptr(X, "X", bf), _ptr(W_t, "W_t", bf, d_out * d_in), a, b, m, n_mask,
+          float(scale), _ptr(Y, "Y", bf, rows * d_out), _ptr(workspace, "workspace", torch.uint8),
+          workspace.numel(), _stream(stream))

@@ -25,7 +25,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libisd.so")
 ARCH = "gfx950"
 
-SOURCES = ["isd_api.cpp", "attention.hip", "accept.hip", "commit.hip", "propose.hip", "loop.hip", "lora.hip"]
+SOURCES = ["isd_api.cpp", "attention.hip", "accept.hip", "commit.hip", "propose.hip", "loop.hip", "lora.hip", "gated_linear.hip"]
 
 
 def hipcc() -> str:

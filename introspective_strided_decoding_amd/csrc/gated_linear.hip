@@ -1,0 +1,305 @@
+// One projection of an R-ISD layer (isd_gated_linear):
+//
+//   Y[m] = X[m] W^T + gate[m] * scale * (X[m] A^T) B^T
+//
+// The adapter's second product rides in the base product's k loop: with
+// T[m] = bf16(gate[m] * scale * X[m] A^T) (zero on CLEAN rows), Y is one
+// product of [X | T] with [W | B] over d_in + rank columns.
+//
+//   lora_down   T_part[kc][g][r] = sum over a 256-wide k chunk of X[row(g)] A^T
+//               (the same kernel as isd_lora_delta's), clearing T on the side
+//   gl_scatter  T[row(g)] = bf16(scale * sum_kc T_part[kc][g]) for gated g
+//   gl_gemm     the product, bf16 matrix-core operands, fp32 sums; the rank
+//               columns come first, so a row whose T is zero enters the base
+//               columns with the same +0 accumulators as the base-only call
+//               and leaves bit for bit equal to it
+//   gl_reduce   only when k is split: Y = bf16(sum of the split partials in
+//               split order)
+//
+// gl_gemm tiling: a workgroup owns a BM x BN tile of Y^T (BM rows of X, BN rows
+// of W), 4 waves in 2 x 2, each wave (BM/2) x (BN/2) as 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16.  k advances 64 at a time: the next block's 16-byte
+// chunks are loaded into registers while the current one is multiplied out of
+// LDS, then staged into the other LDS buffer (one barrier per block).
+#include "device_common.hpp"
+#include "isd_internal.hpp"
+
+namespace isd {
+namespace {
+
+constexpr int kBK = 64;          // k per block: one 128-byte line of every bf16 row
+constexpr int kGlThreads = 256;
+constexpr int kRank = 128;
+
+__device__ __forceinline__ bf16x8 as_b8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Byte offset of 16-byte chunk c of row r in a [rows][64] bf16 LDS tile.  The
+// chunk index is XORed with (r & 7) ^ ((r >> 3) & 1): a matrix-core operand
+// read (16 consecutive rows, one chunk each) and a staging write (the 8 chunks
+// of two rows) both touch every bank once.
+__device__ __forceinline__ int swz(int r, int c) { return (r * 8 + (c ^ (r & 7) ^ ((r >> 3) & 1))) * 16; }
+
+// vmcnt(N) alone (lgkmcnt and expcnt left at their maximum), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS reuse without a memory fence: a fence would also
+// wait for this wave's loads still streaming into later stages.  The wave's
+// own LDS reads are complete first; the asm is a compiler memory barrier too.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+template <int BM, int BN, int ST>
+__global__ __launch_bounds__(kGlThreads) void gl_gemm(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int K, const uint16_t* __restrict__ T,
+    const uint16_t* __restrict__ Bt, int R, int M, int N, int m_tiles, int splits, uint16_t* __restrict__ Y,
+    float* __restrict__ part) {
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int IX = BM / 32, IW = BN / 32;    // 1 KB direct-to-LDS loads per wave per block
+  constexpr int kStageBytes = (BM + BN) * kBK * 2;
+  __shared__ __align__(16) uint8_t sm[ST * kStageBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Workgroups are handed to the 8 XCDs round robin by id: renumber so that
+  // consecutive logical tiles (the m tiles of one W slice) share an XCD's L2.
+  const int G = gridDim.x, b = blockIdx.x;
+  const int xcd = b & 7, per = G >> 3, extra = G & 7;
+  const int l = xcd * per + min(xcd, extra) + (b >> 3);
+  const int mi = l % m_tiles, rest = l / m_tiles;
+  const int s = rest % splits, ni = rest / splits;
+  const int m0 = mi * BM, n0 = ni * BN;
+
+  const int kb_base = K / kBK;
+  const int b0 = s * kb_base / splits, b1 = (s + 1) * kb_base / splits;
+  const int n_ext = s == 0 ? R / kBK : 0;
+  const int nkb = n_ext + (b1 - b0);
+
+  // A load instruction moves 8 rows of 128 bytes: lane i lands at byte 16 i of
+  // the 1 KB it writes, i.e. row i/8, physical chunk i%8, so it fetches the
+  // logical chunk that the swizzle puts there.
+  const int lrow = lane >> 3;
+  auto issue = [&](int j) {
+    const bool ext = j < n_ext;
+    const uint16_t* xs = ext ? T : X;
+    const uint16_t* ws = ext ? Bt : W;
+    const int ld = ext ? R : K;
+    const int k0 = (ext ? j : b0 + j - n_ext) * kBK;
+    uint8_t* st = sm + (j % ST) * kStageBytes;
+#pragma unroll
+    for (int q = 0; q < IX; ++q) {
+      const int r = wave * (BM / 4) + q * 8 + lrow;
+      const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 1);
+      const int row = min(m0 + r, M - 1);     // rows past M are computed, never stored
+      __builtin_amdgcn_global_load_lds((gptr_t)(xs + size_t(row) * ld + k0 + c * 8),
+                                       (lptr_t)(st + (wave * (BM / 4) + q * 8) * 128), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < IW; ++q) {
+      const int r = wave * (BN / 4) + q * 8 + lrow;
+      const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 1);
+      __builtin_amdgcn_global_load_lds((gptr_t)(ws + size_t(n0 + r) * ld + k0 + c * 8),
+                                       (lptr_t)(st + BM * 128 + (wave * (BN / 4) + q * 8) * 128), 16, 0, 0);
+    }
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;
+  const int fr = lane & 31, fh = lane >> 5;
+  f32x16 acc[FN][FM];
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int c = 0; c < FM; ++c) acc[a][c] = f32x16{};
+  auto compute = [&](int j) {
+    const uint8_t* base = sm + (j % ST) * kStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int c = ks * 2 + fh;
+      bf16x8 xf[FM], wf[FN];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) xf[f] = as_b8(*reinterpret_cast<const u32x4*>(base + swz(wm * WM + f * 32 + fr, c)));
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        wf[f] = as_b8(*reinterpret_cast<const u32x4*>(base + BM * 128 + swz(wn * WN + f * 32 + fr, c)));
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int c2 = 0; c2 < FM; ++c2) acc[a][c2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[a], xf[c2], acc[a][c2], 0, 0, 0);
+    }
+  };
+
+  // ST-stage ring: blocks j+1 .. j+ST-1 are in flight while block j is
+  // multiplied.  Per iteration: wait for this wave's loads of block j, barrier
+  // (block j visible to all waves, and every wave is done with block j-1),
+  // refill block j-1's stage with block j+ST-1, multiply block j.
+#pragma unroll
+  for (int j = 0; j < ST - 1; ++j)
+    if (j < nkb) issue(j);
+  for (int j = 0; j < nkb; ++j) {
+    const int newer = min(nkb - 1, j + ST - 2) - j;     // blocks issued after j
+    if (newer >= ST - 2) wait_vm<(ST - 2) * (IX + IW)>();
+    else if (ST > 3 && newer == 1) wait_vm<(IX + IW)>();
+    else wait_vm<0>();
+    lds_barrier();
+    if (j + ST - 1 < nkb) issue(j + ST - 1);
+    compute(j);
+  }
+
+  // acc[a][c] holds Y^T block (n, m): this lane's column m = fr, rows
+  // n = (v/4)*8 + fh*4 + v%4, so each v/4 group is 4 consecutive outputs of one row.
+#pragma unroll
+  for (int c = 0; c < FM; ++c) {
+    const int m = m0 + wm * WM + c * 32 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int a = 0; a < FN; ++a) {
+      const int nb = n0 + wn * WN + a * 32 + fh * 4;
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int n = nb + v4 * 8;
+        const float y0 = acc[a][c][4 * v4], y1 = acc[a][c][4 * v4 + 1];
+        const float y2 = acc[a][c][4 * v4 + 2], y3 = acc[a][c][4 * v4 + 3];
+        if (splits == 1) {
+          *reinterpret_cast<uint2*>(Y + size_t(m) * N + n) =
+              make_uint2(uint32_t(f32_to_bf16_bits(y0)) | (uint32_t(f32_to_bf16_bits(y1)) << 16),
+                         uint32_t(f32_to_bf16_bits(y2)) | (uint32_t(f32_to_bf16_bits(y3)) << 16));
+        } else {
+          *reinterpret_cast<f32x4*>(part + (size_t(s) * M + m) * N + n) = f32x4{y0, y1, y2, y3};
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void gl_reduce(const f32x4* __restrict__ part, int splits, int count4,
+                                                 uint2* __restrict__ Y) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= count4) return;
+  f32x4 v = part[i];
+  for (int s = 1; s < splits; ++s) v += part[size_t(s) * count4 + i];
+  Y[i] = make_uint2(uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16),
+                    uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16));
+}
+
+// One thread per (gated row, rank column); part is [kchunks][m_pad][128].
+__global__ __launch_bounds__(256) void gl_scatter(const float* __restrict__ part, int kchunks, int m_pad,
+                                                  const int32_t* __restrict__ mask_rows, int n_mask, int rows,
+                                                  float scale, uint16_t* __restrict__ T) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int g = e / kRank, r = e % kRank;
+  if (g >= n_mask) return;
+  const int row = mask_rows[g];
+  if (row < 0 || row >= rows) return;        // flagged by lora_down
+  // eight independent running sums, so eight loads are in flight at a time
+  const float* p = part + size_t(g) * kRank + r;
+  const size_t stride = size_t(m_pad) * kRank;
+  float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int kc = 0;
+  for (; kc + 8 <= kchunks; kc += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] += p[(kc + u) * stride];
+  for (int u = 0; kc < kchunks; ++kc, ++u) t[u] += p[kc * stride];
+  const float sum = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+  T[size_t(row) * kRank + r] = f32_to_bf16_bits(scale * sum);
+}
+
+}  // namespace
+
+// Tile shape, stages and k split per shape, from timings on MI355X of every
+// instance over the projections of an 8B-class layer at 224 and 896 rows.
+// Loads into LDS, not the matrix cores, bound these kernels (a variant without
+// the products takes as long), so the plan trades bytes per flop (tile size)
+// against filling all 256 compute units (tile count, split).
+GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out) {
+  GlPlan p;
+  const int kb = d_in / kBK;
+  const long t128 = long((rows + 127) / 128) * (d_out / 128);
+  auto split_to = [&](long tiles) {
+    while (tiles * p.splits < 256 && kb / (2 * p.splits) >= 8) p.splits *= 2;
+  };
+  if (t128 >= 384) {
+    p.stages = 2;                      // two workgroups per CU
+  } else if (t128 >= 160) {
+    if (d_in >= 8192) {
+      p.stages = 2;
+      p.splits = 2;
+    }
+  } else if (d_out <= 2048) {
+    p.bm = 64;
+    split_to(long((rows + 63) / 64) * (d_out / 64));
+  } else {
+    split_to(t128);
+  }
+  return p;
+}
+
+GlLayout gl_layout(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, int32_t n_mask) {
+  GlLayout L;
+  L.plan = gl_plan(rows, d_in, d_out);
+  size_t off = kHeaderBytes;
+  if (rank > 0) {
+    L.t = off;
+    off += (size_t(rows) * rank * 2 + 255) / 256 * 256;
+    L.down = off;
+    off += size_t(d_in / 256) * size_t((n_mask + 31) / 32 * 32) * rank * 4;
+    off = (off + 255) / 256 * 256;
+  }
+  if (L.plan.splits > 1) {
+    L.split = off;
+    off += size_t(L.plan.splits) * rows * d_out * 4;
+  }
+  L.total = (off + 255) / 256 * 256;
+  return L;
+}
+
+hipError_t launch_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
+                               const void* W_t, const void* A_t, const void* B_t, const int32_t* mask_rows,
+                               int32_t n_mask, float scale, void* Y, char* ws, hipStream_t stream) {
+  if (n_mask == 0) rank = 0;     // no gated row: the base projection, bit for bit
+  const GlLayout L = gl_layout(rows, d_in, d_out, rank, n_mask);
+  const uint16_t* T = nullptr;
+  if (rank > 0) {
+    uint16_t* t = reinterpret_cast<uint16_t*>(ws + L.t);
+    float* down = reinterpret_cast<float*>(ws + L.down);
+    hipError_t e = launch_lora_down(X, A_t, mask_rows, n_mask, rows, d_in, down,
+                                    reinterpret_cast<uint32_t*>(ws), t, size_t(rows) * rank * 2, stream);
+    if (e != hipSuccess) return e;
+    const int m_pad = (n_mask + 31) / 32 * 32;
+    hipLaunchKernelGGL(gl_scatter, dim3((n_mask * kRank + 255) / 256), dim3(256), 0, stream, down, d_in / 256,
+                       m_pad, mask_rows, n_mask, rows, scale, t);
+    T = t;
+  }
+  const GlPlan& p = L.plan;
+  float* part = p.splits > 1 ? reinterpret_cast<float*>(ws + L.split) : nullptr;
+  const int R = rank > 0 ? kRank : 0;
+  const auto* x = static_cast<const uint16_t*>(X);
+  const auto* w = static_cast<const uint16_t*>(W_t);
+  const auto* bt = static_cast<const uint16_t*>(B_t);
+  auto* y = static_cast<uint16_t*>(Y);
+  if (p.bm == 128) {
+    const int mt = (rows + 127) / 128;
+    const dim3 grid(mt * (d_out / 128) * p.splits);
+    if (p.stages == 2)
+      hipLaunchKernelGGL((gl_gemm<128, 128, 2>), grid, dim3(kGlThreads), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
+                         mt, p.splits, y, part);
+    else
+      hipLaunchKernelGGL((gl_gemm<128, 128, 4>), grid, dim3(kGlThreads), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
+                         mt, p.splits, y, part);
+  } else {
+    const int mt = (rows + 63) / 64;
+    hipLaunchKernelGGL((gl_gemm<64, 64, 4>), dim3(mt * (d_out / 64) * p.splits), dim3(kGlThreads), 0, stream, x, w,
+                       d_in, T, bt, R, rows, d_out, mt, p.splits, y, part);
+  }
+  if (p.splits > 1) {
+    const int count4 = rows * d_out / 4;
+    hipLaunchKernelGGL(gl_reduce, dim3((count4 + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<const f32x4*>(part), p.splits, count4, reinterpret_cast<uint2*>(Y));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace isd

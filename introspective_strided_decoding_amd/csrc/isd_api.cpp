@@ -159,7 +159,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 5; }
+int32_t isd_abi_version(void) { return 6; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {
@@ -352,6 +352,31 @@ isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t ran
   hipError_t e = launch_lora(rows, d_in, d_out, rank, X, A_t, B_t, mask_rows, n_mask, scale, Y,
                              static_cast<char*>(workspace), stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_lora_delta");
+}
+
+size_t isd_gated_linear_workspace_bytes(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank,
+                                        int32_t n_mask) {
+  if (rows < 1 || rows > kGlMaxRows || d_in < 256 || d_in % 256 || d_out < 128 || d_out % 128) return 0;
+  if ((rank != 0 && rank != 128) || n_mask < 0 || n_mask > rows) return 0;
+  return gl_layout(rows, d_in, d_out, rank, n_mask).total;
+}
+
+isd_status isd_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
+                            const void* W_t, const void* A_t, const void* B_t, const int32_t* mask_rows,
+                            int32_t n_mask, float scale, void* Y, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (rows < 1 || d_in < 1 || d_out < 1 || rank < 0 || n_mask < 0 || n_mask > rows) return ISD_ERR_SHAPE;
+  if (rows > kGlMaxRows || d_in % 256 || d_out % 128 || (rank != 0 && rank != 128)) return ISD_ERR_UNSUPPORTED;
+  if (!(scale == scale) || scale - scale != 0.f) return ISD_ERR_SHAPE;
+  if (!X || !W_t || !Y || !workspace) return ISD_ERR_NULL;
+  if (rank > 0 && (!A_t || !B_t || (n_mask > 0 && !mask_rows))) return ISD_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W_t) || !aligned16(Y) || !aligned16(workspace) ||
+      (rank > 0 && (!aligned16(A_t) || !aligned16(B_t))))
+    return ISD_ERR_ALIGNMENT;
+  if (ws_bytes < gl_layout(rows, d_in, d_out, rank, n_mask).total) return ISD_ERR_WORKSPACE;
+  hipError_t e = launch_gated_linear(rows, d_in, d_out, rank, X, W_t, A_t, B_t, mask_rows, n_mask, scale, Y,
+                                     static_cast<char*>(workspace), stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_gated_linear");
 }
 
 }  // extern "C"

@@ -160,4 +160,32 @@ hipError_t launch_lora(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, 
                        const void* A, const void* Bm, const int32_t* mask_rows, int32_t n_mask,
                        float scale, void* Y, char* ws, hipStream_t stream);
 
+hipError_t launch_lora_down(const void* X, const void* A_t, const int32_t* mask_rows, int32_t n_mask,
+                            int32_t rows, int32_t d_in, float* part, uint32_t* flags, void* zero16,
+                            size_t zero_bytes, hipStream_t stream);
+
+constexpr int32_t kGlMaxRows = 1 << 16;   // rows of one gated projection call
+
+// Gated projection: tile shape and k split, a function of the shape alone so a
+// gated call and the base-only call of the same shape sum in the same order.
+struct GlPlan {
+  int bm = 128;       // 128: 128 x 128 tiles; 64: 64 x 64 tiles
+  int stages = 4;     // LDS ring depth (128 x 128 tiles: 2 or 4; 64 x 64 tiles: 4)
+  int splits = 1;     // k split into this many ranges, summed by a second kernel
+};
+GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out);
+
+struct GlLayout {
+  size_t t = 0;       // bf16 [rows][rank]: gated rows' scaled down-projection, zero elsewhere
+  size_t down = 0;    // float [d_in/256][n_mask padded to 32][rank]
+  size_t split = 0;   // float [splits][rows][d_out]
+  size_t total = 0;
+  GlPlan plan;
+};
+GlLayout gl_layout(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, int32_t n_mask);
+
+hipError_t launch_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
+                               const void* W_t, const void* A_t, const void* B_t, const int32_t* mask_rows,
+                               int32_t n_mask, float scale, void* Y, char* ws, hipStream_t stream);
+
 }  // namespace isd

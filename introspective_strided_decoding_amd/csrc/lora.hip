@@ -36,23 +36,32 @@ __device__ __forceinline__ int gated_row(const int32_t* __restrict__ mask_rows, 
   return row;
 }
 
+// zero16/n16: an optional buffer of n16 16-byte words that the grid clears on
+// the side (the gated projection's full-height intermediate; null otherwise).
 __global__ __launch_bounds__(256) void lora_down(const uint16_t* __restrict__ X, const uint16_t* __restrict__ At,
                                                  const int32_t* __restrict__ mask_rows, int n_mask, int rows,
                                                  int d_in, int m_pad, float* __restrict__ part,
-                                                 uint32_t* __restrict__ flags) {
+                                                 uint32_t* __restrict__ flags, u32x4* __restrict__ zero16,
+                                                 int n16) {
   const int kc = blockIdx.x, mb = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int m = mb * 32 + col;
-  const int row = gated_row(mask_rows, m, n_mask, rows, flags, wave == 0 && h == 0 && kc == 0);
   const int n = wave * 32 + col;
   const uint16_t* arow = At + size_t(n) * d_in + kc * kKChunk + h * 8;
-  const uint16_t* xrow = X + size_t(row < 0 ? 0 : row) * d_in + kc * kKChunk + h * 8;
+  // the adapter rows first: they do not wait for the gated row's index
   u32x4 a[kKChunk / 16], b[kKChunk / 16];
 #pragma unroll
-  for (int s = 0; s < kKChunk / 16; ++s) {
-    a[s] = *reinterpret_cast<const u32x4*>(arow + s * 16);
-    b[s] = (row >= 0) ? *reinterpret_cast<const u32x4*>(xrow + s * 16) : u32x4{0, 0, 0, 0};
+  for (int s = 0; s < kKChunk / 16; ++s) a[s] = *reinterpret_cast<const u32x4*>(arow + s * 16);
+  const int m = mb * 32 + col;
+  const int row = gated_row(mask_rows, m, n_mask, rows, flags, wave == 0 && h == 0 && kc == 0);
+  const uint16_t* xrow = X + size_t(row < 0 ? 0 : row) * d_in + kc * kKChunk + h * 8;
+  // unconditional loads (a row outside the gate reads row 0 and is zeroed after), so all
+  // of them are in flight at once
+#pragma unroll
+  for (int s = 0; s < kKChunk / 16; ++s) b[s] = *reinterpret_cast<const u32x4*>(xrow + s * 16);
+  if (row < 0) {
+#pragma unroll
+    for (int s = 0; s < kKChunk / 16; ++s) b[s] = u32x4{0, 0, 0, 0};
   }
   f32x16 acc = f32x16{};
 #pragma unroll
@@ -62,6 +71,8 @@ __global__ __launch_bounds__(256) void lora_down(const uint16_t* __restrict__ X,
 #pragma unroll
   for (int v4 = 0; v4 < 4; ++v4)
     *reinterpret_cast<f32x4*>(dst + v4 * 8) = f32x4{acc[4 * v4], acc[4 * v4 + 1], acc[4 * v4 + 2], acc[4 * v4 + 3]};
+  for (int i = (mb * gridDim.x + kc) * 256 + threadIdx.x; i < n16; i += gridDim.x * gridDim.y * 256)
+    zero16[i] = u32x4{0, 0, 0, 0};
 }
 
 __global__ __launch_bounds__(256) void lora_reduce(const float* __restrict__ part, int kchunks, int count,
@@ -144,12 +155,22 @@ hipError_t launch_lora(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, 
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
   hipLaunchKernelGGL(lora_down, dim3(kchunks, m_blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(A), mask_rows, n_mask, rows,
-                     d_in, m_pad, part, flags);
+                     d_in, m_pad, part, flags, nullptr, 0);
   const int count = m_pad * rank;
   hipLaunchKernelGGL(lora_reduce, dim3((count + 255) / 256), dim3(256), 0, stream, part, kchunks, count, t_hi, t_lo);
   hipLaunchKernelGGL(lora_up, dim3(d_out / kOBlock, m_blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(Bm), t_hi, t_lo, mask_rows, n_mask, rows, d_out, scale,
                      static_cast<uint16_t*>(Y));
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_down(const void* X, const void* A_t, const int32_t* mask_rows, int32_t n_mask,
+                            int32_t rows, int32_t d_in, float* part, uint32_t* flags, void* zero16,
+                            size_t zero_bytes, hipStream_t stream) {
+  const int m_blocks = (n_mask + 31) / 32;
+  hipLaunchKernelGGL(lora_down, dim3(d_in / kKChunk, m_blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(A_t), mask_rows, n_mask, rows,
+                     d_in, m_blocks * 32, part, flags, static_cast<u32x4*>(zero16), int(zero_bytes / 16));
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 5
+    assert LIB.isd_abi_version() == 6
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"
@@ -204,3 +204,34 @@ def test_lora_validation():
     assert call(Y=MISALIGNED) == 7
     assert call(wsb=100) == 4
     assert call(scale=float("nan")) == 2
+
+
+def test_gated_linear_validation():
+    ws = LIB.isd_gated_linear_workspace_bytes
+    assert ws(896, 4096, 4096, 128, 512) > ws(896, 4096, 4096, 0, 0) > 0
+    for bad in ((0, 4096, 4096, 0, 0), (70000, 4096, 4096, 0, 0), (8, 4000, 4096, 0, 0), (8, 4096, 4000, 0, 0),
+                (8, 4096, 4096, 64, 4), (8, 4096, 4096, 128, 9), (8, 4096, 4096, 128, -1)):
+        assert ws(*bad) == 0, bad
+    n = ws(224, 4096, 1024, 128, 128)
+    ok = dict(rows=224, d_in=4096, d_out=1024, rank=128, X=FAKE, W=FAKE, A=FAKE, B=FAKE, m=FAKE, n_mask=128,
+              scale=1.0, Y=FAKE, ws=FAKE, wsb=n)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return LIB.isd_gated_linear(a["rows"], a["d_in"], a["d_out"], a["rank"], a["X"], a["W"], a["A"], a["B"],
+                                    a["m"], a["n_mask"], a["scale"], a["Y"], a["ws"], a["wsb"], None)
+    assert call(wsb=n - 1) == 4                      # everything else valid
+    assert call(rows=0) == 2
+    assert call(n_mask=225) == 2
+    assert call(scale=float("nan")) == 2
+    assert call(scale=float("inf")) == 2
+    assert call(rank=64) == 5
+    assert call(d_in=4000) == 5
+    assert call(d_out=1000) == 5
+    assert call(rows=70000, n_mask=0) == 5
+    for k in ("X", "W", "Y", "ws", "A", "B", "m"):
+        assert call(**{k: None}) == 1, k
+    assert call(rank=0, A=None, B=None, m=None, n_mask=0, wsb=8) == 4   # base only: no adapter pointers needed
+    assert call(m=None, n_mask=0, wsb=8) == 4                          # an empty gate needs no row list
+    for k in ("X", "W", "A", "B", "Y", "ws"):
+        assert call(**{k: MISALIGNED}) == 7, k

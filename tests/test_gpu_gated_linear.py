@@ -1,0 +1,171 @@
+"""isd_gated_linear on the GPU vs the float64 oracle (one whole R-ISD projection).
+
+Bar, per element, from the arithmetic the header states (bf16 operands, fp32 sums,
+the adapter's rank-128 intermediate rounded once to bf16, one final bf16 rounding):
+
+  |y - y_exact| <= ub |y_exact| + (d_in + r) u (|X||W| + |T||B|)
+                   + (ub |T| + d_in u |scale| |X||A|) |B|
+
+with u = 2^-24 (fp32), ub = 2^-8 (bf16) and T = scale X A on the gated rows.  The
+relative RMS error must also stay at the level of one bf16 rounding.  Rows outside
+the gate must equal the base-only call (rank 0) bit for bit: the property that lets
+the CLEAN rows verify with the base model's own numbers.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.lora import gated_projection
+from parity import needs_gpu
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+U32, UB = 2.0 ** -24, 2.0 ** -8      # unit roundoff of fp32 (24-bit significand) and bf16 (8-bit)
+
+
+def _bf16(rng, shape, std=1.0):
+    return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(torch.bfloat16)
+
+
+def _inputs(rows, d_in, d_out, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = _bf16(rng, (rows, d_in))
+    Wt = _bf16(rng, (d_out, d_in), 0.02)
+    At = _bf16(rng, (128, d_in), 0.02)
+    Bt = _bf16(rng, (d_out, 128), 0.02)
+    return X, Wt, At, Bt
+
+
+def _run(X, Wt, At, Bt, mask, scale=1.0, guard=64):
+    """Returns (Y, flags); Y is written into a buffer with a guard tail that must stay untouched."""
+    from introspective_strided_decoding_amd import _lib
+    rows, d_in = X.shape
+    d_out = Wt.shape[0]
+    rank = 0 if At is None else 128
+    n_mask = 0 if mask is None else len(mask)
+    n = _lib.isd_gated_linear_workspace_bytes(rows, d_in, d_out, rank, n_mask)
+    assert n > 0
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    buf = torch.full((rows * d_out + guard,), 7.0, dtype=torch.bfloat16, device="cuda")
+    Y = buf[:rows * d_out].view(rows, d_out)
+    kw = {}
+    if rank:
+        kw = dict(A_t=At.cuda(), B_t=Bt.cuda(), mask_rows=torch.tensor(mask, dtype=torch.int32, device="cuda"),
+                  scale=scale)
+    _lib.isd_gated_linear(X.cuda(), Wt.cuda(), Y, ws, **kw)
+    torch.cuda.synchronize()
+    assert torch.all(buf[rows * d_out:] == 7.0), "write past the output"
+    flags = int(ws[:4].view(torch.int32).item())
+    return Y.cpu(), flags
+
+
+def _check(Y, X, Wt, At, Bt, mask, scale, sample=None):
+    """Compare rows `sample` (all rows if None) of Y against the oracle, with the bound above."""
+    rows = X.shape[0]
+    idx = np.arange(rows) if sample is None else np.asarray(sample)
+    gate = set(int(m) for m in (mask or []) if 0 <= m < rows)
+    sub_mask = [i for i, r in enumerate(idx) if int(r) in gate]
+    x = X[idx].double().numpy()
+    w = Wt.double().numpy().T
+    a = None if At is None else At.double().numpy().T
+    b = None if Bt is None else Bt.double().numpy().T
+    want = gated_projection(x, w, a, b, sub_mask, scale)
+    got = Y[idx].double().numpy()
+    d_in = x.shape[1]
+    ax, aw = np.abs(x), np.abs(w)
+    bound = UB * np.abs(want) + (d_in + 128) * U32 * (ax @ aw)
+    if At is not None:
+        g = np.zeros((len(idx), 1))
+        g[sub_mask] = 1.0
+        t = g * scale * (x @ a)
+        ab = np.abs(b)
+        bound = bound + (d_in + 128) * U32 * (np.abs(t) @ ab) \
+            + (UB * np.abs(t) + g * d_in * U32 * abs(scale) * (ax @ np.abs(a))) @ ab
+    bound = bound * 1.01
+    err = np.abs(got - want)
+    assert np.all(err <= bound), (float((err / bound).max()), np.unravel_index(np.argmax(err / bound), err.shape))
+    rel_rms = np.sqrt(np.mean((got - want) ** 2) / np.mean(want ** 2))
+    assert rel_rms < 4e-3, rel_rms
+    return rel_rms
+
+
+# (rows, d_in, d_out, gated rows), with the tiling the library picks for each: 64 x 64
+# tiles, one k range; 64 x 64 tiles again; 64 x 64 tiles with the k range split in 4;
+# 128 x 128 tiles with k split in 2 over a ragged last row tile; 128 x 128 tiles, four-stage
+# ring, ragged; 64 x 64 tiles with every row gated; one row gated; 128 x 128 tiles with a
+# two-stage ring (two workgroups per CU).
+CASES = [
+    (20, 256, 128, [1, 3, 4, 17]),
+    (70, 512, 384, list(range(0, 70, 2))),
+    (40, 2048, 128, list(range(3, 40, 3))),
+    (300, 1024, 5376, [r for r in range(300) if r % 7 >= 3]),
+    (333, 512, 8192, [r for r in range(333) if r % 5 == 1]),
+    (33, 256, 256, list(range(33))),
+    (64, 768, 640, [63]),
+    (300, 256, 16384, list(range(1, 300, 3))),
+]
+
+
+@pytest.mark.parametrize("rows,d_in,d_out,mask", CASES)
+def test_gated_projection_small(rows, d_in, d_out, mask):
+    X, Wt, At, Bt = _inputs(rows, d_in, d_out, seed=rows + d_out)
+    Y, flags = _run(X, Wt, At, Bt, mask, scale=0.5)
+    assert flags == 0
+    _check(Y, X, Wt, At, Bt, mask, 0.5)
+    base, _ = _run(X, Wt, None, None, None)
+    _check(base, X, Wt, None, None, None, 1.0)
+    clean = [r for r in range(rows) if r not in set(mask)]
+    assert torch.equal(Y[clean].view(torch.int16), base[clean].view(torch.int16))
+
+
+def test_gated_projection_repeatable_and_duplicate_rows():
+    rows, d_in, d_out = 96, 512, 256
+    X, Wt, At, Bt = _inputs(rows, d_in, d_out, seed=41)
+    mask = [5, 9, 9, 50, 5]
+    Y1, _ = _run(X, Wt, At, Bt, mask)
+    Y2, _ = _run(X, Wt, At, Bt, mask)
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    Y3, _ = _run(X, Wt, At, Bt, [5, 9, 50])
+    assert torch.equal(Y1.view(torch.int16), Y3.view(torch.int16))
+    _check(Y1, X, Wt, At, Bt, mask, 1.0)
+
+
+def test_gated_projection_rows_out_of_range_are_flagged():
+    from introspective_strided_decoding_amd import _lib
+    rows, d_in, d_out = 50, 256, 128
+    X, Wt, At, Bt = _inputs(rows, d_in, d_out, seed=42)
+    Y, flags = _run(X, Wt, At, Bt, [2, 50, -1, 7])
+    assert flags & _lib.FLAG_ROW_RANGE
+    _check(Y, X, Wt, At, Bt, [2, 7], 1.0)
+
+
+def test_gated_projection_empty_gate_is_base():
+    rows, d_in, d_out = 70, 512, 256
+    X, Wt, At, Bt = _inputs(rows, d_in, d_out, seed=43)
+    Y, _ = _run(X, Wt, At, Bt, [])
+    base, _ = _run(X, Wt, None, None, None)
+    assert torch.equal(Y.view(torch.int16), base.view(torch.int16))
+
+
+# The projections of an 8B-class layer (hidden 4096, 32 query and 8 KV heads of 128,
+# MLP 12288) at the stride rows of 32 requests (224 rows, 128 gated) and of 128 requests
+# (896 rows, 512 gated), N = 4: the MASK rows are 3..6 of every request's 7.
+LAYER = {"q": (4096, 4096), "k": (4096, 1024), "gate": (4096, 12288), "down": (12288, 4096)}
+
+
+@pytest.mark.parametrize("batch", [32, 128])
+@pytest.mark.parametrize("proj", list(LAYER))
+def test_gated_projection_r_isd_layer_shapes(batch, proj):
+    d_in, d_out = LAYER[proj]
+    Q, N = 7, 4
+    rows = batch * Q
+    mask = [r * Q + i for r in range(batch) for i in range(N - 1, Q)]
+    X, Wt, At, Bt = _inputs(rows, d_in, d_out, seed=batch + d_in + d_out)
+    Y, flags = _run(X, Wt, At, Bt, mask)
+    assert flags == 0
+    sample = list(range(0, 14)) + list(range(rows - 14, rows)) + list(range(100, rows, 97))
+    _check(Y, X, Wt, At, Bt, mask, 1.0, sample=sample)
+    base, _ = _run(X, Wt, None, None, None)
+    clean = [r * Q + i for r in range(batch) for i in range(N - 1)]
+    assert torch.equal(Y[clean].view(torch.int16), base[clean].view(torch.int16))
