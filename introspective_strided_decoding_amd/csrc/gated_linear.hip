@@ -17,10 +17,10 @@
 //               split order)
 //
 // gl_gemm tiling: a workgroup owns a BM x BN tile of Y^T (BM rows of X, BN rows
-// of W), 4 waves in 2 x 2, each wave (BM/2) x (BN/2) as 32 x 32 blocks of
-// v_mfma_f32_32x32x16_bf16.  k advances 64 at a time: the next block's 16-byte
-// chunks are loaded into registers while the current one is multiplied out of
-// LDS, then staged into the other LDS buffer (one barrier per block).
+// of W), WGM x WGN waves, each (BM/WGM) x (BN/WGN) as 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16.  k advances 64 at a time through a ring of ST LDS
+// stages filled by direct-to-LDS loads (no registers in between), so ST - 1
+// blocks are in flight while one is multiplied.
 #include "device_common.hpp"
 #include "isd_internal.hpp"
 
@@ -28,7 +28,6 @@ namespace isd {
 namespace {
 
 constexpr int kBK = 64;          // k per block: one 128-byte line of every bf16 row
-constexpr int kGlThreads = 256;
 constexpr int kRank = 128;
 
 __device__ __forceinline__ bf16x8 as_b8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -54,13 +53,15 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-template <int BM, int BN, int ST>
-__global__ __launch_bounds__(kGlThreads) void gl_gemm(
+template <int BM, int BN, int ST, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int K, const uint16_t* __restrict__ T,
     const uint16_t* __restrict__ Bt, int R, int M, int N, int m_tiles, int splits, uint16_t* __restrict__ Y,
     float* __restrict__ part) {
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  constexpr int IX = BM / 32, IW = BN / 32;    // 1 KB direct-to-LDS loads per wave per block
+  constexpr int NW = WGM * WGN;                // waves: WGM along X rows, WGN along W rows
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  constexpr int IX = BM / (8 * NW), IW = BN / (8 * NW);    // 1 KB direct-to-LDS loads per wave per block
+  static_assert(IX * 8 * NW == BM && IW * 8 * NW == BN && FM * 32 == WM && FN * 32 == WN, "tile shape");
   constexpr int kStageBytes = (BM + BN) * kBK * 2;
   __shared__ __align__(16) uint8_t sm[ST * kStageBytes];
 
@@ -92,22 +93,22 @@ __global__ __launch_bounds__(kGlThreads) void gl_gemm(
     uint8_t* st = sm + (j % ST) * kStageBytes;
 #pragma unroll
     for (int q = 0; q < IX; ++q) {
-      const int r = wave * (BM / 4) + q * 8 + lrow;
+      const int r = wave * (BM / NW) + q * 8 + lrow;
       const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 1);
       const int row = min(m0 + r, M - 1);     // rows past M are computed, never stored
       __builtin_amdgcn_global_load_lds((gptr_t)(xs + size_t(row) * ld + k0 + c * 8),
-                                       (lptr_t)(st + (wave * (BM / 4) + q * 8) * 128), 16, 0, 0);
+                                       (lptr_t)(st + (wave * (BM / NW) + q * 8) * 128), 16, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < IW; ++q) {
-      const int r = wave * (BN / 4) + q * 8 + lrow;
+      const int r = wave * (BN / NW) + q * 8 + lrow;
       const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 1);
       __builtin_amdgcn_global_load_lds((gptr_t)(ws + size_t(n0 + r) * ld + k0 + c * 8),
-                                       (lptr_t)(st + BM * 128 + (wave * (BN / 4) + q * 8) * 128), 16, 0, 0);
+                                       (lptr_t)(st + BM * 128 + (wave * (BN / NW) + q * 8) * 128), 16, 0, 0);
     }
   };
 
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
   const int fr = lane & 31, fh = lane >> 5;
   f32x16 acc[FN][FM];
 #pragma unroll
@@ -209,24 +210,33 @@ __global__ __launch_bounds__(256) void gl_scatter(const float* __restrict__ part
 
 }  // namespace
 
-// Tile shape, stages and k split per shape, from timings on MI355X of every
-// instance over the projections of an 8B-class layer at 224 and 896 rows.
-// Loads into LDS, not the matrix cores, bound these kernels (a variant without
-// the products takes as long), so the plan trades bytes per flop (tile size)
-// against filling all 256 compute units (tile count, split).
+// Tile shape, waves, stages and k split per shape, from timings on MI355X of
+// every instance over the projections of an 8B-class layer at 224 and 896
+// rows.  Loads into the CUs bound these kernels: a variant without the
+// products takes as long, and plain 16-byte loads into registers stream the
+// same tiles no faster than the direct-to-LDS ones (about 45 GB/s per busy CU
+// from L2 either way).  So the plan trades bytes per flop (tile size) against
+// keeping all 256 CUs busy (tile count, split).
 GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out) {
   GlPlan p;
   const int kb = d_in / kBK;
   const long t128 = long((rows + 127) / 128) * (d_out / 128);
+  const long t256 = d_out % 256 ? 0 : long((rows + 255) / 256) * (d_out / 256);
   auto split_to = [&](long tiles) {
     while (tiles * p.splits < 256 && kb / (2 * p.splits) >= 8) p.splits *= 2;
   };
-  if (t128 >= 384) {
+  if (t256 >= 160 && rows >= 512) {
+    p.bm = 256;                        // 256 x 256 tiles, 8 waves of 128 x 64
+    p.stages = 2;
+    p.waves = 8;
+  } else if (t128 >= 384) {
     p.stages = 2;                      // two workgroups per CU
   } else if (t128 >= 160) {
     if (d_in >= 8192) {
       p.stages = 2;
       p.splits = 2;
+    } else {
+      p.waves = 8;                     // 8 waves of 64 x 32
     }
   } else if (d_out <= 2048) {
     p.bm = 64;
@@ -280,18 +290,25 @@ hipError_t launch_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_
   const auto* w = static_cast<const uint16_t*>(W_t);
   const auto* bt = static_cast<const uint16_t*>(B_t);
   auto* y = static_cast<uint16_t*>(Y);
-  if (p.bm == 128) {
+  if (p.bm == 256) {
+    const int mt = (rows + 255) / 256;
+    hipLaunchKernelGGL((gl_gemm<256, 256, 2, 2, 4>), dim3(mt * (d_out / 256) * p.splits), dim3(512), 0, stream, x, w,
+                       d_in, T, bt, R, rows, d_out, mt, p.splits, y, part);
+  } else if (p.bm == 128) {
     const int mt = (rows + 127) / 128;
     const dim3 grid(mt * (d_out / 128) * p.splits);
     if (p.stages == 2)
-      hipLaunchKernelGGL((gl_gemm<128, 128, 2>), grid, dim3(kGlThreads), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
+      hipLaunchKernelGGL((gl_gemm<128, 128, 2, 2, 2>), grid, dim3(256), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
+                         mt, p.splits, y, part);
+    else if (p.waves == 8)
+      hipLaunchKernelGGL((gl_gemm<128, 128, 4, 2, 4>), grid, dim3(512), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
                          mt, p.splits, y, part);
     else
-      hipLaunchKernelGGL((gl_gemm<128, 128, 4>), grid, dim3(kGlThreads), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
+      hipLaunchKernelGGL((gl_gemm<128, 128, 4, 2, 2>), grid, dim3(256), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
                          mt, p.splits, y, part);
   } else {
     const int mt = (rows + 63) / 64;
-    hipLaunchKernelGGL((gl_gemm<64, 64, 4>), dim3(mt * (d_out / 64) * p.splits), dim3(kGlThreads), 0, stream, x, w,
+    hipLaunchKernelGGL((gl_gemm<64, 64, 4, 2, 2>), dim3(mt * (d_out / 64) * p.splits), dim3(256), 0, stream, x, w,
                        d_in, T, bt, R, rows, d_out, mt, p.splits, y, part);
   }
   if (p.splits > 1) {

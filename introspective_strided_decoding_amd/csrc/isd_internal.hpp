@@ -169,8 +169,9 @@ constexpr int32_t kGlMaxRows = 1 << 16;   // rows of one gated projection call
 // Gated projection: tile shape and k split, a function of the shape alone so a
 // gated call and the base-only call of the same shape sum in the same order.
 struct GlPlan {
-  int bm = 128;       // 128: 128 x 128 tiles; 64: 64 x 64 tiles
-  int stages = 4;     // LDS ring depth (128 x 128 tiles: 2 or 4; 64 x 64 tiles: 4)
+  int bm = 128;       // square tiles of bm x bm outputs: 256, 128 or 64
+  int stages = 4;     // LDS ring depth
+  int waves = 4;      // waves per workgroup: 4 or 8
   int splits = 1;     // k split into this many ranges, summed by a second kernel
 };
 GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out);

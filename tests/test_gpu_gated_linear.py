@@ -92,9 +92,10 @@ def _check(Y, X, Wt, At, Bt, mask, scale, sample=None):
 
 # (rows, d_in, d_out, gated rows), with the tiling the library picks for each: 64 x 64
 # tiles, one k range; 64 x 64 tiles again; 64 x 64 tiles with the k range split in 4;
-# 128 x 128 tiles with k split in 2 over a ragged last row tile; 128 x 128 tiles, four-stage
-# ring, ragged; 64 x 64 tiles with every row gated; one row gated; 128 x 128 tiles with a
-# two-stage ring (two workgroups per CU).
+# 128 x 128 tiles with k split in 2 over a ragged last row tile; 128 x 128 tiles of 8 waves,
+# ragged; 64 x 64 tiles with every row gated; one row gated; 128 x 128 tiles with a
+# two-stage ring (two workgroups per CU); 256 x 256 tiles of 8 waves over a ragged last row
+# tile of 8 rows.
 CASES = [
     (20, 256, 128, [1, 3, 4, 17]),
     (70, 512, 384, list(range(0, 70, 2))),
@@ -104,6 +105,7 @@ CASES = [
     (33, 256, 256, list(range(33))),
     (64, 768, 640, [63]),
     (300, 256, 16384, list(range(1, 300, 3))),
+    (520, 256, 20480, [r for r in range(520) if r % 7 >= 3]),
 ]
 
 
