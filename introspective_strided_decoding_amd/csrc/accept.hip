@@ -458,57 +458,67 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   block_sum_dk<4>(tot, sm4);   // its barriers also publish the boundary list
   const double sp = tot[0], sq = tot[1], a = tot[2], b = tot[3];
   // Entries near the boundary, grouped by their exact logit difference (equal
-  // differences: equal ratios e_p / e_q): one thread, in vocabulary order, so
-  // the sums do not depend on the order the entries were listed in.
+  // differences: equal ratios e_p / e_q) and summed in vocabulary order, so the
+  // sums do not depend on the order the entries were listed in.
   const int na = n_amb_sm;
   if (na > 0) {
-    if (threadIdx.x == 0) {
-      int n_cls = 0;
-      if (na > kAmbSlots) {
-        n_cls = kResidAmb + 1;
-      } else {
-        for (int c = 1; c < na; ++c)      // insertion sort by vocabulary index
-          for (int j = c; j > 0 && amb_idx[j] < amb_idx[j - 1]; --j) {
-            const double tk = amb_key[j];
-            amb_key[j] = amb_key[j - 1];
-            amb_key[j - 1] = tk;
-            const int ti = amb_idx[j];
-            amb_idx[j] = amb_idx[j - 1];
-            amb_idx[j - 1] = ti;
-            const double t0 = amb_e[j][0], t1 = amb_e[j][1];
-            amb_e[j][0] = amb_e[j - 1][0];
-            amb_e[j][1] = amb_e[j - 1][1];
-            amb_e[j - 1][0] = t0;
-            amb_e[j - 1][1] = t1;
-          }
-        for (int j = 0; j < na && n_cls <= kResidAmb; ++j) {
-          int c = 0;
-          while (c < n_cls && cls_key[c] != amb_key[j]) ++c;
-          if (c == n_cls) {
-            if (n_cls == kResidAmb) { n_cls = kResidAmb + 1; break; }
-            cls_key[c] = amb_key[j];
-            cls_sum[c][0] = 0.0;
-            cls_sum[c][1] = 0.0;
-            ++n_cls;
-          }
-          cls_sum[c][0] += amb_e[j][0];
-          cls_sum[c][1] += amb_e[j][1];
-        }
-        if (n_cls <= kResidAmb) {
-          // the groups in increasing order of their difference, so the record is deterministic
-          for (int c = 1; c < n_cls; ++c)
-            for (int j = c; j > 0 && cls_key[j] < cls_key[j - 1]; --j) {
-              const double tk = cls_key[j], tp = cls_sum[j][0], tq = cls_sum[j][1];
-              cls_key[j] = cls_key[j - 1];
-              cls_sum[j][0] = cls_sum[j - 1][0];
-              cls_sum[j][1] = cls_sum[j - 1][1];
-              cls_key[j - 1] = tk;
-              cls_sum[j - 1][0] = tp;
-              cls_sum[j - 1][1] = tq;
-            }
-        }
+    if (na <= kAmbSlots) {
+      // One thread per listed entry, each pass O(na): (1) move the entry to its
+      // rank by vocabulary index (indices are distinct); (2) mark the first
+      // entry of each difference; (3) a first entry's group number is the count
+      // of groups with a smaller difference; (4) one thread per group sums its
+      // members in vocabulary order.  The same sums, in the same order, as a
+      // serial sort and scan.
+      const int t = threadIdx.x;
+      double key = 0.0, e0v = 0.0, e1v = 0.0;
+      int rank = 0;
+      if (t < na) {
+        key = amb_key[t];
+        e0v = amb_e[t][0];
+        e1v = amb_e[t][1];
+        const int idx = amb_idx[t];
+        for (int i = 0; i < na; ++i) rank += amb_idx[i] < idx;
       }
-      n_cls_sm = n_cls;
+      __syncthreads();
+      if (t < na) {
+        amb_key[rank] = key;
+        amb_e[rank][0] = e0v;
+        amb_e[rank][1] = e1v;
+      }
+      __syncthreads();
+      bool first = false;
+      if (t < na) {
+        key = amb_key[t];
+        first = true;
+        for (int i = 0; i < t; ++i) first &= amb_key[i] != key;
+        amb_idx[t] = first ? 1 : 0;            // the index list is free again: first-of-group marks
+      }
+      __syncthreads();
+      if (t < na && first) {
+        int c = 0;
+        for (int i = 0; i < na; ++i) c += (amb_idx[i] != 0) && amb_key[i] < key;
+        if (c < kResidAmb) cls_key[c] = key;
+      }
+      if (t == 0) {
+        int n = 0;
+        for (int i = 0; i < na; ++i) n += amb_idx[i];
+        n_cls_sm = n <= kResidAmb ? n : kResidAmb + 1;
+      }
+      __syncthreads();
+      const int n_cls = n_cls_sm;
+      if (t < n_cls && n_cls <= kResidAmb) {
+        const double ck = cls_key[t];
+        double g0 = 0.0, g1 = 0.0;
+        for (int i = 0; i < na; ++i)
+          if (amb_key[i] == ck) {
+            g0 += amb_e[i][0];
+            g1 += amb_e[i][1];
+          }
+        cls_sum[t][0] = g0;
+        cls_sum[t][1] = g1;
+      }
+    } else if (threadIdx.x == 0) {
+      n_cls_sm = kResidAmb + 1;
     }
     __syncthreads();
     if (na > kAmbSlots) {
