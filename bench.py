@@ -153,7 +153,8 @@ def r_isd_projections(cfg, dev, stream, reps):
     rows = cfg.batch * cfg.q_rows
     proj = RIsdProjections(rows, stride_mask_rows(cfg.batch, cfg.stride_n), hidden=hidden, kv=kv,
                            mlp=3 * hidden, seed=11, device=dev)
-    res = {"what": "q, k, v, o, gate, up, down projections of one layer; adapter rank 128 on the MASK rows",
+    res = {"what": "q, k, v, o, gate, up, down projections of one layer; adapter rank 128 on the MASK rows; "
+                   "q/k/v and gate/up (which share an input) side by side on two streams",
            "rows": rows, "gated_rows": int(proj.mask.numel()), "hidden": hidden, "kv": kv, "mlp": 3 * hidden}
     for gated in (True, False):
         for _ in range(3):
@@ -161,7 +162,7 @@ def r_isd_projections(cfg, dev, stream, reps):
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            proj.run(gated)
+            proj.run(gated)     # siblings that share an input on two streams
         for _ in range(3):
             g.replay()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -184,7 +185,7 @@ def r_isd_projections(cfg, dev, stream, reps):
     t_hbm = proj.bytes(False) / (HBM_PEAK_GBS * 1e6)
     res["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
     res["base_frac_of_bound"] = round(max(t_mfma, t_hbm) / res["base"]["ms"], 4)
-    # the same base projections through torch.nn.functional.linear
+    # the same base projections through torch.nn.functional.linear, one stream
     pairs = [(t["X"], t["W_t"]) for t in proj.p.values()]
     for _ in range(3):
         for x, w in pairs:

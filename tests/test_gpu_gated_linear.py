@@ -171,3 +171,36 @@ def test_gated_projection_r_isd_layer_shapes(batch, proj):
     base, _ = _run(X, Wt, None, None, None)
     clean = [r * Q + i for r in range(batch) for i in range(N - 1)]
     assert torch.equal(Y[clean].view(torch.int16), base[clean].view(torch.int16))
+
+
+def test_layer_projections_overlap_and_graph_replays_match_sequential():
+    """The seven projections with siblings (q/k/v, gate/up) on two streams, eagerly and
+    replayed from a HIP graph (three replays with eager work in between), give every output
+    bit for bit as the one-stream sequence does."""
+    from introspective_strided_decoding_amd.r_isd import RIsdProjections, stride_mask_rows
+    batch, n = 32, 4
+    proj = RIsdProjections(batch * (2 * n - 1), stride_mask_rows(batch, n), hidden=1024, kv=256, mlp=3072,
+                           seed=3, device="cuda")
+    names = [nm for nm, _, _ in proj.shapes]
+    for gated in (True, False):
+        proj.run(gated, overlap=False)
+        torch.cuda.synchronize()
+        want = {nm: proj.p[nm]["Y"].clone() for nm in names}
+        for nm in names:
+            proj.p[nm]["Y"].fill_(0)
+        proj.run(gated, overlap=True)
+        torch.cuda.synchronize()
+        for nm in names:
+            assert torch.equal(proj.p[nm]["Y"].view(torch.int16), want[nm].view(torch.int16)), nm
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            proj.run(gated, overlap=True)
+        for rep in range(3):
+            for nm in names:
+                proj.p[nm]["Y"].fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for nm in names:
+                assert torch.equal(proj.p[nm]["Y"].view(torch.int16), want[nm].view(torch.int16)), (rep, nm)
+        del g
