@@ -324,6 +324,24 @@ def main(argv=None):
                      "eager_steps_per_s": round(args.steps / e_elapsed, 2),
                      "graph_ms_per_step": round(g_elapsed * 1e3 / args.steps, 5)}
             del graphs
+            # the verify step alone (what "value" times eagerly), recorded and replayed
+            vgraphs = []
+            for st in steps:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    one_step(st)
+                vgraphs.append(g)
+            for i in range(args.warmup):
+                vgraphs[i % sets].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                vgraphs[i % sets].replay()
+            torch.cuda.synchronize()
+            v_elapsed = time.perf_counter() - t0
+            graph["verify_step_graph_steps_per_s"] = round(args.steps / v_elapsed, 2)
+            graph["verify_step_graph_ms_per_step"] = round(v_elapsed * 1e3 / args.steps, 5)
+            del vgraphs
 
     # the decoding loop: whole forwards (attention, accept, proposals, bookkeeping, commit in place)
     loop = None
