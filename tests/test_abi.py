@@ -124,6 +124,15 @@ def test_accept_and_commit_validation():
     bad[-2] = 8
     assert LIB.isd_accept_commit(ctypes.byref(s.c()), *bad) == 4
     assert LIB.isd_accept_commit(None, *fargs) == 1
+    # vocabularies past 1024 residual shards of 2048 entries are refused; the limit itself is not
+    for v, want in ((2048 * 1024 + 1, 5), (2048 * 1024, 4)):
+        big = _shape(vocab=v)
+        bad = list(args)
+        bad[-2] = 8
+        assert LIB.isd_accept(ctypes.byref(big.c()), *bad) == want, v
+        bad = list(fargs)
+        bad[-2] = 8
+        assert LIB.isd_accept_commit(ctypes.byref(big.c()), *bad) == want, v
 
 
 def test_propose_validation():

@@ -141,3 +141,12 @@ def test_accept_full_size(name, steps):
     print(f"{name}: {t.decisions} decisions, {t.near_ties} near-ties, {t.resamples} resamples, "
           f"max log-prob err {t.logp_err:.2e}")
     assert t.resamples > 0
+
+
+@pytest.mark.parametrize("vocab", [2048 * 1024, 2048 * 1024 - 5])
+def test_accept_largest_vocabulary(vocab):
+    """The largest vocabulary the library takes (1024 residual shards of 2048 entries per
+    row), exactly full and with a ragged last shard."""
+    wl = make_workload(get_config("b8_ctx2k", batch=2, ctx=16, vocab=vocab, stride_n=3))
+    t = _run(wl, 12)
+    assert t.requests == 24

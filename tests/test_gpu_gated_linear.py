@@ -204,3 +204,18 @@ def test_layer_projections_overlap_and_graph_replays_match_sequential():
             for nm in names:
                 assert torch.equal(proj.p[nm]["Y"].view(torch.int16), want[nm].view(torch.int16)), (rep, nm)
         del g
+
+
+def test_gated_projection_largest_row_count():
+    """65536 rows, the most one call takes (64 x 64 tiles, 1024 row tiles), every third gated;
+    sampled rows against the oracle, CLEAN rows bit-identical to the base-only call."""
+    rows, d_in, d_out = 65536, 256, 128
+    X, Wt, At, Bt = _inputs(rows, d_in, d_out, seed=44)
+    mask = list(range(0, rows, 3))
+    Y, flags = _run(X, Wt, At, Bt, mask)
+    assert flags == 0
+    sample = list(range(0, 64)) + list(range(rows - 64, rows)) + list(range(1000, rows, 4099))
+    _check(Y, X, Wt, At, Bt, mask, 1.0, sample=sample)
+    base, _ = _run(X, Wt, None, None, None)
+    clean = torch.tensor([r for r in range(rows) if r % 3])
+    assert torch.equal(Y[clean].view(torch.int16), base[clean].view(torch.int16))

@@ -85,3 +85,11 @@ def test_propose_extreme_and_tied_logits():
     m[2, 2, 8999] = 50.0                   # maximum in the last entry
     wl.mask_logits = torch.from_numpy(m).to(torch.bfloat16).float().numpy()
     _check(wl, 30)
+
+
+@pytest.mark.parametrize("vocab", [2048 * 1024, 2048 * 1024 - 5])
+def test_propose_largest_vocabulary(vocab):
+    """The largest vocabulary the accept path takes, exactly full and ragged."""
+    wl = make_workload(get_config("b8_ctx2k", batch=1, ctx=16, vocab=vocab, stride_n=3), with_logits=False,
+                       with_mask_logits=True)
+    assert _check(wl, 6) == 18
