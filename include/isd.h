@@ -206,6 +206,14 @@ isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_ne
  *   n_out      [B] int32             written: A + (A < N)
  *   n_commit   [B] int32             written: min(A, N-1), the CLEAN rows to commit
  *   logp_sel, logq_sel [B][N-1] fp32 written: log p(x_k), log q(x_k) for every row
+ *   q_norms    [B][N] float pairs (max, sum of exp(l - max)), 8-byte aligned,
+ *              or NULL.  The q rows are the previous forward's MASK rows
+ *              that proposed x_2..x_N, and isd_propose already normalised
+ *              them: pass the pairs it wrote (its row_norms) and the q rows'
+ *              normalisers are taken from there instead of a second pass
+ *              over q_logits; pair (r, k) belongs to the MASK row that
+ *              proposed x_{k+1}, pair (r, 0) is not read.  q_logits is still
+ *              read at the proposals.  NULL: computed here.
  *
  * The log-normalisers behind logp_sel / logq_sel and rho are fp32; the
  * residual is fp64.  Flags: TOKEN_RANGE (an out-of-range proposal is
@@ -214,7 +222,8 @@ isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_ne
 isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* q_logits,
                       const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
                       uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                      const int64_t* step_per_request, int32_t* accept_len, int32_t* out_tokens,
+                      const int64_t* step_per_request, const float* q_norms, int32_t* accept_len,
+                      int32_t* out_tokens,
                       int32_t* n_out, int32_t* n_commit, float* logp_sel, float* logq_sel,
                       void* workspace, size_t ws_bytes, hipStream_t stream);
 
@@ -261,8 +270,9 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
 isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const void* q_logits,
                              const int32_t* proposals, const int32_t* req_ids,
                              const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
-                             uint32_t step, const int64_t* step_per_request,
-                             int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel, float* logq_sel,
+                             uint32_t step, const int64_t* step_per_request, const float* q_norms,
+                             int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit,
+                             float* logp_sel, float* logq_sel,
                              const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                              const int32_t* page_table, const int32_t* ctx_lens_in,
                              int32_t* ctx_lens_out, void* workspace, size_t ws_bytes,
@@ -294,6 +304,11 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
  *   mask_logits [B][N][V] logit_dtype, 16-byte aligned; every row holds at
  *               least one finite logit
  *   proposals   [B][N] int32, written
+ *   row_norms   [B][N] float pairs, 8-byte aligned, or NULL: written with
+ *               each MASK row's (max logit, sum of exp(l - max)) for the
+ *               isd_accept of the forward that verifies these proposals
+ *               (its q_norms).  ISD_PROPOSE_SAMPLE only (the argmax policy
+ *               sums nothing: ISD_ERR_UNSUPPORTED).
  *
  * Uses the same workspace as the calls above (isd_workspace_bytes()).
  * Supported: batch * stride_n <= 65535.
@@ -306,7 +321,8 @@ typedef enum isd_propose_mode {
 isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const int32_t* req_ids,
                        const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
                        uint32_t step, const int64_t* step_per_request, int32_t mode,
-                       int32_t* proposals, void* workspace, size_t ws_bytes, hipStream_t stream);
+                       int32_t* proposals, float* row_norms, void* workspace, size_t ws_bytes,
+                       hipStream_t stream);
 
 /*
  * isd_loop_advance -- per-request bookkeeping of the multi-step decoding loop.
@@ -343,6 +359,14 @@ isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const in
  *   positions [B] int32           positions argument of the next forward, in/out;
  *                                 start at >= N - 1 so it stays non-negative
  *   tokens, forwards [B] int64    running counts, in/out (start at 0)
+ *   norms_in, norms_out [B][N] float pairs, 8-byte aligned, both or neither
+ *                                 NULL: norms_out <- norms_in, for every
+ *                                 request and mode.  norms_in is this
+ *                                 forward's isd_propose row_norms (written
+ *                                 while its accept test ran beside it), and
+ *                                 norms_out the q_norms of the next forward's
+ *                                 isd_accept, which verifies the proposals
+ *                                 this forward drew.
  *
  * TPF of a request = tokens / forwards.  No workspace; no flags.
  * `forwards` can serve as the step_per_request array of isd_accept and
@@ -355,7 +379,8 @@ isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const in
 isd_status isd_loop_advance(const isd_shape* shape, const int32_t* accept_len, const int32_t* n_out,
                             const int32_t* next_proposals, int32_t* n_commit, int32_t* mode,
                             int32_t* proposals, int32_t* positions, int64_t* tokens,
-                            int64_t* forwards, hipStream_t stream);
+                            int64_t* forwards, const float* norms_in, float* norms_out,
+                            hipStream_t stream);
 
 /*
  * isd_lora_delta -- the gated rank-r delta of Residual ISD (R-ISD).

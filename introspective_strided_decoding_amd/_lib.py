@@ -83,12 +83,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "isd_workspace_init": (I32, [SP, P, SZ, P]),
         "isd_read_flags": (I32, [P, ctypes.POINTER(U32), P]),
         "isd_attention": (I32, [SP, P, P, P, P, P, P, P, ctypes.c_float, P, P, SZ, P]),
-        "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, P, SZ, P]),
+        "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, P, P, SZ, P]),
         "kv_commit": (I32, [SP, P, P, P, P, P, P, P, P, P, SZ, P]),
-        "isd_accept_commit": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P,
+        "isd_accept_commit": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, P,
                                     P, P, P, P, P, P, P, P, SZ, P]),
-        "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, P, I32, P, P, SZ, P]),
-        "isd_loop_advance": (I32, [SP, P, P, P, P, P, P, P, P, P, P]),
+        "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, P, I32, P, P, P, SZ, P]),
+        "isd_loop_advance": (I32, [SP, P, P, P, P, P, P, P, P, P, P, P, P]),
         "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
         "isd_lora_delta": (I32, [I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
         "isd_gated_linear_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
@@ -238,9 +238,15 @@ def isd_attention(shape: Shape, q, k_new, v_new, k_pages, v_pages, page_table, c
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 
+def _norms(t, name, B, N):
+    return None if t is None else _ptr(t, name, torch.float32, B * N * 2)
+
+
 def isd_accept(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
                accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, workspace,
-               stream=None, step_dev=None) -> None:
+               stream=None, step_dev=None, q_norms=None) -> None:
+    """q_norms: [B][N][2] float32 as isd_propose wrote them for the MASK rows that proposed
+    this stride (see include/isd.h), or None."""
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     dt = _tdtype(shape.logit_dtype)
     i32 = torch.int32
@@ -250,6 +256,7 @@ def isd_accept(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, 
         _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
         int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF,
         None if step_dev is None else _ptr(step_dev, "step_dev", torch.int64, B),
+        _norms(q_norms, "q_norms", B, N),
         _ptr(accept_len, "accept_len", i32, B), _ptr(out_tokens, "out_tokens", i32, B * N),
         _ptr(n_out, "n_out", i32, B), _ptr(n_commit, "n_commit", i32, B),
         _ptr(logp_sel, "logp_sel", torch.float32, B * (N - 1)),
@@ -275,7 +282,7 @@ def kv_commit(shape: Shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens
 def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
                       accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new, v_new, k_pages,
                       v_pages, page_table, ctx_lens_in, ctx_lens_out, workspace, stream=None,
-                      step_dev=None) -> None:
+                      step_dev=None, q_norms=None) -> None:
     """isd_accept followed by kv_commit of the accepted rows, in one call."""
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     Q, Hkv, D = shape.q_rows, shape.n_kv_heads, shape.head_dim
@@ -288,6 +295,7 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
         _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
         int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF,
         None if step_dev is None else _ptr(step_dev, "step_dev", torch.int64, B),
+        _norms(q_norms, "q_norms", B, N),
         _ptr(accept_len, "accept_len", i32, B), _ptr(out_tokens, "out_tokens", i32, B * N),
         _ptr(n_out, "n_out", i32, B), _ptr(n_commit, "n_commit", i32, B),
         _ptr(logp_sel, "logp_sel", torch.float32, B * (N - 1)),
@@ -300,7 +308,9 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
 
 
 def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, mode: int,
-                proposals, workspace, stream=None, step_dev=None) -> None:
+                proposals, workspace, stream=None, step_dev=None, row_norms=None) -> None:
+    """row_norms: [B][N][2] float32 written with each MASK row's (max, sum exp(l - max))
+    (sampling policy only), or None."""
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     i32 = torch.int32
     sample = mode == PROPOSE_SAMPLE
@@ -310,12 +320,14 @@ def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, 
         _ptr(positions, "positions", i32, B) if sample or positions is not None else None,
         int(seed[0]) & (2**64 - 1), int(seed[1]) & (2**64 - 1), int(step) & 0xFFFFFFFF,
         None if step_dev is None else _ptr(step_dev, "step_dev", torch.int64, B), int(mode),
-        _ptr(proposals, "proposals", i32, B * N),
+        _ptr(proposals, "proposals", i32, B * N), _norms(row_norms, "row_norms", B, N),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 
 def isd_loop_advance(shape: Shape, accept_len, n_out, next_proposals, n_commit, mode, proposals,
-                     positions, tokens, forwards, stream=None) -> None:
+                     positions, tokens, forwards, stream=None, norms_in=None, norms_out=None) -> None:
+    """norms_in -> norms_out ([B][N][2] float32 each, or both None): the proposals' row
+    normalisers handed to the next forward's accept test."""
     B, N = shape.batch, shape.stride_n
     i32, i64 = torch.int32, torch.int64
     _call("isd_loop_advance",
@@ -323,7 +335,8 @@ def isd_loop_advance(shape: Shape, accept_len, n_out, next_proposals, n_commit, 
         _ptr(next_proposals, "next_proposals", i32, B * N), _ptr(n_commit, "n_commit", i32, B),
         _ptr(mode, "mode", i32, B), _ptr(proposals, "proposals", i32, B * N),
         _ptr(positions, "positions", i32, B), _ptr(tokens, "tokens", i64, B),
-        _ptr(forwards, "forwards", i64, B), _stream(stream))
+        _ptr(forwards, "forwards", i64, B), _norms(norms_in, "norms_in", B, N),
+        _norms(norms_out, "norms_out", B, N), _stream(stream))
 
 
 def isd_lora_workspace_bytes(n_mask: int, d_in: int, rank: int) -> int:

@@ -71,6 +71,7 @@ struct DecideArgs {
   uint64_t seed_lo, seed_hi;
   uint32_t step;
   const int64_t* step_dev;   // per-request step counters in device memory (NULL: `step` for all)
+  const float2* q_norms;     // (max, sum exp(l - max)) per MASK row as isd_propose wrote them (NULL: computed here)
   int N, V, shards;
   int32_t *accept_len, *out_tokens, *n_out, *n_commit;
   float *logp_sel, *logq_sel;
@@ -208,11 +209,13 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   int x = 0, xl = 0;
   float raw_p = 0.f, raw_q = 0.f;
   uint32_t rid32 = 0, pos32 = 0, step32 = a.step;
+  float2 qn = make_float2(0.f, 0.f);
   if (wave == 0) {
     if (lane < R) {
       x = a.proposals[size_t(r) * N + lane + 1];
       raw_p = a.gath[size_t(r) * 2 * R + lane];
-      raw_q = a.gath[size_t(r) * 2 * R + R + lane];
+      if (a.q_norms) qn = a.q_norms[size_t(r) * N + lane + 1];
+      else raw_q = a.gath[size_t(r) * 2 * R + R + lane];
       rid32 = uint32_t(a.req_ids[r]);
       pos32 = uint32_t(a.positions[r]);
       if (a.step_dev) step32 = uint32_t(a.step_dev[r]);
@@ -220,9 +223,19 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
     if (lane < N) xl = a.proposals[size_t(r) * N + lane];
   }
   const bool in_range = x >= 0 && x < V;
-  // every wave: rows wave, wave + 4, ... of the request's 2(N-1) rows
+  // carried q normalisers: the q rows' logits at the proposals are gathered here
+  // (no normaliser pass over the q rows recorded them)
+  if (a.q_norms && wave == 0 && lane < R && in_range)
+    raw_q = to_f32<T>(a.q_logits[(size_t(r) * R + lane) * V + x]);
+  if (a.q_norms && wave == 0 && lane < R) {
+    lse_sm[R + lane] = qn.x + __logf(qn.y);
+    max_sm[R + lane] = qn.x;
+  }
+  // every wave: rows wave, wave + 4, ... of the request's 2(N-1) rows (p rows only when
+  // the q normalisers are carried)
   const float2* req_part = part + size_t(r) * 2 * R * shards;
-  for (int row = wave; row < 2 * R; row += kThreads / 64) {
+  const int n_rows = a.q_norms ? R : 2 * R;
+  for (int row = wave; row < n_rows; row += kThreads / 64) {
     float rm = -INFINITY, rs = 0.f;
     for (int i = lane; i < shards; i += 64) {
       const float2 v = req_part[size_t(row) * shards + i];
@@ -761,7 +774,7 @@ template <typename T>
 hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, const void* ql,
                     const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
                     uint64_t seed_lo, uint64_t seed_hi, uint32_t step, const int64_t* step_dev,
-                    int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit,
+                    const float* q_norms, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit,
                     float* logp_sel, float* logq_sel, char* ws, const WsLayout& L,
                     const CommitArgs* commit, hipStream_t stream) {
   const T* P = static_cast<const T*>(pl);
@@ -781,6 +794,7 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.seed_hi = seed_hi;
   a.step = step;
   a.step_dev = step_dev;
+  a.q_norms = reinterpret_cast<const float2*>(q_norms);
   a.N = N;
   a.V = V;
   a.shards = p.shards;
@@ -794,8 +808,8 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.rej_count = rej_count;
   a.gath = reinterpret_cast<float*>(ws + L.gath);
   a.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
-  hipLaunchKernelGGL((lse_partial<T>), dim3(2 * (N - 1) * p.shards, B), dim3(kThreads), 0, stream, a,
-                     p.shard_len, part);
+  hipLaunchKernelGGL((lse_partial<T>), dim3((q_norms ? 1 : 2) * (N - 1) * p.shards, B), dim3(kThreads), 0, stream,
+                     a, p.shard_len, part);
   hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
   // with a commit, N - 1 more columns of workgroups: one per (CLEAN row, request)
   CommitArgs cm{};
@@ -813,15 +827,15 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
 hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_logits,
                          const void* q_logits, const int32_t* proposals, const int32_t* req_ids,
                          const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                         const int64_t* step_dev, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
-                         int32_t* n_commit, float* logp_sel, float* logq_sel, char* ws, const WsLayout& L,
-                         const CommitArgs* commit, hipStream_t stream) {
+                         const int64_t* step_dev, const float* q_norms, int32_t* accept_len, int32_t* out_tokens,
+                         int32_t* n_out, int32_t* n_commit, float* logp_sel, float* logq_sel, char* ws,
+                         const WsLayout& L, const CommitArgs* commit, hipStream_t stream) {
   if (s.logit_dtype == ISD_BF16)
     return launch_t<uint16_t>(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi,
-                              step, step_dev, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel,
+                              step, step_dev, q_norms, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel,
                               ws, L, commit, stream);
   return launch_t<float>(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi, step,
-                         step_dev, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L, commit,
+                         step_dev, q_norms, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L, commit,
                          stream);
 }
 

@@ -31,6 +31,7 @@ isd_status hip_fail(hipError_t e, const char* where) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }   // NULL passes
 
 int ceil_div(long long a, long long b) { return int((a + b - 1) / b); }
 
@@ -159,7 +160,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 6; }
+int32_t isd_abi_version(void) { return 7; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {
@@ -225,7 +226,7 @@ isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_ne
 isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* q_logits,
                       const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
                       uint64_t seed_lo, uint64_t seed_hi, uint32_t step, const int64_t* step_per_request,
-                      int32_t* accept_len,
+                      const float* q_norms, int32_t* accept_len,
                       int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
                       float* logq_sel, void* workspace, size_t ws_bytes, hipStream_t stream) {
   isd_status st = check_shape(shape);
@@ -233,7 +234,7 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
   if (!p_logits || !q_logits || !proposals || !req_ids || !positions || !accept_len || !out_tokens ||
       !n_out || !n_commit || !logp_sel || !logq_sel)
     return ISD_ERR_NULL;
-  if (!aligned16(p_logits) || !aligned16(q_logits)) return ISD_ERR_ALIGNMENT;
+  if (!aligned16(p_logits) || !aligned16(q_logits) || !aligned8(q_norms)) return ISD_ERR_ALIGNMENT;
   if (shape->batch > 65535) return ISD_ERR_UNSUPPORTED;
   if (shape->vocab > 2048 * 1024) return ISD_ERR_UNSUPPORTED;   // residual shards per row <= 1024
   st = check_ws(shape, workspace, ws_bytes);
@@ -241,7 +242,7 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
   const AcceptPlan p = plan_accept(*shape);
   const WsLayout L = ws_layout(*shape);
   hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
-                               seed_hi, step, step_per_request, accept_len, out_tokens, n_out, n_commit,
+                               seed_hi, step, step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit,
                                logp_sel, logq_sel, static_cast<char*>(workspace), L, nullptr, stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept");
 }
@@ -249,7 +250,7 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
 isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const void* q_logits,
                              const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
                              uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                             const int64_t* step_per_request, int32_t* accept_len,
+                             const int64_t* step_per_request, const float* q_norms, int32_t* accept_len,
                              int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
                              float* logq_sel, const void* k_new, const void* v_new, void* k_pages,
                              void* v_pages, const int32_t* page_table, const int32_t* ctx_lens_in,
@@ -261,7 +262,7 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
       !page_table || !ctx_lens_in || !ctx_lens_out)
     return ISD_ERR_NULL;
   if (!aligned16(p_logits) || !aligned16(q_logits) || !aligned16(k_new) || !aligned16(v_new) ||
-      !aligned16(k_pages))
+      !aligned16(k_pages) || !aligned8(q_norms))
     return ISD_ERR_ALIGNMENT;
   if (shape->batch > 65535) return ISD_ERR_UNSUPPORTED;
   if (shape->vocab > 2048 * 1024) return ISD_ERR_UNSUPPORTED;
@@ -274,7 +275,7 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
                                    ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
                                    reinterpret_cast<uint32_t*>(ws + L.cmt_cnt));
   hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
-                               seed_hi, step, step_per_request, accept_len, out_tokens, n_out, n_commit,
+                               seed_hi, step, step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit,
                                logp_sel, logq_sel, ws, L, &c, stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept_commit");
 }
@@ -302,19 +303,20 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
 
 isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const int32_t* req_ids,
                        const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                       const int64_t* step_per_request, int32_t mode, int32_t* proposals, void* workspace,
-                       size_t ws_bytes, hipStream_t stream) {
+                       const int64_t* step_per_request, int32_t mode, int32_t* proposals, float* row_norms,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
   isd_status st = check_shape(shape);
   if (st != ISD_OK) return st;
   if (mode != ISD_PROPOSE_SAMPLE && mode != ISD_PROPOSE_ARGMAX) return ISD_ERR_UNSUPPORTED;
   if (!mask_logits || !proposals || (mode == ISD_PROPOSE_SAMPLE && (!req_ids || !positions)))
     return ISD_ERR_NULL;
-  if (!aligned16(mask_logits)) return ISD_ERR_ALIGNMENT;
+  if (!aligned16(mask_logits) || !aligned8(row_norms)) return ISD_ERR_ALIGNMENT;
   if ((long long)shape->batch * shape->stride_n > 65535) return ISD_ERR_UNSUPPORTED;
+  if (row_norms && mode != ISD_PROPOSE_SAMPLE) return ISD_ERR_UNSUPPORTED;   // argmax sums nothing
   st = check_ws(shape, workspace, ws_bytes);
   if (st != ISD_OK) return st;
   hipError_t e = launch_propose(*shape, mask_logits, req_ids, positions, seed_lo, seed_hi, step,
-                                step_per_request, mode, proposals, static_cast<char*>(workspace),
+                                step_per_request, mode, proposals, row_norms, static_cast<char*>(workspace),
                                 ws_layout(*shape), stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_propose");
 }
@@ -322,14 +324,16 @@ isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const in
 isd_status isd_loop_advance(const isd_shape* shape, const int32_t* accept_len, const int32_t* n_out,
                             const int32_t* next_proposals, int32_t* n_commit, int32_t* mode,
                             int32_t* proposals, int32_t* positions, int64_t* tokens, int64_t* forwards,
-                            hipStream_t stream) {
+                            const float* norms_in, float* norms_out, hipStream_t stream) {
   isd_status st = check_shape(shape);
   if (st != ISD_OK) return st;
   if (!accept_len || !n_out || !next_proposals || !n_commit || !mode || !proposals || !positions ||
-      !tokens || !forwards)
+      !tokens || !forwards || (!norms_in != !norms_out))
     return ISD_ERR_NULL;
+  if (!aligned8(norms_in) || !aligned8(norms_out)) return ISD_ERR_ALIGNMENT;
   hipError_t e = launch_loop_advance(shape->batch, shape->stride_n, accept_len, n_out, next_proposals,
-                                     n_commit, mode, proposals, positions, tokens, forwards, stream);
+                                     n_commit, mode, proposals, positions, tokens, forwards, norms_in, norms_out,
+                                     stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_loop_advance");
 }
 

@@ -129,7 +129,7 @@ hipError_t launch_attention(const isd_shape& s, const AttnPlan& p, const void* q
 hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_logits,
                          const void* q_logits, const int32_t* proposals, const int32_t* req_ids,
                          const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
-                         uint32_t step, const int64_t* step_dev, int32_t* accept_len,
+                         uint32_t step, const int64_t* step_dev, const float* q_norms, int32_t* accept_len,
                          int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
                          float* logq_sel, char* ws,
                          const WsLayout& L, const CommitArgs* commit, hipStream_t stream);
@@ -138,13 +138,13 @@ hipError_t launch_commit(const isd_shape& s, const CommitArgs& c, hipStream_t st
 
 hipError_t launch_propose(const isd_shape& s, const void* mask_logits, const int32_t* req_ids,
                           const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                          const int64_t* step_dev, int mode, int32_t* proposals, char* ws, const WsLayout& L,
-                          hipStream_t stream);
+                          const int64_t* step_dev, int mode, int32_t* proposals, float* row_norms, char* ws,
+                          const WsLayout& L, hipStream_t stream);
 
 hipError_t launch_loop_advance(int B, int N, const int32_t* accept_len, const int32_t* n_out,
                                const int32_t* next_proposals, int32_t* n_commit, int32_t* mode,
                                int32_t* proposals, int32_t* positions, int64_t* tokens, int64_t* forwards,
-                               hipStream_t stream);
+                               const float* norms_in, float* norms_out, hipStream_t stream);
 
 hipError_t launch_workspace_init(void* ws, size_t header_bytes, hipStream_t stream);
 

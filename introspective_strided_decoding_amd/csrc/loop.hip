@@ -5,7 +5,10 @@
 // proposals unless the forward rejected one (then the next forward
 // re-proposes from the corrected prefix), the positions argument of the next
 // forward moves with them, and the KV rows of a re-proposing forward are not
-// committed.
+// committed.  With a normaliser buffer, the MASK rows' (max, sum exp) pairs
+// this forward's proposals wrote move to where the next forward's accept test
+// reads its q-row normalisers (every forward's: the next forward verifies the
+// proposals this one drew, whatever the mode).
 #include "device_common.hpp"
 #include "isd_internal.hpp"
 
@@ -19,9 +22,13 @@ __global__ __launch_bounds__(256) void loop_advance_kernel(int B, int N, const i
                                                            int32_t* __restrict__ proposals,
                                                            int32_t* __restrict__ positions,
                                                            int64_t* __restrict__ tokens,
-                                                           int64_t* __restrict__ forwards) {
+                                                           int64_t* __restrict__ forwards,
+                                                           const float2* __restrict__ norms_in,
+                                                           float2* __restrict__ norms_out) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= B) return;
+  if (norms_in)
+    for (int j = 0; j < N; ++j) norms_out[size_t(r) * N + j] = norms_in[size_t(r) * N + j];
   forwards[r] += 1;
   bool take = true;
   if (mode[r] != ISD_LOOP_REPROPOSE) {
@@ -48,9 +55,10 @@ __global__ __launch_bounds__(256) void loop_advance_kernel(int B, int N, const i
 hipError_t launch_loop_advance(int B, int N, const int32_t* accept_len, const int32_t* n_out,
                                const int32_t* next_proposals, int32_t* n_commit, int32_t* mode,
                                int32_t* proposals, int32_t* positions, int64_t* tokens, int64_t* forwards,
-                               hipStream_t stream) {
+                               const float* norms_in, float* norms_out, hipStream_t stream) {
   hipLaunchKernelGGL(loop_advance_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, N, accept_len, n_out,
-                     next_proposals, n_commit, mode, proposals, positions, tokens, forwards);
+                     next_proposals, n_commit, mode, proposals, positions, tokens, forwards,
+                     reinterpret_cast<const float2*>(norms_in), reinterpret_cast<float2*>(norms_out));
   return hipGetLastError();
 }
 

@@ -12,6 +12,9 @@
 //                 over them picks the shard holding u * total, and a
 //                 workgroup scan inside that shard in vocabulary order picks
 //                 the first token whose running mass exceeds u * total.
+//                 With a row_norms buffer, the row's (max, sum of exp(l - max))
+//                 is written too: the q-row normaliser of the forward that
+//                 verifies these proposals.
 // Sums and the scan run in float64 (exp by the table-driven exp_nonpos, its
 // 64-entry table in LDS), so the draw agrees with a float64 inverse CDF up to
 // rounding of the running sums.
@@ -128,7 +131,8 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
                                                          const int32_t* __restrict__ positions,
                                                          uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
                                                          const int64_t* __restrict__ step_dev,
-                                                         int32_t* __restrict__ out) {
+                                                         int32_t* __restrict__ out,
+                                                         float2* __restrict__ row_norms) {
   const int row = blockIdx.x;
   const int r = row / N, k = row % N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -181,6 +185,8 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
       }
       double tot;
       const double before_lane = wave_exclusive_d(wsh, tot);
+      // the row's normaliser, for the accept test of the forward that verifies these proposals
+      if (row_norms && lane == 0) row_norms[row] = make_float2(M, float(tot));
       const double target = u * tot;
       double cum = before_lane;
       int pick = -1, last_nz = -1;
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
 template <typename T>
 hipError_t launch_t(const isd_shape& s, const void* logits, const int32_t* req_ids, const int32_t* positions,
                     uint64_t seed_lo, uint64_t seed_hi, uint32_t step, const int64_t* step_dev, int mode,
-                    int32_t* out, char* ws, const WsLayout& L, hipStream_t stream) {
+                    int32_t* out, float* row_norms, char* ws, const WsLayout& L, hipStream_t stream) {
   const T* lg = static_cast<const T*>(logits);
   const int N = s.stride_n, V = s.vocab, B = s.batch;
   const int shards = prop_shards(V);
@@ -277,7 +283,8 @@ hipError_t launch_t(const isd_shape& s, const void* logits, const int32_t* req_i
   hipLaunchKernelGGL((prop_partial<T>), dim3(shards, B * N), dim3(kPThreads), 0, stream, lg, V, shards,
                      sample, part);
   hipLaunchKernelGGL((prop_select<T>), dim3(B * N), dim3(kPThreads), 0, stream, lg, N, V, shards, sample,
-                     part, req_ids, positions, seed_lo, seed_hi, step, step_dev, out);
+                     part, req_ids, positions, seed_lo, seed_hi, step, step_dev, out,
+                     reinterpret_cast<float2*>(row_norms));
   return hipGetLastError();
 }
 
@@ -287,13 +294,13 @@ int prop_shards(int vocab) { return (vocab + kPShard - 1) / kPShard; }
 
 hipError_t launch_propose(const isd_shape& s, const void* mask_logits, const int32_t* req_ids,
                           const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
-                          const int64_t* step_dev, int mode, int32_t* proposals, char* ws, const WsLayout& L,
-                          hipStream_t stream) {
+                          const int64_t* step_dev, int mode, int32_t* proposals, float* row_norms, char* ws,
+                          const WsLayout& L, hipStream_t stream) {
   if (s.logit_dtype == ISD_BF16)
     return launch_t<uint16_t>(s, mask_logits, req_ids, positions, seed_lo, seed_hi, step, step_dev, mode,
-                              proposals, ws, L, stream);
+                              proposals, row_norms, ws, L, stream);
   return launch_t<float>(s, mask_logits, req_ids, positions, seed_lo, seed_hi, step, step_dev, mode,
-                         proposals, ws, L, stream);
+                         proposals, row_norms, ws, L, stream);
 }
 
 }  // namespace isd

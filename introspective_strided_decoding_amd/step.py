@@ -128,12 +128,15 @@ class DeviceStep:
     def _step_dev(self, device_step: bool):
         return self.extra["forwards"] if device_step else None
 
-    def accept(self, stream=None, step: Optional[int] = None, seed=None, device_step: bool = False):
-        """``device_step``: each request's Philox step is its forward count on the device."""
-        self._call(("accept", device_step), lambda: _lib.prepare(
+    def accept(self, stream=None, step: Optional[int] = None, seed=None, device_step: bool = False,
+               q_norms=None):
+        """``device_step``: each request's Philox step is its forward count on the device.
+        ``q_norms``: the q rows' normalisers as the previous forward's proposals wrote them."""
+        self._call(("accept", device_step, q_norms is not None), lambda: _lib.prepare(
             _lib.isd_accept, self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
             self.positions, self.seed, self.step, self.accept_len, self.out_tokens, self.n_out, self.n_commit,
-            self.logp_sel, self.logq_sel, self.workspace, step_dev=self._step_dev(device_step)))(
+            self.logp_sel, self.logq_sel, self.workspace, step_dev=self._step_dev(device_step),
+            q_norms=q_norms))(
             stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def commit(self, stream=None):
@@ -151,10 +154,12 @@ class DeviceStep:
             stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def propose(self, stream=None, mode: int = _lib.PROPOSE_SAMPLE, step: Optional[int] = None, seed=None,
-                device_step: bool = False):
-        self._call(("propose", mode, device_step), lambda: _lib.prepare(
+                device_step: bool = False, row_norms=None):
+        """``row_norms``: written with the MASK rows' normalisers (sampling policy)."""
+        self._call(("propose", mode, device_step, row_norms is not None), lambda: _lib.prepare(
             _lib.isd_propose, self.shape, self.mask_logits, self.req_ids, self.positions, self.seed,
-            self.step, mode, self.next_proposals, self.workspace, step_dev=self._step_dev(device_step)))(
+            self.step, mode, self.next_proposals, self.workspace, step_dev=self._step_dev(device_step),
+            row_norms=row_norms))(
             stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def loop_start(self):
@@ -165,12 +170,22 @@ class DeviceStep:
         self.extra["mode"] = torch.zeros(B, dtype=torch.int32, device=dev)
         self.extra["tokens"] = torch.zeros(B, dtype=torch.int64, device=dev)
         self.extra["forwards"] = torch.zeros(B, dtype=torch.int64, device=dev)
+        # MASK-row normalisers: written by a forward's proposals, handed on by the bookkeeping,
+        # read by the next forward's accept test (two buffers, since accept and proposals run
+        # side by side)
+        N = self.shape.stride_n
+        self.extra["norms_new"] = torch.zeros(B, N, 2, dtype=torch.float32, device=dev)
+        self.extra["norms"] = torch.zeros(B, N, 2, dtype=torch.float32, device=dev)
+        self.extra["norms_valid"] = False
 
-    def loop_advance(self, stream=None):
+    def loop_advance(self, stream=None, carry: bool = False):
+        """The loop's bookkeeping; with ``carry`` it also hands the proposals' row
+        normalisers on to the next forward's accept test."""
         e = self.extra
-        self._call("loop_advance", lambda: _lib.prepare(
+        self._call(("loop_advance", carry), lambda: _lib.prepare(
             _lib.isd_loop_advance, self.shape, self.accept_len, self.n_out, self.next_proposals, self.n_commit,
-            e["mode"], self.proposals, self.positions, e["tokens"], e["forwards"]))(stream)
+            e["mode"], self.proposals, self.positions, e["tokens"], e["forwards"],
+            norms_in=e["norms_new"] if carry else None, norms_out=e["norms"] if carry else None))(stream)
 
     def _side_stream(self):
         """A second stream (default priority) and the two events of a fork and a join."""
@@ -181,7 +196,7 @@ class DeviceStep:
         return s
 
     def _accept_and_propose(self, accept_fn, stream, step: Optional[int], overlap: bool,
-                            device_step: bool = False):
+                            device_step: bool = False, row_norms=None):
         """The accept chain on ``stream`` and the proposals on a second stream, joined after.
 
         Both read this forward's logits and neither writes what the other reads
@@ -194,24 +209,31 @@ class DeviceStep:
             fork.record(main)
             side.wait_event(fork)
             accept_fn(main, step)
-            self.propose(side, step=step, device_step=device_step)
+            self.propose(side, step=step, device_step=device_step, row_norms=row_norms)
             join.record(side)
             main.wait_event(join)
         else:
             accept_fn(stream, step)
-            self.propose(stream, step=step, device_step=device_step)
+            self.propose(stream, step=step, device_step=device_step, row_norms=row_norms)
 
     def loop_forward(self, step: int = 0, attention: bool = True, stream=None, overlap: bool = True,
-                     device_step: bool = False):
+                     device_step: bool = False, carry: bool = True):
         """One forward of the decoding loop: attention, accept and proposals (side by side
         unless ``overlap`` is False), bookkeeping, commit.  With ``device_step`` the Philox
         step of every request is its forward count on the device (``step`` unused), so the
-        forward can be recorded once and replayed."""
+        forward can be recorded once and replayed.  With ``carry`` the proposals also write
+        their rows' normalisers, and the next forward's accept test takes its q-row
+        normalisers from them instead of a pass over the q rows (the q rows of a verify are
+        the MASK rows of the forward before)."""
+        e = self.extra
+        q_norms = e["norms"] if carry and e.get("norms_valid") else None
         if attention:
             self.attention(stream)
-        self._accept_and_propose(lambda s, t: self.accept(s, step=t, device_step=device_step), stream, step,
-                                 overlap, device_step)
-        self.loop_advance(stream)
+        self._accept_and_propose(lambda s, t: self.accept(s, step=t, device_step=device_step, q_norms=q_norms),
+                                 stream, step, overlap, device_step, e["norms_new"] if carry else None)
+        self.loop_advance(stream, carry=carry)
+        if carry:
+            e["norms_valid"] = True
         if attention:
             self.commit(stream)
 
@@ -224,7 +246,7 @@ class DeviceStep:
         every replay, so the caller refreshes them in place between replays.  Recording
         runs nothing; call ``loop_forward(device_step=True, overlap=...)`` eagerly at
         least once before, so every call is marshalled and the second stream exists."""
-        if ("accept", True) not in self.__dict__.get("_calls", {}) or (
+        if ("accept", True, True) not in self.__dict__.get("_calls", {}) or (
                 overlap and "side_stream" not in self.extra):
             raise RuntimeError("run loop_forward(device_step=True) eagerly before recording it")
         graph = torch.cuda.CUDAGraph()

@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 6
+    assert LIB.isd_abi_version() == 7
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"
@@ -90,9 +90,9 @@ def test_attention_validation():
 def test_accept_and_commit_validation():
     s = _shape()
     n = _ws(s)
-    # the accept arguments: 5 tensors, seed_lo, seed_hi, step, step_per_request (may be NULL),
-    # 6 outputs, workspace, its size, stream
-    args = [FAKE] * 5 + [1, 2, 3, None] + [FAKE] * 6 + [FAKE, n, None]
+    # the accept arguments: 5 tensors, seed_lo, seed_hi, step, step_per_request and q_norms
+    # (both may be NULL), 6 outputs, workspace, its size, stream
+    args = [FAKE] * 5 + [1, 2, 3, None, None] + [FAKE] * 6 + [FAKE, n, None]
     bad = list(args)
     bad[2] = None
     assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 1
@@ -100,6 +100,12 @@ def test_accept_and_commit_validation():
     bad[0] = MISALIGNED
     assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 7
     bad = list(args)
+    bad[-2] = 8
+    assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 4
+    bad = list(args)
+    bad[9] = ctypes.c_void_p(0x10004)      # q_norms: pairs of floats, 8-byte aligned
+    assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 7
+    bad[9] = MISALIGNED
     bad[-2] = 8
     assert LIB.isd_accept(ctypes.byref(s.c()), *bad) == 4
     cargs = [FAKE] * 8 + [FAKE, n, None]
@@ -110,15 +116,15 @@ def test_accept_and_commit_validation():
     bad[-2] = 0
     assert LIB.kv_commit(ctypes.byref(s.c()), *bad) == 4
     # isd_accept_commit: the accept arguments, then k_new .. ctx_lens_out, workspace, stream
-    fargs = [FAKE] * 5 + [1, 2, 3, None] + [FAKE] * 6 + [FAKE] * 7 + [FAKE, n, None]
-    assert len(fargs) == 25
-    for i in (2, 15, 19, 21):       # proposals, k_new, page_table, ctx_lens_out
+    fargs = [FAKE] * 5 + [1, 2, 3, None, None] + [FAKE] * 6 + [FAKE] * 7 + [FAKE, n, None]
+    assert len(fargs) == 26
+    for i in (2, 16, 20, 22):       # proposals, k_new, page_table, ctx_lens_out
         bad = list(fargs)
         bad[i] = None
         assert LIB.isd_accept_commit(ctypes.byref(s.c()), *bad) == 1, i
-    for i in (0, 15, 16, 17):       # p_logits, k_new, v_new, k_pages
+    for i in (0, 16, 17, 18, 9):    # p_logits, k_new, v_new, k_pages, q_norms
         bad = list(fargs)
-        bad[i] = MISALIGNED
+        bad[i] = ctypes.c_void_p(0x10004)
         assert LIB.isd_accept_commit(ctypes.byref(s.c()), *bad) == 7, i
     bad = list(fargs)
     bad[-2] = 8
@@ -139,8 +145,8 @@ def test_propose_validation():
     s = _shape()
     n = _ws(s)
 
-    def call(logits=FAKE, req=FAKE, pos=FAKE, mode=0, out=FAKE, ws=FAKE, ws_bytes=n, shape=s):
-        return LIB.isd_propose(ctypes.byref(shape.c()), logits, req, pos, 1, 2, 3, None, mode, out, ws,
+    def call(logits=FAKE, req=FAKE, pos=FAKE, mode=0, out=FAKE, ws=FAKE, ws_bytes=n, shape=s, norms=None):
+        return LIB.isd_propose(ctypes.byref(shape.c()), logits, req, pos, 1, 2, 3, None, mode, out, norms, ws,
                                ws_bytes, None)
 
     assert call(ws_bytes=8) == 4                      # every check passes up to the workspace size
@@ -154,16 +160,23 @@ def test_propose_validation():
     assert call(ws=None) == 1
     assert call(shape=_shape(batch=20000, stride_n=4), ws_bytes=8) == 5   # B * N rows > 65535
     assert call(shape=_shape(logit_dtype=5)) == 3
+    assert call(norms=FAKE, ws_bytes=8) == 4               # sampling may write the row normalisers
+    assert call(norms=FAKE, mode=1) == 5                   # argmax sums nothing
+    assert call(norms=ctypes.c_void_p(0x10004)) == 7
 
 
 def test_loop_advance_validation():
     s = _shape()
-    args = [FAKE] * 9
+    args = [FAKE] * 9 + [None, None]        # the two normaliser buffers may both be NULL
     assert LIB.isd_loop_advance(None, *args, None) == 1
     for i in range(9):
         bad = list(args)
         bad[i] = None
         assert LIB.isd_loop_advance(ctypes.byref(s.c()), *bad, None) == 1, i
+    assert LIB.isd_loop_advance(ctypes.byref(s.c()), *([FAKE] * 9 + [FAKE, None]), None) == 1   # one of two
+    assert LIB.isd_loop_advance(ctypes.byref(s.c()), *([FAKE] * 9 + [None, FAKE]), None) == 1
+    assert LIB.isd_loop_advance(ctypes.byref(s.c()), *([FAKE] * 9 + [FAKE, ctypes.c_void_p(0x10004)]),
+                                None) == 7
     assert LIB.isd_loop_advance(ctypes.byref(_shape(stride_n=1).c()), *args, None) == 2
 
 

@@ -150,3 +150,30 @@ def test_accept_largest_vocabulary(vocab):
     wl = make_workload(get_config("b8_ctx2k", batch=2, ctx=16, vocab=vocab, stride_n=3))
     t = _run(wl, 12)
     assert t.requests == 24
+
+
+def test_accept_with_carried_q_normalisers():
+    """The q rows of a verify are the MASK rows of the forward before: the normalisers
+    isd_propose writes for them (row max exact, log-normaliser to fp32 rounding) stand in
+    for the accept test's own pass over the q rows, with the same decisions."""
+    from oracle.accept import row_normalizers
+    wl = make_workload(get_config("b8_ctx2k", batch=6, ctx=16, vocab=5000, stride_n=4), with_mask_logits=True)
+    st = device_step(wl)
+    B, N = wl.proposals.shape
+    st.mask_logits.copy_(torch.cat([st.mask_logits[:, :1], st.q_logits], dim=1))
+    norms = torch.zeros(B, N, 2, dtype=torch.float32, device="cuda")
+    st.propose(row_norms=norms)
+    torch.cuda.synchronize()
+    got = norms.cpu().numpy()[:, 1:].reshape(-1, 2)
+    q = np.asarray(wl.q_logits, dtype=np.float64).reshape(-1, wl.q_logits.shape[-1])
+    assert np.array_equal(got[:, 0], q.max(axis=1).astype(np.float32))
+    lse = got[:, 0].astype(np.float64) + np.log(got[:, 1].astype(np.float64))
+    np.testing.assert_allclose(lse, row_normalizers(q), rtol=2e-7, atol=2e-6)
+    tally = AcceptTally()
+    for k in range(40):
+        step = wl.step + k
+        st.accept(step=step, q_norms=norms)
+        torch.cuda.synchronize()
+        check_accept_step(wl, fetch_accept(st), wl.philox_seed, step, tally)
+    assert tally.near_tie_rate() < NEAR_TIE_BUDGET, vars(tally)
+    assert tally.resamples > 10

@@ -223,7 +223,7 @@ def test_loop_forward_graph_replays_match_eager(overlap):
     """One loop forward recorded into a HIP graph and replayed forward after forward
     (logits refreshed in place in between) leaves the same state, pools and lengths as
     the same forwards issued eagerly."""
-    T, K, warm = 6, 3, 1
+    T, K, warm = 6, 3, 2      # the second eager forward is the first with carried q normalisers
     cfg = get_config("b8_ctx2k", batch=8, ctx=40, vocab=3000, stride_n=4)
     wl = make_workload(cfg, seed=64, with_mask_logits=True, extra_tokens=(T + warm) * (cfg.stride_n - 1))
     pool = _pool(cfg, K, 330, "batch")
