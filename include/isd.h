@@ -262,9 +262,15 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
  * n_commit, ctx_lens_out, ...) on the same stream, with n_commit the
  * isd_accept output; results are identical to those two calls.  The commit's
  * workgroups run inside the residual launch, next to the residual work,
- * once the accept decision is known.  For the plain step (attention ->
- * accept -> commit); a decoding loop that gates n_commit with
- * isd_loop_advance between accept and commit calls the two separately.
+ * once the accept decision is known.
+ *
+ *   loop_mode [B] int32 or NULL: the decoding loop's per-request mode before
+ *             this forward's isd_loop_advance (ISD_LOOP_VERIFY /
+ *             ISD_LOOP_REPROPOSE, below).  A re-proposing request commits no
+ *             row and keeps its length, the gate isd_loop_advance applies to
+ *             n_commit, so a loop forward can commit here instead of calling
+ *             kv_commit after the bookkeeping.  NULL: no gate.
+ *
  * Flags: those of both calls.
  */
 isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const void* q_logits,
@@ -275,8 +281,8 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
                              float* logp_sel, float* logq_sel,
                              const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                              const int32_t* page_table, const int32_t* ctx_lens_in,
-                             int32_t* ctx_lens_out, void* workspace, size_t ws_bytes,
-                             hipStream_t stream);
+                             int32_t* ctx_lens_out, const int32_t* loop_mode, void* workspace,
+                             size_t ws_bytes, hipStream_t stream);
 
 /*
  * isd_propose -- draw the next N proposals at the MASK rows.

@@ -86,7 +86,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "isd_accept": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, P, P, SZ, P]),
         "kv_commit": (I32, [SP, P, P, P, P, P, P, P, P, P, SZ, P]),
         "isd_accept_commit": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, P,
-                                    P, P, P, P, P, P, P, P, SZ, P]),
+                                    P, P, P, P, P, P, P, P, P, SZ, P]),
         "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, P, I32, P, P, P, SZ, P]),
         "isd_loop_advance": (I32, [SP, P, P, P, P, P, P, P, P, P, P, P, P]),
         "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
@@ -282,8 +282,9 @@ def kv_commit(shape: Shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens
 def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed, step: int,
                       accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new, v_new, k_pages,
                       v_pages, page_table, ctx_lens_in, ctx_lens_out, workspace, stream=None,
-                      step_dev=None, q_norms=None) -> None:
-    """isd_accept followed by kv_commit of the accepted rows, in one call."""
+                      step_dev=None, q_norms=None, loop_mode=None) -> None:
+    """isd_accept followed by kv_commit of the accepted rows, in one call (loop_mode: a
+    re-proposing request of the decoding loop commits nothing)."""
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     Q, Hkv, D = shape.q_rows, shape.n_kv_heads, shape.head_dim
     dt, kt = _tdtype(shape.logit_dtype), _tdtype(shape.kv_dtype)
@@ -304,6 +305,7 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
         _ptr(k_pages, "k_pages", kt, pool), _ptr(v_pages, "v_pages", kt, pool),
         _ptr(page_table, "page_table", i32, B * shape.max_pages),
         _ptr(ctx_lens_in, "ctx_lens_in", i32, B), _ptr(ctx_lens_out, "ctx_lens_out", i32, B),
+        None if loop_mode is None else _ptr(loop_mode, "loop_mode", i32, B),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 

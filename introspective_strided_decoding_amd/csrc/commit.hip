@@ -21,7 +21,8 @@ __global__ void fill_zero_u32(uint32_t* p, int n) {
 
 CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
                        void* v_pages, const int32_t* table, const int32_t* ctx_in,
-                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags, uint32_t* arrivals) {
+                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags, uint32_t* arrivals,
+                       const int32_t* loop_mode) {
   CommitArgs c;
   c.k_new = k_new;
   c.v_new = v_new;
@@ -33,6 +34,7 @@ CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new,
   c.ctx_out = ctx_out;
   c.flags = flags;
   c.arrivals = arrivals;
+  c.loop_mode = loop_mode;
   c.N = s.stride_n;
   c.Hkv = s.n_kv_heads;
   c.D = s.head_dim;

@@ -69,6 +69,7 @@ __device__ __forceinline__ void commit_row(const CommitArgs& c, int i, int r, in
   int L = c.ctx_in[r], n = c.n_commit[r];
   const bool bad_n = n < 0 || n > R, bad_L = L < 0 || L > cap;
   if (bad_n) n = n < 0 ? 0 : R;
+  if (c.loop_mode && c.loop_mode[r] == ISD_LOOP_REPROPOSE) n = 0;   // its accept result is ignored
   if (bad_L) { L = L < 0 ? 0 : cap; n = 0; }
   // rows 0..i must all be mapped for row i to be stored
   bool store = i < n;

@@ -254,7 +254,8 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
                              int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
                              float* logq_sel, const void* k_new, const void* v_new, void* k_pages,
                              void* v_pages, const int32_t* page_table, const int32_t* ctx_lens_in,
-                             int32_t* ctx_lens_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+                             int32_t* ctx_lens_out, const int32_t* loop_mode, void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
   isd_status st = check_shape(shape);
   if (st != ISD_OK) return st;
   if (!p_logits || !q_logits || !proposals || !req_ids || !positions || !accept_len || !out_tokens ||
@@ -273,7 +274,7 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
   char* ws = static_cast<char*>(workspace);
   const CommitArgs c = commit_args(*shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
                                    ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
-                                   reinterpret_cast<uint32_t*>(ws + L.cmt_cnt));
+                                   reinterpret_cast<uint32_t*>(ws + L.cmt_cnt), loop_mode);
   hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
                                seed_hi, step, step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit,
                                logp_sel, logq_sel, ws, L, &c, stream);

@@ -112,12 +112,14 @@ struct CommitArgs {
   int32_t* ctx_out;
   uint32_t* flags;
   uint32_t* arrivals;     // per request, rewound by the last arrival
+  const int32_t* loop_mode;   // per request (NULL: none): a re-proposing request commits nothing
   int N, Hkv, D, max_pages, num_pages;
   int kv_bf16;            // 1: bf16 pages, 0: fp32
 };
 CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
                        void* v_pages, const int32_t* table, const int32_t* ctx_in,
-                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags, uint32_t* arrivals);
+                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags, uint32_t* arrivals,
+                       const int32_t* loop_mode = nullptr);
 
 // Launchers (return the first HIP error, hipSuccess otherwise).
 hipError_t launch_attention(const isd_shape& s, const AttnPlan& p, const void* q,

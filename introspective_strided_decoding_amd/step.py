@@ -144,13 +144,16 @@ class DeviceStep:
             _lib.kv_commit, self.shape, self.k_new, self.v_new, self.k_pages, self.v_pages, self.page_table,
             self.ctx_lens, self.n_commit, self.ctx_lens_out, self.workspace))(stream)
 
-    def accept_commit(self, stream=None, step: Optional[int] = None, seed=None):
-        """accept, then commit of the accepted rows, in one library call."""
-        self._call("accept_commit", lambda: _lib.prepare(
+    def accept_commit(self, stream=None, step: Optional[int] = None, seed=None, device_step: bool = False,
+                      q_norms=None, loop: bool = False):
+        """accept, then commit of the accepted rows, in one library call; ``loop``: a
+        re-proposing request of the decoding loop commits nothing (the loop's mode)."""
+        self._call(("accept_commit", device_step, q_norms is not None, loop), lambda: _lib.prepare(
             _lib.isd_accept_commit, self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
             self.positions, self.seed, self.step, self.accept_len, self.out_tokens, self.n_out, self.n_commit,
             self.logp_sel, self.logq_sel, self.k_new, self.v_new, self.k_pages, self.v_pages, self.page_table,
-            self.ctx_lens, self.ctx_lens_out, self.workspace))(
+            self.ctx_lens, self.ctx_lens_out, self.workspace, step_dev=self._step_dev(device_step),
+            q_norms=q_norms, loop_mode=self.extra["mode"] if loop else None))(
             stream, self.step if step is None else step, self.seed if seed is None else seed)
 
     def propose(self, stream=None, mode: int = _lib.PROPOSE_SAMPLE, step: Optional[int] = None, seed=None,
@@ -228,14 +231,17 @@ class DeviceStep:
         e = self.extra
         q_norms = e["norms"] if carry and e.get("norms_valid") else None
         if attention:
+            # the accepted CLEAN rows are committed inside the accept launches, gated by the
+            # loop's mode as the bookkeeping gates n_commit
             self.attention(stream)
-        self._accept_and_propose(lambda s, t: self.accept(s, step=t, device_step=device_step, q_norms=q_norms),
-                                 stream, step, overlap, device_step, e["norms_new"] if carry else None)
+            accept = lambda s, t: self.accept_commit(s, step=t, device_step=device_step, q_norms=q_norms,
+                                                     loop=True)
+        else:
+            accept = lambda s, t: self.accept(s, step=t, device_step=device_step, q_norms=q_norms)
+        self._accept_and_propose(accept, stream, step, overlap, device_step, e["norms_new"] if carry else None)
         self.loop_advance(stream, carry=carry)
         if carry:
             e["norms_valid"] = True
-        if attention:
-            self.commit(stream)
 
     def capture_loop_forward(self, overlap: bool = True):
         """Record one ``loop_forward(device_step=True)`` into a HIP graph and return it.
@@ -245,8 +251,9 @@ class DeviceStep:
         comes from the forward counts.  The logits are read from the same buffers on
         every replay, so the caller refreshes them in place between replays.  Recording
         runs nothing; call ``loop_forward(device_step=True, overlap=...)`` eagerly at
-        least once before, so every call is marshalled and the second stream exists."""
-        if ("accept", True, True) not in self.__dict__.get("_calls", {}) or (
+        least twice before (the second forward is the first with carried q normalisers),
+        so every call is marshalled and the second stream exists."""
+        if ("accept_commit", True, True, True) not in self.__dict__.get("_calls", {}) or (
                 overlap and "side_stream" not in self.extra):
             raise RuntimeError("run loop_forward(device_step=True) eagerly before recording it")
         graph = torch.cuda.CUDAGraph()

@@ -116,8 +116,9 @@ def test_accept_and_commit_validation():
     bad[-2] = 0
     assert LIB.kv_commit(ctypes.byref(s.c()), *bad) == 4
     # isd_accept_commit: the accept arguments, then k_new .. ctx_lens_out, workspace, stream
-    fargs = [FAKE] * 5 + [1, 2, 3, None, None] + [FAKE] * 6 + [FAKE] * 7 + [FAKE, n, None]
-    assert len(fargs) == 26
+    # (then loop_mode, which may be NULL)
+    fargs = [FAKE] * 5 + [1, 2, 3, None, None] + [FAKE] * 6 + [FAKE] * 7 + [None] + [FAKE, n, None]
+    assert len(fargs) == 27
     for i in (2, 16, 20, 22):       # proposals, k_new, page_table, ctx_lens_out
         bad = list(fargs)
         bad[i] = None

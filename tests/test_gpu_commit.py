@@ -123,3 +123,34 @@ def test_accept_commit_equals_accept_then_commit(name, over, in_place):
     assert np.array_equal(v_got, v_ref)
     from introspective_strided_decoding_amd import isd_read_flags
     assert isd_read_flags(a.workspace) == 0 and isd_read_flags(b.workspace) == 0
+
+
+def test_accept_commit_with_loop_mode_commits_verifying_requests_only():
+    """With the decoding loop's modes, a re-proposing request commits no row and keeps its
+    length; the others commit what isd_accept decided: the same pools and lengths as
+    isd_accept, the gate isd_loop_advance applies, then kv_commit."""
+    from introspective_strided_decoding_amd._lib import LOOP_REPROPOSE, LOOP_VERIFY
+    cfg = get_config("b8_ctx2k", batch=9, ctx=20, vocab=3000)
+    steps = 3
+    wl = make_workload(cfg, seed=33, extra_tokens=steps * (cfg.stride_n - 1))
+    a = device_step(wl, commit_in_place=True)
+    b = device_step(wl, commit_in_place=True)
+    b.loop_start()
+    modes = [np.array([LOOP_REPROPOSE if (r + s) % 3 == 0 else LOOP_VERIFY for r in range(cfg.batch)],
+                      dtype=np.int32) for s in range(steps)]
+    for step in range(steps):
+        b.extra["mode"].copy_(torch.from_numpy(modes[step]).cuda())
+        a.accept(step=step)
+        torch.cuda.synchronize()
+        gated = a.n_commit.cpu().numpy().copy()
+        gated[modes[step] == LOOP_REPROPOSE] = 0
+        a.n_commit.copy_(torch.from_numpy(gated).cuda())
+        a.commit()
+        b.accept_commit(step=step, loop=True)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(a.ctx_lens_out), _bits(b.ctx_lens_out)), step
+        assert torch.equal(_bits(a.k_pages), _bits(b.k_pages)), step
+        assert torch.equal(_bits(a.v_pages), _bits(b.v_pages)), step
+        for f in ("accept_len", "out_tokens", "n_out"):
+            assert torch.equal(_bits(getattr(a, f)), _bits(getattr(b, f))), (step, f)
+    assert (modes[0] == LOOP_REPROPOSE).any() and (modes[0] == LOOP_VERIFY).any()
