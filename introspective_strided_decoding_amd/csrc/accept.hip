@@ -318,6 +318,8 @@ constexpr int kRPer = 8;
 constexpr int kRShard = kThreads * kRPer;
 constexpr double kResidBand = 1e-4;
 constexpr int kAmbSlots = 64;   // boundary entries a pass workgroup lists (more: the shard is recomputed)
+constexpr int kSerialAmb = 4;   // up to this many, one thread groups them
+static_assert(kSerialAmb <= kResidAmb, "a serial grouping never overflows");
 
 // 2^(j/64), j = 0..63, for exp_nonpos; call with all threads of the workgroup.
 __device__ __forceinline__ void fill_exp_table(double* tab64) {
@@ -475,7 +477,49 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   // sums do not depend on the order the entries were listed in.
   const int na = n_amb_sm;
   if (na > 0) {
-    if (na <= kAmbSlots) {
+    if (na <= kSerialAmb) {
+      // a few entries (most shards that have any): one thread sorts them by
+      // vocabulary index, groups them and orders the groups, without barriers
+      if (threadIdx.x == 0) {
+        for (int c = 1; c < na; ++c)
+          for (int j = c; j > 0 && amb_idx[j] < amb_idx[j - 1]; --j) {
+            const double tk = amb_key[j], t0 = amb_e[j][0], t1 = amb_e[j][1];
+            const int ti = amb_idx[j];
+            amb_key[j] = amb_key[j - 1];
+            amb_idx[j] = amb_idx[j - 1];
+            amb_e[j][0] = amb_e[j - 1][0];
+            amb_e[j][1] = amb_e[j - 1][1];
+            amb_key[j - 1] = tk;
+            amb_idx[j - 1] = ti;
+            amb_e[j - 1][0] = t0;
+            amb_e[j - 1][1] = t1;
+          }
+        int n_cls = 0;
+        for (int j = 0; j < na; ++j) {
+          int c = 0;
+          while (c < n_cls && cls_key[c] != amb_key[j]) ++c;
+          if (c == n_cls) {
+            cls_key[c] = amb_key[j];
+            cls_sum[c][0] = 0.0;
+            cls_sum[c][1] = 0.0;
+            ++n_cls;
+          }
+          cls_sum[c][0] += amb_e[j][0];
+          cls_sum[c][1] += amb_e[j][1];
+        }
+        for (int c = 1; c < n_cls; ++c)   // the groups in increasing order of their difference
+          for (int j = c; j > 0 && cls_key[j] < cls_key[j - 1]; --j) {
+            const double tk = cls_key[j], tp = cls_sum[j][0], tq = cls_sum[j][1];
+            cls_key[j] = cls_key[j - 1];
+            cls_sum[j][0] = cls_sum[j - 1][0];
+            cls_sum[j][1] = cls_sum[j - 1][1];
+            cls_key[j - 1] = tk;
+            cls_sum[j - 1][0] = tp;
+            cls_sum[j - 1][1] = tq;
+          }
+        n_cls_sm = n_cls;
+      }
+    } else if (na <= kAmbSlots) {
       // One thread per listed entry, each pass O(na): (1) move the entry to its
       // rank by vocabulary index (indices are distinct); (2) mark the first
       // entry of each difference; (3) a first entry's group number is the count
