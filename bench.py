@@ -154,15 +154,17 @@ def r_isd_projections(cfg, dev, stream, reps):
     proj = RIsdProjections(rows, stride_mask_rows(cfg.batch, cfg.stride_n), hidden=hidden, kv=kv,
                            mlp=3 * hidden, seed=11, device=dev)
     res = {"what": "q, k, v, o, gate, up, down projections of one layer; adapter rank 128 on the MASK rows; "
-                   "q/k/v and gate/up (which share an input) side by side on two streams",
+                   "one isd_gated_linear_group call per set of projections that share an input "
+                   "(q/k/v, o, gate/up, down)",
            "rows": rows, "gated_rows": int(proj.mask.numel()), "hidden": hidden, "kv": kv, "mlp": 3 * hidden}
-    for gated in (True, False):
+
+    def replay_ms(gated, mode):
         for _ in range(3):
-            proj.run(gated)
+            proj.run(gated, mode)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            proj.run(gated)     # siblings that share an input on two streams
+            proj.run(gated, mode)
         for _ in range(3):
             g.replay()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -172,33 +174,48 @@ def r_isd_projections(cfg, dev, stream, reps):
             g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
+        del g
+        return a.elapsed_time(b) / reps
+
+    for gated in (True, False):
+        ms = replay_ms(gated, "group")
         f, by = proj.flops(gated), proj.bytes(gated)
         res["gated" if gated else "base"] = {
             "ms": round(ms, 5), "tflops": round(f / ms / 1e9, 1),
             "mfma_frac": round(f / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
             "GBs": round(by / ms / 1e6, 1), "hbm_frac": round(by / ms / 1e6 / HBM_PEAK_GBS, 4),
             "flops": int(f), "bytes": int(by)}
-        del g
+    # one isd_gated_linear call per projection, siblings on two streams
+    per = {"gated_ms": round(replay_ms(True, "overlap"), 5), "base_ms": round(replay_ms(False, "overlap"), 5)}
+    per["alpha"] = round(per["gated_ms"] / per["base_ms"], 4)
+    res["per_projection_calls"] = per
     res["alpha"] = round(res["gated"]["ms"] / res["base"]["ms"], 4)
     t_mfma = proj.flops(False) / (MFMA_BF16_PEAK_TFLOPS * 1e9)
     t_hbm = proj.bytes(False) / (HBM_PEAK_GBS * 1e6)
     res["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
     res["base_frac_of_bound"] = round(max(t_mfma, t_hbm) / res["base"]["ms"], 4)
-    # the same base projections through torch.nn.functional.linear, one stream
+    # the same base projections through torch.nn.functional.linear, one stream: one call per
+    # projection, and one call per group on the group's weights concatenated (as a fused
+    # q/k/v or gate/up layer stores them)
+    def torch_ms(pairs):
+        for _ in range(3):
+            for x, w in pairs:
+                F.linear(x, w)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            for x, w in pairs:
+                F.linear(x, w)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    from introspective_strided_decoding_amd.r_isd import GROUPS
     pairs = [(t["X"], t["W_t"]) for t in proj.p.values()]
-    for _ in range(3):
-        for x, w in pairs:
-            F.linear(x, w)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(reps):
-        for x, w in pairs:
-            F.linear(x, w)
-    b.record(stream)
-    torch.cuda.synchronize()
-    res["torch_linear_base_ms"] = round(a.elapsed_time(b) / reps, 5)
+    res["torch_linear_base_ms"] = round(torch_ms(pairs), 5)
+    pairs = [(proj.p[grp[0]]["X"], torch.cat([proj.p[nm]["W_t"] for nm in grp])) for grp in GROUPS]
+    res["torch_linear_fused_base_ms"] = round(torch_ms(pairs), 5)
     del proj, pairs
     torch.cuda.empty_cache()
     return res

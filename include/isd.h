@@ -24,6 +24,8 @@
  *                  MASK rows only.
  *   isd_gated_linear  a whole R-ISD projection: base weights on every row,
  *                  the adapter fused in on the MASK rows.
+ *   isd_gated_linear_group  up to four such projections of one input (the
+ *                  q, k and v projections; gate and up) in one set of launches.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -449,8 +451,9 @@ isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t ran
  * over W run in an order fixed by (rows, d_in, d_out) alone), provided B_t is
  * finite.
  *
- * Supported: 1 <= rows <= 65536, d_in % 256 == 0, d_out % 128 == 0, rank in
- * {0, 128}, 0 <= n_mask <= rows, scale not NaN or infinite.  Workspace: at
+ * Supported: 1 <= rows <= 65536, 256 <= d_in <= 65536 with d_in % 256 == 0,
+ * d_out % 128 == 0, rows * d_out <= 2^30, rank in {0, 128}, 0 <= n_mask <=
+ * rows, scale not NaN or infinite.  Workspace: at
  * least isd_gated_linear_workspace_bytes() bytes (0 for an unsupported
  * shape); its first 4 bytes are a flag word that the caller zeroes before
  * the first call (ISD_FLAG_ROW_RANGE: a gated row outside [0, rows) is
@@ -465,6 +468,41 @@ isd_status isd_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_t r
                             const void* W_t, const void* A_t, const void* B_t, const int32_t* mask_rows,
                             int32_t n_mask, float scale, void* Y, void* workspace, size_t ws_bytes,
                             hipStream_t stream);
+
+/*
+ * isd_gated_linear_group -- n_proj (1..4) projections of the same input X
+ * and the same gated rows, each as isd_gated_linear defines it:
+ *
+ *   Y_p[m][:] = X[m][:] @ W_p + gate[m] * scale * (X[m][:] @ A_p) @ B_p
+ *
+ * (source as isd_gated_linear's).  In a transformer layer the q, k and v
+ * projections read the same normed hidden state, and so do the MLP's gate
+ * and up projections; one call reads X's gated rows once for all adapters
+ * and runs every projection's product in one launch whose output tiles span
+ * the group, so narrow members (k, v) fill the chip together with the wide
+ * one instead of each splitting its k range alone.
+ *
+ * d_out, W_t, A_t, B_t and Y are HOST arrays of n_proj entries, read during
+ * the call only; the pointers they hold are device pointers with the
+ * layouts of isd_gated_linear ([d_out[p]][d_in], [rank][d_in],
+ * [d_out[p]][rank], [rows][d_out[p]]).  A_t and B_t may be NULL when
+ * rank == 0.  The outputs Y[p] must not overlap each other or X.  With one
+ * projection the call is isd_gated_linear (same kernels, same results).
+ * The tiling follows the summed width sum_p d_out[p]; a row outside the gate
+ * equals the rank == 0 group call's row bit for bit (not necessarily the
+ * single-projection call's, whose k split may differ).
+ *
+ * Supported: 1 <= n_proj <= 4, each d_out[p] % 128 == 0, rows * sum_p
+ * d_out[p] <= 2^30, and the limits of isd_gated_linear.  Workspace: at least
+ * isd_gated_linear_group_workspace_bytes() bytes (0 for an unsupported
+ * shape), flag word as isd_gated_linear's.  Errors: as isd_gated_linear's.
+ */
+size_t isd_gated_linear_group_workspace_bytes(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out,
+                                              int32_t rank, int32_t n_mask);
+isd_status isd_gated_linear_group(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out, int32_t rank,
+                                  const void* X, const void* const* W_t, const void* const* A_t,
+                                  const void* const* B_t, const int32_t* mask_rows, int32_t n_mask, float scale,
+                                  void* const* Y, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Text for a status code (static storage). */
 const char* isd_status_string(isd_status status);

@@ -28,6 +28,7 @@ STATUS = {0: "ISD_OK", 1: "ISD_ERR_NULL", 2: "ISD_ERR_SHAPE", 3: "ISD_ERR_DTYPE"
 EXPORTS = ("isd_workspace_bytes", "isd_workspace_init", "isd_read_flags", "isd_attention",
            "isd_accept", "kv_commit", "isd_accept_commit", "isd_propose", "isd_loop_advance", "isd_lora_workspace_bytes",
            "isd_lora_delta", "isd_gated_linear_workspace_bytes", "isd_gated_linear",
+           "isd_gated_linear_group_workspace_bytes", "isd_gated_linear_group",
            "isd_status_string", "isd_last_error", "isd_abi_version")
 PROPOSE_SAMPLE, PROPOSE_ARGMAX = 0, 1
 LOOP_VERIFY, LOOP_REPROPOSE = 0, 1
@@ -93,6 +94,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "isd_lora_delta": (I32, [I32, I32, I32, I32, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
         "isd_gated_linear_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
         "isd_gated_linear": (I32, [I32, I32, I32, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
+        "isd_gated_linear_group_workspace_bytes": (SZ, [I32, I32, I32, P, I32, I32]),
+        "isd_gated_linear_group": (I32, [I32, I32, I32, P, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, SZ, P]),
         "isd_status_string": (ctypes.c_char_p, [I32]),
         "isd_last_error": (ctypes.c_char_p, []),
         "isd_abi_version": (I32, []),
@@ -381,3 +384,41 @@ def isd_gated_linear(X, W_t, Y, workspace, A_t=None, B_t=None, mask_rows=None, s
           rows, d_in, d_out, rank, _ptr(X, "X", bf), _ptr(W_t, "W_t", bf, d_out * d_in), a, b, m, n_mask,
           float(scale), _ptr(Y, "Y", bf, rows * d_out), _ptr(workspace, "workspace", torch.uint8),
           workspace.numel(), _stream(stream))
+
+
+def _host_array(ctype, values):
+    """A host array of ctype (the group call's per-projection sizes and pointers)."""
+    return (ctype * len(values))(*values)
+
+
+def isd_gated_linear_group_workspace_bytes(rows: int, d_in: int, d_outs, rank: int, n_mask: int) -> int:
+    d = _host_array(ctypes.c_int32, [int(v) for v in d_outs])
+    return int(LIB.isd_gated_linear_group_workspace_bytes(len(d_outs), rows, d_in, d, rank, n_mask))
+
+
+def isd_gated_linear_group(X, W_ts, Ys, workspace, A_ts=None, B_ts=None, mask_rows=None, scale: float = 1.0,
+                           stream=None) -> None:
+    """Ys[p] = X @ W_ts[p].T, plus scale * (X[m] @ A_ts[p].T) @ B_ts[p].T on the gated rows m
+    when adapters are given: up to four projections of one input in one set of launches
+    (see include/isd.h)."""
+    rows, d_in = X.shape
+    n = len(W_ts)
+    if len(Ys) != n or (A_ts is not None and (len(A_ts) != n or len(B_ts) != n)):
+        raise ValueError("W_ts, Ys, A_ts and B_ts need one entry per projection")
+    bf = torch.bfloat16
+    d_outs = [int(w.shape[0]) for w in W_ts]
+    d = _host_array(ctypes.c_int32, d_outs)
+    w = _host_array(ctypes.c_void_p, [_ptr(t, f"W_ts[{i}]", bf, d_outs[i] * d_in) for i, t in enumerate(W_ts)])
+    y = _host_array(ctypes.c_void_p, [_ptr(t, f"Ys[{i}]", bf, rows * d_outs[i]) for i, t in enumerate(Ys)])
+    if A_ts is None:
+        rank, a, b, m, n_mask = 0, None, None, None, 0
+    else:
+        rank = A_ts[0].shape[0]
+        a = _host_array(ctypes.c_void_p, [_ptr(t, f"A_ts[{i}]", bf, rank * d_in) for i, t in enumerate(A_ts)])
+        b = _host_array(ctypes.c_void_p, [_ptr(t, f"B_ts[{i}]", bf, d_outs[i] * rank) for i, t in enumerate(B_ts)])
+        n_mask = mask_rows.numel()
+        m = _ptr(mask_rows, "mask_rows", torch.int32)
+    # the host arrays themselves go into the call, so a recorded argument list keeps them alive
+    _call("isd_gated_linear_group",
+          n, rows, d_in, d, rank, _ptr(X, "X", bf), w, a, b, m, n_mask, float(scale),
+          y, _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))

@@ -1,14 +1,18 @@
-// One projection of an R-ISD layer (isd_gated_linear):
+// The projections of an R-ISD layer (isd_gated_linear, and
+// isd_gated_linear_group for up to four projections of one input):
 //
-//   Y[m] = X[m] W^T + gate[m] * scale * (X[m] A^T) B^T
+//   Y_p[m] = X[m] W_p^T + gate[m] * scale * (X[m] A_p^T) B_p^T
+//
+// A group runs as one projection whose output columns are the projections'
+// side by side: each launch below covers every projection of the group.
 //
 // The adapter's second product rides in the base product's k loop: with
 // T[m] = bf16(gate[m] * scale * X[m] A^T) (zero on CLEAN rows), Y is one
 // product of [X | T] with [W | B] over d_in + rank columns.
 //
-//   lora_down   T_part[kc][g][r] = sum over a 256-wide k chunk of X[row(g)] A^T
+//   lora_down   T_part[p][kc][g][r] = sum over a 256-wide k chunk of X[row(g)] A_p^T
 //               (the same kernel as isd_lora_delta's), clearing T on the side
-//   gl_scatter  T[row(g)] = bf16(scale * sum_kc T_part[kc][g]) for gated g
+//   gl_scatter  T_p[row(g)] = bf16(scale * sum_kc T_part[p][kc][g]) for gated g
 //   gl_gemm     the product, bf16 matrix-core operands, fp32 sums; the rank
 //               columns come first, so a row whose T is zero enters the base
 //               columns with the same +0 accumulators as the base-only call
@@ -53,11 +57,39 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
+// The projections of one launch.  Output tiles are numbered across the group:
+// projection p owns tile columns tile_end[p-1] .. tile_end[p]-1 (tile_end[-1] = 0).
+struct GlGroup {
+  int n;
+  int tile_end[kGlMaxProj];
+  int d_out[kGlMaxProj];
+  const uint16_t* W[kGlMaxProj];    // [d_out][K]
+  const uint16_t* Bt[kGlMaxProj];   // [d_out][R]
+  const uint16_t* T[kGlMaxProj];    // [M][R]
+  uint16_t* Y[kGlMaxProj];          // [M][d_out]
+  float* part[kGlMaxProj];          // [splits][M][d_out]
+};
+
+// Projection owning global tile column ni, and its members (constant indices
+// only, so the group stays in the kernel-argument segment).
+struct GlProj {
+  int first_tile, N;
+  const uint16_t *W, *Bt, *T;
+  uint16_t* Y;
+  float* part;
+};
+__device__ __forceinline__ GlProj gl_proj(const GlGroup& g, int ni) {
+  GlProj q{0, g.d_out[0], g.W[0], g.Bt[0], g.T[0], g.Y[0], g.part[0]};
+#pragma unroll
+  for (int i = 1; i < kGlMaxProj; ++i)
+    if (i < g.n && ni >= g.tile_end[i - 1])
+      q = GlProj{g.tile_end[i - 1], g.d_out[i], g.W[i], g.Bt[i], g.T[i], g.Y[i], g.part[i]};
+  return q;
+}
+
 template <int BM, int BN, int ST, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int K, const uint16_t* __restrict__ T,
-    const uint16_t* __restrict__ Bt, int R, int M, int N, int m_tiles, int splits, uint16_t* __restrict__ Y,
-    float* __restrict__ part) {
+    const uint16_t* __restrict__ X, int K, int R, int M, int m_tiles, int splits, const GlGroup g) {
   constexpr int NW = WGM * WGN;                // waves: WGM along X rows, WGN along W rows
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   constexpr int IX = BM / (8 * NW), IW = BN / (8 * NW);    // 1 KB direct-to-LDS loads per wave per block
@@ -73,7 +105,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
   const int l = xcd * per + min(xcd, extra) + (b >> 3);
   const int mi = l % m_tiles, rest = l / m_tiles;
   const int s = rest % splits, ni = rest / splits;
-  const int m0 = mi * BM, n0 = ni * BN;
+  const GlProj pj = gl_proj(g, ni);
+  const uint16_t* __restrict__ W = pj.W;
+  const uint16_t* __restrict__ T = pj.T;
+  const uint16_t* __restrict__ Bt = pj.Bt;
+  const int N = pj.N;
+  const int m0 = mi * BM, n0 = (ni - pj.first_tile) * BN;
 
   const int kb_base = K / kBK;
   const int b0 = s * kb_base / splits, b1 = (s + 1) * kb_base / splits;
@@ -165,31 +202,45 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
         const float y0 = acc[a][c][4 * v4], y1 = acc[a][c][4 * v4 + 1];
         const float y2 = acc[a][c][4 * v4 + 2], y3 = acc[a][c][4 * v4 + 3];
         if (splits == 1) {
-          *reinterpret_cast<uint2*>(Y + size_t(m) * N + n) =
+          *reinterpret_cast<uint2*>(pj.Y + size_t(m) * N + n) =
               make_uint2(uint32_t(f32_to_bf16_bits(y0)) | (uint32_t(f32_to_bf16_bits(y1)) << 16),
                          uint32_t(f32_to_bf16_bits(y2)) | (uint32_t(f32_to_bf16_bits(y3)) << 16));
         } else {
-          *reinterpret_cast<f32x4*>(part + (size_t(s) * M + m) * N + n) = f32x4{y0, y1, y2, y3};
+          *reinterpret_cast<f32x4*>(pj.part + (size_t(s) * M + m) * N + n) = f32x4{y0, y1, y2, y3};
         }
       }
     }
   }
 }
 
-__global__ __launch_bounds__(256) void gl_reduce(const f32x4* __restrict__ part, int splits, int count4,
-                                                 uint2* __restrict__ Y) {
+// One thread per 4 outputs of projection blockIdx.y.
+__global__ __launch_bounds__(256) void gl_reduce(const GlGroup g, int M, int splits) {
+  const int p = blockIdx.y;
+  int c4 = M * (g.d_out[0] / 4);
+  const f32x4* __restrict__ part = reinterpret_cast<const f32x4*>(g.part[0]);
+  uint2* __restrict__ Y = reinterpret_cast<uint2*>(g.Y[0]);
+#pragma unroll
+  for (int i = 1; i < kGlMaxProj; ++i)
+    if (p == i) {
+      c4 = M * (g.d_out[i] / 4);
+      part = reinterpret_cast<const f32x4*>(g.part[i]);
+      Y = reinterpret_cast<uint2*>(g.Y[i]);
+    }
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= count4) return;
+  if (i >= c4) return;
   f32x4 v = part[i];
-  for (int s = 1; s < splits; ++s) v += part[size_t(s) * count4 + i];
+  for (int s = 1; s < splits; ++s) v += part[size_t(s) * c4 + i];
   Y[i] = make_uint2(uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16),
                     uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16));
 }
 
-// One thread per (gated row, rank column); part is [kchunks][m_pad][128].
+// One thread per (gated row, rank column) of projection blockIdx.y; part is
+// [projection][kchunks][m_pad][128], T is [projection][rows][128].
 __global__ __launch_bounds__(256) void gl_scatter(const float* __restrict__ part, int kchunks, int m_pad,
                                                   const int32_t* __restrict__ mask_rows, int n_mask, int rows,
                                                   float scale, uint16_t* __restrict__ T) {
+  part += size_t(blockIdx.y) * kchunks * m_pad * kRank;
+  T += size_t(blockIdx.y) * rows * kRank;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int g = e / kRank, r = e % kRank;
   if (g >= n_mask) return;
@@ -217,16 +268,25 @@ __global__ __launch_bounds__(256) void gl_scatter(const float* __restrict__ part
 // same tiles no faster than the direct-to-LDS ones (about 45 GB/s per busy CU
 // from L2 either way).  So the plan trades bytes per flop (tile size) against
 // keeping all 256 CUs busy (tile count, split).
-GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out) {
+// A group is planned as one projection of the summed width; a tile width
+// only when every member's width is a multiple of it (no tile straddles two).
+// Between 256 x 256 and 256 x 192 tiles the cost is rounds of the chip times
+// the bytes a tile loads per k block: a 256 x 192 tiling that fills whole
+// rounds (512 tiles of an 896-row, 24576-wide group, where 256 x 256 leaves
+// 384 = 1.5 rounds) loads less per CU.
+GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out, bool all256, bool all192) {
   GlPlan p;
   const int kb = d_in / kBK;
   const long t128 = long((rows + 127) / 128) * (d_out / 128);
-  const long t256 = d_out % 256 ? 0 : long((rows + 255) / 256) * (d_out / 256);
+  const long t256 = all256 ? long((rows + 255) / 256) * (d_out / 256) : 0;
+  const long t192 = all192 ? long((rows + 255) / 256) * (d_out / 192) : 0;
+  auto cost = [](long tiles, int bn) { return (tiles + 255) / 256 * (256 + bn); };
   auto split_to = [&](long tiles) {
     while (tiles * p.splits < 256 && kb / (2 * p.splits) >= 8) p.splits *= 2;
   };
-  if (t256 >= 160 && rows >= 512) {
-    p.bm = 256;                        // 256 x 256 tiles, 8 waves of 128 x 64
+  if (rows >= 512 && std::max(t256, t192) >= 160) {
+    p.bm = 256;                        // 8 waves: of 128 x 64 (256 x 256) or 64 x 96 (256 x 192)
+    p.bn = (t192 >= 160 && (t256 < 160 || cost(t192, 192) < cost(t256, 256))) ? 192 : 256;
     p.stages = 2;
     p.waves = 8;
   } else if (t128 >= 384) {
@@ -239,7 +299,7 @@ GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out) {
       p.waves = 8;                     // 8 waves of 64 x 32
     }
   } else if (d_out <= 2048) {
-    p.bm = 64;
+    p.bm = p.bn = 64;
     split_to(long((rows + 63) / 64) * (d_out / 64));
   } else {
     split_to(t128);
@@ -247,74 +307,106 @@ GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out) {
   return p;
 }
 
-GlLayout gl_layout(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, int32_t n_mask) {
+GlLayout gl_layout(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out, int32_t rank,
+                   int32_t n_mask) {
   GlLayout L;
-  L.plan = gl_plan(rows, d_in, d_out);
+  long total = 0;
+  bool all256 = true, all192 = true;
+  for (int p = 0; p < n_proj; ++p) {
+    total += d_out[p];
+    all256 = all256 && d_out[p] % 256 == 0;
+    all192 = all192 && d_out[p] % 192 == 0;
+  }
+  L.plan = gl_plan(rows, d_in, int32_t(total), all256, all192);
   size_t off = kHeaderBytes;
   if (rank > 0) {
     L.t = off;
-    off += (size_t(rows) * rank * 2 + 255) / 256 * 256;
+    off += (size_t(n_proj) * rows * rank * 2 + 255) / 256 * 256;
     L.down = off;
-    off += size_t(d_in / 256) * size_t((n_mask + 31) / 32 * 32) * rank * 4;
+    off += size_t(n_proj) * size_t(d_in / 256) * size_t((n_mask + 31) / 32 * 32) * rank * 4;
     off = (off + 255) / 256 * 256;
   }
   if (L.plan.splits > 1) {
     L.split = off;
-    off += size_t(L.plan.splits) * rows * d_out * 4;
+    off += size_t(L.plan.splits) * rows * size_t(total) * 4;
   }
   L.total = (off + 255) / 256 * 256;
   return L;
 }
 
-hipError_t launch_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
-                               const void* W_t, const void* A_t, const void* B_t, const int32_t* mask_rows,
-                               int32_t n_mask, float scale, void* Y, char* ws, hipStream_t stream) {
-  if (n_mask == 0) rank = 0;     // no gated row: the base projection, bit for bit
-  const GlLayout L = gl_layout(rows, d_in, d_out, rank, n_mask);
-  const uint16_t* T = nullptr;
+hipError_t launch_gated_linear(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out, int32_t rank,
+                               const void* X, const void* const* W_t, const void* const* A_t,
+                               const void* const* B_t, const int32_t* mask_rows, int32_t n_mask, float scale,
+                               void* const* Y, char* ws, hipStream_t stream) {
+  if (n_mask == 0) rank = 0;     // no gated row: the base projections, bit for bit
+  const GlLayout L = gl_layout(n_proj, rows, d_in, d_out, rank, n_mask);
+  const GlPlan& pl = L.plan;
+  GlGroup g{};
+  g.n = n_proj;
+  int max_d = 0;
+  for (int p = 0; p < n_proj; ++p) {
+    g.d_out[p] = d_out[p];
+    g.W[p] = static_cast<const uint16_t*>(W_t[p]);
+    g.Y[p] = static_cast<uint16_t*>(Y[p]);
+    max_d = d_out[p] > max_d ? d_out[p] : max_d;
+  }
   if (rank > 0) {
     uint16_t* t = reinterpret_cast<uint16_t*>(ws + L.t);
     float* down = reinterpret_cast<float*>(ws + L.down);
-    hipError_t e = launch_lora_down(X, A_t, mask_rows, n_mask, rows, d_in, down,
-                                    reinterpret_cast<uint32_t*>(ws), t, size_t(rows) * rank * 2, stream);
+    hipError_t e = launch_lora_down(X, A_t, n_proj, mask_rows, n_mask, rows, d_in, down,
+                                    reinterpret_cast<uint32_t*>(ws), t, size_t(n_proj) * rows * rank * 2, stream);
     if (e != hipSuccess) return e;
     const int m_pad = (n_mask + 31) / 32 * 32;
-    hipLaunchKernelGGL(gl_scatter, dim3((n_mask * kRank + 255) / 256), dim3(256), 0, stream, down, d_in / 256,
-                       m_pad, mask_rows, n_mask, rows, scale, t);
-    T = t;
+    hipLaunchKernelGGL(gl_scatter, dim3((n_mask * kRank + 255) / 256, n_proj), dim3(256), 0, stream, down,
+                       d_in / 256, m_pad, mask_rows, n_mask, rows, scale, t);
+    for (int p = 0; p < n_proj; ++p) {
+      g.T[p] = t + size_t(p) * rows * kRank;
+      g.Bt[p] = static_cast<const uint16_t*>(B_t[p]);
+    }
   }
-  const GlPlan& p = L.plan;
-  float* part = p.splits > 1 ? reinterpret_cast<float*>(ws + L.split) : nullptr;
+  if (pl.splits > 1) {
+    float* part = reinterpret_cast<float*>(ws + L.split);
+    size_t off = 0;
+    for (int p = 0; p < n_proj; ++p) {
+      g.part[p] = part + off;
+      off += size_t(pl.splits) * rows * d_out[p];
+    }
+  }
+  auto tiles = [&](int bn) {
+    int end = 0;
+    for (int p = 0; p < n_proj; ++p) g.tile_end[p] = end += d_out[p] / bn;
+    return end;
+  };
   const int R = rank > 0 ? kRank : 0;
   const auto* x = static_cast<const uint16_t*>(X);
-  const auto* w = static_cast<const uint16_t*>(W_t);
-  const auto* bt = static_cast<const uint16_t*>(B_t);
-  auto* y = static_cast<uint16_t*>(Y);
-  if (p.bm == 256) {
+  if (pl.bm == 256) {
     const int mt = (rows + 255) / 256;
-    hipLaunchKernelGGL((gl_gemm<256, 256, 2, 2, 4>), dim3(mt * (d_out / 256) * p.splits), dim3(512), 0, stream, x, w,
-                       d_in, T, bt, R, rows, d_out, mt, p.splits, y, part);
-  } else if (p.bm == 128) {
-    const int mt = (rows + 127) / 128;
-    const dim3 grid(mt * (d_out / 128) * p.splits);
-    if (p.stages == 2)
-      hipLaunchKernelGGL((gl_gemm<128, 128, 2, 2, 2>), grid, dim3(256), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
-                         mt, p.splits, y, part);
-    else if (p.waves == 8)
-      hipLaunchKernelGGL((gl_gemm<128, 128, 4, 2, 4>), grid, dim3(512), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
-                         mt, p.splits, y, part);
+    if (pl.bn == 192)
+      hipLaunchKernelGGL((gl_gemm<256, 192, 2, 4, 2>), dim3(mt * tiles(192) * pl.splits), dim3(512), 0, stream, x,
+                         d_in, R, rows, mt, pl.splits, g);
     else
-      hipLaunchKernelGGL((gl_gemm<128, 128, 4, 2, 2>), grid, dim3(256), 0, stream, x, w, d_in, T, bt, R, rows, d_out,
-                         mt, p.splits, y, part);
+      hipLaunchKernelGGL((gl_gemm<256, 256, 2, 2, 4>), dim3(mt * tiles(256) * pl.splits), dim3(512), 0, stream, x,
+                         d_in, R, rows, mt, pl.splits, g);
+  } else if (pl.bm == 128) {
+    const int mt = (rows + 127) / 128;
+    const dim3 grid(mt * tiles(128) * pl.splits);
+    if (pl.stages == 2)
+      hipLaunchKernelGGL((gl_gemm<128, 128, 2, 2, 2>), grid, dim3(256), 0, stream, x, d_in, R, rows, mt, pl.splits,
+                         g);
+    else if (pl.waves == 8)
+      hipLaunchKernelGGL((gl_gemm<128, 128, 4, 2, 4>), grid, dim3(512), 0, stream, x, d_in, R, rows, mt, pl.splits,
+                         g);
+    else
+      hipLaunchKernelGGL((gl_gemm<128, 128, 4, 2, 2>), grid, dim3(256), 0, stream, x, d_in, R, rows, mt, pl.splits,
+                         g);
   } else {
     const int mt = (rows + 63) / 64;
-    hipLaunchKernelGGL((gl_gemm<64, 64, 4, 2, 2>), dim3(mt * (d_out / 64) * p.splits), dim3(256), 0, stream, x, w,
-                       d_in, T, bt, R, rows, d_out, mt, p.splits, y, part);
+    hipLaunchKernelGGL((gl_gemm<64, 64, 4, 2, 2>), dim3(mt * tiles(64) * pl.splits), dim3(256), 0, stream, x, d_in,
+                       R, rows, mt, pl.splits, g);
   }
-  if (p.splits > 1) {
-    const int count4 = rows * d_out / 4;
-    hipLaunchKernelGGL(gl_reduce, dim3((count4 + 255) / 256), dim3(256), 0, stream,
-                       reinterpret_cast<const f32x4*>(part), p.splits, count4, reinterpret_cast<uint2*>(Y));
+  if (pl.splits > 1) {
+    const int count4 = rows * (max_d / 4);
+    hipLaunchKernelGGL(gl_reduce, dim3((count4 + 255) / 256, n_proj), dim3(256), 0, stream, g, rows, pl.splits);
   }
   return hipGetLastError();
 }

@@ -160,7 +160,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 7; }
+int32_t isd_abi_version(void) { return 8; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {
@@ -359,29 +359,73 @@ isd_status isd_lora_delta(int32_t rows, int32_t d_in, int32_t d_out, int32_t ran
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_lora_delta");
 }
 
+namespace {
+
+// Shape check shared by the gated projection entries: ISD_OK, or the status
+// the call returns (the workspace query answers 0 for any failure).
+isd_status gl_shape(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out, int32_t rank,
+                    int32_t n_mask) {
+  if (!d_out) return ISD_ERR_NULL;
+  if (n_proj < 1 || rows < 1 || d_in < 1 || rank < 0 || n_mask < 0 || n_mask > rows) return ISD_ERR_SHAPE;
+  if (n_proj > kGlMaxProj || rows > kGlMaxRows || d_in > (1 << 16) || d_in % 256 || (rank != 0 && rank != 128))
+    return ISD_ERR_UNSUPPORTED;
+  long total = 0;
+  for (int p = 0; p < n_proj; ++p) {
+    if (d_out[p] < 1) return ISD_ERR_SHAPE;
+    if (d_out[p] % 128) return ISD_ERR_UNSUPPORTED;
+    total += d_out[p];
+  }
+  if (long(rows) * total > kGlMaxOut) return ISD_ERR_UNSUPPORTED;
+  return ISD_OK;
+}
+
+isd_status gated_group(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out, int32_t rank,
+                       const void* X, const void* const* W_t, const void* const* A_t, const void* const* B_t,
+                       const int32_t* mask_rows, int32_t n_mask, float scale, void* const* Y, void* workspace,
+                       size_t ws_bytes, hipStream_t stream, const char* name) {
+  if (isd_status st = gl_shape(n_proj, rows, d_in, d_out, rank, n_mask)) return st;
+  if (!(scale == scale) || scale - scale != 0.f) return ISD_ERR_SHAPE;
+  if (!X || !W_t || !Y || !workspace) return ISD_ERR_NULL;
+  if (rank > 0 && (!A_t || !B_t || (n_mask > 0 && !mask_rows))) return ISD_ERR_NULL;
+  if (!aligned16(X) || !aligned16(workspace)) return ISD_ERR_ALIGNMENT;
+  for (int p = 0; p < n_proj; ++p) {
+    if (!W_t[p] || !Y[p] || (rank > 0 && (!A_t[p] || !B_t[p]))) return ISD_ERR_NULL;
+    if (!aligned16(W_t[p]) || !aligned16(Y[p]) || (rank > 0 && (!aligned16(A_t[p]) || !aligned16(B_t[p]))))
+      return ISD_ERR_ALIGNMENT;
+  }
+  if (ws_bytes < gl_layout(n_proj, rows, d_in, d_out, rank, n_mask).total) return ISD_ERR_WORKSPACE;
+  hipError_t e = launch_gated_linear(n_proj, rows, d_in, d_out, rank, X, W_t, A_t, B_t, mask_rows, n_mask, scale,
+                                     Y, static_cast<char*>(workspace), stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, name);
+}
+
+}  // namespace
+
 size_t isd_gated_linear_workspace_bytes(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank,
                                         int32_t n_mask) {
-  if (rows < 1 || rows > kGlMaxRows || d_in < 256 || d_in % 256 || d_out < 128 || d_out % 128) return 0;
-  if ((rank != 0 && rank != 128) || n_mask < 0 || n_mask > rows) return 0;
-  return gl_layout(rows, d_in, d_out, rank, n_mask).total;
+  return isd_gated_linear_group_workspace_bytes(1, rows, d_in, &d_out, rank, n_mask);
 }
 
 isd_status isd_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
                             const void* W_t, const void* A_t, const void* B_t, const int32_t* mask_rows,
                             int32_t n_mask, float scale, void* Y, void* workspace, size_t ws_bytes,
                             hipStream_t stream) {
-  if (rows < 1 || d_in < 1 || d_out < 1 || rank < 0 || n_mask < 0 || n_mask > rows) return ISD_ERR_SHAPE;
-  if (rows > kGlMaxRows || d_in % 256 || d_out % 128 || (rank != 0 && rank != 128)) return ISD_ERR_UNSUPPORTED;
-  if (!(scale == scale) || scale - scale != 0.f) return ISD_ERR_SHAPE;
-  if (!X || !W_t || !Y || !workspace) return ISD_ERR_NULL;
-  if (rank > 0 && (!A_t || !B_t || (n_mask > 0 && !mask_rows))) return ISD_ERR_NULL;
-  if (!aligned16(X) || !aligned16(W_t) || !aligned16(Y) || !aligned16(workspace) ||
-      (rank > 0 && (!aligned16(A_t) || !aligned16(B_t))))
-    return ISD_ERR_ALIGNMENT;
-  if (ws_bytes < gl_layout(rows, d_in, d_out, rank, n_mask).total) return ISD_ERR_WORKSPACE;
-  hipError_t e = launch_gated_linear(rows, d_in, d_out, rank, X, W_t, A_t, B_t, mask_rows, n_mask, scale, Y,
-                                     static_cast<char*>(workspace), stream);
-  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_gated_linear");
+  return gated_group(1, rows, d_in, &d_out, rank, X, &W_t, rank > 0 ? &A_t : nullptr, rank > 0 ? &B_t : nullptr,
+                     mask_rows, n_mask, scale, &Y, workspace, ws_bytes, stream, "isd_gated_linear");
+}
+
+size_t isd_gated_linear_group_workspace_bytes(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out,
+                                              int32_t rank, int32_t n_mask) {
+  if (gl_shape(n_proj, rows, d_in, d_out, rank, n_mask) != ISD_OK) return 0;
+  return gl_layout(n_proj, rows, d_in, d_out, rank, n_mask).total;
+}
+
+isd_status isd_gated_linear_group(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out, int32_t rank,
+                                  const void* X, const void* const* W_t, const void* const* A_t,
+                                  const void* const* B_t, const int32_t* mask_rows, int32_t n_mask, float scale,
+                                  void* const* Y, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return gated_group(n_proj, rows, d_in, d_out, rank, X, W_t, A_t, B_t, mask_rows, n_mask, scale, Y, workspace,
+                     ws_bytes, stream, "isd_gated_linear_group");
 }
 
 }  // extern "C"

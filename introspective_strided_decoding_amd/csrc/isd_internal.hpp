@@ -162,33 +162,41 @@ hipError_t launch_lora(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, 
                        const void* A, const void* Bm, const int32_t* mask_rows, int32_t n_mask,
                        float scale, void* Y, char* ws, hipStream_t stream);
 
-hipError_t launch_lora_down(const void* X, const void* A_t, const int32_t* mask_rows, int32_t n_mask,
-                            int32_t rows, int32_t d_in, float* part, uint32_t* flags, void* zero16,
-                            size_t zero_bytes, hipStream_t stream);
+constexpr int kGlMaxProj = 4;             // projections of one gated group call
+
+// The adapter's down-projection partials of up to kGlMaxProj adapters A_t[p]
+// over the same gated rows of X: part is [p][d_in/256][n_mask padded to 32][128].
+hipError_t launch_lora_down(const void* X, const void* const* A_t, int32_t n_sets, const int32_t* mask_rows,
+                            int32_t n_mask, int32_t rows, int32_t d_in, float* part, uint32_t* flags,
+                            void* zero16, size_t zero_bytes, hipStream_t stream);
 
 constexpr int32_t kGlMaxRows = 1 << 16;   // rows of one gated projection call
+constexpr long kGlMaxOut = 1L << 30;      // rows x summed output width of one call
 
 // Gated projection: tile shape and k split, a function of the shape alone so a
 // gated call and the base-only call of the same shape sum in the same order.
 struct GlPlan {
-  int bm = 128;       // square tiles of bm x bm outputs: 256, 128 or 64
+  int bm = 128;       // tiles of bm rows x bn outputs: 256 x 256, 256 x 192, 128 x 128 or 64 x 64
+  int bn = 128;
   int stages = 4;     // LDS ring depth
   int waves = 4;      // waves per workgroup: 4 or 8
   int splits = 1;     // k split into this many ranges, summed by a second kernel
 };
-GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out);
+GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out, bool all256, bool all192);
 
 struct GlLayout {
-  size_t t = 0;       // bf16 [rows][rank]: gated rows' scaled down-projection, zero elsewhere
-  size_t down = 0;    // float [d_in/256][n_mask padded to 32][rank]
-  size_t split = 0;   // float [splits][rows][d_out]
+  size_t t = 0;       // bf16 [n_proj][rows][rank]: gated rows' scaled down-projections, zero elsewhere
+  size_t down = 0;    // float [n_proj][d_in/256][n_mask padded to 32][rank]
+  size_t split = 0;   // float, per projection p in turn: [splits][rows][d_out[p]]
   size_t total = 0;
   GlPlan plan;
 };
-GlLayout gl_layout(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, int32_t n_mask);
+GlLayout gl_layout(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out, int32_t rank,
+                   int32_t n_mask);
 
-hipError_t launch_gated_linear(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, const void* X,
-                               const void* W_t, const void* A_t, const void* B_t, const int32_t* mask_rows,
-                               int32_t n_mask, float scale, void* Y, char* ws, hipStream_t stream);
+hipError_t launch_gated_linear(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_out, int32_t rank,
+                               const void* X, const void* const* W_t, const void* const* A_t,
+                               const void* const* B_t, const int32_t* mask_rows, int32_t n_mask, float scale,
+                               void* const* Y, char* ws, hipStream_t stream);
 
 }  // namespace isd

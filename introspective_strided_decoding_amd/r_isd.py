@@ -1,4 +1,5 @@
-"""The projections of one R-ISD transformer layer, each one isd_gated_linear call.
+"""The projections of one R-ISD transformer layer: one isd_gated_linear_group call per
+group of projections that share an input, or one isd_gated_linear call per projection.
 
 R-ISD ("自省扩散语言模型的 token 生成机制与工程实践", section "Token 生成的核心参数与验收
 机制"; I-DLM project page, R-ISD card) keeps the base weights on the verifying
@@ -68,6 +69,14 @@ class RIsdProjections:
                                     A_t=rnd((RANK, d_in), weight_std), B_t=rnd((d_out, RANK), weight_std),
                                     Y=torch.empty((rows, d_out), dtype=torch.bfloat16, device=device),
                                     ws=torch.zeros(n, dtype=torch.uint8, device=device))
+        self.group_ws: Dict[Tuple[str, ...], torch.Tensor] = {}
+        for group in GROUPS:
+            d_in, d_outs = dims[group[0]][0], [dims[name][1] for name in group]
+            n = max(_lib.isd_gated_linear_group_workspace_bytes(rows, d_in, d_outs, RANK, self.mask.numel()),
+                    _lib.isd_gated_linear_group_workspace_bytes(rows, d_in, d_outs, 0, 0))
+            if n == 0:
+                raise ValueError(f"group {group} at {rows} rows is not supported")
+            self.group_ws[group] = torch.zeros(n, dtype=torch.uint8, device=device)
         self._side = torch.cuda.Stream(device=device)      # default priority
 
     def _one(self, name: str, gated: bool, stream) -> None:
@@ -78,16 +87,33 @@ class RIsdProjections:
         else:
             _lib.isd_gated_linear(t["X"], t["W_t"], t["Y"], t["ws"], stream=stream)
 
-    def run(self, gated: bool = True, overlap: bool = True) -> None:
+    def _group(self, group: Tuple[str, ...], gated: bool, stream) -> None:
+        ts = [self.p[name] for name in group]
+        X = ts[0]["X"]
+        Ws, Ys = [t["W_t"] for t in ts], [t["Y"] for t in ts]
+        if gated:
+            _lib.isd_gated_linear_group(X, Ws, Ys, self.group_ws[group], A_ts=[t["A_t"] for t in ts],
+                                        B_ts=[t["B_t"] for t in ts], mask_rows=self.mask, stream=stream)
+        else:
+            _lib.isd_gated_linear_group(X, Ws, Ys, self.group_ws[group], stream=stream)
+
+    def run(self, gated: bool = True, mode: str = "group") -> None:
         """Enqueue the seven projections on the current stream; gated=False runs the base
-        weights alone.  With overlap, the second projection of a group runs on a side
-        stream (forked from and joined back into the current stream by events), so one
-        projection's latency-bound adapter kernels run under its sibling's product.
-        Every projection has its own output and workspace, so siblings share no buffer
-        they write."""
+        weights alone.  mode "group": one group call per set of projections sharing an
+        input (q/k/v, o, gate/up, down).  mode "overlap": one call per projection, the
+        second projection of a group on a side stream (forked from and joined back into the
+        current stream by events), so one projection's latency-bound adapter kernels run
+        under its sibling's product.  mode "sequential": one call per projection, in order.
+        Every projection has its own output and every call its own workspace, so calls in
+        flight together share no buffer they write."""
+        if mode not in ("group", "overlap", "sequential"):
+            raise ValueError(f"unknown mode {mode!r}")
         main = torch.cuda.current_stream()
         for group in GROUPS:
-            if not overlap or len(group) == 1:
+            if mode == "group":
+                self._group(group, gated, main)
+                continue
+            if mode == "sequential" or len(group) == 1:
                 for name in group:
                     self._one(name, gated, main)
                 continue

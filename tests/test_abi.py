@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 7
+    assert LIB.isd_abi_version() == 8
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"
@@ -258,3 +258,51 @@ def test_gated_linear_validation():
     assert call(m=None, n_mask=0, wsb=8) == 4                          # an empty gate needs no row list
     for k in ("X", "W", "A", "B", "Y", "ws"):
         assert call(**{k: MISALIGNED}) == 7, k
+    assert call(d_in=1 << 17) == 5                                     # past the largest input width
+    assert call(rows=65536, d_out=1 << 15, n_mask=0) == 5              # rows x width past 2^30
+
+
+def _i32s(*v):
+    return (ctypes.c_int32 * len(v))(*v)
+
+
+def _ptrs(*v):
+    return (ctypes.c_void_p * len(v))(*v)
+
+
+def test_gated_linear_group_validation():
+    gws = LIB.isd_gated_linear_group_workspace_bytes
+    ws = LIB.isd_gated_linear_workspace_bytes
+    # a group of one is the single-projection call
+    for shape in ((224, 4096, 1024, 128, 128), (896, 4096, 12288, 128, 512), (40, 2048, 128, 0, 0)):
+        rows, d_in, d_out, rank, n_mask = shape
+        assert gws(1, rows, d_in, _i32s(d_out), rank, n_mask) == ws(*shape) > 0
+    qkv = _i32s(4096, 1024, 1024)
+    assert gws(3, 224, 4096, qkv, 128, 128) > gws(3, 224, 4096, qkv, 0, 0) > 0
+    for bad in ((0, 224, 4096, qkv, 0, 0), (5, 224, 4096, _i32s(128, 128, 128, 128, 128), 0, 0),
+                (3, 224, 4096, _i32s(4096, 1000, 1024), 0, 0), (2, 224, 4096, _i32s(4096, 0), 0, 0),
+                (3, 224, 4096, None, 0, 0), (2, 65536, 4096, _i32s(1 << 14, 1 << 14), 0, 0),
+                (3, 224, 4000, qkv, 0, 0), (3, 224, 4096, qkv, 64, 4)):
+        assert gws(*bad) == 0, bad
+    n = gws(3, 224, 4096, qkv, 128, 128)
+    three = _ptrs(FAKE.value, FAKE.value, FAKE.value)
+    ok = dict(n=3, rows=224, d_in=4096, d_out=qkv, rank=128, X=FAKE, W=three, A=three, B=three, m=FAKE,
+              n_mask=128, scale=1.0, Y=three, ws=FAKE, wsb=n)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return LIB.isd_gated_linear_group(a["n"], a["rows"], a["d_in"], a["d_out"], a["rank"], a["X"], a["W"],
+                                          a["A"], a["B"], a["m"], a["n_mask"], a["scale"], a["Y"], a["ws"], a["wsb"],
+                                          None)
+    assert call(wsb=n - 1) == 4                      # everything else valid
+    assert call(n=0) == 2
+    assert call(n=5) == 5
+    assert call(d_out=_i32s(4096, 1000, 1024)) == 5
+    assert call(d_out=None) == 1
+    assert call(scale=float("nan")) == 2
+    for k in ("X", "W", "Y", "ws", "A", "B", "m"):
+        assert call(**{k: None}) == 1, k
+    for k in ("W", "A", "B", "Y"):
+        assert call(**{k: _ptrs(FAKE.value, None, FAKE.value)}) == 1, k        # one member missing
+        assert call(**{k: _ptrs(FAKE.value, FAKE.value, MISALIGNED.value)}) == 7, k
+    assert call(rank=0, A=None, B=None, m=None, n_mask=0, wsb=8) == 4

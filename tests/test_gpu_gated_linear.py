@@ -95,7 +95,7 @@ def _check(Y, X, Wt, At, Bt, mask, scale, sample=None):
 # 128 x 128 tiles with k split in 2 over a ragged last row tile; 128 x 128 tiles of 8 waves,
 # ragged; 64 x 64 tiles with every row gated; one row gated; 128 x 128 tiles with a
 # two-stage ring (two workgroups per CU); 256 x 256 tiles of 8 waves over a ragged last row
-# tile of 8 rows.
+# tile of 8 rows; 256 x 192 tiles of 8 waves over a ragged last row tile of 88 rows.
 CASES = [
     (20, 256, 128, [1, 3, 4, 17]),
     (70, 512, 384, list(range(0, 70, 2))),
@@ -106,6 +106,7 @@ CASES = [
     (64, 768, 640, [63]),
     (300, 256, 16384, list(range(1, 300, 3))),
     (520, 256, 20480, [r for r in range(520) if r % 7 >= 3]),
+    (600, 512, 12288, list(range(2, 600, 4))),
 ]
 
 
@@ -173,37 +174,47 @@ def test_gated_projection_r_isd_layer_shapes(batch, proj):
     assert torch.equal(Y[clean].view(torch.int16), base[clean].view(torch.int16))
 
 
-def test_layer_projections_overlap_and_graph_replays_match_sequential():
-    """The seven projections with siblings (q/k/v, gate/up) on two streams, eagerly and
-    replayed from a HIP graph (three replays with eager work in between), give every output
-    bit for bit as the one-stream sequence does."""
+def test_layer_projections_overlap_group_and_graph_replays():
+    """The seven projections of a layer: siblings (q/k/v, gate/up) on two streams give every
+    output bit for bit as the one-stream sequence does; the group calls give every output as
+    their own eager run does when replayed from a HIP graph (three replays with eager work in
+    between), and equal the sequence wherever the two plans sum in the same order (o and down
+    are groups of one)."""
     from introspective_strided_decoding_amd.r_isd import RIsdProjections, stride_mask_rows
     batch, n = 32, 4
     proj = RIsdProjections(batch * (2 * n - 1), stride_mask_rows(batch, n), hidden=1024, kv=256, mlp=3072,
                            seed=3, device="cuda")
     names = [nm for nm, _, _ in proj.shapes]
-    for gated in (True, False):
-        proj.run(gated, overlap=False)
-        torch.cuda.synchronize()
-        want = {nm: proj.p[nm]["Y"].clone() for nm in names}
+
+    def outputs():
+        return {nm: proj.p[nm]["Y"].clone() for nm in names}
+
+    def clear():
         for nm in names:
             proj.p[nm]["Y"].fill_(0)
-        proj.run(gated, overlap=True)
+
+    for gated in (True, False):
+        proj.run(gated, "sequential")
         torch.cuda.synchronize()
-        for nm in names:
-            assert torch.equal(proj.p[nm]["Y"].view(torch.int16), want[nm].view(torch.int16)), nm
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            proj.run(gated, overlap=True)
-        for rep in range(3):
-            for nm in names:
-                proj.p[nm]["Y"].fill_(0)
+        seq = outputs()
+        for mode in ("overlap", "group"):
+            clear()
+            proj.run(gated, mode)
             torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            for nm in names:
-                assert torch.equal(proj.p[nm]["Y"].view(torch.int16), want[nm].view(torch.int16)), (rep, nm)
-        del g
+            want = outputs()
+            for nm in (names if mode == "overlap" else ["o", "down"]):
+                assert torch.equal(want[nm].view(torch.int16), seq[nm].view(torch.int16)), (mode, nm)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                proj.run(gated, mode)
+            for rep in range(3):
+                clear()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                for nm in names:
+                    assert torch.equal(proj.p[nm]["Y"].view(torch.int16), want[nm].view(torch.int16)), (mode, rep, nm)
+            del g
 
 
 def test_gated_projection_largest_row_count():
@@ -219,3 +230,104 @@ def test_gated_projection_largest_row_count():
     base, _ = _run(X, Wt, None, None, None)
     clean = torch.tensor([r for r in range(rows) if r % 3])
     assert torch.equal(Y[clean].view(torch.int16), base[clean].view(torch.int16))
+
+
+def _run_group(X, Wts, Ats, Bts, mask, scale=1.0, guard=64):
+    """isd_gated_linear_group; returns ([Y_p], flags).  Every output sits in a buffer with a
+    guard tail that must stay untouched."""
+    from introspective_strided_decoding_amd import _lib
+    rows, d_in = X.shape
+    d_outs = [w.shape[0] for w in Wts]
+    rank = 0 if Ats is None else 128
+    n_mask = 0 if mask is None else len(mask)
+    n = _lib.isd_gated_linear_group_workspace_bytes(rows, d_in, d_outs, rank, n_mask)
+    assert n > 0
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    bufs = [torch.full((rows * d + guard,), 7.0, dtype=torch.bfloat16, device="cuda") for d in d_outs]
+    Ys = [b[:rows * d].view(rows, d) for b, d in zip(bufs, d_outs)]
+    kw = {}
+    if rank:
+        kw = dict(A_ts=[a.cuda() for a in Ats], B_ts=[b.cuda() for b in Bts],
+                  mask_rows=torch.tensor(mask, dtype=torch.int32, device="cuda"), scale=scale)
+    _lib.isd_gated_linear_group(X.cuda(), [w.cuda() for w in Wts], Ys, ws, **kw)
+    torch.cuda.synchronize()
+    for b, d in zip(bufs, d_outs):
+        assert torch.all(b[rows * d:] == 7.0), "write past an output"
+    return [y.cpu() for y in Ys], int(ws[:4].view(torch.int32).item())
+
+
+def _group_inputs(rows, d_in, d_outs, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = _bf16(rng, (rows, d_in))
+    Wts = [_bf16(rng, (d, d_in), 0.02) for d in d_outs]
+    Ats = [_bf16(rng, (128, d_in), 0.02) for _ in d_outs]
+    Bts = [_bf16(rng, (d, 128), 0.02) for d in d_outs]
+    return X, Wts, Ats, Bts
+
+
+# (rows, d_in, output widths, gated rows), with the tiling the library picks for the summed
+# width: 64 x 64 tiles with k split; four members of 64 x 64 tiles; 128 x 128 tiles with k
+# split over a ragged row tile (a q/k/v-like group); 128 x 128 tiles of 8 waves; 128 x 128
+# tiles with a two-stage ring (one member's width not a multiple of 256, so no 256 tiles);
+# 256 x 256 tiles over a ragged last row tile; 256 x 192 tiles over a ragged last row tile.
+GROUP_CASES = [
+    (20, 2048, [128, 256, 128], [1, 3, 4, 17]),
+    (64, 768, [128, 256, 384, 128], [63, 0, 31]),
+    (300, 1024, [2048, 512, 512], [r for r in range(300) if r % 7 >= 3]),
+    (333, 512, [4096, 4096], [r for r in range(333) if r % 5 == 1]),
+    (520, 256, [8192, 8064], list(range(1, 520, 3))),
+    (520, 256, [8192, 8192], [r for r in range(520) if r % 7 >= 3]),
+    (520, 768, [6144, 6144], [r for r in range(520) if r % 3 == 0]),
+]
+
+
+@pytest.mark.parametrize("rows,d_in,d_outs,mask", GROUP_CASES)
+def test_gated_group_small(rows, d_in, d_outs, mask):
+    X, Wts, Ats, Bts = _group_inputs(rows, d_in, d_outs, seed=rows + sum(d_outs))
+    Ys, flags = _run_group(X, Wts, Ats, Bts, mask, scale=0.5)
+    assert flags == 0
+    base, _ = _run_group(X, Wts, None, None, None)
+    clean = [r for r in range(rows) if r not in set(mask)]
+    for p in range(len(d_outs)):
+        _check(Ys[p], X, Wts[p], Ats[p], Bts[p], mask, 0.5)
+        _check(base[p], X, Wts[p], None, None, None, 1.0)
+        assert torch.equal(Ys[p][clean].view(torch.int16), base[p][clean].view(torch.int16)), p
+
+
+def test_gated_group_of_one_is_the_single_call():
+    rows, d_in, d_out = 300, 1024, 5376
+    X, Wts, Ats, Bts = _group_inputs(rows, d_in, [d_out], seed=45)
+    mask = [r for r in range(rows) if r % 7 >= 3]
+    Ys, _ = _run_group(X, Wts, Ats, Bts, mask, scale=0.5)
+    Y, _ = _run(X, Wts[0], Ats[0], Bts[0], mask, scale=0.5)
+    assert torch.equal(Ys[0].view(torch.int16), Y.view(torch.int16))
+
+
+def test_gated_group_flags_rows_out_of_range():
+    from introspective_strided_decoding_amd import _lib
+    rows = 50
+    X, Wts, Ats, Bts = _group_inputs(rows, 256, [128, 256], seed=46)
+    Ys, flags = _run_group(X, Wts, Ats, Bts, [2, 50, -1, 7])
+    assert flags & _lib.FLAG_ROW_RANGE
+    for p in range(2):
+        _check(Ys[p], X, Wts[p], Ats[p], Bts[p], [2, 7], 1.0)
+
+
+# The two groups of an 8B-class layer that share an input: q, k, v (hidden 4096 -> 4096,
+# 1024, 1024) and gate, up (4096 -> 12288 each), at 224 rows (32 requests x 7, 128 gated)
+# and 896 rows (128 x 7, 512 gated); sampled rows against the oracle.
+@pytest.mark.parametrize("batch", [32, 128])
+@pytest.mark.parametrize("group", [[4096, 1024, 1024], [12288, 12288]])
+def test_gated_group_r_isd_layer_shapes(batch, group):
+    Q, N = 7, 4
+    rows = batch * Q
+    mask = [r * Q + i for r in range(batch) for i in range(N - 1, Q)]
+    X, Wts, Ats, Bts = _group_inputs(rows, 4096, group, seed=batch + sum(group))
+    Ys, flags = _run_group(X, Wts, Ats, Bts, mask)
+    assert flags == 0
+    base, _ = _run_group(X, Wts, None, None, None)
+    sample = list(range(0, 14)) + list(range(rows - 14, rows)) + list(range(100, rows, 97))
+    clean = [r * Q + i for r in range(batch) for i in range(N - 1)]
+    for p in range(len(group)):
+        _check(Ys[p], X, Wts[p], Ats[p], Bts[p], mask, 1.0, sample=sample)
+        assert torch.equal(Ys[p][clean].view(torch.int16), base[p][clean].view(torch.int16)), p
