@@ -273,13 +273,18 @@ __global__ __launch_bounds__(256) void gl_scatter(const float* __restrict__ part
 // Between 256 x 256 and 256 x 192 tiles the cost is rounds of the chip times
 // the bytes a tile loads per k block: a 256 x 192 tiling that fills whole
 // rounds (512 tiles of an 896-row, 24576-wide group, where 256 x 256 leaves
-// 384 = 1.5 rounds) loads less per CU.
+// 384 = 1.5 rounds) loads less per CU.  Likewise 128 x 192 or 128 x 256 tiles
+// where they fit one round and 128 x 128 tiles would not (an 896-row q/k/v
+// group: 168 tiles of 128 x 256 against 336 of 128 x 128).
 GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out, bool all256, bool all192) {
   GlPlan p;
   const int kb = d_in / kBK;
   const long t128 = long((rows + 127) / 128) * (d_out / 128);
   const long t256 = all256 ? long((rows + 255) / 256) * (d_out / 256) : 0;
   const long t192 = all192 ? long((rows + 255) / 256) * (d_out / 192) : 0;
+  const long t128x192 = all192 ? long((rows + 127) / 128) * (d_out / 192) : 0;
+  const long t128x256 = all256 ? long((rows + 127) / 128) * (d_out / 256) : 0;
+  auto one_round = [](long tiles) { return tiles > 0 && tiles <= 256; };
   auto cost = [](long tiles, int bn) { return (tiles + 255) / 256 * (256 + bn); };
   auto split_to = [&](long tiles) {
     while (tiles * p.splits < 256 && kb / (2 * p.splits) >= 8) p.splits *= 2;
@@ -289,6 +294,12 @@ GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out, bool all256, bool all1
     p.bn = (t192 >= 160 && (t256 < 160 || cost(t192, 192) < cost(t256, 256))) ? 192 : 256;
     p.stages = 2;
     p.waves = 8;
+  } else if (t128 > 256 && (one_round(t128x192) || one_round(t128x256))) {
+    // one round of 128 x 192 tiles (4 waves of 64 x 96), else of 128 x 256 tiles
+    // (8 waves of 64 x 64), instead of more than one round of 128 x 128
+    p.bn = one_round(t128x192) ? 192 : 256;
+    p.waves = p.bn == 192 ? 4 : 8;
+    p.stages = 3;
   } else if (t128 >= 384) {
     p.stages = 2;                      // two workgroups per CU
   } else if (t128 >= 160) {
@@ -389,8 +400,14 @@ hipError_t launch_gated_linear(int32_t n_proj, int32_t rows, int32_t d_in, const
                          d_in, R, rows, mt, pl.splits, g);
   } else if (pl.bm == 128) {
     const int mt = (rows + 127) / 128;
-    const dim3 grid(mt * tiles(128) * pl.splits);
-    if (pl.stages == 2)
+    const dim3 grid(mt * tiles(pl.bn) * pl.splits);
+    if (pl.bn == 192)
+      hipLaunchKernelGGL((gl_gemm<128, 192, 3, 2, 2>), grid, dim3(256), 0, stream, x, d_in, R, rows, mt, pl.splits,
+                         g);
+    else if (pl.bn == 256)
+      hipLaunchKernelGGL((gl_gemm<128, 256, 3, 2, 4>), grid, dim3(512), 0, stream, x, d_in, R, rows, mt, pl.splits,
+                         g);
+    else if (pl.stages == 2)
       hipLaunchKernelGGL((gl_gemm<128, 128, 2, 2, 2>), grid, dim3(256), 0, stream, x, d_in, R, rows, mt, pl.splits,
                          g);
     else if (pl.waves == 8)

@@ -176,7 +176,7 @@ constexpr long kGlMaxOut = 1L << 30;      // rows x summed output width of one c
 // Gated projection: tile shape and k split, a function of the shape alone so a
 // gated call and the base-only call of the same shape sum in the same order.
 struct GlPlan {
-  int bm = 128;       // tiles of bm rows x bn outputs: 256 x 256, 256 x 192, 128 x 128 or 64 x 64
+  int bm = 128;       // tiles of bm rows x bn outputs: 256 x 256 / 192, 128 x 256 / 192 / 128, 64 x 64
   int bn = 128;
   int stages = 4;     // LDS ring depth
   int waves = 4;      // waves per workgroup: 4 or 8

@@ -269,7 +269,9 @@ def _group_inputs(rows, d_in, d_outs, seed):
 # width: 64 x 64 tiles with k split; four members of 64 x 64 tiles; 128 x 128 tiles with k
 # split over a ragged row tile (a q/k/v-like group); 128 x 128 tiles of 8 waves; 128 x 128
 # tiles with a two-stage ring (one member's width not a multiple of 256, so no 256 tiles);
-# 256 x 256 tiles over a ragged last row tile; 256 x 192 tiles over a ragged last row tile.
+# 256 x 256 tiles over a ragged last row tile; 256 x 192 tiles over a ragged last row tile;
+# 128 x 192 tiles (one round where 128 x 128 would take two) over a ragged row tile; 128 x
+# 256 tiles (the same, with widths that 192 does not divide).
 GROUP_CASES = [
     (20, 2048, [128, 256, 128], [1, 3, 4, 17]),
     (64, 768, [128, 256, 384, 128], [63, 0, 31]),
@@ -278,6 +280,8 @@ GROUP_CASES = [
     (520, 256, [8192, 8064], list(range(1, 520, 3))),
     (520, 256, [8192, 8192], [r for r in range(520) if r % 7 >= 3]),
     (520, 768, [6144, 6144], [r for r in range(520) if r % 3 == 0]),
+    (330, 512, [6144, 3072, 3072], [r for r in range(330) if r % 4 == 2]),
+    (330, 512, [8192, 2048, 2048], list(range(0, 330, 5))),
 ]
 
 
