@@ -335,3 +335,20 @@ def test_gated_group_r_isd_layer_shapes(batch, group):
     for p in range(len(group)):
         _check(Ys[p], X, Wts[p], Ats[p], Bts[p], mask, 1.0, sample=sample)
         assert torch.equal(Ys[p][clean].view(torch.int16), base[p][clean].view(torch.int16)), p
+
+
+def test_gated_group_empty_gate_and_duplicate_rows():
+    """An empty gate gives the base-only group call bit for bit; a row listed twice is adapted
+    once (same bits as the list without the repeat); results repeat call to call."""
+    rows, d_in, d_outs = 96, 512, [256, 128, 384]
+    X, Wts, Ats, Bts = _group_inputs(rows, d_in, d_outs, seed=47)
+    empty, _ = _run_group(X, Wts, Ats, Bts, [])
+    base, _ = _run_group(X, Wts, None, None, None)
+    dup, _ = _run_group(X, Wts, Ats, Bts, [5, 9, 9, 50, 5])
+    dup2, _ = _run_group(X, Wts, Ats, Bts, [5, 9, 9, 50, 5])
+    once, _ = _run_group(X, Wts, Ats, Bts, [5, 9, 50])
+    for p in range(len(d_outs)):
+        assert torch.equal(empty[p].view(torch.int16), base[p].view(torch.int16)), p
+        assert torch.equal(dup[p].view(torch.int16), once[p].view(torch.int16)), p
+        assert torch.equal(dup[p].view(torch.int16), dup2[p].view(torch.int16)), p
+        _check(dup[p], X, Wts[p], Ats[p], Bts[p], [5, 9, 50], 1.0)
