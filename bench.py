@@ -435,6 +435,12 @@ def main(argv=None):
     prop["steps_per_s_with_sampled_proposals"] = round(1e3 / (ms_per_step + prop["sample"]["avg_call_ms"]), 2)
 
     r_isd = None if args.no_r_isd else r_isd_projections(cfg, dev, stream, reps=max(20, args.steps // 3))
+    if r_isd is not None:
+        # one layer's attention (this step's launch) plus its seven projections, gated over
+        # base-only: the adapter's share once attention is in the layer (norms, rotary
+        # embedding, the SiLU product and residual adds left out)
+        r_isd["attention_ms"] = round(attn_ms, 5)
+        r_isd["alpha_with_attention"] = round((attn_ms + r_isd["gated"]["ms"]) / (attn_ms + r_isd["base"]["ms"]), 4)
 
     # accepted / committed tokens of the timed steps (identical draws per set)
     acc = [int(st.accept_len.sum().item()) for st in steps]
