@@ -10,8 +10,9 @@
 // T[m] = bf16(gate[m] * scale * X[m] A^T) (zero on CLEAN rows), Y is one
 // product of [X | T] with [W | B] over d_in + rank columns.
 //
-//   lora_down   T_part[p][kc][g][r] = sum over a 256-wide k chunk of X[row(g)] A_p^T
-//               (the same kernel as isd_lora_delta's), clearing T on the side
+//   gl_gemm     (gathering) T_part[p][kc][g][r] = sum over a 256-wide k chunk of
+//               X[row(g)] A_p^T: the product kernel below with X rows taken
+//               through the gate list, k split into chunks, clearing T on the side
 //   gl_scatter  T_p[row(g)] = bf16(scale * sum_kc T_part[p][kc][g]) for gated g
 //   gl_gemm     the product, bf16 matrix-core operands, fp32 sums; the rank
 //               columns come first, so a row whose T is zero enters the base
@@ -89,7 +90,8 @@ __device__ __forceinline__ GlProj gl_proj(const GlGroup& g, int ni) {
 
 template <int BM, int BN, int ST, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
-    const uint16_t* __restrict__ X, int K, int R, int M, int m_tiles, int splits, const GlGroup g) {
+    const uint16_t* __restrict__ X, int K, int R, int M, int m_tiles, int splits, const GlGroup g,
+    const int32_t* __restrict__ gather, int x_rows, u32x4* __restrict__ zero16, int n16) {
   constexpr int NW = WGM * WGN;                // waves: WGM along X rows, WGN along W rows
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   constexpr int IX = BM / (8 * NW), IW = BN / (8 * NW);    // 1 KB direct-to-LDS loads per wave per block
@@ -121,6 +123,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
   // the 1 KB it writes, i.e. row i/8, physical chunk i%8, so it fetches the
   // logical chunk that the swizzle puts there.
   const int lrow = lane >> 3;
+  // X row of each of this lane's row chunks, fixed over k: output row m reads X
+  // row m, or row gather[m] (0 when out of range; that output is never used)
+  int xrow[IX];
+#pragma unroll
+  for (int q = 0; q < IX; ++q) {
+    const int m = min(m0 + wave * (BM / NW) + q * 8 + lrow, M - 1);   // rows past M are computed, never stored
+    if (gather) {
+      const int gr = gather[m];
+      xrow[q] = (gr >= 0 && gr < x_rows) ? gr : 0;
+    } else {
+      xrow[q] = m;
+    }
+  }
   auto issue = [&](int j) {
     const bool ext = j < n_ext;
     const uint16_t* xs = ext ? T : X;
@@ -132,7 +147,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
     for (int q = 0; q < IX; ++q) {
       const int r = wave * (BM / NW) + q * 8 + lrow;
       const int c = (lane & 7) ^ (r & 7) ^ ((r >> 3) & 1);
-      const int row = min(m0 + r, M - 1);     // rows past M are computed, never stored
+      const int row = ext ? min(m0 + r, M - 1) : xrow[q];
       __builtin_amdgcn_global_load_lds((gptr_t)(xs + size_t(row) * ld + k0 + c * 8),
                                        (lptr_t)(st + (wave * (BM / NW) + q * 8) * 128), 16, 0, 0);
     }
@@ -201,7 +216,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
         const int n = nb + v4 * 8;
         const float y0 = acc[a][c][4 * v4], y1 = acc[a][c][4 * v4 + 1];
         const float y2 = acc[a][c][4 * v4 + 2], y3 = acc[a][c][4 * v4 + 3];
-        if (splits == 1) {
+        if (splits == 1 && !gather) {     // a gathering product always leaves fp32 partials
           *reinterpret_cast<uint2*>(pj.Y + size_t(m) * N + n) =
               make_uint2(uint32_t(f32_to_bf16_bits(y0)) | (uint32_t(f32_to_bf16_bits(y1)) << 16),
                          uint32_t(f32_to_bf16_bits(y2)) | (uint32_t(f32_to_bf16_bits(y3)) << 16));
@@ -211,6 +226,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gl_gemm(
       }
     }
   }
+  // optional side job: clear n16 16-byte words (the adapter intermediate T)
+  if (zero16)
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x) zero16[i] = u32x4{0, 0, 0, 0};
 }
 
 // One thread per 4 outputs of projection blockIdx.y.
@@ -238,14 +256,17 @@ __global__ __launch_bounds__(256) void gl_reduce(const GlGroup g, int M, int spl
 // [projection][kchunks][m_pad][128], T is [projection][rows][128].
 __global__ __launch_bounds__(256) void gl_scatter(const float* __restrict__ part, int kchunks, int m_pad,
                                                   const int32_t* __restrict__ mask_rows, int n_mask, int rows,
-                                                  float scale, uint16_t* __restrict__ T) {
+                                                  float scale, uint16_t* __restrict__ T, uint32_t* __restrict__ flags) {
   part += size_t(blockIdx.y) * kchunks * m_pad * kRank;
   T += size_t(blockIdx.y) * rows * kRank;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int g = e / kRank, r = e % kRank;
   if (g >= n_mask) return;
   const int row = mask_rows[g];
-  if (row < 0 || row >= rows) return;        // flagged by lora_down
+  if (row < 0 || row >= rows) {              // skipped, and flagged once per entry
+    if (r == 0 && blockIdx.y == 0) raise_flag(flags, ISD_FLAG_ROW_RANGE);
+    return;
+  }
   // eight independent running sums, so eight loads are in flight at a time
   const float* p = part + size_t(g) * kRank + r;
   const size_t stride = size_t(m_pad) * kRank;
@@ -334,7 +355,7 @@ GlLayout gl_layout(int32_t n_proj, int32_t rows, int32_t d_in, const int32_t* d_
     L.t = off;
     off += (size_t(n_proj) * rows * rank * 2 + 255) / 256 * 256;
     L.down = off;
-    off += size_t(n_proj) * size_t(d_in / 256) * size_t((n_mask + 31) / 32 * 32) * rank * 4;
+    off += size_t(n_proj) * size_t(d_in / 256) * size_t(n_mask) * rank * 4;
     off = (off + 255) / 256 * 256;
   }
   if (L.plan.splits > 1) {
@@ -364,12 +385,24 @@ hipError_t launch_gated_linear(int32_t n_proj, int32_t rows, int32_t d_in, const
   if (rank > 0) {
     uint16_t* t = reinterpret_cast<uint16_t*>(ws + L.t);
     float* down = reinterpret_cast<float*>(ws + L.down);
-    hipError_t e = launch_lora_down(X, A_t, n_proj, mask_rows, n_mask, rows, d_in, down,
-                                    reinterpret_cast<uint32_t*>(ws), t, size_t(n_proj) * rows * rank * 2, stream);
-    if (e != hipSuccess) return e;
-    const int m_pad = (n_mask + 31) / 32 * 32;
-    hipLaunchKernelGGL(gl_scatter, dim3((n_mask * kRank + 255) / 256, n_proj), dim3(256), 0, stream, down,
-                       d_in / 256, m_pad, mask_rows, n_mask, rows, scale, t);
+    // the adapters' down-projection of the gated rows, every adapter of the group in
+    // one launch: 64 x 64 tiles of [gathered X rows] x [A_p rows], k split into
+    // 256-wide chunks whose partials gl_scatter sums; T is cleared on the side
+    const int kchunks = d_in / 256;
+    GlGroup gd{};
+    gd.n = n_proj;
+    for (int p = 0; p < n_proj; ++p) {
+      gd.d_out[p] = kRank;
+      gd.tile_end[p] = (p + 1) * (kRank / 64);
+      gd.W[p] = static_cast<const uint16_t*>(A_t[p]);
+      gd.part[p] = down + size_t(p) * kchunks * n_mask * kRank;
+    }
+    const int mtd = (n_mask + 63) / 64;
+    hipLaunchKernelGGL((gl_gemm<64, 64, 4, 2, 2>), dim3(mtd * n_proj * (kRank / 64) * kchunks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(X), d_in, 0, n_mask, mtd, kchunks, gd, mask_rows, rows,
+                       reinterpret_cast<u32x4*>(t), int(size_t(n_proj) * rows * rank * 2 / 16));
+    hipLaunchKernelGGL(gl_scatter, dim3((n_mask * kRank + 255) / 256, n_proj), dim3(256), 0, stream, down, kchunks,
+                       n_mask, mask_rows, n_mask, rows, scale, t, reinterpret_cast<uint32_t*>(ws));
     for (int p = 0; p < n_proj; ++p) {
       g.T[p] = t + size_t(p) * rows * kRank;
       g.Bt[p] = static_cast<const uint16_t*>(B_t[p]);
@@ -394,32 +427,32 @@ hipError_t launch_gated_linear(int32_t n_proj, int32_t rows, int32_t d_in, const
     const int mt = (rows + 255) / 256;
     if (pl.bn == 192)
       hipLaunchKernelGGL((gl_gemm<256, 192, 2, 4, 2>), dim3(mt * tiles(192) * pl.splits), dim3(512), 0, stream, x,
-                         d_in, R, rows, mt, pl.splits, g);
+                         d_in, R, rows, mt, pl.splits, g, nullptr, 0, nullptr, 0);
     else
       hipLaunchKernelGGL((gl_gemm<256, 256, 2, 2, 4>), dim3(mt * tiles(256) * pl.splits), dim3(512), 0, stream, x,
-                         d_in, R, rows, mt, pl.splits, g);
+                         d_in, R, rows, mt, pl.splits, g, nullptr, 0, nullptr, 0);
   } else if (pl.bm == 128) {
     const int mt = (rows + 127) / 128;
     const dim3 grid(mt * tiles(pl.bn) * pl.splits);
     if (pl.bn == 192)
       hipLaunchKernelGGL((gl_gemm<128, 192, 3, 2, 2>), grid, dim3(256), 0, stream, x, d_in, R, rows, mt, pl.splits,
-                         g);
+                         g, nullptr, 0, nullptr, 0);
     else if (pl.bn == 256)
       hipLaunchKernelGGL((gl_gemm<128, 256, 3, 2, 4>), grid, dim3(512), 0, stream, x, d_in, R, rows, mt, pl.splits,
-                         g);
+                         g, nullptr, 0, nullptr, 0);
     else if (pl.stages == 2)
       hipLaunchKernelGGL((gl_gemm<128, 128, 2, 2, 2>), grid, dim3(256), 0, stream, x, d_in, R, rows, mt, pl.splits,
-                         g);
+                         g, nullptr, 0, nullptr, 0);
     else if (pl.waves == 8)
       hipLaunchKernelGGL((gl_gemm<128, 128, 4, 2, 4>), grid, dim3(512), 0, stream, x, d_in, R, rows, mt, pl.splits,
-                         g);
+                         g, nullptr, 0, nullptr, 0);
     else
       hipLaunchKernelGGL((gl_gemm<128, 128, 4, 2, 2>), grid, dim3(256), 0, stream, x, d_in, R, rows, mt, pl.splits,
-                         g);
+                         g, nullptr, 0, nullptr, 0);
   } else {
     const int mt = (rows + 63) / 64;
     hipLaunchKernelGGL((gl_gemm<64, 64, 4, 2, 2>), dim3(mt * tiles(64) * pl.splits), dim3(256), 0, stream, x, d_in,
-                       R, rows, mt, pl.splits, g);
+                       R, rows, mt, pl.splits, g, nullptr, 0, nullptr, 0);
   }
   if (pl.splits > 1) {
     const int count4 = rows * (max_d / 4);

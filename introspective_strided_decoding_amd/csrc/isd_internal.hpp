@@ -164,12 +164,6 @@ hipError_t launch_lora(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, 
 
 constexpr int kGlMaxProj = 4;             // projections of one gated group call
 
-// The adapter's down-projection partials of up to kGlMaxProj adapters A_t[p]
-// over the same gated rows of X: part is [p][d_in/256][n_mask padded to 32][128].
-hipError_t launch_lora_down(const void* X, const void* const* A_t, int32_t n_sets, const int32_t* mask_rows,
-                            int32_t n_mask, int32_t rows, int32_t d_in, float* part, uint32_t* flags,
-                            void* zero16, size_t zero_bytes, hipStream_t stream);
-
 constexpr int32_t kGlMaxRows = 1 << 16;   // rows of one gated projection call
 constexpr long kGlMaxOut = 1L << 30;      // rows x summed output width of one call
 

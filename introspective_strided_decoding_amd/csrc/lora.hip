@@ -36,26 +36,11 @@ __device__ __forceinline__ int gated_row(const int32_t* __restrict__ mask_rows, 
   return row;
 }
 
-// The adapters of one launch: blockIdx.z picks one of up to kGlMaxProj, all
-// over the same gated rows (a gated projection group); part gains a leading
-// [adapter] index.
-struct LoraDownA {
-  const uint16_t* At[kGlMaxProj];
-};
-
-// zero16/n16: an optional buffer of n16 16-byte words that the grid clears on
-// the side (the gated projection's full-height intermediate; null otherwise).
-__global__ __launch_bounds__(256) void lora_down(const uint16_t* __restrict__ X, const LoraDownA as,
+__global__ __launch_bounds__(256) void lora_down(const uint16_t* __restrict__ X, const uint16_t* __restrict__ At,
                                                  const int32_t* __restrict__ mask_rows, int n_mask, int rows,
                                                  int d_in, int m_pad, float* __restrict__ part,
-                                                 uint32_t* __restrict__ flags, u32x4* __restrict__ zero16,
-                                                 int n16) {
-  const int kc = blockIdx.x, mb = blockIdx.y, set = blockIdx.z;
-  const uint16_t* __restrict__ At = as.At[0];
-#pragma unroll
-  for (int i = 1; i < kGlMaxProj; ++i)
-    if (set == i) At = as.At[i];
-  part += size_t(set) * gridDim.x * m_pad * kLoraRank;
+                                                 uint32_t* __restrict__ flags) {
+  const int kc = blockIdx.x, mb = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int n = wave * 32 + col;
@@ -65,7 +50,7 @@ __global__ __launch_bounds__(256) void lora_down(const uint16_t* __restrict__ X,
 #pragma unroll
   for (int s = 0; s < kKChunk / 16; ++s) a[s] = *reinterpret_cast<const u32x4*>(arow + s * 16);
   const int m = mb * 32 + col;
-  const int row = gated_row(mask_rows, m, n_mask, rows, flags, wave == 0 && h == 0 && kc == 0 && set == 0);
+  const int row = gated_row(mask_rows, m, n_mask, rows, flags, wave == 0 && h == 0 && kc == 0);
   const uint16_t* xrow = X + size_t(row < 0 ? 0 : row) * d_in + kc * kKChunk + h * 8;
   // unconditional loads (a row outside the gate reads row 0 and is zeroed after), so all
   // of them are in flight at once
@@ -83,9 +68,6 @@ __global__ __launch_bounds__(256) void lora_down(const uint16_t* __restrict__ X,
 #pragma unroll
   for (int v4 = 0; v4 < 4; ++v4)
     *reinterpret_cast<f32x4*>(dst + v4 * 8) = f32x4{acc[4 * v4], acc[4 * v4 + 1], acc[4 * v4 + 2], acc[4 * v4 + 3]};
-  for (int i = ((set * gridDim.y + mb) * gridDim.x + kc) * 256 + threadIdx.x; i < n16;
-       i += gridDim.x * gridDim.y * gridDim.z * 256)
-    zero16[i] = u32x4{0, 0, 0, 0};
 }
 
 __global__ __launch_bounds__(256) void lora_reduce(const float* __restrict__ part, int kchunks, int count,
@@ -166,27 +148,14 @@ hipError_t launch_lora(int32_t rows, int32_t d_in, int32_t d_out, int32_t rank, 
   uint16_t* t_hi = reinterpret_cast<uint16_t*>(ws + L.t_hi);
   uint16_t* t_lo = reinterpret_cast<uint16_t*>(ws + L.t_lo);
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
-  LoraDownA as{};
-  as.At[0] = static_cast<const uint16_t*>(A);
-  hipLaunchKernelGGL(lora_down, dim3(kchunks, m_blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(X), as,
-                     mask_rows, n_mask, rows, d_in, m_pad, part, flags, nullptr, 0);
+  hipLaunchKernelGGL(lora_down, dim3(kchunks, m_blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(A), mask_rows, n_mask, rows,
+                     d_in, m_pad, part, flags);
   const int count = m_pad * rank;
   hipLaunchKernelGGL(lora_reduce, dim3((count + 255) / 256), dim3(256), 0, stream, part, kchunks, count, t_hi, t_lo);
   hipLaunchKernelGGL(lora_up, dim3(d_out / kOBlock, m_blocks), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(Bm), t_hi, t_lo, mask_rows, n_mask, rows, d_out, scale,
                      static_cast<uint16_t*>(Y));
-  return hipGetLastError();
-}
-
-hipError_t launch_lora_down(const void* X, const void* const* A_t, int32_t n_sets, const int32_t* mask_rows,
-                            int32_t n_mask, int32_t rows, int32_t d_in, float* part, uint32_t* flags,
-                            void* zero16, size_t zero_bytes, hipStream_t stream) {
-  const int m_blocks = (n_mask + 31) / 32;
-  LoraDownA as{};
-  for (int p = 0; p < n_sets; ++p) as.At[p] = static_cast<const uint16_t*>(A_t[p]);
-  hipLaunchKernelGGL(lora_down, dim3(d_in / kKChunk, m_blocks, n_sets), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(X), as, mask_rows, n_mask, rows, d_in, m_blocks * 32, part, flags,
-                     static_cast<u32x4*>(zero16), int(zero_bytes / 16));
   return hipGetLastError();
 }
 
