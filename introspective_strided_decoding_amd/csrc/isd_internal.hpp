@@ -180,7 +180,7 @@ GlPlan gl_plan(int32_t rows, int32_t d_in, int32_t d_out, bool all256, bool all1
 
 struct GlLayout {
   size_t t = 0;       // bf16 [n_proj][rows][rank]: gated rows' scaled down-projections, zero elsewhere
-  size_t down = 0;    // float [n_proj][d_in/256][n_mask padded to 32][rank]
+  size_t down = 0;    // float [n_proj][d_in/256][n_mask][rank]: the down-projection partials
   size_t split = 0;   // float, per projection p in turn: [splits][rows][d_out[p]]
   size_t total = 0;
   GlPlan plan;
