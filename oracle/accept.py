@@ -8,11 +8,17 @@ min(1, p(x)/q(x)); [project] caption on geometric acceptance: position 1 is
 always accepted because of the logit shift):
 
 1. Row layout (logit shift, [hypho] "三项关键训练创新", item 2: the hidden
-   state at i predicts token i+1).  The stride carries proposals x_1..x_N.
-   x_1 was decided before this pass and needs no test.  CLEAN row j
-   (0 <= j <= N-2) holds x_{j+1}; its logits are the anchor p for x_{j+2}.
-   The q logits for x_{j+2} are those the previous pass's MASK row produced;
-   the caller keeps them.
+   state at i predicts token i+1).  The stride carries proposals x_1..x_N at
+   consecutive positions.  CLEAN row j (0 <= j <= N-2) holds x_{j+1}; its
+   logits are the anchor p for x_{j+2}.  Row N-1, the first of the N rows
+   that propose, holds x_N; under the logit shift its logits predict the
+   token after x_N from an all-clean prefix, i.e. the anchor distribution
+   itself, so the next stride's first proposal is drawn from p and needs no
+   test ([project] caption on geometric acceptance: position 1 is always
+   accepted because of the logit shift).  x_1 was drawn that way by the
+   previous pass.  Rows N..2N-2 hold MASK and give q for the next stride's
+   positions 2..N; the q logits for x_{j+2} are those the previous pass's
+   MASK rows produced, kept by the caller.
 2. Normalise every row: lse = max + log(sum exp(l - max)); the log-probability
    of a token is l[x] - lse.
 3. For k = 2..N in order: rho_k = p_k(x_k) / q_k(x_k), computed as
@@ -28,8 +34,12 @@ always accepted because of the logit shift):
    distributed as p (the lossless claim in [project] and [hotdry]).  If S is
    0 in float64 (p and q equal up to rounding) y* is drawn the same way from
    p itself.
-5. Committed tokens: x_1..x_A, then y* if A < N.  The KV rows to commit are
-   the CLEAN rows holding accepted tokens: n_commit = min(A, N-1).
+5. Committed tokens: x_1..x_A, then y* if A < N.  A row's key and value are
+   valid exactly when the token it holds and every token before it are
+   accepted, so the KV rows to commit are rows 0..A-1, the accepted prefix
+   x_1..x_A: n_commit = A.  y* has no row in this pass; the decoding loop
+   (``oracle.loop``) commits it from the row that carries it in the next
+   forward.
 """
 
 from __future__ import annotations
@@ -89,7 +99,7 @@ class StrideResult:
     accept_len: int                    # A in [1, N]
     out_tokens: List[int]              # committed tokens (length n_out)
     n_out: int
-    n_commit: int                      # CLEAN rows whose KV is committed
+    n_commit: int                      # stride rows whose KV is committed (= A)
     logp_sel: np.ndarray               # [N-1] log p at the proposals
     logq_sel: np.ndarray               # [N-1] log q at the proposals
     rho: np.ndarray                    # [N-1] p/q at the proposals
@@ -148,7 +158,7 @@ def verify_stride(p_rows, q_rows, proposals: Sequence[int], uniforms, lse_p=None
         tokens = tokens + [y]
     margins = np.abs(u_acc[:decided] - rho[:decided])
     return StrideResult(accept_len=accept_len, out_tokens=tokens, n_out=len(tokens),
-                        n_commit=min(accept_len, n - 1), logp_sel=logp, logq_sel=logq,
+                        n_commit=accept_len, logp_sel=logp, logq_sel=logq,
                         rho=rho, u_accept=u_acc, decided=decided, reject_row=reject_row,
                         resample_margin=margin, resample_fallback=fallback,
                         accept_margins=margins)

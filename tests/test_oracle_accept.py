@@ -167,7 +167,7 @@ def test_position_one_always_accepted():
         assert res.out_tokens[0] == x[0]
         assert res.out_tokens[: res.accept_len] == [int(t) for t in x[: res.accept_len]]
         assert res.n_out == res.accept_len + (1 if res.accept_len < N else 0)
-        assert res.n_commit == min(res.accept_len, N - 1)
+        assert res.n_commit == res.accept_len           # rows 0..A-1: the accepted prefix
 
 
 def test_strict_boundary_and_ratio_at_least_one():
