@@ -367,7 +367,7 @@ def main(argv=None):
         # per-position acceptance is the workload's target
         # the same workload with page room for the tokens the loop commits
         room = 2 * loop_forwards + 16          # the eager forwards, then the same number replayed
-        lwl = make_workload(cfg, with_mask_logits=True, extra_tokens=room * (cfg.stride_n - 1))
+        lwl = make_workload(cfg, with_mask_logits=True, extra_tokens=room * cfg.stride_n)
         lp = DeviceStep.from_arrays(lwl, device=dev, max_ctx=int(lwl.ctx_lens.max()) + room * cfg.stride_n,
                                     commit_in_place=True)
         del lwl

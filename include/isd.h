@@ -5,19 +5,23 @@
  * The step (I-DLM project page, ISD card; "I-DLM：扩散模型如何用'自省一致性'
  * 追上自回归模型质量", section "Introspective Strided Decoding（ISD）";
  * "自省扩散语言模型的 token 生成机制与工程实践", section "Token 生成的核心参数与
- * 验收机制"): every request carries a stride of Q = 2N-1 query rows.  Rows
- * 0..N-2 are CLEAN rows holding the previous pass's proposals x_1..x_{N-1};
- * rows N-1..2N-2 are MASK rows that propose the next N tokens.  One forward
- * both verifies and proposes:
+ * 验收机制"): every request carries a stride of Q = 2N-1 query rows at
+ * consecutive positions.  Rows 0..N-2 are CLEAN rows holding the previous
+ * pass's proposals x_1..x_{N-1}; rows N-1..2N-2 propose the next N tokens.
+ * Under the logit shift (a row's output predicts the next position), row N-1
+ * holds x_N, the stride's last token, so its output is the anchor
+ * distribution of the token after x_N (the next stride's first proposal,
+ * always kept), and rows N..2N-2 hold MASK.  One forward both verifies and
+ * proposes:
  *
  *   isd_attention  strictly causal multi-query attention of the stride over
  *                  the request's paged KV cache and the stride itself;
  *   isd_accept     the p/q test: accept x_k with probability min(1, p/q),
  *                  resample from normalize(max(0, p - q)) at the first
  *                  rejection;
- *   kv_commit      append the CLEAN rows of accepted tokens to the KV pages
+ *   kv_commit      append the rows of the accepted prefix to the KV pages
  *                  (isd_accept_commit: both in one call);
- *   isd_propose    draw the next N proposals at the MASK rows (sampling or
+ *   isd_propose    draw the next N proposals at rows N-1..2N-2 (sampling or
  *                  argmax);
  *   isd_loop_advance  per-request bookkeeping of the multi-step decoding loop;
  *   isd_lora_delta the gated low-rank delta of Residual ISD (R-ISD), added at
@@ -34,7 +38,7 @@
  *   allocates, frees or synchronises on these calls; the work is enqueued on
  *   `stream` and the call returns at once.  Calls on one stream run in order;
  *   the intended order per step is attention -> accept -> commit (a decoding
- *   loop: attention -> accept -> propose -> loop_advance -> commit).  Calls
+ *   loop: attention -> accept_commit and propose -> loop_advance).  Calls
  *   enqueue kernels only (no memset, no allocation), so they may be recorded
  *   into a HIP graph.  The only state kept between calls is each device's
  *   compute-unit count, queried once.
@@ -84,7 +88,7 @@ typedef enum isd_dtype {
 #define ISD_FLAG_CTX_RANGE 0x1u    /* ctx_lens[r] < 0 or > max_pages * page_size */
 #define ISD_FLAG_PAGE_RANGE 0x2u   /* a needed page_table entry is outside [0, num_pages) */
 #define ISD_FLAG_TOKEN_RANGE 0x4u  /* a proposal id is outside [0, vocab) */
-#define ISD_FLAG_COMMIT_RANGE 0x8u /* n_commit[r] outside [0, N-1], or no page for a commit slot */
+#define ISD_FLAG_COMMIT_RANGE 0x8u /* n_commit[r] outside [0, N], or no page for a commit slot */
 #define ISD_FLAG_ROW_RANGE 0x10u   /* a LoRA mask row is outside [0, rows) */
 
 /*
@@ -206,7 +210,8 @@ isd_status isd_attention(const isd_shape* shape, const void* q, const void* k_ne
  *   accept_len [B] int32             written: A
  *   out_tokens [B][N] int32          written: x_1..x_A, then y* if A < N, then -1
  *   n_out      [B] int32             written: A + (A < N)
- *   n_commit   [B] int32             written: min(A, N-1), the CLEAN rows to commit
+ *   n_commit   [B] int32             written: A, the stride rows 0..A-1 that hold
+ *                                    the accepted prefix and are committed
  *   logp_sel, logq_sel [B][N-1] fp32 written: log p(x_k), log q(x_k) for every row
  *   q_norms    [B][N] float pairs (max, sum of exp(l - max)), 8-byte aligned,
  *              or NULL.  The q rows are the previous forward's MASK rows
@@ -230,20 +235,22 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
                       void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
- * kv_commit -- append the accepted CLEAN rows of every stride to the KV pages.
+ * kv_commit -- append the accepted prefix of every stride to the KV pages.
  *
  * Definition (paged KV cache reused from the AR serving stack:
  * "I-DLM：扩散模型如何用'自省一致性'追上自回归模型质量", section "推理：复用 AR
- * 推理栈"): a CLEAN row's key/value is valid iff its token was accepted, so
- * rows 0..n_commit[r]-1 of k_new[r] / v_new[r] are written to positions
- * ctx_lens_in[r] + i, and ctx_lens_out[r] = ctx_lens_in[r] + n_commit[r].
+ * 推理栈"; the accepted prefix is committed, and a row's key/value is valid
+ * iff its token and every token before it were accepted): rows
+ * 0..n_commit[r]-1 of k_new[r] / v_new[r] (the rows holding x_1..x_A) are
+ * written to positions ctx_lens_in[r] + i, and ctx_lens_out[r] =
+ * ctx_lens_in[r] + n_commit[r].
  *
  *   k_new, v_new  [B][Q][Hkv][D] kv_dtype
  *   k_pages, v_pages  pool layout above, written in the committed slots only
  *   page_table    [B][max_pages] int32; the caller maps pages for every slot
- *                 it may commit (positions up to ctx_len + N - 2)
+ *                 it may commit (positions up to ctx_len + N - 1)
  *   ctx_lens_in   [B] int32
- *   n_commit      [B] int32 in [0, N-1] (isd_accept's output)
+ *   n_commit      [B] int32 in [0, N] (isd_accept's output)
  *   ctx_lens_out  [B] int32, written; may alias ctx_lens_in
  *
  * Flags: CTX_RANGE, COMMIT_RANGE, PAGE_RANGE (the row is skipped and the
@@ -268,10 +275,12 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
  *
  *   loop_mode [B] int32 or NULL: the decoding loop's per-request mode before
  *             this forward's isd_loop_advance (ISD_LOOP_VERIFY /
- *             ISD_LOOP_REPROPOSE, below).  A re-proposing request commits no
- *             row and keeps its length, the gate isd_loop_advance applies to
- *             n_commit, so a loop forward can commit here instead of calling
- *             kv_commit after the bookkeeping.  NULL: no gate.
+ *             ISD_LOOP_REPROPOSE, below).  A verifying request commits its
+ *             accepted prefix as above; a re-proposing request commits one
+ *             row, its stride row N-1 (which carries the token the forward
+ *             before resampled), at position ctx_lens_in[r], and its length
+ *             grows by one.  A loop forward commits here; there is no
+ *             kv_commit after the bookkeeping.  NULL: every request verifies.
  *
  * Flags: those of both calls.
  */
@@ -342,26 +351,37 @@ isd_status isd_propose(const isd_shape* shape, const void* mask_logits, const in
  * more forward that proposes again from the corrected prefix, the reading
  * that reproduces the TPF column of "自省扩散语言模型的 token 生成机制与工程
  * 实践", section "Token 生成的核心参数与验收机制").  A forward of the batch is
- * isd_attention -> isd_accept -> isd_propose -> isd_loop_advance -> kv_commit
- * on one stream, with isd_accept and isd_propose called with `proposals` and
- * `positions` below.  Per request r:
+ * isd_attention (with ctx_lens = positions) -> isd_accept_commit (with
+ * loop_mode = mode) and isd_propose -> isd_loop_advance on one stream (or
+ * the two middle calls on two streams, joined before the bookkeeping), with
+ * isd_accept_commit and isd_propose called with `proposals` and `positions`
+ * below.  Per request r:
  *
  *   forwards[r] += 1, and
  *   mode VERIFY, accept_len A = N: tokens += N, proposals <- next_proposals,
  *                                   positions += N;
  *   mode VERIFY, A < N:            tokens += n_out (= A + 1), proposals kept,
  *                                   mode <- REPROPOSE, positions += n_out - N
- *                                   (so the re-proposing forward's MASK row k
+ *                                   (so the re-proposing forward's row N-1 sits
+ *                                   at the resampled token's position and
+ *                                   carries it, and its proposing row k
  *                                   proposes the token right after the
  *                                   committed prefix, plus k);
- *   mode REPROPOSE:                its accept result is ignored, n_commit <- 0
- *                                   (no KV rows committed), proposals <-
+ *   mode REPROPOSE:                its accept result is ignored, n_commit <- 1
+ *                                   (its row N-1 was committed), proposals <-
  *                                   next_proposals, mode <- VERIFY,
  *                                   positions += N.
  *
+ * Every committed token's key and value are then written exactly once, at
+ * its own position: between forwards the committed length is positions[r]
+ * in VERIFY mode and positions[r] + N - 1 in REPROPOSE mode (the resampled
+ * token still waits for its row), and positions[r] is the context length the
+ * next forward's attention reads.
+ *
  *   accept_len, n_out [B] int32   this forward's isd_accept outputs
  *   next_proposals [B][N] int32   this forward's isd_propose output
- *   n_commit  [B] int32           isd_accept's output, gated in place
+ *   n_commit  [B] int32           isd_accept's output; set to 1 for a
+ *                                 re-proposing request (rows committed)
  *   mode      [B] int32           ISD_LOOP_VERIFY / ISD_LOOP_REPROPOSE, in/out
  *   proposals [B][N] int32        the stride's x_1..x_N, in/out
  *   positions [B] int32           positions argument of the next forward, in/out;

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   if (lane == 0) {
     a.accept_len[r] = A;
     a.n_out[r] = A + (A < N ? 1 : 0);
-    a.n_commit[r] = min(A, N - 1);
+    a.n_commit[r] = A;                  // rows 0..A-1 hold the accepted prefix
     if (first >= 0) {
       ReqState st;
       st.req = r;
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   __shared__ int commit_last;
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
-  // columns past the residual shards (isd_accept_commit only): commit CLEAN
+  // columns past the residual shards (isd_accept_commit only): commit stride
   // row sh - r_shards of request k while the residual work runs
   if (sh >= r_shards) {
     if (cm.kv_bf16)
@@ -855,10 +855,10 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   hipLaunchKernelGGL((lse_partial<T>), dim3((q_norms ? 1 : 2) * (N - 1) * p.shards, B), dim3(kThreads), 0, stream,
                      a, p.shard_len, part);
   hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
-  // with a commit, N - 1 more columns of workgroups: one per (CLEAN row, request)
+  // with a commit, N more columns of workgroups: one per (stride row 0..N-1, request)
   CommitArgs cm{};
   if (commit) cm = *commit;
-  const int cols = p.r_shards + (commit ? N - 1 : 0);
+  const int cols = p.r_shards + (commit ? N : 0);
   hipLaunchKernelGGL((resid_pass<T>), dim3(cols, B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,
                      rej_count, rshards, cm);
   hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,

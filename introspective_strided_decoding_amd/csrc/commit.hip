@@ -1,6 +1,6 @@
-// Appending accepted CLEAN rows to the KV pages (kv_commit) and the
+// Appending accepted stride rows to the KV pages (kv_commit) and the
 // workspace header fill (isd_workspace_init).  The row commit itself lives
-// in commit_row.hpp: one workgroup per (request, CLEAN row).
+// in commit_row.hpp: one workgroup per (request, stride row 0..N-1).
 #include "commit_row.hpp"
 
 namespace isd {
@@ -45,7 +45,7 @@ CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new,
 }
 
 hipError_t launch_commit(const isd_shape& s, const CommitArgs& c, hipStream_t stream) {
-  const dim3 grid(s.stride_n - 1, s.batch);
+  const dim3 grid(s.stride_n, s.batch);
   if (c.kv_bf16)
     hipLaunchKernelGGL((kv_commit_kernel<uint16_t>), grid, dim3(kCommitThreads), 0, stream, c);
   else

@@ -1,12 +1,18 @@
-// Appending one accepted CLEAN row to the KV pages: the device code shared by
+// Appending accepted stride rows to the KV pages: the device code shared by
 // the kv_commit kernel and the accept launch that also commits.
 //
-// One workgroup of kCommitThreads threads per (request r, CLEAN row i).  It
-// requests the row's key and value vectors before the request's length and
-// page id arrive, stores them if i < n_commit and the pages of rows 0..i are
-// mapped (16-byte stores into the key layout, element stores into the
-// transposed value layout), and counts its arrival; the request's last
-// arrival writes the new length, so ctx_lens_out may alias ctx_lens_in.
+// One workgroup of kCommitThreads threads per (request r, stride row i),
+// i = 0..N-1.  A request commits n rows starting at stride row f: row f + t
+// goes to position L + t (L = its length before the commit).  Normally f = 0
+// and n = n_commit[r] (the accepted prefix x_1..x_A); a request of the
+// decoding loop in re-proposing mode commits row N-1 only (f = N-1, n = 1),
+// which carries the token its previous forward resampled.  The workgroup
+// requests its row's key and value vectors before the request's length and
+// page id arrive, stores them if its row is committed and the pages of the
+// positions L..L+t are all mapped (16-byte stores into the key layout,
+// element stores into the transposed value layout), and counts its arrival;
+// the request's last arrival writes the new length, so ctx_lens_out may
+// alias ctx_lens_in.
 #pragma once
 
 #include "device_common.hpp"
@@ -52,7 +58,7 @@ template <typename T>
 __device__ __forceinline__ void commit_row(const CommitArgs& c, int i, int r, int* s_last) {
   constexpr int EV = 16 / sizeof(T);
   const int N = c.N, Hkv = c.Hkv, D = c.D, max_pages = c.max_pages, num_pages = c.num_pages;
-  const int R = N - 1, Qn = 2 * N - 1;
+  const int Qn = 2 * N - 1;
   const int rvec = Hkv * D / EV;                 // 16-byte vectors per key (or value) row
   const size_t row_off = (size_t(r) * Qn + i) * Hkv * D;
   const u32x4* ksrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(c.k_new) + row_off);
@@ -66,22 +72,26 @@ __device__ __forceinline__ void commit_row(const CommitArgs& c, int i, int r, in
     if (w < 2 * rvec) pre[m] = (w < rvec) ? ksrc[w] : vsrc[w - rvec];
   }
   const int cap = max_pages * kPage;
-  int L = c.ctx_in[r], n = c.n_commit[r];
-  const bool bad_n = n < 0 || n > R, bad_L = L < 0 || L > cap;
-  if (bad_n) n = n < 0 ? 0 : R;
-  if (c.loop_mode && c.loop_mode[r] == ISD_LOOP_REPROPOSE) n = 0;   // its accept result is ignored
+  int L = c.ctx_in[r], n = c.n_commit[r], f = 0;
+  const bool bad_n = n < 0 || n > N, bad_L = L < 0 || L > cap;
+  if (bad_n) n = n < 0 ? 0 : N;
+  if (c.loop_mode && c.loop_mode[r] == ISD_LOOP_REPROPOSE) {   // the resampled token's row
+    n = 1;
+    f = N - 1;
+  }
   if (bad_L) { L = L < 0 ? 0 : cap; n = 0; }
-  // rows 0..i must all be mapped for row i to be stored
-  bool store = i < n;
+  // positions L..L+t must all be mapped for row f + t to be stored
+  const int t = i - f;
+  bool store = t >= 0 && t < n;
   if (store) {
     const int lane = threadIdx.x & 63;
-    const int pid_t = (lane <= i) ? commit_page(c.table, r, L, lane, max_pages, num_pages) : 0;
+    const int pid_t = (lane <= t) ? commit_page(c.table, r, L, lane, max_pages, num_pages) : 0;
     const uint64_t bad = __ballot(pid_t < 0);
     store = (bad == 0);
   }
   if (store) {
-    const int pid = commit_page(c.table, r, L, i, max_pages, num_pages);
-    const int slot = (L + i) % kPage;
+    const int pid = commit_page(c.table, r, L, t, max_pages, num_pages);
+    const int slot = (L + t) % kPage;
 #pragma unroll
     for (int m = 0; m < kCommitPre; ++m) {
       const int w = threadIdx.x + m * kCommitThreads;
@@ -90,7 +100,7 @@ __device__ __forceinline__ void commit_row(const CommitArgs& c, int i, int r, in
     for (int w = threadIdx.x + kCommitPre * kCommitThreads; w < 2 * rvec; w += kCommitThreads)
       commit_store<T>(w, rvec, D, Hkv, pid, slot, (w < rvec) ? ksrc[w] : vsrc[w - rvec], kp, vp);
   }
-  if (!arrive_last(&c.arrivals[r], uint32_t(R), s_last)) return;
+  if (!arrive_last(&c.arrivals[r], uint32_t(N), s_last)) return;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int pid_t = (lane < n) ? commit_page(c.table, r, L, lane, max_pages, num_pages) : 0;

@@ -160,7 +160,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 8; }
+int32_t isd_abi_version(void) { return 9; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {

@@ -1,11 +1,12 @@
 // Per-request bookkeeping of the multi-step decoding loop (isd_loop_advance).
 //
 // One thread per request applies one forward's results: committed tokens and
-// forwards are counted, the stride's proposals are replaced by the MASK-row
-// proposals unless the forward rejected one (then the next forward
-// re-proposes from the corrected prefix), the positions argument of the next
-// forward moves with them, and the KV rows of a re-proposing forward are not
-// committed.  With a normaliser buffer, the MASK rows' (max, sum exp) pairs
+// forwards are counted, the stride's proposals are replaced by this forward's
+// proposals unless it rejected one (then the next forward re-proposes from
+// the corrected prefix, its row N-1 carrying the resampled token), the
+// positions argument of the next forward moves with them, and n_commit
+// reports the KV rows the forward committed (a re-proposing forward: one,
+// its row N-1).  With a normaliser buffer, the MASK rows' (max, sum exp) pairs
 // this forward's proposals wrote move to where the next forward's accept test
 // reads its q-row normalisers (every forward's: the next forward verifies the
 // proposals this one drew, whatever the mode).
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void loop_advance_kernel(int B, int N, const i
       take = false;
     }
   } else {
-    n_commit[r] = 0;
+    n_commit[r] = 1;
     mode[r] = ISD_LOOP_VERIFY;
     positions[r] += N;
   }

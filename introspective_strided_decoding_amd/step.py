@@ -120,10 +120,13 @@ class DeviceStep:
             c = calls[key] = build()
         return c
 
-    def attention(self, stream=None):
-        self._call("attention", lambda: _lib.prepare(
+    def attention(self, stream=None, loop: bool = False):
+        """``loop``: the decoding loop's forward, whose context length is the positions
+        argument (the stride's first row sits there; while a resampled token waits for
+        its row the committed length runs N - 1 ahead of it)."""
+        self._call(("attention", loop), lambda: _lib.prepare(
             _lib.isd_attention, self.shape, self.q, self.k_new, self.v_new, self.k_pages, self.v_pages,
-            self.page_table, self.ctx_lens, self.out, self.workspace))(stream)
+            self.page_table, self.positions if loop else self.ctx_lens, self.out, self.workspace))(stream)
 
     def _step_dev(self, device_step: bool):
         return self.extra["forwards"] if device_step else None
@@ -146,8 +149,9 @@ class DeviceStep:
 
     def accept_commit(self, stream=None, step: Optional[int] = None, seed=None, device_step: bool = False,
                       q_norms=None, loop: bool = False):
-        """accept, then commit of the accepted rows, in one library call; ``loop``: a
-        re-proposing request of the decoding loop commits nothing (the loop's mode)."""
+        """accept, then commit of the accepted prefix, in one library call; ``loop``: by the
+        decoding loop's mode, a re-proposing request commits its row N-1 instead (the token
+        the forward before resampled)."""
         self._call(("accept_commit", device_step, q_norms is not None, loop), lambda: _lib.prepare(
             _lib.isd_accept_commit, self.shape, self.p_logits, self.q_logits, self.proposals, self.req_ids,
             self.positions, self.seed, self.step, self.accept_len, self.out_tokens, self.n_out, self.n_commit,
@@ -221,8 +225,10 @@ class DeviceStep:
 
     def loop_forward(self, step: int = 0, attention: bool = True, stream=None, overlap: bool = True,
                      device_step: bool = False, carry: bool = True):
-        """One forward of the decoding loop: attention, accept and proposals (side by side
-        unless ``overlap`` is False), bookkeeping, commit.  With ``device_step`` the Philox
+        """One forward of the decoding loop: attention over ``positions`` cached tokens,
+        accept with the commit of the forward's rows, and proposals (side by side unless
+        ``overlap`` is False), bookkeeping.  Lengths are updated in place, so build the
+        step with ``commit_in_place=True``.  With ``device_step`` the Philox
         step of every request is its forward count on the device (``step`` unused), so the
         forward can be recorded once and replayed.  With ``carry`` the proposals also write
         their rows' normalisers, and the next forward's accept test takes its q-row
@@ -231,9 +237,9 @@ class DeviceStep:
         e = self.extra
         q_norms = e["norms"] if carry and e.get("norms_valid") else None
         if attention:
-            # the accepted CLEAN rows are committed inside the accept launches, gated by the
-            # loop's mode as the bookkeeping gates n_commit
-            self.attention(stream)
+            # the forward's rows are committed inside the accept launches, by the loop's mode:
+            # a verifying request its accepted prefix, a re-proposing one its row N-1
+            self.attention(stream, loop=True)
             accept = lambda s, t: self.accept_commit(s, step=t, device_step=device_step, q_norms=q_norms,
                                                      loop=True)
         else:

@@ -117,3 +117,28 @@ def fetch_accept(st):
             "n_out": st.n_out.cpu().numpy(), "n_commit": st.n_commit.cpu().numpy(),
             "logp_sel": st.logp_sel.cpu().numpy().astype(np.float64),
             "logq_sel": st.logq_sel.cpu().numpy().astype(np.float64)}
+
+
+def check_step_against_oracle(wl, st, tally: AcceptTally = None):
+    """Every output of one whole step (st.run(): attention, accept + commit, and the next
+    proposals when the workload carries MASK-row logits) against the oracle on the same
+    inputs: attention element-wise, accept results outside near-ties, both pools bit for bit
+    after the oracle's commit of the GPU's counts, the new lengths, and the proposals."""
+    from oracle.commit import kv_commit as oracle_commit
+    from oracle.propose import isd_propose as oracle_propose
+    from introspective_strided_decoding_amd.layout import unpack_k_pages, unpack_v_pages
+    tally = tally if tally is not None else AcceptTally()
+    check_attention(wl, st.out)
+    got = fetch_accept(st)
+    check_accept_step(wl, got, wl.philox_seed, wl.step, tally)
+    assert tally.near_ties <= max(0, NEAR_TIE_BUDGET * tally.decisions), tally.near_ties
+    k_ref, v_ref, lens_ref = oracle_commit(wl.k_pool, wl.v_pool, wl.page_table, wl.ctx_lens,
+                                           wl.k_new, wl.v_new, got["n_commit"], wl.cfg.page_size)
+    assert np.array_equal(st.ctx_lens_out.cpu().numpy(), lens_ref)
+    assert np.array_equal(unpack_k_pages(st.k_pages).float().cpu().numpy(), k_ref)
+    assert np.array_equal(unpack_v_pages(st.v_pages).float().cpu().numpy(), v_ref)
+    if getattr(wl, "mask_logits", None) is not None and st.next_proposals is not None:
+        nxt, margins = oracle_propose(wl.mask_logits, wl.req_ids, wl.positions, wl.philox_seed, wl.step)
+        prop = st.next_proposals.cpu().numpy()
+        assert ((prop == nxt) | (margins < PROPOSE_NEAR_TIE)).all()
+    return tally

@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 8
+    assert LIB.isd_abi_version() == 9
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"

@@ -117,7 +117,7 @@ def test_accept_identical_rows_always_accept():
     torch.cuda.synchronize()
     g = fetch_accept(st)
     assert (g["accept_len"] == wl.cfg.stride_n).all()
-    assert (g["n_commit"] == wl.cfg.stride_n - 1).all()
+    assert (g["n_commit"] == wl.cfg.stride_n).all()       # rows 0..N-1 hold x_1..x_N
     assert np.array_equal(g["out_tokens"], wl.proposals)
 
 

@@ -33,8 +33,8 @@ def test_commit_matches_oracle(name, over, in_place):
     cfg = get_config(name, **over)
     wl = make_workload(cfg, seed=21, with_logits=False)
     rng = np.random.Generator(np.random.PCG64(5))
-    n_commit = rng.integers(0, cfg.stride_n, size=cfg.batch).astype(np.int32)
-    n_commit[0] = cfg.stride_n - 1
+    n_commit = rng.integers(0, cfg.stride_n + 1, size=cfg.batch).astype(np.int32)
+    n_commit[0] = cfg.stride_n
     st = device_step(wl, commit_in_place=in_place)
     st.n_commit.copy_(torch.from_numpy(n_commit))
     st.commit()
@@ -52,7 +52,7 @@ def test_commit_matches_oracle(name, over, in_place):
 def test_commit_then_attention_sees_grown_context():
     cfg = get_config("b8_ctx2k", batch=3, ctx=30, vocab=64)
     wl = make_workload(cfg, seed=22, with_logits=False)
-    n_commit = np.array([3, 1, 2], dtype=np.int32)
+    n_commit = np.array([4, 1, 2], dtype=np.int32)
     st = device_step(wl, commit_in_place=True)
     st.n_commit.copy_(torch.from_numpy(n_commit))
     st.commit()
@@ -75,13 +75,13 @@ def test_commit_range_flags():
     wl.page_table[2, 2] = -1                       # page of positions 32..47 unmapped
     wl.ctx_lens[2] = 30
     st = device_step(wl)
-    st.n_commit.copy_(torch.tensor([7, 1, 3], dtype=torch.int32))
+    st.n_commit.copy_(torch.tensor([7, 1, 3], dtype=torch.int32))    # 7 > N = 4: clamped to N
     st.commit()
     torch.cuda.synchronize()
     flags = isd_read_flags(st.workspace)
     assert flags & 8 and flags & 2
     lens = st.ctx_lens_out.cpu().numpy()
-    assert lens[0] == 40 + 3 and lens[1] == 41 and lens[2] == 32
+    assert lens[0] == 40 + 4 and lens[1] == 41 and lens[2] == 32
 
 
 def _bits(t):
@@ -100,7 +100,7 @@ def test_accept_commit_equals_accept_then_commit(name, over, in_place):
     oracle's commit of the accepted counts."""
     cfg = get_config(name, **over)
     steps = 4
-    wl = make_workload(cfg, seed=31, extra_tokens=steps * (cfg.stride_n - 1))
+    wl = make_workload(cfg, seed=31, extra_tokens=steps * cfg.stride_n)
     a = device_step(wl, commit_in_place=in_place)
     b = device_step(wl, commit_in_place=in_place)
     k_ref, v_ref, lens = wl.k_pool, wl.v_pool, wl.ctx_lens.copy()
@@ -125,32 +125,67 @@ def test_accept_commit_equals_accept_then_commit(name, over, in_place):
     assert isd_read_flags(a.workspace) == 0 and isd_read_flags(b.workspace) == 0
 
 
-def test_accept_commit_with_loop_mode_commits_verifying_requests_only():
-    """With the decoding loop's modes, a re-proposing request commits no row and keeps its
-    length; the others commit what isd_accept decided: the same pools and lengths as
-    isd_accept, the gate isd_loop_advance applies, then kv_commit."""
+def test_accept_commit_with_loop_mode():
+    """With the decoding loop's modes, a verifying request commits its accepted prefix
+    (what isd_accept decided) and a re-proposing request commits one row, its stride
+    row N-1 (the row that carries the token the forward before resampled), at its
+    length: pools and lengths bit for bit against the oracle's commit of those rows,
+    forward after forward, and the accept outputs as isd_accept alone gives them."""
     from introspective_strided_decoding_amd._lib import LOOP_REPROPOSE, LOOP_VERIFY
     cfg = get_config("b8_ctx2k", batch=9, ctx=20, vocab=3000)
-    steps = 3
-    wl = make_workload(cfg, seed=33, extra_tokens=steps * (cfg.stride_n - 1))
+    n, steps = cfg.stride_n, 3
+    wl = make_workload(cfg, seed=33, extra_tokens=steps * n)
     a = device_step(wl, commit_in_place=True)
     b = device_step(wl, commit_in_place=True)
     b.loop_start()
     modes = [np.array([LOOP_REPROPOSE if (r + s) % 3 == 0 else LOOP_VERIFY for r in range(cfg.batch)],
                       dtype=np.int32) for s in range(steps)]
+    k_ref, v_ref, lens = wl.k_pool, wl.v_pool, wl.ctx_lens.copy()
     for step in range(steps):
         b.extra["mode"].copy_(torch.from_numpy(modes[step]).cuda())
         a.accept(step=step)
-        torch.cuda.synchronize()
-        gated = a.n_commit.cpu().numpy().copy()
-        gated[modes[step] == LOOP_REPROPOSE] = 0
-        a.n_commit.copy_(torch.from_numpy(gated).cuda())
-        a.commit()
         b.accept_commit(step=step, loop=True)
         torch.cuda.synchronize()
-        assert torch.equal(_bits(a.ctx_lens_out), _bits(b.ctx_lens_out)), step
-        assert torch.equal(_bits(a.k_pages), _bits(b.k_pages)), step
-        assert torch.equal(_bits(a.v_pages), _bits(b.v_pages)), step
-        for f in ("accept_len", "out_tokens", "n_out"):
+        for f in ("accept_len", "out_tokens", "n_out", "n_commit"):
             assert torch.equal(_bits(getattr(a, f)), _bits(getattr(b, f))), (step, f)
+        rep = modes[step] == LOOP_REPROPOSE
+        n_rows = np.where(rep, 1, a.n_commit.cpu().numpy())
+        first = np.where(rep, n - 1, 0)
+        k_ref, v_ref, lens = oracle_commit(k_ref, v_ref, wl.page_table, lens, wl.k_new, wl.v_new, n_rows,
+                                           cfg.page_size, first_row=first)
+        assert np.array_equal(b.ctx_lens.cpu().numpy(), lens), step
+    k_got, v_got = _unpacked(b)
+    assert np.array_equal(k_got, k_ref)
+    assert np.array_equal(v_got, v_ref)
     assert (modes[0] == LOOP_REPROPOSE).any() and (modes[0] == LOOP_VERIFY).any()
+    from introspective_strided_decoding_amd import isd_read_flags
+    assert isd_read_flags(b.workspace) == 0
+
+
+@pytest.mark.parametrize("name", ["c32_ctx4k", "c64_ragged"])
+def test_accept_commit_full_size(name):
+    """isd_accept_commit at the workload's real shape, in the launch configuration the
+    benchmark times (shuffled page tables, lengths updated in place): every request's
+    accept length, committed tokens and counts against the oracle (near-ties counted),
+    the new lengths exactly, and both whole pools, unpacked, bit for bit against the
+    oracle's commit of the GPU's counts (equal to the oracle's own outside near-ties)."""
+    from parity import AcceptTally, NEAR_TIE_BUDGET, check_accept_step, fetch_accept
+    cfg = get_config(name)
+    wl = make_workload(cfg, seed=41)
+    st = device_step(wl, max_ctx=int(wl.ctx_lens.max()), commit_in_place=True)
+    st.accept_commit(step=wl.step)
+    torch.cuda.synchronize()
+    got = fetch_accept(st)
+    tally = AcceptTally()
+    check_accept_step(wl, got, wl.philox_seed, wl.step, tally)
+    assert tally.requests == cfg.batch
+    assert tally.near_ties <= max(0, NEAR_TIE_BUDGET * tally.decisions), tally.near_ties
+    k_ref, v_ref, lens_ref = oracle_commit(wl.k_pool, wl.v_pool, wl.page_table, wl.ctx_lens,
+                                           wl.k_new, wl.v_new, got["n_commit"], cfg.page_size)
+    assert np.array_equal(st.ctx_lens.cpu().numpy(), lens_ref)
+    k_got, v_got = _unpacked(st)
+    assert np.array_equal(k_got, k_ref)
+    del k_got, k_ref
+    assert np.array_equal(v_got, v_ref)
+    from introspective_strided_decoding_amd import isd_read_flags
+    assert isd_read_flags(st.workspace) == 0

@@ -1,16 +1,17 @@
 """The step recorded into a HIP graph and replayed.
 
 A graph of one whole step (attention -> accept -> commit -> proposals) must
-reproduce the eager step bit for bit on every replay.  Between replays the
-outputs are cleared and unrelated eager work runs on the same device, so a
-replay that skipped a kernel, or a counter that was not rewound, shows up as
-a difference.
+reproduce the eager step bit for bit on every replay, and the replayed outputs
+must match the oracle on the same inputs (attention element-wise, accept
+results, both pools, lengths and proposals).  Between replays the outputs are
+cleared and unrelated eager work runs on the same device, so a replay that
+skipped a kernel, or a counter that was not rewound, shows up as a difference.
 """
 
 import pytest
 import torch
 
-from parity import device_step, needs_gpu
+from parity import check_step_against_oracle, device_step, needs_gpu
 from workloads import get_config, make_workload
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -48,6 +49,8 @@ def test_graph_replays_match_eager(name, over):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
+        if rep == 0:
+            check_step_against_oracle(wl, st)           # the replay against the oracle
         for k in OUTPUTS:
             assert torch.equal(getattr(st, k), ref[k]), (name, rep, k)
     from introspective_strided_decoding_amd import isd_read_flags

@@ -1,13 +1,16 @@
 """The multi-step decoding loop on the GPU.
 
-* Transition parity: a full loop (attention, accept, proposals, bookkeeping,
-  commit) runs for a number of forwards; before each forward the GPU's loop
-  state is read back and the oracle applies the same forward to it (accept
-  test, proposals, bookkeeping, commit).  Accept lengths, committed tokens,
-  proposals, the new state and the gated commit counts must be identical,
-  except for requests with a near-tie decision; the KV pools and lengths are
-  compared bit for bit at the end, and a last attention call is checked on
-  the grown contexts.
+* Transition parity: a full loop (attention, accept with the commit,
+  proposals, bookkeeping) runs for a number of forwards; before each forward
+  the GPU's loop state is read back and the oracle applies the same forward to
+  it (accept test, proposals, bookkeeping, commit of the forward's rows).
+  Accept lengths, committed tokens, proposals, the new state and the commit
+  counts must be identical, except for requests with a near-tie decision; the
+  lengths must keep the loop's invariant (committed length = positions, or
+  positions + N - 1 while a resampled token waits for its row); the KV pools
+  and lengths are compared bit for bit, and a last attention call is checked
+  on the grown contexts.  The same check runs on every replay of a recorded
+  loop forward.
 * TPF: the loop's measured tokens per forward (accept + proposals +
   bookkeeping, logits with per-row acceptance 0.9) reproduce the closed form
   and the printed TPF column for N = 2, 3, 4, 5, 8.
@@ -49,76 +52,105 @@ def _dev(x, like):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device=like.device, dtype=like.dtype)
 
 
-def test_loop_transitions_match_oracle():
-    from oracle import accept as oaccept
-    from oracle import loop as oloop
-    from oracle import propose as oprop
-    from oracle.commit import kv_commit as ocommit
-    from oracle.attention import stride_attention
+class OracleLoop:
+    """The oracle's copy of a GPU loop: applies each forward the GPU ran to the GPU's own
+    state before it, checks every transition, and keeps the oracle's pools and lengths."""
 
-    T, K = 12, 3
-    cfg = get_config("b8_ctx2k", batch=12, ctx=40, vocab=1000, stride_n=4)
-    n = cfg.stride_n
-    wl = make_workload(cfg, seed=61, with_mask_logits=True, extra_tokens=T * (n - 1))
-    pool = _pool(cfg, K, 300, "batch")
-    st = device_step(wl, commit_in_place=True)
-    st.loop_start()
-    seeds = wl.philox_seed
-    k_pool, v_pool, ctx = wl.k_pool.copy(), wl.v_pool.copy(), wl.ctx_lens.copy()
-    near = 0
-    for t in range(T):
-        p, q = (wl.p_logits, wl.q_logits) if t == 0 else pool[(t - 1) % K][:2]
-        mask = pool[t % K][2]
-        st.p_logits.copy_(_dev(p, st.p_logits))
-        st.q_logits.copy_(_dev(q, st.q_logits))
-        st.mask_logits.copy_(_dev(mask, st.mask_logits))
-        pre = oloop.LoopState(st.extra["mode"].cpu().numpy().astype(np.int64),
-                              st.proposals.cpu().numpy().astype(np.int64),
-                              st.positions.cpu().numpy().astype(np.int64),
-                              st.extra["tokens"].cpu().numpy(), st.extra["forwards"].cpu().numpy())
-        st.loop_forward(step=t)
-        torch.cuda.synchronize()
-        # the oracle applies the same forward to the same state
-        res = oaccept.isd_accept(p, q, pre.proposals, wl.req_ids, pre.pos, seeds, t)
-        nxt, margins = oprop.isd_propose(mask, wl.req_ids, pre.pos, seeds, t)
+    def __init__(self, wl):
+        self.wl = wl
+        self.k_pool, self.v_pool, self.ctx = wl.k_pool.copy(), wl.v_pool.copy(), wl.ctx_lens.copy()
+        self.near = 0
+        self.decisions = 0
+
+    @staticmethod
+    def state(st):
+        from oracle import loop as oloop
+        return oloop.LoopState(st.extra["mode"].cpu().numpy().astype(np.int64),
+                               st.proposals.cpu().numpy().astype(np.int64),
+                               st.positions.cpu().numpy().astype(np.int64),
+                               st.extra["tokens"].cpu().numpy(), st.extra["forwards"].cpu().numpy())
+
+    def check(self, st, pre, p, q, mask, t, step):
+        """``pre``: the GPU state before forward t (Philox step ``step``), read by ``state``."""
+        from oracle import accept as oaccept
+        from oracle import loop as oloop
+        from oracle import propose as oprop
+        from oracle.commit import kv_commit as ocommit
+        wl, cfg = self.wl, self.wl.cfg
+        n = cfg.stride_n
+        res = oaccept.isd_accept(p, q, pre.proposals, wl.req_ids, pre.pos, wl.philox_seed, step)
+        nxt, margins = oprop.isd_propose(mask, wl.req_ids, pre.pos, wl.philox_seed, step)
         post = pre.copy()
-        gated = oloop.advance(post, [o.accept_len for o in res], [o.n_out for o in res], nxt,
-                              [o.n_commit for o in res])
+        n_commit, first_row = oloop.advance(post, [o.accept_len for o in res], [o.n_out for o in res], nxt)
+        verifying = pre.mode == oloop.VERIFY
         tie = np.zeros(cfg.batch, dtype=bool)
         for r, o in enumerate(res):
-            verifying = pre.mode[r] == oloop.VERIFY
-            tie[r] = verifying and (bool((o.accept_margins < ACCEPT_NEAR_TIE).any())
-                                    or o.resample_margin < RESAMPLE_NEAR_TIE)
+            tie[r] = verifying[r] and (bool((o.accept_margins < ACCEPT_NEAR_TIE).any())
+                                       or o.resample_margin < RESAMPLE_NEAR_TIE)
             tie[r] |= bool((margins[r] < PROPOSE_NEAR_TIE).any())
-        near += int(tie.sum())
+            self.decisions += o.decided if verifying[r] else 0
+        self.near += int(tie.sum())
         ok = ~tie
         got = {k: v.cpu().numpy() for k, v in (("accept_len", st.accept_len), ("n_out", st.n_out),
                                                 ("next", st.next_proposals), ("n_commit", st.n_commit),
                                                 ("mode", st.extra["mode"]), ("proposals", st.proposals),
                                                 ("positions", st.positions), ("tokens", st.extra["tokens"]),
                                                 ("forwards", st.extra["forwards"]))}
-        verifying = pre.mode == oloop.VERIFY
         assert (got["accept_len"][ok & verifying] == np.array([o.accept_len for o in res])[ok & verifying]).all(), t
         assert (got["n_out"][ok & verifying] == np.array([o.n_out for o in res])[ok & verifying]).all(), t
         assert (got["next"][ok] == nxt[ok]).all(), t
-        assert (got["n_commit"][ok] == gated[ok]).all(), t
+        assert (got["n_commit"][ok] == n_commit[ok]).all(), t
         assert (got["mode"][ok] == post.mode[ok]).all(), t
         assert (got["proposals"][ok] == post.proposals[ok]).all(), t
         assert (got["positions"][ok] == post.pos[ok]).all(), t
         assert (got["tokens"][ok] == post.tokens[ok]).all(), t
-        assert (got["forwards"] == t + 1).all()
-        # the oracle's commit with the GPU's gated counts (equal to its own outside near-ties)
-        k_pool, v_pool, ctx = ocommit(k_pool, v_pool, wl.page_table, ctx, wl.k_new, wl.v_new,
-                                      got["n_commit"], cfg.page_size)
-        assert (st.ctx_lens.cpu().numpy() == ctx).all(), t
-    assert near == 0 or near / (T * cfg.batch) < 1e-4
-    from introspective_strided_decoding_amd.layout import unpack_k_pages, unpack_v_pages
-    assert np.array_equal(unpack_k_pages(st.k_pages).float().cpu().numpy(), k_pool)
-    assert np.array_equal(unpack_v_pages(st.v_pages).float().cpu().numpy(), v_pool)
-    # attention over the grown contexts
+        assert (got["forwards"] == pre.forwards + 1).all()
+        # the oracle's commit of the GPU's rows (equal to its own outside near-ties)
+        first = np.where(pre.mode == oloop.REPROPOSE, n - 1, 0)
+        self.k_pool, self.v_pool, self.ctx = ocommit(self.k_pool, self.v_pool, wl.page_table, self.ctx,
+                                                     wl.k_new, wl.v_new, got["n_commit"], cfg.page_size,
+                                                     first_row=first)
+        lens = st.ctx_lens.cpu().numpy()
+        assert (lens == self.ctx).all(), t
+        pending = got["mode"] == oloop.REPROPOSE
+        assert (lens == got["positions"] + np.where(pending, n - 1, 0)).all(), t
+
+    def check_pools(self, st):
+        from introspective_strided_decoding_amd.layout import unpack_k_pages, unpack_v_pages
+        assert np.array_equal(unpack_k_pages(st.k_pages).float().cpu().numpy(), self.k_pool)
+        assert np.array_equal(unpack_v_pages(st.v_pages).float().cpu().numpy(), self.v_pool)
+
+    def check_budget(self):
+        assert self.near == 0 or self.near / max(1, self.decisions) < 1e-4
+
+
+def test_loop_transitions_match_oracle():
+    T, K = 12, 3
+    cfg = get_config("b8_ctx2k", batch=12, ctx=40, vocab=1000, stride_n=4)
+    wl = make_workload(cfg, seed=61, with_mask_logits=True, extra_tokens=T * cfg.stride_n)
+    pool = _pool(cfg, K, 300, "batch")
+    st = device_step(wl, commit_in_place=True)
+    st.loop_start()
+    orc = OracleLoop(wl)
+    reproposed = 0
+    for t in range(T):
+        p, q = (wl.p_logits, wl.q_logits) if t == 0 else pool[(t - 1) % K][:2]
+        mask = pool[t % K][2]
+        st.p_logits.copy_(_dev(p, st.p_logits))
+        st.q_logits.copy_(_dev(q, st.q_logits))
+        st.mask_logits.copy_(_dev(mask, st.mask_logits))
+        pre = orc.state(st)
+        reproposed += int((pre.mode == 1).sum())
+        st.loop_forward(step=t)
+        torch.cuda.synchronize()
+        orc.check(st, pre, p, q, mask, t, t)
+    orc.check_budget()
+    orc.check_pools(st)
+    assert reproposed > 0                     # re-proposing forwards committed their row N-1
+    # attention over the grown (committed) contexts
     st.attention()
     torch.cuda.synchronize()
-    wl.k_pool, wl.v_pool, wl.ctx_lens = k_pool, v_pool, ctx
+    wl.k_pool, wl.v_pool, wl.ctx_lens = orc.k_pool, orc.v_pool, orc.ctx
     check_attention(wl, st.out)
     from introspective_strided_decoding_amd import isd_read_flags
     assert isd_read_flags(st.workspace) == 0
@@ -157,7 +189,7 @@ def test_loop_with_proposals_beside_accept_matches_sequential():
     bit for bit, as the calls issued one after another."""
     T, K = 6, 3
     cfg = get_config("b8_ctx2k", batch=10, ctx=40, vocab=3000, stride_n=4)
-    wl = make_workload(cfg, seed=62, with_mask_logits=True, extra_tokens=T * (cfg.stride_n - 1))
+    wl = make_workload(cfg, seed=62, with_mask_logits=True, extra_tokens=T * cfg.stride_n)
     pool = _pool(cfg, K, 310, "batch")
     a = device_step(wl, commit_in_place=True)
     b = device_step(wl, commit_in_place=True)
@@ -203,7 +235,7 @@ def test_loop_device_step_matches_step_argument():
     draws when every request started together (forwards = t)."""
     T, K = 5, 3
     cfg = get_config("b8_ctx2k", batch=9, ctx=40, vocab=3000, stride_n=4)
-    wl = make_workload(cfg, seed=63, with_mask_logits=True, extra_tokens=T * (cfg.stride_n - 1))
+    wl = make_workload(cfg, seed=63, with_mask_logits=True, extra_tokens=T * cfg.stride_n)
     pool = _pool(cfg, K, 320, "batch")
     a = device_step(wl, commit_in_place=True)
     b = device_step(wl, commit_in_place=True)
@@ -222,27 +254,38 @@ def test_loop_device_step_matches_step_argument():
 def test_loop_forward_graph_replays_match_eager(overlap):
     """One loop forward recorded into a HIP graph and replayed forward after forward
     (logits refreshed in place in between) leaves the same state, pools and lengths as
-    the same forwards issued eagerly."""
+    the same forwards issued eagerly, and every replay's transition, commit and lengths
+    match the oracle's forward on the state before it."""
     T, K, warm = 6, 3, 2      # the second eager forward is the first with carried q normalisers
     cfg = get_config("b8_ctx2k", batch=8, ctx=40, vocab=3000, stride_n=4)
-    wl = make_workload(cfg, seed=64, with_mask_logits=True, extra_tokens=(T + warm) * (cfg.stride_n - 1))
+    wl = make_workload(cfg, seed=64, with_mask_logits=True, extra_tokens=(T + warm) * cfg.stride_n)
     pool = _pool(cfg, K, 330, "batch")
     a = device_step(wl, commit_in_place=True)
     b = device_step(wl, commit_in_place=True)
     for st in (a, b):
         st.loop_start()
+    orc = OracleLoop(wl)
     for t in range(warm):
         for st in (a, b):
             _feed(st, pool, wl, t, K)
+        pre = orc.state(b)
+        for st in (a, b):
             st.loop_forward(device_step=True, overlap=overlap)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        p, q = (wl.p_logits, wl.q_logits) if t == 0 else pool[(t - 1) % K][:2]
+        orc.check(b, pre, p, q, pool[t % K][2], t, t)
     graph = b.capture_loop_forward(overlap=overlap)
     for t in range(warm, warm + T):
         for st in (a, b):
             _feed(st, pool, wl, t, K)
         a.loop_forward(device_step=True, overlap=overlap)
         torch.cuda.synchronize()
+        pre = orc.state(b)
         graph.replay()
         torch.cuda.synchronize()
         _same_state(a, b, t)
+        p, q = pool[(t - 1) % K][:2]
+        orc.check(b, pre, p, q, pool[t % K][2], t, t)       # Philox step = forward count = t
+    orc.check_budget()
+    orc.check_pools(b)
     assert int(b.extra["forwards"][0]) == warm + T
