@@ -20,7 +20,8 @@
  *                  resample from normalize(max(0, p - q)) at the first
  *                  rejection;
  *   kv_commit      append the rows of the accepted prefix to the KV pages
- *                  (isd_accept_commit: both in one call);
+ *                  (isd_accept_commit: both in one call; isd_accept_commit_noalloc:
+ *                  the same without a caller workspace);
  *   isd_propose    draw the next N proposals at rows N-1..2N-2 (sampling or
  *                  argmax);
  *   isd_loop_advance  per-request bookkeeping of the multi-step decoding loop;
@@ -294,6 +295,39 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
                              const int32_t* page_table, const int32_t* ctx_lens_in,
                              int32_t* ctx_lens_out, const int32_t* loop_mode, void* workspace,
                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * isd_accept_commit_noalloc -- isd_accept_commit for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Same definitions, arguments, outputs and launches as isd_accept_commit,
+ * without `workspace` / `ws_bytes`: the partials live in a scratch array the
+ * library holds on each device (16 MiB, held until the process ends; its
+ * counter region is cleared by the first call on the device, and the kernels
+ * rewind every counter they use).  The call allocates nothing and calls no
+ * allocating routine.
+ *
+ *   flags  device pointer to one uint32 the caller owns (or NULL: not
+ *          reported), into which the kernels OR the ISD_FLAG_* bits that
+ *          isd_accept_commit would raise in its workspace.
+ *
+ * Returns ISD_ERR_WORKSPACE when the shape needs more than the 16 MiB
+ * (batch * ceil(vocab / 2048) * 176 bytes of residual partials dominate:
+ * e.g. 128 requests at a 1.2M-entry vocabulary fit).  Every call on one
+ * device shares that device's scratch: calls that overlap in time on one
+ * device (two streams, two threads) race; issue them in one stream's order.
+ */
+isd_status isd_accept_commit_noalloc(const isd_shape* shape, const void* p_logits, const void* q_logits,
+                                     const int32_t* proposals, const int32_t* req_ids,
+                                     const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi,
+                                     uint32_t step, const int64_t* step_per_request, const float* q_norms,
+                                     int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
+                                     int32_t* n_commit, float* logp_sel, float* logq_sel,
+                                     const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                                     const int32_t* page_table, const int32_t* ctx_lens_in,
+                                     int32_t* ctx_lens_out, const int32_t* loop_mode, uint32_t* flags,
+                                     hipStream_t stream);
 
 /*
  * isd_propose -- draw the next N proposals at the MASK rows.

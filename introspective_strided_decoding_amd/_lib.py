@@ -26,7 +26,7 @@ STATUS = {0: "ISD_OK", 1: "ISD_ERR_NULL", 2: "ISD_ERR_SHAPE", 3: "ISD_ERR_DTYPE"
 
 # Every symbol include/isd.h declares.
 EXPORTS = ("isd_workspace_bytes", "isd_workspace_init", "isd_read_flags", "isd_attention",
-           "isd_accept", "kv_commit", "isd_accept_commit", "isd_propose", "isd_loop_advance", "isd_lora_workspace_bytes",
+           "isd_accept", "kv_commit", "isd_accept_commit", "isd_accept_commit_noalloc", "isd_propose", "isd_loop_advance", "isd_lora_workspace_bytes",
            "isd_lora_delta", "isd_gated_linear_workspace_bytes", "isd_gated_linear",
            "isd_gated_linear_group_workspace_bytes", "isd_gated_linear_group",
            "isd_status_string", "isd_last_error", "isd_abi_version")
@@ -88,6 +88,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kv_commit": (I32, [SP, P, P, P, P, P, P, P, P, P, SZ, P]),
         "isd_accept_commit": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, P,
                                     P, P, P, P, P, P, P, P, P, SZ, P]),
+        "isd_accept_commit_noalloc": (I32, [SP, P, P, P, P, P, U64, U64, U32, P, P, P, P, P, P, P, P,
+                                            P, P, P, P, P, P, P, P, P, P]),
         "isd_propose": (I32, [SP, P, P, P, U64, U64, U32, P, I32, P, P, P, SZ, P]),
         "isd_loop_advance": (I32, [SP, P, P, P, P, P, P, P, P, P, P, P, P]),
         "isd_lora_workspace_bytes": (SZ, [I32, I32, I32]),
@@ -152,7 +154,7 @@ def _call(name: str, *args) -> None:
 
 
 # argument index of seed_lo (seed_hi and step follow) in the calls that draw
-_DRAW_POS = {"isd_accept": 6, "isd_accept_commit": 6, "isd_propose": 4}
+_DRAW_POS = {"isd_accept": 6, "isd_accept_commit": 6, "isd_accept_commit_noalloc": 6, "isd_propose": 4}
 _M64 = 2**64 - 1
 
 
@@ -286,14 +288,38 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
                       accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new, v_new, k_pages,
                       v_pages, page_table, ctx_lens_in, ctx_lens_out, workspace, stream=None,
                       step_dev=None, q_norms=None, loop_mode=None) -> None:
-    """isd_accept followed by kv_commit of the accepted rows, in one call (loop_mode: a
-    re-proposing request of the decoding loop commits nothing)."""
+    """isd_accept followed by kv_commit of the accepted prefix, in one call (loop_mode: a
+    re-proposing request of the decoding loop commits its row N-1 instead)."""
+    _call("isd_accept_commit", *_accept_commit_args(
+        shape, p_logits, q_logits, proposals, req_ids, positions, seed, step, accept_len, out_tokens, n_out,
+        n_commit, logp_sel, logq_sel, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, ctx_lens_out,
+        step_dev, q_norms, loop_mode),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+
+
+def isd_accept_commit_noalloc(shape: Shape, p_logits, q_logits, proposals, req_ids, positions, seed,
+                              step: int, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new,
+                              v_new, k_pages, v_pages, page_table, ctx_lens_in, ctx_lens_out, flags=None,
+                              stream=None, step_dev=None, q_norms=None, loop_mode=None) -> None:
+    """isd_accept_commit with the library's own per-device scratch instead of a workspace;
+    ``flags``: one uint32 device word the kernels OR their flag bits into (or None)."""
+    _call("isd_accept_commit_noalloc", *_accept_commit_args(
+        shape, p_logits, q_logits, proposals, req_ids, positions, seed, step, accept_len, out_tokens, n_out,
+        n_commit, logp_sel, logq_sel, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, ctx_lens_out,
+        step_dev, q_norms, loop_mode),
+        None if flags is None else _ptr(flags, "flags", torch.int32, 1), _stream(stream))
+
+
+def _accept_commit_args(shape, p_logits, q_logits, proposals, req_ids, positions, seed, step, accept_len,
+                        out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new, v_new, k_pages, v_pages,
+                        page_table, ctx_lens_in, ctx_lens_out, step_dev, q_norms, loop_mode):
+    """The arguments isd_accept_commit and its no-allocation variant share, marshalled."""
     B, N, V = shape.batch, shape.stride_n, shape.vocab
     Q, Hkv, D = shape.q_rows, shape.n_kv_heads, shape.head_dim
     dt, kt = _tdtype(shape.logit_dtype), _tdtype(shape.kv_dtype)
     pool = shape.num_pages * Hkv * shape.page_size * D
     i32 = torch.int32
-    _call("isd_accept_commit",
+    return (
         ctypes.byref(shape.c()), _ptr(p_logits, "p_logits", dt, B * (N - 1) * V),
         _ptr(q_logits, "q_logits", dt, B * (N - 1) * V), _ptr(proposals, "proposals", i32, B * N),
         _ptr(req_ids, "req_ids", i32, B), _ptr(positions, "positions", i32, B),
@@ -308,8 +334,7 @@ def isd_accept_commit(shape: Shape, p_logits, q_logits, proposals, req_ids, posi
         _ptr(k_pages, "k_pages", kt, pool), _ptr(v_pages, "v_pages", kt, pool),
         _ptr(page_table, "page_table", i32, B * shape.max_pages),
         _ptr(ctx_lens_in, "ctx_lens_in", i32, B), _ptr(ctx_lens_out, "ctx_lens_out", i32, B),
-        None if loop_mode is None else _ptr(loop_mode, "loop_mode", i32, B),
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+        None if loop_mode is None else _ptr(loop_mode, "loop_mode", i32, B))
 
 
 def isd_propose(shape: Shape, mask_logits, req_ids, positions, seed, step: int, mode: int,

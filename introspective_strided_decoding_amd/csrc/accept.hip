@@ -819,7 +819,7 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
                     const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
                     uint64_t seed_lo, uint64_t seed_hi, uint32_t step, const int64_t* step_dev,
                     const float* q_norms, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out, int32_t* n_commit,
-                    float* logp_sel, float* logq_sel, char* ws, const WsLayout& L,
+                    float* logp_sel, float* logq_sel, char* ws, const WsLayout& L, uint32_t* flags,
                     const CommitArgs* commit, hipStream_t stream) {
   const T* P = static_cast<const T*>(pl);
   const T* Qp = static_cast<const T*>(ql);
@@ -851,7 +851,7 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.jobs = jobs;
   a.rej_count = rej_count;
   a.gath = reinterpret_cast<float*>(ws + L.gath);
-  a.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+  a.flags = flags;
   hipLaunchKernelGGL((lse_partial<T>), dim3((q_norms ? 1 : 2) * (N - 1) * p.shards, B), dim3(kThreads), 0, stream,
                      a, p.shard_len, part);
   hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
@@ -873,14 +873,14 @@ hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_
                          const int32_t* positions, uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
                          const int64_t* step_dev, const float* q_norms, int32_t* accept_len, int32_t* out_tokens,
                          int32_t* n_out, int32_t* n_commit, float* logp_sel, float* logq_sel, char* ws,
-                         const WsLayout& L, const CommitArgs* commit, hipStream_t stream) {
+                         const WsLayout& L, uint32_t* flags, const CommitArgs* commit, hipStream_t stream) {
   if (s.logit_dtype == ISD_BF16)
     return launch_t<uint16_t>(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi,
                               step, step_dev, q_norms, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel,
-                              ws, L, commit, stream);
+                              ws, L, flags, commit, stream);
   return launch_t<float>(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi, step,
-                         step_dev, q_norms, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L, commit,
-                         stream);
+                         step_dev, q_norms, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws, L, flags,
+                         commit, stream);
 }
 
 }  // namespace isd

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "isd.h"
 #include "isd_internal.hpp"
@@ -62,6 +63,101 @@ isd_status check_ws(const isd_shape* s, const void* ws, size_t bytes) {
   if (!aligned16(ws)) return ISD_ERR_ALIGNMENT;
   if (bytes < ws_layout(*s).total) return ISD_ERR_WORKSPACE;
   return ISD_OK;
+}
+
+// ---- the scratch of isd_accept_commit_noalloc ----
+// One array per device, owned by the library for the life of the process.
+// Its first kScratchZeroBytes hold the header and the per-request counters
+// (cleared once per device at set-up; the kernels rewind every counter they
+// use); the partials follow.  In host code `scratch` names a host-side stand-in:
+// the device address comes from hipGetSymbolAddress, per device.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchZeroBytes = size_t(1) << 20;
+static_assert(kHeaderBytes + 65535 * 4 <= kScratchZeroBytes, "per-request counters fit the cleared region");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+char* g_scratch[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's scratch address; the first call on a device resolves it
+// and clears the counter region on `stream`.
+hipError_t device_scratch(char** out, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [&] {
+    void* p = nullptr;
+    hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r == hipSuccess) r = launch_workspace_init(p, kScratchZeroBytes, stream);
+    g_scratch[dev] = (r == hipSuccess) ? static_cast<char*>(p) : nullptr;
+    g_scratch_err[dev] = r;
+  });
+  if (!g_scratch[dev]) return g_scratch_err[dev] != hipSuccess ? g_scratch_err[dev] : hipErrorNotInitialized;
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+// Regions of isd_accept + commit inside the scratch: counters in the cleared
+// region (the list count at header offset kRejCountOffset, the commit's
+// per-request arrivals after the header), partials after it.  The flag word is
+// the caller's.
+WsLayout scratch_layout(const isd_shape& s) {
+  WsLayout L;
+  const AcceptPlan c = plan_accept(s);
+  L.cmt_cnt = kHeaderBytes;
+  L.zero_end = kScratchZeroBytes;
+  size_t off = kScratchZeroBytes;
+  L.lse = off;
+  off = align_up(off + (size_t)c.rows * c.shards * 8, 256);
+  L.jobs = off;
+  off = align_up(off + (size_t)s.batch * sizeof(ReqState), 256);
+  L.gath = off;
+  off = align_up(off + (size_t)c.rows * 4, 256);
+  L.resid = off;
+  off = align_up(off + (size_t)s.batch * c.r_shards * sizeof(ResidShard), 256);
+  L.total = off;
+  return L;
+}
+
+// Checks of isd_accept_commit's arguments other than the workspace.
+isd_status check_accept_commit(const isd_shape* shape, const void* p_logits, const void* q_logits,
+                               const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
+                               const float* q_norms, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
+                               int32_t* n_commit, float* logp_sel, float* logq_sel, const void* k_new,
+                               const void* v_new, void* k_pages, void* v_pages, const int32_t* page_table,
+                               const int32_t* ctx_lens_in, int32_t* ctx_lens_out) {
+  isd_status st = check_shape(shape);
+  if (st != ISD_OK) return st;
+  if (!p_logits || !q_logits || !proposals || !req_ids || !positions || !accept_len || !out_tokens ||
+      !n_out || !n_commit || !logp_sel || !logq_sel || !k_new || !v_new || !k_pages || !v_pages ||
+      !page_table || !ctx_lens_in || !ctx_lens_out)
+    return ISD_ERR_NULL;
+  if (!aligned16(p_logits) || !aligned16(q_logits) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned16(k_pages) || !aligned8(q_norms))
+    return ISD_ERR_ALIGNMENT;
+  if (shape->batch > 65535) return ISD_ERR_UNSUPPORTED;
+  if (shape->vocab > 2048 * 1024) return ISD_ERR_UNSUPPORTED;
+  return ISD_OK;
+}
+
+// isd_accept_commit on validated arguments, its partials at `ws` laid out by `L`.
+hipError_t run_accept_commit(const isd_shape& s, const void* p_logits, const void* q_logits,
+                             const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
+                             uint64_t seed_lo, uint64_t seed_hi, uint32_t step, const int64_t* step_per_request,
+                             const float* q_norms, int32_t* accept_len, int32_t* out_tokens, int32_t* n_out,
+                             int32_t* n_commit, float* logp_sel, float* logq_sel, const void* k_new,
+                             const void* v_new, void* k_pages, void* v_pages, const int32_t* page_table,
+                             const int32_t* ctx_lens_in, int32_t* ctx_lens_out, const int32_t* loop_mode,
+                             char* ws, const WsLayout& L, uint32_t* flags, hipStream_t stream) {
+  const AcceptPlan p = plan_accept(s);
+  const CommitArgs c = commit_args(s, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
+                                   ctx_lens_out, flags, reinterpret_cast<uint32_t*>(ws + L.cmt_cnt), loop_mode);
+  return launch_accept(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi, step,
+                       step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws,
+                       L, flags, &c, stream);
 }
 
 }  // namespace
@@ -160,7 +256,7 @@ using namespace isd;
 
 extern "C" {
 
-int32_t isd_abi_version(void) { return 9; }
+int32_t isd_abi_version(void) { return 10; }
 
 const char* isd_status_string(isd_status status) {
   switch (status) {
@@ -241,9 +337,11 @@ isd_status isd_accept(const isd_shape* shape, const void* p_logits, const void* 
   if (st != ISD_OK) return st;
   const AcceptPlan p = plan_accept(*shape);
   const WsLayout L = ws_layout(*shape);
+  char* ws = static_cast<char*>(workspace);
   hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
                                seed_hi, step, step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit,
-                               logp_sel, logq_sel, static_cast<char*>(workspace), L, nullptr, stream);
+                               logp_sel, logq_sel, ws, L, reinterpret_cast<uint32_t*>(ws + L.flags), nullptr,
+                               stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept");
 }
 
@@ -256,29 +354,50 @@ isd_status isd_accept_commit(const isd_shape* shape, const void* p_logits, const
                              void* v_pages, const int32_t* page_table, const int32_t* ctx_lens_in,
                              int32_t* ctx_lens_out, const int32_t* loop_mode, void* workspace, size_t ws_bytes,
                              hipStream_t stream) {
-  isd_status st = check_shape(shape);
+  isd_status st = check_accept_commit(shape, p_logits, q_logits, proposals, req_ids, positions, q_norms,
+                                      accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new, v_new,
+                                      k_pages, v_pages, page_table, ctx_lens_in, ctx_lens_out);
   if (st != ISD_OK) return st;
-  if (!p_logits || !q_logits || !proposals || !req_ids || !positions || !accept_len || !out_tokens ||
-      !n_out || !n_commit || !logp_sel || !logq_sel || !k_new || !v_new || !k_pages || !v_pages ||
-      !page_table || !ctx_lens_in || !ctx_lens_out)
-    return ISD_ERR_NULL;
-  if (!aligned16(p_logits) || !aligned16(q_logits) || !aligned16(k_new) || !aligned16(v_new) ||
-      !aligned16(k_pages) || !aligned8(q_norms))
-    return ISD_ERR_ALIGNMENT;
-  if (shape->batch > 65535) return ISD_ERR_UNSUPPORTED;
-  if (shape->vocab > 2048 * 1024) return ISD_ERR_UNSUPPORTED;
   st = check_ws(shape, workspace, ws_bytes);
   if (st != ISD_OK) return st;
-  const AcceptPlan p = plan_accept(*shape);
   const WsLayout L = ws_layout(*shape);
   char* ws = static_cast<char*>(workspace);
-  const CommitArgs c = commit_args(*shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
-                                   ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
-                                   reinterpret_cast<uint32_t*>(ws + L.cmt_cnt), loop_mode);
-  hipError_t e = launch_accept(*shape, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo,
-                               seed_hi, step, step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit,
-                               logp_sel, logq_sel, ws, L, &c, stream);
+  hipError_t e = run_accept_commit(*shape, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi,
+                                   step, step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit,
+                                   logp_sel, logq_sel, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in,
+                                   ctx_lens_out, loop_mode, ws, L, reinterpret_cast<uint32_t*>(ws + L.flags),
+                                   stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept_commit");
+}
+
+isd_status isd_accept_commit_noalloc(const isd_shape* shape, const void* p_logits, const void* q_logits,
+                                     const int32_t* proposals, const int32_t* req_ids, const int32_t* positions,
+                                     uint64_t seed_lo, uint64_t seed_hi, uint32_t step,
+                                     const int64_t* step_per_request, const float* q_norms, int32_t* accept_len,
+                                     int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
+                                     float* logq_sel, const void* k_new, const void* v_new, void* k_pages,
+                                     void* v_pages, const int32_t* page_table, const int32_t* ctx_lens_in,
+                                     int32_t* ctx_lens_out, const int32_t* loop_mode, uint32_t* flags,
+                                     hipStream_t stream) {
+  isd_status st = check_accept_commit(shape, p_logits, q_logits, proposals, req_ids, positions, q_norms,
+                                      accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, k_new, v_new,
+                                      k_pages, v_pages, page_table, ctx_lens_in, ctx_lens_out);
+  if (st != ISD_OK) return st;
+  const WsLayout L = scratch_layout(*shape);
+  if (L.total > kScratchBytes) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "isd_accept_commit_noalloc: this shape needs %zu bytes of scratch, the library holds %zu",
+                  L.total, kScratchBytes);
+    return ISD_ERR_WORKSPACE;
+  }
+  char* ws = nullptr;
+  hipError_t e = device_scratch(&ws, stream);
+  if (e == hipSuccess)
+    e = run_accept_commit(*shape, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi, step,
+                          step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel,
+                          k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, ctx_lens_out, loop_mode, ws, L,
+                          flags, stream);
+  return e == hipSuccess ? ISD_OK : hip_fail(e, "isd_accept_commit_noalloc");
 }
 
 isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_new, void* k_pages,

@@ -112,7 +112,7 @@ struct CommitArgs {
   int32_t* ctx_out;
   uint32_t* flags;
   uint32_t* arrivals;     // per request, rewound by the last arrival
-  const int32_t* loop_mode;   // per request (NULL: none): a re-proposing request commits nothing
+  const int32_t* loop_mode;   // per request (NULL: none): a re-proposing request commits its row N-1
   int N, Hkv, D, max_pages, num_pages;
   int kv_bf16;            // 1: bf16 pages, 0: fp32
 };
@@ -134,7 +134,7 @@ hipError_t launch_accept(const isd_shape& s, const AcceptPlan& p, const void* p_
                          uint32_t step, const int64_t* step_dev, const float* q_norms, int32_t* accept_len,
                          int32_t* out_tokens, int32_t* n_out, int32_t* n_commit, float* logp_sel,
                          float* logq_sel, char* ws,
-                         const WsLayout& L, const CommitArgs* commit, hipStream_t stream);
+                         const WsLayout& L, uint32_t* flags, const CommitArgs* commit, hipStream_t stream);
 
 hipError_t launch_commit(const isd_shape& s, const CommitArgs& c, hipStream_t stream);
 

@@ -32,7 +32,7 @@ def test_header_and_library_agree():
 
 
 def test_abi_version_and_status_strings():
-    assert LIB.isd_abi_version() == 9
+    assert LIB.isd_abi_version() == 10
     for code in range(8):
         assert LIB.isd_status_string(code)
     assert LIB.isd_status_string(99) == b"unknown status"
@@ -140,6 +140,31 @@ def test_accept_and_commit_validation():
         bad = list(fargs)
         bad[-2] = 8
         assert LIB.isd_accept_commit(ctypes.byref(big.c()), *bad) == want, v
+
+
+def test_accept_commit_noalloc_validation():
+    """The no-allocation variant takes isd_accept_commit's arguments without the workspace,
+    plus a flag word (NULL allowed), and refuses before any launch what does not fit the
+    library's 16 MiB scratch."""
+    s = _shape()
+    # the accept arguments, then k_new .. ctx_lens_out, loop_mode, flags, stream
+    gargs = [FAKE] * 5 + [1, 2, 3, None, None] + [FAKE] * 6 + [FAKE] * 7 + [None, None, None]
+    assert len(gargs) == 26
+    for i in (2, 16, 20, 22):       # proposals, k_new, page_table, ctx_lens_out
+        bad = list(gargs)
+        bad[i] = None
+        assert LIB.isd_accept_commit_noalloc(ctypes.byref(s.c()), *bad) == 1, i
+    for i in (0, 16, 17, 18, 9):    # p_logits, k_new, v_new, k_pages, q_norms
+        bad = list(gargs)
+        bad[i] = ctypes.c_void_p(0x10004)
+        assert LIB.isd_accept_commit_noalloc(ctypes.byref(s.c()), *bad) == 7, i
+    assert LIB.isd_accept_commit_noalloc(None, *gargs) == 1
+    assert LIB.isd_accept_commit_noalloc(ctypes.byref(_shape(stride_n=1).c()), *gargs) == 2
+    # residual partials: batch * ceil(V / 2048) * 176 bytes must fit beside the counters
+    too_big = _shape(batch=2048, vocab=151936, max_pages=16, num_pages=32768)     # 27 MB of partials
+    assert LIB.isd_accept_commit_noalloc(ctypes.byref(too_big.c()), *gargs) == 4
+    assert b"scratch" in LIB.isd_last_error()
+    assert LIB.isd_accept_commit_noalloc(ctypes.byref(_shape(vocab=2048 * 1024 + 1).c()), *gargs) == 5
 
 
 def test_propose_validation():
