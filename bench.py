@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 MALL_BYTES = 256 * 2 ** 20
+SAMPLE_FIRST, SAMPLE_EVERY = 5, 10   # timed steps whose calls are bracketed by HIP events
 
 
 def measured_traffic(cfg_name):
@@ -75,10 +76,10 @@ def algorithmic_bytes(wl):
     return {"attention": attn, "accept": accept}
 
 
-def commit_bytes(wl, n_commit):
+def commit_bytes(wl, rows):
+    """KV rows committed (read from the stride, written to the pages), plus lengths and counts."""
     cfg = wl.cfg
-    rows = int(n_commit.sum())
-    return rows * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes * 2 * 2 + cfg.batch * 12
+    return int(round(rows * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes * 2 * 2)) + cfg.batch * 12
 
 
 def lora_bytes(cfg):
@@ -87,48 +88,76 @@ def lora_bytes(cfg):
     return (m * d + d * r + r * d + 2 * m * d) * 2 + m * 4
 
 
+def lora_report(cfg, ms):
+    """isd_lora_delta: time per call, its flops against the bf16 matrix-core peak and its bytes
+    against HBM (the rank-128 delta is HBM-bound: about 73 flop per byte)."""
+    d, r = cfg.lora_dim, cfg.lora_rank
+    m = cfg.batch * cfg.stride_n
+    flops = 2 * m * d * r * 2
+    by = lora_bytes(cfg)
+    return {"what": "isd_lora_delta: rank-128 adapter on the MASK rows of a 4096 -> 4096 projection",
+            "gated_rows": m, "avg_call_ms": round(ms, 5), "flops": int(flops), "bytes": int(by),
+            "tflops": round(flops / ms / 1e9, 2), "mfma_frac": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "achieved_GBs": round(by / ms / 1e6, 1), "hbm_frac": round(by / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def propose_bytes(cfg):
     """MASK-row logits read once, proposals written once."""
     return cfg.batch * cfg.stride_n * (cfg.vocab * cfg.elem_bytes + 4)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s: float = 10.0, max_steps: int = 8):
     """Time the float64 oracle on the host: whole steps (attention for every request, accept,
-    commit) of the same workload, repeated until about ``budget_s`` seconds have passed."""
+    commit) of the same workload, repeated until about ``budget_s`` seconds have passed, with
+    the BLAS threads pinned to the CPUs this process may run on."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle.accept import isd_accept as o_accept
     from oracle.attention import stride_attention
     from oracle.commit import kv_commit as o_commit
 
     cfg = wl.cfg
-    t_start = time.perf_counter()
-    steps_done = 0
-    accepted = 0
-    while steps_done < max_steps:
-        stride_attention(wl.q, wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, wl.page_table,
-                         wl.ctx_lens, cfg.page_size)
-        res = o_accept(wl.p_logits, wl.q_logits, wl.proposals, wl.req_ids, wl.positions,
-                       wl.philox_seed, wl.step)
-        n_commit = np.array([o.n_commit for o in res])
-        o_commit(wl.k_pool, wl.v_pool, wl.page_table, wl.ctx_lens, wl.k_new, wl.v_new, n_commit,
-                 cfg.page_size)
-        accepted += sum(o.accept_len for o in res)
-        steps_done += 1
-        if time.perf_counter() - t_start > budget_s:
-            break
-    elapsed = time.perf_counter() - t_start
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    host_cpus = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=host_cpus):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t_start = time.perf_counter()
+        steps_done = 0
+        accepted = 0
+        while steps_done < max_steps:
+            stride_attention(wl.q, wl.k_new, wl.v_new, wl.k_pool, wl.v_pool, wl.page_table,
+                             wl.ctx_lens, cfg.page_size)
+            res = o_accept(wl.p_logits, wl.q_logits, wl.proposals, wl.req_ids, wl.positions,
+                           wl.philox_seed, wl.step + steps_done)
+            n_commit = np.array([o.n_commit for o in res])
+            o_commit(wl.k_pool, wl.v_pool, wl.page_table, wl.ctx_lens, wl.k_new, wl.v_new, n_commit,
+                     cfg.page_size)
+            accepted += sum(o.accept_len for o in res)
+            steps_done += 1
+            if time.perf_counter() - t_start > budget_s:
+                break
+        elapsed = time.perf_counter() - t_start
     return {
         "value": round(steps_done / elapsed, 4),
         "unit": "verify-steps/s",
         "accepted_tokens_per_s": round(accepted / elapsed, 2),
         "cores": int(threads),
-        "host_cpus": len(os.sched_getaffinity(0)),
+        "host_cpus": host_cpus,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{steps_done} whole steps of the {cfg.name} workload (float64 attention for "
-                   f"every request, accept with residual, commit)"),
+                   f"every request, accept with residual, commit), BLAS threads pinned to the "
+                   f"{host_cpus} CPUs of this process"),
         "seconds": round(elapsed, 2),
     }
 
@@ -276,15 +305,20 @@ def main(argv=None):
 
     stream = torch.cuda.current_stream()
 
-    def one_step(st, ev=None):
+    def one_step(st, step, ev=None):
+        """One verify step; ``ev``: events around its calls (attention, accept + commit, LoRA)."""
         if ev is not None:
             ev[0].record(stream)
         st.attention()
         if ev is not None:
             ev[1].record(stream)
-        st.accept_commit()
+        st.accept_commit(step=step)
+        if ev is not None:
+            ev[2].record(stream)
         if use_lora:
             st.lora_delta()
+            if ev is not None:
+                ev[3].record(stream)
 
     if args.calibrate_copy:
         src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
@@ -294,25 +328,49 @@ def main(argv=None):
         del src, dst
 
     for i in range(args.warmup):
-        one_step(steps[i % sets])
+        one_step(steps[i % sets], wl.step + i)
     torch.cuda.synchronize()
 
-    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+    # Every timed step draws with its own Philox step.  HIP events bracket the calls of
+    # every EVERY-th step only (an event costs the stream about 2 us), so the per-kernel
+    # figures are measured live in the timed region while the step rate is not skewed.
+    sampled = {i for i in range(SAMPLE_FIRST, args.steps, SAMPLE_EVERY)} or {0}
+    events = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for i in sampled}
+    span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    t_base = wl.step + args.warmup
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    span[0].record(stream)
     for i in range(args.steps):
-        one_step(steps[i % sets], events[i])
+        one_step(steps[i % sets], t_base + i, events.get(i))
+    span[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    attn_each = np.array([e[0].elapsed_time(e[1]) for e in events])
-    # a step's duration: from its first event to the next step's (no extra event in the loop)
-    step_each = np.array([a[0].elapsed_time(b[0]) for a, b in zip(events[:-1], events[1:])])
+    attn_each = np.array([e[0].elapsed_time(e[1]) for e in events.values()])
+    accept_each = np.array([e[1].elapsed_time(e[2]) for e in events.values()])
+    lora_each = np.array([e[2].elapsed_time(e[3]) for e in events.values()]) if use_lora else None
     attn_ms = float(np.mean(attn_each))
+    accept_ms = float(np.mean(accept_each))
     pct = lambda x: {"p10": round(float(np.percentile(x, 10)), 5), "p50": round(float(np.percentile(x, 50)), 5),
                      "p90": round(float(np.percentile(x, 90)), 5)}
     ms_per_step = elapsed * 1e3 / args.steps
     steps_per_s = args.steps / elapsed
+    gpu_ms_per_step = span[0].elapsed_time(span[1]) / args.steps
+
+    # the timed steps' draws again, untimed: accepted / committed tokens and committed rows
+    # averaged over every timed step (inputs are unchanged between steps, so step i draws
+    # exactly what it drew in the timed loop)
+    acc_tot, out_tot, cm_tot = (torch.zeros((), dtype=torch.int64, device=dev) for _ in range(3))
+    for i in range(args.steps):
+        st = steps[i % sets]
+        st.accept(step=t_base + i)
+        acc_tot += st.accept_len.sum()
+        out_tot += st.n_out.sum()
+        cm_tot += st.n_commit.sum()
+    accepted_per_step = float(acc_tot.item()) / args.steps
+    committed_per_step = float(out_tot.item()) / args.steps
+    committed_rows_per_step = float(cm_tot.item()) / args.steps
 
     # the same steps replayed from HIP graphs (one recorded step per input set)
     graph = None
@@ -346,7 +404,7 @@ def main(argv=None):
             for st in steps:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
-                    one_step(st)
+                    one_step(st, wl.step)
                 vgraphs.append(g)
             for i in range(args.warmup):
                 vgraphs[i % sets].replay()
@@ -442,12 +500,9 @@ def main(argv=None):
         r_isd["attention_ms"] = round(attn_ms, 5)
         r_isd["alpha_with_attention"] = round((attn_ms + r_isd["gated"]["ms"]) / (attn_ms + r_isd["base"]["ms"]), 4)
 
-    # accepted / committed tokens of the timed steps (identical draws per set)
-    acc = [int(st.accept_len.sum().item()) for st in steps]
-    ncommit = steps[0].n_commit.cpu().numpy()
-    accepted_per_step = float(np.mean(acc))
-    committed_per_step = float(np.mean([int(st.n_out.sum().item()) for st in steps]))
-    total_bytes = step_bytes + commit_bytes(wl, ncommit) + (lora_bytes(cfg) if use_lora else 0)
+    c_bytes = commit_bytes(wl, committed_rows_per_step)
+    total_bytes = step_bytes + c_bytes + (lora_bytes(cfg) if use_lora else 0)
+    accept_bytes = nbytes["accept"] + c_bytes
 
     out = {
         "metric": "ISD verify-steps/s + accepted tokens/s at concurrency 32, N=4; % HBM peak",
@@ -470,8 +525,10 @@ def main(argv=None):
         "accepted_tokens_per_s": round(accepted_per_step * steps_per_s, 1),
         "committed_tokens_per_s": round(committed_per_step * steps_per_s, 1),
         "request_steps_per_s": round(cfg.batch * steps_per_s, 1),
-        "accepted_per_step": accepted_per_step,
-        "event_ms": {"step": pct(step_each), "attention": pct(attn_each)},
+        "accepted_per_step": round(accepted_per_step, 3),
+        "committed_per_step": round(committed_per_step, 3),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 5),
+        "event_ms": {"samples": len(events), "attention": pct(attn_each), "accept_commit": pct(accept_each)},
         "step_hbm": {"bytes": int(total_bytes), "achieved_GBs": round(total_bytes / ms_per_step / 1e6, 1),
                      "frac": round(total_bytes / ms_per_step / 1e6 / HBM_PEAK_GBS, 4)},
         "roofline": {
@@ -485,6 +542,16 @@ def main(argv=None):
             "bytes_per_launch": int(nbytes["attention"]),
             "avg_launch_ms": round(attn_ms, 5),
         },
+        "accept": {
+            "what": "isd_accept_commit: row normalisers and decision, residual pass with the KV commit, "
+                    "residual selection (three launches)",
+            "bound": "hbm",
+            "bytes_per_call": int(accept_bytes),
+            "avg_call_ms": round(accept_ms, 5),
+            "achieved_GBs": round(accept_bytes / accept_ms / 1e6, 1),
+            "frac": round(accept_bytes / accept_ms / 1e6 / HBM_PEAK_GBS, 4),
+        },
+        "lora": None if lora_each is None else lora_report(cfg, float(np.mean(lora_each))),
         "propose": prop,
         "graph": graph,
         "loop": loop,

@@ -114,8 +114,8 @@ typedef struct isd_shape {
   int32_t num_pages;    /* pages in the pool */
   int32_t vocab;        /* V */
   int32_t max_ctx;      /* hint, see above */
-  isd_dtype kv_dtype;   /* q, k_new, v_new, pages, out */
-  isd_dtype logit_dtype;/* p_logits, q_logits */
+  int32_t kv_dtype;     /* an isd_dtype: q, k_new, v_new, pages, out */
+  int32_t logit_dtype;  /* an isd_dtype: p_logits, q_logits */
 } isd_shape;
 
 /*
@@ -558,8 +558,10 @@ isd_status isd_gated_linear_group(int32_t n_proj, int32_t rows, int32_t d_in, co
                                   const void* const* B_t, const int32_t* mask_rows, int32_t n_mask, float scale,
                                   void* const* Y, void* workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Text for a status code (static storage). */
-const char* isd_status_string(isd_status status);
+/* Text for a status code (static storage); `status` is an isd_status value,
+ * taken as a plain integer so that any code a caller holds, valid or not, is
+ * safe to pass (one outside the enumeration gives "unknown status"). */
+const char* isd_status_string(int32_t status);
 
 /* Text of the last ISD_ERR_HIP on the calling thread ("" if none). */
 const char* isd_last_error(void);

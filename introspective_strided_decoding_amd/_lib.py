@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libisd.so")
+# ISD_LIBRARY may name another build of the library (the host-sanitizer build the ABI
+# tests run against); the default is the in-tree libisd.so.
+LIB_PATH = os.environ.get("ISD_LIBRARY") or os.path.join(_PKG, "libisd.so")
 
 ISD_F32, ISD_BF16 = 0, 1
 FLAG_CTX_RANGE, FLAG_PAGE_RANGE, FLAG_TOKEN_RANGE, FLAG_COMMIT_RANGE, FLAG_ROW_RANGE = 1, 2, 4, 8, 16

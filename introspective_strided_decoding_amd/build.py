@@ -41,9 +41,9 @@ def _flags():
             "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + _flags() + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,23 +56,32 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host code instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+# (device code is built as usual): each -fsanitize= applies to the host pass only.
+HOST_SANITIZERS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def build(verbose: bool = False, out: str = LIB, extra=(), link_extra=()) -> str:
+    """Compile every source and link ``out``; ``extra`` is added to every compile line and
+    ``link_extra`` to the link line (HOST_SANITIZERS for the sanitizer build)."""
+    build_dir = BUILD if out == LIB else os.path.join(BUILD, os.path.basename(os.path.dirname(out)) or "alt")
+    os.makedirs(build_dir, exist_ok=True)
     srcs = list(SOURCES)
     missing = [s for s in srcs if not os.path.exists(os.path.join(CSRC, s))]
     if missing:
         raise RuntimeError(f"missing sources: {missing}")
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), srcs))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + list(link_extra) + ["-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

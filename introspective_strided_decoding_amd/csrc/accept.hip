@@ -10,7 +10,10 @@
 //                  partials of the request's rows into log-normalisers while
 //                  the first wave loads the recorded logits at the proposals;
 //                  rho = exp(log p - log q), Philox uniforms, accept iff
-//                  u < rho, first rejection by a wave ballot.
+//                  u < rho, first rejection by a wave ballot; a rejecting
+//                  request appends its record to a compact list.  (A last-arrival hand-off
+//                  inside the normaliser launch measured slower: its 60-odd
+//                  arrivals per request counter serialise.)
 //   resid_pass     rejecting requests only, one pass over the rejected p
 //                  and q rows, sharded finely over the vocabulary: fp64 sums
 //                  of e_p = exp(l_p - max p) and e_q = exp(l_q - max q) (the
@@ -20,7 +23,9 @@
 //   resid_select   per rejecting request: exact shard masses from those
 //                  pieces, a prefix over them picks the shard holding
 //                  u' * S, a workgroup scan inside that shard in vocabulary
-//                  order picks y*.
+//                  order picks y*.  With a commit, one more workgroup per
+//                  request writes its accepted rows to the KV pages beside the
+//                  selections.
 // The residual runs in fp64 so the inverse CDF agrees with a float64
 // reference up to rounding of the running sums.  The decision lists the
 // rejecting requests compactly (an atomic counter the normaliser kernel
@@ -37,7 +42,7 @@ namespace isd {
 namespace {
 
 constexpr int kThreads = 256;
-static_assert(kThreads == kCommitThreads, "commit workgroups run inside the residual pass launch");
+static_assert(kThreads == kCommitThreads, "commit workgroups run inside the selection launch");
 
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> { static constexpr int N = 8; };
@@ -84,117 +89,6 @@ struct DecideArgs {
 // A shard holds at most kThreads * kLseVec vectors, so every thread issues all
 // of its 16-byte loads before it waits on any of them.
 constexpr int kLseVec = 8;
-
-// Grid (2(N-1) * shards, B): workgroup (jj * shards + sh, r) reduces shard sh
-// of row jj of request r, where rows jj < N-1 are p rows and the rest q rows;
-// its partial lands at part[(r * 2(N-1) + jj) * shards + sh].
-template <typename T>
-__global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int shard_len,
-                                                        float2* __restrict__ part) {
-  constexpr int VN = Vec<T>::N;
-  const int V = args.V, shards = args.shards, R = args.N - 1;
-  const int r = blockIdx.y;
-  const int jj = blockIdx.x / shards, sh = blockIdx.x % shards;
-  const bool is_q = jj >= R;
-  const size_t row_off = (size_t(r) * R + (is_q ? jj - R : jj)) * V;
-  const T* base = (is_q ? args.q_logits : args.p_logits) + row_off;
-  const int e0 = sh * shard_len;
-  const int e1 = min(V, e0 + shard_len);
-  // the proposal this row tests (x_{j+2} for p row and q row j)
-  const int xg = args.proposals[size_t(r) * args.N + (is_q ? jj - R : jj) + 1];
-  float xv = 0.f;
-  bool has_x = false;
-  float m = -INFINITY, s = 0.f;
-  if (e0 < e1) {
-    // scalar head up to 16-byte alignment of the absolute element index, vector body, scalar tail
-    const int head = int((VN - ((row_off + e0) % VN)) % VN);
-    const int hb = min(e1, e0 + head);
-    const int nvec = (e1 - hb) / VN;
-    const int tb = hb + nvec * VN;
-    const u32x4* vb = reinterpret_cast<const u32x4*>(base + hb);
-    u32x4 raw[kLseVec];
-#pragma unroll
-    for (int k = 0; k < kLseVec; ++k) {
-      const int v = threadIdx.x + k * kThreads;
-      raw[k] = (v < nvec) ? __builtin_nontemporal_load(vb + v) : u32x4{0, 0, 0, 0};
-    }
-    float tail = -INFINITY;
-    bool has_tail = false;
-    for (int e = e0 + threadIdx.x; e < hb; e += kThreads) {
-      const float v = to_f32<T>(base[e]);
-      tail = fmaxf(tail, v);
-      has_tail = true;
-      if (e == xg) { xv = v; has_x = true; }
-    }
-    for (int e = tb + threadIdx.x; e < e1; e += kThreads) {
-      const float v = to_f32<T>(base[e]);
-      tail = fmaxf(tail, v);
-      has_tail = true;
-      if (e == xg) { xv = v; has_x = true; }
-    }
-    // the logit at the proposal, from the registers of the thread that holds it
-    if (xg >= hb && xg < tb && (xg - hb) / VN % kThreads == int(threadIdx.x)) {
-      const int kx = (xg - hb) / VN / kThreads, ix = (xg - hb) % VN;
-#pragma unroll
-      for (int k = 0; k < kLseVec; ++k)
-        if (k == kx) {
-          float x[VN];
-          unpack(raw[k], x, T());
-#pragma unroll
-          for (int i = 0; i < VN; ++i)
-            if (i == ix) xv = x[i];
-        }
-      has_x = true;
-    }
-    // pass 1: max over this thread's values (registers only)
-    float mx = tail;
-#pragma unroll
-    for (int k = 0; k < kLseVec; ++k) {
-      if (threadIdx.x + k * kThreads < nvec) {
-        float x[VN];
-        unpack(raw[k], x, T());
-#pragma unroll
-        for (int i = 0; i < VN; ++i) mx = fmaxf(mx, x[i]);
-      }
-    }
-    // pass 2: sum of exp(x - mx) in base 2
-    if (mx != -INFINITY) {
-      const float mb = mx * kLog2e;
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < kLseVec; ++k) {
-        if (threadIdx.x + k * kThreads < nvec) {
-          float x[VN];
-          unpack(raw[k], x, T());
-#pragma unroll
-          for (int i = 0; i < VN; ++i) acc += exp2f(fmaf(x[i], kLog2e, -mb));
-        }
-      }
-      if (has_tail) {
-        for (int e = e0 + threadIdx.x; e < hb; e += kThreads) acc += exp2f(fmaf(to_f32<T>(base[e]), kLog2e, -mb));
-        for (int e = tb + threadIdx.x; e < e1; e += kThreads) acc += exp2f(fmaf(to_f32<T>(base[e]), kLog2e, -mb));
-      }
-      m = mx;
-      s = acc;
-    }
-  }
-  // wave reduce of (m, s)
-  const float wm = wave_max(m);
-  float ws = (m == -INFINITY) ? 0.f : s * exp2f((m - wm) * kLog2e);
-  ws = wave_sum(ws);
-  __shared__ float sm[kThreads / 64][2];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { sm[wave][0] = wm; sm[wave][1] = ws; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = -INFINITY, S = 0.f;
-    for (int w = 0; w < kThreads / 64; ++w) ms_merge(M, S, sm[w][0], sm[w][1]);
-    part[(size_t(r) * 2 * R + jj) * shards + sh] = make_float2(M, S);
-    // the decision kernel, next in the stream, lists rejecting requests from zero
-    if (blockIdx.x == 0 && blockIdx.y == 0) *args.rej_count = 0u;
-  }
-  if (has_x) args.gath[size_t(r) * 2 * R + jj] = xv;
-}
 
 // One workgroup per request.  Lane j < N-1 of wave 0 tests x_{j+2} against
 // p row j and q row j (their logits there were recorded by the normaliser
@@ -291,6 +185,124 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
       a.jobs[atomicAdd(a.rej_count, 1u)] = st;
     }
   }
+}
+
+// Grid (n_rows * shards, B), n_rows = 2(N-1) (p rows, then q rows) or N-1
+// (p rows only, when the q normalisers are carried): workgroup
+// (jj * shards + sh, r) reduces shard sh of row jj of request r; its partial
+// lands at part[(r * 2(N-1) + jj) * shards + sh].
+template <typename T>
+__global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int shard_len, float2* __restrict__ part) {
+  constexpr int VN = Vec<T>::N;
+  const int V = args.V, shards = args.shards, R = args.N - 1;
+  const int r = blockIdx.y;
+  const int jj = blockIdx.x / shards, sh = blockIdx.x % shards;
+  const bool is_q = jj >= R;
+  const size_t row_off = (size_t(r) * R + (is_q ? jj - R : jj)) * V;
+  const T* base = (is_q ? args.q_logits : args.p_logits) + row_off;
+  const int e0 = sh * shard_len;
+  const int e1 = min(V, e0 + shard_len);
+  // the proposal this row tests (x_{j+2} for p row and q row j)
+  const int xg = args.proposals[size_t(r) * args.N + (is_q ? jj - R : jj) + 1];
+  float xv = 0.f;
+  bool has_x = false;
+  float m = -INFINITY, s = 0.f;
+  if (e0 < e1) {
+    // scalar head up to 16-byte alignment of the absolute element index, vector body, scalar tail
+    const int head = int((VN - ((row_off + e0) % VN)) % VN);
+    const int hb = min(e1, e0 + head);
+    const int nvec = (e1 - hb) / VN;
+    const int tb = hb + nvec * VN;
+    const u32x4* vb = reinterpret_cast<const u32x4*>(base + hb);
+    u32x4 raw[kLseVec];
+    if (nvec > 0) {   // the same for the whole workgroup
+      // every load unconditional (indices clamped into the shard) and issued
+      // before any is used
+#pragma unroll
+      for (int k = 0; k < kLseVec; ++k)
+        raw[k] = __builtin_nontemporal_load(vb + min(int(threadIdx.x) + k * kThreads, nvec - 1));
+    }
+    // pass 1: max over this thread's values (registers, then the scalar head
+    // and tail: rows not 16-byte aligned, shard ends)
+    float mx = -INFINITY;
+    if (nvec > 0) {
+#pragma unroll
+      for (int k = 0; k < kLseVec; ++k) {
+        if (threadIdx.x + k * kThreads < nvec) {
+          float x[VN];
+          unpack(raw[k], x, T());
+#pragma unroll
+          for (int i = 0; i < VN; ++i) mx = fmaxf(mx, x[i]);
+        }
+      }
+    }
+    bool has_tail = false;
+    for (int e = e0 + threadIdx.x; e < hb; e += kThreads) {
+      const float x = to_f32<T>(base[e]);
+      mx = fmaxf(mx, x);
+      has_tail = true;
+      if (e == xg) { xv = x; has_x = true; }
+    }
+    for (int e = tb + threadIdx.x; e < e1; e += kThreads) {
+      const float x = to_f32<T>(base[e]);
+      mx = fmaxf(mx, x);
+      has_tail = true;
+      if (e == xg) { xv = x; has_x = true; }
+    }
+    // pass 2: sum of exp(x - mx) in base 2 (the exponentials, about a quarter of
+    // the VALU rate, are what this kernel spends beyond its streaming read)
+    if (mx != -INFINITY) {
+      const float mb = mx * kLog2e;
+      float acc = 0.f;
+      if (nvec > 0) {
+#pragma unroll
+        for (int k = 0; k < kLseVec; ++k) {
+          if (threadIdx.x + k * kThreads < nvec) {
+            float x[VN];
+            unpack(raw[k], x, T());
+#pragma unroll
+            for (int i = 0; i < VN; ++i) acc += exp2f(fmaf(x[i], kLog2e, -mb));
+          }
+        }
+      }
+      if (has_tail) {
+        for (int e = e0 + threadIdx.x; e < hb; e += kThreads) acc += exp2f(fmaf(to_f32<T>(base[e]), kLog2e, -mb));
+        for (int e = tb + threadIdx.x; e < e1; e += kThreads) acc += exp2f(fmaf(to_f32<T>(base[e]), kLog2e, -mb));
+      }
+      m = mx;
+      s = acc;
+    }
+    // the logit at the proposal, from the registers of the thread that holds it
+    if (nvec > 0 && xg >= hb && xg < tb && (xg - hb) / VN % kThreads == int(threadIdx.x)) {
+      const int kx = (xg - hb) / VN / kThreads, ix = (xg - hb) % VN;
+#pragma unroll
+      for (int k = 0; k < kLseVec; ++k)
+        if (k == kx) {
+          float x[VN];
+          unpack(raw[k], x, T());
+#pragma unroll
+          for (int i = 0; i < VN; ++i)
+            if (i == ix) xv = x[i];
+        }
+      has_x = true;
+    }
+  }
+  // wave reduce of (m, s)
+  const float wm = wave_max(m);
+  float ws = (m == -INFINITY) ? 0.f : s * exp2f((m - wm) * kLog2e);
+  ws = wave_sum(ws);
+  __shared__ float sm[kThreads / 64][2];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sm[wave][0] = wm; sm[wave][1] = ws; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = -INFINITY, S = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) ms_merge(M, S, sm[w][0], sm[w][1]);
+    part[(size_t(r) * 2 * R + jj) * shards + sh] = make_float2(M, S);
+    // the decision kernel, next in the stream, lists rejecting requests from zero
+    if (blockIdx.x == 0 && blockIdx.y == 0) *args.rej_count = 0u;
+  }
+  if (has_x) args.gath[size_t(r) * 2 * R + jj] = xv;
 }
 
 // ---- fp64 residual ----
@@ -406,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
                                                         const T* __restrict__ q_logits, int N, int V,
                                                         int r_shards, const ReqState* __restrict__ jobs,
                                                         const uint32_t* __restrict__ rej_count,
-                                                        ResidShard* __restrict__ shard_out, CommitArgs cm) {
+                                                        ResidShard* __restrict__ shard_out) {
   __shared__ double tab64[64];
   __shared__ double sm4[kThreads / 64][4];
   // entries near the boundary, listed as they are found (rare): exact logit
@@ -421,18 +433,8 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   __shared__ unsigned long long cls_bits[kResidAmb];
   __shared__ float shift_sm[2];
   __shared__ double sm2[kThreads / 64][2];
-  __shared__ int commit_last;
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
-  // columns past the residual shards (isd_accept_commit only): commit stride
-  // row sh - r_shards of request k while the residual work runs
-  if (sh >= r_shards) {
-    if (cm.kv_bf16)
-      commit_row<uint16_t>(cm, sh - r_shards, k, &commit_last);
-    else
-      commit_row<float>(cm, sh - r_shards, k, &commit_last);
-    return;
-  }
   const ReqState st = jobs[k];
   if (k >= int(*rej_count)) return;
   const size_t row = size_t(st.req) * (N - 1) + st.reject_row;
@@ -667,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
                                                           int r_shards, const ReqState* __restrict__ jobs,
                                                           const uint32_t* __restrict__ rej_count,
                                                           const ResidShard* __restrict__ shards_in,
-                                                          int32_t* __restrict__ out_tokens) {
+                                                          int32_t* __restrict__ out_tokens, int B, CommitArgs cm) {
   __shared__ double tab64[64];
   __shared__ double rmass[kMaxResidShards], pmass[kMaxResidShards];
   __shared__ int redo[kMaxResidShards];
@@ -678,6 +680,15 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   __shared__ int hit_sm[kThreads / 64], last_sm[kThreads / 64];
   __shared__ double wsum[kThreads / 64];
   __shared__ double sm2[kThreads / 64][2];
+  // workgroups past the first B (isd_accept_commit only): commit request
+  // blockIdx.x - B's accepted rows while the selections run
+  if (int(blockIdx.x) >= B) {
+    if (cm.kv_bf16)
+      commit_request<uint16_t>(cm, blockIdx.x - B);
+    else
+      commit_request<float>(cm, blockIdx.x - B);
+    return;
+  }
   const int k = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const ResidShard* recs = shards_in + size_t(k) * r_shards;
@@ -855,14 +866,13 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   hipLaunchKernelGGL((lse_partial<T>), dim3((q_norms ? 1 : 2) * (N - 1) * p.shards, B), dim3(kThreads), 0, stream,
                      a, p.shard_len, part);
   hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
-  // with a commit, N more columns of workgroups: one per (stride row 0..N-1, request)
+  hipLaunchKernelGGL((resid_pass<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards,
+                     jobs, rej_count, rshards);
+  // with a commit, B more workgroups in the selection launch: one per request
   CommitArgs cm{};
   if (commit) cm = *commit;
-  const int cols = p.r_shards + (commit ? N : 0);
-  hipLaunchKernelGGL((resid_pass<T>), dim3(cols, B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,
-                     rej_count, rshards, cm);
-  hipLaunchKernelGGL((resid_select<T>), dim3(B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards, jobs,
-                     rej_count, rshards, out_tokens);
+  hipLaunchKernelGGL((resid_select<T>), dim3(commit ? 2 * B : B), dim3(kThreads), 0, stream, P, Qp, N, V,
+                     p.r_shards, jobs, rej_count, rshards, out_tokens, B, cm);
   return hipGetLastError();
 }
 

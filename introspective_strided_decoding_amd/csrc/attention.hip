@@ -212,8 +212,12 @@ __device__ __forceinline__ void combine_rk(const T* __restrict__ q, const T* __r
   }
 }
 
-template <int D, int W, bool NT>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16(
+// RB = row blocks of 32 query columns per wave: 1 (two waves per SIMD, two
+// workgroups per CU), or 2 for groups of 33..64 query rows, where every wave
+// applies its key and value tiles to both blocks (so a tile crosses from L2
+// into the CU once) and takes a whole SIMD's registers.
+template <int D, int W, bool NT, int RB>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 3 - RB))) void attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out, int Qn, int Hq, int Hkv, int G,
@@ -223,8 +227,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     uint32_t* __restrict__ flags) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int RB = 1;          // row blocks of 32 columns per wave
-  constexpr int COLS = RB * 32;
+  constexpr int COLS = RB * 32;  // query columns of a workgroup
   constexpr int OSTR = D + 4;  // padded LDS row stride
   __shared__ float sm_m[W][COLS];
   __shared__ float sm_l[W][COLS];
@@ -770,7 +773,8 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
   float* po = reinterpret_cast<float*>(ws + Lw.attn_o);
   const int nwg = s.batch * s.n_kv_heads * p.n_splits;
   const int grid8 = (nwg + 7) / 8 * 8;          // work units rounded up to a multiple of 8
-  const int longest_first = (grid8 * p.row_blocks > device_cus()) ? 1 : 0;
+  // one resident workgroup per CU with two row blocks, two with one
+  const int longest_first = (grid8 > device_cus() * (p.row_blocks == 1 ? 2 : 1) / 2) ? 1 : 0;
   if (s.kv_dtype == ISD_BF16) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kn = static_cast<const uint16_t*>(k_new);
@@ -778,17 +782,18 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
     const uint16_t* kp = static_cast<const uint16_t*>(k_pages);
     const uint16_t* vp = static_cast<const uint16_t*>(v_pages);
     uint16_t* o = static_cast<uint16_t*>(out);
-    // one workgroup per 32 query rows of a (request, KV head, split)
+    // one workgroup per (request, KV head, split): its waves cover the 32 query rows,
+    // or 64 in two row blocks
     if (p.row_blocks == 1)
-      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, true>), dim3(grid8), dim3(64 * kAttnWaves), 0, stream,
+      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, true, 1>), dim3(grid8), dim3(64 * kAttnWaves), 0, stream,
                          qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group,
                          p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, 1, nwg, longest_first,
                          scale_log2, ml, po, arrivals, flags);
     else
-      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, false>), dim3(grid8 * p.row_blocks), dim3(64 * kAttnWaves), 0,
-                         stream, qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads,
-                         p.group, p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, p.row_blocks,
-                         nwg, longest_first, scale_log2, ml, po, arrivals, flags);
+      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, true, 2>), dim3(grid8), dim3(64 * kAttnWaves), 0, stream,
+                         qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group,
+                         p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, 1, nwg, longest_first,
+                         scale_log2, ml, po, arrivals, flags);
   } else {
     const float* qq = static_cast<const float*>(q);
     hipLaunchKernelGGL((attn_split_f32<D>), dim3(nwg, p.rows), dim3(64), 0, stream, qq,

@@ -1,6 +1,6 @@
 // Appending accepted stride rows to the KV pages (kv_commit) and the
-// workspace header fill (isd_workspace_init).  The row commit itself lives
-// in commit_row.hpp: one workgroup per (request, stride row 0..N-1).
+// workspace header fill (isd_workspace_init).  The commit itself lives in
+// commit_row.hpp: one workgroup per request.
 #include "commit_row.hpp"
 
 namespace isd {
@@ -8,8 +8,7 @@ namespace {
 
 template <typename T>
 __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitArgs c) {
-  __shared__ int s_last;
-  commit_row<T>(c, blockIdx.x, blockIdx.y, &s_last);
+  commit_request<T>(c, blockIdx.x);
 }
 
 __global__ void fill_zero_u32(uint32_t* p, int n) {
@@ -21,7 +20,7 @@ __global__ void fill_zero_u32(uint32_t* p, int n) {
 
 CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
                        void* v_pages, const int32_t* table, const int32_t* ctx_in,
-                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags, uint32_t* arrivals,
+                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags,
                        const int32_t* loop_mode) {
   CommitArgs c;
   c.k_new = k_new;
@@ -33,7 +32,6 @@ CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new,
   c.n_commit = n_commit;
   c.ctx_out = ctx_out;
   c.flags = flags;
-  c.arrivals = arrivals;
   c.loop_mode = loop_mode;
   c.N = s.stride_n;
   c.Hkv = s.n_kv_heads;
@@ -45,7 +43,7 @@ CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new,
 }
 
 hipError_t launch_commit(const isd_shape& s, const CommitArgs& c, hipStream_t stream) {
-  const dim3 grid(s.stride_n, s.batch);
+  const dim3 grid(s.batch);
   if (c.kv_bf16)
     hipLaunchKernelGGL((kv_commit_kernel<uint16_t>), grid, dim3(kCommitThreads), 0, stream, c);
   else

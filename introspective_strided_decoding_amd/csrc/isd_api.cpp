@@ -36,7 +36,7 @@ bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0
 
 int ceil_div(long long a, long long b) { return int((a + b - 1) / b); }
 
-isd_status check_dtype(isd_dtype d) {
+isd_status check_dtype(int32_t d) {
   return (d == ISD_F32 || d == ISD_BF16) ? ISD_OK : ISD_ERR_DTYPE;
 }
 
@@ -67,13 +67,12 @@ isd_status check_ws(const isd_shape* s, const void* ws, size_t bytes) {
 
 // ---- the scratch of isd_accept_commit_noalloc ----
 // One array per device, owned by the library for the life of the process.
-// Its first kScratchZeroBytes hold the header and the per-request counters
-// (cleared once per device at set-up; the kernels rewind every counter they
-// use); the partials follow.  In host code `scratch` names a host-side stand-in:
-// the device address comes from hipGetSymbolAddress, per device.
+// Its header is cleared once per device at set-up; the partials follow, each
+// written before it is read within a call, so nothing else needs clearing.  In
+// host code `scratch` names a host-side stand-in: the device address comes from
+// hipGetSymbolAddress, per device.
 constexpr size_t kScratchBytes = size_t(16) << 20;
-constexpr size_t kScratchZeroBytes = size_t(1) << 20;
-static_assert(kHeaderBytes + 65535 * 4 <= kScratchZeroBytes, "per-request counters fit the cleared region");
+constexpr size_t kScratchZeroBytes = kHeaderBytes;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -100,14 +99,11 @@ hipError_t device_scratch(char** out, hipStream_t stream) {
   return hipSuccess;
 }
 
-// Regions of isd_accept + commit inside the scratch: counters in the cleared
-// region (the list count at header offset kRejCountOffset, the commit's
-// per-request arrivals after the header), partials after it.  The flag word is
-// the caller's.
+// Regions of isd_accept + commit inside the scratch: the header, then the
+// partials.  The flag word is the caller's.
 WsLayout scratch_layout(const isd_shape& s) {
   WsLayout L;
   const AcceptPlan c = plan_accept(s);
-  L.cmt_cnt = kHeaderBytes;
   L.zero_end = kScratchZeroBytes;
   size_t off = kScratchZeroBytes;
   L.lse = off;
@@ -154,7 +150,7 @@ hipError_t run_accept_commit(const isd_shape& s, const void* p_logits, const voi
                              char* ws, const WsLayout& L, uint32_t* flags, hipStream_t stream) {
   const AcceptPlan p = plan_accept(s);
   const CommitArgs c = commit_args(s, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
-                                   ctx_lens_out, flags, reinterpret_cast<uint32_t*>(ws + L.cmt_cnt), loop_mode);
+                                   ctx_lens_out, flags, loop_mode);
   return launch_accept(s, p, p_logits, q_logits, proposals, req_ids, positions, seed_lo, seed_hi, step,
                        step_per_request, q_norms, accept_len, out_tokens, n_out, n_commit, logp_sel, logq_sel, ws,
                        L, flags, &c, stream);
@@ -228,8 +224,6 @@ WsLayout ws_layout(const isd_shape& s) {
   size_t off = kHeaderBytes;
   L.attn_cnt = off;
   off = align_up(off + (size_t)s.batch * s.n_kv_heads * a.row_blocks * 4, 256);
-  L.cmt_cnt = off;
-  off = align_up(off + (size_t)s.batch * 4, 256);
   L.zero_end = off;
   const size_t partial_rows = (size_t)s.batch * s.n_kv_heads * a.n_splits * a.rows_pad;
   L.attn_ml = off;
@@ -258,7 +252,7 @@ extern "C" {
 
 int32_t isd_abi_version(void) { return 10; }
 
-const char* isd_status_string(isd_status status) {
+const char* isd_status_string(int32_t status) {
   switch (status) {
     case ISD_OK: return "ok";
     case ISD_ERR_NULL: return "a required pointer is NULL";
@@ -415,8 +409,7 @@ isd_status kv_commit(const isd_shape* shape, const void* k_new, const void* v_ne
   const WsLayout L = ws_layout(*shape);
   char* ws = static_cast<char*>(workspace);
   const CommitArgs c = commit_args(*shape, k_new, v_new, k_pages, v_pages, page_table, ctx_lens_in, n_commit,
-                                   ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags),
-                                   reinterpret_cast<uint32_t*>(ws + L.cmt_cnt));
+                                   ctx_lens_out, reinterpret_cast<uint32_t*>(ws + L.flags));
   hipError_t e = launch_commit(*shape, c, stream);
   return e == hipSuccess ? ISD_OK : hip_fail(e, "kv_commit");
 }

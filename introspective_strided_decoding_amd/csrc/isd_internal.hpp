@@ -41,7 +41,6 @@ struct AcceptPlan {
 struct WsLayout {
   size_t flags = 0;          // uint32 device flags
   size_t attn_cnt = 0;       // uint32 per (request, kv head, row block): split arrivals
-  size_t cmt_cnt = 0;        // uint32 per request: commit workgroups arrived
   size_t zero_end = 0;       // [0, zero_end) is zeroed by isd_workspace_init
   size_t attn_ml = 0;        // float2 (m, l) per partial row
   size_t attn_o = 0;         // float [D] per partial row
@@ -52,7 +51,6 @@ struct WsLayout {
   size_t prop = 0;           // PropPart per (MASK row, proposal shard)
   size_t total = 0;
 };
-
 
 // Header word (uint32 at this byte offset of the workspace).
 constexpr size_t kRejCountOffset = 4;     // entries in the list of rejecting requests
@@ -111,14 +109,13 @@ struct CommitArgs {
   const int32_t* n_commit;
   int32_t* ctx_out;
   uint32_t* flags;
-  uint32_t* arrivals;     // per request, rewound by the last arrival
   const int32_t* loop_mode;   // per request (NULL: none): a re-proposing request commits its row N-1
   int N, Hkv, D, max_pages, num_pages;
   int kv_bf16;            // 1: bf16 pages, 0: fp32
 };
 CommitArgs commit_args(const isd_shape& s, const void* k_new, const void* v_new, void* k_pages,
                        void* v_pages, const int32_t* table, const int32_t* ctx_in,
-                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags, uint32_t* arrivals,
+                       const int32_t* n_commit, int32_t* ctx_out, uint32_t* flags,
                        const int32_t* loop_mode = nullptr);
 
 // Launchers (return the first HIP error, hipSuccess otherwise).
