@@ -252,32 +252,45 @@ __global__ __launch_bounds__(256) void gl_reduce(const GlGroup g, int M, int spl
                     uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16));
 }
 
-// One thread per (gated row, rank column) of projection blockIdx.y; part is
-// [projection][kchunks][m_pad][128], T is [projection][rows][128].
-__global__ __launch_bounds__(256) void gl_scatter(const float* __restrict__ part, int kchunks, int m_pad,
-                                                  const int32_t* __restrict__ mask_rows, int n_mask, int rows,
-                                                  float scale, uint16_t* __restrict__ T, uint32_t* __restrict__ flags) {
+// One thread per (gated row, 4 rank columns) of projection blockIdx.y; part is
+// [projection][kchunks][m_pad][128], T is [projection][rows][128].  Every
+// thread issues all its loads of a batch of 16 chunks before it adds any.
+constexpr int kScatterThreads = 64;
+__global__ __launch_bounds__(kScatterThreads) void gl_scatter(const float* __restrict__ part, int kchunks, int m_pad,
+                                                              const int32_t* __restrict__ mask_rows, int n_mask,
+                                                              int rows, float scale, uint16_t* __restrict__ T,
+                                                              uint32_t* __restrict__ flags) {
   part += size_t(blockIdx.y) * kchunks * m_pad * kRank;
   T += size_t(blockIdx.y) * rows * kRank;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const int g = e / kRank, r = e % kRank;
+  const int e = blockIdx.x * kScatterThreads + threadIdx.x;
+  const int g = e / (kRank / 4), r = (e % (kRank / 4)) * 4;
   if (g >= n_mask) return;
   const int row = mask_rows[g];
   if (row < 0 || row >= rows) {              // skipped, and flagged once per entry
     if (r == 0 && blockIdx.y == 0) raise_flag(flags, ISD_FLAG_ROW_RANGE);
     return;
   }
-  // eight independent running sums, so eight loads are in flight at a time
-  const float* p = part + size_t(g) * kRank + r;
-  const size_t stride = size_t(m_pad) * kRank;
-  float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int kc = 0;
-  for (; kc + 8 <= kchunks; kc += 8)
+  // eight running sums, chunk kc going to sum kc % 8
+  const f32x4* p = reinterpret_cast<const f32x4*>(part + size_t(g) * kRank + r);
+  const size_t stride = size_t(m_pad) * (kRank / 4);
+  f32x4 t[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] += p[(kc + u) * stride];
-  for (int u = 0; kc < kchunks; ++kc, ++u) t[u] += p[kc * stride];
-  const float sum = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
-  T[size_t(row) * kRank + r] = f32_to_bf16_bits(scale * sum);
+  for (int u = 0; u < 8; ++u) t[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int kc = 0;
+  for (; kc + 16 <= kchunks; kc += 16) {
+    f32x4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = p[(kc + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] += v[u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] += v[8 + u];
+  }
+  for (; kc < kchunks; ++kc) t[kc % 8] += p[kc * stride];
+  const f32x4 sum = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+  *reinterpret_cast<uint2*>(T + size_t(row) * kRank + r) =
+      make_uint2(uint32_t(f32_to_bf16_bits(scale * sum[0])) | (uint32_t(f32_to_bf16_bits(scale * sum[1])) << 16),
+                 uint32_t(f32_to_bf16_bits(scale * sum[2])) | (uint32_t(f32_to_bf16_bits(scale * sum[3])) << 16));
 }
 
 }  // namespace
@@ -401,8 +414,9 @@ hipError_t launch_gated_linear(int32_t n_proj, int32_t rows, int32_t d_in, const
     hipLaunchKernelGGL((gl_gemm<64, 64, 4, 2, 2>), dim3(mtd * n_proj * (kRank / 64) * kchunks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(X), d_in, 0, n_mask, mtd, kchunks, gd, mask_rows, rows,
                        reinterpret_cast<u32x4*>(t), int(size_t(n_proj) * rows * rank * 2 / 16));
-    hipLaunchKernelGGL(gl_scatter, dim3((n_mask * kRank + 255) / 256, n_proj), dim3(256), 0, stream, down, kchunks,
-                       n_mask, mask_rows, n_mask, rows, scale, t, reinterpret_cast<uint32_t*>(ws));
+    hipLaunchKernelGGL(gl_scatter, dim3((n_mask * (kRank / 4) + kScatterThreads - 1) / kScatterThreads, n_proj),
+                       dim3(kScatterThreads), 0, stream, down, kchunks, n_mask, mask_rows, n_mask, rows, scale, t,
+                       reinterpret_cast<uint32_t*>(ws));
     for (int p = 0; p < n_proj; ++p) {
       g.T[p] = t + size_t(p) * rows * kRank;
       g.Bt[p] = static_cast<const uint16_t*>(B_t[p]);
