@@ -249,8 +249,9 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
       has_tail = true;
       if (e == xg) { xv = x; has_x = true; }
     }
-    // pass 2: sum of exp(x - mx) in base 2 (the exponentials, about a quarter of
-    // the VALU rate, are what this kernel spends beyond its streaming read)
+    // pass 2: sum of exp(x - mx) in base 2 by the hardware exp2 (a quarter of the
+    // VALU rate; no range fix-up: a term below 2^-126 cannot change a sum that
+    // holds the thread's max term, about 1)
     if (mx != -INFINITY) {
       const float mb = mx * kLog2e;
       float acc = 0.f;
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
             float x[VN];
             unpack(raw[k], x, T());
 #pragma unroll
-            for (int i = 0; i < VN; ++i) acc += exp2f(fmaf(x[i], kLog2e, -mb));
+            for (int i = 0; i < VN; ++i) acc += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mb));
           }
         }
       }

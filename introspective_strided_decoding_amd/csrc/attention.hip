@@ -237,7 +237,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
   __shared__ float sm_ml[COLS][2];
   __shared__ int s_last;
 
-  // Work unit u = (request, KV head, split); with nb > 1 each unit is served by
+  // Work unit u = (request, split, KV head), the head varying fastest; with nb > 1 each unit is served by
   // nb workgroups, one per block of COLS query rows.  Workgroup ids are laid
   // out as [group of 8 units][row block][unit in group], so the row blocks of
   // a unit land on the same XCD (ids equal mod 8) at nearly the same time and
@@ -246,8 +246,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
   const int b = rem / 8;
   const int u = grp * 8 + rem % 8;
   if (u >= units) return;
-  const int split = u % n_splits;
-  const int hk = (u / n_splits) % Hkv;
+  // Workgroup ids equal mod 8 go to one XCD; with the head fastest every XCD
+  // gets the same heads of every split of every request (equal work for 8 KV
+  // heads), where split-fastest ids would leave the XCDs that hold the later
+  // splits idle while short requests, which use one split, run on the others
+  const int hk = u % Hkv;
+  const int split = (u / Hkv) % n_splits;
   // When the grid takes more than one round of the chip, requests are served
   // longest first (ties in index order): long contexts start early and short
   // ones fill in at the end.  For up to kRankMax requests every workgroup
@@ -416,13 +420,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run[rb], mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[rb] - m_new);
+      // the hardware exp2 (no range fix-up: arguments are <= 0 and a weight below
+      // 2^-126 is negligible against the running sum, which holds a 1); a -inf
+      // argument gives 0
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // all masked so far: every s is -inf
       m_run[rb] = m_new;
       float psum = 0.f;
       bf16x8 pb[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = (s[rb][v] == -INFINITY) ? 0.f : exp2f(s[rb][v] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[rb][v] - m_use);
         psum += p;
         pb[v >> 3][v & 7] = (__bf16)p;
       }
