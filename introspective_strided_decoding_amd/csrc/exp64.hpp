@@ -4,7 +4,10 @@
 // arguments the samplers need: t = logit - (a max over the same logits), so
 // t <= 0 and no overflow handling is needed.
 //
-//   n = rint(t * 64 / ln 2),  n = 64 m + j  (0 <= j < 64)
+//   n = rint(t * 64 / ln 2),  n = 64 m + j  (0 <= j < 64); n is formed by
+//                              adding 1.5 * 2^52 in the same fma that scales t
+//                              (the sum's low word then holds n), which saves
+//                              the rounding and conversion instructions
 //   r = t - n * (ln 2 / 64)   (|r| <= ln 2 / 128; ln 2 / 64 split as hi + lo
 //                              with hi's low 17 mantissa bits zero, so n * hi
 //                              is exact for |n| < 2^17)
@@ -27,12 +30,20 @@ constexpr double kExpStepHi = 0x1.62e42fefa0000p-7;      // ln 2 / 64, high part
 constexpr double kExpStepLo = 0x1.cf79abc9e3b3ap-46;     // ln 2 / 64 - high part
 constexpr double kExpClamp = -746.0;
 
+constexpr double kExpShifter = 0x1.8p52;                // 1.5 * 2^52
+
 __host__ __device__ inline double exp_nonpos(double t, const double* __restrict__ tab64) {
   t = fmax(t, kExpClamp);
-  const double n = rint(t * kExpInvStep);
-  const int ni = static_cast<int>(n);
+  // |t * 64 / ln 2| < 2^17, so the shifted sum lies in [2^52, 2^53), where the
+  // spacing is 1: it is rounded to the nearest integer, held two's-complement
+  // in the low word of the mantissa
+  const double k = fma(t, kExpInvStep, kExpShifter);
+  const double n = k - kExpShifter;
+  unsigned long long kb;
+  __builtin_memcpy(&kb, &k, sizeof(kb));
+  const int ni = static_cast<int>(static_cast<unsigned int>(kb));
   const int j = ni & 63;
-  const int m = (ni - j) / 64;
+  const int m = ni >> 6;                                 // floor(n / 64)
   const double r = fma(-n, kExpStepLo, fma(-n, kExpStepHi, t));
   double p = 1.0 / 120.0;
   p = fma(p, r, 1.0 / 24.0);
