@@ -254,8 +254,10 @@ __global__ __launch_bounds__(256) void gl_reduce(const GlGroup g, int M, int spl
 
 // One thread per (gated row, 4 rank columns) of projection blockIdx.y; part is
 // [projection][kchunks][m_pad][128], T is [projection][rows][128].  Every
-// thread issues all its loads of a batch of 16 chunks before it adds any.
+// thread requests the partials of a batch of chunks (16, or 48 for d_in up to
+// 12288) before it reads the gate list or adds any: one memory round trip.
 constexpr int kScatterThreads = 64;
+template <int kScatterBatch>
 __global__ __launch_bounds__(kScatterThreads) void gl_scatter(const float* __restrict__ part, int kchunks, int m_pad,
                                                               const int32_t* __restrict__ mask_rows, int n_mask,
                                                               int rows, float scale, uint16_t* __restrict__ T,
@@ -265,28 +267,26 @@ __global__ __launch_bounds__(kScatterThreads) void gl_scatter(const float* __res
   const int e = blockIdx.x * kScatterThreads + threadIdx.x;
   const int g = e / (kRank / 4), r = (e % (kRank / 4)) * 4;
   if (g >= n_mask) return;
-  const int row = mask_rows[g];
-  if (row < 0 || row >= rows) {              // skipped, and flagged once per entry
-    if (r == 0 && blockIdx.y == 0) raise_flag(flags, ISD_FLAG_ROW_RANGE);
-    return;
-  }
-  // eight running sums, chunk kc going to sum kc % 8
+  // eight running sums, chunk kc going to sum kc % 8, chunks in increasing order
   const f32x4* p = reinterpret_cast<const f32x4*>(part + size_t(g) * kRank + r);
   const size_t stride = size_t(m_pad) * (kRank / 4);
   f32x4 t[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) t[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int kc = 0;
-  for (; kc + 16 <= kchunks; kc += 16) {
-    f32x4 v[16];
+  int row = 0;
+  for (int kc = 0; kc < kchunks; kc += kScatterBatch) {
+    f32x4 v[kScatterBatch];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = p[(kc + u) * stride];
+    for (int u = 0; u < kScatterBatch; ++u) v[u] = p[min(kc + u, kchunks - 1) * stride];   // in bounds, unconditional
+    if (kc == 0) row = mask_rows[g];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] += v[u];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] += v[8 + u];
+    for (int u = 0; u < kScatterBatch; ++u)
+      if (kc + u < kchunks) t[u % 8] += v[u];
   }
-  for (; kc < kchunks; ++kc) t[kc % 8] += p[kc * stride];
+  if (row < 0 || row >= rows) {              // skipped, and flagged once per entry
+    if (r == 0 && blockIdx.y == 0) raise_flag(flags, ISD_FLAG_ROW_RANGE);
+    return;
+  }
   const f32x4 sum = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
   *reinterpret_cast<uint2*>(T + size_t(row) * kRank + r) =
       make_uint2(uint32_t(f32_to_bf16_bits(scale * sum[0])) | (uint32_t(f32_to_bf16_bits(scale * sum[1])) << 16),
@@ -414,9 +414,13 @@ hipError_t launch_gated_linear(int32_t n_proj, int32_t rows, int32_t d_in, const
     hipLaunchKernelGGL((gl_gemm<64, 64, 4, 2, 2>), dim3(mtd * n_proj * (kRank / 64) * kchunks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(X), d_in, 0, n_mask, mtd, kchunks, gd, mask_rows, rows,
                        reinterpret_cast<u32x4*>(t), int(size_t(n_proj) * rows * rank * 2 / 16));
-    hipLaunchKernelGGL(gl_scatter, dim3((n_mask * (kRank / 4) + kScatterThreads - 1) / kScatterThreads, n_proj),
-                       dim3(kScatterThreads), 0, stream, down, kchunks, n_mask, mask_rows, n_mask, rows, scale, t,
-                       reinterpret_cast<uint32_t*>(ws));
+    const dim3 sgrid((n_mask * (kRank / 4) + kScatterThreads - 1) / kScatterThreads, n_proj);
+    if (kchunks <= 16)
+      hipLaunchKernelGGL(gl_scatter<16>, sgrid, dim3(kScatterThreads), 0, stream, down, kchunks, n_mask, mask_rows,
+                         n_mask, rows, scale, t, reinterpret_cast<uint32_t*>(ws));
+    else
+      hipLaunchKernelGGL(gl_scatter<48>, sgrid, dim3(kScatterThreads), 0, stream, down, kchunks, n_mask, mask_rows,
+                         n_mask, rows, scale, t, reinterpret_cast<uint32_t*>(ws));
     for (int p = 0; p < n_proj; ++p) {
       g.T[p] = t + size_t(p) * rows * kRank;
       g.Bt[p] = static_cast<const uint16_t*>(B_t[p]);
