@@ -618,9 +618,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
                         (uint64_t(__float_as_uint(sm_ml[threadIdx.x][1])) << 32);
     st_coherent(reinterpret_cast<uint64_t*>(ws_ml + base + threadIdx.x), ml);
   }
-  for (int f = threadIdx.x; f < rows_b * D; f += blockDim.x) {
-    const int c = f / D, d = f % D;
-    st_coherent(ws_o + (base + c) * D + d, sm_o0[c * OSTR + d] + sm_o1[c * OSTR + d]);
+  // the O rows of this (request, KV head): [split][RSTR rows][D], as 16-byte pieces
+  const size_t base0 = size_t(rk) * n_splits * RSTR + row0;
+  const __amdgpu_buffer_rsrc_t o_rsrc =
+      coherent_rsrc(ws_o + size_t(rk) * n_splits * RSTR * D, n_splits * RSTR * D * int(sizeof(float)));
+  for (int f4 = threadIdx.x; f4 < rows_b * V4; f4 += blockDim.x) {
+    const int c = f4 / V4, d0 = (f4 % V4) * 4;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(&sm_o0[c * OSTR + d0]);
+    const f32x4 b2 = *reinterpret_cast<const f32x4*>(&sm_o1[c * OSTR + d0]);
+    st_coherent16(o_rsrc, ((split * RSTR + row0 + c) * D + d0) * int(sizeof(float)), a + b2);
   }
   if (!arrive_last(&arrivals[size_t(rk) * nb + b], uint32_t(active), &s_last)) return;
   // The partials were written through to memory before their writers
@@ -631,7 +637,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
   // loads of each batch of splits are all issued before any is used
   __shared__ float sm_w[COLS][kMaxSplits];
   __shared__ float sm_sm[COLS][kMaxSplits];
-  const size_t base0 = size_t(rk) * n_splits * RSTR + row0;
   if (threadIdx.x < rows_b) {
     const int c = threadIdx.x;
     float M = -INFINITY;
@@ -662,30 +667,34 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
     for (int s = 0; s < active; ++s) sm_w[c][s] *= inv;
   }
   __syncthreads();
-  // every thread owns up to J 4-float pieces of the output; per split, the
-  // loads of all of them go out before the sums
+  // every thread owns up to J 4-float pieces of the output; the 16-byte loads
+  // of SB splits at a time go out before their sums (added in split order)
   constexpr int J = (COLS * V4 + 64 * W - 1) / (64 * W);
+  constexpr int SB = 4;
   const int n4 = rows_b * V4;
   f32x4 acc[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < active; ++s) {
-    f32x4 v[J];
+  int off[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int f4 = threadIdx.x + j * 64 * W;
-      v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (f4 < n4) {
-        const int c = f4 / V4, d0 = (f4 % V4) * 4;
-        const float* src = ws_o + (base0 + size_t(s) * RSTR + c) * D + d0;
-        v[j] = f32x4{MERGE_LD(src), MERGE_LD(src + 1), MERGE_LD(src + 2), MERGE_LD(src + 3)};
+  for (int j = 0; j < J; ++j) {
+    const int f4 = min(int(threadIdx.x) + j * 64 * W, n4 - 1);
+    off[j] = ((row0 + f4 / V4) * D + (f4 % V4) * 4) * int(sizeof(float));
+  }
+  const int split_bytes = RSTR * D * int(sizeof(float));
+  for (int s0 = 0; s0 < active; s0 += SB) {
+    f32x4 v[SB][J];
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+#pragma unroll
+      for (int j = 0; j < J; ++j) v[k][j] = ld_coherent16(o_rsrc, min(s0 + k, active - 1) * split_bytes + off[j]);
+#pragma unroll
+    for (int k = 0; k < SB; ++k)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int f4 = threadIdx.x + j * 64 * W;
+        if (s0 + k < active && f4 < n4) acc[j] += v[k][j] * sm_w[f4 / V4][s0 + k];
       }
-    }
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int f4 = threadIdx.x + j * 64 * W;
-      if (f4 < n4) acc[j] += v[j] * sm_w[f4 / V4][s];
-    }
   }
 #pragma unroll
   for (int j = 0; j < J; ++j) {

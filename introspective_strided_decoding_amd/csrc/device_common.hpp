@@ -168,6 +168,21 @@ template <typename T>
 __device__ __forceinline__ T ld_coherent(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte forms of the same accesses, through a buffer resource over a region
+// of `bytes` bytes at `base` (16-byte aligned, bytes < 2^31): buffer loads and
+// stores with the sc1 cache policy, the encoding the agent-scope relaxed
+// atomics above take on this architecture.  Offsets are in bytes; an offset
+// past the region reads 0 and writes nothing.
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 ld_coherent16(__amdgpu_buffer_rsrc_t r, int offset) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ void st_coherent16(__amdgpu_buffer_rsrc_t r, int offset, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, offset, 0, kCachePolicySc1);
+}
 // Wait until this wave's stores have completed (s_waitcnt vmcnt(0)).
 __device__ __forceinline__ void wait_stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
