@@ -2,10 +2,10 @@
 //
 // Work split: a work unit is (request r, KV head hk, split s): a run of
 // 32-token tiles (two 16-token pages) of r's context.  One workgroup of W
-// waves (four: one per SIMD, two workgroups per CU) serves one unit for one
-// block of 32 query columns (the GQA group's G
-// heads x Q stride rows; groups of more than 32 columns get one workgroup per
-// block, placed on the same XCD so the second read of the pages hits L2).
+// waves (four, one per SIMD) serves one unit for all the query columns of
+// the GQA group (its G heads x Q stride rows): RB = 1 block of 32 columns
+// (two workgroups per CU), or RB = 2 blocks for 33..64 columns, every tile
+// then feeding both blocks (one workgroup per CU), so each page is read once.
 // The waves take the unit's tiles round-robin, and wave 0 of split 0 also
 // takes the stride's own strictly causal block (row i sees stride rows 0..i)
 // as one extra, masked tile.  Each wave keeps per column an online softmax
@@ -66,19 +66,14 @@ __device__ __forceinline__ int active_splits(int n_tiles, int n_splits, int tps)
   return max(1, min(n_splits, (n_tiles + tps - 1) / tps));
 }
 
-// KV page loads.  Pages read exactly once per step are streamed past the
-// caches (NT); pages that a second workgroup of the same XCD reads moments
-// later (row-block workgroups) are loaded normally so that read hits L2.
-template <bool NT>
-__device__ __forceinline__ u32x4 kv_load(const u32x4* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(p);
-  else return *p;
-}
+// KV page loads: every page is read exactly once per call, so the loads
+// stream past the caches (nontemporal).
+__device__ __forceinline__ u32x4 kv_load(const u32x4* p) { return __builtin_nontemporal_load(p); }
 
 // Operand loads of one 32-token tile (pages pid0, pid1; both valid ids).
 // One base pointer per lane and page; the unrolled k-steps / dim blocks are
 // immediate offsets from it.
-template <int D, bool NT>
+template <int D>
 __device__ __forceinline__ void load_k(u32x4 (&k)[D / 16], const uint16_t* __restrict__ kp, int pid0,
                                        int pid1, int hk, int Hkv, int lane) {
   const int h = lane >> 5;
@@ -87,10 +82,10 @@ __device__ __forceinline__ void load_k(u32x4 (&k)[D / 16], const uint16_t* __res
   const u32x4* base = reinterpret_cast<const u32x4*>(
       kp + (size_t(pid) * Hkv + hk) * (D * kPage) + (h * kPage + (i & 15)) * 8);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) k[s] = kv_load<NT>(base + s * 2 * kPage);
+  for (int s = 0; s < D / 16; ++s) k[s] = kv_load(base + s * 2 * kPage);
 }
 
-template <int D, bool NT>
+template <int D>
 __device__ __forceinline__ void load_v(u32x4 (&v)[2][D / 32], const uint16_t* __restrict__ vp, int pid0,
                                        int pid1, int hk, int Hkv, int lane) {
   const int h = lane >> 5;
@@ -100,7 +95,7 @@ __device__ __forceinline__ void load_v(u32x4 (&v)[2][D / 32], const uint16_t* __
     const u32x4* base = reinterpret_cast<const u32x4*>(
         vp + (size_t(m ? pid1 : pid0) * Hkv + hk) * (D * kPage) + i * kPage + h * 8);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) v[m][db] = kv_load<NT>(base + db * 32 * 2);
+    for (int db = 0; db < D / 32; ++db) v[m][db] = kv_load(base + db * 32 * 2);
   }
 }
 
@@ -216,12 +211,12 @@ __device__ __forceinline__ void combine_rk(const T* __restrict__ q, const T* __r
 // workgroups per CU), or 2 for groups of 33..64 query rows, where every wave
 // applies its key and value tiles to both blocks (so a tile crosses from L2
 // into the CU once) and takes a whole SIMD's registers.
-template <int D, int W, bool NT, int RB>
+template <int D, int W, int RB>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 3 - RB))) void attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctx_lens, uint16_t* __restrict__ out, int Qn, int Hq, int Hkv, int G,
-    int rows, int max_pages, int num_pages, int tps, int n_splits, int nb, int units, int longest_first,
+    int rows, int max_pages, int num_pages, int tps, int n_splits, int units, int longest_first,
     float scale_log2,
     float2* __restrict__ ws_ml, float* __restrict__ ws_o, uint32_t* __restrict__ arrivals,
     uint32_t* __restrict__ flags) {
@@ -237,14 +232,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
   __shared__ float sm_ml[COLS][2];
   __shared__ int s_last;
 
-  // Work unit u = (request, split, KV head), the head varying fastest; with nb > 1 each unit is served by
-  // nb workgroups, one per block of COLS query rows.  Workgroup ids are laid
-  // out as [group of 8 units][row block][unit in group], so the row blocks of
-  // a unit land on the same XCD (ids equal mod 8) at nearly the same time and
-  // the second read of the unit's pages is served by that XCD's L2.
-  const int grp = blockIdx.x / (8 * nb), rem = blockIdx.x % (8 * nb);
-  const int b = rem / 8;
-  const int u = grp * 8 + rem % 8;
+  // Work unit u = blockIdx.x = (request, split, KV head), the head varying
+  // fastest; the workgroup serves every query column of its unit.
+  const int u = blockIdx.x;
   if (u >= units) return;
   // Workgroup ids equal mod 8 go to one XCD; with the head fastest every XCD
   // gets the same heads of every split of every request (equal work for 8 KV
@@ -277,8 +267,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
     r = sm_req;
   }
   const int rk = r * Hkv + hk;
-  const int row0 = b * COLS;                    // first query row of this workgroup
-  const int rows_b = min(COLS, rows - row0);    // query rows of this workgroup
+  const int row0 = 0;                           // first query row of this workgroup
+  const int rows_b = min(COLS, rows);           // query rows of this workgroup
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;
@@ -376,8 +366,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
   if (n > 0) {
     int p0, p1;
     pages_i(0, p0, p1);
-    load_k<D, NT>(ak, kp, p0, p1, hk, Hkv, lane);
-    load_v<D, NT>(av, vp, p0, p1, hk, Hkv, lane);
+    load_k<D>(ak, kp, p0, p1, hk, Hkv, lane);
+    load_v<D>(av, vp, p0, p1, hk, Hkv, lane);
   }
   __syncthreads();
 
@@ -496,7 +486,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
     const bool partial = tok0 + kTileTokens > L;
     f32x16 s[RB];
     scores(ck, s);
-    if constexpr (decltype(prefetch)::value) load_v<D, NT>(nv, vp, np0, np1, hk, Hkv, lane);
+    if constexpr (decltype(prefetch)::value) load_v<D>(nv, vp, np0, np1, hk, Hkv, lane);
     if (partial) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
@@ -514,16 +504,16 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
     for (; i + 2 < n; i += 2) {
       const int ta = first + i * W, tb = ta + W;
       pages_i(i + 1, p0, p1);
-      load_k<D, NT>(bk, kp, p0, p1, hk, Hkv, lane);
+      load_k<D>(bk, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, ak, av, bv, ta, p0, p1);
       pages_i(i + 2, p0, p1);
-      load_k<D, NT>(ak, kp, p0, p1, hk, Hkv, lane);
+      load_k<D>(ak, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, bk, bv, av, tb, p0, p1);
     }
     const int ta = first + i * W;
     if (i + 1 < n) {
       pages_i(i + 1, p0, p1);
-      load_k<D, NT>(bk, kp, p0, p1, hk, Hkv, lane);
+      load_k<D>(bk, kp, p0, p1, hk, Hkv, lane);
       tile(Pre{}, ak, av, bv, ta, p0, p1);
       tile(NoPre{}, bk, bv, av, ta + W, 0, 0);
     } else {
@@ -609,7 +599,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
   }
 
   // several splits: publish this split's partial, the last to arrive merges
-  const int RSTR = nb * COLS;                   // partial rows per (request, KV head, split)
+  const int RSTR = COLS;                        // partial rows per (request, KV head, split)
   const size_t base = (size_t(rk) * n_splits + split) * RSTR + row0;
   // Write-through stores, consecutive lanes on consecutive addresses, so each
   // store instruction covers whole cache lines.
@@ -628,7 +618,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3 - RB, 
     const f32x4 b2 = *reinterpret_cast<const f32x4*>(&sm_o1[c * OSTR + d0]);
     st_coherent16(o_rsrc, ((split * RSTR + row0 + c) * D + d0) * int(sizeof(float)), a + b2);
   }
-  if (!arrive_last(&arrivals[size_t(rk) * nb + b], uint32_t(active), &s_last)) return;
+  if (!arrive_last(&arrivals[rk], uint32_t(active), &s_last)) return;
   // The partials were written through to memory before their writers
   // arrived; device-coherent loads read them from there.  (An acquire fence
   // plus plain loads invalidates the XCD's L2 and costs far more.)
@@ -789,9 +779,9 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
   float2* ml = reinterpret_cast<float2*>(ws + Lw.attn_ml);
   float* po = reinterpret_cast<float*>(ws + Lw.attn_o);
   const int nwg = s.batch * s.n_kv_heads * p.n_splits;
-  const int grid8 = (nwg + 7) / 8 * 8;          // work units rounded up to a multiple of 8
-  // one resident workgroup per CU with two row blocks, two with one
-  const int longest_first = (grid8 > device_cus() * (p.row_blocks == 1 ? 2 : 1) / 2) ? 1 : 0;
+  // longest requests first once the grid takes more than half a round of the
+  // chip (one resident workgroup per CU with two row blocks, two with one)
+  const int longest_first = (nwg > device_cus() * (p.row_blocks == 1 ? 2 : 1) / 2) ? 1 : 0;
   if (s.kv_dtype == ISD_BF16) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kn = static_cast<const uint16_t*>(k_new);
@@ -802,14 +792,14 @@ hipError_t launch_d(const isd_shape& s, const AttnPlan& p, const void* q, const 
     // one workgroup per (request, KV head, split): its waves cover the 32 query rows,
     // or 64 in two row blocks
     if (p.row_blocks == 1)
-      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, true, 1>), dim3(grid8), dim3(64 * kAttnWaves), 0, stream,
+      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, 1>), dim3(nwg), dim3(64 * kAttnWaves), 0, stream,
                          qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group,
-                         p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, 1, nwg, longest_first,
+                         p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, nwg, longest_first,
                          scale_log2, ml, po, arrivals, flags);
     else
-      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, true, 2>), dim3(grid8), dim3(64 * kAttnWaves), 0, stream,
+      hipLaunchKernelGGL((attn_bf16<D, kAttnWaves, 2>), dim3(nwg), dim3(64 * kAttnWaves), 0, stream,
                          qq, kn, vn, kp, vp, table, ctx_lens, o, p.q_rows, s.n_q_heads, s.n_kv_heads, p.group,
-                         p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, 1, nwg, longest_first,
+                         p.rows, s.max_pages, s.num_pages, p.tiles_per_split, p.n_splits, nwg, longest_first,
                          scale_log2, ml, po, arrivals, flags);
   } else {
     const float* qq = static_cast<const float*>(q);

@@ -223,7 +223,7 @@ WsLayout ws_layout(const isd_shape& s) {
   const AcceptPlan c = plan_accept(s);
   size_t off = kHeaderBytes;
   L.attn_cnt = off;
-  off = align_up(off + (size_t)s.batch * s.n_kv_heads * a.row_blocks * 4, 256);
+  off = align_up(off + (size_t)s.batch * s.n_kv_heads * 4, 256);
   L.zero_end = off;
   const size_t partial_rows = (size_t)s.batch * s.n_kv_heads * a.n_splits * a.rows_pad;
   L.attn_ml = off;

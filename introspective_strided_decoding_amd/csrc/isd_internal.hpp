@@ -40,7 +40,7 @@ struct AcceptPlan {
 
 struct WsLayout {
   size_t flags = 0;          // uint32 device flags
-  size_t attn_cnt = 0;       // uint32 per (request, kv head, row block): split arrivals
+  size_t attn_cnt = 0;       // uint32 per (request, kv head): split arrivals
   size_t zero_end = 0;       // [0, zero_end) is zeroed by isd_workspace_init
   size_t attn_ml = 0;        // float2 (m, l) per partial row
   size_t attn_o = 0;         // float [D] per partial row

@@ -21,7 +21,7 @@ Modules:
   philox     Philox4x64-10 and the per-decision uniforms
   attention  strictly causal stride attention over a paged KV cache
   accept     log-normalisers, the p/q acceptance test, residual resampling
-  commit     writing the accepted CLEAN rows into KV pages
+  commit     writing the stride rows of the accepted prefix into KV pages
   lora       the gated low-rank delta of R-ISD, and a whole gated projection
   tpf        expected acceptance, tokens per forward, the compute-bound identity
   propose    drawing the next N tokens at the MASK rows (sampling or argmax)
