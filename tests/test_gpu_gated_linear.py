@@ -95,7 +95,9 @@ def _check(Y, X, Wt, At, Bt, mask, scale, sample=None):
 # 128 x 128 tiles with k split in 2 over a ragged last row tile; 128 x 128 tiles of 8 waves,
 # ragged; 64 x 64 tiles with every row gated; one row gated; 128 x 128 tiles with a
 # two-stage ring (two workgroups per CU); 256 x 256 tiles of 8 waves over a ragged last row
-# tile of 8 rows; 256 x 192 tiles of 8 waves over a ragged last row tile of 88 rows.
+# tile of 8 rows; 256 x 192 tiles of 8 waves over a ragged last row tile of 88 rows; a
+# 16640-deep input, whose adapter down-projection leaves 65 chunk partials (summed in two
+# batches of 48, the second mostly clamped).
 CASES = [
     (20, 256, 128, [1, 3, 4, 17]),
     (70, 512, 384, list(range(0, 70, 2))),
@@ -107,6 +109,7 @@ CASES = [
     (300, 256, 16384, list(range(1, 300, 3))),
     (520, 256, 20480, [r for r in range(520) if r % 7 >= 3]),
     (600, 512, 12288, list(range(2, 600, 4))),
+    (48, 16640, 256, [r for r in range(48) if r % 3 != 1]),
 ]
 
 
