@@ -70,12 +70,22 @@ __global__ __launch_bounds__(256) void lora_down(const uint16_t* __restrict__ X,
     *reinterpret_cast<f32x4*>(dst + v4 * 8) = f32x4{acc[4 * v4], acc[4 * v4 + 1], acc[4 * v4 + 2], acc[4 * v4 + 3]};
 }
 
+// Chunk partials are requested 16 at a time (indices clamped into range, so every
+// load is unconditional and in flight together) and added in chunk order.
+constexpr int kReduceBatch = 16;
 __global__ __launch_bounds__(256) void lora_reduce(const float* __restrict__ part, int kchunks, int count,
                                                    uint16_t* __restrict__ t_hi, uint16_t* __restrict__ t_lo) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= count) return;
   float t = 0.f;
-  for (int kc = 0; kc < kchunks; ++kc) t += part[size_t(kc) * count + e];
+  for (int k0 = 0; k0 < kchunks; k0 += kReduceBatch) {
+    float v[kReduceBatch];
+#pragma unroll
+    for (int u = 0; u < kReduceBatch; ++u) v[u] = part[size_t(min(k0 + u, kchunks - 1)) * count + e];
+#pragma unroll
+    for (int u = 0; u < kReduceBatch; ++u)
+      if (k0 + u < kchunks) t += v[u];
+  }
   const uint16_t hi = f32_to_bf16_bits(t);
   t_hi[e] = hi;
   t_lo[e] = f32_to_bf16_bits(t - bf16_bits_to_f32(hi));
@@ -93,28 +103,49 @@ __global__ __launch_bounds__(256) void lora_up(const uint16_t* __restrict__ Bt, 
   const uint16_t* brow = Bt + size_t(o) * kLoraRank + h * 8;
   const uint16_t* hrow = t_hi + size_t(m) * kLoraRank + h * 8;
   const uint16_t* lrow = t_lo + size_t(m) * kLoraRank + h * 8;
+  // the gate list, the operands and then the gated row's outputs are all requested
+  // before the products, so the read of Y overlaps them (a lane outside the gate
+  // reads row 0 and stores nothing)
+  const int gr = mask_rows[min(m, n_mask - 1)];                  // unconditional: in flight with the rest
+  // every operand load is issued before the first product
+  constexpr int KS = kLoraRank / 16;
+  u32x4 bv[KS], hv[KS], lv[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    bv[s] = *reinterpret_cast<const u32x4*>(brow + s * 16);
+    hv[s] = *reinterpret_cast<const u32x4*>(hrow + s * 16);
+    lv[s] = *reinterpret_cast<const u32x4*>(lrow + s * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int row = (m < n_mask && gr >= 0 && gr < rows) ? gr : -1;
+  // C^T[o][m]: this lane holds m, and o = ob*128 + wave*32 + (v/4)*8 + h*4 + v%4
+  uint16_t* yrow = Y + size_t(row < 0 ? 0 : row) * d_out + ob * kOBlock + wave * 32 + h * 4;
+  uint2 yv[4];
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4) yv[v4] = *reinterpret_cast<const uint2*>(yrow + v4 * 8);
+  __builtin_amdgcn_sched_barrier(0);   // keep the loads above ahead of every product
   f32x16 acc = f32x16{};
 #pragma unroll
-  for (int s = 0; s < kLoraRank / 16; ++s) {
-    const bf16x8 a = as_b8(*reinterpret_cast<const u32x4*>(brow + s * 16));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_b8(*reinterpret_cast<const u32x4*>(hrow + s * 16)), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_b8(*reinterpret_cast<const u32x4*>(lrow + s * 16)), acc, 0, 0, 0);
+  for (int s = 0; s < KS; ++s) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(bv[s]), as_b8(hv[s]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(bv[s]), as_b8(lv[s]), acc, 0, 0, 0);
   }
-  const int row = gated_row(mask_rows, m, n_mask, rows, nullptr, false);
-  if (row < 0) return;
-  // C^T[o][m]: this lane holds m, and o = ob*128 + wave*32 + (v/4)*8 + h*4 + v%4
-  uint16_t* yrow = Y + size_t(row) * d_out + ob * kOBlock + wave * 32 + h * 4;
+  // the sums are formed on every lane (so the reads of Y stay where they were
+  // issued) and stored only for gated rows
+  uint2 out[4];
 #pragma unroll
   for (int v4 = 0; v4 < 4; ++v4) {
-    uint2* p = reinterpret_cast<uint2*>(yrow + v4 * 8);
-    const uint2 y = *p;
+    const uint2 y = yv[v4];
     const float y0 = bf16_lo(y.x) + scale * acc[4 * v4 + 0];
     const float y1 = bf16_hi(y.x) + scale * acc[4 * v4 + 1];
     const float y2 = bf16_lo(y.y) + scale * acc[4 * v4 + 2];
     const float y3 = bf16_hi(y.y) + scale * acc[4 * v4 + 3];
-    *p = make_uint2(uint32_t(f32_to_bf16_bits(y0)) | (uint32_t(f32_to_bf16_bits(y1)) << 16),
-                    uint32_t(f32_to_bf16_bits(y2)) | (uint32_t(f32_to_bf16_bits(y3)) << 16));
+    out[v4] = make_uint2(uint32_t(f32_to_bf16_bits(y0)) | (uint32_t(f32_to_bf16_bits(y1)) << 16),
+                         uint32_t(f32_to_bf16_bits(y2)) | (uint32_t(f32_to_bf16_bits(y3)) << 16));
   }
+  if (row < 0) return;
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4) *reinterpret_cast<uint2*>(yrow + v4 * 8) = out[v4];
 }
 
 }  // namespace
