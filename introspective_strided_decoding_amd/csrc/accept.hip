@@ -99,22 +99,36 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   const int N = a.N, V = a.V, R = N - 1, shards = a.shards;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float lse_sm[64], max_sm[64];
+  // every wave: the shard partials of rows wave, wave + 4, ... of the request's
+  // 2(N-1) rows (p rows only when the q normalisers are carried), at most 8 rows
+  // for N <= 16; with one shard per lane they are all requested first
+  const float2* req_part = part + size_t(r) * 2 * R * shards;
+  const int n_rows = a.q_norms ? R : 2 * R;
+  constexpr int kRowsPerWave = 8;
+  float2 pre[kRowsPerWave];
+  if (shards <= 64) {
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int row = min(wave + k * (kThreads / 64), n_rows - 1);
+      pre[k] = req_part[size_t(row) * shards + min(lane, shards - 1)];
+    }
+  }
   // wave 0: the proposals and the logits at them, requested before the combine
   int x = 0, xl = 0;
   float raw_p = 0.f, raw_q = 0.f;
   uint32_t rid32 = 0, pos32 = 0, step32 = a.step;
   float2 qn = make_float2(0.f, 0.f);
   if (wave == 0) {
-    if (lane < R) {
-      x = a.proposals[size_t(r) * N + lane + 1];
-      raw_p = a.gath[size_t(r) * 2 * R + lane];
-      if (a.q_norms) qn = a.q_norms[size_t(r) * N + lane + 1];
-      else raw_q = a.gath[size_t(r) * 2 * R + R + lane];
-      rid32 = uint32_t(a.req_ids[r]);
-      pos32 = uint32_t(a.positions[r]);
-      if (a.step_dev) step32 = uint32_t(a.step_dev[r]);
-    }
-    if (lane < N) xl = a.proposals[size_t(r) * N + lane];
+    // indices clamped into range so that every load is unconditional and in flight together
+    const int j = min(lane, R - 1);
+    xl = a.proposals[size_t(r) * N + min(lane, N - 1)];
+    raw_p = a.gath[size_t(r) * 2 * R + j];
+    if (a.q_norms) qn = a.q_norms[size_t(r) * N + j + 1];
+    else raw_q = a.gath[size_t(r) * 2 * R + R + j];
+    rid32 = uint32_t(a.req_ids[r]);
+    pos32 = uint32_t(a.positions[r]);
+    if (a.step_dev) step32 = uint32_t(a.step_dev[r]);
+    x = __shfl(xl, min(lane + 1, 63));     // lane j < R tests x_{j+2}, proposal j + 1
   }
   const bool in_range = x >= 0 && x < V;
   // carried q normalisers: the q rows' logits at the proposals are gathered here
@@ -125,19 +139,26 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
     lse_sm[R + lane] = qn.x + __logf(qn.y);
     max_sm[R + lane] = qn.x;
   }
-  // every wave: rows wave, wave + 4, ... of the request's 2(N-1) rows (p rows only when
-  // the q normalisers are carried)
-  const float2* req_part = part + size_t(r) * 2 * R * shards;
-  const int n_rows = a.q_norms ? R : 2 * R;
-  for (int row = wave; row < n_rows; row += kThreads / 64) {
-    float rm = -INFINITY, rs = 0.f;
-    for (int i = lane; i < shards; i += 64) {
-      const float2 v = req_part[size_t(row) * shards + i];
-      ms_merge(rm, rs, v.x, v.y);
-    }
+  auto row_done = [&](int row, float rm, float rs) {
     const float M = wave_max(rm);
     const float S = wave_sum((rm == -INFINITY) ? 0.f : rs * __expf(rm - M));
     if (lane == 0) { lse_sm[row] = M + __logf(S); max_sm[row] = M; }
+  };
+  if (shards <= 64) {
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int row = wave + k * (kThreads / 64);
+      if (row < n_rows) row_done(row, lane < shards ? pre[k].x : -INFINITY, lane < shards ? pre[k].y : 0.f);
+    }
+  } else {
+    for (int row = wave; row < n_rows; row += kThreads / 64) {
+      float rm = -INFINITY, rs = 0.f;
+      for (int i = lane; i < shards; i += 64) {
+        const float2 v = req_part[size_t(row) * shards + i];
+        ms_merge(rm, rs, v.x, v.y);
+      }
+      row_done(row, rm, rs);
+    }
   }
   __syncthreads();
   if (wave != 0) return;
