@@ -324,13 +324,17 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
     // the decision kernel, next in the stream, lists rejecting requests from zero
     if (blockIdx.x == 0 && blockIdx.y == 0) *args.rej_count = 0u;
   }
+  // and every list entry it does not fill reads as empty (req = -1), so the
+  // residual kernels need only their own entry, not the count
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < int(gridDim.y); i += kThreads) args.jobs[i].req = -1;
   if (has_x) args.gath[size_t(r) * 2 * R + jj] = xv;
 }
 
 // ---- fp64 residual ----
-// Residual workgroup (shard, k) serves the k-th listed rejecting request; it
-// requests its list entry together with the count (the selection kernel also
-// its shard records).  A residual shard is 2048 vocabulary entries: 256
+// Residual workgroup (shard, k) serves the k-th listed rejecting request; its
+// list entry alone says whether there is one (an unfilled entry has req = -1;
+// the selection kernel requests its shard records together with the entry).  A residual shard is 2048 vocabulary entries: 256
 // threads x 8 consecutive entries.
 //
 // Every value is e = exp(l - m) in float64 with m the row's exact max (carried
@@ -439,7 +443,6 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_logits,
                                                         const T* __restrict__ q_logits, int N, int V,
                                                         int r_shards, const ReqState* __restrict__ jobs,
-                                                        const uint32_t* __restrict__ rej_count,
                                                         ResidShard* __restrict__ shard_out) {
   __shared__ double tab64[64];
   __shared__ double sm4[kThreads / 64][4];
@@ -458,7 +461,11 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   const int sh = blockIdx.x;
   const int k = blockIdx.y;
   const ReqState st = jobs[k];
-  if (k >= int(*rej_count)) return;
+  // all of the entry is requested at once, not the gating field first and the
+  // rest after the test (the empty asm keeps the compiler from sinking them)
+  asm volatile("" ::"s"(st.req), "s"(st.reject_row), "s"(st.log_kappa), "s"(st.max_p), "s"(st.max_q),
+               "s"(p_logits), "s"(q_logits));
+  if (st.req < 0) return;                        // past the listed rejecting requests
   const size_t row = size_t(st.req) * (N - 1) + st.reject_row;
   const int e1 = min(V, (sh + 1) * kRShard);
   const int e0 = sh * kRShard + threadIdx.x * kRPer;
@@ -689,7 +696,6 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p_logits,
                                                           const T* __restrict__ q_logits, int N, int V,
                                                           int r_shards, const ReqState* __restrict__ jobs,
-                                                          const uint32_t* __restrict__ rej_count,
                                                           const ResidShard* __restrict__ shards_in,
                                                           int32_t* __restrict__ out_tokens, int B, CommitArgs cm) {
   __shared__ double tab64[64];
@@ -719,7 +725,10 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   ResidShard mine;
   if (mine_ok) mine = recs[threadIdx.x];
   const ReqState st = jobs[k];
-  if (k >= int(*rej_count)) return;
+  // all of the entry at once (see resid_pass)
+  asm volatile("" ::"s"(st.req), "s"(st.reject_row), "s"(st.log_kappa), "s"(st.max_p), "s"(st.max_q),
+               "s"(st.accept_len), "s"(st.u_resample));
+  if (st.req < 0) return;                        // past the listed rejecting requests
   const int r = st.req;
   const size_t row = size_t(r) * (N - 1) + st.reject_row;
   if (threadIdx.x == 0) n_redo_sm = 0;
@@ -889,12 +898,12 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
                      a, p.shard_len, part);
   hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
   hipLaunchKernelGGL((resid_pass<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards,
-                     jobs, rej_count, rshards);
+                     jobs, rshards);
   // with a commit, B more workgroups in the selection launch: one per request
   CommitArgs cm{};
   if (commit) cm = *commit;
   hipLaunchKernelGGL((resid_select<T>), dim3(commit ? 2 * B : B), dim3(kThreads), 0, stream, P, Qp, N, V,
-                     p.r_shards, jobs, rej_count, rshards, out_tokens, B, cm);
+                     p.r_shards, jobs, rshards, out_tokens, B, cm);
   return hipGetLastError();
 }
 
