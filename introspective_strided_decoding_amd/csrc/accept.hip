@@ -29,8 +29,9 @@
 // The residual runs in fp64 so the inverse CDF agrees with a float64
 // reference up to rounding of the running sums.  The decision lists the
 // rejecting requests compactly (an atomic counter the normaliser kernel
-// rewinds), so the residual workgroups that have work are the first ones
-// dispatched; the rest return after reading the count.
+// rewinds, and the normaliser marks every entry empty first), so the residual
+// workgroups that have work are the first ones dispatched; the rest return
+// after reading their empty entry.
 #include <climits>
 
 #include "commit_row.hpp"
