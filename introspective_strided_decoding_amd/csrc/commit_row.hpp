@@ -10,14 +10,20 @@
 // positions are mapped, and the new length is L plus the rows written, so
 // ctx_lens_out may alias ctx_lens_in.
 //
-// The work is split into cells of (KV head, 8 head dims).  A key cell writes
-// its n slot vectors (8 dims each, consecutive slots: contiguous in the key
-// layout).  A value cell rewrites, for each of its 8 dims, the dim's whole
-// 16-slot row of every page the committed positions touch: it reads the row,
-// puts the new values at their (swizzled) slots and writes the row back with
-// full 16-byte stores, so no store writes a partial 32-byte sector (a row
-// holds one token per slot, 2 bytes each in bf16, and a commit adds only a
-// few tokens to it).  One workgroup per request owns every row it rewrites.
+// Keys: one item per (row t, KV head, 8 head dims), a 16-byte slot vector
+// (consecutive slots are contiguous in the key layout), read and written with
+// consecutive items on consecutive lanes.  Values: a thread owns value rows
+// (KV head, head dim) h*D + d, consecutive rows on consecutive lanes, and
+// rewrites each row's whole 16 slots on every page the committed positions
+// touch (at most two): it reads the row, puts the new tokens' values at their
+// (swizzled) slots and writes the row back with full 16-byte stores, so no
+// store writes a partial 32-byte sector (a row holds one token per slot, 2
+// bytes each in bf16, and a commit adds only a few tokens to it), and a
+// wave's reads and writes of a page are contiguous.  Every wave looks the
+// page ids up itself, so no barrier stands between a thread's loads and its
+// stores: a request's commit is three memory round trips (its length and
+// count; the page ids and the new rows; the value rows).  One workgroup per
+// request owns every row it rewrites.
 #pragma once
 
 #include "device_common.hpp"
@@ -60,98 +66,163 @@ __device__ __forceinline__ void row_put(u32x4 (&row)[RV], int k, T v) {
 }
 
 // Commit request r's rows; call with all kCommitThreads threads.
+constexpr int kCommitPre = 8;        // new tokens whose values a value thread requests with its rows
+constexpr int kCommitRowsPer = 4;    // value rows a thread rewrites in one pass
+constexpr int kCommitKeyItems = 2;   // key items a thread requests before the first store
+
 template <typename T>
 __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
   constexpr int EV = 16 / int(sizeof(T));      // elements per 16-byte vector
-  constexpr int CV = 8 / EV;                   // vectors per 8-dim cell (1 bf16, 2 fp32)
+  constexpr int CV = 8 / EV;                   // vectors per 8-dim key cell (1 bf16, 2 fp32)
   constexpr int RV = kPage * int(sizeof(T)) / 16;   // vectors per value-page row (2 bf16, 4 fp32)
-  constexpr int JD = (sizeof(T) == 2) ? 8 : 4;      // value rows rewritten together
-  __shared__ int s_pid[kMaxCommitRows];
-  __shared__ int s_nv;
   const int N = c.N, Hkv = c.Hkv, D = c.D, max_pages = c.max_pages, num_pages = c.num_pages;
   const int Qn = 2 * N - 1;
   const int cap = max_pages * kPage;
+  const int lane = threadIdx.x & 63;
+  // the mode is read through a valid address either way, so that the three
+  // loads are in flight together
+  const int mode = *(c.loop_mode ? c.loop_mode + r : c.ctx_in + r);
   int L = c.ctx_in[r], n = c.n_commit[r], f = 0;
   const bool bad_n = n < 0 || n > N, bad_L = L < 0 || L > cap;
   if (bad_n) n = n < 0 ? 0 : N;
-  if (c.loop_mode && c.loop_mode[r] == ISD_LOOP_REPROPOSE) {   // the resampled token's row
+  if (c.loop_mode && mode == ISD_LOOP_REPROPOSE) {   // the resampled token's row
     n = 1;
     f = N - 1;
   }
   if (bad_L) { L = L < 0 ? 0 : cap; n = 0; }
-  // the pages of positions L..L+n-1; rows are written up to the first unmapped one
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int pid = (lane < n) ? commit_page(c.table, r, L, lane, max_pages, num_pages) : 0;
-    const uint64_t bad = __ballot(pid < 0);
-    const int nv = bad ? (__ffsll((unsigned long long)bad) - 1) : n;
-    const int first_bad = __shfl(pid, bad ? nv : 0);
-    if (lane < n) s_pid[lane] = pid;
-    if (lane == 0) {
-      s_nv = nv;
-      if (bad_n) raise_flag(c.flags, ISD_FLAG_COMMIT_RANGE);
-      if (bad_L) raise_flag(c.flags, ISD_FLAG_CTX_RANGE);
-      if (bad) raise_flag(c.flags, first_bad == -1 ? ISD_FLAG_COMMIT_RANGE : ISD_FLAG_PAGE_RANGE);
-    }
-  }
-  __syncthreads();
-  const int nv = s_nv;
   const T* __restrict__ kn = static_cast<const T*>(c.k_new) + size_t(r) * Qn * Hkv * D;
   const T* __restrict__ vn = static_cast<const T*>(c.v_new) + size_t(r) * Qn * Hkv * D;
   T* __restrict__ kp = static_cast<T*>(c.k_pages);
   T* __restrict__ vp = static_cast<T*>(c.v_pages);
-  const int cells = Hkv * D / 8;
-  for (int u = threadIdx.x; u < 2 * cells && nv > 0; u += kCommitThreads) {
-    const bool is_v = u >= cells;
-    const int cell = is_v ? u - cells : u;
-    const int h = cell / (D / 8), db = cell % (D / 8);
-    if (!is_v) {
-      // keys: slot vectors of consecutive positions
-      for (int t = 0; t < nv; ++t) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(kn + (size_t(f + t) * Hkv + h) * D + db * 8);
-        u32x4* dst = reinterpret_cast<u32x4*>(
-            kp + ((size_t(s_pid[t]) * Hkv + h) * (D / 8) + db) * (kPage * 8) + ((L + t) % kPage) * 8);
+  const int cells = Hkv * D / 8;   // key items per row: (KV head, 8 head dims)
+  const int rows = Hkv * D;        // value rows per page: (KV head, head dim)
+  const int t_last = max(n, 1) - 1;   // loads past the commit read its last row again (row f when empty)
+  auto key_src = [&](int t, int cell) {
+    return reinterpret_cast<const u32x4*>(kn + (size_t(f + t) * Hkv + cell / (D / 8)) * D + (cell % (D / 8)) * 8);
+  };
+  // Requested together with the page ids: this thread's first key items and
+  // the new tokens' values of its first value rows (they need only f and n).
+  u32x4 kv[kCommitKeyItems][CV];
 #pragma unroll
-        for (int q = 0; q < CV; ++q) dst[q] = src[q];
-      }
-      continue;
+  for (int j = 0; j < kCommitKeyItems; ++j) {
+    const int i = min(int(threadIdx.x) + j * kCommitThreads, cells * (t_last + 1) - 1);
+    const u32x4* src = key_src(i / cells, i % cells);
+#pragma unroll
+    for (int q = 0; q < CV; ++q) kv[j][q] = src[q];
+  }
+  T x[kCommitRowsPer][kCommitPre];
+  auto load_values = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < kCommitRowsPer; ++j) {
+      const int row = min(base + int(threadIdx.x) + j * kCommitThreads, rows - 1);
+#pragma unroll
+      for (int t = 0; t < kCommitPre; ++t) x[j][t] = vn[size_t(f + min(t, t_last)) * rows + row];
     }
-    // values: for every page the committed positions touch (one or two: nv <= 16),
-    // JD dims at a time, the dims' rows are read, the new tokens put in (four
-    // rows' values in registers at a time) and the rows written back
-    for (int t0 = 0; t0 < nv;) {
-      const int t1 = min(nv, (L + t0) / kPage * kPage + kPage - L);   // positions of this page
-      T* rows = vp + ((size_t(s_pid[t0]) * Hkv + h) * D + db * 8) * kPage;   // 8 consecutive dims' rows
+  };
+  load_values(0);
+  // the pages of positions L..L+n-1 (lane t: position L + t); rows are written
+  // up to the first unmapped one
+  const int pid = (lane < n) ? commit_page(c.table, r, L, lane, max_pages, num_pages) : 0;
+  const uint64_t bad = __ballot(pid < 0);
+  const int nv = bad ? (__ffsll((unsigned long long)bad) - 1) : n;
+  const int first_bad = __shfl(pid, bad ? nv : 0);
+  if (threadIdx.x == 0) {
+    if (bad_n) raise_flag(c.flags, ISD_FLAG_COMMIT_RANGE);
+    if (bad_L) raise_flag(c.flags, ISD_FLAG_CTX_RANGE);
+    if (bad) raise_flag(c.flags, first_bad == -1 ? ISD_FLAG_COMMIT_RANGE : ISD_FLAG_PAGE_RANGE);
+  }
+  if (nv > 0) {
+    // positions [0, t_split) lie on the first page, the rest (nv <= 16) on the next one
+    const int t_split = min(nv, kPage - L % kPage);
+    const bool two_pages = t_split < nv;
+    const int page_a = __builtin_amdgcn_readlane(pid, 0);
+    const int page_b = __builtin_amdgcn_readlane(pid, two_pages ? t_split : 0);
+    // value rows (whole 16-slot rows of both pages; the second is the first
+    // again when one page holds every position)
+    u32x4 ra[kCommitRowsPer][RV], rb[kCommitRowsPer][RV];
+    auto load_rows = [&](int base) {
 #pragma unroll
-      for (int j0 = 0; j0 < 8; j0 += JD) {
-        u32x4 row[JD][RV];
+      for (int j = 0; j < kCommitRowsPer; ++j) {
+        const int row = min(base + int(threadIdx.x) + j * kCommitThreads, rows - 1);
+        const u32x4* a = reinterpret_cast<const u32x4*>(vp + (size_t(page_a) * rows + row) * kPage);
+        const u32x4* b = reinterpret_cast<const u32x4*>(vp + (size_t(page_b) * rows + row) * kPage);
 #pragma unroll
-        for (int j = 0; j < JD; ++j)
-#pragma unroll
-          for (int q = 0; q < RV; ++q) row[j][q] = reinterpret_cast<const u32x4*>(rows + (j0 + j) * kPage)[q];
-        for (int tc = t0; tc < t1; tc += 4) {
-          T x[4][JD];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (tc + i < t1) {
-              const T* src = vn + (size_t(f + tc + i) * Hkv + h) * D + db * 8 + j0;
-#pragma unroll
-              for (int j = 0; j < JD; ++j) x[i][j] = src[j];
-            }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (tc + i < t1) {
-              const int k = v_sigma((L + tc + i) % kPage);
-#pragma unroll
-              for (int j = 0; j < JD; ++j) row_put<T, RV>(row[j], k, x[i][j]);
-            }
+        for (int q = 0; q < RV; ++q) {
+          ra[j][q] = a[q];
+          rb[j][q] = b[q];
         }
-#pragma unroll
-        for (int j = 0; j < JD; ++j)
-#pragma unroll
-          for (int q = 0; q < RV; ++q) reinterpret_cast<u32x4*>(rows + (j0 + j) * kPage)[q] = row[j][q];
       }
-      t0 = t1;
+    };
+    // the new tokens' values put at their (swizzled) slots, the rows written back
+    auto update_rows = [&](int base) {
+#pragma unroll
+      for (int t = 0; t < kCommitPre; ++t)
+        if (t < nv) {
+          const int k = v_sigma((L + t) % kPage);
+#pragma unroll
+          for (int j = 0; j < kCommitRowsPer; ++j) {
+            if (t < t_split)
+              row_put<T, RV>(ra[j], k, x[j][t]);
+            else
+              row_put<T, RV>(rb[j], k, x[j][t]);
+          }
+        }
+      for (int t = kCommitPre; t < nv; ++t) {   // N > 8 only
+        const int k = v_sigma((L + t) % kPage);
+#pragma unroll
+        for (int j = 0; j < kCommitRowsPer; ++j) {
+          const int row = min(base + int(threadIdx.x) + j * kCommitThreads, rows - 1);
+          const T v = vn[size_t(f + t) * rows + row];
+          if (t < t_split)
+            row_put<T, RV>(ra[j], k, v);
+          else
+            row_put<T, RV>(rb[j], k, v);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kCommitRowsPer; ++j) {
+        const int row = base + int(threadIdx.x) + j * kCommitThreads;
+        if (row < rows) {
+          u32x4* a = reinterpret_cast<u32x4*>(vp + (size_t(page_a) * rows + row) * kPage);
+          u32x4* b = reinterpret_cast<u32x4*>(vp + (size_t(page_b) * rows + row) * kPage);
+#pragma unroll
+          for (int q = 0; q < RV; ++q) {
+            a[q] = ra[j][q];
+            if (two_pages) b[q] = rb[j][q];
+          }
+        }
+      }
+    };
+    load_rows(0);   // requested before the key stores, which need nothing more
+    // ---- keys: slot vectors of consecutive positions ----
+    const int items = cells * nv;
+    auto key_dst = [&](int t, int cell) {
+      const int page = t < t_split ? page_a : page_b;
+      return reinterpret_cast<u32x4*>(kp + ((size_t(page) * Hkv + cell / (D / 8)) * (D / 8) + cell % (D / 8)) *
+                                               (kPage * 8) + ((L + t) % kPage) * 8);
+    };
+#pragma unroll
+    for (int j = 0; j < kCommitKeyItems; ++j) {
+      const int i = int(threadIdx.x) + j * kCommitThreads;
+      if (i < items) {
+        u32x4* dst = key_dst(i / cells, i % cells);
+#pragma unroll
+        for (int q = 0; q < CV; ++q) dst[q] = kv[j][q];
+      }
+    }
+    // more key items than the first passes hold (large heads or many rows)
+    for (int i = int(threadIdx.x) + kCommitKeyItems * kCommitThreads; i < items; i += kCommitThreads) {
+      const u32x4* src = key_src(i / cells, i % cells);
+      u32x4* dst = key_dst(i / cells, i % cells);
+#pragma unroll
+      for (int q = 0; q < CV; ++q) dst[q] = src[q];
+    }
+    // ---- values ----
+    update_rows(0);
+    for (int base = kCommitRowsPer * kCommitThreads; base < rows; base += kCommitRowsPer * kCommitThreads) {
+      load_values(base);   // more value rows than one pass holds (large heads)
+      load_rows(base);
+      update_rows(base);
     }
   }
   // every wave has read the length before it may be overwritten (ctx_lens_out may alias it)
