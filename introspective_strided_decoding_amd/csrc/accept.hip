@@ -43,7 +43,6 @@ namespace isd {
 namespace {
 
 constexpr int kThreads = 256;
-static_assert(kThreads == kCommitThreads, "commit workgroups run inside the selection launch");
 
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> { static constexpr int N = 8; };
@@ -370,6 +369,7 @@ __device__ __forceinline__ double exp_shift(float x, float m, const double* tab6
   return (x == -INFINITY) ? 0.0 : exp_nonpos(double(x) - double(m), tab64);
 }
 
+template <int W = kThreads / 64>
 __device__ __forceinline__ double block_sum_d(double x, double* sm) {
   x = wave_sum_d(x);
   const int wave = threadIdx.x >> 6;
@@ -377,12 +377,12 @@ __device__ __forceinline__ double block_sum_d(double x, double* sm) {
   if ((threadIdx.x & 63) == 0) sm[wave] = x;
   __syncthreads();
   double t = 0.0;
-  for (int w = 0; w < kThreads / 64; ++w) t += sm[w];
+  for (int w = 0; w < W; ++w) t += sm[w];
   return t;
 }
 
-// Workgroup sums of K doubles per thread, with one pair of barriers for all K.
-template <int K>
+// Workgroup sums of K doubles per thread (W waves), with one pair of barriers for all K.
+template <int K, int W = kThreads / 64>
 __device__ __forceinline__ void block_sum_dk(double* x, double (*sm)[K]) {
 #pragma unroll
   for (int i = 0; i < K; ++i) x[i] = wave_sum_d(x[i]);
@@ -395,48 +395,50 @@ __device__ __forceinline__ void block_sum_dk(double* x, double (*sm)[K]) {
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     double t = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) t += sm[w][i];
+    for (int w = 0; w < W; ++w) t += sm[w][i];
     x[i] = t;
   }
 }
 
-// 8 consecutive logits of a p row and of a q row starting at e0 (entries
+// P consecutive logits of a p row and of a q row starting at e0 (entries
 // >= e1 read as -inf), all loads in flight together.  Whole 16-byte aligned
-// runs are one or two vector loads per row; otherwise the indices are clamped
-// into the shard so that every load is unconditional.
-template <typename T>
+// runs are vector loads; otherwise the indices are clamped into the shard so
+// that every load is unconditional.
+template <typename T, int P = kRPer>
 __device__ __forceinline__ void load_runs(const T* __restrict__ prow, const T* __restrict__ qrow, int e0,
                                           int e1, float* xp, float* xq) {
   constexpr int VN = Vec<T>::N;
-  const bool vec = e0 + kRPer <= e1 && ((reinterpret_cast<uintptr_t>(prow + e0) |
-                                         reinterpret_cast<uintptr_t>(qrow + e0)) & 15) == 0;
-  if (vec) {
-    const u32x4* vp = reinterpret_cast<const u32x4*>(prow + e0);
-    const u32x4* vq = reinterpret_cast<const u32x4*>(qrow + e0);
-    u32x4 rp[kRPer / VN], rq[kRPer / VN];
+  if constexpr (P % VN == 0) {
+    const bool vec = e0 + P <= e1 && ((reinterpret_cast<uintptr_t>(prow + e0) |
+                                       reinterpret_cast<uintptr_t>(qrow + e0)) & 15) == 0;
+    if (vec) {
+      const u32x4* vp = reinterpret_cast<const u32x4*>(prow + e0);
+      const u32x4* vq = reinterpret_cast<const u32x4*>(qrow + e0);
+      u32x4 rp[P / VN], rq[P / VN];
 #pragma unroll
-    for (int k = 0; k < kRPer / VN; ++k) {
-      rp[k] = vp[k];
-      rq[k] = vq[k];
-    }
+      for (int k = 0; k < P / VN; ++k) {
+        rp[k] = vp[k];
+        rq[k] = vq[k];
+      }
 #pragma unroll
-    for (int k = 0; k < kRPer / VN; ++k) {
-      unpack(rp[k], xp + k * VN, T());
-      unpack(rq[k], xq + k * VN, T());
+      for (int k = 0; k < P / VN; ++k) {
+        unpack(rp[k], xp + k * VN, T());
+        unpack(rq[k], xq + k * VN, T());
+      }
+      return;
     }
-  } else {
-    T rp[kRPer], rq[kRPer];
+  }
+  T rp[P], rq[P];
 #pragma unroll
-    for (int k = 0; k < kRPer; ++k) {
-      const int e = min(e0 + k, e1 - 1);
-      rp[k] = prow[e];
-      rq[k] = qrow[e];
-    }
+  for (int k = 0; k < P; ++k) {
+    const int e = min(e0 + k, e1 - 1);
+    rp[k] = prow[e];
+    rq[k] = qrow[e];
+  }
 #pragma unroll
-    for (int k = 0; k < kRPer; ++k) {
-      xp[k] = (e0 + k < e1) ? to_f32<T>(rp[k]) : -INFINITY;
-      xq[k] = (e0 + k < e1) ? to_f32<T>(rq[k]) : -INFINITY;
-    }
+  for (int k = 0; k < P; ++k) {
+    xp[k] = (e0 + k < e1) ? to_f32<T>(rp[k]) : -INFINITY;
+    xq[k] = (e0 + k < e1) ? to_f32<T>(rq[k]) : -INFINITY;
   }
 }
 
@@ -679,22 +681,30 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   }
 }
 
-// r(y) = max(0, p(y) - q(y)) and p(y) for 8 consecutive entries
+// r(y) = max(0, p(y) - q(y)) and p(y) for P consecutive entries
+template <int P>
 __device__ __forceinline__ void resid_values(const float* xp, const float* xq, const ReqState& st, double ip,
                                              double iq, const double* tab64, double* rv, double* pv) {
 #pragma unroll
-  for (int i = 0; i < kRPer; ++i) {
+  for (int i = 0; i < P; ++i) {
     const double p = exp_shift(xp[i], st.max_p, tab64) * ip;
     rv[i] = fmax(0.0, p - exp_shift(xq[i], st.max_q, tab64) * iq);
     pv[i] = p;
   }
 }
 
-// One workgroup per listed request: exact shard masses, then the inverse-CDF
-// draw.  A wave-wide prefix over the shard masses picks the shard holding
-// u' * S, a scan inside that shard in vocabulary order picks y*.
+// One workgroup of kSelThreads per listed request: exact shard masses, then
+// the inverse-CDF draw.  A wave-wide prefix over the shard masses picks the
+// shard holding u' * S, a scan inside that shard in vocabulary order picks y*
+// (kSelPer entries per thread: the few selection workgroups have the chip to
+// themselves, so the scan's float64 exponentials are spread over 16 waves).
+constexpr int kSelThreads = 1024;
+constexpr int kSelPer = kRShard / kSelThreads;
+constexpr int kSelWaves = kSelThreads / 64;
+static_assert(kMaxResidShards <= kSelThreads, "one shard record per thread");
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p_logits,
+__global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict__ p_logits,
                                                           const T* __restrict__ q_logits, int N, int V,
                                                           int r_shards, const ReqState* __restrict__ jobs,
                                                           const ResidShard* __restrict__ shards_in,
@@ -703,19 +713,19 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   __shared__ double rmass[kMaxResidShards], pmass[kMaxResidShards];
   __shared__ int redo[kMaxResidShards];
   __shared__ int n_redo_sm;
-  __shared__ double red[kThreads / 64];
+  __shared__ double red[kSelWaves];
   __shared__ double before_sm, target_sm;
   __shared__ int shard_sm, fb_sm;
-  __shared__ int hit_sm[kThreads / 64], last_sm[kThreads / 64];
-  __shared__ double wsum[kThreads / 64];
-  __shared__ double sm2[kThreads / 64][2];
+  __shared__ int hit_sm[kSelWaves], last_sm[kSelWaves];
+  __shared__ double wsum[kSelWaves];
+  __shared__ double sm2[kSelWaves][2];
   // workgroups past the first B (isd_accept_commit only): commit request
   // blockIdx.x - B's accepted rows while the selections run
   if (int(blockIdx.x) >= B) {
     if (cm.kv_bf16)
-      commit_request<uint16_t>(cm, blockIdx.x - B);
+      commit_request<uint16_t, kSelThreads>(cm, blockIdx.x - B);
     else
-      commit_request<float>(cm, blockIdx.x - B);
+      commit_request<float, kSelThreads>(cm, blockIdx.x - B);
     return;
   }
   const int k = blockIdx.x;
@@ -736,11 +746,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   fill_exp_table(tab64);
   // exact row sums and kappa (threads over shards)
   double tot[2] = {mine_ok ? mine.sp : 0.0, mine_ok ? mine.sq : 0.0};
-  for (int i = threadIdx.x + kThreads; i < r_shards; i += kThreads) {
-    tot[0] += recs[i].sp;
-    tot[1] += recs[i].sq;
-  }
-  block_sum_dk<2>(tot, sm2);
+  block_sum_dk<2, kSelWaves>(tot, sm2);
   const double sp = tot[0], sq = tot[1];
   const double kap = sp / sq;
   const bool estimate_ok = fabs(exp(double(st.log_kappa)) / kap - 1.0) < 0.5 * kResidBand;
@@ -759,22 +765,21 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
     }
   };
   if (mine_ok) shard_mass(mine, threadIdx.x);
-  for (int i = threadIdx.x + kThreads; i < r_shards; i += kThreads) shard_mass(recs[i], i);
   __syncthreads();
   // rare: recompute queued shards from the logits
   const int n_redo = n_redo_sm;
   for (int t = 0; t < n_redo; ++t) {
     const int i = redo[t];
     const int e1 = min(V, (i + 1) * kRShard);
-    const int e0 = i * kRShard + threadIdx.x * kRPer;
-    float xp[kRPer], xq[kRPer];
-    load_runs<T>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
-    double rv[kRPer], pv[kRPer];
-    resid_values(xp, xq, st, ip, iq, tab64, rv, pv);
+    const int e0 = i * kRShard + threadIdx.x * kSelPer;
+    float xp[kSelPer], xq[kSelPer];
+    load_runs<T, kSelPer>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
+    double rv[kSelPer], pv[kSelPer];
+    resid_values<kSelPer>(xp, xq, st, ip, iq, tab64, rv, pv);
     double m = 0.0;
 #pragma unroll
-    for (int j = 0; j < kRPer; ++j) m += rv[j];
-    m = block_sum_d(m, red);
+    for (int j = 0; j < kSelPer; ++j) m += rv[j];
+    m = block_sum_d<kSelWaves>(m, red);
     if (threadIdx.x == 0) rmass[i] = m;
     __syncthreads();
   }
@@ -823,15 +828,15 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   const int sh = shard_sm;
   const double target = target_sm;
   const int e1 = min(V, (sh + 1) * kRShard);
-  const int e0 = sh * kRShard + threadIdx.x * kRPer;
-  float xp[kRPer], xq[kRPer];
-  load_runs<T>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
-  double rv[kRPer], pv[kRPer], c[kRPer];
-  resid_values(xp, xq, st, ip, iq, tab64, rv, pv);
+  const int e0 = sh * kRShard + threadIdx.x * kSelPer;
+  float xp[kSelPer], xq[kSelPer];
+  load_runs<T, kSelPer>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
+  double rv[kSelPer], pv[kSelPer], c[kSelPer];
+  resid_values<kSelPer>(xp, xq, st, ip, iq, tab64, rv, pv);
   double run = 0.0;
   int last_here = -1;
 #pragma unroll
-  for (int i = 0; i < kRPer; ++i) {
+  for (int i = 0; i < kSelPer; ++i) {
     const double v = fb_sm ? pv[i] : rv[i];
     if (v > 0.0 && e0 + i < e1) last_here = e0 + i;
     run += v;
@@ -846,7 +851,7 @@ __global__ __launch_bounds__(kThreads) void resid_select(const T* __restrict__ p
   for (int w = 0; w < wave; ++w) before += wsum[w];
   int hit = INT_MAX;
 #pragma unroll
-  for (int i = kRPer - 1; i >= 0; --i)
+  for (int i = kSelPer - 1; i >= 0; --i)
     if (e0 + i < e1 && before + c[i] > target) hit = e0 + i;
   int first_hit, last_nz;
   block_first_last(hit, last_here, hit_sm, last_sm, first_hit, last_nz);
@@ -903,7 +908,7 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   // with a commit, B more workgroups in the selection launch: one per request
   CommitArgs cm{};
   if (commit) cm = *commit;
-  hipLaunchKernelGGL((resid_select<T>), dim3(commit ? 2 * B : B), dim3(kThreads), 0, stream, P, Qp, N, V,
+  hipLaunchKernelGGL((resid_select<T>), dim3(commit ? 2 * B : B), dim3(kSelThreads), 0, stream, P, Qp, N, V,
                      p.r_shards, jobs, rshards, out_tokens, B, cm);
   return hipGetLastError();
 }

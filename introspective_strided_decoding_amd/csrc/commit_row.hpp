@@ -1,9 +1,9 @@
 // Appending accepted stride rows to the KV pages: the device code shared by
 // the kv_commit kernel and the accept launch that also commits.
 //
-// One workgroup of kCommitThreads threads per request r.  The request commits
-// n rows starting at stride row f: row f + t goes to position L + t (L = its
-// length before the commit).  Normally f = 0 and n = n_commit[r] (the accepted
+// One workgroup per request r.  The request commits n rows starting at
+// stride row f: row f + t goes to position L + t (L = its length before the
+// commit).  Normally f = 0 and n = n_commit[r] (the accepted
 // prefix x_1..x_A); a request of the decoding loop in re-proposing mode
 // commits row N-1 only (f = N-1, n = 1), which carries the token its previous
 // forward resampled.  The rows are written only as far as the pages of their
@@ -65,13 +65,14 @@ __device__ __forceinline__ void row_put(u32x4 (&row)[RV], int k, T v) {
   }
 }
 
-// Commit request r's rows; call with all kCommitThreads threads.
+// Commit request r's rows; call with all kT threads of the workgroup (256 in
+// kv_commit, 1024 inside the selection launch).
 constexpr int kCommitPre = 8;        // new tokens whose values a value thread requests with its rows
-constexpr int kCommitRowsPer = 4;    // value rows a thread rewrites in one pass
-constexpr int kCommitKeyItems = 2;   // key items a thread requests before the first store
 
-template <typename T>
+template <typename T, int kT = kCommitThreads>
 __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
+  constexpr int kCommitRowsPer = kT >= 1024 ? 1 : 1024 / kT;   // value rows a thread rewrites in one pass
+  constexpr int kCommitKeyItems = kT >= 512 ? 1 : 512 / kT;    // key items requested before the first store
   constexpr int EV = 16 / int(sizeof(T));      // elements per 16-byte vector
   constexpr int CV = 8 / EV;                   // vectors per 8-dim key cell (1 bf16, 2 fp32)
   constexpr int RV = kPage * int(sizeof(T)) / 16;   // vectors per value-page row (2 bf16, 4 fp32)
@@ -105,7 +106,7 @@ __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
   u32x4 kv[kCommitKeyItems][CV];
 #pragma unroll
   for (int j = 0; j < kCommitKeyItems; ++j) {
-    const int i = min(int(threadIdx.x) + j * kCommitThreads, cells * (t_last + 1) - 1);
+    const int i = min(int(threadIdx.x) + j * kT, cells * (t_last + 1) - 1);
     const u32x4* src = key_src(i / cells, i % cells);
 #pragma unroll
     for (int q = 0; q < CV; ++q) kv[j][q] = src[q];
@@ -114,7 +115,7 @@ __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
   auto load_values = [&](int base) {
 #pragma unroll
     for (int j = 0; j < kCommitRowsPer; ++j) {
-      const int row = min(base + int(threadIdx.x) + j * kCommitThreads, rows - 1);
+      const int row = min(base + int(threadIdx.x) + j * kT, rows - 1);
 #pragma unroll
       for (int t = 0; t < kCommitPre; ++t) x[j][t] = vn[size_t(f + min(t, t_last)) * rows + row];
     }
@@ -143,7 +144,7 @@ __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
     auto load_rows = [&](int base) {
 #pragma unroll
       for (int j = 0; j < kCommitRowsPer; ++j) {
-        const int row = min(base + int(threadIdx.x) + j * kCommitThreads, rows - 1);
+        const int row = min(base + int(threadIdx.x) + j * kT, rows - 1);
         const u32x4* a = reinterpret_cast<const u32x4*>(vp + (size_t(page_a) * rows + row) * kPage);
         const u32x4* b = reinterpret_cast<const u32x4*>(vp + (size_t(page_b) * rows + row) * kPage);
 #pragma unroll
@@ -171,7 +172,7 @@ __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
         const int k = v_sigma((L + t) % kPage);
 #pragma unroll
         for (int j = 0; j < kCommitRowsPer; ++j) {
-          const int row = min(base + int(threadIdx.x) + j * kCommitThreads, rows - 1);
+          const int row = min(base + int(threadIdx.x) + j * kT, rows - 1);
           const T v = vn[size_t(f + t) * rows + row];
           if (t < t_split)
             row_put<T, RV>(ra[j], k, v);
@@ -181,7 +182,7 @@ __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
       }
 #pragma unroll
       for (int j = 0; j < kCommitRowsPer; ++j) {
-        const int row = base + int(threadIdx.x) + j * kCommitThreads;
+        const int row = base + int(threadIdx.x) + j * kT;
         if (row < rows) {
           u32x4* a = reinterpret_cast<u32x4*>(vp + (size_t(page_a) * rows + row) * kPage);
           u32x4* b = reinterpret_cast<u32x4*>(vp + (size_t(page_b) * rows + row) * kPage);
@@ -203,7 +204,7 @@ __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
     };
 #pragma unroll
     for (int j = 0; j < kCommitKeyItems; ++j) {
-      const int i = int(threadIdx.x) + j * kCommitThreads;
+      const int i = int(threadIdx.x) + j * kT;
       if (i < items) {
         u32x4* dst = key_dst(i / cells, i % cells);
 #pragma unroll
@@ -211,7 +212,7 @@ __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
       }
     }
     // more key items than the first passes hold (large heads or many rows)
-    for (int i = int(threadIdx.x) + kCommitKeyItems * kCommitThreads; i < items; i += kCommitThreads) {
+    for (int i = int(threadIdx.x) + kCommitKeyItems * kT; i < items; i += kT) {
       const u32x4* src = key_src(i / cells, i % cells);
       u32x4* dst = key_dst(i / cells, i % cells);
 #pragma unroll
@@ -219,7 +220,7 @@ __device__ __forceinline__ void commit_request(const CommitArgs& c, int r) {
     }
     // ---- values ----
     update_rows(0);
-    for (int base = kCommitRowsPer * kCommitThreads; base < rows; base += kCommitRowsPer * kCommitThreads) {
+    for (int base = kCommitRowsPer * kT; base < rows; base += kCommitRowsPer * kT) {
       load_values(base);   // more value rows than one pass holds (large heads)
       load_rows(base);
       update_rows(base);
