@@ -694,14 +694,42 @@ __device__ __forceinline__ void resid_values(const float* xp, const float* xq, c
 }
 
 // One workgroup of kSelThreads per listed request: exact shard masses, then
-// the inverse-CDF draw.  A wave-wide prefix over the shard masses picks the
-// shard holding u' * S, a scan inside that shard in vocabulary order picks y*
-// (kSelPer entries per thread: the few selection workgroups have the chip to
-// themselves, so the scan's float64 exponentials are spread over 16 waves).
+// the inverse-CDF draw.  Wave 0 alone reads the shard records (lane l owns
+// the shards [l*per, (l+1)*per), in vocabulary order), sums S_p and S_q by
+// lane exchange, turns each record into the shard's exact masses and picks
+// the shard holding u' * S by a wave-wide prefix, while wave 1 fills the
+// exponential's table; after one barrier every thread scans that shard in
+// vocabulary order (kSelPer entries per thread: the few selection workgroups
+// have the chip to themselves, so the scan's float64 exponentials are spread
+// over 16 waves) and the first crossing is y*.
 constexpr int kSelThreads = 1024;
 constexpr int kSelPer = kRShard / kSelThreads;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelRecs = 2;   // records per lane read in one round trip (per <= 2: V <= 262144)
 static_assert(kMaxResidShards <= kSelThreads, "one shard record per thread");
+
+// The head of a shard record: its sums and its first kHeadAmb boundary groups
+// (seven 16-byte vectors; the other groups are read only when a record has them).
+constexpr int kHeadAmb = 4;
+struct RecHead {
+  double sp, sq, a, b;
+  int32_t n_amb, pad;
+  double amb[kHeadAmb][2];
+};
+static_assert(sizeof(ResidShard) % 16 == 0 && (sizeof(RecHead) + 15) / 16 * 16 <= sizeof(ResidShard) &&
+                  offsetof(ResidShard, amb) == offsetof(RecHead, amb),
+              "record heads are read as 16-byte vectors inside the record");
+
+__device__ __forceinline__ RecHead load_head(const ResidShard* rec) {
+  constexpr int NV = (int(sizeof(RecHead)) + 15) / 16;
+  const u32x4* src = reinterpret_cast<const u32x4*>(rec);
+  u32x4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = src[i];
+  RecHead h;
+  __builtin_memcpy(&h, v, sizeof(RecHead));
+  return h;
+}
 
 template <typename T>
 __global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict__ p_logits,
@@ -714,11 +742,10 @@ __global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict_
   __shared__ int redo[kMaxResidShards];
   __shared__ int n_redo_sm;
   __shared__ double red[kSelWaves];
-  __shared__ double before_sm, target_sm;
+  __shared__ double before_sm, target_sm, ip_sm, iq_sm;
   __shared__ int shard_sm, fb_sm;
   __shared__ int hit_sm[kSelWaves], last_sm[kSelWaves];
   __shared__ double wsum[kSelWaves];
-  __shared__ double sm2[kSelWaves][2];
   // workgroups past the first B (isd_accept_commit only): commit request
   // blockIdx.x - B's accepted rows while the selections run
   if (int(blockIdx.x) >= B) {
@@ -731,10 +758,14 @@ __global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict_
   const int k = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const ResidShard* recs = shards_in + size_t(k) * r_shards;
-  // thread t's first shard record is requested together with the list entry
-  const bool mine_ok = threadIdx.x < r_shards;
-  ResidShard mine;
-  if (mine_ok) mine = recs[threadIdx.x];
+  const int per = (r_shards + 63) / 64;
+  const int s0 = min(r_shards, lane * per), s1 = min(r_shards, s0 + per);
+  // wave 0: the heads of its lanes' records requested together with the list entry
+  RecHead rec[kSelRecs];
+  if (wave == 0 && per <= kSelRecs) {
+#pragma unroll
+    for (int j = 0; j < kSelRecs; ++j) rec[j] = load_head(recs + min(s0 + j, r_shards - 1));
+  }
   const ReqState st = jobs[k];
   // all of the entry at once (see resid_pass)
   asm volatile("" ::"s"(st.req), "s"(st.reject_row), "s"(st.log_kappa), "s"(st.max_p), "s"(st.max_q),
@@ -742,56 +773,9 @@ __global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict_
   if (st.req < 0) return;                        // past the listed rejecting requests
   const int r = st.req;
   const size_t row = size_t(r) * (N - 1) + st.reject_row;
-  if (threadIdx.x == 0) n_redo_sm = 0;
-  fill_exp_table(tab64);
-  // exact row sums and kappa (threads over shards)
-  double tot[2] = {mine_ok ? mine.sp : 0.0, mine_ok ? mine.sq : 0.0};
-  block_sum_dk<2, kSelWaves>(tot, sm2);
-  const double sp = tot[0], sq = tot[1];
-  const double kap = sp / sq;
-  const bool estimate_ok = fabs(exp(double(st.log_kappa)) / kap - 1.0) < 0.5 * kResidBand;
-  const double ip = 1.0 / sp, iq = 1.0 / sq;
-  // exact shard masses from the records; shards that cannot be completed are queued
-  auto shard_mass = [&](const ResidShard& rs, int i) {
-    pmass[i] = rs.sp * ip;
-    if (estimate_ok && rs.n_amb <= kResidAmb) {
-      double m = rs.a - kap * rs.b;
-#pragma unroll
-      for (int j = 0; j < kResidAmb; ++j)
-        if (j < rs.n_amb) m += fmax(0.0, rs.amb[j][0] - kap * rs.amb[j][1]);
-      rmass[i] = fmax(0.0, m) * ip;
-    } else {
-      redo[atomicAdd(&n_redo_sm, 1)] = i;
-    }
-  };
-  if (mine_ok) shard_mass(mine, threadIdx.x);
-  __syncthreads();
-  // rare: recompute queued shards from the logits
-  const int n_redo = n_redo_sm;
-  for (int t = 0; t < n_redo; ++t) {
-    const int i = redo[t];
-    const int e1 = min(V, (i + 1) * kRShard);
-    const int e0 = i * kRShard + threadIdx.x * kSelPer;
-    float xp[kSelPer], xq[kSelPer];
-    load_runs<T, kSelPer>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
-    double rv[kSelPer], pv[kSelPer];
-    resid_values<kSelPer>(xp, xq, st, ip, iq, tab64, rv, pv);
-    double m = 0.0;
-#pragma unroll
-    for (int j = 0; j < kSelPer; ++j) m += rv[j];
-    m = block_sum_d<kSelWaves>(m, red);
-    if (threadIdx.x == 0) rmass[i] = m;
-    __syncthreads();
-  }
-  if (wave == 0) {
-    // shard masses in vocabulary order: lane l owns shards [l*per, (l+1)*per)
-    const int per = (r_shards + 63) / 64;
-    const int s0 = min(r_shards, lane * per), s1 = min(r_shards, s0 + per);
-    double rsum = 0.0, psum = 0.0;
-    for (int i = s0; i < s1; ++i) {
-      rsum += rmass[i];
-      psum += pmass[i];
-    }
+  // wave 0: the inverse CDF over the shard masses held in rmass / pmass (this
+  // lane's shards written by this lane, or by every thread after a recompute)
+  auto pick_shard = [&](double rsum, double psum, double* rm, double* pm) {
     double rtot, ptot;
     const double rbefore = wave_exclusive_d(rsum, rtot);
     const double pbefore = wave_exclusive_d(psum, ptot);
@@ -802,7 +786,7 @@ __global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict_
     int pick = -1, last_nz = -1;
     double pick_before = 0.0, last_before = 0.0;
     for (int i = s0; i < s1; ++i) {
-      const double mi = fb ? pmass[i] : rmass[i];
+      const double mi = fb ? pm[i] : rm[i];
       if (mi > 0.0) { last_nz = i; last_before = cum; }
       if (pick < 0 && cum + mi > target) { pick = i; pick_before = cum; }
       cum += mi;
@@ -823,8 +807,102 @@ __global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict_
       if (lane == 0) { shard_sm = sh < 0 ? 0 : sh; before_sm = bf; }
     }
     if (lane == 0) { target_sm = target; fb_sm = fb; }
+  };
+  if (wave == 0) {
+    // exact row sums and kappa
+    double psp = 0.0, psq = 0.0;
+    if (per <= kSelRecs) {
+#pragma unroll
+      for (int j = 0; j < kSelRecs; ++j)
+        if (s0 + j < s1) {
+          psp += rec[j].sp;
+          psq += rec[j].sq;
+        }
+    } else {
+      for (int i = s0; i < s1; ++i) {
+        psp += recs[i].sp;
+        psq += recs[i].sq;
+      }
+    }
+    const double sp = wave_sum_d(psp), sq = wave_sum_d(psq);
+    const double kap = sp / sq;
+    const bool estimate_ok = fabs(exp(double(st.log_kappa)) / kap - 1.0) < 0.5 * kResidBand;
+    const double ip = 1.0 / sp, iq = 1.0 / sq;
+    // exact shard masses from the records; shards that cannot be completed are listed
+    bool needs_redo = false;
+    auto shard_mass = [&](const RecHead& rs, int i, double& rsum, double& psum) {
+      const double pm = rs.sp * ip;
+      pmass[i] = pm;
+      psum += pm;
+      if (estimate_ok && rs.n_amb <= kResidAmb) {
+        double m = rs.a - kap * rs.b;
+#pragma unroll
+        for (int j = 0; j < kHeadAmb; ++j)
+          if (j < rs.n_amb) m += fmax(0.0, rs.amb[j][0] - kap * rs.amb[j][1]);
+        for (int j = kHeadAmb; j < rs.n_amb; ++j)   // groups past the head (rare)
+          m += fmax(0.0, recs[i].amb[j][0] - kap * recs[i].amb[j][1]);
+        const double rm = fmax(0.0, m) * ip;
+        rmass[i] = rm;
+        rsum += rm;
+      } else {
+        needs_redo = true;
+      }
+    };
+    double rsum = 0.0, psum = 0.0;
+    if (per <= kSelRecs) {
+#pragma unroll
+      for (int j = 0; j < kSelRecs; ++j)
+        if (s0 + j < s1) shard_mass(rec[j], s0 + j, rsum, psum);
+    } else {
+      for (int i = s0; i < s1; ++i) shard_mass(load_head(recs + i), i, rsum, psum);
+    }
+    const uint64_t any_redo = __ballot(needs_redo);
+    if (any_redo) {
+      // rare: mark the shards to recompute (each lane its own)
+      for (int i = s0; i < s1; ++i) {
+        const ResidShard* rs = recs + i;
+        redo[i] = !(estimate_ok && rs->n_amb <= kResidAmb);
+      }
+    } else {
+      pick_shard(rsum, psum, rmass, pmass);
+    }
+    if (lane == 0) {
+      ip_sm = ip;
+      iq_sm = iq;
+      n_redo_sm = any_redo ? 1 : 0;
+    }
+  } else if (wave == 1) {
+    tab64[lane] = exp2(double(lane) * (1.0 / 64.0));
   }
   __syncthreads();
+  const double ip = ip_sm, iq = iq_sm;
+  if (n_redo_sm != 0) {
+    // rare: recompute the marked shards' residual masses from the logits, then pick again
+    for (int i = 0; i < r_shards; ++i) {
+      if (!redo[i]) continue;
+      const int e1 = min(V, (i + 1) * kRShard);
+      const int e0 = i * kRShard + threadIdx.x * kSelPer;
+      float xp[kSelPer], xq[kSelPer];
+      load_runs<T, kSelPer>(p_logits + row * V, q_logits + row * V, e0, e1, xp, xq);
+      double rv[kSelPer], pv[kSelPer];
+      resid_values<kSelPer>(xp, xq, st, ip, iq, tab64, rv, pv);
+      double m = 0.0;
+#pragma unroll
+      for (int j = 0; j < kSelPer; ++j) m += rv[j];
+      m = block_sum_d<kSelWaves>(m, red);
+      if (threadIdx.x == 0) rmass[i] = m;
+      __syncthreads();
+    }
+    if (wave == 0) {
+      double rsum = 0.0, psum = 0.0;
+      for (int i = s0; i < s1; ++i) {
+        rsum += rmass[i];
+        psum += pmass[i];
+      }
+      pick_shard(rsum, psum, rmass, pmass);
+    }
+    __syncthreads();
+  }
   const int sh = shard_sm;
   const double target = target_sm;
   const int e1 = min(V, (sh + 1) * kRShard);
@@ -842,13 +920,13 @@ __global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict_
     run += v;
     c[i] = run;
   }
-  // exclusive scan of thread totals (threads in vocabulary order)
+  // exclusive scan of thread totals (threads in vocabulary order); a wave adds
+  // the totals of the waves before it with one lane each
   double wtot;
   const double wbefore = wave_exclusive_d(run, wtot);
   if (lane == 0) wsum[wave] = wtot;
   __syncthreads();
-  double before = before_sm + wbefore;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const double before = before_sm + wbefore + wave_sum_d(lane < wave ? wsum[lane] : 0.0);
   int hit = INT_MAX;
 #pragma unroll
   for (int i = kSelPer - 1; i >= 0; --i)
