@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   float raw_p = 0.f, raw_q = 0.f;
   uint32_t rid32 = 0, pos32 = 0, step32 = a.step;
   float2 qn = make_float2(0.f, 0.f);
+  double u_acc = 0.0, u_res = 0.0;
   if (wave == 0) {
     // indices clamped into range so that every load is unconditional and in flight together
     const int j = min(lane, R - 1);
@@ -128,6 +129,13 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
     rid32 = uint32_t(a.req_ids[r]);
     pos32 = uint32_t(a.positions[r]);
     if (a.step_dev) step32 = uint32_t(a.step_dev[r]);
+    // lane j's uniforms (Philox keyed by request, position L + j + 1 and step),
+    // computed while the partials are in flight: its inputs arrive by the
+    // scalar path, so this long dependent chain waits on none of the vector loads
+    const uint64_t pos = uint64_t(pos32) + uint64_t(j + 1);
+    const Philox4x64Out w = philox4x64_10(uint64_t(rid32), pos, uint64_t(step32), 0, a.seed_lo, a.seed_hi);
+    u_acc = unit_double(w.w[0]);
+    u_res = unit_double(w.w[1]);
     x = __shfl(xl, min(lane + 1, 63));     // lane j < R tests x_{j+2}, proposal j + 1
   }
   const bool in_range = x >= 0 && x < V;
@@ -163,7 +171,6 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   __syncthreads();
   if (wave != 0) return;
   bool reject = false;
-  double u_res = 0.0;
   if (lane < R) {
     const int j = lane;
     const size_t row = size_t(r) * R + j;
@@ -179,11 +186,7 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
     a.logp_sel[row] = lp;
     a.logq_sel[row] = lq;
     const float rho = __expf(lp - lq);
-    const uint64_t pos = uint64_t(pos32) + uint64_t(j + 1);
-    const Philox4x64Out w = philox4x64_10(uint64_t(rid32), pos, uint64_t(step32), 0, a.seed_lo, a.seed_hi);
-    const double u = unit_double(w.w[0]);
-    u_res = unit_double(w.w[1]);
-    reject = !(u < double(rho));
+    reject = !(u_acc < double(rho));
   }
   const uint64_t mask = __ballot(reject);
   const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
