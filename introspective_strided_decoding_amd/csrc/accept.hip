@@ -5,11 +5,13 @@
 //                  the max and the sum of exp(l - max), fp32, 16-byte
 //                  streaming loads, wave reductions by lane exchange, then
 //                  across the 4 waves; the workgroup whose shard holds the
-//                  row's proposal also records the logit there.
+//                  row's proposal also records the logit there, and the
+//                  first workgroup of each request draws its Philox uniforms
+//                  (a long dependent chain, hidden under that workgroup's loads).
 //   accept_decide  one workgroup per request: its waves combine the shard
 //                  partials of the request's rows into log-normalisers while
-//                  the first wave loads the recorded logits at the proposals;
-//                  rho = exp(log p - log q), Philox uniforms, accept iff
+//                  the first wave loads the recorded logits at the proposals
+//                  and the uniforms; rho = exp(log p - log q), accept iff
 //                  u < rho, first rejection by a wave ballot; a rejecting
 //                  request appends its record to a compact list.  (A last-arrival hand-off
 //                  inside the normaliser launch measured slower: its 60-odd
@@ -83,6 +85,7 @@ struct DecideArgs {
   ReqState* jobs;          // compact list of rejecting requests
   uint32_t* rej_count;     // its length
   float* gath;             // per (request, p/q row): the row's logit at its proposal
+  double* unif;            // per (request, stride row j < N-1): Philox uniforms u, u' (two doubles)
   uint32_t* flags;
 };
 
@@ -116,7 +119,6 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
   // wave 0: the proposals and the logits at them, requested before the combine
   int x = 0, xl = 0;
   float raw_p = 0.f, raw_q = 0.f;
-  uint32_t rid32 = 0, pos32 = 0, step32 = a.step;
   float2 qn = make_float2(0.f, 0.f);
   double u_acc = 0.0, u_res = 0.0;
   if (wave == 0) {
@@ -126,16 +128,10 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
     raw_p = a.gath[size_t(r) * 2 * R + j];
     if (a.q_norms) qn = a.q_norms[size_t(r) * N + j + 1];
     else raw_q = a.gath[size_t(r) * 2 * R + R + j];
-    rid32 = uint32_t(a.req_ids[r]);
-    pos32 = uint32_t(a.positions[r]);
-    if (a.step_dev) step32 = uint32_t(a.step_dev[r]);
-    // lane j's uniforms (Philox keyed by request, position L + j + 1 and step),
-    // computed while the partials are in flight: its inputs arrive by the
-    // scalar path, so this long dependent chain waits on none of the vector loads
-    const uint64_t pos = uint64_t(pos32) + uint64_t(j + 1);
-    const Philox4x64Out w = philox4x64_10(uint64_t(rid32), pos, uint64_t(step32), 0, a.seed_lo, a.seed_hi);
-    u_acc = unit_double(w.w[0]);
-    u_res = unit_double(w.w[1]);
+    // lane j's uniforms, drawn by the normaliser kernel
+    const double2 uu = reinterpret_cast<const double2*>(a.unif)[size_t(r) * R + j];
+    u_acc = uu.x;
+    u_res = uu.y;
     x = __shfl(xl, min(lane + 1, 63));     // lane j < R tests x_{j+2}, proposal j + 1
   }
   const bool in_range = x >= 0 && x < V;
@@ -245,6 +241,18 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
 #pragma unroll
       for (int k = 0; k < kLseVec; ++k)
         raw[k] = __builtin_nontemporal_load(vb + min(int(threadIdx.x) + k * kThreads, nvec - 1));
+    }
+    // block (0, r): request r's Philox uniforms (keyed by request, position
+    // L + j + 1 and step) for its rows j < N-1, one lane each, drawn while the
+    // logits are in flight so the decision does not wait for this long chain
+    if (blockIdx.x == 0 && threadIdx.x < 64) {
+      const int j = min(int(threadIdx.x), R - 1);
+      const uint32_t step32 = args.step_dev ? uint32_t(args.step_dev[r]) : args.step;
+      const uint64_t pos = uint64_t(uint32_t(args.positions[r])) + uint64_t(j + 1);
+      const Philox4x64Out w =
+          philox4x64_10(uint64_t(uint32_t(args.req_ids[r])), pos, uint64_t(step32), 0, args.seed_lo, args.seed_hi);
+      if (int(threadIdx.x) < R)
+        reinterpret_cast<double2*>(args.unif)[size_t(r) * R + j] = make_double2(unit_double(w.w[0]), unit_double(w.w[1]));
     }
     // pass 1: max over this thread's values (registers, then the scalar head
     // and tail: rows not 16-byte aligned, shard ends)
@@ -980,6 +988,7 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.jobs = jobs;
   a.rej_count = rej_count;
   a.gath = reinterpret_cast<float*>(ws + L.gath);
+  a.unif = reinterpret_cast<double*>(ws + L.unif);
   a.flags = flags;
   hipLaunchKernelGGL((lse_partial<T>), dim3((q_norms ? 1 : 2) * (N - 1) * p.shards, B), dim3(kThreads), 0, stream,
                      a, p.shard_len, part);

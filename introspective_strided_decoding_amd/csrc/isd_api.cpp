@@ -112,6 +112,8 @@ WsLayout scratch_layout(const isd_shape& s) {
   off = align_up(off + (size_t)s.batch * sizeof(ReqState), 256);
   L.gath = off;
   off = align_up(off + (size_t)c.rows * 4, 256);
+  L.unif = off;
+  off = align_up(off + (size_t)s.batch * (s.stride_n - 1) * 16, 256);
   L.resid = off;
   off = align_up(off + (size_t)s.batch * c.r_shards * sizeof(ResidShard), 256);
   L.total = off;
@@ -236,6 +238,8 @@ WsLayout ws_layout(const isd_shape& s) {
   off = align_up(off + (size_t)s.batch * sizeof(ReqState), 256);
   L.gath = off;
   off = align_up(off + (size_t)c.rows * 4, 256);
+  L.unif = off;
+  off = align_up(off + (size_t)s.batch * (s.stride_n - 1) * 16, 256);
   L.resid = off;
   off = align_up(off + (size_t)s.batch * c.r_shards * sizeof(ResidShard), 256);
   L.prop = off;

@@ -47,6 +47,7 @@ struct WsLayout {
   size_t lse = 0;            // float2 (max, sum) per (row, shard)
   size_t jobs = 0;           // ReqState per rejecting request, compacted
   size_t gath = 0;           // float per (request, p/q row): the logit at the row's proposal
+  size_t unif = 0;           // double pair per (request, stride row j < N-1): the Philox uniforms (u, u')
   size_t resid = 0;          // ResidShard per (listed request, residual shard)
   size_t prop = 0;           // PropPart per (MASK row, proposal shard)
   size_t total = 0;
