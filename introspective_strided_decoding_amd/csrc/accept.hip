@@ -376,8 +376,11 @@ __device__ __forceinline__ void fill_exp_table(double* tab64) {
   __syncthreads();
 }
 
+// exp(x - m) for x <= m; x = -inf gives 0 without a test (exp_nonpos clamps the
+// argument to -746, whose result underflows to 0), and so does an all -inf row (m = -inf:
+// the NaN difference is clamped the same way)
 __device__ __forceinline__ double exp_shift(float x, float m, const double* tab64) {
-  return (x == -INFINITY) ? 0.0 : exp_nonpos(double(x) - double(m), tab64);
+  return exp_nonpos(double(x) - double(m), tab64);
 }
 
 template <int W = kThreads / 64>

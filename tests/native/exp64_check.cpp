@@ -28,6 +28,8 @@ int main() {
   std::printf("exp0 %.17g\n", isd::exp_nonpos(0.0, tab));
   std::printf("exp_minus_tiny %.17g\n", isd::exp_nonpos(-1e-300, tab));
   std::printf("exp_minus_inf %.17g\n", isd::exp_nonpos(-INFINITY, tab));
+  // the difference of two -inf logits (a row with no finite entry) is NaN: also 0
+  std::printf("exp_nan %.17g\n", isd::exp_nonpos(-INFINITY - -INFINITY, tab));
   std::printf("exp_minus_800 %.17g\n", isd::exp_nonpos(-800.0, tab));
   std::printf("exp_minus_745_3 %.17g\n", isd::exp_nonpos(-745.3, tab));
   std::printf("exp_minus_1 %.17g %.17g\n", isd::exp_nonpos(-1.0, tab), std::exp(-1.0));

@@ -4,7 +4,7 @@ The proposal sampler sums exp(logit - max) in float64 with a table-driven
 exp of its own; its draws agree with a float64 inverse CDF only if that exp
 is accurate to a few units in the last place.  This sweep compares it with
 the C library's exp over [-746, 0] (4 million points) and checks the special
-cases: exp(0) = 1 exactly, -inf and arguments past the underflow threshold
+cases: exp(0) = 1 exactly, -inf, NaN (the difference of two -inf logits) and arguments past the underflow threshold
 give 0, results in the subnormal range are within two subnormal steps.
 """
 
@@ -43,6 +43,7 @@ def test_special_cases(sweep):
     assert sweep["exp0"][0] == 1.0
     assert sweep["exp_minus_tiny"][0] == 1.0
     assert sweep["exp_minus_inf"][0] == 0.0
+    assert sweep["exp_nan"][0] == 0.0
     assert sweep["exp_minus_800"][0] == 0.0
     assert sweep["exp_minus_745_3"][0] == 0.0        # below half the smallest subnormal
     a, b = sweep["exp_minus_1"]
