@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
   int last_here = -1;
 #pragma unroll
   for (int i = 0; i < kPPer; ++i) {
-    const double v = (x[i] == -INFINITY) ? 0.0 : exp_nonpos(double(x[i]) - ms, tab64) * scale;
+    const double v = exp_nonpos(double(x[i]) - ms, tab64) * scale;   // -inf entries give 0
     if (v > 0.0) last_here = e0 + i;
     run += v;
     c[i] = run;
