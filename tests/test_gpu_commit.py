@@ -27,6 +27,8 @@ def _unpacked(st):
     ("b8_ctx2k", dict(batch=4, ctx=0, vocab=64)),
     ("c64_ragged", dict(batch=6, ctx_range=(1, 100), vocab=64)),
     ("b8_ctx2k", dict(batch=2, ctx=40, vocab=64, head_dim=64)),
+    ("b8_ctx2k", dict(batch=3, ctx=37, vocab=64, stride_n=16, n_q_heads=16, n_kv_heads=8)),   # up to 16 rows: past the 8 requested up front
+    ("b8_ctx2k", dict(batch=2, ctx=5, vocab=64, n_q_heads=32, n_kv_heads=16)),   # 2048 value rows per page
 ])
 @pytest.mark.parametrize("in_place", [False, True])
 def test_commit_matches_oracle(name, over, in_place):
@@ -93,6 +95,9 @@ def _bits(t):
     ("b8_ctx2k", dict(batch=5, ctx=14, vocab=4099, stride_n=5), True),
     ("tiny_fp32", dict(batch=4, ctx=13, vocab=1000), True),
     ("c64_ragged", dict(batch=7, ctx_range=(1, 100), vocab=2048), True),
+    # N = 16 (commits past the 8 rows a thread requests up front) and 2048 value rows
+    # per page (two passes of the selection launch's 1024 commit threads)
+    ("b8_ctx2k", dict(batch=3, ctx=21, vocab=512, stride_n=16, n_q_heads=32, n_kv_heads=16), True),
 ])
 def test_accept_commit_equals_accept_then_commit(name, over, in_place):
     """isd_accept_commit leaves every output, the pools and the lengths exactly as
@@ -104,11 +109,13 @@ def test_accept_commit_equals_accept_then_commit(name, over, in_place):
     a = device_step(wl, commit_in_place=in_place)
     b = device_step(wl, commit_in_place=in_place)
     k_ref, v_ref, lens = wl.k_pool, wl.v_pool, wl.ctx_lens.copy()
+    most = 0
     for step in range(steps):
         a.accept(step=step)
         a.commit()
         b.accept_commit(step=step)
         torch.cuda.synchronize()
+        most = max(most, int(b.n_commit.max()))
         for f in ("accept_len", "out_tokens", "n_out", "n_commit", "logp_sel", "logq_sel", "ctx_lens_out"):
             assert torch.equal(_bits(getattr(a, f)), _bits(getattr(b, f))), (step, f)
         assert torch.equal(_bits(a.k_pages), _bits(b.k_pages)), step
@@ -121,6 +128,8 @@ def test_accept_commit_equals_accept_then_commit(name, over, in_place):
     k_got, v_got = _unpacked(b)
     assert np.array_equal(k_got, k_ref)
     assert np.array_equal(v_got, v_ref)
+    if cfg.stride_n == 16:
+        assert most > 8   # some request committed past the rows requested up front
     from introspective_strided_decoding_amd import isd_read_flags
     assert isd_read_flags(a.workspace) == 0 and isd_read_flags(b.workspace) == 0
 
