@@ -8,20 +8,28 @@
 //                  row's proposal also records the logit there, and the
 //                  first workgroup of each request draws its Philox uniforms
 //                  (a long dependent chain, hidden under that workgroup's loads).
-//   accept_decide  one workgroup per request: its waves combine the shard
-//                  partials of the request's rows into log-normalisers while
-//                  the first wave loads the recorded logits at the proposals
-//                  and the uniforms; rho = exp(log p - log q), accept iff
-//                  u < rho, first rejection by a wave ballot; a rejecting
-//                  request appends its record to a compact list.  (A last-arrival hand-off
-//                  inside the normaliser launch measured slower: its 60-odd
-//                  arrivals per request counter serialise.)
-//   resid_pass     rejecting requests only, one pass over the rejected p
-//                  and q rows, sharded finely over the vocabulary: fp64 sums
-//                  of e_p = exp(l_p - max p) and e_q = exp(l_q - max q) (the
-//                  row maxima come exact from the decision), and the
-//                  residual's pieces under the decision's fp32 estimate of
-//                  the normaliser ratio (see below).
+//   accept_decide  (larger batches) one workgroup per request: its waves
+//                  combine the shard partials of the request's rows into
+//                  log-normalisers while the first wave loads the recorded
+//                  logits at the proposals and the uniforms; rho = exp(log p -
+//                  log q), accept iff u < rho, first rejection by a wave
+//                  ballot; a rejecting request appends its job to a compact
+//                  list.  (A last-arrival hand-off inside the normaliser
+//                  launch measured slower: its 60-odd arrivals per request
+//                  counter serialise.)
+//   resid_pass     (larger batches) rejecting requests only, one pass over
+//                  the rejected p and q rows, sharded finely over the
+//                  vocabulary: fp64 sums of e_p = exp(l_p - max p) and e_q =
+//                  exp(l_q - max q) (the row maxima come exact from the
+//                  decision), and the residual's pieces under the decision's
+//                  fp32 estimate of the normaliser ratio (see below).
+//   decide_resid_pass
+//                  (small batches, instead of the two above) grid (residual
+//                  shards, requests): every workgroup makes its request's
+//                  decision as accept_decide does (the request's first
+//                  workgroup stores the results and the job at the request's
+//                  slot) and, if the request rejected, serves its shard of
+//                  the residual pass; one launch and one dependent read fewer.
 //   resid_select   per rejecting request: exact shard masses from those
 //                  pieces, a prefix over them picks the shard holding
 //                  u' * S, a workgroup scan inside that shard in vocabulary
@@ -29,11 +37,7 @@
 //                  request writes its accepted rows to the KV pages beside the
 //                  selections.
 // The residual runs in fp64 so the inverse CDF agrees with a float64
-// reference up to rounding of the running sums.  The decision lists the
-// rejecting requests compactly (an atomic counter the normaliser kernel
-// rewinds, and the normaliser marks every entry empty first), so the residual
-// workgroups that have work are the first ones dispatched; the rest return
-// after reading their empty entry.
+// reference up to rounding of the running sums.
 #include <climits>
 
 #include "commit_row.hpp"
@@ -82,8 +86,8 @@ struct DecideArgs {
   int N, V, shards;
   int32_t *accept_len, *out_tokens, *n_out, *n_commit;
   float *logp_sel, *logq_sel;
-  ReqState* jobs;          // compact list of rejecting requests
-  uint32_t* rej_count;     // its length
+  ReqState* jobs;          // jobs: a compact list of rejecting requests (decision launch) or one per request
+  uint32_t* rej_count;     // the compact list's length
   float* gath;             // per (request, p/q row): the row's logit at its proposal
   double* unif;            // per (request, stride row j < N-1): Philox uniforms u, u' (two doubles)
   uint32_t* flags;
@@ -93,23 +97,33 @@ struct DecideArgs {
 // of its 16-byte loads before it waits on any of them.
 constexpr int kLseVec = 8;
 
-// One workgroup per request.  Lane j < N-1 of wave 0 tests x_{j+2} against
-// p row j and q row j (their logits there were recorded by the normaliser
-// kernel); a ballot finds the first rejection.
+// The accept decision for request r, made by each workgroup of the residual
+// launch that serves the request (what it reads, the shard partials, the
+// logits at the proposals and the uniforms, is a few hundred bytes in L2).
+// Every wave combines rows of shard partials into log-normalisers; lane
+// j < N-1 of wave 0 tests x_{j+2} against p row j and q row j (their logits
+// there were recorded by the normaliser kernel) and a ballot finds the first
+// rejection.  With write_out the workgroup also stores the request's results
+// and its job: appended to the compact list when it rejected (append), else
+// at the request's own slot.  Every thread gets the job (req = -1: nothing
+// rejected).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const float2* __restrict__ part) {
-  const int r = blockIdx.x;
+__device__ __forceinline__ ReqState decide_request(const DecideArgs<T>& a, const float2* __restrict__ part, int r,
+                                                   bool write_out, bool append) {
   const int N = a.N, V = a.V, R = N - 1, shards = a.shards;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float lse_sm[64], max_sm[64];
+  __shared__ ReqState job_sm;
   // every wave: the shard partials of rows wave, wave + 4, ... of the request's
-  // 2(N-1) rows (p rows only when the q normalisers are carried), at most 8 rows
-  // for N <= 16; with one shard per lane they are all requested first
+  // 2(N-1) rows (p rows only when the q normalisers are carried); with one
+  // shard per lane and at most 4 rows per wave (N <= 9) they are all requested
+  // first, otherwise row by row
   const float2* req_part = part + size_t(r) * 2 * R * shards;
   const int n_rows = a.q_norms ? R : 2 * R;
-  constexpr int kRowsPerWave = 8;
+  constexpr int kRowsPerWave = 4;
+  const bool one_pass = shards <= 64 && n_rows <= kRowsPerWave * (kThreads / 64);
   float2 pre[kRowsPerWave];
-  if (shards <= 64) {
+  if (one_pass) {
 #pragma unroll
     for (int k = 0; k < kRowsPerWave; ++k) {
       const int row = min(wave + k * (kThreads / 64), n_rows - 1);
@@ -148,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
     const float S = wave_sum((rm == -INFINITY) ? 0.f : rs * __expf(rm - M));
     if (lane == 0) { lse_sm[row] = M + __logf(S); max_sm[row] = M; }
   };
-  if (shards <= 64) {
+  if (one_pass) {
 #pragma unroll
     for (int k = 0; k < kRowsPerWave; ++k) {
       const int row = wave + k * (kThreads / 64);
@@ -165,46 +179,68 @@ __global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const
     }
   }
   __syncthreads();
-  if (wave != 0) return;
-  bool reject = false;
-  if (lane < R) {
-    const int j = lane;
-    const size_t row = size_t(r) * R + j;
-    float lp, lq;
-    if (!in_range) {
-      raise_flag(a.flags, ISD_FLAG_TOKEN_RANGE);
-      lp = -INFINITY;
-      lq = 0.f;
-    } else {
-      lp = raw_p - lse_sm[j];
-      lq = raw_q - lse_sm[R + j];
+  if (wave == 0) {
+    bool reject = false;
+    if (lane < R) {
+      const int j = lane;
+      const size_t row = size_t(r) * R + j;
+      float lp, lq;
+      if (!in_range) {
+        if (write_out) raise_flag(a.flags, ISD_FLAG_TOKEN_RANGE);
+        lp = -INFINITY;
+        lq = 0.f;
+      } else {
+        lp = raw_p - lse_sm[j];
+        lq = raw_q - lse_sm[R + j];
+      }
+      if (write_out) {
+        a.logp_sel[row] = lp;
+        a.logq_sel[row] = lq;
+      }
+      const float rho = __expf(lp - lq);
+      reject = !(u_acc < double(rho));
     }
-    a.logp_sel[row] = lp;
-    a.logq_sel[row] = lq;
-    const float rho = __expf(lp - lq);
-    reject = !(u_acc < double(rho));
-  }
-  const uint64_t mask = __ballot(reject);
-  const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
-  const int A = (first < 0) ? N : first + 1;
-  const double u_first = __shfl(u_res, first < 0 ? 0 : first);
-  if (lane < N) a.out_tokens[size_t(r) * N + lane] = (lane < A) ? xl : -1;
-  if (lane == 0) {
-    a.accept_len[r] = A;
-    a.n_out[r] = A + (A < N ? 1 : 0);
-    a.n_commit[r] = A;                  // rows 0..A-1 hold the accepted prefix
-    if (first >= 0) {
+    const uint64_t mask = __ballot(reject);
+    const int first = mask ? (__ffsll((unsigned long long)mask) - 1) : -1;
+    const int A = (first < 0) ? N : first + 1;
+    const double u_first = __shfl(u_res, first < 0 ? 0 : first);
+    if (write_out && lane < N) a.out_tokens[size_t(r) * N + lane] = (lane < A) ? xl : -1;
+    if (lane == 0) {
+      const int fr = first < 0 ? 0 : first;
       ReqState st;
-      st.req = r;
+      st.req = first < 0 ? -1 : r;
       st.accept_len = A;
-      st.reject_row = first;
-      st.log_kappa = (lse_sm[first] - max_sm[first]) - (lse_sm[R + first] - max_sm[R + first]);
-      st.max_p = max_sm[first];
-      st.max_q = max_sm[R + first];
+      st.reject_row = fr;
+      st.log_kappa = (lse_sm[fr] - max_sm[fr]) - (lse_sm[R + fr] - max_sm[R + fr]);
+      st.max_p = max_sm[fr];
+      st.max_q = max_sm[R + fr];
       st.u_resample = u_first;
-      a.jobs[atomicAdd(a.rej_count, 1u)] = st;
+      job_sm = st;
+      if (write_out) {
+        a.accept_len[r] = A;
+        a.n_out[r] = A + (A < N ? 1 : 0);
+        a.n_commit[r] = A;                  // rows 0..A-1 hold the accepted prefix
+        if (!append)
+          a.jobs[r] = st;
+        else if (first >= 0)
+          a.jobs[atomicAdd(a.rej_count, 1u)] = st;
+      }
     }
   }
+  __syncthreads();
+  // wave-uniform copies (scalar registers), so the caller's branch on req and
+  // the addresses it forms from the job stay scalar
+  ReqState st;
+  st.req = __builtin_amdgcn_readfirstlane(job_sm.req);
+  st.accept_len = __builtin_amdgcn_readfirstlane(job_sm.accept_len);
+  st.reject_row = __builtin_amdgcn_readfirstlane(job_sm.reject_row);
+  st.log_kappa = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, job_sm.log_kappa)));
+  st.max_p = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, job_sm.max_p)));
+  st.max_q = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, job_sm.max_q)));
+  const long long u = __builtin_bit_cast(long long, job_sm.u_resample);
+  st.u_resample = __builtin_bit_cast(double, (long long)((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(int(u)) |
+                                                         ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(int(u >> 32)) << 32)));
+  return st;
 }
 
 // Grid (n_rows * shards, B), n_rows = 2(N-1) (p rows, then q rows) or N-1
@@ -332,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
     float M = -INFINITY, S = 0.f;
     for (int w = 0; w < kThreads / 64; ++w) ms_merge(M, S, sm[w][0], sm[w][1]);
     part[(size_t(r) * 2 * R + jj) * shards + sh] = make_float2(M, S);
-    // the decision kernel, next in the stream, lists rejecting requests from zero
+    // a decision launch, next in the stream, lists rejecting requests from zero
     if (blockIdx.x == 0 && blockIdx.y == 0) *args.rej_count = 0u;
   }
   // and every list entry it does not fill reads as empty (req = -1), so the
@@ -343,13 +379,13 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
 }
 
 // ---- fp64 residual ----
-// Residual workgroup (shard, k) serves the k-th listed rejecting request; its
-// list entry alone says whether there is one (an unfilled entry has req = -1;
-// the selection kernel requests its shard records together with the entry).  A residual shard is 2048 vocabulary entries: 256
+// Residual workgroup (shard, r) serves request r once its decision found a
+// rejection; the selection kernel requests its shard records together with
+// the request's job.  A residual shard is 2048 vocabulary entries: 256
 // threads x 8 consecutive entries.
 //
 // Every value is e = exp(l - m) in float64 with m the row's exact max (carried
-// in the list entry), by the table-driven exp_nonpos (its 64-entry table in
+// in the job), by the table-driven exp_nonpos (its 64-entry table in
 // LDS), so both kernels recompute exactly the same values.  With
 // S_p = sum e_p, S_q = sum e_q and kappa = S_p / S_q, the residual is
 // r(y) = max(0, e_p - kappa e_q) / S_p.  kappa is only known once every shard
@@ -456,11 +492,11 @@ __device__ __forceinline__ void load_runs(const T* __restrict__ prow, const T* _
   }
 }
 
+// Shard sh of job st's residual (k: where its records go); call with all threads.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_logits,
-                                                        const T* __restrict__ q_logits, int N, int V,
-                                                        int r_shards, const ReqState* __restrict__ jobs,
-                                                        ResidShard* __restrict__ shard_out) {
+__device__ __forceinline__ void resid_shard(const T* __restrict__ p_logits, const T* __restrict__ q_logits, int N,
+                                            int V, int r_shards, const ReqState& st, int k, int sh,
+                                            ResidShard* __restrict__ shard_out) {
   __shared__ double tab64[64];
   __shared__ double sm4[kThreads / 64][4];
   // entries near the boundary, listed as they are found (rare): exact logit
@@ -475,14 +511,6 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   __shared__ unsigned long long cls_bits[kResidAmb];
   __shared__ float shift_sm[2];
   __shared__ double sm2[kThreads / 64][2];
-  const int sh = blockIdx.x;
-  const int k = blockIdx.y;
-  const ReqState st = jobs[k];
-  // all of the entry is requested at once, not the gating field first and the
-  // rest after the test (the empty asm keeps the compiler from sinking them)
-  asm volatile("" ::"s"(st.req), "s"(st.reject_row), "s"(st.log_kappa), "s"(st.max_p), "s"(st.max_q),
-               "s"(p_logits), "s"(q_logits));
-  if (st.req < 0) return;                        // past the listed rejecting requests
   const size_t row = size_t(st.req) * (N - 1) + st.reject_row;
   const int e1 = min(V, (sh + 1) * kRShard);
   const int e0 = sh * kRShard + threadIdx.x * kRPer;
@@ -695,6 +723,44 @@ __global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_l
   }
 }
 
+// The decision launch: one workgroup per request; a rejecting request appends
+// its job to the compact list.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void accept_decide(DecideArgs<T> a, const float2* __restrict__ part) {
+  decide_request(a, part, blockIdx.x, true, true);
+}
+
+// Grid (residual shards, list length B) after a decision launch: workgroup
+// (sh, k) serves the k-th listed rejecting request, so the workgroups with
+// work are the first ones dispatched; the rest return after reading their
+// empty entry.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void resid_pass(const T* __restrict__ p_logits, const T* __restrict__ q_logits,
+                                                        int N, int V, int r_shards, const ReqState* __restrict__ jobs,
+                                                        ResidShard* __restrict__ shard_out) {
+  const ReqState st = jobs[blockIdx.y];
+  // all of the entry is requested at once, not the gating field first and the
+  // rest after the test (the empty asm keeps the compiler from sinking them)
+  asm volatile("" ::"s"(st.req), "s"(st.reject_row), "s"(st.log_kappa), "s"(st.max_p), "s"(st.max_q),
+               "s"(p_logits), "s"(q_logits));
+  if (st.req < 0) return;                        // past the listed rejecting requests
+  resid_shard<T>(p_logits, q_logits, N, V, r_shards, st, blockIdx.y, blockIdx.x, shard_out);
+}
+
+// Grid (residual shards, requests) with the decision inside: every workgroup
+// makes its request's decision (the request's first workgroup stores the
+// results and the job at the request's slot), then serves shard sh of the
+// residual if the request rejected.  Chosen for small batches, whose grid
+// leaves room for the repeated decisions (see plan_accept).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void decide_resid_pass(DecideArgs<T> args, const float2* __restrict__ part,
+                                                               int r_shards, ResidShard* __restrict__ shard_out) {
+  const int sh = blockIdx.x, r = blockIdx.y;
+  const ReqState st = decide_request(args, part, r, sh == 0, false);
+  if (st.req < 0) return;                        // nothing rejected: no residual
+  resid_shard<T>(args.p_logits, args.q_logits, args.N, args.V, r_shards, st, r, sh, shard_out);
+}
+
 // r(y) = max(0, p(y) - q(y)) and p(y) for P consecutive entries
 template <int P>
 __device__ __forceinline__ void resid_values(const float* xp, const float* xq, const ReqState& st, double ip,
@@ -707,7 +773,8 @@ __device__ __forceinline__ void resid_values(const float* xp, const float* xq, c
   }
 }
 
-// One workgroup of kSelThreads per listed request: exact shard masses, then
+// One workgroup of kSelThreads per request (those that rejected nothing
+// return after reading their job): exact shard masses, then
 // the inverse-CDF draw.  Wave 0 alone reads the shard records (lane l owns
 // the shards [l*per, (l+1)*per), in vocabulary order), sums S_p and S_q by
 // lane exchange, turns each record into the shard's exact masses and picks
@@ -774,17 +841,18 @@ __global__ __launch_bounds__(kSelThreads) void resid_select(const T* __restrict_
   const ResidShard* recs = shards_in + size_t(k) * r_shards;
   const int per = (r_shards + 63) / 64;
   const int s0 = min(r_shards, lane * per), s1 = min(r_shards, s0 + per);
-  // wave 0: the heads of its lanes' records requested together with the list entry
+  // wave 0: the heads of its lanes' records requested together with the job
   RecHead rec[kSelRecs];
   if (wave == 0 && per <= kSelRecs) {
 #pragma unroll
     for (int j = 0; j < kSelRecs; ++j) rec[j] = load_head(recs + min(s0 + j, r_shards - 1));
   }
   const ReqState st = jobs[k];
-  // all of the entry at once (see resid_pass)
+  // all of the job at once (the empty asm keeps the compiler from requesting the
+  // gating field first and the rest after the test)
   asm volatile("" ::"s"(st.req), "s"(st.reject_row), "s"(st.log_kappa), "s"(st.max_p), "s"(st.max_q),
                "s"(st.accept_len), "s"(st.u_resample));
-  if (st.req < 0) return;                        // past the listed rejecting requests
+  if (st.req < 0) return;                        // the request rejected nothing
   const int r = st.req;
   const size_t row = size_t(r) * (N - 1) + st.reject_row;
   // wave 0: the inverse CDF over the shard masses held in rmass / pmass (this
@@ -966,8 +1034,8 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   const int N = s.stride_n, V = s.vocab, B = s.batch;
   float2* part = reinterpret_cast<float2*>(ws + L.lse);
   ReqState* jobs = reinterpret_cast<ReqState*>(ws + L.jobs);
-  uint32_t* rej_count = reinterpret_cast<uint32_t*>(ws + kRejCountOffset);
   ResidShard* rshards = reinterpret_cast<ResidShard*>(ws + L.resid);
+  uint32_t* rej_count = reinterpret_cast<uint32_t*>(ws + kRejCountOffset);
   DecideArgs<T> a;
   a.p_logits = P;
   a.q_logits = Qp;
@@ -995,9 +1063,14 @@ hipError_t launch_t(const isd_shape& s, const AcceptPlan& p, const void* pl, con
   a.flags = flags;
   hipLaunchKernelGGL((lse_partial<T>), dim3((q_norms ? 1 : 2) * (N - 1) * p.shards, B), dim3(kThreads), 0, stream,
                      a, p.shard_len, part);
-  hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
-  hipLaunchKernelGGL((resid_pass<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards,
-                     jobs, rshards);
+  if (p.fuse_decision) {
+    hipLaunchKernelGGL((decide_resid_pass<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, a, part, p.r_shards,
+                       rshards);
+  } else {
+    hipLaunchKernelGGL((accept_decide<T>), dim3(B), dim3(kThreads), 0, stream, a, part);
+    hipLaunchKernelGGL((resid_pass<T>), dim3(p.r_shards, B), dim3(kThreads), 0, stream, P, Qp, N, V, p.r_shards,
+                       jobs, rshards);
+  }
   // with a commit, B more workgroups in the selection launch: one per request
   CommitArgs cm{};
   if (commit) cm = *commit;

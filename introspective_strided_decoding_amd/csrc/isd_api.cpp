@@ -216,6 +216,12 @@ AcceptPlan plan_accept(const isd_shape& s) {
   // the fp64 residual works on 2048-element shards (256 threads x 8 entries)
   p.r_shard_len = 2048;
   p.r_shards = ceil_div(V, p.r_shard_len);
+  // The decision inside the residual pass saves a launch and the pass's dependent
+  // read of the job, at the price of every pass workgroup repeating its
+  // request's decision (~2 us): measured ahead where the pass grid stays
+  // within four workgroups per CU (b8_ctx2k, 600 workgroups: +4 %), behind
+  // where it takes more than one resident round (c32_ctx4k -1 %, c128_lora -3.6 %).
+  p.fuse_decision = (size_t)s.batch * p.r_shards <= (size_t)4 * device_cus() ? 1 : 0;
   return p;
 }
 

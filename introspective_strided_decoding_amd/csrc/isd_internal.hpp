@@ -36,6 +36,7 @@ struct AcceptPlan {
   int shard_len;        // elements per shard (multiple of 8)
   int r_shards;         // shards per row for the fp64 residual
   int r_shard_len;
+  int fuse_decision;    // 1: every residual workgroup makes its request's decision (no decision launch)
 };
 
 struct WsLayout {
@@ -45,19 +46,21 @@ struct WsLayout {
   size_t attn_ml = 0;        // float2 (m, l) per partial row
   size_t attn_o = 0;         // float [D] per partial row
   size_t lse = 0;            // float2 (max, sum) per (row, shard)
-  size_t jobs = 0;           // ReqState per rejecting request, compacted
+  size_t jobs = 0;           // ReqState per request (or per listed rejecting request)
   size_t gath = 0;           // float per (request, p/q row): the logit at the row's proposal
   size_t unif = 0;           // double pair per (request, stride row j < N-1): the Philox uniforms (u, u')
-  size_t resid = 0;          // ResidShard per (listed request, residual shard)
+  size_t resid = 0;          // ResidShard per (request, residual shard)
   size_t prop = 0;           // PropPart per (MASK row, proposal shard)
   size_t total = 0;
 };
 
 // Header word (uint32 at this byte offset of the workspace).
-constexpr size_t kRejCountOffset = 4;     // entries in the list of rejecting requests
+constexpr size_t kRejCountOffset = 4;     // entries in the compact list of rejecting requests
 
-// One entry of the list of rejecting requests, handed from the accept
-// decision to the residual kernels.
+// One request's job, written by the accept decision (req = -1: nothing
+// rejected) and read by the residual kernels: either a compact list of the
+// rejecting requests (a decision launch of its own) or one slot per request
+// (the decision inside the residual pass).
 struct ReqState {
   int32_t req;          // request index r
   int32_t accept_len;   // A
@@ -68,7 +71,7 @@ struct ReqState {
   double u_resample;    // u' of the rejected position
 };
 
-// Residual pass output per (listed request, 2048-entry shard): float64 sums
+// Residual pass output per (request, 2048-entry shard): float64 sums
 // of e_p = exp(l_p - max p) and e_q, the same over the entries clearly in the
 // residual's support under the estimated ratio, and the same again for each
 // group of entries near its boundary that share one exact logit difference.
