@@ -379,10 +379,11 @@ __global__ __launch_bounds__(kThreads) void lse_partial(DecideArgs<T> args, int 
 }
 
 // ---- fp64 residual ----
-// Residual workgroup (shard, r) serves request r once its decision found a
-// rejection; the selection kernel requests its shard records together with
-// the request's job.  A residual shard is 2048 vocabulary entries: 256
-// threads x 8 consecutive entries.
+// Residual workgroup (shard, k) serves job k (the k-th listed rejecting
+// request after a decision launch, request k when the decision runs inside
+// the pass) and writes its record at k; the selection kernel requests its
+// shard records together with the job.  A residual shard is 2048 vocabulary
+// entries: 256 threads x 8 consecutive entries.
 //
 // Every value is e = exp(l - m) in float64 with m the row's exact max (carried
 // in the job), by the table-driven exp_nonpos (its 64-entry table in
@@ -773,8 +774,8 @@ __device__ __forceinline__ void resid_values(const float* xp, const float* xq, c
   }
 }
 
-// One workgroup of kSelThreads per request (those that rejected nothing
-// return after reading their job): exact shard masses, then
+// One workgroup of kSelThreads per job (entry k of the compact list, or
+// request k; an empty job, req = -1, returns at once): exact shard masses, then
 // the inverse-CDF draw.  Wave 0 alone reads the shard records (lane l owns
 // the shards [l*per, (l+1)*per), in vocabulary order), sums S_p and S_q by
 // lane exchange, turns each record into the shard's exact masses and picks
