@@ -202,14 +202,27 @@ class DeviceStep:
             s = self.extra["side_stream"] = (torch.cuda.Stream(device=dev), torch.cuda.Event(), torch.cuda.Event())
         return s
 
-    def _accept_and_propose(self, accept_fn, stream, step: Optional[int], overlap: bool,
+    def side_by_side(self) -> bool:
+        """Whether the proposals run beside the accept chain on a second stream by default.
+
+        Issued eagerly, the fork and the join cost the queues 5-7 us of idle time per
+        forward (measured on MI355X), which only proposals over many logits repay: side by
+        side from 16 M MASK-row logits on (c32_ctx4k, 128 rows of 151 936: 6990 against 6665
+        forwards/s), one after the other below (b8_ctx2k 17.0 k against 12.2 k, tiny_fp32
+        20.8 k against 11.3 k forwards/s)."""
+        return self.shape.batch * self.shape.stride_n * self.shape.vocab >= 16 * 2**20
+
+    def _accept_and_propose(self, accept_fn, stream, step: Optional[int], overlap: Optional[bool],
                             device_step: bool = False, row_norms=None):
-        """The accept chain on ``stream`` and the proposals on a second stream, joined after.
+        """The accept chain on ``stream`` and the proposals on a second stream, joined after
+        (``overlap``; None: ``side_by_side()``), or both on ``stream``.
 
         Both read this forward's logits and neither writes what the other reads
         (their workspace regions are disjoint), so they may run side by side; the
         proposals still start only after everything enqueued before on ``stream``.
         """
+        if overlap is None:
+            overlap = self.side_by_side()
         if overlap and (stream is None or isinstance(stream, torch.cuda.Stream)):
             main = torch.cuda.current_stream() if stream is None else stream
             side, fork, join = self._side_stream()
@@ -223,11 +236,11 @@ class DeviceStep:
             accept_fn(stream, step)
             self.propose(stream, step=step, device_step=device_step, row_norms=row_norms)
 
-    def loop_forward(self, step: int = 0, attention: bool = True, stream=None, overlap: bool = True,
+    def loop_forward(self, step: int = 0, attention: bool = True, stream=None, overlap: Optional[bool] = None,
                      device_step: bool = False, carry: bool = True):
         """One forward of the decoding loop: attention over ``positions`` cached tokens,
-        accept with the commit of the forward's rows, and proposals (side by side unless
-        ``overlap`` is False), bookkeeping.  Lengths are updated in place, so build the
+        accept with the commit of the forward's rows, and proposals (side by side with
+        ``overlap``, after the accept chain without it; None: ``side_by_side()``), bookkeeping.  Lengths are updated in place, so build the
         step with ``commit_in_place=True``.  With ``device_step`` the Philox
         step of every request is its forward count on the device (``step`` unused), so the
         forward can be recorded once and replayed.  With ``carry`` the proposals also write
@@ -249,7 +262,7 @@ class DeviceStep:
         if carry:
             e["norms_valid"] = True
 
-    def capture_loop_forward(self, overlap: bool = True):
+    def capture_loop_forward(self, overlap: Optional[bool] = None):
         """Record one ``loop_forward(device_step=True)`` into a HIP graph and return it.
 
         Every replay is the next forward: the loop state (proposals, positions, mode,
@@ -259,6 +272,8 @@ class DeviceStep:
         runs nothing; call ``loop_forward(device_step=True, overlap=...)`` eagerly at
         least twice before (the second forward is the first with carried q normalisers),
         so every call is marshalled and the second stream exists."""
+        if overlap is None:
+            overlap = self.side_by_side()
         if ("accept_commit", True, True, True) not in self.__dict__.get("_calls", {}) or (
                 overlap and "side_stream" not in self.extra):
             raise RuntimeError("run loop_forward(device_step=True) eagerly before recording it")
@@ -290,9 +305,10 @@ class DeviceStep:
             self.run()
         return graph
 
-    def run(self, stream=None, overlap: bool = True):
+    def run(self, stream=None, overlap: Optional[bool] = None):
         """One ISD step: attention -> accept + commit (-> LoRA delta); with MASK logits the
-        next proposals run beside the accept chain (``overlap``) or after it."""
+        next proposals run beside the accept chain (``overlap``) or after it (None:
+        ``side_by_side()``)."""
         self.attention(stream)
         if self.mask_logits is not None:
             self._accept_and_propose(lambda s, t: self.accept_commit(s, step=t), stream, None, overlap)
