@@ -152,13 +152,19 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
   first_part.max = -INFINITY;
   first_part.idx = INT_MAX;
   if (wave == 0 && s0 < s1) first_part = rp[s0];
-  uint32_t rid32 = 0, pos32 = 0, step32 = step;
+  // wave 0: this proposal's uniform, counter (request, position + N + k, step, 1),
+  // word 0, drawn while the shard records are in flight (its inputs come by the
+  // scalar path); wave 1 fills the exponential's table meanwhile
+  double u = 0.0;
   if (wave == 0 && sample) {
-    rid32 = uint32_t(req_ids[r]);
-    pos32 = uint32_t(positions[r]);
-    if (step_dev) step32 = uint32_t(step_dev[r]);
+    const uint32_t step32 = step_dev ? uint32_t(step_dev[r]) : step;
+    const uint64_t pos = uint64_t(uint32_t(positions[r])) + uint64_t(N + k);
+    u = unit_double(philox4x64_10(uint64_t(uint32_t(req_ids[r])), pos, uint64_t(step32), 1, seed_lo, seed_hi).w[0]);
   }
-  if (sample) fill_exp_table(tab64);
+  if (sample) {
+    if (wave == 1) tab64[lane] = exp2(double(lane) * (1.0 / 64.0));
+    __syncthreads();
+  }
   if (wave == 0) {
     float mx = -INFINITY;
     int ix = INT_MAX;
@@ -172,10 +178,6 @@ __global__ __launch_bounds__(kPThreads) void prop_select(const T* __restrict__ l
     if (!sample) {
       if (lane == 0) out[row] = (I == INT_MAX) ? 0 : I;
     } else {
-      // uniform of this proposal: counter (request, position + N + k, step, 1), word 0
-      const uint64_t rid = uint64_t(rid32);
-      const uint64_t pos = uint64_t(pos32) + uint64_t(N + k);
-      const double u = unit_double(philox4x64_10(rid, pos, uint64_t(step32), 1, seed_lo, seed_hi).w[0]);
       // shard masses in units of exp(row max)
       const double Md = M;
       double wsh = 0.0;
