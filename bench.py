@@ -543,8 +543,9 @@ def main(argv=None):
             "avg_launch_ms": round(attn_ms, 5),
         },
         "accept": {
-            "what": "isd_accept_commit: row normalisers and decision, residual pass with the KV commit, "
-                    "residual selection (three launches)",
+            "what": "isd_accept_commit: row normalisers, accept decision (its own launch, or inside "
+                    "every residual pass workgroup on small batches), residual pass, residual selection "
+                    "with the KV commit",
             "bound": "hbm",
             "bytes_per_call": int(accept_bytes),
             "avg_call_ms": round(accept_ms, 5),
